@@ -1,0 +1,261 @@
+"""Plain float64 CPU oracle of the SuperGlue matching forward pass.
+
+TEST INFRASTRUCTURE ONLY.  This package is the slow, obviously correct
+definition that the HIP library is checked against.  Only the tests, the
+smoke check and the CPU-baseline leg of the benchmark may import it; the
+product path never does, and this package imports nothing from the product.
+
+Every function follows the pages it cites, in their order and notation, in
+float64 with numpy.  Library primitives (matrix products, exp, log) serve as
+steps; there is no blocking, fusion or reordering beyond what the cited
+definitions state.  Pages cited (by title):
+
+* "SuperGlue 的注意力图神经网络怎样传递信息" (huluoboge.top blog)  -> [GNN-blog]
+* "SuperGlue:Learning Feature Matching with Graph Neural Networks论文阅读"
+  (realcat.vercel.app notes)                                        -> [realcat]
+* "SuperGlue_model_forward_learning" (SuperGlue_Code_Learning notes) -> [forward-notes]
+* "论文解读:LightGlue,让稀疏特征匹配随难度自适应地快" (vincentqin.tech) -> [LightGlue-review]
+
+Readings taken where the pages are silent (each also pinned by a test):
+
+* attention logits are scaled by 1/sqrt(d_head) per head;
+* heads own contiguous channel blocks [h*d_head, (h+1)*d_head);
+* the concatenated heads pass a Linear(D, D) merge projection with bias;
+* batch normalisation between MLP layers is omitted (it folds into W, b);
+* both images are updated from the pre-stage states of a stage;
+* argmax ties go to the lowest index; the match threshold is strict '>';
+* masked (padded) keys and points are simply absent: a padded pair is the
+  unpadded pair.
+
+Parity status: every function below is pinned by `tests/test_oracle_*.py`
+except the end-to-end composition with trained weights, which no page prints
+(parity unpinned beyond the invariants and per-step pins).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "normalize_keypoints", "keypoint_encoder", "multi_head_attention",
+    "attentional_propagation", "attentional_gnn", "final_projection",
+    "score_matrix", "logsumexp", "log_sinkhorn_iterations",
+    "log_optimal_transport", "extract_matches", "superglue_match",
+    "superglue_descriptors", "sinkhorn_knopp_exp", "match_from_descriptors",
+]
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def normalize_keypoints(kpts, width, height):
+    """[forward-notes] normalize_keypoints: centre on (width/2, height/2) and
+    divide both coordinates by 0.7 * max(width, height)."""
+    kpts = _f64(kpts)
+    size = np.array([width, height], dtype=np.float64)
+    center = size / 2.0
+    scaling = size.max() * 0.7
+    return (kpts - center[None, :]) / scaling
+
+
+def keypoint_encoder(kpts_n, conf, layers):
+    """[realcat] section "特征点Encode" (KeypointEncoder / MLP): the input per
+    point is (x, y, c); each layer is a per-point linear map W p + b
+    (Conv1d with kernel 1), followed by ReLU except after the last layer."""
+    h = np.concatenate([_f64(kpts_n), _f64(conf)[:, None]], axis=1)
+    for i, (W, b) in enumerate(layers):
+        h = h @ _f64(W).T + _f64(b)
+        if i < len(layers) - 1:
+            h = np.maximum(h, 0.0)
+    return h
+
+
+def _softmax_rows(e):
+    """[GNN-blog] section "Attention 让节点自己选择消息来源": alpha_ij =
+    exp(e_ij) / sum_r exp(e_ir) over the allowed sources of row i."""
+    e = e - e.max(axis=1, keepdims=True)
+    a = np.exp(e)
+    return a / a.sum(axis=1, keepdims=True)
+
+
+def multi_head_attention(x, src, st, heads):
+    """Message m for every query point of `x` from the source points `src`.
+
+    [realcat] section "Attentional Aggregation": q_i = W1 x_i^Q + b1 from the
+    query image, [k_j; v_j] = [W2; W3] x_j^S + [b2; b3] from the source image,
+    m_i = sum_j alpha_ij v_j with alpha_ij = softmax_j(q_i^T k_j).
+    [GNN-blog] section "Attention 让节点自己选择消息来源": logits divided by
+    sqrt(d_k), d_k the per-head dimension.  Heads split D into contiguous
+    blocks; the concatenated heads then pass the merge projection
+    W_m m + b_m.  Stage weights `st` hold Wq,bq,Wk,bk,Wv,bv,Wm,bm.
+    """
+    x, src = _f64(x), _f64(src)
+    D = x.shape[1]
+    dh = D // heads
+    q = x @ _f64(st["Wq"]).T + _f64(st["bq"])
+    k = src @ _f64(st["Wk"]).T + _f64(st["bk"])
+    v = src @ _f64(st["Wv"]).T + _f64(st["bv"])
+    msg = np.zeros((x.shape[0], D))
+    for h in range(heads):
+        c = slice(h * dh, (h + 1) * dh)
+        e = (q[:, c] @ k[:, c].T) / np.sqrt(dh)
+        msg[:, c] = _softmax_rows(e) @ v[:, c]
+    return msg @ _f64(st["Wm"]).T + _f64(st["bm"])
+
+
+def attentional_propagation(x, src, st, heads):
+    """[realcat] section "多层GNN" (AttentionalPropagation): the residual
+    update MLP([x || m]) with channels [2D, 2D, D], ReLU between the two
+    layers.  Returns the update (delta), not x + delta."""
+    m = multi_head_attention(x, src, st, heads)
+    h = np.concatenate([_f64(x), m], axis=1) @ _f64(st["W1"]).T + _f64(st["b1"])
+    h = np.maximum(h, 0.0)
+    return h @ _f64(st["W2"]).T + _f64(st["b2"])
+
+
+def attentional_gnn(xA, xB, stages, heads):
+    """[realcat] section "多层GNN" (AttentionalGNN) and [GNN-blog] section
+    "多轮消息怎样回到同一幅图": stages alternate self (sources = own image)
+    and cross (sources = the other image), self first; each stage has its own
+    weights, shared by both images, and both deltas are computed from the
+    states before the stage, then added."""
+    xA, xB = _f64(xA).copy(), _f64(xB).copy()
+    for s, st in enumerate(stages):
+        if s % 2 == 0:          # self
+            srcA, srcB = xA, xB
+        else:                   # cross
+            srcA, srcB = xB, xA
+        dA = attentional_propagation(xA, srcA, st, heads)
+        dB = attentional_propagation(xB, srcB, st, heads)
+        xA, xB = xA + dA, xB + dB
+    return xA, xB
+
+
+def final_projection(x, Wf, bf):
+    """[realcat] section "Attentional Aggregation" (last equation): matching
+    descriptors f_i = W x_i^(L) + b."""
+    return _f64(x) @ _f64(Wf).T + _f64(bf)
+
+
+def score_matrix(fA, fB):
+    """[realcat] section "匹配得分预测": S_ij = <f_i^A, f_j^B>; [forward-notes]
+    forward: divided by sqrt(descriptor_dim)."""
+    fA, fB = _f64(fA), _f64(fB)
+    return (fA @ fB.T) / np.sqrt(fA.shape[1])
+
+
+def logsumexp(X, axis):
+    """log sum exp along `axis`, as max + log(sum(exp(X - max)))."""
+    m = X.max(axis=axis, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    return np.squeeze(m, axis=axis) + np.log(np.exp(X - m).sum(axis=axis))
+
+
+def log_sinkhorn_iterations(Z, log_mu, log_nu, iters):
+    """[realcat] section "Sinkhorn Algorithm" (log_sinkhorn_iterations): from
+    u = v = 0, repeat `iters` times: u = log_mu - lse_j(Z_ij + v_j), then
+    v = log_nu - lse_i(Z_ij + u_i); return Z + u + v."""
+    u = np.zeros_like(log_mu)
+    v = np.zeros_like(log_nu)
+    for _ in range(iters):
+        u = log_mu - logsumexp(Z + v[None, :], axis=1)
+        v = log_nu - logsumexp(Z + u[:, None], axis=0)
+    return Z + u[:, None] + v[None, :]
+
+
+def log_optimal_transport(S, alpha, iters):
+    """[realcat] sections "遮挡以及可见性" and "Sinkhorn Algorithm"
+    (log_optimal_transport): append a dustbin column, row and corner all
+    equal to alpha; marginals a = [1_M, N], b = [1_N, M] normalised by M+N in
+    log space (norm = -log(M+N)); run the log-domain iterations; then
+    subtract norm (multiply the probabilities by M+N).  Returns the
+    (M+1) x (N+1) log assignment."""
+    S = _f64(S)
+    M, N = S.shape
+    Z = np.full((M + 1, N + 1), float(alpha))
+    Z[:M, :N] = S
+    norm = -np.log(M + N)
+    log_mu = np.concatenate([np.full(M, norm), [np.log(N) + norm]])
+    log_nu = np.concatenate([np.full(N, norm), [np.log(M) + norm]])
+    return log_sinkhorn_iterations(Z, log_mu, log_nu, iters) - norm
+
+
+def extract_matches(logP, threshold=0.0):
+    """[forward-notes] forward, "Get the matches with score above
+    match_threshold": argmax of every row and column of the real block
+    (lowest index on ties), mutual check, score = exp(row max) for mutual
+    rows, valid if mutual and score > threshold; -1 / 0 elsewhere.
+    Returns (matches0, scores0, matches1, scores1)."""
+    P = _f64(logP)[:-1, :-1]
+    M, N = P.shape
+    idx0 = P.argmax(axis=1)
+    idx1 = P.argmax(axis=0)
+    max0 = P[np.arange(M), idx0]
+    mutual0 = idx1[idx0] == np.arange(M)
+    mutual1 = idx0[idx1] == np.arange(N)
+    ms0 = np.where(mutual0, np.exp(max0), 0.0)
+    ms1 = np.where(mutual1, ms0[idx1], 0.0)
+    valid0 = mutual0 & (ms0 > threshold)
+    valid1 = mutual1 & valid0[idx1]
+    m0 = np.where(valid0, idx0, -1).astype(np.int32)
+    m1 = np.where(valid1, idx1, -1).astype(np.int32)
+    return m0, ms0, m1, ms1
+
+
+def superglue_descriptors(pair, weights, L=None):
+    """Encoder + GNN + final projection for one unpadded pair; returns a dict
+    with x0 (initial states), xL (last states) and f (matching descriptors)
+    for both images.  [realcat] "特征点Encode": x^(0) = d + MLP_enc(p);
+    [forward-notes] forward: normalise keypoints by the image size first."""
+    L = weights["L"] if L is None else L
+    H = weights["H"]
+    out = {}
+    xs = []
+    for side in ("0", "1"):
+        w, h = pair["image_size" + side]
+        kn = normalize_keypoints(pair["kpts" + side], w, h)
+        x0 = _f64(pair["desc" + side]) + keypoint_encoder(kn, pair["conf" + side], weights["enc"])
+        xs.append(x0)
+        out["x0_" + side] = x0
+    xA, xB = attentional_gnn(xs[0], xs[1], weights["stages"][:2 * L], H)
+    out["xL_0"], out["xL_1"] = xA, xB
+    out["f0"] = final_projection(xA, weights["Wf"], weights["bf"])
+    out["f1"] = final_projection(xB, weights["Wf"], weights["bf"])
+    return out
+
+
+def match_from_descriptors(fA, fB, alpha, T, threshold=0.0):
+    """Scores, optimal transport and extraction from matching descriptors."""
+    S = score_matrix(fA, fB)
+    logP = log_optimal_transport(S, alpha, T)
+    m0, s0, m1, s1 = extract_matches(logP, threshold)
+    return {"S": S, "logP": logP, "matches0": m0, "scores0": s0, "matches1": m1, "scores1": s1}
+
+
+def superglue_match(pair, weights, L=None, T=100, threshold=0.0):
+    """The whole forward pass for one pair.  [forward-notes] forward: with no
+    keypoints in either image, matches are -1 and scores 0 and nothing else
+    is computed."""
+    M = len(pair["kpts0"])
+    N = len(pair["kpts1"])
+    if M == 0 or N == 0:
+        return {"matches0": -np.ones(M, np.int32), "scores0": np.zeros(M),
+                "matches1": -np.ones(N, np.int32), "scores1": np.zeros(N)}
+    out = superglue_descriptors(pair, weights, L)
+    out.update(match_from_descriptors(out["f0"], out["f1"], weights["alpha"], T, threshold))
+    return out
+
+
+def sinkhorn_knopp_exp(Zbar, a, b, iters):
+    """Second, independent algorithm for the same iteration, in the
+    probability domain: [realcat] section "Sinkhorn Algorithm" (the MATLAB
+    demo's loop) with the kernel exp(+Zbar) of a similarity matrix: start from
+    exp(Zbar) normalised to sum 1, then `iters` times scale the rows to sum to
+    a and the columns to sum to b.  No early stop.  Test use only."""
+    P = np.exp(_f64(Zbar))
+    P = P / P.sum()
+    a, b = _f64(a), _f64(b)
+    for _ in range(iters):
+        P = P * (a / P.sum(axis=1))[:, None]
+        P = P * (b / P.sum(axis=0))[None, :]
+    return P
