@@ -195,7 +195,14 @@ def extract_matches(logP, threshold=0.0):
     mutual1 = idx0[idx1] == np.arange(N)
     ms0 = np.where(mutual0, np.exp(max0), 0.0)
     ms1 = np.where(mutual1, ms0[idx1], 0.0)
-    valid0 = mutual0 & (ms0 > threshold)
+    # exp(max0) > threshold, decided exactly: in log space for a positive
+    # threshold, and always true otherwise (exp never reaches 0), so that the
+    # underflow of exp for very negative log assignments cannot flip it
+    if threshold > 0:
+        above = max0 > np.log(threshold)
+    else:
+        above = np.ones(M, dtype=bool)
+    valid0 = mutual0 & above
     valid1 = mutual1 & valid0[idx1]
     m0 = np.where(valid0, idx0, -1).astype(np.int32)
     m1 = np.where(valid1, idx1, -1).astype(np.int32)

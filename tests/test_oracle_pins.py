@@ -384,3 +384,17 @@ def test_final_projection_orientation():
     for i in range(4):
         for o in range(5):
             assert abs(f[i, o] - (sum(W[o, k] * x[i, k] for k in range(3)) + b[o])) < 1e-12
+
+
+def test_extraction_threshold_is_exact_for_tiny_probabilities():
+    """A mutual match whose exp underflows in floating point still has a
+    positive score in exact arithmetic, so it is valid at threshold 0."""
+    logP = np.full((3, 3), -2000.0)
+    logP[0, 0] = -800.0           # exp(-800) == 0.0 in float64
+    logP[1, 1] = np.log(0.3)
+    m0, s0, m1, _ = oracle.extract_matches(logP, 0.0)
+    np.testing.assert_array_equal(m0, [0, 1])
+    m0, _, _, _ = oracle.extract_matches(logP, 0.25)
+    np.testing.assert_array_equal(m0, [-1, 1])
+    m0, _, _, _ = oracle.extract_matches(logP, 0.35)
+    np.testing.assert_array_equal(m0, [-1, -1])
