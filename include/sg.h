@@ -1,0 +1,202 @@
+/*
+ * sg.h - C ABI of the MI355X (gfx950) SuperGlue matching forward pass.
+ *
+ * The method: a keypoint encoder MLP over (x, y, c) added to each descriptor,
+ * 2L attentional message-passing stages alternating self and cross attention
+ * with residual MLP updates, a final linear projection, an inner-product
+ * score matrix augmented with a dustbin row and column, log-domain Sinkhorn
+ * normalisation, and mutual-argmax match extraction.  Sources (by page title):
+ *   "SuperGlue 的注意力图神经网络怎样传递信息" (huluoboge.top blog),
+ *   "SuperGlue:Learning Feature Matching with Graph Neural Networks论文阅读"
+ *   (realcat.vercel.app notes), "SuperGlue_model_forward_learning"
+ *   (SuperGlue_Code_Learning notes).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers unless marked "host".  All buffers belong
+ *    to the caller; the library never frees them.
+ *  - Point-major layouts: kpts [n][2] (x, y), conf [n], desc [n][D],
+ *    matrices row-major [out][in] (a kernel-1 Conv1d / Linear weight).
+ *  - Every call is asynchronous on opts->stream (NULL = default stream):
+ *    it validates its arguments on the host, enqueues kernels and returns.
+ *    Outputs are valid once the caller synchronises that stream.  No call
+ *    copies between host and device or synchronises.
+ *  - All validation happens before the first HIP call: on any error nothing
+ *    is enqueued and outputs are untouched; sg_last_error() describes it.
+ *  - Scratch memory: the caller may pass a workspace of at least
+ *    sg_workspace_size() bytes; with none, the library keeps one grow-only
+ *    buffer per device (allocated on first use, held until process exit).
+ *    Calls that share a workspace (or the library's) must not overlap in
+ *    time on different streams.
+ */
+#ifndef SG_H
+#define SG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* sg_stream_t; /* identical to hipStream_t */
+typedef struct ihipEvent_t* sg_event_t;   /* identical to hipEvent_t  */
+
+typedef enum {
+  SG_OK = 0,
+  SG_ERR_INVALID_ARG = -1, /* NULL pointer, negative size, bad L/T/D/H ... */
+  SG_ERR_UNSUPPORTED = -2, /* shape with no kernel specialisation          */
+  SG_ERR_WEIGHTS = -3,     /* weight blob too small / inconsistent config  */
+  SG_ERR_WORKSPACE = -4,   /* caller workspace smaller than required       */
+  SG_ERR_HIP = -5          /* HIP runtime error (message in sg_last_error) */
+} sg_status;
+
+typedef enum { SG_F32 = 0, SG_BF16 = 1 } sg_dtype;
+
+#define SG_MAX_ENC 8     /* hidden layers of the keypoint encoder          */
+#define SG_MAX_BATCH 64  /* pairs per sg_match_batch call                  */
+
+/*
+ * Network description plus a device weight blob.
+ *
+ * D: descriptor dimension; H: attention heads (D % H == 0; supported head
+ * dimensions 16 and 64).  enc[0..n_enc-1]: hidden widths of the keypoint
+ * encoder MLP [3, enc..., D] ("特征点Encode" section of the realcat notes;
+ * the pages' batch normalisation is folded away).  L_max: self+cross pairs
+ * stored (2*L_max stages).  dtype: type of every matrix and bias in the blob
+ * and of the GNN's contraction operands (accumulation is always fp32; the
+ * residual stream, the encoder, scores and Sinkhorn are always fp32).
+ *
+ * Blob layout: tensors in the order below, each starting at a 256-byte
+ * aligned offset (sg_weights_tensor() enumerates offsets and shapes):
+ *   encoder layer i = 0..n_enc: W [w_{i+1}][w_i], b [w_{i+1}]
+ *   stage s = 0..2*L_max-1 (even s = self, odd s = cross):
+ *     W_qkv [3D][D] (rows: q, then k, then v), b_qkv [3D],
+ *     W_m [D][D], b_m [D]          (merge of the concatenated heads),
+ *     W_1 [2D][2D], b_1 [2D]       (columns 0..D-1 multiply x, D..2D-1 m),
+ *     W_2 [D][2D], b_2 [D]
+ *   W_f [D][D], b_f [D]            (final projection)
+ *   alpha: one float32             (dustbin score, always fp32)
+ * Head h owns channels [h*D/H, (h+1)*D/H) of q, k, v and of the merge input.
+ */
+typedef struct {
+  int32_t D, H;
+  int32_t n_enc;
+  int32_t enc[SG_MAX_ENC];
+  int32_t L_max;
+  int32_t dtype;       /* sg_dtype */
+  const void* blob;    /* device pointer, caller-owned */
+  size_t blob_bytes;
+} sg_weights;
+
+/* Optional per-stage / per-kernel timing (hipEvents created by the caller). */
+enum {
+  SG_EV_START = 0,     /* before the encoder                       */
+  SG_EV_ENCODED = 1,   /* after the encoder                        */
+  SG_EV_GNN = 2,       /* after the 2L stages                      */
+  SG_EV_SCORES = 3,    /* after final projection + score matrix    */
+  SG_EV_SINKHORN = 4,  /* after the T iterations                   */
+  SG_EV_END = 5,       /* after extraction (and optional outputs)  */
+  SG_N_STAGE_EVENTS = 6
+};
+enum { /* kernel classes that can be bracketed by kernel_events */
+  SG_K_NONE = 0, SG_K_GEMM = 1, SG_K_ATTENTION = 2, SG_K_SINKHORN = 3
+};
+
+typedef struct {
+  sg_stream_t stream;          /* NULL = default stream */
+  void* workspace;             /* NULL = library-owned per-device buffer */
+  size_t workspace_bytes;
+  float match_threshold;       /* valid match iff mutual and exp(logP) > threshold */
+  float image_size[4];         /* wA, hA, wB, hB (pixels); all 0: kpts already normalised */
+  int32_t* out_matches1;       /* optional [N] (batch: [B][Npad]) */
+  float* out_scores1;          /* optional [N] */
+  float* out_desc_A;           /* optional matching descriptors f, [M][D] fp32 */
+  float* out_desc_B;           /* optional [N][D] fp32 */
+  float* out_logP;             /* optional (M+1) x (N+1) log assignment, fp32 */
+  int64_t logP_ld;             /* leading dimension of out_logP (>= N+1)    */
+  sg_event_t* stage_events;    /* optional: SG_N_STAGE_EVENTS events, recorded at the boundaries */
+  int32_t n_stage_events;
+  int32_t timed_kernel;        /* SG_K_* class to bracket with kernel_events */
+  sg_event_t* kernel_events;   /* optional: 2 per launch (before, after), in launch order */
+  int32_t n_kernel_events;     /* capacity; launches beyond it are not bracketed */
+  int32_t* n_kernel_launches;  /* host: receives the number of bracketed launches */
+} sg_opts;
+
+/* Number of tensors in the blob (the alpha scalar counts as one). */
+int32_t sg_weights_count(const sg_weights* w);
+/* Offset (bytes), rows and cols of tensor `index` (biases: rows = 1; alpha: 1 x 1). */
+sg_status sg_weights_tensor(const sg_weights* w, int32_t index, size_t* offset,
+                            int32_t* rows, int32_t* cols);
+/* Total blob bytes for this configuration. */
+size_t sg_weights_bytes(const sg_weights* w);
+
+/* Workspace bytes for pairs of at most Mmax x Nmax points, `batch` pairs. */
+size_t sg_workspace_size(const sg_weights* w, int32_t Mmax, int32_t Nmax, int32_t batch);
+
+/*
+ * The whole forward pass for one pair (A: M points, B: N points), using the
+ * first L self+cross pairs of the blob and T Sinkhorn iterations.
+ * Outputs: out_matches [M] int32 (index into B, or -1), out_scores [M]
+ * (exp of the log assignment of a mutual match, else 0).  Optional outputs
+ * in opts.  M == 0 or N == 0: matches -1, scores 0, nothing else computed
+ * (the forward walk-through of the SuperGlue_Code_Learning notes).
+ * kpts: pixels when opts->image_size is set, else already normalised as
+ * (kpt - size/2) / (0.7 max(w, h)).  desc: float32 [n][D].
+ */
+sg_status sg_match(const float* kptsA, const float* descA, const float* confA, int32_t M,
+                   const float* kptsB, const float* descB, const float* confB, int32_t N,
+                   const sg_weights* weights, int32_t L, int32_t T,
+                   int32_t* out_matches, float* out_scores, const sg_opts* opts);
+
+/*
+ * B independent pairs in one call.  Inputs are padded: kptsA [B][Mpad][2],
+ * descA [B][Mpad][D], confA [B][Mpad] (B likewise with Npad); M, N are HOST
+ * arrays of the true counts (0 <= M[b] <= Mpad).  Padded points are absent
+ * from every softmax, from Sinkhorn (whose marginals use the true counts) and
+ * from the outputs: each pair's result equals sg_match on the unpadded pair.
+ * Outputs: out_matches [B][Mpad], out_scores [B][Mpad]; padded entries are
+ * -1 / 0.  opts->out_matches1/out_scores1 are [B][Npad]; out_logP is
+ * [B][Mpad+1][logP_ld] with logP_ld >= Npad+1 (entries beyond a pair's
+ * (M+1) x (N+1) block are left untouched); out_desc_* are [B][Mpad|Npad][D].
+ */
+sg_status sg_match_batch(int32_t B, int32_t Mpad, int32_t Npad, const int32_t* M, const int32_t* N,
+                         const float* kptsA, const float* descA, const float* confA,
+                         const float* kptsB, const float* descB, const float* confB,
+                         const sg_weights* weights, int32_t L, int32_t T,
+                         int32_t* out_matches, float* out_scores, const sg_opts* opts);
+
+/* ---- stage entry points (same conventions; for per-stage parity and timing) ---- */
+
+/* Encoder: x0 [n][D] fp32 = desc + MLP_enc(normalised kpts, conf).
+   image_w/image_h > 0: kpts in pixels; both 0: already normalised. */
+sg_status sg_stage_encode(const float* kpts, const float* conf, const float* desc, int32_t n,
+                          float image_w, float image_h, const sg_weights* weights,
+                          float* x_out, const sg_opts* opts);
+
+/* Stages s0 .. s1-1 of the GNN, in place on the fp32 states xA [M][D], xB [N][D]. */
+sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weights* weights,
+                       int32_t s0, int32_t s1, const sg_opts* opts);
+
+/* Final projection f [n][D] fp32 = W_f x + b_f. */
+sg_status sg_stage_project(const float* x, int32_t n, const sg_weights* weights, float* f_out,
+                           const sg_opts* opts);
+
+/* Scores S = fA fB^T / sqrt(D), dustbin alpha, T Sinkhorn iterations and
+   extraction, from matching descriptors fA [M][D], fB [N][D] (fp32). */
+sg_status sg_stage_match(const float* fA, int32_t M, const float* fB, int32_t N, int32_t D,
+                         float alpha, int32_t T, int32_t* out_matches, float* out_scores,
+                         const sg_opts* opts);
+
+/* Workspace bytes of sg_stage_match for M x N points of dimension D. */
+size_t sg_stage_match_workspace_size(int32_t M, int32_t N, int32_t D);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* sg_last_error(void);
+
+/* Library version string. */
+const char* sg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SG_H */

@@ -1,0 +1,314 @@
+"""Python binding of libsg, the MI355X (gfx950) SuperGlue matching forward pass.
+
+Every entry point mirrors the C function of the same name in include/sg.h and
+only marshals arguments: torch tensors supply device memory and the stream,
+and every step of the pass runs in the library's HIP kernels.  There is no
+CPU fallback: without the built library (or without a GPU) calls raise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import (SG_BF16, SG_F32, SG_K_ATTENTION, SG_K_GEMM, SG_K_NONE, SG_K_SINKHORN,
+                   SG_MAX_BATCH, SG_N_STAGE_EVENTS, SgError, SgOpts, SgWeights)
+
+__all__ = ["Weights", "weights_config", "pack_weights", "workspace_size", "sg_match",
+           "sg_match_batch", "sg_stage_encode", "sg_stage_gnn", "sg_stage_project",
+           "sg_stage_match", "lib", "SgError", "SG_K_GEMM", "SG_K_ATTENTION", "SG_K_SINKHORN",
+           "SG_N_STAGE_EVENTS"]
+
+
+def lib():
+    return _lib.load()
+
+
+def _dtype_code(dtype: str) -> int:
+    return {"f32": SG_F32, "bf16": SG_BF16}[dtype]
+
+
+def weights_config(D: int, H: int, enc: Sequence[int], L_max: int, dtype: str = "f32") -> SgWeights:
+    st = SgWeights()
+    st.D, st.H, st.n_enc, st.L_max, st.dtype = D, H, len(enc), L_max, _dtype_code(dtype)
+    for i, e in enumerate(enc):
+        st.enc[i] = e
+    return st
+
+
+class Weights:
+    """A device weight blob plus the sg_weights struct that describes it."""
+
+    def __init__(self, struct: SgWeights, blob: torch.Tensor, L_max: int):
+        self.struct = struct
+        self.blob = blob
+        self.L_max = L_max
+        struct.blob = blob.data_ptr()
+        struct.blob_bytes = blob.numel()
+
+    @property
+    def ref(self):
+        return C.byref(self.struct)
+
+    @property
+    def D(self):
+        return self.struct.D
+
+
+def _ordered_tensors(w: dict):
+    out = []
+    for W, b in w["enc"]:
+        out += [W, b]
+    for st in w["stages"]:
+        out += [np.concatenate([st["Wq"], st["Wk"], st["Wv"]]), np.concatenate([st["bq"], st["bk"], st["bv"]]),
+                st["Wm"], st["bm"], st["W1"], st["b1"], st["W2"], st["b2"]]
+    out += [w["Wf"], w["bf"], np.array([w["alpha"]], dtype=np.float32)]
+    return out
+
+
+def pack_weights(w: dict, device="cuda") -> Weights:
+    """Lay the weight dictionary (row-major [out][in] matrices) out as the
+    library's blob, in the blob dtype, and upload it."""
+    enc = [W.shape[0] for W, _ in w["enc"][:-1]]
+    L_max = len(w["stages"]) // 2
+    st = weights_config(w["D"], w["H"], enc, L_max, w["dtype"])
+    L = lib()
+    nbytes = L.sg_weights_bytes(C.byref(st))
+    count = L.sg_weights_count(C.byref(st))
+    if nbytes == 0 or count <= 0:
+        raise SgError(-1, "sg_weights_bytes")
+    tensors = _ordered_tensors(w)
+    if len(tensors) != count:
+        raise ValueError(f"weight dictionary has {len(tensors)} tensors, the layout {count}")
+    host = torch.zeros(nbytes, dtype=torch.uint8)
+    tdt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
+    off, rows, cols = C.c_size_t(), C.c_int32(), C.c_int32()
+    for i, arr in enumerate(tensors):
+        _lib.check(L.sg_weights_tensor(C.byref(st), i, C.byref(off), C.byref(rows), C.byref(cols)),
+                   "sg_weights_tensor")
+        arr = np.ascontiguousarray(arr, dtype=np.float32).reshape(-1)
+        if arr.size != rows.value * cols.value:
+            raise ValueError(f"tensor {i}: {arr.size} values, layout {rows.value}x{cols.value}")
+        t = torch.from_numpy(arr).to(torch.float32 if i == count - 1 else tdt)
+        raw = t.view(torch.uint8)
+        host[off.value: off.value + raw.numel()] = raw
+    return Weights(st, host.to(device), L_max)
+
+
+def workspace_size(weights: Weights, Mmax: int, Nmax: int, batch: int = 1) -> int:
+    return int(lib().sg_workspace_size(weights.ref, Mmax, Nmax, batch))
+
+
+_ws_cache = {}
+
+
+def _workspace(device, nbytes):
+    key = torch.device(device).index or 0
+    t = _ws_cache.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _ws_cache[key] = t
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _check_tensor(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _events_array(events):
+    if not events:
+        return None, 0
+    arr = (C.c_void_p * len(events))(*[e.cuda_event for e in events])
+    return arr, len(events)
+
+
+def make_events(n: int):
+    """Timing events usable by the library (created on the current stream)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()  # materialise the underlying hipEvent
+    return evs
+
+
+def _opts(device, *, threshold=0.0, image_size=None, workspace=None, ws_bytes=0, m1=None, s1=None,
+          fA=None, fB=None, logP=None, logP_ld=0, stage_events=None, timed_kernel=SG_K_NONE,
+          kernel_events=None, stream=None):
+    o = SgOpts()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    o.stream = s.cuda_stream
+    if workspace is not None:
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel()
+    o.match_threshold = float(threshold)
+    if image_size is not None:
+        for i, v in enumerate(image_size):
+            o.image_size[i] = float(v)
+    o.out_matches1 = None if m1 is None else m1.data_ptr()
+    o.out_scores1 = None if s1 is None else s1.data_ptr()
+    o.out_desc_A = None if fA is None else fA.data_ptr()
+    o.out_desc_B = None if fB is None else fB.data_ptr()
+    o.out_logP = None if logP is None else logP.data_ptr()
+    o.logP_ld = logP_ld
+    keep = []
+    arr, n = _events_array(stage_events)
+    if arr is not None:
+        o.stage_events, o.n_stage_events = C.cast(arr, C.c_void_p), n
+        keep.append(arr)
+    arr, n = _events_array(kernel_events)
+    if arr is not None:
+        o.timed_kernel = timed_kernel
+        o.kernel_events, o.n_kernel_events = C.cast(arr, C.c_void_p), n
+        keep.append(arr)
+    count = C.c_int32(0)
+    o.n_kernel_launches = C.pointer(count)
+    keep.append(count)
+    return o, keep, count
+
+
+def sg_match(kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int, T: int, *,
+             threshold: float = 0.0, image_size=None, want_matches1=True, want_logP=False,
+             want_desc=False, workspace=None, stage_events=None, timed_kernel=SG_K_NONE,
+             kernel_events=None, stream=None) -> dict:
+    """One pair.  kpts [n][2] (pixels if image_size=(wA, hA, wB, hB) is given),
+    desc [n][D], conf [n]: float32 CUDA tensors.  Returns device tensors."""
+    dev = descA.device
+    M, N, D = kptsA.shape[0], kptsB.shape[0], weights.D
+    for t, nm, shp in ((kptsA, "kptsA", (M, 2)), (descA, "descA", (M, D)), (confA, "confA", (M,)),
+                       (kptsB, "kptsB", (N, 2)), (descB, "descB", (N, D)), (confB, "confB", (N,))):
+        _check_tensor(t, nm, torch.float32, shp)
+    out = {"matches0": torch.empty(M, dtype=torch.int32, device=dev),
+           "scores0": torch.empty(M, dtype=torch.float32, device=dev)}
+    if want_matches1:
+        out["matches1"] = torch.empty(N, dtype=torch.int32, device=dev)
+        out["scores1"] = torch.empty(N, dtype=torch.float32, device=dev)
+    if want_logP:
+        out["logP"] = torch.empty((M + 1, N + 1), dtype=torch.float32, device=dev)
+    if want_desc:
+        out["f0"] = torch.empty((M, D), dtype=torch.float32, device=dev)
+        out["f1"] = torch.empty((N, D), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(dev, workspace_size(weights, M, N, 1))
+    o, keep, count = _opts(dev, threshold=threshold, image_size=image_size, workspace=workspace,
+                           m1=out.get("matches1"), s1=out.get("scores1"), fA=out.get("f0"),
+                           fB=out.get("f1"), logP=out.get("logP"), logP_ld=N + 1,
+                           stage_events=stage_events, timed_kernel=timed_kernel,
+                           kernel_events=kernel_events, stream=stream)
+    st = lib().sg_match(_ptr(kptsA), _ptr(descA), _ptr(confA), M, _ptr(kptsB), _ptr(descB), _ptr(confB), N,
+                        weights.ref, L, T, _ptr(out["matches0"]), _ptr(out["scores0"]), C.byref(o))
+    _lib.check(st, "sg_match")
+    out["n_kernel_launches"] = count.value
+    return out
+
+
+def sg_match_batch(M, N, kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int, T: int, *,
+                   threshold: float = 0.0, image_size=None, want_matches1=True, want_logP=False,
+                   want_desc=False, workspace=None, stage_events=None, timed_kernel=SG_K_NONE,
+                   kernel_events=None, stream=None) -> dict:
+    """B padded pairs: kptsA [B][Mpad][2], descA [B][Mpad][D], confA [B][Mpad] (and B
+    likewise); M, N: sequences of the true counts."""
+    dev = descA.device
+    B, Mpad, Npad, D = kptsA.shape[0], kptsA.shape[1], kptsB.shape[1], weights.D
+    for t, nm, shp in ((kptsA, "kptsA", (B, Mpad, 2)), (descA, "descA", (B, Mpad, D)), (confA, "confA", (B, Mpad)),
+                       (kptsB, "kptsB", (B, Npad, 2)), (descB, "descB", (B, Npad, D)), (confB, "confB", (B, Npad))):
+        _check_tensor(t, nm, torch.float32, shp)
+    Ma = (C.c_int32 * B)(*[int(x) for x in M])
+    Na = (C.c_int32 * B)(*[int(x) for x in N])
+    out = {"matches0": torch.empty((B, Mpad), dtype=torch.int32, device=dev),
+           "scores0": torch.empty((B, Mpad), dtype=torch.float32, device=dev)}
+    if want_matches1:
+        out["matches1"] = torch.empty((B, Npad), dtype=torch.int32, device=dev)
+        out["scores1"] = torch.empty((B, Npad), dtype=torch.float32, device=dev)
+    if want_logP:
+        out["logP"] = torch.full((B, Mpad + 1, Npad + 1), float("nan"), dtype=torch.float32, device=dev)
+    if want_desc:
+        out["f0"] = torch.zeros((B, Mpad, D), dtype=torch.float32, device=dev)
+        out["f1"] = torch.zeros((B, Npad, D), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(dev, workspace_size(weights, Mpad, Npad, B))
+    o, keep, count = _opts(dev, threshold=threshold, image_size=image_size, workspace=workspace,
+                           m1=out.get("matches1"), s1=out.get("scores1"), fA=out.get("f0"),
+                           fB=out.get("f1"), logP=out.get("logP"), logP_ld=Npad + 1,
+                           stage_events=stage_events, timed_kernel=timed_kernel,
+                           kernel_events=kernel_events, stream=stream)
+    st = lib().sg_match_batch(B, Mpad, Npad, Ma, Na, _ptr(kptsA), _ptr(descA), _ptr(confA), _ptr(kptsB),
+                              _ptr(descB), _ptr(confB), weights.ref, L, T, _ptr(out["matches0"]),
+                              _ptr(out["scores0"]), C.byref(o))
+    _lib.check(st, "sg_match_batch")
+    out["n_kernel_launches"] = count.value
+    return out
+
+
+def sg_stage_encode(kpts, conf, desc, weights: Weights, image_size=(0.0, 0.0), workspace=None) -> torch.Tensor:
+    n, D = desc.shape[0], weights.D
+    _check_tensor(kpts, "kpts", torch.float32, (n, 2))
+    _check_tensor(conf, "conf", torch.float32, (n,))
+    _check_tensor(desc, "desc", torch.float32, (n, D))
+    x = torch.empty((n, D), dtype=torch.float32, device=desc.device)
+    if workspace is None:
+        workspace = _workspace(desc.device, workspace_size(weights, n, 0, 1))
+    o, keep, _ = _opts(desc.device, workspace=workspace)
+    _lib.check(lib().sg_stage_encode(_ptr(kpts), _ptr(conf), _ptr(desc), n, float(image_size[0]),
+                                     float(image_size[1]), weights.ref, _ptr(x), C.byref(o)),
+               "sg_stage_encode")
+    return x
+
+
+def sg_stage_gnn(xA, xB, weights: Weights, s0: int, s1: int, workspace=None, timed_kernel=SG_K_NONE,
+                 kernel_events=None):
+    """Runs stages [s0, s1) in place on float32 states xA [M][D], xB [N][D]."""
+    M, N, D = xA.shape[0], xB.shape[0], weights.D
+    _check_tensor(xA, "xA", torch.float32, (M, D))
+    _check_tensor(xB, "xB", torch.float32, (N, D))
+    if workspace is None:
+        workspace = _workspace(xA.device, workspace_size(weights, M, N, 1))
+    o, keep, count = _opts(xA.device, workspace=workspace, timed_kernel=timed_kernel,
+                           kernel_events=kernel_events)
+    _lib.check(lib().sg_stage_gnn(_ptr(xA), M, _ptr(xB), N, weights.ref, s0, s1, C.byref(o)), "sg_stage_gnn")
+    return count.value
+
+
+def sg_stage_project(x, weights: Weights) -> torch.Tensor:
+    n, D = x.shape[0], weights.D
+    _check_tensor(x, "x", torch.float32, (n, D))
+    f = torch.empty((n, D), dtype=torch.float32, device=x.device)
+    o, keep, _ = _opts(x.device)
+    _lib.check(lib().sg_stage_project(_ptr(x), n, weights.ref, _ptr(f), C.byref(o)), "sg_stage_project")
+    return f
+
+
+def sg_stage_match(fA, fB, alpha: float, T: int, *, threshold: float = 0.0, want_logP=True,
+                   workspace=None, stage_events=None, timed_kernel=SG_K_NONE, kernel_events=None) -> dict:
+    """Scores, dustbin, T Sinkhorn iterations and extraction from matching descriptors."""
+    M, N, D = fA.shape[0], fB.shape[0], fA.shape[1]
+    _check_tensor(fA, "fA", torch.float32, (M, D))
+    _check_tensor(fB, "fB", torch.float32, (N, D))
+    dev = fA.device
+    out = {"matches0": torch.empty(M, dtype=torch.int32, device=dev),
+           "scores0": torch.empty(M, dtype=torch.float32, device=dev),
+           "matches1": torch.empty(N, dtype=torch.int32, device=dev),
+           "scores1": torch.empty(N, dtype=torch.float32, device=dev)}
+    if want_logP:
+        out["logP"] = torch.empty((M + 1, N + 1), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib().sg_stage_match_workspace_size(M, N, D)))
+    o, keep, count = _opts(dev, threshold=threshold, workspace=workspace, m1=out["matches1"], s1=out["scores1"],
+                           logP=out.get("logP"), logP_ld=N + 1, stage_events=stage_events,
+                           timed_kernel=timed_kernel, kernel_events=kernel_events)
+    _lib.check(lib().sg_stage_match(_ptr(fA), M, _ptr(fB), N, D, float(alpha), T, _ptr(out["matches0"]),
+                                    _ptr(out["scores0"]), C.byref(o)), "sg_stage_match")
+    out["n_kernel_launches"] = count.value
+    return out

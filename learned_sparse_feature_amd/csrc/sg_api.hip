@@ -1,0 +1,747 @@
+// Host side of libsg: argument validation, weight-blob layout, workspace
+// layout and the launch sequence of the matching forward pass.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "sg_internal.h"
+
+namespace {
+
+using namespace sg;
+
+thread_local std::string g_err;
+
+sg_status fail(sg_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+sg_status hip_fail(hipError_t e, const char* where) {
+  return fail(SG_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int round32(int n) { return (n + 31) & ~31; }
+
+// ------------------------------------------------------------ weight layout
+
+struct Tensor {
+  size_t off;
+  int rows, cols;
+};
+
+struct WLayout {
+  std::vector<Tensor> t;
+  size_t bytes = 0;
+  int enc_first = 0;    // index of encoder layer 0 W
+  int stage_first = 0;  // index of stage 0 W_qkv
+  int final_first = 0;  // index of W_f
+  int alpha = 0;        // index of alpha
+};
+
+constexpr int kPerStage = 8;  // W_qkv, b_qkv, W_m, b_m, W_1, b_1, W_2, b_2
+
+sg_status check_config(const sg_weights* w) {
+  if (!w) return fail(SG_ERR_INVALID_ARG, "weights is NULL");
+  if (w->D <= 0 || w->H <= 0) return fail(SG_ERR_INVALID_ARG, "D and H must be positive");
+  if (w->D % w->H) return fail(SG_ERR_INVALID_ARG, "D (%d) is not a multiple of H (%d)", w->D, w->H);
+  if (w->n_enc < 1 || w->n_enc > SG_MAX_ENC)
+    return fail(SG_ERR_INVALID_ARG, "n_enc must be in [1, %d]", SG_MAX_ENC);
+  for (int i = 0; i < w->n_enc; ++i)
+    if (w->enc[i] <= 0) return fail(SG_ERR_INVALID_ARG, "encoder width %d is not positive", i);
+  if (w->L_max < 1) return fail(SG_ERR_INVALID_ARG, "L_max must be >= 1");
+  if (w->dtype != SG_F32 && w->dtype != SG_BF16) return fail(SG_ERR_INVALID_ARG, "unknown dtype %d", w->dtype);
+  const int dh = w->D / w->H;
+  if (dh != 16 && dh != 64) return fail(SG_ERR_UNSUPPORTED, "head dimension %d (supported: 16, 64)", dh);
+  if (w->D % 32 || w->D > 1024) return fail(SG_ERR_UNSUPPORTED, "D = %d (supported: multiples of 32 up to 1024)", w->D);
+  for (int i = 0; i < w->n_enc; ++i)
+    if (w->enc[i] % 8) return fail(SG_ERR_UNSUPPORTED, "encoder width %d must be a multiple of 8", w->enc[i]);
+  return SG_OK;
+}
+
+WLayout layout_of(const sg_weights* w) {
+  WLayout L;
+  const size_t es = w->dtype == SG_BF16 ? 2 : 4;
+  size_t off = 0;
+  auto add = [&](int rows, int cols, size_t elt) {
+    L.t.push_back({off, rows, cols});
+    off = align256(off + (size_t)rows * cols * elt);
+  };
+  const int D = w->D;
+  L.enc_first = 0;
+  int prev = 3;
+  for (int i = 0; i <= w->n_enc; ++i) {
+    const int out = i < w->n_enc ? w->enc[i] : D;
+    add(out, prev, es);
+    add(1, out, es);
+    prev = out;
+  }
+  L.stage_first = (int)L.t.size();
+  for (int s = 0; s < 2 * w->L_max; ++s) {
+    add(3 * D, D, es); add(1, 3 * D, es);
+    add(D, D, es); add(1, D, es);
+    add(2 * D, 2 * D, es); add(1, 2 * D, es);
+    add(D, 2 * D, es); add(1, D, es);
+  }
+  L.final_first = (int)L.t.size();
+  add(D, D, es);
+  add(1, D, es);
+  L.alpha = (int)L.t.size();
+  add(1, 1, 4);
+  L.bytes = off;
+  return L;
+}
+
+sg_status check_weights(const sg_weights* w, WLayout* out) {
+  sg_status s = check_config(w);
+  if (s != SG_OK) return s;
+  if (!w->blob) return fail(SG_ERR_INVALID_ARG, "weights->blob is NULL");
+  WLayout L = layout_of(w);
+  if (w->blob_bytes < L.bytes)
+    return fail(SG_ERR_WEIGHTS, "weight blob has %zu bytes, the configuration needs %zu", w->blob_bytes, L.bytes);
+  *out = L;
+  return SG_OK;
+}
+
+// ---------------------------------------------------------- workspace layout
+
+struct WsLayout {
+  size_t X, H0, H1, QK, VT, MB, M2, HB, F, Z, ZT, U, V, IDX0, VAL0, IDX1, total;
+  int ldvt;
+};
+
+WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, long uf, long vf, long na,
+                       long nb) {
+  WsLayout L;
+  L.ldvt = (int)((R + 63) & ~63L);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+  L.X = take((size_t)R * D * 4);
+  L.H0 = take((size_t)R * maxw * 4);
+  L.H1 = take((size_t)R * maxw * 4);
+  L.QK = take((size_t)R * 2 * D * os);
+  L.VT = take((size_t)D * L.ldvt * os);
+  L.MB = take((size_t)R * D * os);
+  L.M2 = take((size_t)R * D * os);
+  L.HB = take((size_t)R * 2 * D * os);
+  L.F = take((size_t)R * D * 4);
+  L.Z = take((size_t)zf * 4);
+  L.ZT = take((size_t)ztf * 4);
+  L.U = take((size_t)uf * 4);
+  L.V = take((size_t)vf * 4);
+  L.IDX0 = take((size_t)na * 4);
+  L.VAL0 = take((size_t)na * 4);
+  L.IDX1 = take((size_t)nb * 4);
+  L.total = o;
+  return L;
+}
+
+WsLayout ws_layout(const sg_weights* w, long R, long zf, long ztf, long uf, long vf, long na, long nb) {
+  int maxw = 0;
+  for (int i = 0; i < w->n_enc; ++i) maxw = std::max(maxw, w->enc[i]);
+  return ws_layout_raw(w->D, w->dtype == SG_BF16 ? 2 : 4, maxw, R, zf, ztf, uf, vf, na, nb);
+}
+
+// ----------------------------------------------------------- library workspace
+
+struct OwnedWs {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+OwnedWs g_ws[64];
+
+sg_status get_workspace(const sg_opts* o, size_t need, void** ptr) {
+  if (o && o->workspace) {
+    if (o->workspace_bytes < need)
+      return fail(SG_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", o->workspace_bytes, need);
+    *ptr = o->workspace;
+    return SG_OK;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(SG_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  OwnedWs& w = g_ws[dev];
+  if (w.bytes < need) {
+    if (w.ptr) {
+      // the buffer may still be in use by enqueued work on any stream
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    e = hipMalloc(&w.ptr, need);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+    w.bytes = need;
+  }
+  *ptr = w.ptr;
+  return SG_OK;
+}
+
+// -------------------------------------------------------------- timing hooks
+
+struct Timer {
+  const sg_opts* o;
+  hipStream_t st;
+  int launches = 0;
+  void stage(int k) {
+    if (o && o->stage_events && k < o->n_stage_events) (void)hipEventRecord((hipEvent_t)o->stage_events[k], st);
+  }
+  bool bracket(int kind) const {
+    return o && o->kernel_events && o->timed_kernel == kind && 2 * (launches + 1) <= o->n_kernel_events;
+  }
+  template <class F>
+  hipError_t run(int kind, F&& f) {
+    if (bracket(kind)) {
+      (void)hipEventRecord((hipEvent_t)o->kernel_events[2 * launches], st);
+      hipError_t e = f();
+      (void)hipEventRecord((hipEvent_t)o->kernel_events[2 * launches + 1], st);
+      ++launches;
+      return e;
+    }
+    return f();
+  }
+  void finish() {
+    if (o && o->n_kernel_launches) *o->n_kernel_launches = launches;
+  }
+};
+
+// ------------------------------------------------------------- the pipeline
+
+struct Problem {
+  int B = 1, Mpad = 0, Npad = 0;
+  std::vector<int> M, N;
+  const float *kp[2] = {nullptr, nullptr}, *cf[2] = {nullptr, nullptr}, *de[2] = {nullptr, nullptr};
+  float img[4] = {0, 0, 0, 0};
+};
+
+struct Plan {
+  SegTable seg;
+  PairTable pt;
+  int R = 0;
+  long zf = 0, ztf = 0, uf = 0, vf = 0, na = 0, nb = 0;
+  std::vector<int> rowB;
+};
+
+void make_plan(const Problem& p, Plan& pl) {
+  memset(&pl.seg, 0, sizeof(pl.seg));
+  memset(&pl.pt, 0, sizeof(pl.pt));
+  pl.rowB.assign(p.B, 0);
+  int R = 0;
+  long zf = 0, ztf = 0;
+  pl.pt.n_pairs = p.B;
+  pl.seg.n_seg = 2 * p.B;
+  for (int b = 0; b < p.B; ++b) {
+    const int M = p.M[b], N = p.N[b];
+    const int sa = 2 * b, sb = 2 * b + 1;
+    pl.seg.row0[sa] = R; pl.seg.n[sa] = M; pl.seg.in_off[sa] = b * p.Mpad; pl.seg.side[sa] = 0; pl.seg.partner[sa] = sb;
+    R += round32(M);
+    pl.seg.row0[sb] = R; pl.seg.n[sb] = N; pl.seg.in_off[sb] = b * p.Npad; pl.seg.side[sb] = 1; pl.seg.partner[sb] = sa;
+    pl.rowB[b] = R;
+    R += round32(N);
+    pl.pt.M[b] = M; pl.pt.N[b] = N; pl.pt.rowA[b] = pl.seg.row0[sa];
+    pl.pt.z_off[b] = (int)zf; pl.pt.zt_off[b] = (int)ztf;
+    zf += (long)M * ld4(N);
+    ztf += (long)N * ld4(M);
+    pl.pt.upre[b + 1] = pl.pt.upre[b] + M + 1;
+    pl.pt.vpre[b + 1] = pl.pt.vpre[b] + N + 1;
+  }
+  pl.R = R;
+  pl.zf = zf; pl.ztf = ztf;
+  pl.uf = pl.pt.upre[p.B]; pl.vf = pl.pt.vpre[p.B];
+  pl.na = pl.uf - p.B; pl.nb = pl.vf - p.B;
+}
+
+template <class T>
+const T* at(const sg_weights* w, const WLayout& L, int idx) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(w->blob) + L.t[idx].off);
+}
+const void* atv(const sg_weights* w, const WLayout& L, int idx) {
+  return reinterpret_cast<const char*>(w->blob) + L.t[idx].off;
+}
+
+struct Outputs {
+  int32_t* m0 = nullptr; float* s0 = nullptr;
+  int32_t* m1 = nullptr; float* s1 = nullptr;
+  float* descA = nullptr; float* descB = nullptr;
+  float* logP = nullptr; int64_t logP_ld = 0; int64_t logP_stride = 0;
+};
+
+GemmBatch single(int rows, int n_out, int ldc, int c_off = 0) {
+  GemmBatch b;
+  memset(&b, 0, sizeof(b));
+  b.n = 1;
+  b.p[0] = GemmProblem{0, 0, rows, n_out, c_off, 0, ldc, 0};
+  return b;
+}
+
+#define HIPCHK(expr, where)                      \
+  do {                                            \
+    hipError_t e_ = (expr);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+// Encoder: layer 0 (with normalisation) then GEMM layers; the last adds into X.
+sg_status run_encoder(const Problem& p, const Plan& pl, const sg_weights* w, const WLayout& L,
+                      char* ws, const WsLayout& wl, Timer& tm, hipStream_t st) {
+  const int D = w->D;
+  float* X = reinterpret_cast<float*>(ws + wl.X);
+  float* Hs[2] = {reinterpret_cast<float*>(ws + wl.H0), reinterpret_cast<float*>(ws + wl.H1)};
+  HIPCHK(launch_encode_l0(p.kp[0], p.cf[0], p.de[0], p.kp[1], p.cf[1], p.de[1], p.img, pl.seg, pl.R,
+                          D, atv(w, L, L.enc_first), atv(w, L, L.enc_first + 1), w->enc[0], w->dtype,
+                          Hs[0], X, st),
+         "encoder layer 0");
+  int prev = w->enc[0];
+  for (int i = 1; i <= w->n_enc; ++i) {
+    const bool last = i == w->n_enc;
+    const int out = last ? D : w->enc[i];
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.A0 = Hs[(i - 1) & 1]; g.lda0 = prev; g.K0 = prev; g.K = prev;
+    g.W = atv(w, L, L.enc_first + 2 * i); g.ldw = prev;
+    g.bias = atv(w, L, L.enc_first + 2 * i + 1);
+    g.C = last ? (void*)X : (void*)Hs[i & 1];
+    GemmBatch b = single(pl.R, out, out);
+    HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(SG_F32, 1, w->dtype, 1, last ? EPI_RESID : EPI_RELU, g, b, pl.R, out, st); }),
+           "encoder GEMM");
+    prev = out;
+  }
+  return SG_OK;
+}
+
+// Stages [s0, s1) in place on X (compact rows of every image of the plan).
+sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0, int s1, char* ws,
+                  const WsLayout& wl, Timer& tm, hipStream_t st) {
+  const int D = w->D, op = w->dtype, R = pl.R;
+  float* X = reinterpret_cast<float*>(ws + wl.X);
+  void* QK = ws + wl.QK;
+  void* VT = ws + wl.VT;
+  void* MB = ws + wl.MB;
+  void* M2 = ws + wl.M2;
+  void* HB = ws + wl.HB;
+  const float log2e = 1.4426950408889634f;
+  for (int s = s0; s < s1; ++s) {
+    const int base = L.stage_first + kPerStage * s;
+    // q | k | v = x W_qkv^T + b_qkv  (v written transposed)
+    {
+      GemmArgs g;
+      memset(&g, 0, sizeof(g));
+      g.A0 = X; g.lda0 = D; g.K0 = D; g.K = D;
+      g.W = atv(w, L, base); g.ldw = D; g.bias = atv(w, L, base + 1);
+      g.C = QK; g.C2 = VT; g.split = 2 * D;
+      GemmBatch b = single(R, 3 * D, 2 * D);
+      b.p[0].ldct = wl.ldvt;
+      HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, 0, EPI_QKV, g, b, R, 3 * D, st); }), "qkv GEMM");
+    }
+    // multi-head attention: self on even stages, cross on odd stages
+    {
+      AttnArgs a;
+      a.qk = QK; a.vt = VT; a.out = MB; a.D = D; a.ldvt = wl.ldvt; a.cross = s & 1;
+      const int dh = D / w->H;
+      a.scale2 = log2e / sqrtf((float)dh);
+      HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_attention(op, dh, a, pl.seg, w->H, st); }), "attention");
+    }
+    // merge projection
+    {
+      GemmArgs g;
+      memset(&g, 0, sizeof(g));
+      g.A0 = MB; g.lda0 = D; g.K0 = D; g.K = D;
+      g.W = atv(w, L, base + 2); g.ldw = D; g.bias = atv(w, L, base + 3);
+      g.C = M2;
+      GemmBatch b = single(R, D, D);
+      HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, op == SG_F32, op, op == SG_F32, EPI_BIAS, g, b, R, D, st); }), "merge GEMM");
+    }
+    // h = ReLU(W_1 [x || m] + b_1)
+    {
+      GemmArgs g;
+      memset(&g, 0, sizeof(g));
+      g.A0 = X; g.lda0 = D; g.K0 = D; g.A1 = M2; g.lda1 = D; g.K = 2 * D;
+      g.W = atv(w, L, base + 4); g.ldw = 2 * D; g.bias = atv(w, L, base + 5);
+      g.C = HB;
+      GemmBatch b = single(R, 2 * D, 2 * D);
+      HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, op == SG_F32, EPI_RELU, g, b, R, 2 * D, st); }), "mlp1 GEMM");
+    }
+    // x += W_2 h + b_2
+    {
+      GemmArgs g;
+      memset(&g, 0, sizeof(g));
+      g.A0 = HB; g.lda0 = 2 * D; g.K0 = 2 * D; g.K = 2 * D;
+      g.W = atv(w, L, base + 6); g.ldw = 2 * D; g.bias = atv(w, L, base + 7);
+      g.C = X;
+      GemmBatch b = single(R, D, D);
+      HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, op == SG_F32, op, 1, EPI_RESID, g, b, R, D, st); }), "mlp2 GEMM");
+    }
+  }
+  return SG_OK;
+}
+
+// Final projection of every row of X into F (fp32).
+sg_status run_project(const Plan& pl, const sg_weights* w, const WLayout& L, const float* X, float* F,
+                      Timer& tm, hipStream_t st) {
+  const int D = w->D, op = w->dtype;
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.A0 = X; g.lda0 = D; g.K0 = D; g.K = D;
+  g.W = atv(w, L, L.final_first); g.ldw = D; g.bias = atv(w, L, L.final_first + 1);
+  g.C = F;
+  GemmBatch b = single(pl.R, D, D);
+  HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, 1, EPI_BIAS, g, b, pl.R, D, st); }), "final projection");
+  return SG_OK;
+}
+
+// Scores, Sinkhorn and extraction from F (rows of the plan).
+sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, const float* alpha_dev,
+                       int T, float thr,
+                       const float* F, char* ws, const WsLayout& wl, const Outputs& out, Timer& tm,
+                       hipStream_t st) {
+  const float log2e = 1.4426950408889634f;
+  float* Z = reinterpret_cast<float*>(ws + wl.Z);
+  float* ZT = reinterpret_cast<float*>(ws + wl.ZT);
+  float* U = reinterpret_cast<float*>(ws + wl.U);
+  float* V = reinterpret_cast<float*>(ws + wl.V);
+  int* idx0 = reinterpret_cast<int*>(ws + wl.IDX0);
+  float* val0 = reinterpret_cast<float*>(ws + wl.VAL0);
+  int* idx1 = reinterpret_cast<int*>(ws + wl.IDX1);
+  const float alpha2 = alpha * log2e;
+  // S * log2(e) / sqrt(D) into Z and ZT
+  {
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.A0 = F; g.lda0 = D; g.K0 = D; g.K = D;
+    g.W = F; g.ldw = D;
+    g.C = Z; g.C2 = ZT;
+    g.scale = log2e / sqrtf((float)D);
+    GemmBatch b;
+    memset(&b, 0, sizeof(b));
+    b.n = p.B;
+    int mr = 0, mn = 0;
+    for (int i = 0; i < p.B; ++i) {
+      b.p[i] = GemmProblem{pl.pt.rowA[i], pl.rowB[i], p.M[i], p.N[i], pl.pt.z_off[i], pl.pt.zt_off[i],
+                           ld4(p.N[i]), ld4(p.M[i])};
+      mr = std::max(mr, p.M[i]);
+      mn = std::max(mn, p.N[i]);
+    }
+    HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(SG_F32, 1, SG_F32, 1, EPI_SCORE, g, b, mr, mn, st); }), "score GEMM");
+  }
+  tm.stage(SG_EV_SCORES);
+  // T iterations: u = log mu - lse_j(Z + v); v = log nu - lse_i(Z + u)
+  for (int it = 0; it < T; ++it) {
+    HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(Z, pl.pt, 0, it == 0 ? nullptr : V, U, alpha2, alpha_dev, (int)pl.uf, st); }), "sinkhorn rows");
+    HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(ZT, pl.pt, 1, U, V, alpha2, alpha_dev, (int)pl.vf, st); }), "sinkhorn cols");
+  }
+  if (T == 0) {
+    HIPCHK(launch_fill_f32(U, 0.f, (int)pl.uf, st), "zero u");
+    HIPCHK(launch_fill_f32(V, 0.f, (int)pl.vf, st), "zero v");
+  }
+  tm.stage(SG_EV_SINKHORN);
+  HIPCHK(launch_argmax(Z, ZT, pl.pt, U, V, idx0, val0, idx1, (int)pl.na, (int)pl.nb, st), "argmax");
+  HIPCHK(launch_finalize(pl.pt, idx0, val0, idx1, U, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, st),
+         "finalize");
+  if (out.logP)
+    HIPCHK(launch_write_logp(Z, pl.pt, U, V, alpha2, alpha_dev, out.logP, out.logP_ld, out.logP_stride, (int)pl.uf, st),
+           "logP");
+  return SG_OK;
+}
+
+sg_status check_opts(const sg_opts* o) {
+  if (!o) return SG_OK;
+  if (o->workspace && o->workspace_bytes == 0) return fail(SG_ERR_WORKSPACE, "workspace given with 0 bytes");
+  if (o->kernel_events && o->n_kernel_events < 0) return fail(SG_ERR_INVALID_ARG, "n_kernel_events < 0");
+  return SG_OK;
+}
+
+hipStream_t stream_of(const sg_opts* o) { return o ? (hipStream_t)o->stream : (hipStream_t)0; }
+
+sg_status run_full(const Problem& p, const sg_weights* w, const WLayout& L, int Lst, int T,
+                   const Outputs& out, const sg_opts* o) {
+  Plan pl;
+  make_plan(p, pl);
+  WsLayout wl = ws_layout(w, pl.R, pl.zf, pl.ztf, pl.uf, pl.vf, pl.na, pl.nb);
+  void* wsp = nullptr;
+  sg_status s = get_workspace(o, wl.total, &wsp);
+  if (s != SG_OK) return s;
+  char* ws = reinterpret_cast<char*>(wsp);
+  hipStream_t st = stream_of(o);
+  Timer tm{o, st};
+  // alpha stays in device memory: the Sinkhorn and logP kernels read it there
+  const float* alpha_dev = at<float>(w, L, L.alpha);
+  tm.stage(SG_EV_START);
+  if ((s = run_encoder(p, pl, w, L, ws, wl, tm, st)) != SG_OK) return s;
+  tm.stage(SG_EV_ENCODED);
+  if ((s = run_gnn(pl, w, L, 0, 2 * Lst, ws, wl, tm, st)) != SG_OK) return s;
+  tm.stage(SG_EV_GNN);
+  float* F = reinterpret_cast<float*>(ws + wl.F);
+  if ((s = run_project(pl, w, L, reinterpret_cast<float*>(ws + wl.X), F, tm, st)) != SG_OK) return s;
+  for (int b = 0; b < p.B; ++b) {
+    if (out.descA && p.M[b])
+      HIPCHK(hipMemcpyAsync(out.descA + (size_t)b * p.Mpad * w->D, F + (size_t)pl.seg.row0[2 * b] * w->D,
+                            (size_t)p.M[b] * w->D * 4, hipMemcpyDeviceToDevice, st), "copy f_A");
+    if (out.descB && p.N[b])
+      HIPCHK(hipMemcpyAsync(out.descB + (size_t)b * p.Npad * w->D, F + (size_t)pl.seg.row0[2 * b + 1] * w->D,
+                            (size_t)p.N[b] * w->D * 4, hipMemcpyDeviceToDevice, st), "copy f_B");
+  }
+  const float thr = o ? o->match_threshold : 0.f;
+  if ((s = run_matching(p, pl, w->D, 0.f, alpha_dev, T, thr, F, ws, wl, out, tm, st)) != SG_OK) return s;
+  tm.stage(SG_EV_END);
+  tm.finish();
+  return SG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sg_last_error(void) { return g_err.c_str(); }
+const char* sg_version(void) { return "sg-mi355x 0.1 (gfx950)"; }
+
+int32_t sg_weights_count(const sg_weights* w) {
+  if (check_config(w) != SG_OK) return -1;
+  return (int32_t)layout_of(w).t.size();
+}
+
+sg_status sg_weights_tensor(const sg_weights* w, int32_t index, size_t* offset, int32_t* rows, int32_t* cols) {
+  sg_status s = check_config(w);
+  if (s != SG_OK) return s;
+  WLayout L = layout_of(w);
+  if (index < 0 || index >= (int32_t)L.t.size()) return fail(SG_ERR_INVALID_ARG, "tensor index %d out of range", index);
+  if (offset) *offset = L.t[index].off;
+  if (rows) *rows = L.t[index].rows;
+  if (cols) *cols = L.t[index].cols;
+  return SG_OK;
+}
+
+size_t sg_weights_bytes(const sg_weights* w) {
+  if (check_config(w) != SG_OK) return 0;
+  return layout_of(w).bytes;
+}
+
+size_t sg_workspace_size(const sg_weights* w, int32_t Mmax, int32_t Nmax, int32_t batch) {
+  if (check_config(w) != SG_OK || Mmax < 0 || Nmax < 0 || batch < 1) return 0;
+  const long B = batch;
+  const long R = B * (round32(Mmax) + round32(Nmax));
+  WsLayout wl = ws_layout(w, R, B * Mmax * ld4(Nmax), B * Nmax * ld4(Mmax), B * (Mmax + 1), B * (Nmax + 1),
+                          B * Mmax, B * Nmax);
+  return wl.total;
+}
+
+size_t sg_stage_match_workspace_size(int32_t M, int32_t N, int32_t D) {
+  if (M < 0 || N < 0 || D <= 0) return 0;
+  const long R = round32(M) + round32(N);
+  return ws_layout_raw(D, 4, 0, R, (long)M * ld4(N), (long)N * ld4(M), M + 1, N + 1, M, N).total;
+}
+
+sg_status sg_match(const float* kptsA, const float* descA, const float* confA, int32_t M,
+                   const float* kptsB, const float* descB, const float* confB, int32_t N,
+                   const sg_weights* weights, int32_t L, int32_t T, int32_t* out_matches,
+                   float* out_scores, const sg_opts* opts) {
+  g_err.clear();
+  WLayout WL;
+  sg_status s = check_weights(weights, &WL);
+  if (s != SG_OK) return s;
+  if ((s = check_opts(opts)) != SG_OK) return s;
+  if (M < 0 || N < 0) return fail(SG_ERR_INVALID_ARG, "negative point count");
+  if (M > 4096 || N > 4096) return fail(SG_ERR_UNSUPPORTED, "more than 4096 points per image");
+  if (L < 1 || L > weights->L_max) return fail(SG_ERR_INVALID_ARG, "L = %d outside [1, %d]", L, weights->L_max);
+  if (T < 0) return fail(SG_ERR_INVALID_ARG, "T < 0");
+  if ((M > 0 && !out_matches) || (M > 0 && !out_scores)) return fail(SG_ERR_INVALID_ARG, "out_matches/out_scores is NULL");
+  if (M > 0 && N > 0 && (!kptsA || !descA || !confA || !kptsB || !descB || !confB))
+    return fail(SG_ERR_INVALID_ARG, "input pointer is NULL");
+  if (opts && opts->out_logP && opts->logP_ld < N + 1) return fail(SG_ERR_INVALID_ARG, "logP_ld < N+1");
+  hipStream_t st = stream_of(opts);
+  if (M == 0 || N == 0) {
+    HIPCHK(launch_fill_empty(out_matches, out_scores, M, st), "empty output");
+    if (opts && opts->out_matches1) HIPCHK(launch_fill_empty(opts->out_matches1, opts->out_scores1, N, st), "empty output");
+    return SG_OK;
+  }
+  Problem p;
+  p.B = 1; p.Mpad = M; p.Npad = N;
+  p.M = {M}; p.N = {N};
+  p.kp[0] = kptsA; p.cf[0] = confA; p.de[0] = descA;
+  p.kp[1] = kptsB; p.cf[1] = confB; p.de[1] = descB;
+  if (opts) memcpy(p.img, opts->image_size, sizeof(p.img));
+  Outputs out;
+  out.m0 = out_matches; out.s0 = out_scores;
+  if (opts) {
+    out.m1 = opts->out_matches1; out.s1 = opts->out_scores1;
+    out.descA = opts->out_desc_A; out.descB = opts->out_desc_B;
+    out.logP = opts->out_logP; out.logP_ld = opts->logP_ld; out.logP_stride = 0;
+  }
+  return run_full(p, weights, WL, L, T, out, opts);
+}
+
+sg_status sg_match_batch(int32_t B, int32_t Mpad, int32_t Npad, const int32_t* M, const int32_t* N,
+                         const float* kptsA, const float* descA, const float* confA,
+                         const float* kptsB, const float* descB, const float* confB,
+                         const sg_weights* weights, int32_t L, int32_t T, int32_t* out_matches,
+                         float* out_scores, const sg_opts* opts) {
+  g_err.clear();
+  WLayout WL;
+  sg_status s = check_weights(weights, &WL);
+  if (s != SG_OK) return s;
+  if ((s = check_opts(opts)) != SG_OK) return s;
+  if (B < 1 || B > SG_MAX_BATCH) return fail(SG_ERR_INVALID_ARG, "B = %d outside [1, %d]", B, SG_MAX_BATCH);
+  if (!M || !N) return fail(SG_ERR_INVALID_ARG, "M/N host arrays are NULL");
+  if (Mpad < 0 || Npad < 0 || Mpad > 4096 || Npad > 4096) return fail(SG_ERR_UNSUPPORTED, "Mpad/Npad outside [0, 4096]");
+  for (int b = 0; b < B; ++b)
+    if (M[b] < 0 || M[b] > Mpad || N[b] < 0 || N[b] > Npad)
+      return fail(SG_ERR_INVALID_ARG, "pair %d: counts (%d, %d) outside [0, pad]", b, M[b], N[b]);
+  if (L < 1 || L > weights->L_max) return fail(SG_ERR_INVALID_ARG, "L = %d outside [1, %d]", L, weights->L_max);
+  if (T < 0) return fail(SG_ERR_INVALID_ARG, "T < 0");
+  if (!out_matches || !out_scores) return fail(SG_ERR_INVALID_ARG, "out_matches/out_scores is NULL");
+  if (!kptsA || !descA || !confA || !kptsB || !descB || !confB) return fail(SG_ERR_INVALID_ARG, "input pointer is NULL");
+  if (opts && opts->out_logP && opts->logP_ld < Npad + 1) return fail(SG_ERR_INVALID_ARG, "logP_ld < Npad+1");
+  Problem p;
+  p.B = B; p.Mpad = Mpad; p.Npad = Npad;
+  p.M.assign(M, M + B); p.N.assign(N, N + B);
+  p.kp[0] = kptsA; p.cf[0] = confA; p.de[0] = descA;
+  p.kp[1] = kptsB; p.cf[1] = confB; p.de[1] = descB;
+  if (opts) memcpy(p.img, opts->image_size, sizeof(p.img));
+  Outputs out;
+  out.m0 = out_matches; out.s0 = out_scores;
+  if (opts) {
+    out.m1 = opts->out_matches1; out.s1 = opts->out_scores1;
+    out.descA = opts->out_desc_A; out.descB = opts->out_desc_B;
+    out.logP = opts->out_logP; out.logP_ld = opts->logP_ld; out.logP_stride = (int64_t)(Mpad + 1) * opts->logP_ld;
+  }
+  return run_full(p, weights, WL, L, T, out, opts);
+}
+
+sg_status sg_stage_encode(const float* kpts, const float* conf, const float* desc, int32_t n, float image_w,
+                          float image_h, const sg_weights* weights, float* x_out, const sg_opts* opts) {
+  g_err.clear();
+  WLayout WL;
+  sg_status s = check_weights(weights, &WL);
+  if (s != SG_OK) return s;
+  if ((s = check_opts(opts)) != SG_OK) return s;
+  if (n < 0 || n > 4096) return fail(SG_ERR_INVALID_ARG, "n = %d outside [0, 4096]", n);
+  if (n == 0) return SG_OK;
+  if (!kpts || !conf || !desc || !x_out) return fail(SG_ERR_INVALID_ARG, "NULL pointer");
+  Problem p;
+  p.B = 1; p.Mpad = n; p.Npad = 0; p.M = {n}; p.N = {0};
+  p.kp[0] = kpts; p.cf[0] = conf; p.de[0] = desc;
+  p.kp[1] = kpts; p.cf[1] = conf; p.de[1] = desc;
+  p.img[0] = image_w; p.img[1] = image_h;
+  Plan pl;
+  make_plan(p, pl);
+  WsLayout wl = ws_layout(weights, pl.R, 0, 0, 0, 0, 0, 0);
+  void* wsp;
+  if ((s = get_workspace(opts, wl.total, &wsp)) != SG_OK) return s;
+  hipStream_t st = stream_of(opts);
+  Timer tm{opts, st};
+  if ((s = run_encoder(p, pl, weights, WL, reinterpret_cast<char*>(wsp), wl, tm, st)) != SG_OK) return s;
+  HIPCHK(hipMemcpyAsync(x_out, reinterpret_cast<char*>(wsp) + wl.X, (size_t)n * weights->D * 4,
+                        hipMemcpyDeviceToDevice, st), "copy x");
+  tm.finish();
+  return SG_OK;
+}
+
+sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weights* weights, int32_t s0,
+                       int32_t s1, const sg_opts* opts) {
+  g_err.clear();
+  WLayout WL;
+  sg_status s = check_weights(weights, &WL);
+  if (s != SG_OK) return s;
+  if ((s = check_opts(opts)) != SG_OK) return s;
+  if (M < 0 || N < 0 || M > 4096 || N > 4096) return fail(SG_ERR_INVALID_ARG, "counts outside [0, 4096]");
+  if (s0 < 0 || s1 < s0 || s1 > 2 * weights->L_max) return fail(SG_ERR_INVALID_ARG, "stage range [%d, %d) invalid", s0, s1);
+  if ((M && !xA) || (N && !xB)) return fail(SG_ERR_INVALID_ARG, "NULL state pointer");
+  Problem p;
+  p.B = 1; p.Mpad = M; p.Npad = N; p.M = {M}; p.N = {N};
+  Plan pl;
+  make_plan(p, pl);
+  WsLayout wl = ws_layout(weights, pl.R, 0, 0, 0, 0, 0, 0);
+  void* wsp;
+  if ((s = get_workspace(opts, wl.total, &wsp)) != SG_OK) return s;
+  char* ws = reinterpret_cast<char*>(wsp);
+  hipStream_t st = stream_of(opts);
+  const size_t rb = (size_t)weights->D * 4;
+  float* X = reinterpret_cast<float*>(ws + wl.X);
+  if (M) HIPCHK(hipMemcpyAsync(X, xA, M * rb, hipMemcpyDeviceToDevice, st), "copy xA");
+  if (N) HIPCHK(hipMemcpyAsync(X + (size_t)pl.seg.row0[1] * weights->D, xB, N * rb, hipMemcpyDeviceToDevice, st), "copy xB");
+  Timer tm{opts, st};
+  if ((s = run_gnn(pl, weights, WL, s0, s1, ws, wl, tm, st)) != SG_OK) return s;
+  if (M) HIPCHK(hipMemcpyAsync(xA, X, M * rb, hipMemcpyDeviceToDevice, st), "copy xA back");
+  if (N) HIPCHK(hipMemcpyAsync(xB, X + (size_t)pl.seg.row0[1] * weights->D, N * rb, hipMemcpyDeviceToDevice, st), "copy xB back");
+  tm.finish();
+  return SG_OK;
+}
+
+sg_status sg_stage_project(const float* x, int32_t n, const sg_weights* weights, float* f_out, const sg_opts* opts) {
+  g_err.clear();
+  WLayout WL;
+  sg_status s = check_weights(weights, &WL);
+  if (s != SG_OK) return s;
+  if ((s = check_opts(opts)) != SG_OK) return s;
+  if (n < 0) return fail(SG_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return SG_OK;
+  if (!x || !f_out) return fail(SG_ERR_INVALID_ARG, "NULL pointer");
+  Plan pl;
+  pl.R = n;
+  hipStream_t st = stream_of(opts);
+  Timer tm{opts, st};
+  if ((s = run_project(pl, weights, WL, x, f_out, tm, st)) != SG_OK) return s;
+  tm.finish();
+  return SG_OK;
+}
+
+sg_status sg_stage_match(const float* fA, int32_t M, const float* fB, int32_t N, int32_t D, float alpha, int32_t T,
+                         int32_t* out_matches, float* out_scores, const sg_opts* opts) {
+  g_err.clear();
+  sg_status s;
+  if ((s = check_opts(opts)) != SG_OK) return s;
+  if (M < 0 || N < 0) return fail(SG_ERR_INVALID_ARG, "negative point count");
+  if (M > 4096 || N > 4096) return fail(SG_ERR_UNSUPPORTED, "more than 4096 points per image");
+  if (D <= 0 || D % 8) return fail(SG_ERR_UNSUPPORTED, "D = %d (must be a positive multiple of 8)", D);
+  if (T < 0) return fail(SG_ERR_INVALID_ARG, "T < 0");
+  if (M > 0 && (!out_matches || !out_scores)) return fail(SG_ERR_INVALID_ARG, "NULL output");
+  if (M > 0 && N > 0 && (!fA || !fB)) return fail(SG_ERR_INVALID_ARG, "NULL descriptors");
+  if (opts && opts->out_logP && opts->logP_ld < N + 1) return fail(SG_ERR_INVALID_ARG, "logP_ld < N+1");
+  hipStream_t st = stream_of(opts);
+  if (M == 0 || N == 0) {
+    HIPCHK(launch_fill_empty(out_matches, out_scores, M, st), "empty output");
+    if (opts && opts->out_matches1) HIPCHK(launch_fill_empty(opts->out_matches1, opts->out_scores1, N, st), "empty output");
+    return SG_OK;
+  }
+  Problem p;
+  p.B = 1; p.Mpad = M; p.Npad = N; p.M = {M}; p.N = {N};
+  Plan pl;
+  make_plan(p, pl);
+  // f_A and f_B are staged into the compact F rows of the workspace
+  WsLayout wl = ws_layout_raw(D, 4, 0, pl.R, pl.zf, pl.ztf, pl.uf, pl.vf, pl.na, pl.nb);
+  void* wsp;
+  if ((s = get_workspace(opts, wl.total, &wsp)) != SG_OK) return s;
+  char* ws = reinterpret_cast<char*>(wsp);
+  float* F = reinterpret_cast<float*>(ws + wl.F);
+  HIPCHK(hipMemcpyAsync(F, fA, (size_t)M * D * 4, hipMemcpyDeviceToDevice, st), "copy fA");
+  HIPCHK(hipMemcpyAsync(F + (size_t)pl.seg.row0[1] * D, fB, (size_t)N * D * 4, hipMemcpyDeviceToDevice, st), "copy fB");
+  Outputs out;
+  out.m0 = out_matches; out.s0 = out_scores;
+  if (opts) {
+    out.m1 = opts->out_matches1; out.s1 = opts->out_scores1;
+    out.logP = opts->out_logP; out.logP_ld = opts->logP_ld;
+  }
+  Timer tm{opts, st};
+  tm.stage(SG_EV_GNN);
+  if ((s = run_matching(p, pl, D, alpha, nullptr, T, opts ? opts->match_threshold : 0.f, F, ws, wl, out, tm, st)) != SG_OK)
+    return s;
+  tm.stage(SG_EV_END);
+  tm.finish();
+  return SG_OK;
+}
+
+}  // extern "C"

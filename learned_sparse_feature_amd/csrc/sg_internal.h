@@ -1,0 +1,105 @@
+// Internal declarations shared by the HIP kernels and the host side of libsg.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sg.h"
+
+namespace sg {
+
+constexpr int kMaxSeg = 2 * SG_MAX_BATCH;  // one segment per image
+
+// Images of the call in the compact row space (rows of every image stacked,
+// A then B for each pair).  Passed by value as a kernel argument.
+struct SegTable {
+  int n_seg;
+  int row0[kMaxSeg];     // first compact row of the image
+  int n[kMaxSeg];        // points of the image
+  int in_off[kMaxSeg];   // first point of the image in the caller's (padded) inputs
+  int side[kMaxSeg];     // 0: image A inputs, 1: image B inputs
+  int partner[kMaxSeg];  // segment of the other image of the pair
+};
+
+// Pairs of the call, for the score matrix, Sinkhorn and extraction.
+// Z holds S*log2(e) of the real block only ([M][ldz], ldz = N rounded up to
+// 4); ZT its transpose ([N][ldzt], ldzt = M rounded up to 4).  The dustbin
+// row, column and corner are the constant alpha and are never stored.
+// u (M+1 entries per pair) and v (N+1) are base-2 dual variables, stored
+// flattened over the pairs at upre[b] and vpre[b].
+struct PairTable {
+  int n_pairs;
+  int M[SG_MAX_BATCH], N[SG_MAX_BATCH];
+  int rowA[SG_MAX_BATCH];                         // compact row of f_A (f_B follows at +M)
+  int z_off[SG_MAX_BATCH], zt_off[SG_MAX_BATCH];  // float offsets of Z and ZT
+  int upre[SG_MAX_BATCH + 1];                     // prefix sums of (M+1)
+  int vpre[SG_MAX_BATCH + 1];                     // prefix sums of (N+1)
+};
+
+__host__ __device__ inline int ld4(int n) { return (n + 3) & ~3; }
+
+// One GEMM problem: rows of A starting at a_row0 times rows of W starting at
+// w_row0 (the score matrix uses f_B as "W").
+struct GemmProblem {
+  int a_row0, w_row0, rows, n_out, c_off, ct_off, ldc, ldct;
+};
+struct GemmBatch {
+  int n;
+  GemmProblem p[SG_MAX_BATCH];
+};
+
+enum Epilogue {
+  EPI_BIAS = 0,   // C = A W^T + b
+  EPI_RELU = 1,   // C = max(A W^T + b, 0)
+  EPI_RESID = 2,  // C (fp32) = C + A W^T + b   (in place residual add)
+  EPI_QKV = 3,    // columns < split: QK = A W^T + b; others: VT (transposed)
+  EPI_SCORE = 4   // C = scale * A W^T and CT = its transpose (fp32)
+};
+
+struct GemmArgs {
+  const void* A0; int lda0; int K0;  // columns [0, K0) of A
+  const void* A1; int lda1;          // columns [K0, K) of A (operand type)
+  const void* W; int ldw;            // weights [n_out][K]
+  const void* bias;                  // [n_out] or null
+  int K;
+  void* C; void* C2;                 // outputs (C2: VT or ZT)
+  float scale;
+  int split;                         // EPI_QKV: first column that goes to VT
+};
+
+struct AttnArgs {
+  const void* qk;    // [R][2D]: q at columns h*dh.., k at D + h*dh..
+  const void* vt;    // [D][ldvt]: v transposed
+  void* out;         // [R][D] message (heads concatenated)
+  int D, ldvt, cross;
+  float scale2;      // log2(e) / sqrt(dh)
+};
+
+// Host-side launchers (sg_kernels.hip).
+hipError_t launch_encode_l0(const float* kptsA, const float* confA, const float* descA,
+                            const float* kptsB, const float* confB, const float* descB,
+                            const float img[4], const SegTable& seg, int R, int D,
+                            const void* W0, const void* b0, int w0, int dtype, float* H0,
+                            float* X, hipStream_t st);
+hipError_t launch_gemm(int op_dtype, int a0_is_f32, int w_dtype, int out_is_f32, int epi,
+                       const GemmArgs& g, const GemmBatch& b, int max_rows, int max_n,
+                       hipStream_t st);
+hipError_t launch_attention(int op_dtype, int dh, const AttnArgs& a, const SegTable& seg,
+                            int heads, hipStream_t st);
+// alpha_dev (device pointer to the dustbin score) overrides alpha2 when non-null.
+hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const float* w_in,
+                      float* w_out, float alpha2, const float* alpha_dev, int total_rows,
+                      hipStream_t st);
+hipError_t launch_argmax(const float* Z, const float* ZT, const PairTable& pt, const float* u,
+                         const float* v, int* idx0, float* val0, int* idx1, int rowsA, int rowsB,
+                         hipStream_t st);
+hipError_t launch_finalize(const PairTable& pt, const int* idx0, const float* val0,
+                           const int* idx1, const float* u, int Mpad, int Npad, float thr,
+                           int32_t* m0, float* s0, int32_t* m1, float* s1, hipStream_t st);
+hipError_t launch_write_logp(const float* Z, const PairTable& pt, const float* u, const float* v,
+                             float alpha2, const float* alpha_dev, float* logP, int64_t ld,
+                             int64_t pair_stride, int total_rows, hipStream_t st);
+hipError_t launch_fill_f32(float* p, float v, int n, hipStream_t st);
+hipError_t launch_fill_empty(int32_t* m, float* s, int n, hipStream_t st);
+
+}  // namespace sg

@@ -113,14 +113,15 @@ def attentional_propagation(x, src, st, heads):
     return h @ _f64(st["W2"]).T + _f64(st["b2"])
 
 
-def attentional_gnn(xA, xB, stages, heads):
+def attentional_gnn(xA, xB, stages, heads, first_stage=0):
     """[realcat] section "多层GNN" (AttentionalGNN) and [GNN-blog] section
     "多轮消息怎样回到同一幅图": stages alternate self (sources = own image)
     and cross (sources = the other image), self first; each stage has its own
     weights, shared by both images, and both deltas are computed from the
-    states before the stage, then added."""
+    states before the stage, then added.  `stages` may be a slice of the
+    network starting at stage index `first_stage` (even = self)."""
     xA, xB = _f64(xA).copy(), _f64(xB).copy()
-    for s, st in enumerate(stages):
+    for s, st in enumerate(stages, start=first_stage):
         if s % 2 == 0:          # self
             srcA, srcB = xA, xB
         else:                   # cross

@@ -241,9 +241,10 @@ def random_states(n: int, D: int, seed: int, scale: float = 1.0) -> np.ndarray:
     return np.ascontiguousarray(scale * rng.standard_normal((n, D)), dtype=np.float32)
 
 
-def random_matching_descriptors(M: int, N: int, D: int, seed: int, scale: float = 6.0,
+def random_matching_descriptors(M: int, N: int, D: int, seed: int, scale: float = 3.0,
                                 planted_frac: float = 0.4, noise: float = 0.3) -> tuple:
-    """Matching descriptors for score/Sinkhorn/extraction tests.
+    """Matching descriptors for score/Sinkhorn/extraction tests (scale 3 gives |S| up to
+    about 150 at D = 256, the range the full network produces).
 
     f_A ~ N(0, scale^2 I); a fraction of f_B's rows are noisy copies of f_A rows
     (so the score matrix has clear matches, as a trained network would give),

@@ -1,0 +1,192 @@
+"""Per-stage parity of the HIP library against the float64 oracle (GPU).
+
+Every call goes through the C ABI (libsg.so via the ctypes binding).
+Inputs come from the seeded generator; expected values from the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import check_matches, dev, host, rel_rows
+
+pytestmark = pytest.mark.gpu
+
+sg = pytest.importorskip("learned_sparse_feature_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    sg.lib()  # fails loudly when libsg.so is missing
+
+
+def _weights(cid, bias_on=False, L=None):
+    return synth.make_weights(synth.CONFIGS[cid], bias_on=bias_on, L=L)
+
+
+# ------------------------------------------------------- worked example
+
+def _example_network(dtype):
+    """D=64, H=4, L=1: stage 0 does nothing; stage 1 (cross) passes the
+    message of head 0 through (merge = I, MLP selects m), with q, k, v set
+    so that the single point of A sees scores [2, 1, 0] and values
+    [1,0], [0,1], [0,0] from the three points of B."""
+    D = 64
+    Z, I = np.zeros((D, D), np.float32), np.eye(D, dtype=np.float32)
+    zero = {"Wq": Z, "bq": np.zeros(D, np.float32), "Wk": Z, "bk": np.zeros(D, np.float32), "Wv": Z,
+            "bv": np.zeros(D, np.float32), "Wm": Z, "bm": np.zeros(D, np.float32),
+            "W1": np.zeros((2 * D, 2 * D), np.float32), "b1": np.zeros(2 * D, np.float32),
+            "W2": np.zeros((D, 2 * D), np.float32), "b2": np.zeros(D, np.float32)}
+    Wk = Z.copy(); Wk[0, 0] = 1.0
+    Wv = Z.copy(); Wv[0, 0], Wv[0, 1], Wv[1, 1] = 0.5, -0.5, 1.0
+    cross = dict(zero, Wq=I, Wk=Wk, Wv=Wv, Wm=I, W1=np.block([[Z, I], [Z, Z]]).astype(np.float32),
+                 W2=np.block([I, Z]).astype(np.float32))
+    cfg = synth.CONFIGS[0]
+    w = synth.make_weights(cfg, L=1)
+    w["stages"] = [zero, cross]
+    w["dtype"] = dtype
+    return w
+
+
+@pytest.mark.parametrize("dtype,tol", [("f32", 5e-4), ("bf16", 4e-3)])
+def test_attention_worked_example(dtype, tol):
+    """Page example: scores [2,1,0] -> message ~[0.665, 0.245] (three decimals
+    printed; bf16 probabilities carry about 3 significant digits)."""
+    w = _example_network(dtype)
+    W = sg.pack_weights(w)
+    xA = np.zeros((1, 64), np.float32)
+    xA[0, 0] = 4.0                      # q = x, so q.k_j / sqrt(16) = k_j[0]
+    xB = np.zeros((3, 64), np.float32)
+    xB[0, 0], xB[1, 0], xB[1, 1] = 2.0, 1.0, 1.0
+    a, b = dev(xA), dev(xB)
+    sg.sg_stage_gnn(a, b, W, 0, 2)
+    m = host(a)[0] - xA[0]
+    np.testing.assert_allclose(m[:2], [0.665, 0.245], atol=tol)
+    np.testing.assert_allclose(m[2:], 0.0, atol=1e-6)
+    # and the oracle agrees to float precision
+    A, _ = oracle.attentional_gnn(xA, xB, w["stages"], 4)
+    np.testing.assert_allclose(m[:2], (A[0] - xA[0])[:2], atol=tol)
+
+
+# ---------------------------------------------------------------- encoder
+
+@pytest.mark.parametrize("cid,n,bias_on", [(0, 10, True), (1, 512, False), (1, 77, True), (2, 1024, True)])
+def test_encoder_parity(cid, n, bias_on):
+    cfg = synth.CONFIGS[cid]
+    w = _weights(cid, bias_on, L=1)
+    W = sg.pack_weights(w)
+    pair = synth.make_pair(cfg, M=n, N=4)
+    x = host(sg.sg_stage_encode(dev(pair["kpts0"]), dev(pair["conf0"]), dev(pair["desc0"]), W,
+                                image_size=pair["image_size0"]))
+    kn = oracle.normalize_keypoints(pair["kpts0"], *pair["image_size0"])
+    want = pair["desc0"].astype(np.float64) + oracle.keypoint_encoder(kn, pair["conf0"], w["enc"])
+    assert rel_rows(x, want).max() < 1e-5
+
+
+# -------------------------------------------------------------- GNN stages
+
+# fp32: every stage is a few fp32 contractions of length <= 2D, so the
+# per-row relative error stays near 1e-6; bf16 operands carry 2^-9 relative
+# rounding, so one stage moves a state by about 1e-3 of its update.
+@pytest.mark.parametrize("cid,M,N,stages,tol", [
+    (0, 10, 12, (0, 4), 1e-5),
+    (1, 512, 512, (0, 2), 1e-5),
+    (1, 100, 77, (1, 3), 1e-5),
+    (3, 2048, 1536, (0, 2), 1e-5),
+    (2, 1024, 1024, (0, 2), 5e-3),
+    (2, 300, 45, (3, 5), 5e-3),
+])
+def test_gnn_stage_parity(cid, M, N, stages, tol):
+    cfg = synth.CONFIGS[cid]
+    w = _weights(cid, bias_on=True)
+    W = sg.pack_weights(w)
+    xA = synth.random_states(M, cfg.D, seed=10 + cid)
+    xB = synth.random_states(N, cfg.D, seed=20 + cid)
+    a, b = dev(xA), dev(xB)
+    sg.sg_stage_gnn(a, b, W, *stages)
+    A, B = oracle.attentional_gnn(xA, xB, w["stages"][stages[0]:stages[1]], cfg.H, first_stage=stages[0])
+    ea, eb = rel_rows(host(a), A), rel_rows(host(b), B)
+    print(f"cfg{cid} {M}x{N} stages {stages}: max rel err A {ea.max():.2e} B {eb.max():.2e}")
+    assert ea.max() < tol and eb.max() < tol
+
+
+@pytest.mark.parametrize("cid,n", [(1, 512), (2, 1000), (0, 12)])
+def test_final_projection_parity(cid, n):
+    cfg = synth.CONFIGS[cid]
+    w = _weights(cid, bias_on=True, L=1)
+    W = sg.pack_weights(w)
+    x = synth.random_states(n, cfg.D, seed=5)
+    f = host(sg.sg_stage_project(dev(x), W))
+    want = oracle.final_projection(x, w["Wf"], w["bf"])
+    tol = 1e-5 if cfg.dtype == "f32" else 1e-2
+    assert rel_rows(f, want).max() < tol
+
+
+# --------------------------------------------- scores + Sinkhorn + extraction
+
+@pytest.mark.parametrize("M,N,D,T,alpha", [
+    (10, 12, 64, 20, 1.0),
+    (33, 65, 256, 100, 1.0),
+    (512, 512, 256, 100, 1.0),
+    (1024, 1024, 256, 100, 1.0),
+    (2048, 1536, 256, 100, 1.0),
+    (1, 1, 64, 5, 0.5),
+    (700, 3, 64, 50, -1.0),
+    (0, 5, 64, 10, 1.0),
+])
+def test_match_stage_parity(M, N, D, T, alpha):
+    fA, fB = synth.random_matching_descriptors(M, N, D, seed=M * 7 + N)
+    out = sg.sg_stage_match(dev(fA), dev(fB), alpha, T)
+    torch.cuda.synchronize()
+    if M == 0 or N == 0:
+        assert (host(out["matches1"]) == -1).all() and (host(out["scores1"]) == 0).all()
+        return
+    r = oracle.match_from_descriptors(fA, fB, alpha, T)
+    err = np.abs(host(out["logP"]) - r["logP"]).max()
+    ex = check_matches(host(out["matches0"]), host(out["matches1"]), r["logP"], r["matches0"], r["matches1"])
+    print(f"{M}x{N} T={T}: max |dlogP| {err:.2e}, |logP| max {np.abs(r['logP']).max():.1f}, "
+          f"matches {int((r['matches0'] >= 0).sum())}, near-tie exemptions {ex}")
+    assert err < 1e-3
+    ok = host(out["matches0"]) == r["matches0"]
+    np.testing.assert_allclose(host(out["scores0"])[ok], r["scores0"][ok], rtol=2e-3, atol=1e-6)
+
+
+def test_match_stage_threshold():
+    fA, fB = synth.random_matching_descriptors(300, 280, 256, seed=3, scale=2.0)
+    thr = 0.2
+    out = sg.sg_stage_match(dev(fA), dev(fB), 1.0, 100, threshold=thr)
+    r = oracle.match_from_descriptors(fA, fB, 1.0, 100, threshold=thr)
+    check_matches(host(out["matches0"]), host(out["matches1"]), r["logP"], r["matches0"], r["matches1"],
+                  threshold=thr)
+    assert (host(out["matches0"]) >= 0).sum() > 0
+
+
+def test_match_stage_column_sums_are_marginals():
+    """After any T the column sums of exp(logP) are b = [1_N, M]."""
+    M, N = 2048, 1536
+    fA, fB = synth.random_matching_descriptors(M, N, 256, seed=11)
+    out = sg.sg_stage_match(dev(fA), dev(fB), 1.0, 100)
+    P = np.exp(host(out["logP"]).astype(np.float64))
+    b = np.concatenate([np.ones(N), [M]])
+    np.testing.assert_allclose(P.sum(axis=0), b, rtol=2e-3)
+
+
+def test_match_stage_max_size():
+    """4096 x 4096 points (the library's limit), T = 20: sampled rows of logP."""
+    M = N = 4096
+    fA, fB = synth.random_matching_descriptors(M, N, 64, seed=17, scale=3.0)
+    out = sg.sg_stage_match(dev(fA), dev(fB), 1.0, 20)
+    r = oracle.match_from_descriptors(fA, fB, 1.0, 20)
+    g = host(out["logP"])
+    rows = np.random.Generator(np.random.PCG64(0)).choice(M + 1, 64, replace=False)
+    assert np.abs(g[rows] - r["logP"][rows]).max() < 1e-3
+    check_matches(host(out["matches0"]), host(out["matches1"]), r["logP"], r["matches0"], r["matches1"])
+
+
+def test_match_stage_deterministic():
+    fA, fB = synth.random_matching_descriptors(600, 500, 256, seed=23)
+    a = sg.sg_stage_match(dev(fA), dev(fB), 1.0, 100)
+    b = sg.sg_stage_match(dev(fA), dev(fB), 1.0, 100)
+    assert torch.equal(a["logP"], b["logP"]) and torch.equal(a["matches0"], b["matches0"])

@@ -398,3 +398,12 @@ def test_extraction_threshold_is_exact_for_tiny_probabilities():
     np.testing.assert_array_equal(m0, [-1, 1])
     m0, _, _, _ = oracle.extract_matches(logP, 0.35)
     np.testing.assert_array_equal(m0, [-1, -1])
+
+
+def test_gnn_slice_starting_at_an_odd_stage_is_cross():
+    rng = _rng(26)
+    D = 8
+    xA, xB = rng.uniform(0.1, 1, (5, D)), rng.uniform(0.1, 1, (7, D))
+    A, B = oracle.attentional_gnn(xA, xB, [_mean_stage(D)], heads=2, first_stage=1)
+    np.testing.assert_allclose(A, xA + xB.mean(0), rtol=1e-13)
+    np.testing.assert_allclose(B, xB + xA.mean(0), rtol=1e-13)
