@@ -22,6 +22,12 @@
  *    copies between host and device or synchronises.
  *  - All validation happens before the first HIP call: on any error nothing
  *    is enqueued and outputs are untouched; sg_last_error() describes it.
+ *  - Graph replay: the second call with given shapes, pointers and options
+ *    captures its launch sequence into a HIP graph (on a private stream) and
+ *    every later identical call replays it on opts->stream (the first one
+ *    enqueues its kernels directly).  Calls with
+ *    timing events or SG_FLAG_NO_GRAPH, or on a stream being captured by the
+ *    caller, enqueue their kernels directly.  Up to 64 graphs are cached.
  *  - Scratch memory: the caller may pass a workspace of at least
  *    sg_workspace_size() bytes; with none, the library keeps one grow-only
  *    buffer per device (allocated on first use, held until process exit).
@@ -120,7 +126,11 @@ typedef struct {
   sg_event_t* kernel_events;   /* optional: 2 per launch (before, after), in launch order */
   int32_t n_kernel_events;     /* capacity; launches beyond it are not bracketed */
   int32_t* n_kernel_launches;  /* host: receives the number of bracketed launches */
+  int32_t flags;               /* SG_FLAG_* */
 } sg_opts;
+
+/* sg_opts.flags: run eagerly instead of replaying the captured HIP graph. */
+#define SG_FLAG_NO_GRAPH 1
 
 /* Number of tensors in the blob (the alpha scalar counts as one). */
 int32_t sg_weights_count(const sg_weights* w);

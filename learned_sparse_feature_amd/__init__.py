@@ -146,8 +146,9 @@ def make_events(n: int):
 
 def _opts(device, *, threshold=0.0, image_size=None, workspace=None, ws_bytes=0, m1=None, s1=None,
           fA=None, fB=None, logP=None, logP_ld=0, stage_events=None, timed_kernel=SG_K_NONE,
-          kernel_events=None, stream=None):
+          kernel_events=None, stream=None, graph=True):
     o = SgOpts()
+    o.flags = 0 if graph else _lib.SG_FLAG_NO_GRAPH
     s = stream if stream is not None else torch.cuda.current_stream(device)
     o.stream = s.cuda_stream
     if workspace is not None:
@@ -182,31 +183,41 @@ def _opts(device, *, threshold=0.0, image_size=None, workspace=None, ws_bytes=0,
 def sg_match(kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int, T: int, *,
              threshold: float = 0.0, image_size=None, want_matches1=True, want_logP=False,
              want_desc=False, workspace=None, stage_events=None, timed_kernel=SG_K_NONE,
-             kernel_events=None, stream=None) -> dict:
+             kernel_events=None, stream=None, graph=True, out: Optional[dict] = None) -> dict:
     """One pair.  kpts [n][2] (pixels if image_size=(wA, hA, wB, hB) is given),
-    desc [n][D], conf [n]: float32 CUDA tensors.  Returns device tensors."""
+    desc [n][D], conf [n]: float32 CUDA tensors.  Returns device tensors;
+    `out` may supply them (same keys) so that repeated calls reuse buffers."""
     dev = descA.device
     M, N, D = kptsA.shape[0], kptsB.shape[0], weights.D
     for t, nm, shp in ((kptsA, "kptsA", (M, 2)), (descA, "descA", (M, D)), (confA, "confA", (M,)),
                        (kptsB, "kptsB", (N, 2)), (descB, "descB", (N, D)), (confB, "confB", (N,))):
         _check_tensor(t, nm, torch.float32, shp)
-    out = {"matches0": torch.empty(M, dtype=torch.int32, device=dev),
-           "scores0": torch.empty(M, dtype=torch.float32, device=dev)}
-    if want_matches1:
-        out["matches1"] = torch.empty(N, dtype=torch.int32, device=dev)
-        out["scores1"] = torch.empty(N, dtype=torch.float32, device=dev)
-    if want_logP:
-        out["logP"] = torch.empty((M + 1, N + 1), dtype=torch.float32, device=dev)
-    if want_desc:
-        out["f0"] = torch.empty((M, D), dtype=torch.float32, device=dev)
-        out["f1"] = torch.empty((N, D), dtype=torch.float32, device=dev)
+    if out is None:
+        out = {"matches0": torch.empty(M, dtype=torch.int32, device=dev),
+               "scores0": torch.empty(M, dtype=torch.float32, device=dev)}
+        if want_matches1:
+            out["matches1"] = torch.empty(N, dtype=torch.int32, device=dev)
+            out["scores1"] = torch.empty(N, dtype=torch.float32, device=dev)
+        if want_logP:
+            out["logP"] = torch.empty((M + 1, N + 1), dtype=torch.float32, device=dev)
+        if want_desc:
+            out["f0"] = torch.empty((M, D), dtype=torch.float32, device=dev)
+            out["f1"] = torch.empty((N, D), dtype=torch.float32, device=dev)
+    else:
+        out = dict(out)
+        for k, dt_, shp in (("matches0", torch.int32, (M,)), ("scores0", torch.float32, (M,)),
+                            ("matches1", torch.int32, (N,)), ("scores1", torch.float32, (N,)),
+                            ("logP", torch.float32, (M + 1, N + 1)), ("f0", torch.float32, (M, D)),
+                            ("f1", torch.float32, (N, D))):
+            if k in out:
+                _check_tensor(out[k], k, dt_, shp)
     if workspace is None:
         workspace = _workspace(dev, workspace_size(weights, M, N, 1))
     o, keep, count = _opts(dev, threshold=threshold, image_size=image_size, workspace=workspace,
                            m1=out.get("matches1"), s1=out.get("scores1"), fA=out.get("f0"),
                            fB=out.get("f1"), logP=out.get("logP"), logP_ld=N + 1,
                            stage_events=stage_events, timed_kernel=timed_kernel,
-                           kernel_events=kernel_events, stream=stream)
+                           kernel_events=kernel_events, stream=stream, graph=graph)
     st = lib().sg_match(_ptr(kptsA), _ptr(descA), _ptr(confA), M, _ptr(kptsB), _ptr(descB), _ptr(confB), N,
                         weights.ref, L, T, _ptr(out["matches0"]), _ptr(out["scores0"]), C.byref(o))
     _lib.check(st, "sg_match")
@@ -217,7 +228,7 @@ def sg_match(kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int,
 def sg_match_batch(M, N, kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int, T: int, *,
                    threshold: float = 0.0, image_size=None, want_matches1=True, want_logP=False,
                    want_desc=False, workspace=None, stage_events=None, timed_kernel=SG_K_NONE,
-                   kernel_events=None, stream=None) -> dict:
+                   kernel_events=None, stream=None, graph=True) -> dict:
     """B padded pairs: kptsA [B][Mpad][2], descA [B][Mpad][D], confA [B][Mpad] (and B
     likewise); M, N: sequences of the true counts."""
     dev = descA.device
@@ -243,7 +254,7 @@ def sg_match_batch(M, N, kptsA, descA, confA, kptsB, descB, confB, weights: Weig
                            m1=out.get("matches1"), s1=out.get("scores1"), fA=out.get("f0"),
                            fB=out.get("f1"), logP=out.get("logP"), logP_ld=Npad + 1,
                            stage_events=stage_events, timed_kernel=timed_kernel,
-                           kernel_events=kernel_events, stream=stream)
+                           kernel_events=kernel_events, stream=stream, graph=graph)
     st = lib().sg_match_batch(B, Mpad, Npad, Ma, Na, _ptr(kptsA), _ptr(descA), _ptr(confA), _ptr(kptsB),
                               _ptr(descB), _ptr(confB), weights.ref, L, T, _ptr(out["matches0"]),
                               _ptr(out["scores0"]), C.byref(o))

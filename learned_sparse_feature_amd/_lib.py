@@ -13,6 +13,7 @@ SG_MAX_ENC = 8
 SG_MAX_BATCH = 64
 SG_N_STAGE_EVENTS = 6
 SG_K_NONE, SG_K_GEMM, SG_K_ATTENTION, SG_K_SINKHORN = 0, 1, 2, 3
+SG_FLAG_NO_GRAPH = 1
 
 STATUS_NAMES = {0: "SG_OK", -1: "SG_ERR_INVALID_ARG", -2: "SG_ERR_UNSUPPORTED", -3: "SG_ERR_WEIGHTS",
                 -4: "SG_ERR_WORKSPACE", -5: "SG_ERR_HIP"}
@@ -32,7 +33,8 @@ class SgOpts(C.Structure):
                 ("out_logP", C.c_void_p), ("logP_ld", C.c_int64),
                 ("stage_events", C.c_void_p), ("n_stage_events", C.c_int32),
                 ("timed_kernel", C.c_int32), ("kernel_events", C.c_void_p),
-                ("n_kernel_events", C.c_int32), ("n_kernel_launches", C.POINTER(C.c_int32))]
+                ("n_kernel_events", C.c_int32), ("n_kernel_launches", C.POINTER(C.c_int32)),
+                ("flags", C.c_int32)]
 
 
 _P = C.c_void_p

@@ -66,8 +66,12 @@ sg_status check_config(const sg_weights* w) {
   const int dh = w->D / w->H;
   if (dh != 16 && dh != 64) return fail(SG_ERR_UNSUPPORTED, "head dimension %d (supported: 16, 64)", dh);
   if (w->D % 32 || w->D > 1024) return fail(SG_ERR_UNSUPPORTED, "D = %d (supported: multiples of 32 up to 1024)", w->D);
-  for (int i = 0; i < w->n_enc; ++i)
-    if (w->enc[i] % 8) return fail(SG_ERR_UNSUPPORTED, "encoder width %d must be a multiple of 8", w->enc[i]);
+  // the fused encoder keeps hidden layers in LDS and runs them on 32x32 MFMAs
+  for (int i = 0; i < w->n_enc; ++i) {
+    if (w->enc[i] > kMaxEncWidth || w->enc[i] % 16 || (i > 0 && w->enc[i] % 32))
+      return fail(SG_ERR_UNSUPPORTED, "encoder width %d (hidden widths: multiples of 32 up to %d; the first may be 16)",
+                  w->enc[i], kMaxEncWidth);
+  }
   return SG_OK;
 }
 
@@ -119,19 +123,22 @@ sg_status check_weights(const sg_weights* w, WLayout* out) {
 
 struct WsLayout {
   size_t X, H0, H1, QK, VT, MB, M2, HB, F, Z, ZT, U, V, IDX0, VAL0, IDX1, total;
-  int ldvt;
+  int ldvt, ldqk;
 };
 
 WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, long uf, long vf, long na,
                        long nb) {
   WsLayout L;
-  L.ldvt = (int)((R + 63) & ~63L);
+  // row strides are kept off powers of two (+64 / +16 bytes) so that the
+  // strided accesses of the attention kernel spread over the L2 channels
+  L.ldvt = (int)((R + 63) & ~63L) + 32;
+  L.ldqk = (int)(2 * D + 8);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   L.X = take((size_t)R * D * 4);
   L.H0 = take((size_t)R * maxw * 4);
   L.H1 = take((size_t)R * maxw * 4);
-  L.QK = take((size_t)R * 2 * D * os);
+  L.QK = take((size_t)R * L.ldqk * os);
   L.VT = take((size_t)D * L.ldvt * os);
   L.MB = take((size_t)R * D * os);
   L.M2 = take((size_t)R * D * os);
@@ -235,6 +242,7 @@ struct Plan {
   PairTable pt;
   int R = 0;
   long zf = 0, ztf = 0, uf = 0, vf = 0, na = 0, nb = 0;
+  int ru = 0, rv = 0;  // flattened u rows (sum of M+1) and v rows (sum of N+1)
   std::vector<int> rowB;
 };
 
@@ -242,6 +250,7 @@ void make_plan(const Problem& p, Plan& pl) {
   memset(&pl.seg, 0, sizeof(pl.seg));
   memset(&pl.pt, 0, sizeof(pl.pt));
   pl.rowB.assign(p.B, 0);
+  pl.uf = pl.vf = 0;
   int R = 0;
   long zf = 0, ztf = 0;
   pl.pt.n_pairs = p.B;
@@ -260,11 +269,15 @@ void make_plan(const Problem& p, Plan& pl) {
     ztf += (long)N * ld4(M);
     pl.pt.upre[b + 1] = pl.pt.upre[b] + M + 1;
     pl.pt.vpre[b + 1] = pl.pt.vpre[b] + N + 1;
+    pl.pt.uoff[b] = (int)pl.uf;
+    pl.pt.voff[b] = (int)pl.vf;
+    pl.uf += ld4(M + 1);
+    pl.vf += ld4(N + 1);
   }
   pl.R = R;
   pl.zf = zf; pl.ztf = ztf;
-  pl.uf = pl.pt.upre[p.B]; pl.vf = pl.pt.vpre[p.B];
-  pl.na = pl.uf - p.B; pl.nb = pl.vf - p.B;
+  pl.ru = pl.pt.upre[p.B]; pl.rv = pl.pt.vpre[p.B];
+  pl.na = pl.ru - p.B; pl.nb = pl.rv - p.B;
 }
 
 template <class T>
@@ -299,28 +312,23 @@ GemmBatch single(int rows, int n_out, int ldc, int c_off = 0) {
 // Encoder: layer 0 (with normalisation) then GEMM layers; the last adds into X.
 sg_status run_encoder(const Problem& p, const Plan& pl, const sg_weights* w, const WLayout& L,
                       char* ws, const WsLayout& wl, Timer& tm, hipStream_t st) {
-  const int D = w->D;
-  float* X = reinterpret_cast<float*>(ws + wl.X);
-  float* Hs[2] = {reinterpret_cast<float*>(ws + wl.H0), reinterpret_cast<float*>(ws + wl.H1)};
-  HIPCHK(launch_encode_l0(p.kp[0], p.cf[0], p.de[0], p.kp[1], p.cf[1], p.de[1], p.img, pl.seg, pl.R,
-                          D, atv(w, L, L.enc_first), atv(w, L, L.enc_first + 1), w->enc[0], w->dtype,
-                          Hs[0], X, st),
-         "encoder layer 0");
-  int prev = w->enc[0];
-  for (int i = 1; i <= w->n_enc; ++i) {
-    const bool last = i == w->n_enc;
-    const int out = last ? D : w->enc[i];
-    GemmArgs g;
-    memset(&g, 0, sizeof(g));
-    g.A0 = Hs[(i - 1) & 1]; g.lda0 = prev; g.K0 = prev; g.K = prev;
-    g.W = atv(w, L, L.enc_first + 2 * i); g.ldw = prev;
-    g.bias = atv(w, L, L.enc_first + 2 * i + 1);
-    g.C = last ? (void*)X : (void*)Hs[i & 1];
-    GemmBatch b = single(pl.R, out, out);
-    HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(SG_F32, 1, w->dtype, 1, last ? EPI_RESID : EPI_RELU, g, b, pl.R, out, st); }),
-           "encoder GEMM");
-    prev = out;
+  (void)tm;
+  EncArgs e;
+  memset(&e, 0, sizeof(e));
+  for (int i = 0; i < 2; ++i) { e.kpts[i] = p.kp[i]; e.conf[i] = p.cf[i]; e.desc[i] = p.de[i]; }
+  memcpy(e.img, p.img, sizeof(e.img));
+  e.D = w->D;
+  e.ldx = w->D;
+  e.n_layers = w->n_enc + 1;
+  e.width[0] = 3;
+  for (int i = 0; i < w->n_enc; ++i) e.width[i + 1] = w->enc[i];
+  e.width[w->n_enc + 1] = w->D;
+  for (int i = 0; i <= w->n_enc; ++i) {
+    e.W[i] = atv(w, L, L.enc_first + 2 * i);
+    e.b[i] = atv(w, L, L.enc_first + 2 * i + 1);
   }
+  e.X = reinterpret_cast<float*>(ws + wl.X);
+  HIPCHK(launch_encoder(w->dtype, w->dtype, e, pl.seg, st), "encoder");
   return SG_OK;
 }
 
@@ -344,14 +352,15 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       g.A0 = X; g.lda0 = D; g.K0 = D; g.K = D;
       g.W = atv(w, L, base); g.ldw = D; g.bias = atv(w, L, base + 1);
       g.C = QK; g.C2 = VT; g.split = 2 * D;
-      GemmBatch b = single(R, 3 * D, 2 * D);
+      GemmBatch b = single(R, 3 * D, wl.ldqk);
       b.p[0].ldct = wl.ldvt;
       HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, 0, EPI_QKV, g, b, R, 3 * D, st); }), "qkv GEMM");
     }
     // multi-head attention: self on even stages, cross on odd stages
     {
       AttnArgs a;
-      a.qk = QK; a.vt = VT; a.out = MB; a.D = D; a.ldvt = wl.ldvt; a.cross = s & 1;
+      a.qk = QK; a.vt = VT; a.out = MB; a.D = D; a.ldvt = wl.ldvt; a.ldqk = wl.ldqk; a.cross = s & 1;
+      a.heads = w->H;
       const int dh = D / w->H;
       a.scale2 = log2e / sqrtf((float)dh);
       HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_attention(op, dh, a, pl.seg, w->H, st); }), "attention");
@@ -441,8 +450,8 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
   tm.stage(SG_EV_SCORES);
   // T iterations: u = log mu - lse_j(Z + v); v = log nu - lse_i(Z + u)
   for (int it = 0; it < T; ++it) {
-    HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(Z, pl.pt, 0, it == 0 ? nullptr : V, U, alpha2, alpha_dev, (int)pl.uf, st); }), "sinkhorn rows");
-    HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(ZT, pl.pt, 1, U, V, alpha2, alpha_dev, (int)pl.vf, st); }), "sinkhorn cols");
+    HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(Z, pl.pt, 0, it == 0 ? nullptr : V, U, alpha2, alpha_dev, pl.ru, st); }), "sinkhorn rows");
+    HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(ZT, pl.pt, 1, U, V, alpha2, alpha_dev, pl.rv, st); }), "sinkhorn cols");
   }
   if (T == 0) {
     HIPCHK(launch_fill_f32(U, 0.f, (int)pl.uf, st), "zero u");
@@ -453,7 +462,7 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
   HIPCHK(launch_finalize(pl.pt, idx0, val0, idx1, U, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, st),
          "finalize");
   if (out.logP)
-    HIPCHK(launch_write_logp(Z, pl.pt, U, V, alpha2, alpha_dev, out.logP, out.logP_ld, out.logP_stride, (int)pl.uf, st),
+    HIPCHK(launch_write_logp(Z, pl.pt, U, V, alpha2, alpha_dev, out.logP, out.logP_ld, out.logP_stride, pl.ru, st),
            "logP");
   return SG_OK;
 }
@@ -467,6 +476,102 @@ sg_status check_opts(const sg_opts* o) {
 
 hipStream_t stream_of(const sg_opts* o) { return o ? (hipStream_t)o->stream : (hipStream_t)0; }
 
+// ------------------------------------------------------------ graph replay
+//
+// The launch sequence of a call depends only on its shapes and pointers, so
+// it is captured once into a HIP graph (on a private capture stream) and
+// replayed on the caller's stream afterwards, which removes most of the
+// per-kernel launch cost of the ~300 small kernels of one pass.  Calls that
+// ask for timing events, set SG_FLAG_NO_GRAPH, or arrive on a stream that
+// the caller is capturing run eagerly.
+
+struct GraphCache {
+  std::mutex mu;
+  std::vector<std::pair<std::string, hipGraphExec_t>> entries;
+  std::vector<std::string> seen;  // keys called once so far
+  hipStream_t cap[64] = {};
+};
+GraphCache g_graphs;
+constexpr size_t kMaxGraphs = 64;
+
+template <class F>
+sg_status run_maybe_graph(const std::string& key_in, const sg_opts* o, hipStream_t st, F&& enqueue) {
+  bool use = !(o && (o->stage_events || o->kernel_events || (o->flags & SG_FLAG_NO_GRAPH)));
+  if (use) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (st && hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone) use = false;
+  }
+  if (!use) return enqueue(st);
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= 64) return enqueue(st);
+  std::string key = key_in;
+  key.append(reinterpret_cast<const char*>(&dev), sizeof(dev));
+  std::lock_guard<std::mutex> lk(g_graphs.mu);
+  for (auto& e : g_graphs.entries)
+    if (e.first == key) {
+      HIPCHK(hipGraphLaunch(e.second, st), "hipGraphLaunch");
+      return SG_OK;
+    }
+  // capture only calls that repeat: the first call with a key runs eagerly
+  bool seen = false;
+  for (auto& k : g_graphs.seen) seen = seen || k == key;
+  if (!seen) {
+    if (g_graphs.seen.size() >= 4 * kMaxGraphs) g_graphs.seen.clear();
+    g_graphs.seen.push_back(key);
+    return enqueue(st);
+  }
+  if (!g_graphs.cap[dev]) HIPCHK(hipStreamCreateWithFlags(&g_graphs.cap[dev], hipStreamNonBlocking), "capture stream");
+  hipStream_t cap = g_graphs.cap[dev];
+  HIPCHK(hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
+  sg_status s = enqueue(cap);
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamEndCapture(cap, &graph);
+  if (s != SG_OK || e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return s != SG_OK ? s : hip_fail(e, "hipStreamEndCapture");
+  }
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
+  if (g_graphs.entries.size() >= kMaxGraphs) {
+    // replays already enqueued keep their executable alive until they finish
+    HIPCHK(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    for (auto& x : g_graphs.entries) (void)hipGraphExecDestroy(x.second);
+    g_graphs.entries.clear();
+  }
+  g_graphs.entries.emplace_back(key, exec);
+  HIPCHK(hipGraphLaunch(exec, st), "hipGraphLaunch");
+  return SG_OK;
+}
+
+template <class T>
+void put(std::string& k, const T& v) {
+  k.append(reinterpret_cast<const char*>(&v), sizeof(T));
+}
+
+std::string call_key(int kind, const Problem& p, const sg_weights* w, int Lst, int T, const Outputs& out,
+                     const sg_opts* o, const void* ws) {
+  std::string k;
+  put(k, kind); put(k, p.B); put(k, p.Mpad); put(k, p.Npad);
+  for (int b = 0; b < p.B; ++b) { put(k, p.M[b]); put(k, p.N[b]); }
+  for (int i = 0; i < 2; ++i) { put(k, p.kp[i]); put(k, p.cf[i]); put(k, p.de[i]); }
+  put(k, p.img);
+  if (w) {
+    put(k, w->D); put(k, w->H); put(k, w->n_enc);
+    for (int i = 0; i < w->n_enc; ++i) put(k, w->enc[i]);
+    put(k, w->L_max); put(k, w->dtype); put(k, w->blob); put(k, w->blob_bytes);
+  }
+  put(k, Lst); put(k, T); put(k, out);
+  put(k, o ? o->match_threshold : 0.f);
+  put(k, ws);
+  return k;
+}
+
+sg_status enqueue_full(const Problem& p, const Plan& pl, const WsLayout& wl, char* ws, const sg_weights* w,
+                       const WLayout& L, int Lst, int T, const Outputs& out, const sg_opts* o, hipStream_t st);
+
 sg_status run_full(const Problem& p, const sg_weights* w, const WLayout& L, int Lst, int T,
                    const Outputs& out, const sg_opts* o) {
   Plan pl;
@@ -475,8 +580,14 @@ sg_status run_full(const Problem& p, const sg_weights* w, const WLayout& L, int 
   void* wsp = nullptr;
   sg_status s = get_workspace(o, wl.total, &wsp);
   if (s != SG_OK) return s;
-  char* ws = reinterpret_cast<char*>(wsp);
-  hipStream_t st = stream_of(o);
+  return run_maybe_graph(call_key(0, p, w, Lst, T, out, o, wsp), o, stream_of(o), [&](hipStream_t st) {
+    return enqueue_full(p, pl, wl, reinterpret_cast<char*>(wsp), w, L, Lst, T, out, o, st);
+  });
+}
+
+sg_status enqueue_full(const Problem& p, const Plan& pl, const WsLayout& wl, char* ws, const sg_weights* w,
+                       const WLayout& L, int Lst, int T, const Outputs& out, const sg_opts* o, hipStream_t st) {
+  sg_status s;
   Timer tm{o, st};
   // alpha stays in device memory: the Sinkhorn and logP kernels read it there
   const float* alpha_dev = at<float>(w, L, L.alpha);
@@ -727,21 +838,27 @@ sg_status sg_stage_match(const float* fA, int32_t M, const float* fB, int32_t N,
   if ((s = get_workspace(opts, wl.total, &wsp)) != SG_OK) return s;
   char* ws = reinterpret_cast<char*>(wsp);
   float* F = reinterpret_cast<float*>(ws + wl.F);
-  HIPCHK(hipMemcpyAsync(F, fA, (size_t)M * D * 4, hipMemcpyDeviceToDevice, st), "copy fA");
-  HIPCHK(hipMemcpyAsync(F + (size_t)pl.seg.row0[1] * D, fB, (size_t)N * D * 4, hipMemcpyDeviceToDevice, st), "copy fB");
   Outputs out;
   out.m0 = out_matches; out.s0 = out_scores;
   if (opts) {
     out.m1 = opts->out_matches1; out.s1 = opts->out_scores1;
     out.logP = opts->out_logP; out.logP_ld = opts->logP_ld;
   }
-  Timer tm{opts, st};
-  tm.stage(SG_EV_GNN);
-  if ((s = run_matching(p, pl, D, alpha, nullptr, T, opts ? opts->match_threshold : 0.f, F, ws, wl, out, tm, st)) != SG_OK)
-    return s;
-  tm.stage(SG_EV_END);
-  tm.finish();
-  return SG_OK;
+  p.kp[0] = fA; p.kp[1] = fB;  // part of the replay key
+  std::string key = call_key(1, p, nullptr, D, T, out, opts, wsp);
+  key.append(reinterpret_cast<const char*>(&alpha), sizeof(alpha));
+  return run_maybe_graph(key, opts, st, [&](hipStream_t cs) -> sg_status {
+    HIPCHK(hipMemcpyAsync(F, fA, (size_t)M * D * 4, hipMemcpyDeviceToDevice, cs), "copy fA");
+    HIPCHK(hipMemcpyAsync(F + (size_t)pl.seg.row0[1] * D, fB, (size_t)N * D * 4, hipMemcpyDeviceToDevice, cs),
+           "copy fB");
+    Timer tm{opts, cs};
+    tm.stage(SG_EV_GNN);
+    sg_status r = run_matching(p, pl, D, alpha, nullptr, T, opts ? opts->match_threshold : 0.f, F, ws, wl, out, tm, cs);
+    if (r != SG_OK) return r;
+    tm.stage(SG_EV_END);
+    tm.finish();
+    return SG_OK;
+  });
 }
 
 }  // extern "C"

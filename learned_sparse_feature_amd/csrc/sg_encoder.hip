@@ -1,0 +1,132 @@
+// Keypoint encoder MLP_enc([x, y, c]) added to the descriptors (gfx950).
+//
+// One fused kernel: a 256-thread workgroup takes 32 points of one image,
+// normalises their positions, runs the whole MLP with the hidden
+// activations kept in LDS (layer 0 on the VALU, K = 3; the other layers on
+// MFMA in the operand type of the network), and writes x0 = d + MLP_enc(p)
+// as fp32 states.  The four waves split each layer's outputs into 32-column
+// blocks; weights stream from L2.
+#include "sg_device.h"
+
+namespace sg {
+
+template <typename OpT, typename WT>
+__global__ __launch_bounds__(256) void k_encoder(EncArgs e, SegTable seg) {
+  constexpr bool BF = std::is_same<OpT, bf16>::value;
+  constexpr int PADE = BF ? 8 : 4;
+  constexpr int LDH = kMaxEncWidth + PADE;
+  __shared__ __attribute__((aligned(16))) OpT hbuf[2][32 * LDH];
+
+  int t = blockIdx.x;
+  const int s = find_segment(seg, &t);
+  if (s >= seg.n_seg) return;
+  const int p0 = t * 32, np = min(32, seg.n[s] - p0);
+  const bool isA = seg.side[s] == 0;
+  const float* kp = e.kpts[isA ? 0 : 1] + 2 * (size_t)(seg.in_off[s] + p0);
+  const float* cf = e.conf[isA ? 0 : 1] + (size_t)(seg.in_off[s] + p0);
+  const float* de = e.desc[isA ? 0 : 1] + (size_t)e.D * (seg.in_off[s] + p0);
+  const float iw = e.img[isA ? 0 : 2], ih = e.img[isA ? 1 : 3];
+  const size_t row0 = (size_t)seg.row0[s] + p0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // layer 0 (3 -> w1) with ReLU; rows past the image are zero
+  {
+    const WT* W0 = reinterpret_cast<const WT*>(e.W[0]);
+    const WT* b0 = reinterpret_cast<const WT*>(e.b[0]);
+    const int w1 = e.width[1];
+    for (int idx = tid; idx < 32 * w1; idx += 256) {
+      const int r = idx / w1, o = idx % w1;
+      float h = 0.f;
+      if (r < np) {
+        float x = kp[2 * r], y = kp[2 * r + 1];
+        if (iw > 0.f) {
+          const float sc = 0.7f * fmaxf(iw, ih);
+          x = (x - 0.5f * iw) / sc;
+          y = (y - 0.5f * ih) / sc;
+        }
+        h = (float)W0[3 * o] * x + (float)W0[3 * o + 1] * y + (float)W0[3 * o + 2] * cf[r] + (float)b0[o];
+        h = fmaxf(h, 0.f);
+      }
+      hbuf[0][r * LDH + o] = (OpT)h;
+    }
+  }
+  __syncthreads();
+
+  int cur = 0;
+  for (int l = 1; l < e.n_layers; ++l) {
+    const int K = e.width[l], n_out = e.width[l + 1];
+    const bool last = l == e.n_layers - 1;
+    const WT* W = reinterpret_cast<const WT*>(e.W[l]);
+    const WT* bias = reinterpret_cast<const WT*>(e.b[l]);
+    const OpT* hin = hbuf[cur];
+    OpT* hout = hbuf[cur ^ 1];
+    for (int nb = wave; nb * 32 < n_out; nb += 4) {
+      const int n = nb * 32 + (lane & 31);
+      const WT* wrow = W + (size_t)n * K;
+      f32x16 acc = zero16();
+      // the whole weight row slice of this lane is requested before the MFMAs
+      // (the loop is bound by load latency, not by the contraction)
+      constexpr int KMAX = kMaxEncWidth;
+      if constexpr (BF) {
+        bf16x8 wb[KMAX / 16];
+#pragma unroll
+        for (int q = 0; q < KMAX / 16; ++q)
+          if (q * 16 < K) wb[q] = *reinterpret_cast<const bf16x8*>(wrow + q * 16 + (lane >> 5) * 8);
+#pragma unroll
+        for (int q = 0; q < KMAX / 16; ++q)
+          if (q * 16 < K) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(hin + (lane & 31) * LDH + q * 16 + (lane >> 5) * 8);
+            acc = mfma(a, wb[q], acc);
+          }
+      } else {
+        // k-slot l/32 covers the half [ (l/32) K/2, (l/32 + 1) K/2 ) of the contraction
+        const int kh = (lane >> 5) * (K / 2);
+        float4 wb[KMAX / 8];
+#pragma unroll
+        for (int q = 0; q < KMAX / 8; ++q)
+          if (q * 4 < K / 2) wb[q] = *reinterpret_cast<const float4*>(wrow + kh + 4 * q);
+#pragma unroll
+        for (int q = 0; q < KMAX / 8; ++q)
+          if (q * 4 < K / 2) {
+            const float4 a = *reinterpret_cast<const float4*>(hin + (lane & 31) * LDH + kh + 4 * q);
+            acc = mfma(a.x, wb[q].x, acc);
+            acc = mfma(a.y, wb[q].y, acc);
+            acc = mfma(a.z, wb[q].z, acc);
+            acc = mfma(a.w, wb[q].w, acc);
+          }
+      }
+      const float bv = (float)bias[n];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const float v = acc[i] + bv;
+        if (!last) {
+          hout[r * LDH + n] = (OpT)fmaxf(v, 0.f);
+        } else if (r < np) {
+          e.X[(row0 + r) * e.ldx + n] = de[(size_t)r * e.D + n] + v;
+        }
+      }
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+}
+
+hipError_t launch_encoder(int op, int wd, const EncArgs& e, const SegTable& seg, hipStream_t st) {
+  int tiles = 0;
+  for (int s = 0; s < seg.n_seg; ++s) tiles += (seg.n[s] + 31) / 32;
+  if (tiles == 0) return hipSuccess;
+  for (int l = 1; l < e.n_layers; ++l)
+    if (e.width[l] > kMaxEncWidth) return hipErrorInvalidValue;
+  for (int l = 1; l < e.n_layers; ++l)
+    if (e.width[l] % 16 || e.width[l + 1] % 32) return hipErrorInvalidValue;
+  if (op == SG_BF16 && wd == SG_BF16)
+    hipLaunchKernelGGL((k_encoder<bf16, bf16>), dim3(tiles), dim3(256), 0, st, e, seg);
+  else if (op == SG_F32 && wd == SG_F32)
+    hipLaunchKernelGGL((k_encoder<float, float>), dim3(tiles), dim3(256), 0, st, e, seg);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace sg

@@ -32,8 +32,9 @@ struct PairTable {
   int M[SG_MAX_BATCH], N[SG_MAX_BATCH];
   int rowA[SG_MAX_BATCH];                         // compact row of f_A (f_B follows at +M)
   int z_off[SG_MAX_BATCH], zt_off[SG_MAX_BATCH];  // float offsets of Z and ZT
-  int upre[SG_MAX_BATCH + 1];                     // prefix sums of (M+1)
-  int vpre[SG_MAX_BATCH + 1];                     // prefix sums of (N+1)
+  int upre[SG_MAX_BATCH + 1];                     // prefix sums of (M+1): flattened u rows
+  int vpre[SG_MAX_BATCH + 1];                     // prefix sums of (N+1): flattened v rows
+  int uoff[SG_MAX_BATCH], voff[SG_MAX_BATCH];     // storage offsets of u, v (multiples of 4)
 };
 
 __host__ __device__ inline int ld4(int n) { return (n + 3) & ~3; }
@@ -67,20 +68,31 @@ struct GemmArgs {
   int split;                         // EPI_QKV: first column that goes to VT
 };
 
+// Fused keypoint encoder: linear layers [3 -> width[1] -> ... -> D].
+constexpr int kMaxEncWidth = 256;  // widest hidden layer (held in LDS)
+struct EncArgs {
+  const float* kpts[2];  // image A / B inputs (caller layout, padded in batch mode)
+  const float* conf[2];
+  const float* desc[2];
+  float img[4];          // wA, hA, wB, hB; 0 = positions already normalised
+  int D, ldx, n_layers;  // n_layers linear layers (n_enc + 1)
+  int width[SG_MAX_ENC + 2];
+  const void* W[SG_MAX_ENC + 1];
+  const void* b[SG_MAX_ENC + 1];
+  float* X;              // states [R][ldx]
+};
+
 struct AttnArgs {
   const void* qk;    // [R][2D]: q at columns h*dh.., k at D + h*dh..
   const void* vt;    // [D][ldvt]: v transposed
   void* out;         // [R][D] message (heads concatenated)
-  int D, ldvt, cross;
+  int D, ldvt, ldqk, cross, heads;
   float scale2;      // log2(e) / sqrt(dh)
 };
 
 // Host-side launchers (sg_kernels.hip).
-hipError_t launch_encode_l0(const float* kptsA, const float* confA, const float* descA,
-                            const float* kptsB, const float* confB, const float* descB,
-                            const float img[4], const SegTable& seg, int R, int D,
-                            const void* W0, const void* b0, int w0, int dtype, float* H0,
-                            float* X, hipStream_t st);
+hipError_t launch_encoder(int op_dtype, int w_dtype, const EncArgs& e, const SegTable& seg,
+                          hipStream_t st);
 hipError_t launch_gemm(int op_dtype, int a0_is_f32, int w_dtype, int out_is_f32, int epi,
                        const GemmArgs& g, const GemmBatch& b, int max_rows, int max_n,
                        hipStream_t st);

@@ -119,6 +119,33 @@ def test_end_to_end_deterministic():
     assert np.array_equal(a["logP"], b["logP"]) and np.array_equal(a["matches0"], b["matches0"])
 
 
+def test_graph_replay_equals_eager():
+    """Identical repeated calls are captured into a HIP graph and replayed;
+    every replay equals the eager result bitwise, with other eager work and
+    synchronisations in between."""
+    cfg = synth.CONFIGS[2]
+    w = synth.make_weights(cfg)
+    W = sg.pack_weights(w)
+    pair = synth.make_pair(cfg)
+    other = synth.make_pair(cfg, seed=77)
+    keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
+    t = [dev(pair[k]) for k in keys]
+    t2 = [dev(other[k]) for k in keys]
+    img = (*pair["image_size0"], *pair["image_size1"])
+    ref = sg.sg_match(*t, W, cfg.L, cfg.T, image_size=img, want_logP=True, graph=False)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in ref.items() if isinstance(v, torch.Tensor)}
+    bufs = {k: torch.full_like(v, -7) for k, v in ref.items()}
+    for rep in range(5):
+        sg.sg_match(*t, W, cfg.L, cfg.T, image_size=img, want_logP=True, out=bufs)
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(bufs[k], ref[k]), (rep, k)
+            bufs[k].fill_(-7)
+        sg.sg_match(*t2, W, cfg.L, cfg.T, image_size=img, graph=False)   # eager work in between
+        torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ batch
 
 @functools.lru_cache(maxsize=None)

@@ -82,7 +82,10 @@ def test_encoder_parity(cid, n, bias_on):
                                 image_size=pair["image_size0"]))
     kn = oracle.normalize_keypoints(pair["kpts0"], *pair["image_size0"])
     want = pair["desc0"].astype(np.float64) + oracle.keypoint_encoder(kn, pair["conf0"], w["enc"])
-    assert rel_rows(x, want).max() < 1e-5
+    err = rel_rows(x, want).max()
+    print(f"cfg{cid} n={n}: encoder rel err {err:.2e}")
+    # fp32 networks: fp32 MFMA chain; bf16 networks: bf16 activations (2^-9 rounding per layer)
+    assert err < (1e-5 if cfg.dtype == "f32" else 1e-2)
 
 
 # -------------------------------------------------------------- GNN stages
