@@ -80,6 +80,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="also time sg_match_batch on this many 1024x1024 pairs per call")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="before the steps, copy this many MiB with a plain device copy (counter scaling)")
     args = ap.parse_args()
@@ -197,6 +199,32 @@ def main():
                         "peak": PEAK["bf16_TFLOPs"], "unit": "TFLOP/s", "frac": round(ach / PEAK["bf16_TFLOPs"], 4),
                         "traffic": None}
 
+    batch = None
+    if args.batch:
+        Bn = args.batch
+        pairs = [synth.make_pair(cfg, seed=synth.INPUT_SEED_BASE + 100 + i) for i in range(Bn)]
+        bt = {k: torch.from_numpy(np.stack([p[k] for p in pairs])).to(dev) for k in keys}
+        Ms, Ns = [M] * Bn, [N] * Bn
+        wsb = torch.empty(sg.workspace_size(W, M, N, Bn), dtype=torch.uint8, device=dev)
+        bbufs = {"matches0": torch.empty((Bn, M), dtype=torch.int32, device=dev),
+                 "scores0": torch.empty((Bn, M), dtype=torch.float32, device=dev)}
+
+        def bstep():
+            return sg.sg_match_batch(Ms, Ns, *[bt[k] for k in keys], W, cfg.L, cfg.T, image_size=img,
+                                     workspace=wsb, want_matches1=False)
+        for _ in range(max(2, args.warmup)):
+            bstep()
+        torch.cuda.synchronize()
+        nb = max(3, args.steps // 10)
+        t0 = time.perf_counter()
+        for _ in range(nb):
+            bstep()
+        torch.cuda.synchronize()
+        dtb = time.perf_counter() - t0
+        batch = {"pairs_per_call": Bn, "calls": nb, "ms_per_call": round(1e3 * dtb / nb, 3),
+                 "pairs_per_s": round(nb * Bn / dtb, 2)}
+        log(f"batch: {batch}")
+
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
@@ -212,6 +240,7 @@ def main():
                                "bf16 GNN operands / fp32 accumulation, fp32 scores + Sinkhorn",
                    "pairs_per_step": 1, "M": M, "N": N, "D": cfg.D, "L": cfg.L, "T": cfg.T},
         "roofline": roofline, "cpu_baseline": cpu, "stages_ms": stages, "kernels": kernels,
+        "batch_throughput": batch,
         "baseline_context": {"pages_ms_per_pair": {"GTX1080_1024kp": 87.0, "unstated_hw_2048kp": 70.0},
                              "pages_pairs_per_s": {"GTX1080_1024kp": 11.5, "unstated_hw_aachen_4096kp": 6.5}},
     }

@@ -645,7 +645,7 @@ size_t sg_workspace_size(const sg_weights* w, int32_t Mmax, int32_t Nmax, int32_
   if (check_config(w) != SG_OK || Mmax < 0 || Nmax < 0 || batch < 1) return 0;
   const long B = batch;
   const long R = B * (round32(Mmax) + round32(Nmax));
-  WsLayout wl = ws_layout(w, R, B * Mmax * ld4(Nmax), B * Nmax * ld4(Mmax), B * (Mmax + 1), B * (Nmax + 1),
+  WsLayout wl = ws_layout(w, R, B * Mmax * ld4(Nmax), B * Nmax * ld4(Mmax), B * ld4(Mmax + 1), B * ld4(Nmax + 1),
                           B * Mmax, B * Nmax);
   return wl.total;
 }
@@ -653,7 +653,7 @@ size_t sg_workspace_size(const sg_weights* w, int32_t Mmax, int32_t Nmax, int32_
 size_t sg_stage_match_workspace_size(int32_t M, int32_t N, int32_t D) {
   if (M < 0 || N < 0 || D <= 0) return 0;
   const long R = round32(M) + round32(N);
-  return ws_layout_raw(D, 4, 0, R, (long)M * ld4(N), (long)N * ld4(M), M + 1, N + 1, M, N).total;
+  return ws_layout_raw(D, 4, 0, R, (long)M * ld4(N), (long)N * ld4(M), ld4(M + 1), ld4(N + 1), M, N).total;
 }
 
 sg_status sg_match(const float* kptsA, const float* descA, const float* confA, int32_t M,

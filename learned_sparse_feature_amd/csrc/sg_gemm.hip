@@ -2,11 +2,22 @@
 //
 // C = A W^T (+ epilogue) with A [rows][K] (optionally two sources split at
 // column K0: the [x || m] concatenation of the update MLP) and W [n][K] the
-// row-major weight of a kernel-1 Conv1d / Linear layer.  One 256-thread
-// workgroup computes a 64x64 output tile as four waves of 32x32.  The K loop
-// is double buffered: the next K tile is fetched from global memory into
-// registers while the MFMAs consume the current one from LDS, and it is
-// converted to the operand type (bf16 or fp32) on its way into LDS.
+// row-major weight of a kernel-1 Conv1d / Linear layer.  A 256-thread
+// workgroup computes a BM x BN output tile as 2 x 2 waves; each wave owns
+// (BM/2) x (BN/2) as 32x32 MFMA blocks.  A and W tiles are converted to the
+// operand type (bf16 or fp32) on their way into LDS (double buffered).
+//
+// Two shapes are instantiated:
+//  * 64 x 64 tiles with up to 8 K steps in flight (PF = 8) for small
+//    problems: a single pair has too few tiles to fill the chip, and the
+//    kernel is bound by the latency of its loads, so the whole K range is
+//    requested before the first MFMA;
+//  * 128 x 128 tiles with one K step in flight (PF = 2) for large problems
+//    (batches): each 64x64 wave tile reuses every LDS fragment twice, and
+//    several resident workgroups per CU hide the load latency.
+// The grid's x axis walks row tiles, so consecutive workgroups (which the
+// dispatcher sends to different XCDs) split the A rows between the XCDs'
+// L2 caches.
 #include "sg_device.h"
 
 namespace sg {
@@ -42,36 +53,32 @@ __device__ __forceinline__ typename Chunk<OpT, CH>::type load_chunk(const SrcT* 
 
 }  // namespace
 
-template <typename OpT, typename A0T, typename WT, typename OutT, int EPI>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs g, GemmBatch bt) {
+template <typename OpT, typename A0T, typename WT, typename OutT, int EPI, int BM, int BN, int PF>
+__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   constexpr bool BF = std::is_same<OpT, bf16>::value;
-  constexpr int BM = 64, BN = 64;
   constexpr int CH = BF ? 8 : 4;   // elements per 16-byte chunk
   constexpr int BK = 8 * CH;       // 64 bf16 or 32 fp32 per K step
   constexpr int PITCH = BK + CH;   // rows padded by 16 bytes
+  constexpr int AC = BM * 8 / 256, WC = BN * 8 / 256;  // chunks per thread per K step
+  constexpr int MB = BM / 64, NB = BN / 64;            // 32x32 blocks per wave
   typedef typename Chunk<OpT, CH>::type VecT;
   __shared__ __attribute__((aligned(16))) OpT As[2][BM * PITCH];
   __shared__ __attribute__((aligned(16))) OpT Ws[2][BN * PITCH];
 
   const GemmProblem P = bt.p[blockIdx.z];
-  // blockIdx.x walks the row tiles: consecutive workgroups are dispatched to
-  // different XCDs, so each XCD's L2 holds only its share of the A rows
-  // (while every XCD reads the - smaller - weight tile columns)
   const int r0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   if (r0 >= P.rows || n0 >= P.n_out) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Each thread stages two 16-byte chunks of A and of W per K step:
-  // chunk c = tid + 256 h covers row c / 8, columns (c % 8) * CH ...
-  // Register slot q holds K step kb + q of the current round.
-  constexpr int PF = 8;
-  VecT ra[PF][2], rw[PF][2];
+  // chunk c = tid + 256 h of a tile covers row c / 8, columns (c % 8) * CH;
+  // register slot q holds K step kb + q of the current round
+  VecT ra[PF][AC], rw[PF][WC];
   auto gload = [&](int k0, int q) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < AC; ++h) {
       const int c = tid + 256 * h, row = c >> 3, k = k0 + (c & 7) * CH;
-      const int r = r0 + row, n = n0 + row;
+      const int r = r0 + row;
       if (r < P.rows && k < g.K) {
         if (k < g.K0)
           ra[q][h] = load_chunk<A0T, OpT, CH>(reinterpret_cast<const A0T*>(g.A0) + (size_t)(P.a_row0 + r) * g.lda0 + k);
@@ -80,6 +87,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, GemmBatch bt) {
       } else {
         ra[q][h] = (VecT)(OpT)0.f;
       }
+    }
+#pragma unroll
+    for (int h = 0; h < WC; ++h) {
+      const int c = tid + 256 * h, row = c >> 3, k = k0 + (c & 7) * CH;
+      const int n = n0 + row;
       if (n < P.n_out && k < g.K)
         rw[q][h] = load_chunk<WT, OpT, CH>(reinterpret_cast<const WT*>(g.W) + (size_t)(P.w_row0 + n) * g.ldw + k);
       else
@@ -88,42 +100,60 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, GemmBatch bt) {
   };
   auto sstore = [&](int buf, int q) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = tid + 256 * h, row = c >> 3, col = (c & 7) * CH;
-      *reinterpret_cast<VecT*>(&As[buf][row * PITCH + col]) = ra[q][h];
-      *reinterpret_cast<VecT*>(&Ws[buf][row * PITCH + col]) = rw[q][h];
+    for (int h = 0; h < AC; ++h) {
+      const int c = tid + 256 * h;
+      *reinterpret_cast<VecT*>(&As[buf][(c >> 3) * PITCH + (c & 7) * CH]) = ra[q][h];
+    }
+#pragma unroll
+    for (int h = 0; h < WC; ++h) {
+      const int c = tid + 256 * h;
+      *reinterpret_cast<VecT*>(&Ws[buf][(c >> 3) * PITCH + (c & 7) * CH]) = rw[q][h];
     }
   };
-  f32x16 acc;
+  f32x16 acc[MB][NB];
   auto compute = [&](int cur) {
-    const OpT* ap = &As[cur][(wm * 32 + (lane & 31)) * PITCH];
-    const OpT* wp = &Ws[cur][(wn * 32 + (lane & 31)) * PITCH];
+    const OpT* ap = &As[cur][(wm * (BM / 2) + (lane & 31)) * PITCH];
+    const OpT* wp = &Ws[cur][(wn * (BN / 2) + (lane & 31)) * PITCH];
     if constexpr (BF) {
 #pragma unroll
       for (int s = 0; s < BK / 16; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ap + s * 16 + (lane >> 5) * 8);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(wp + s * 16 + (lane >> 5) * 8);
-        acc = mfma(a, b, acc);
+        bf16x8 a[MB], b[NB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) a[i] = *reinterpret_cast<const bf16x8*>(ap + i * 32 * PITCH + s * 16 + (lane >> 5) * 8);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) b[j] = *reinterpret_cast<const bf16x8*>(wp + j * 32 * PITCH + s * 16 + (lane >> 5) * 8);
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma(a[i], b[j], acc[i][j]);
       }
     } else {
-      // k-slot l/32 of the 16 MFMAs covers tile columns 16*(l/32) .. +15
+      // k-slot l/32 of the MFMAs covers tile columns 16*(l/32) .. +15
 #pragma unroll
       for (int s4 = 0; s4 < BK / 8; ++s4) {
-        const float4 a = *reinterpret_cast<const float4*>(ap + (lane >> 5) * (BK / 2) + 4 * s4);
-        const float4 b = *reinterpret_cast<const float4*>(wp + (lane >> 5) * (BK / 2) + 4 * s4);
-        acc = mfma(a.x, b.x, acc);
-        acc = mfma(a.y, b.y, acc);
-        acc = mfma(a.z, b.z, acc);
-        acc = mfma(a.w, b.w, acc);
+        float4 a[MB], b[NB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) a[i] = *reinterpret_cast<const float4*>(ap + i * 32 * PITCH + (lane >> 5) * (BK / 2) + 4 * s4);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) b[j] = *reinterpret_cast<const float4*>(wp + j * 32 * PITCH + (lane >> 5) * (BK / 2) + 4 * s4);
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            acc[i][j] = mfma(a[i].x, b[j].x, acc[i][j]);
+            acc[i][j] = mfma(a[i].y, b[j].y, acc[i][j]);
+            acc[i][j] = mfma(a[i].z, b[j].z, acc[i][j]);
+            acc[i][j] = mfma(a[i].w, b[j].w, acc[i][j]);
+          }
       }
     }
   };
 
-  acc = zero16();
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = zero16();
   const int nk = (g.K + BK - 1) / BK;
-  // Up to PF K steps are in flight at once: at these sizes a GEMM is bound by
-  // the latency of its global loads, not by the MFMAs, so the whole K range
-  // (K <= PF * BK) is requested before the first MFMA.
 #pragma unroll
   for (int q = 0; q < PF; ++q)
     if (q < nk) gload(q * BK, q);
@@ -140,82 +170,123 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, GemmBatch bt) {
     }
   }
 
-  const int n = n0 + wn * 32 + (lane & 31);
-  if (n >= P.n_out) return;
-  float bias = 0.f;
-  if (EPI != EPI_SCORE && g.bias) bias = (float)reinterpret_cast<const WT*>(g.bias)[n];
+  if constexpr (EPI == EPI_QKV) {
+    if (n0 >= g.split) {
+      // V columns: written transposed (VT [n - split][r]).  Each 32x32 block
+      // is turned around in LDS so that the stores run along rows of VT.
+      constexpr int TP = 32 + 16 / (int)sizeof(OutT);
+      OutT* tt = reinterpret_cast<OutT*>(&As[0][0]) + wave * 32 * TP;
+      constexpr int CO = 16 / (int)sizeof(OutT);  // elements per 16-byte store
+      typedef typename Chunk<OutT, CO>::type OVec;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = r0 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-    if (r >= P.rows) continue;
-    float v = acc[i] + bias;
-    if constexpr (EPI == EPI_BIAS || EPI == EPI_RELU) {
-      if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
-      reinterpret_cast<OutT*>(g.C)[P.c_off + (size_t)r * P.ldc + n] = (OutT)v;
-    } else if constexpr (EPI == EPI_RESID) {
-      float* c = reinterpret_cast<float*>(g.C) + P.c_off + (size_t)r * P.ldc + n;
-      *c = *c + v;
-    } else if constexpr (EPI == EPI_QKV) {
-      if (n < g.split)
-        reinterpret_cast<OutT*>(g.C)[P.c_off + (size_t)r * P.ldc + n] = (OutT)v;
-      else
-        reinterpret_cast<OutT*>(g.C2)[P.ct_off + (size_t)(n - g.split) * P.ldct + r] = (OutT)v;
-    } else {  // EPI_SCORE
-      v = acc[i] * g.scale;
-      reinterpret_cast<float*>(g.C)[P.c_off + (size_t)r * P.ldc + n] = v;
-      reinterpret_cast<float*>(g.C2)[P.ct_off + (size_t)n * P.ldct + r] = v;
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int nl = lane & 31;
+          const int nn = n0 + wn * (BN / 2) + j * 32 + nl;
+          const float bias = g.bias && nn < P.n_out ? (float)reinterpret_cast<const WT*>(g.bias)[nn] : 0.f;
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int rl = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            tt[nl * TP + rl] = (OutT)(acc[i][j][e] + bias);
+          }
+          __syncthreads();
+          for (int c = lane; c < 32 * (32 / CO); c += 64) {
+            const int nlc = c / (32 / CO), part = c % (32 / CO);
+            const int n = n0 + wn * (BN / 2) + j * 32 + nlc;
+            const int r = r0 + wm * (BM / 2) + i * 32 + part * CO;
+            if (n < P.n_out && r < P.rows) {
+              OVec v;
+#pragma unroll
+              for (int x = 0; x < CO; ++x) v[x] = tt[nlc * TP + part * CO + x];
+              *reinterpret_cast<OVec*>(reinterpret_cast<OutT*>(g.C2) + P.ct_off + (size_t)(n - g.split) * P.ldct + r) = v;
+            }
+          }
+        }
+      return;
     }
+  }
+
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+    if (n >= P.n_out) continue;
+    float bias = 0.f;
+    if (EPI != EPI_SCORE && g.bias) bias = (float)reinterpret_cast<const WT*>(g.bias)[n];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = r0 + wm * (BM / 2) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (r >= P.rows) continue;
+        float v = acc[i][j][e] + bias;
+        if constexpr (EPI == EPI_BIAS || EPI == EPI_RELU || EPI == EPI_QKV) {
+          if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+          reinterpret_cast<OutT*>(g.C)[P.c_off + (size_t)r * P.ldc + n] = (OutT)v;
+        } else if constexpr (EPI == EPI_RESID) {
+          float* c = reinterpret_cast<float*>(g.C) + P.c_off + (size_t)r * P.ldc + n;
+          *c = *c + v;
+        } else {  // EPI_SCORE
+          v = acc[i][j][e] * g.scale;
+          reinterpret_cast<float*>(g.C)[P.c_off + (size_t)r * P.ldc + n] = v;
+          if (g.C2) reinterpret_cast<float*>(g.C2)[P.ct_off + (size_t)n * P.ldct + r] = v;
+        }
+      }
   }
 }
 
 template <typename OpT, typename A0T, typename WT, typename OutT, int EPI>
-static void gemm_go(const GemmArgs& g, const GemmBatch& b, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI>), grid, dim3(256), 0, st, g, b);
+static void gemm_go(const GemmArgs& g, const GemmBatch& b, int max_rows, int max_n, hipStream_t st) {
+  // large problems (several tiles per CU even at 128 x 128): the LDS-efficient shape
+  const long big_tiles = (long)((max_rows + 127) / 128) * ((max_n + 127) / 128) * b.n;
+  if (big_tiles >= 1024) {
+    dim3 grid((max_rows + 127) / 128, (max_n + 127) / 128, b.n);
+    hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 128, 128, 2>), grid, dim3(256), 0, st, g, b);
+  } else {
+    dim3 grid((max_rows + 63) / 64, (max_n + 63) / 64, b.n);
+    hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 64, 64, 8>), grid, dim3(256), 0, st, g, b);
+  }
 }
 
 hipError_t launch_gemm(int op, int a0f, int wd, int outf, int epi, const GemmArgs& g,
                        const GemmBatch& b, int max_rows, int max_n, hipStream_t st) {
   if (max_rows <= 0 || max_n <= 0 || b.n <= 0) return hipSuccess;
   if (g.K % 8 || g.K0 % 8) return hipErrorInvalidValue;
-  dim3 grid((max_rows + 63) / 64, (max_n + 63) / 64, b.n);
+  if (epi == EPI_QKV && g.split % 128) return hipErrorInvalidValue;  // V columns start on a tile edge
+#define SG_GO(O, A, W, OUT, E) gemm_go<O, A, W, OUT, E>(g, b, max_rows, max_n, st)
   // The operand-type / epilogue combinations the pipeline uses.
   if (op == SG_F32) {
-    if (wd == SG_F32) {
-      switch (epi) {
-        case EPI_BIAS: gemm_go<float, float, float, float, EPI_BIAS>(g, b, grid, st); break;
-        case EPI_RELU: gemm_go<float, float, float, float, EPI_RELU>(g, b, grid, st); break;
-        case EPI_RESID: gemm_go<float, float, float, float, EPI_RESID>(g, b, grid, st); break;
-        case EPI_QKV: gemm_go<float, float, float, float, EPI_QKV>(g, b, grid, st); break;
-        case EPI_SCORE: gemm_go<float, float, float, float, EPI_SCORE>(g, b, grid, st); break;
-        default: return hipErrorInvalidValue;
-      }
-    } else {  // fp32 encoder on a bf16 blob
-      switch (epi) {
-        case EPI_RELU: gemm_go<float, float, bf16, float, EPI_RELU>(g, b, grid, st); break;
-        case EPI_RESID: gemm_go<float, float, bf16, float, EPI_RESID>(g, b, grid, st); break;
-        default: return hipErrorInvalidValue;
-      }
+    if (wd != SG_F32) return hipErrorInvalidValue;
+    switch (epi) {
+      case EPI_BIAS: SG_GO(float, float, float, float, EPI_BIAS); break;
+      case EPI_RELU: SG_GO(float, float, float, float, EPI_RELU); break;
+      case EPI_RESID: SG_GO(float, float, float, float, EPI_RESID); break;
+      case EPI_QKV: SG_GO(float, float, float, float, EPI_QKV); break;
+      case EPI_SCORE: SG_GO(float, float, float, float, EPI_SCORE); break;
+      default: return hipErrorInvalidValue;
     }
   } else {
     if (wd != SG_BF16) return hipErrorInvalidValue;
     if (a0f) {
       switch (epi) {
-        case EPI_QKV: gemm_go<bf16, float, bf16, bf16, EPI_QKV>(g, b, grid, st); break;
-        case EPI_RELU: gemm_go<bf16, float, bf16, bf16, EPI_RELU>(g, b, grid, st); break;
+        case EPI_QKV: SG_GO(bf16, float, bf16, bf16, EPI_QKV); break;
+        case EPI_RELU: SG_GO(bf16, float, bf16, bf16, EPI_RELU); break;
         case EPI_BIAS:
-          if (outf) gemm_go<bf16, float, bf16, float, EPI_BIAS>(g, b, grid, st);
-          else gemm_go<bf16, float, bf16, bf16, EPI_BIAS>(g, b, grid, st);
+          if (outf) SG_GO(bf16, float, bf16, float, EPI_BIAS);
+          else SG_GO(bf16, float, bf16, bf16, EPI_BIAS);
           break;
         default: return hipErrorInvalidValue;
       }
     } else {
       switch (epi) {
-        case EPI_BIAS: gemm_go<bf16, bf16, bf16, bf16, EPI_BIAS>(g, b, grid, st); break;
-        case EPI_RESID: gemm_go<bf16, bf16, bf16, float, EPI_RESID>(g, b, grid, st); break;
+        case EPI_BIAS: SG_GO(bf16, bf16, bf16, bf16, EPI_BIAS); break;
+        case EPI_RESID: SG_GO(bf16, bf16, bf16, float, EPI_RESID); break;
         default: return hipErrorInvalidValue;
       }
     }
   }
+#undef SG_GO
   return hipGetLastError();
 }
 
