@@ -82,6 +82,8 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--batch", type=int, default=0,
                     help="also time sg_match_batch on this many 1024x1024 pairs per call")
+    ap.add_argument("--sinkhorn", choices=["auto", "two", "one"], default="auto",
+                    help="Sinkhorn schedule (default: chosen by problem size)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="before the steps, copy this many MiB with a plain device copy (counter scaling)")
     args = ap.parse_args()
@@ -106,7 +108,7 @@ def main():
     t = [torch.from_numpy(pair[k]).to(dev) for k in keys]
     img = (*pair["image_size0"], *pair["image_size1"])
     M, N = cfg.M, cfg.N
-    ws = torch.empty(sg.workspace_size(W, M, N, 1), dtype=torch.uint8, device=dev)
+    ws = torch.empty(sg.workspace_size(W, M, N, 1) + 4 * M * N, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     if args.calibrate_copy:
@@ -122,7 +124,7 @@ def main():
             "scores0": torch.empty(M, dtype=torch.float32, device=dev)}
 
     def step(**kw):
-        return sg.sg_match(*t, W, cfg.L, cfg.T, image_size=img, workspace=ws, out=bufs, **kw)
+        return sg.sg_match(*t, W, cfg.L, cfg.T, image_size=img, workspace=ws, out=bufs, sinkhorn=args.sinkhorn, **kw)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -205,13 +207,13 @@ def main():
         pairs = [synth.make_pair(cfg, seed=synth.INPUT_SEED_BASE + 100 + i) for i in range(Bn)]
         bt = {k: torch.from_numpy(np.stack([p[k] for p in pairs])).to(dev) for k in keys}
         Ms, Ns = [M] * Bn, [N] * Bn
-        wsb = torch.empty(sg.workspace_size(W, M, N, Bn), dtype=torch.uint8, device=dev)
+        wsb = torch.empty(sg.workspace_size(W, M, N, Bn) + 4 * Bn * M * N, dtype=torch.uint8, device=dev)
         bbufs = {"matches0": torch.empty((Bn, M), dtype=torch.int32, device=dev),
                  "scores0": torch.empty((Bn, M), dtype=torch.float32, device=dev)}
 
         def bstep():
             return sg.sg_match_batch(Ms, Ns, *[bt[k] for k in keys], W, cfg.L, cfg.T, image_size=img,
-                                     workspace=wsb, want_matches1=False)
+                                     workspace=wsb, want_matches1=False, sinkhorn=args.sinkhorn)
         for _ in range(max(2, args.warmup)):
             bstep()
         torch.cuda.synchronize()

@@ -131,6 +131,17 @@ typedef struct {
 
 /* sg_opts.flags: run eagerly instead of replaying the captured HIP graph. */
 #define SG_FLAG_NO_GRAPH 1
+/* sg_opts.flags: Sinkhorn schedule.  By default a call whose score matrices
+ * total at most SG_TWO_SWEEP_MAX_BYTES runs two sweeps per iteration (rows
+ * of Z, then rows of its transpose, which the score GEMM also writes) and a
+ * larger one reads Z once per iteration (row update plus per-block column
+ * partials, then a column reduction).  Both compute the same iteration of
+ * the page's algorithm; these flags force one schedule (setting both is
+ * SG_ERR_INVALID_ARG).  A forced two-sweep schedule above the threshold
+ * needs a workspace beyond sg_workspace_size(). */
+#define SG_FLAG_SINKHORN_TWO_SWEEP 2
+#define SG_FLAG_SINKHORN_ONE_SWEEP 4
+#define SG_TWO_SWEEP_MAX_BYTES (48u << 20)
 
 /* Number of tensors in the blob (the alpha scalar counts as one). */
 int32_t sg_weights_count(const sg_weights* w);

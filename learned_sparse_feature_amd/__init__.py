@@ -144,11 +144,20 @@ def make_events(n: int):
     return evs
 
 
+_SINKHORN_FLAGS = {"auto": 0, "two": _lib.SG_FLAG_SINKHORN_TWO_SWEEP, "one": _lib.SG_FLAG_SINKHORN_ONE_SWEEP}
+
+
+def _transposed_extra(sinkhorn, B, M, N):
+    """Workspace bytes beyond workspace_size() for a forced two-sweep schedule
+    (the transposed scores, [N][ld4(M)] fp32 per pair)."""
+    return B * N * ((M + 3) // 4 * 4) * 4 if sinkhorn == "two" else 0
+
+
 def _opts(device, *, threshold=0.0, image_size=None, workspace=None, ws_bytes=0, m1=None, s1=None,
           fA=None, fB=None, logP=None, logP_ld=0, stage_events=None, timed_kernel=SG_K_NONE,
-          kernel_events=None, stream=None, graph=True):
+          kernel_events=None, stream=None, graph=True, sinkhorn="auto"):
     o = SgOpts()
-    o.flags = 0 if graph else _lib.SG_FLAG_NO_GRAPH
+    o.flags = (0 if graph else _lib.SG_FLAG_NO_GRAPH) | _SINKHORN_FLAGS[sinkhorn]
     s = stream if stream is not None else torch.cuda.current_stream(device)
     o.stream = s.cuda_stream
     if workspace is not None:
@@ -183,10 +192,12 @@ def _opts(device, *, threshold=0.0, image_size=None, workspace=None, ws_bytes=0,
 def sg_match(kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int, T: int, *,
              threshold: float = 0.0, image_size=None, want_matches1=True, want_logP=False,
              want_desc=False, workspace=None, stage_events=None, timed_kernel=SG_K_NONE,
-             kernel_events=None, stream=None, graph=True, out: Optional[dict] = None) -> dict:
+             kernel_events=None, stream=None, graph=True, out: Optional[dict] = None,
+             sinkhorn: str = "auto") -> dict:
     """One pair.  kpts [n][2] (pixels if image_size=(wA, hA, wB, hB) is given),
     desc [n][D], conf [n]: float32 CUDA tensors.  Returns device tensors;
-    `out` may supply them (same keys) so that repeated calls reuse buffers."""
+    `out` may supply them (same keys) so that repeated calls reuse buffers.
+    sinkhorn: "auto", or "two" / "one" to force a Sinkhorn schedule."""
     dev = descA.device
     M, N, D = kptsA.shape[0], kptsB.shape[0], weights.D
     for t, nm, shp in ((kptsA, "kptsA", (M, 2)), (descA, "descA", (M, D)), (confA, "confA", (M,)),
@@ -212,12 +223,12 @@ def sg_match(kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int,
             if k in out:
                 _check_tensor(out[k], k, dt_, shp)
     if workspace is None:
-        workspace = _workspace(dev, workspace_size(weights, M, N, 1))
+        workspace = _workspace(dev, workspace_size(weights, M, N, 1) + _transposed_extra(sinkhorn, 1, M, N))
     o, keep, count = _opts(dev, threshold=threshold, image_size=image_size, workspace=workspace,
                            m1=out.get("matches1"), s1=out.get("scores1"), fA=out.get("f0"),
                            fB=out.get("f1"), logP=out.get("logP"), logP_ld=N + 1,
                            stage_events=stage_events, timed_kernel=timed_kernel,
-                           kernel_events=kernel_events, stream=stream, graph=graph)
+                           kernel_events=kernel_events, stream=stream, graph=graph, sinkhorn=sinkhorn)
     st = lib().sg_match(_ptr(kptsA), _ptr(descA), _ptr(confA), M, _ptr(kptsB), _ptr(descB), _ptr(confB), N,
                         weights.ref, L, T, _ptr(out["matches0"]), _ptr(out["scores0"]), C.byref(o))
     _lib.check(st, "sg_match")
@@ -228,7 +239,7 @@ def sg_match(kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int,
 def sg_match_batch(M, N, kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int, T: int, *,
                    threshold: float = 0.0, image_size=None, want_matches1=True, want_logP=False,
                    want_desc=False, workspace=None, stage_events=None, timed_kernel=SG_K_NONE,
-                   kernel_events=None, stream=None, graph=True) -> dict:
+                   kernel_events=None, stream=None, graph=True, sinkhorn: str = "auto") -> dict:
     """B padded pairs: kptsA [B][Mpad][2], descA [B][Mpad][D], confA [B][Mpad] (and B
     likewise); M, N: sequences of the true counts."""
     dev = descA.device
@@ -249,12 +260,12 @@ def sg_match_batch(M, N, kptsA, descA, confA, kptsB, descB, confB, weights: Weig
         out["f0"] = torch.zeros((B, Mpad, D), dtype=torch.float32, device=dev)
         out["f1"] = torch.zeros((B, Npad, D), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = _workspace(dev, workspace_size(weights, Mpad, Npad, B))
+        workspace = _workspace(dev, workspace_size(weights, Mpad, Npad, B) + _transposed_extra(sinkhorn, B, Mpad, Npad))
     o, keep, count = _opts(dev, threshold=threshold, image_size=image_size, workspace=workspace,
                            m1=out.get("matches1"), s1=out.get("scores1"), fA=out.get("f0"),
                            fB=out.get("f1"), logP=out.get("logP"), logP_ld=Npad + 1,
                            stage_events=stage_events, timed_kernel=timed_kernel,
-                           kernel_events=kernel_events, stream=stream, graph=graph)
+                           kernel_events=kernel_events, stream=stream, graph=graph, sinkhorn=sinkhorn)
     st = lib().sg_match_batch(B, Mpad, Npad, Ma, Na, _ptr(kptsA), _ptr(descA), _ptr(confA), _ptr(kptsB),
                               _ptr(descB), _ptr(confB), weights.ref, L, T, _ptr(out["matches0"]),
                               _ptr(out["scores0"]), C.byref(o))
@@ -302,7 +313,8 @@ def sg_stage_project(x, weights: Weights) -> torch.Tensor:
 
 
 def sg_stage_match(fA, fB, alpha: float, T: int, *, threshold: float = 0.0, want_logP=True,
-                   workspace=None, stage_events=None, timed_kernel=SG_K_NONE, kernel_events=None) -> dict:
+                   workspace=None, stage_events=None, timed_kernel=SG_K_NONE, kernel_events=None,
+                   sinkhorn: str = "auto") -> dict:
     """Scores, dustbin, T Sinkhorn iterations and extraction from matching descriptors."""
     M, N, D = fA.shape[0], fB.shape[0], fA.shape[1]
     _check_tensor(fA, "fA", torch.float32, (M, D))
@@ -315,10 +327,11 @@ def sg_stage_match(fA, fB, alpha: float, T: int, *, threshold: float = 0.0, want
     if want_logP:
         out["logP"] = torch.empty((M + 1, N + 1), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = _workspace(dev, int(lib().sg_stage_match_workspace_size(M, N, D)))
+        workspace = _workspace(dev, int(lib().sg_stage_match_workspace_size(M, N, D))
+                               + _transposed_extra(sinkhorn, 1, M, N))
     o, keep, count = _opts(dev, threshold=threshold, workspace=workspace, m1=out["matches1"], s1=out["scores1"],
                            logP=out.get("logP"), logP_ld=N + 1, stage_events=stage_events,
-                           timed_kernel=timed_kernel, kernel_events=kernel_events)
+                           timed_kernel=timed_kernel, kernel_events=kernel_events, sinkhorn=sinkhorn)
     _lib.check(lib().sg_stage_match(_ptr(fA), M, _ptr(fB), N, D, float(alpha), T, _ptr(out["matches0"]),
                                     _ptr(out["scores0"]), C.byref(o)), "sg_stage_match")
     out["n_kernel_launches"] = count.value

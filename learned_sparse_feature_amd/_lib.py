@@ -14,6 +14,8 @@ SG_MAX_BATCH = 64
 SG_N_STAGE_EVENTS = 6
 SG_K_NONE, SG_K_GEMM, SG_K_ATTENTION, SG_K_SINKHORN = 0, 1, 2, 3
 SG_FLAG_NO_GRAPH = 1
+SG_FLAG_SINKHORN_TWO_SWEEP = 2
+SG_FLAG_SINKHORN_ONE_SWEEP = 4
 
 STATUS_NAMES = {0: "SG_OK", -1: "SG_ERR_INVALID_ARG", -2: "SG_ERR_UNSUPPORTED", -3: "SG_ERR_WEIGHTS",
                 -4: "SG_ERR_WORKSPACE", -5: "SG_ERR_HIP"}

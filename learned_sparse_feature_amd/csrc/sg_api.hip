@@ -122,11 +122,11 @@ sg_status check_weights(const sg_weights* w, WLayout* out) {
 // ---------------------------------------------------------- workspace layout
 
 struct WsLayout {
-  size_t X, H0, H1, QK, VT, MB, M2, HB, F, Z, ZT, U, V, IDX0, VAL0, IDX1, total;
+  size_t X, H0, H1, QK, VT, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, IDX1, total;
   int ldvt, ldqk;
 };
 
-WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, long uf, long vf, long na,
+WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, long pf, long pd, long uf, long vf,
                        long nb) {
   WsLayout L;
   // row strides are kept off powers of two (+64 / +16 bytes) so that the
@@ -146,19 +146,21 @@ WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, l
   L.F = take((size_t)R * D * 4);
   L.Z = take((size_t)zf * 4);
   L.ZT = take((size_t)ztf * 4);
+  L.P = take((size_t)pf * 4);
+  L.PD = take((size_t)pd * 4);
+  L.PV = take((size_t)pf * 4);
+  L.PI = take((size_t)pf * 4);
   L.U = take((size_t)uf * 4);
   L.V = take((size_t)vf * 4);
-  L.IDX0 = take((size_t)na * 4);
-  L.VAL0 = take((size_t)na * 4);
   L.IDX1 = take((size_t)nb * 4);
   L.total = o;
   return L;
 }
 
-WsLayout ws_layout(const sg_weights* w, long R, long zf, long ztf, long uf, long vf, long na, long nb) {
+WsLayout ws_layout(const sg_weights* w, long R, long zf, long ztf, long pf, long pd, long uf, long vf, long nb) {
   int maxw = 0;
   for (int i = 0; i < w->n_enc; ++i) maxw = std::max(maxw, w->enc[i]);
-  return ws_layout_raw(w->D, w->dtype == SG_BF16 ? 2 : 4, maxw, R, zf, ztf, uf, vf, na, nb);
+  return ws_layout_raw(w->D, w->dtype == SG_BF16 ? 2 : 4, maxw, R, zf, ztf, pf, pd, uf, vf, nb);
 }
 
 // ----------------------------------------------------------- library workspace
@@ -232,6 +234,7 @@ struct Timer {
 
 struct Problem {
   int B = 1, Mpad = 0, Npad = 0;
+  int flags = 0;  // SG_FLAG_*
   std::vector<int> M, N;
   const float *kp[2] = {nullptr, nullptr}, *cf[2] = {nullptr, nullptr}, *de[2] = {nullptr, nullptr};
   float img[4] = {0, 0, 0, 0};
@@ -241,7 +244,8 @@ struct Plan {
   SegTable seg;
   PairTable pt;
   int R = 0;
-  long zf = 0, ztf = 0, uf = 0, vf = 0, na = 0, nb = 0;
+  long zf = 0, ztf = 0, pf = 0, pd = 0, uf = 0, vf = 0, nb = 0;
+  bool two_sweep = false;  // Sinkhorn schedule (see SG_FLAG_SINKHORN_*)
   int ru = 0, rv = 0;  // flattened u rows (sum of M+1) and v rows (sum of N+1)
   std::vector<int> rowB;
 };
@@ -252,8 +256,9 @@ void make_plan(const Problem& p, Plan& pl) {
   pl.rowB.assign(p.B, 0);
   pl.uf = pl.vf = 0;
   int R = 0;
-  long zf = 0, ztf = 0;
+  long zf = 0, ztf = 0, pf = 0;
   pl.pt.n_pairs = p.B;
+  pl.pt.rb = sink_rows_per_block(p.M.data(), p.N.data(), p.B);
   pl.seg.n_seg = 2 * p.B;
   for (int b = 0; b < p.B; ++b) {
     const int M = p.M[b], N = p.N[b];
@@ -264,9 +269,14 @@ void make_plan(const Problem& p, Plan& pl) {
     pl.rowB[b] = R;
     R += round32(N);
     pl.pt.M[b] = M; pl.pt.N[b] = N; pl.pt.rowA[b] = pl.seg.row0[sa];
-    pl.pt.z_off[b] = (int)zf; pl.pt.zt_off[b] = (int)ztf;
+    pl.pt.z_off[b] = (int)zf;
+    pl.pt.zt_off[b] = (int)ztf;
+    pl.pt.p_off[b] = (int)pf;
     zf += (long)M * ld4(N);
     ztf += (long)N * ld4(M);
+    const int G = (M + 1 + pl.pt.rb - 1) / pl.pt.rb;
+    pf += (long)G * ld4(N);
+    pl.pt.gpre[b + 1] = pl.pt.gpre[b] + G;
     pl.pt.upre[b + 1] = pl.pt.upre[b] + M + 1;
     pl.pt.vpre[b + 1] = pl.pt.vpre[b] + N + 1;
     pl.pt.uoff[b] = (int)pl.uf;
@@ -275,9 +285,12 @@ void make_plan(const Problem& p, Plan& pl) {
     pl.vf += ld4(N + 1);
   }
   pl.R = R;
-  pl.zf = zf; pl.ztf = ztf;
+  pl.zf = zf; pl.pf = pf; pl.pd = pl.pt.gpre[p.B];
+  pl.two_sweep = (p.flags & SG_FLAG_SINKHORN_TWO_SWEEP) ||
+                 (!(p.flags & SG_FLAG_SINKHORN_ONE_SWEEP) && zf * 4 <= (long)SG_TWO_SWEEP_MAX_BYTES);
+  pl.ztf = pl.two_sweep ? ztf : 0;
   pl.ru = pl.pt.upre[p.B]; pl.rv = pl.pt.vpre[p.B];
-  pl.na = pl.ru - p.B; pl.nb = pl.rv - p.B;
+  pl.nb = pl.rv - p.B;
 }
 
 template <class T>
@@ -421,19 +434,21 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
   const float log2e = 1.4426950408889634f;
   float* Z = reinterpret_cast<float*>(ws + wl.Z);
   float* ZT = reinterpret_cast<float*>(ws + wl.ZT);
+  float* P = reinterpret_cast<float*>(ws + wl.P);
+  float* Pd = reinterpret_cast<float*>(ws + wl.PD);
+  float* PV = reinterpret_cast<float*>(ws + wl.PV);
+  int* PI = reinterpret_cast<int*>(ws + wl.PI);
   float* U = reinterpret_cast<float*>(ws + wl.U);
   float* V = reinterpret_cast<float*>(ws + wl.V);
-  int* idx0 = reinterpret_cast<int*>(ws + wl.IDX0);
-  float* val0 = reinterpret_cast<float*>(ws + wl.VAL0);
   int* idx1 = reinterpret_cast<int*>(ws + wl.IDX1);
   const float alpha2 = alpha * log2e;
-  // S * log2(e) / sqrt(D) into Z and ZT
+  // S * log2(e) / sqrt(D) into Z (and its transpose into ZT for two sweeps)
   {
     GemmArgs g;
     memset(&g, 0, sizeof(g));
     g.A0 = F; g.lda0 = D; g.K0 = D; g.K = D;
     g.W = F; g.ldw = D;
-    g.C = Z; g.C2 = ZT;
+    g.C = Z; g.C2 = pl.two_sweep ? ZT : nullptr;
     g.scale = log2e / sqrtf((float)D);
     GemmBatch b;
     memset(&b, 0, sizeof(b));
@@ -448,19 +463,45 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
     HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(SG_F32, 1, SG_F32, 1, EPI_SCORE, g, b, mr, mn, st); }), "score GEMM");
   }
   tm.stage(SG_EV_SCORES);
-  // T iterations: u = log mu - lse_j(Z + v); v = log nu - lse_i(Z + u)
-  for (int it = 0; it < T; ++it) {
-    HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(Z, pl.pt, 0, it == 0 ? nullptr : V, U, alpha2, alpha_dev, pl.ru, st); }), "sinkhorn rows");
-    HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(ZT, pl.pt, 1, U, V, alpha2, alpha_dev, pl.rv, st); }), "sinkhorn cols");
-  }
-  if (T == 0) {
-    HIPCHK(launch_fill_f32(U, 0.f, (int)pl.uf, st), "zero u");
-    HIPCHK(launch_fill_f32(V, 0.f, (int)pl.vf, st), "zero v");
+  if (pl.two_sweep) {
+    // T iterations: u = log mu - lse_j(Z + v) over the rows of Z, then
+    // v = log nu - lse_i(Z + u) over the rows of ZT
+    for (int it = 0; it < T; ++it) {
+      HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(Z, pl.pt, 0, it == 0 ? nullptr : V, U, alpha2, alpha_dev, pl.ru, st); }),
+             "sinkhorn rows");
+      HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(ZT, pl.pt, 1, U, V, alpha2, alpha_dev, pl.rv, st); }),
+             "sinkhorn cols");
+    }
+    if (T == 0) {
+      HIPCHK(launch_fill_f32(U, 0.f, (int)pl.uf, st), "zero u");
+      HIPCHK(launch_fill_f32(V, 0.f, (int)pl.vf, st), "zero v");
+    }
+    HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, st), "column argmax");
+  } else {
+    // T iterations: u = log mu - lse_j(Z + v) with the column partials of
+    // Z + u in the same pass; then v = log nu - lse over the partials.  The
+    // last pass also leaves the per-block column argmax of Z + u.
+    for (int it = 0; it < T; ++it) {
+      const bool last = it == T - 1;
+      HIPCHK(tm.run(SG_K_SINKHORN, [&] {
+               return launch_sink_rows(Z, pl.pt, it == 0 ? nullptr : V, U, P, Pd, last ? PV : nullptr,
+                                       last ? PI : nullptr, alpha2, alpha_dev, 1, st);
+             }), "sinkhorn rows");
+      HIPCHK(tm.run(SG_K_SINKHORN, [&] {
+               return launch_sink_cols(pl.pt, P, Pd, V, last ? PV : nullptr, last ? PI : nullptr, idx1, 1, p.Npad,
+                                       out.m1, out.s1, st);
+             }), "sinkhorn cols");
+    }
+    if (T == 0) {
+      HIPCHK(launch_fill_f32(U, 0.f, (int)pl.uf, st), "zero u");
+      HIPCHK(launch_fill_f32(V, 0.f, (int)pl.vf, st), "zero v");
+      HIPCHK(launch_sink_rows(Z, pl.pt, nullptr, U, P, Pd, PV, PI, alpha2, alpha_dev, 0, st), "column argmax");
+      HIPCHK(launch_sink_cols(pl.pt, P, Pd, V, PV, PI, idx1, 0, p.Npad, out.m1, out.s1, st), "column argmax");
+    }
   }
   tm.stage(SG_EV_SINKHORN);
-  HIPCHK(launch_argmax(Z, ZT, pl.pt, U, V, idx0, val0, idx1, (int)pl.na, (int)pl.nb, st), "argmax");
-  HIPCHK(launch_finalize(pl.pt, idx0, val0, idx1, U, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, st),
-         "finalize");
+  HIPCHK(launch_sink_extract(Z, pl.pt, U, V, idx1, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, st),
+         "extract");
   if (out.logP)
     HIPCHK(launch_write_logp(Z, pl.pt, U, V, alpha2, alpha_dev, out.logP, out.logP_ld, out.logP_stride, pl.ru, st),
            "logP");
@@ -471,6 +512,8 @@ sg_status check_opts(const sg_opts* o) {
   if (!o) return SG_OK;
   if (o->workspace && o->workspace_bytes == 0) return fail(SG_ERR_WORKSPACE, "workspace given with 0 bytes");
   if (o->kernel_events && o->n_kernel_events < 0) return fail(SG_ERR_INVALID_ARG, "n_kernel_events < 0");
+  if ((o->flags & SG_FLAG_SINKHORN_TWO_SWEEP) && (o->flags & SG_FLAG_SINKHORN_ONE_SWEEP))
+    return fail(SG_ERR_INVALID_ARG, "both Sinkhorn schedules forced");
   return SG_OK;
 }
 
@@ -565,6 +608,7 @@ std::string call_key(int kind, const Problem& p, const sg_weights* w, int Lst, i
   }
   put(k, Lst); put(k, T); put(k, out);
   put(k, o ? o->match_threshold : 0.f);
+  put(k, o ? o->flags : 0);
   put(k, ws);
   return k;
 }
@@ -576,7 +620,7 @@ sg_status run_full(const Problem& p, const sg_weights* w, const WLayout& L, int 
                    const Outputs& out, const sg_opts* o) {
   Plan pl;
   make_plan(p, pl);
-  WsLayout wl = ws_layout(w, pl.R, pl.zf, pl.ztf, pl.uf, pl.vf, pl.na, pl.nb);
+  WsLayout wl = ws_layout(w, pl.R, pl.zf, pl.ztf, pl.pf, pl.pd, pl.uf, pl.vf, pl.nb);
   void* wsp = nullptr;
   sg_status s = get_workspace(o, wl.total, &wsp);
   if (s != SG_OK) return s;
@@ -645,15 +689,23 @@ size_t sg_workspace_size(const sg_weights* w, int32_t Mmax, int32_t Nmax, int32_
   if (check_config(w) != SG_OK || Mmax < 0 || Nmax < 0 || batch < 1) return 0;
   const long B = batch;
   const long R = B * (round32(Mmax) + round32(Nmax));
-  WsLayout wl = ws_layout(w, R, B * Mmax * ld4(Nmax), B * Nmax * ld4(Mmax), B * ld4(Mmax + 1), B * ld4(Nmax + 1),
-                          B * Mmax, B * Nmax);
+  // column partials: at most ceil((Mmax+1)/4) row blocks per pair
+  // the transposed scores exist only for the two-sweep schedule, which the
+  // default rule picks for at most SG_TWO_SWEEP_MAX_BYTES of Z (ZT exceeds Z
+  // by at most its row padding)
+  const long ztf = std::min(B * Nmax * ld4(Mmax), (long)(SG_TWO_SWEEP_MAX_BYTES / 4) + 3 * B * Nmax);
+  WsLayout wl = ws_layout(w, R, B * Mmax * ld4(Nmax), ztf, B * ((Mmax + 4) / 4) * ld4(Nmax), B * ((Mmax + 4) / 4),
+                          B * ld4(Mmax + 1), B * ld4(Nmax + 1), B * Nmax);
   return wl.total;
 }
 
 size_t sg_stage_match_workspace_size(int32_t M, int32_t N, int32_t D) {
   if (M < 0 || N < 0 || D <= 0) return 0;
   const long R = round32(M) + round32(N);
-  return ws_layout_raw(D, 4, 0, R, (long)M * ld4(N), (long)N * ld4(M), ld4(M + 1), ld4(N + 1), M, N).total;
+  const long ztf = std::min((long)N * ld4(M), (long)(SG_TWO_SWEEP_MAX_BYTES / 4) + 3L * N);
+  return ws_layout_raw(D, 4, 0, R, (long)M * ld4(N), ztf, (long)((M + 4) / 4) * ld4(N), (M + 4) / 4, ld4(M + 1),
+                       ld4(N + 1), N)
+      .total;
 }
 
 sg_status sg_match(const float* kptsA, const float* descA, const float* confA, int32_t M,
@@ -680,6 +732,7 @@ sg_status sg_match(const float* kptsA, const float* descA, const float* confA, i
     return SG_OK;
   }
   Problem p;
+  p.flags = opts ? opts->flags : 0;
   p.B = 1; p.Mpad = M; p.Npad = N;
   p.M = {M}; p.N = {N};
   p.kp[0] = kptsA; p.cf[0] = confA; p.de[0] = descA;
@@ -717,6 +770,7 @@ sg_status sg_match_batch(int32_t B, int32_t Mpad, int32_t Npad, const int32_t* M
   if (!kptsA || !descA || !confA || !kptsB || !descB || !confB) return fail(SG_ERR_INVALID_ARG, "input pointer is NULL");
   if (opts && opts->out_logP && opts->logP_ld < Npad + 1) return fail(SG_ERR_INVALID_ARG, "logP_ld < Npad+1");
   Problem p;
+  p.flags = opts ? opts->flags : 0;
   p.B = B; p.Mpad = Mpad; p.Npad = Npad;
   p.M.assign(M, M + B); p.N.assign(N, N + B);
   p.kp[0] = kptsA; p.cf[0] = confA; p.de[0] = descA;
@@ -743,13 +797,14 @@ sg_status sg_stage_encode(const float* kpts, const float* conf, const float* des
   if (n == 0) return SG_OK;
   if (!kpts || !conf || !desc || !x_out) return fail(SG_ERR_INVALID_ARG, "NULL pointer");
   Problem p;
+  p.flags = opts ? opts->flags : 0;
   p.B = 1; p.Mpad = n; p.Npad = 0; p.M = {n}; p.N = {0};
   p.kp[0] = kpts; p.cf[0] = conf; p.de[0] = desc;
   p.kp[1] = kpts; p.cf[1] = conf; p.de[1] = desc;
   p.img[0] = image_w; p.img[1] = image_h;
   Plan pl;
   make_plan(p, pl);
-  WsLayout wl = ws_layout(weights, pl.R, 0, 0, 0, 0, 0, 0);
+  WsLayout wl = ws_layout(weights, pl.R, 0, 0, 0, 0, 0, 0, 0);
   void* wsp;
   if ((s = get_workspace(opts, wl.total, &wsp)) != SG_OK) return s;
   hipStream_t st = stream_of(opts);
@@ -772,10 +827,11 @@ sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weig
   if (s0 < 0 || s1 < s0 || s1 > 2 * weights->L_max) return fail(SG_ERR_INVALID_ARG, "stage range [%d, %d) invalid", s0, s1);
   if ((M && !xA) || (N && !xB)) return fail(SG_ERR_INVALID_ARG, "NULL state pointer");
   Problem p;
+  p.flags = opts ? opts->flags : 0;
   p.B = 1; p.Mpad = M; p.Npad = N; p.M = {M}; p.N = {N};
   Plan pl;
   make_plan(p, pl);
-  WsLayout wl = ws_layout(weights, pl.R, 0, 0, 0, 0, 0, 0);
+  WsLayout wl = ws_layout(weights, pl.R, 0, 0, 0, 0, 0, 0, 0);
   void* wsp;
   if ((s = get_workspace(opts, wl.total, &wsp)) != SG_OK) return s;
   char* ws = reinterpret_cast<char*>(wsp);
@@ -829,11 +885,12 @@ sg_status sg_stage_match(const float* fA, int32_t M, const float* fB, int32_t N,
     return SG_OK;
   }
   Problem p;
+  p.flags = opts ? opts->flags : 0;
   p.B = 1; p.Mpad = M; p.Npad = N; p.M = {M}; p.N = {N};
   Plan pl;
   make_plan(p, pl);
   // f_A and f_B are staged into the compact F rows of the workspace
-  WsLayout wl = ws_layout_raw(D, 4, 0, pl.R, pl.zf, pl.ztf, pl.uf, pl.vf, pl.na, pl.nb);
+  WsLayout wl = ws_layout_raw(D, 4, 0, pl.R, pl.zf, pl.ztf, pl.pf, pl.pd, pl.uf, pl.vf, pl.nb);
   void* wsp;
   if ((s = get_workspace(opts, wl.total, &wsp)) != SG_OK) return s;
   char* ws = reinterpret_cast<char*>(wsp);

@@ -29,13 +29,65 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
+// Cross-lane moves inside each row of 16 lanes (DPP): quad_perm [1,0,3,2]
+// and [2,3,0,1] swap neighbours and pairs, row_half_mirror (0x141) and
+// row_mirror (0x140) reverse 8- and 16-lane groups.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Wave-wide reduction, result in every lane: four DPP steps leave each row
+// of 16 lanes holding its row's result, then the four rows are combined from
+// scalar reads of lanes 0, 16, 32, 48.  Call with the whole wave active.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp_f<kDppXor1>(v));
+  v = op(v, dpp_f<kDppXor2>(v));
+  v = op(v, dpp_f<kDppHalfMirror>(v));
+  v = op(v, dpp_f<kDppMirror>(v));
+  return op(op(lane_f(v, 0), lane_f(v, 16)), op(lane_f(v, 32), lane_f(v, 48)));
+}
 __device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
+}
+
+// (value, index) argmax over the wave: the larger value wins, the lower
+// index among equal values.  Result in every lane.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = dpp_f<CTRL>(v);
+  const int oi = dpp_i<CTRL>(i);
+  argmax_merge(v, i, ov, oi);
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<kDppXor1>(v, i);
+  argmax_step<kDppXor2>(v, i);
+  argmax_step<kDppHalfMirror>(v, i);
+  argmax_step<kDppMirror>(v, i);
+  float bv = lane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) argmax_merge(bv, bi, lane_f(v, r), __builtin_amdgcn_readlane(i, r));
+  v = bv;
+  i = bi;
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {

@@ -29,12 +29,16 @@ struct SegTable {
 // flattened over the pairs at upre[b] and vpre[b].
 struct PairTable {
   int n_pairs;
+  int rb;                                          // Sinkhorn rows per workgroup (4 or 8)
   int M[SG_MAX_BATCH], N[SG_MAX_BATCH];
-  int rowA[SG_MAX_BATCH];                         // compact row of f_A (f_B follows at +M)
-  int z_off[SG_MAX_BATCH], zt_off[SG_MAX_BATCH];  // float offsets of Z and ZT
-  int upre[SG_MAX_BATCH + 1];                     // prefix sums of (M+1): flattened u rows
-  int vpre[SG_MAX_BATCH + 1];                     // prefix sums of (N+1): flattened v rows
-  int uoff[SG_MAX_BATCH], voff[SG_MAX_BATCH];     // storage offsets of u, v (multiples of 4)
+  int rowA[SG_MAX_BATCH];                          // compact row of f_A (f_B follows at +M)
+  int z_off[SG_MAX_BATCH];                         // float offset of Z ([M][ld4(N)])
+  int zt_off[SG_MAX_BATCH];                        // float offset of ZT ([N][ld4(M)]), two-sweep only
+  int p_off[SG_MAX_BATCH];                         // float offset of the column partials ([G][ld4(N)])
+  int upre[SG_MAX_BATCH + 1];                      // prefix sums of (M+1): flattened u rows
+  int vpre[SG_MAX_BATCH + 1];                      // prefix sums of (N+1): flattened v rows
+  int gpre[SG_MAX_BATCH + 1];                      // prefix sums of G = ceil((M+1)/rb): row blocks
+  int uoff[SG_MAX_BATCH], voff[SG_MAX_BATCH];      // storage offsets of u, v (multiples of 4)
 };
 
 __host__ __device__ inline int ld4(int n) { return (n + 3) & ~3; }
@@ -99,15 +103,21 @@ hipError_t launch_gemm(int op_dtype, int a0_is_f32, int w_dtype, int out_is_f32,
 hipError_t launch_attention(int op_dtype, int dh, const AttnArgs& a, const SegTable& seg,
                             int heads, hipStream_t st);
 // alpha_dev (device pointer to the dustbin score) overrides alpha2 when non-null.
-hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const float* w_in,
-                      float* w_out, float alpha2, const float* alpha_dev, int total_rows,
-                      hipStream_t st);
-hipError_t launch_argmax(const float* Z, const float* ZT, const PairTable& pt, const float* u,
-                         const float* v, int* idx0, float* val0, int* idx1, int rowsA, int rowsB,
-                         hipStream_t st);
-hipError_t launch_finalize(const PairTable& pt, const int* idx0, const float* val0,
-                           const int* idx1, const float* u, int Mpad, int Npad, float thr,
-                           int32_t* m0, float* s0, int32_t* m1, float* s1, hipStream_t st);
+// Sinkhorn rows per workgroup (4 or 8) for a batch of pairs.
+int sink_rows_per_block(const int* M, const int* N, int n_pairs);
+hipError_t launch_sink_rows(const float* Z, const PairTable& pt, const float* v_in, float* u_out,
+                            float* P, float* Pd, float* PV, int* PI, float alpha2, const float* alpha_dev,
+                            int update_u, hipStream_t st);
+hipError_t launch_sink_cols(const PairTable& pt, const float* P, const float* Pd, float* v_out, const float* PV,
+                            const int* PI, int* idx1, int write_v, int Npad, int32_t* m1, float* s1,
+                            hipStream_t st);
+hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const float* w_in, float* w_out,
+                      float alpha2, const float* alpha_dev, int total_rows, hipStream_t st);
+hipError_t launch_col_argmax(const float* ZT, const PairTable& pt, const float* u, int* idx1, int Npad,
+                             int32_t* m1, float* s1, hipStream_t st);
+hipError_t launch_sink_extract(const float* Z, const PairTable& pt, const float* u, const float* v,
+                               const int* idx1, int Mpad, int Npad, float thr, int32_t* m0, float* s0,
+                               int32_t* m1, float* s1, hipStream_t st);
 hipError_t launch_write_logp(const float* Z, const PairTable& pt, const float* u, const float* v,
                              float alpha2, const float* alpha_dev, float* logP, int64_t ld,
                              int64_t pair_stride, int total_rows, hipStream_t st);

@@ -1,24 +1,371 @@
 // Log-domain Sinkhorn normalisation and mutual-argmax extraction (gfx950).
 //
 // The couplings are never materialised with their dustbins: Z holds
-// S*log2(e) for the real block and ZT its transpose; the dustbin row, column
-// and corner are the constant alpha*log2(e).  All exponentials and logarithms
-// are base 2.
+// S*log2(e) for the real block of every pair ([M][ld4(N)]); the dustbin row,
+// column and corner are the constant alpha*log2(e).  All exponentials and
+// logarithms are base 2, so u and v below are the dual variables times
+// log2(e).
+//
+// One iteration reads Z once (the two updates of the page's loop are split
+// so that no transposed copy is needed):
+//  * k_sink_rows: a workgroup takes RB = 4*RPW consecutive rows of one pair
+//    (the dustbin row included), each of its four waves RPW whole rows.
+//    Per row, with t = Z + v: m_i = max_j t_ij, e_ij = 2^(t_ij - m_i),
+//    s_i = sum_j e_ij and the row update u_i = log2 mu_i - m_i - log2 s_i.
+//    The block's column partial lse2_{i in block}(Z_ij + u_i) reuses e:
+//    2^(Z_ij + u_i) = e_ij 2^(m_i + u_i) 2^(-v_j) and m_i + u_i =
+//    log2(mu_i / s_i), so relative to W = -log2(M+N) the row weights are
+//    c_i / s_i (c_i = 1, N on the dustbin row) and the partial is
+//    log2(sum_i e_ij c_i / s_i) + W - v_j: one FMA per entry.  A term lost
+//    to underflow of e is below 2^-126, so a sum of at least 2^-100 is exact
+//    to fp32 rounding; a smaller one is recomputed as the plain log-sum-exp
+//    over the block's rows.
+//  * k_sink_cols: v_j = log2 nu_j - lse2_g P[g][j].
+// After the last iteration the per-block column maxima of Z + u (argmax
+// over the real rows) are reduced the same way, and k_sink_extract takes the
+// row argmax, the mutual check, the scores and the threshold.
 #include <algorithm>
 
 #include "sg_device.h"
 
 namespace sg {
 
-// --------------------------------------------------------------- Sinkhorn
+constexpr float kSumFloor = 0x1p-100f;
+
+__device__ __forceinline__ float f4c(const float4& q, int c) {
+  return c == 0 ? q.x : c == 1 ? q.y : c == 2 ? q.z : q.w;
+}
+
+// P: [G][ld4(N)] partials of the real columns, Pd: [G] partials of the
+// dustbin column (flattened over pairs by gpre).  ARG: also the per-block
+// column argmax of Z + u over the real rows into PV / PI.  update_u = 0
+// (no Sinkhorn iteration) takes u = 0 and writes only PV / PI.
+template <int RPW, int NV4, bool ARG>
+__global__ __launch_bounds__(256) void k_sink_rows(const float* __restrict__ Zb, PairTable pt,
+                                                   const float* __restrict__ v_in,
+                                                   float* __restrict__ u_out, float* __restrict__ P,
+                                                   float* __restrict__ Pd, float* __restrict__ PV,
+                                                   int* __restrict__ PI, float alpha2,
+                                                   const float* __restrict__ alpha_dev, int update_u) {
+  constexpr int RB = 4 * RPW;
+  constexpr int NG = 64 * NV4;  // float4 column groups of a row held by one wave
+  __shared__ float4 sm[4][NG];
+  __shared__ float sm_u[RB], sm_d[4];
+  if (alpha_dev) alpha2 = alpha_dev[0] * kLog2e;
+  const int b = find_pair(pt.gpre, pt.n_pairs, blockIdx.x);
+  if (b >= pt.n_pairs) return;
+  const int gb = blockIdx.x - pt.gpre[b];
+  const int M = pt.M[b], N = pt.N[b];
+  const int i0 = gb * RB;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ldz = ld4(N);
+  const float* zp = Zb + pt.z_off[b];
+  const float* vv = v_in ? v_in + pt.voff[b] : nullptr;
+  const float lmn = log2f((float)(M + N));
+
+  float vc[NV4][4];
+#pragma unroll
+  for (int k = 0; k < NV4; ++k) {
+    const int j = 4 * (lane + 64 * k);
+    const float4 q = (vv && j < N) ? *reinterpret_cast<const float4*>(vv + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vc[k][c] = f4c(q, c);
+  }
+  const float vN = vv ? vv[N] : 0.f;
+
+  // ---- row update of the wave's rows; e keeps 2^(t - m)
+  float e[RPW][NV4][4], wgt[RPW];
+  float dT = 0.f;  // lane 0: this wave's dustbin-column partial
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int i = i0 + w * RPW + r;
+    if (i > M) {  // past the dustbin row: no contribution
+      wgt[r] = 0.f;
+#pragma unroll
+      for (int k = 0; k < NV4; ++k)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) e[r][k][c] = 0.f;
+      if (lane == 0) sm_u[w * RPW + r] = -INFINITY;
+      continue;
+    }
+#pragma unroll
+    for (int k = 0; k < NV4; ++k) {
+      const int j = 4 * (lane + 64 * k);
+      float4 q = make_float4(alpha2, alpha2, alpha2, alpha2);
+      if (i < M && j < N) q = *reinterpret_cast<const float4*>(zp + (size_t)i * ldz + j);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) e[r][k][c] = j + c < N ? f4c(q, c) + vc[k][c] : -INFINITY;
+    }
+    float mx = lane == 0 ? alpha2 + vN : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NV4; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx = fmaxf(mx, e[r][k][c]);
+    mx = wave_max(mx);
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV4; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        e[r][k][c] = exp2_fast(e[r][k][c] - mx);
+        s += e[r][k][c];
+      }
+    const float ed = lane == 0 ? exp2_fast(alpha2 + vN - mx) : 0.f;
+    s = wave_sum(s + ed);
+    const float cr = i < M ? 1.f : (float)N;
+    const float ur = log2f(cr) - lmn - mx - log2_fast(s);
+    wgt[r] = cr / s;
+    dT += ed * wgt[r];
+    if (lane == 0) {
+      sm_u[w * RPW + r] = update_u ? ur : 0.f;
+      if (update_u) u_out[pt.uoff[b] + i] = ur;
+    }
+  }
+
+  const size_t pbase = (size_t)pt.p_off[b] + (size_t)gb * ldz;
+  if (update_u) {
+#pragma unroll
+    for (int k = 0; k < NV4; ++k) {
+      float t[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        t[c] = e[0][k][c] * wgt[0];
+#pragma unroll
+        for (int r = 1; r < RPW; ++r) t[c] = fmaf(e[r][k][c], wgt[r], t[c]);
+      }
+      sm[w][lane + 64 * k] = make_float4(t[0], t[1], t[2], t[3]);
+    }
+    if (lane == 0) sm_d[w] = dT;
+  }
+  __syncthreads();
+
+  // exact partial of column jj over the block's rows (jj == N: the dustbin)
+  auto exact = [&](int jj) -> float {
+    float y[RB];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int i = i0 + r;
+      const float z = (i < M && jj < N) ? zp[(size_t)i * ldz + jj] : alpha2;
+      y[r] = i <= M ? z + sm_u[r] : -INFINITY;
+      mx = fmaxf(mx, y[r]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) s += exp2_fast(y[r] - mx);
+    return mx + log2_fast(s);
+  };
+
+  if (update_u) {
+    for (int q = threadIdx.x; q < NG; q += 256) {
+      const int j = 4 * q;
+      if (j >= N) break;
+      const float4 a0 = sm[0][q], a1 = sm[1][q], a2 = sm[2][q], a3 = sm[3][q];
+      const float4 vq = vv ? *reinterpret_cast<const float4*>(vv + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      float o[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float T = (f4c(a0, c) + f4c(a1, c)) + (f4c(a2, c) + f4c(a3, c));
+        if (j + c >= N) o[c] = -INFINITY;
+        else if (T >= kSumFloor) o[c] = log2_fast(T) - lmn - f4c(vq, c);
+        else o[c] = exact(j + c);
+      }
+      *reinterpret_cast<float4*>(P + pbase + j) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    if (threadIdx.x == 0) {
+      const float T = (sm_d[0] + sm_d[1]) + (sm_d[2] + sm_d[3]);
+      Pd[pt.gpre[b] + gb] = T >= kSumFloor ? log2_fast(T) - lmn - vN : exact(N);
+    }
+  }
+
+  if constexpr (ARG) {
+    // column argmax of Z + u over the wave's real rows (lowest row on ties),
+    // then over the four waves (rows ascending with the wave index)
+    __shared__ int4 smi[4][NG];
+    __syncthreads();  // the partial sums in sm have been read
+#pragma unroll
+    for (int k = 0; k < NV4; ++k) {
+      const int j = 4 * (lane + 64 * k);
+      float bv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      int bi[4] = {-1, -1, -1, -1};
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const int i = i0 + w * RPW + r;
+        if (i < M && j < N) {
+          const float4 q = *reinterpret_cast<const float4*>(zp + (size_t)i * ldz + j);
+          const float ua = sm_u[w * RPW + r];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float y = f4c(q, c) + ua;
+            if (y > bv[c]) {
+              bv[c] = y;
+              bi[c] = i;
+            }
+          }
+        }
+      }
+      sm[w][lane + 64 * k] = make_float4(bv[0], bv[1], bv[2], bv[3]);
+      smi[w][lane + 64 * k] = make_int4(bi[0], bi[1], bi[2], bi[3]);
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < NG; q += 256) {
+      const int j = 4 * q;
+      if (j >= N) break;
+      float bv[4];
+      int bi[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bv[c] = f4c(sm[0][q], c);
+        bi[c] = c == 0 ? smi[0][q].x : c == 1 ? smi[0][q].y : c == 2 ? smi[0][q].z : smi[0][q].w;
+      }
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) {
+        const float4 a = sm[ww][q];
+        const int4 ai = smi[ww][q];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float y = f4c(a, c);
+          if (y > bv[c]) {
+            bv[c] = y;
+            bi[c] = c == 0 ? ai.x : c == 1 ? ai.y : c == 2 ? ai.z : ai.w;
+          }
+        }
+      }
+      *reinterpret_cast<float4*>(PV + pbase + j) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+      *reinterpret_cast<int4*>(PI + pbase + j) = make_int4(bi[0], bi[1], bi[2], bi[3]);
+    }
+  }
+}
+
+// Column reduction of the block partials of every pair: v_j = log2 nu_j -
+// lse2_g P[g][j] (write_v), and after the last iteration the column argmax
+// over the real rows (idx1) plus the default (-1 / 0) side-B outputs.
+// A workgroup takes 64 columns of one pair (16 lanes x float4, so that each
+// partial row is read in whole 256-byte runs); its 16 row lanes
+// (threadIdx / 16) take the partial rows g = gl (mod 16).
+__device__ __forceinline__ void set4(float4& a, int c, float v) {
+  if (c == 0) a.x = v;
+  else if (c == 1) a.y = v;
+  else if (c == 2) a.z = v;
+  else a.w = v;
+}
+
+template <bool ARG>
+__global__ __launch_bounds__(256) void k_sink_cols(PairTable pt, const float* __restrict__ P,
+                                                   const float* __restrict__ Pd,
+                                                   float* __restrict__ v_out,
+                                                   const float* __restrict__ PV,
+                                                   const int* __restrict__ PI, int* __restrict__ idx1,
+                                                   int write_v, int Npad, int32_t* __restrict__ m1,
+                                                   float* __restrict__ s1) {
+  constexpr int GL = 16, U = 8;
+  __shared__ float sm_m[GL][64], sm_s[GL][64], sm_b[GL][64];
+  __shared__ int sm_i[GL][64];
+  const int b = blockIdx.y;
+  const int M = pt.M[b], N = pt.N[b];
+  if (blockIdx.x * 64 > N) return;
+  const int G = pt.gpre[b + 1] - pt.gpre[b];
+  const int cl = threadIdx.x % 16, gl = threadIdx.x / 16;
+  const int js = blockIdx.x * 64 + 4 * cl;  // first of this lane's four columns
+  const int ldp = ld4(N);
+  const float* pp = P + pt.p_off[b];
+  const float* pd = Pd + pt.gpre[b];
+  const bool real = js < N;  // the float4 at js lies inside the padded row
+  const int dpos = N - js;   // the dustbin column's place in the group, if 0..3
+  const bool dust = dpos >= 0 && dpos < 4;
+  const bool want_a = ARG && real;
+  const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  float mx[4], s[4], best[4];
+  int bi[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    mx[c] = -INFINITY;
+    s[c] = 0.f;
+    best[c] = -INFINITY;
+    bi[c] = 0x7fffffff;
+  }
+  for (int g0 = gl; g0 < G; g0 += GL * U) {
+    constexpr int UA = ARG ? U : 1;
+    float4 xs[U], bv[UA];
+    int4 bx[UA];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int g = g0 + GL * q;
+      const bool ok = g < G;
+      const size_t o = (size_t)g * ldp + js;
+      xs[q] = ok && write_v && real ? *reinterpret_cast<const float4*>(pp + o) : ninf;
+      if (ok && write_v && dust) set4(xs[q], dpos, pd[g]);
+      if constexpr (ARG) {
+        bv[q] = ok && want_a ? *reinterpret_cast<const float4*>(PV + pt.p_off[b] + o) : ninf;
+        bx[q] = ok && want_a ? *reinterpret_cast<const int4*>(PI + pt.p_off[b] + o)
+                             : make_int4(0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float m2 = mx[c];
+#pragma unroll
+      for (int q = 0; q < U; ++q) m2 = fmaxf(m2, f4c(xs[q], c));
+      if (m2 != -INFINITY) {
+        float t = mx[c] == -INFINITY ? 0.f : s[c] * exp2_fast(mx[c] - m2);
+#pragma unroll
+        for (int q = 0; q < U; ++q) t += exp2_fast(f4c(xs[q], c) - m2);
+        s[c] = t;
+        mx[c] = m2;
+      }
+      if constexpr (ARG) {
+#pragma unroll
+        for (int q = 0; q < UA; ++q) {
+          const int4 ix = bx[q];
+          argmax_merge(best[c], bi[c], f4c(bv[q], c), c == 0 ? ix.x : c == 1 ? ix.y : c == 2 ? ix.z : ix.w);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    sm_m[gl][4 * cl + c] = mx[c];
+    sm_s[gl][4 * cl + c] = s[c];
+    sm_b[gl][4 * cl + c] = best[c];
+    sm_i[gl][4 * cl + c] = bi[c];
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int j = blockIdx.x * 64 + t;
+  if (t >= 64 || j > N) return;
+  float mm = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < GL; ++q) mm = fmaxf(mm, sm_m[q][t]);
+  float ss = 0.f, bb = -INFINITY;
+  int ii = 0x7fffffff;
+#pragma unroll
+  for (int q = 0; q < GL; ++q) {
+    if (sm_m[q][t] != -INFINITY) ss += sm_s[q][t] * exp2_fast(sm_m[q][t] - mm);
+    argmax_merge(bb, ii, sm_b[q][t], sm_i[q][t]);
+  }
+  if (write_v) {
+    const float ln = (j < N ? 0.f : log2f((float)M)) - log2f((float)(M + N));
+    v_out[pt.voff[b] + j] = ln - (mm + log2_fast(ss));
+  }
+  if (ARG && j < N) {
+    idx1[pt.vpre[b] - b + j] = ii;
+    if (m1) {
+      m1[(size_t)b * Npad + j] = -1;
+      if (s1) s1[(size_t)b * Npad + j] = 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------- two-sweep variant
 //
-// One wave per row of Z (which = 0: rows i of the (M+1)x(N+1) couplings,
-// producing u) or of ZT (which = 1: columns j, producing v):
+// For problems whose Z and its transpose ZT stay resident in the L2 caches
+// the two updates run as separate sweeps, one wave per row of Z (which = 0:
+// rows i of the couplings, producing u) or of ZT (which = 1: columns j,
+// producing v), so that only the duals cross between kernels:
 //   out_i = log2 marginal_i - log2 sum_j 2^(Z2_ij + w_j),
 // with the dustbin row/column equal to alpha2 and the base-2 marginals
 // -log2(M+N) (real rows) and log2(count of the other side) - log2(M+N)
 // (dustbin).  w_in == nullptr stands for w = 0 (the first iteration).
-
 template <int NV4>
 __global__ __launch_bounds__(256) void k_lse(const float* __restrict__ Zbase, PairTable pt,
                                              int which, const float* __restrict__ w_in,
@@ -34,46 +381,31 @@ __global__ __launch_bounds__(256) void k_lse(const float* __restrict__ Zbase, Pa
   const int M = pt.M[b], N = pt.N[b];
   const int nr = which ? N : M, nc = which ? M : N;
   const float* wv = w_in ? w_in + (which ? pt.uoff[b] : pt.voff[b]) : nullptr;
-  const int last4 = ld4(nc) - 4;  // last float4 of a row (rows are padded to ld4(nc))
-  // every lane owns NV4 float4 groups of the row: columns 4*(lane + 64 t) .. +3
-  float x[4 * NV4];
-  if (nc == 0) {  // an empty other side: only the dustbin column remains
+  const float* row = which ? Zbase + pt.zt_off[b] + (size_t)i * ld4(M) : Zbase + pt.z_off[b] + (size_t)i * ld4(N);
+  // every lane owns NV4 float4 groups of the row: columns 4*(lane + 64 k) .. +3
+  float x[NV4][4];
 #pragma unroll
-    for (int k = 0; k < 4 * NV4; ++k) x[k] = -INFINITY;
-  } else if (i < nr) {
-    const float* row = Zbase + (which ? pt.zt_off[b] + (size_t)i * ld4(M) : pt.z_off[b] + (size_t)i * ld4(N));
+  for (int k = 0; k < NV4; ++k) {
+    const int j = 4 * (lane + 64 * k);
+    float4 z = make_float4(alpha2, alpha2, alpha2, alpha2);  // the dustbin row
+    if (i < nr && j < nc) z = *reinterpret_cast<const float4*>(row + j);
+    const float4 w = (wv && j < nc) ? *reinterpret_cast<const float4*>(wv + j) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int t = 0; t < NV4; ++t) {
-      const int j = 4 * (lane + 64 * t);
-      const int jc = min(j, last4);  // clamped: loads are unconditional and in bounds
-      float4 z = *reinterpret_cast<const float4*>(row + jc);
-      float4 w = wv ? *reinterpret_cast<const float4*>(wv + jc) : make_float4(0.f, 0.f, 0.f, 0.f);
-      x[4 * t + 0] = j + 0 < nc ? z.x + w.x : -INFINITY;
-      x[4 * t + 1] = j + 1 < nc ? z.y + w.y : -INFINITY;
-      x[4 * t + 2] = j + 2 < nc ? z.z + w.z : -INFINITY;
-      x[4 * t + 3] = j + 3 < nc ? z.w + w.w : -INFINITY;
-    }
-  } else {  // the dustbin row: alpha everywhere
-#pragma unroll
-    for (int t = 0; t < NV4; ++t) {
-      const int j = 4 * (lane + 64 * t);
-      const int jc = min(j, last4);
-      float4 w = wv ? *reinterpret_cast<const float4*>(wv + jc) : make_float4(0.f, 0.f, 0.f, 0.f);
-      x[4 * t + 0] = j + 0 < nc ? alpha2 + w.x : -INFINITY;
-      x[4 * t + 1] = j + 1 < nc ? alpha2 + w.y : -INFINITY;
-      x[4 * t + 2] = j + 2 < nc ? alpha2 + w.z : -INFINITY;
-      x[4 * t + 3] = j + 3 < nc ? alpha2 + w.w : -INFINITY;
-    }
+    for (int c = 0; c < 4; ++c) x[k][c] = j + c < nc ? f4c(z, c) + f4c(w, c) : -INFINITY;
   }
   // the dustbin column (j = nc) is alpha for every row
   const float xd = alpha2 + (wv ? wv[nc] : 0.f);
   float mx = xd;
 #pragma unroll
-  for (int k = 0; k < 4 * NV4; ++k) mx = fmaxf(mx, x[k]);
+  for (int k = 0; k < NV4; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mx = fmaxf(mx, x[k][c]);
   mx = wave_max(mx);
   float sum = lane == 0 ? exp2_fast(xd - mx) : 0.f;
 #pragma unroll
-  for (int k = 0; k < 4 * NV4; ++k) sum += exp2_fast(x[k] - mx);
+  for (int k = 0; k < NV4; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sum += exp2_fast(x[k][c] - mx);
   sum = wave_sum(sum);
   if (lane == 0) {
     const float lm = (i < nr ? 0.f : log2f((float)nc)) - log2f((float)(M + N));
@@ -81,108 +413,121 @@ __global__ __launch_bounds__(256) void k_lse(const float* __restrict__ Zbase, Pa
   }
 }
 
-// ------------------------------------------------------------- extraction
-//
-// Row argmax over the real block of the final log assignment (row i:
-// argmax_j Z2_ij + v_j, since u_i is constant along the row) and column
-// argmax (column j: argmax_i Z2_ij + u_i, read from ZT).  Lowest index wins
-// ties.  Waves [0, rowsA) take rows of A, the rest columns.
-
-template <int MAXV>
-__global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ Zb,
-                                                const float* __restrict__ ZTb, PairTable pt,
-                                                const float* __restrict__ u,
-                                                const float* __restrict__ v, int* __restrict__ idx0,
-                                                float* __restrict__ val0, int* __restrict__ idx1,
-                                                int rowsA, int rowsB) {
+// Column argmax over the real rows (argmax_i Z2_ij + u_i, lowest index on
+// ties) from the rows of ZT, one wave per column; also the default (-1 / 0)
+// side-B outputs that the extraction overwrites for mutual matches.
+template <int NV4>
+__global__ __launch_bounds__(256) void k_col_argmax(const float* __restrict__ ZTb, PairTable pt,
+                                                    const float* __restrict__ u,
+                                                    int* __restrict__ idx1, int Npad,
+                                                    int32_t* __restrict__ m1, float* __restrict__ s1) {
   const int lane = threadIdx.x & 63;
-  int g = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= rowsA + rowsB) return;
-  const int which = g >= rowsA ? 1 : 0;
-  if (which) g -= rowsA;
-  // flattened real rows: prefix of M is upre[b] - b, prefix of N is vpre[b] - b
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // flattened real columns: the prefix of N over the pairs is vpre[b] - b
   int b = 0;
-  const int* pre = which ? pt.vpre : pt.upre;
-  while (b < pt.n_pairs && g >= pre[b + 1] - (b + 1)) ++b;
+  while (b < pt.n_pairs && g >= pt.vpre[b + 1] - (b + 1)) ++b;
   if (b >= pt.n_pairs) return;
-  const int i = g - (pre[b] - b);
-  const int M = pt.M[b], N = pt.N[b];
-  const int nc = which ? M : N;
-  const float* row = which ? ZTb + pt.zt_off[b] + (size_t)i * ld4(M) : Zb + pt.z_off[b] + (size_t)i * ld4(N);
-  const float* wv = which ? u + pt.uoff[b] : v + pt.voff[b];
+  const int j = g - (pt.vpre[b] - b);
+  const int M = pt.M[b];
+  const float* row = ZTb + pt.zt_off[b] + (size_t)j * ld4(M);
+  const float* uu = u + pt.uoff[b];
   float best = -INFINITY;
-  int bj = 0x7fffffff;
+  int bi = 0x7fffffff;
 #pragma unroll
-  for (int t = 0; t < MAXV; ++t) {
-    const int j = lane + 64 * t;
-    if (j < nc) {
-      const float x = row[j] + wv[j];
-      if (x > best) { best = x; bj = j; }
+  for (int k = 0; k < NV4; ++k) {
+    const int i = 4 * (lane + 64 * k);
+    if (i < M) {
+      const float4 z = *reinterpret_cast<const float4*>(row + i);
+      const float4 q = *reinterpret_cast<const float4*>(uu + i);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float y = f4c(z, c) + f4c(q, c);
+        if (i + c < M && y > best) {
+          best = y;
+          bi = i + c;
+        }
+      }
     }
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ob = __shfl_xor(best, o);
-    const int oj = __shfl_xor(bj, o);
-    if (ob > best || (ob == best && oj < bj)) { best = ob; bj = oj; }
-  }
+  wave_argmax(best, bi);
   if (lane == 0) {
-    if (which) {
-      idx1[g] = bj;
-    } else {
-      idx0[g] = bj;
-      val0[g] = best;
+    idx1[g] = bi;
+    if (m1) {
+      m1[(size_t)b * Npad + j] = -1;
+      if (s1) s1[(size_t)b * Npad + j] = 0.f;
     }
   }
 }
 
-// Mutual check, score and threshold for both sides of every pair; padded
-// entries (and pairs with an empty image) get -1 / 0.
-__global__ __launch_bounds__(256) void k_finalize(PairTable pt, const int* __restrict__ idx0,
-                                                  const float* __restrict__ val0,
-                                                  const int* __restrict__ idx1,
-                                                  const float* __restrict__ u, int Mpad, int Npad,
-                                                  float thr, int32_t* __restrict__ m0,
-                                                  float* __restrict__ s0, int32_t* __restrict__ m1,
-                                                  float* __restrict__ s1) {
+// Row argmax of the final log assignment (argmax_j Z_ij + v_j; lowest index
+// on ties), mutual check against idx1, score exp(logP), threshold; side-B
+// outputs of mutual pairs; -1 / 0 for padded entries and empty pairs.
+template <int NV4>
+__global__ __launch_bounds__(256) void k_sink_extract(const float* __restrict__ Zb, PairTable pt,
+                                                      const float* __restrict__ u,
+                                                      const float* __restrict__ v,
+                                                      const int* __restrict__ idx1, int Mpad,
+                                                      int Npad, float thr, int32_t* __restrict__ m0,
+                                                      float* __restrict__ s0,
+                                                      int32_t* __restrict__ m1,
+                                                      float* __restrict__ s1) {
   const int b = blockIdx.y;
-  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int M = pt.M[b], N = pt.N[b];
   const bool empty = M == 0 || N == 0;
-  const int mpre = pt.upre[b] - b, npre = pt.vpre[b] - b;
-  const float lmn = empty ? 0.f : log2f((float)(M + N));
-  // exp(logP) > thr decided in the log domain (exact for any finite logP:
-  // exp never reaches 0, so a non-positive threshold accepts every mutual match)
-  const float lthr = thr > 0.f ? log2f(thr) : -INFINITY;
-  if (t < Mpad) {
-    const size_t o = (size_t)b * Mpad + t;
-    int mo = -1;
-    float so = 0.f;
-    if (t < M && !empty) {
-      const int j = idx0[mpre + t];
-      if (idx1[npre + j] == t) {
-        const float lp2 = val0[mpre + t] + u[pt.uoff[b] + t] + lmn;
-        so = exp2f(lp2);
-        if (lp2 > lthr) mo = j;
-      }
-    }
-    m0[o] = mo;
-    s0[o] = so;
+  if (m1 && t >= N && t < Npad && lane == 0) {  // padded side-B entries
+    m1[(size_t)b * Npad + t] = -1;
+    if (s1) s1[(size_t)b * Npad + t] = 0.f;
   }
-  if (m1 && t < Npad) {
-    const size_t o = (size_t)b * Npad + t;
-    int mo = -1;
-    float so = 0.f;
-    if (t < N && !empty) {
-      const int i = idx1[npre + t];
-      if (idx0[mpre + i] == t) {
-        const float lp2 = val0[mpre + i] + u[pt.uoff[b] + i] + lmn;
-        so = exp2f(lp2);
-        if (lp2 > lthr) mo = i;
-      }
-    }
-    m1[o] = mo;
-    if (s1) s1[o] = so;
+  if (empty && m1 && t < N && lane == 0) {
+    m1[(size_t)b * Npad + t] = -1;
+    if (s1) s1[(size_t)b * Npad + t] = 0.f;
   }
+  if (t >= Mpad) return;
+  if (t >= M || empty) {
+    if (lane == 0) {
+      m0[(size_t)b * Mpad + t] = -1;
+      s0[(size_t)b * Mpad + t] = 0.f;
+    }
+    return;
+  }
+  const int ldz = ld4(N);
+  const float* row = Zb + pt.z_off[b] + (size_t)t * ldz;
+  const float* vv = v + pt.voff[b];
+  float best = -INFINITY;
+  int bj = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < NV4; ++k) {
+    const int j = 4 * (lane + 64 * k);
+    if (j < N) {
+      const float4 z = *reinterpret_cast<const float4*>(row + j);
+      const float4 q = *reinterpret_cast<const float4*>(vv + j);
+      const float x[4] = {z.x + q.x, z.y + q.y, z.z + q.z, z.w + q.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j + e < N && x[e] > best) { best = x[e]; bj = j + e; }
+    }
+  }
+  wave_argmax(best, bj);
+  if (lane != 0) return;
+  // (bj stays out of range only when no entry of the row compares, e.g. NaN scores)
+  const bool mutual = bj < N && idx1[pt.vpre[b] - b + bj] == t;
+  float score = 0.f;
+  int mo = -1;
+  if (mutual) {
+    const float lp2 = best + u[pt.uoff[b] + t] + log2f((float)(M + N));
+    score = exp2f(lp2);
+    // exp(logP) > thr decided in the log domain (exact for any finite logP:
+    // exp never reaches 0, so a non-positive threshold accepts every mutual match)
+    if (thr <= 0.f || lp2 > log2f(thr)) mo = bj;
+    if (m1) {
+      m1[(size_t)b * Npad + bj] = mo >= 0 ? t : -1;
+      if (s1) s1[(size_t)b * Npad + bj] = score;
+    }
+  }
+  m0[(size_t)b * Mpad + t] = mo;
+  s0[(size_t)b * Mpad + t] = score;
 }
 
 // Optional output: the (M+1) x (N+1) log assignment of every pair,
@@ -221,51 +566,113 @@ __global__ void k_fill_empty(int32_t* m, float* s, int n) {
   }
 }
 
-static int max_cols(const PairTable& pt, int which) {
+// ------------------------------------------------------------- launchers
+
+static int max_n(const PairTable& pt) {
   int m = 0;
-  for (int b = 0; b < pt.n_pairs; ++b) m = std::max(m, (which ? pt.M[b] : pt.N[b]) + 1);
+  for (int b = 0; b < pt.n_pairs; ++b) m = std::max(m, pt.N[b]);
   return m;
 }
+// float4 groups per lane that cover the longest row of the batch (power of two)
+static int sink_nv4(int max_n) {
+  int nv4 = 1;
+  while (256 * nv4 < max_n) nv4 *= 2;
+  return nv4;
+}
 
-hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const float* w_in,
-                      float* w_out, float alpha2, const float* alpha_dev, int total_rows,
-                      hipStream_t st) {
+int sink_rows_per_block(const int* M, const int* N, int n_pairs) {
+  (void)M;
+  int mn = 0;
+  for (int b = 0; b < n_pairs; ++b) mn = std::max(mn, N[b]);
+  // two rows per wave (eight per workgroup) up to 2048 columns, where the
+  // row values still fit the registers; one beyond
+  return sink_nv4(mn) <= 8 ? 8 : 4;
+}
+
+hipError_t launch_sink_rows(const float* Z, const PairTable& pt, const float* v_in, float* u_out,
+                            float* P, float* Pd, float* PV, int* PI, float alpha2, const float* alpha_dev,
+                            int update_u, hipStream_t st) {
+  const int blocks = pt.gpre[pt.n_pairs];
+  if (blocks <= 0) return hipSuccess;
+  const int nv4 = sink_nv4(max_n(pt));
+  const int rpw = pt.rb / 4;
+  if (rpw * nv4 > 16 || rpw * 4 != pt.rb) return hipErrorInvalidValue;
+  const bool arg = PV != nullptr;
+#define SG_ROWS(R, NV)                                                                                   \
+  if (rpw == R && nv4 == NV) {                                                                            \
+    if (arg)                                                                                             \
+      hipLaunchKernelGGL((k_sink_rows<R, NV, true>), dim3(blocks), dim3(256), 0, st, Z, pt, v_in, u_out, P, \
+                         Pd, PV, PI, alpha2, alpha_dev, update_u);                                        \
+    else                                                                                                 \
+      hipLaunchKernelGGL((k_sink_rows<R, NV, false>), dim3(blocks), dim3(256), 0, st, Z, pt, v_in, u_out, \
+                         P, Pd, PV, PI, alpha2, alpha_dev, update_u);                                     \
+    return hipGetLastError();                                                                             \
+  }
+  SG_ROWS(2, 1) SG_ROWS(2, 2) SG_ROWS(2, 4) SG_ROWS(2, 8)
+  SG_ROWS(1, 1) SG_ROWS(1, 2) SG_ROWS(1, 4) SG_ROWS(1, 8) SG_ROWS(1, 16)
+#undef SG_ROWS
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_sink_cols(const PairTable& pt, const float* P, const float* Pd, float* v_out, const float* PV,
+                            const int* PI, int* idx1, int write_v, int Npad, int32_t* m1, float* s1,
+                            hipStream_t st) {
+  if (pt.n_pairs <= 0) return hipSuccess;
+  dim3 grid((max_n(pt) + 1 + 63) / 64, pt.n_pairs);
+  if (PV)
+    hipLaunchKernelGGL(k_sink_cols<true>, grid, dim3(256), 0, st, pt, P, Pd, v_out, PV, PI, idx1, write_v, Npad, m1, s1);
+  else
+    hipLaunchKernelGGL(k_sink_cols<false>, grid, dim3(256), 0, st, pt, P, Pd, v_out, PV, PI, idx1, write_v, Npad, m1, s1);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const float* w_in, float* w_out,
+                      float alpha2, const float* alpha_dev, int total_rows, hipStream_t st) {
   if (total_rows <= 0) return hipSuccess;
-  const int nc = max_cols(pt, which) - 1;  // real columns of the longest row
+  int nc = 0;
+  for (int b = 0; b < pt.n_pairs; ++b) nc = std::max(nc, which ? pt.M[b] : pt.N[b]);
+  const int nv4 = sink_nv4(nc);
   dim3 grid((total_rows + 3) / 4);
-#define SG_LSE(NV) hipLaunchKernelGGL(k_lse<NV>, grid, dim3(256), 0, st, Z, pt, which, w_in, w_out, alpha2, alpha_dev)
-  if (nc <= 256) SG_LSE(1);
-  else if (nc <= 512) SG_LSE(2);
-  else if (nc <= 1024) SG_LSE(4);
-  else if (nc <= 2048) SG_LSE(8);
-  else if (nc <= 4096) SG_LSE(16);
-  else return hipErrorInvalidValue;
+#define SG_LSE(NV) \
+  if (nv4 == NV) { hipLaunchKernelGGL(k_lse<NV>, grid, dim3(256), 0, st, Z, pt, which, w_in, w_out, alpha2, alpha_dev); return hipGetLastError(); }
+  SG_LSE(1) SG_LSE(2) SG_LSE(4) SG_LSE(8) SG_LSE(16)
 #undef SG_LSE
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_argmax(const float* Z, const float* ZT, const PairTable& pt, const float* u,
-                         const float* v, int* idx0, float* val0, int* idx1, int rowsA, int rowsB,
-                         hipStream_t st) {
-  if (rowsA + rowsB <= 0) return hipSuccess;
-  const int nc = std::max(max_cols(pt, 0), max_cols(pt, 1));
-  dim3 grid((rowsA + rowsB + 3) / 4);
-  if (nc <= 256) hipLaunchKernelGGL(k_argmax<4>, grid, dim3(256), 0, st, Z, ZT, pt, u, v, idx0, val0, idx1, rowsA, rowsB);
-  else if (nc <= 576) hipLaunchKernelGGL(k_argmax<9>, grid, dim3(256), 0, st, Z, ZT, pt, u, v, idx0, val0, idx1, rowsA, rowsB);
-  else if (nc <= 1088) hipLaunchKernelGGL(k_argmax<17>, grid, dim3(256), 0, st, Z, ZT, pt, u, v, idx0, val0, idx1, rowsA, rowsB);
-  else if (nc <= 2112) hipLaunchKernelGGL(k_argmax<33>, grid, dim3(256), 0, st, Z, ZT, pt, u, v, idx0, val0, idx1, rowsA, rowsB);
-  else if (nc <= 4160) hipLaunchKernelGGL(k_argmax<65>, grid, dim3(256), 0, st, Z, ZT, pt, u, v, idx0, val0, idx1, rowsA, rowsB);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+hipError_t launch_col_argmax(const float* ZT, const PairTable& pt, const float* u, int* idx1, int Npad,
+                             int32_t* m1, float* s1, hipStream_t st) {
+  int cols = 0, mr = 0;
+  for (int b = 0; b < pt.n_pairs; ++b) {
+    cols += pt.N[b];
+    mr = std::max(mr, pt.M[b]);
+  }
+  if (cols <= 0) return hipSuccess;
+  const int nv4 = sink_nv4(mr);
+  dim3 grid((cols + 3) / 4);
+#define SG_CA(NV) \
+  if (nv4 == NV) { hipLaunchKernelGGL(k_col_argmax<NV>, grid, dim3(256), 0, st, ZT, pt, u, idx1, Npad, m1, s1); return hipGetLastError(); }
+  SG_CA(1) SG_CA(2) SG_CA(4) SG_CA(8) SG_CA(16)
+#undef SG_CA
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_finalize(const PairTable& pt, const int* idx0, const float* val0, const int* idx1,
-                           const float* u, int Mpad, int Npad, float thr, int32_t* m0, float* s0,
-                           int32_t* m1, float* s1, hipStream_t st) {
+hipError_t launch_sink_extract(const float* Z, const PairTable& pt, const float* u, const float* v,
+                               const int* idx1, int Mpad, int Npad, float thr, int32_t* m0, float* s0,
+                               int32_t* m1, float* s1, hipStream_t st) {
   const int n = std::max(Mpad, m1 ? Npad : 0);
   if (n <= 0 || pt.n_pairs <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_finalize, dim3((n + 255) / 256, pt.n_pairs), dim3(256), 0, st, pt, idx0,
-                     val0, idx1, u, Mpad, Npad, thr, m0, s0, m1, s1);
+  const int nc = max_n(pt);
+  const int nv4 = (nc + 255) / 256;
+  dim3 grid((n + 3) / 4, pt.n_pairs);
+#define SG_EXT(NV) hipLaunchKernelGGL(k_sink_extract<NV>, grid, dim3(256), 0, st, Z, pt, u, v, idx1, Mpad, Npad, thr, m0, s0, m1, s1)
+  if (nv4 <= 1) SG_EXT(1);
+  else if (nv4 <= 2) SG_EXT(2);
+  else if (nv4 <= 4) SG_EXT(4);
+  else if (nv4 <= 8) SG_EXT(8);
+  else if (nv4 <= 16) SG_EXT(16);
+  else return hipErrorInvalidValue;
+#undef SG_EXT
   return hipGetLastError();
 }
 
@@ -273,7 +680,7 @@ hipError_t launch_write_logp(const float* Z, const PairTable& pt, const float* u
                              float alpha2, const float* alpha_dev, float* logP, int64_t ld,
                              int64_t pair_stride, int total_rows, hipStream_t st) {
   if (total_rows <= 0) return hipSuccess;
-  const int nc = max_cols(pt, 0);
+  const int nc = max_n(pt) + 1;
   hipLaunchKernelGGL(k_write_logp, dim3((nc + 255) / 256, total_rows), dim3(256), 0, st, Z, pt, u,
                      v, alpha2, alpha_dev, logP, ld, pair_stride);
   return hipGetLastError();
