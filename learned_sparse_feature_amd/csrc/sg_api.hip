@@ -476,6 +476,7 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
       HIPCHK(launch_fill_f32(U, 0.f, (int)pl.uf, st), "zero u");
       HIPCHK(launch_fill_f32(V, 0.f, (int)pl.vf, st), "zero v");
     }
+    tm.stage(SG_EV_SINKHORN);
     HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, st), "column argmax");
   } else {
     // T iterations: u = log mu - lse_j(Z + v) with the column partials of
@@ -498,8 +499,8 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
       HIPCHK(launch_sink_rows(Z, pl.pt, nullptr, U, P, Pd, PV, PI, alpha2, alpha_dev, 0, st), "column argmax");
       HIPCHK(launch_sink_cols(pl.pt, P, Pd, V, PV, PI, idx1, 0, p.Npad, out.m1, out.s1, st), "column argmax");
     }
+    tm.stage(SG_EV_SINKHORN);
   }
-  tm.stage(SG_EV_SINKHORN);
   HIPCHK(launch_sink_extract(Z, pl.pt, U, V, idx1, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, st),
          "extract");
   if (out.logP)
