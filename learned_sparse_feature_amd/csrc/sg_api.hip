@@ -347,8 +347,9 @@ sg_status run_encoder(const Problem& p, const Plan& pl, const sg_weights* w, con
 
 // Stages [s0, s1) in place on X (compact rows of every image of the plan).
 sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0, int s1, char* ws,
-                  const WsLayout& wl, Timer& tm, hipStream_t st) {
+                  const WsLayout& wl, int flags, Timer& tm, hipStream_t st) {
   const int D = w->D, op = w->dtype, R = pl.R;
+  (void)flags;
   float* X = reinterpret_cast<float*>(ws + wl.X);
   void* QK = ws + wl.QK;
   void* VT = ws + wl.VT;
@@ -639,7 +640,7 @@ sg_status enqueue_full(const Problem& p, const Plan& pl, const WsLayout& wl, cha
   tm.stage(SG_EV_START);
   if ((s = run_encoder(p, pl, w, L, ws, wl, tm, st)) != SG_OK) return s;
   tm.stage(SG_EV_ENCODED);
-  if ((s = run_gnn(pl, w, L, 0, 2 * Lst, ws, wl, tm, st)) != SG_OK) return s;
+  if ((s = run_gnn(pl, w, L, 0, 2 * Lst, ws, wl, o ? o->flags : 0, tm, st)) != SG_OK) return s;
   tm.stage(SG_EV_GNN);
   float* F = reinterpret_cast<float*>(ws + wl.F);
   if ((s = run_project(pl, w, L, reinterpret_cast<float*>(ws + wl.X), F, tm, st)) != SG_OK) return s;
@@ -842,7 +843,7 @@ sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weig
   if (M) HIPCHK(hipMemcpyAsync(X, xA, M * rb, hipMemcpyDeviceToDevice, st), "copy xA");
   if (N) HIPCHK(hipMemcpyAsync(X + (size_t)pl.seg.row0[1] * weights->D, xB, N * rb, hipMemcpyDeviceToDevice, st), "copy xB");
   Timer tm{opts, st};
-  if ((s = run_gnn(pl, weights, WL, s0, s1, ws, wl, tm, st)) != SG_OK) return s;
+  if ((s = run_gnn(pl, weights, WL, s0, s1, ws, wl, opts ? opts->flags : 0, tm, st)) != SG_OK) return s;
   if (M) HIPCHK(hipMemcpyAsync(xA, X, M * rb, hipMemcpyDeviceToDevice, st), "copy xA back");
   if (N) HIPCHK(hipMemcpyAsync(xB, X + (size_t)pl.seg.row0[1] * weights->D, N * rb, hipMemcpyDeviceToDevice, st), "copy xB back");
   tm.finish();

@@ -102,8 +102,10 @@ __global__ __launch_bounds__(256) void k_encoder(EncArgs e, SegTable seg) {
         const float v = acc[i] + bv;
         if (!last) {
           hout[r * LDH + n] = (OpT)fmaxf(v, 0.f);
-        } else if (r < np) {
-          e.X[(row0 + r) * e.ldx + n] = de[(size_t)r * e.D + n] + v;
+        } else {
+          // rows past the image (the tile's padding) are zero, so that every
+          // later product over the padded row space stays finite
+          e.X[(row0 + r) * e.ldx + n] = r < np ? de[(size_t)r * e.D + n] + v : 0.f;
         }
       }
     }

@@ -15,9 +15,12 @@
 //  * 128 x 128 tiles with one K step in flight (PF = 2) for large problems
 //    (batches): each 64x64 wave tile reuses every LDS fragment twice, and
 //    several resident workgroups per CU hide the load latency.
-// The grid's x axis walks row tiles, so consecutive workgroups (which the
-// dispatcher sends to different XCDs) split the A rows between the XCDs'
-// L2 caches.
+// Tile order is XCD-aware: the dispatcher sends workgroup i to XCD i % 8, so
+// workgroup i takes tile (i % 8) * ceil(T / 8) + i / 8 of the row-major tile
+// sequence (column tiles innermost).  Each XCD then walks a contiguous run of
+// tiles, the column tiles of one row tile run together on one XCD, and each
+// A row tile is fetched into that XCD's L2 once instead of once per column
+// tile.
 #include "sg_device.h"
 
 namespace sg {
@@ -65,8 +68,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   __shared__ __attribute__((aligned(16))) OpT As[2][BM * PITCH];
   __shared__ __attribute__((aligned(16))) OpT Ws[2][BN * PITCH];
 
-  const GemmProblem P = bt.p[blockIdx.z];
-  const int r0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int T = g.gx * g.gy * bt.n;
+  const int t = (int)(blockIdx.x % 8) * ((T + 7) / 8) + (int)(blockIdx.x / 8);
+  if (t >= T) return;
+  const int ty = t % g.gy, tx = (t / g.gy) % g.gx, tz = t / (g.gy * g.gx);
+  const GemmProblem P = bt.p[tz];
+  const int r0 = tx * BM, n0 = ty * BN;
   if (r0 >= P.rows || n0 >= P.n_out) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -240,12 +247,17 @@ template <typename OpT, typename A0T, typename WT, typename OutT, int EPI>
 static void gemm_go(const GemmArgs& g, const GemmBatch& b, int max_rows, int max_n, hipStream_t st) {
   // large problems (several tiles per CU even at 128 x 128): the LDS-efficient shape
   const long big_tiles = (long)((max_rows + 127) / 128) * ((max_n + 127) / 128) * b.n;
+  GemmArgs a = g;
   if (big_tiles >= 1024) {
-    dim3 grid((max_rows + 127) / 128, (max_n + 127) / 128, b.n);
-    hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 128, 128, 2>), grid, dim3(256), 0, st, g, b);
+    a.gx = (max_rows + 127) / 128;
+    a.gy = (max_n + 127) / 128;
+    const int T = a.gx * a.gy * b.n;
+    hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 128, 128, 2>), dim3(8 * ((T + 7) / 8)), dim3(256), 0, st, a, b);
   } else {
-    dim3 grid((max_rows + 63) / 64, (max_n + 63) / 64, b.n);
-    hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 64, 64, 8>), grid, dim3(256), 0, st, g, b);
+    a.gx = (max_rows + 63) / 64;
+    a.gy = (max_n + 63) / 64;
+    const int T = a.gx * a.gy * b.n;
+    hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 64, 64, 8>), dim3(8 * ((T + 7) / 8)), dim3(256), 0, st, a, b);
   }
 }
 

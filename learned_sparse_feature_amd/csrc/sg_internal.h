@@ -70,6 +70,7 @@ struct GemmArgs {
   void* C; void* C2;                 // outputs (C2: VT or ZT)
   float scale;
   int split;                         // EPI_QKV: first column that goes to VT
+  int gx, gy;                        // row and column tiles (set by the launcher)
 };
 
 // Fused keypoint encoder: linear layers [3 -> width[1] -> ... -> D].

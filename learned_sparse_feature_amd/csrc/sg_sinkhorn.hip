@@ -240,16 +240,12 @@ __global__ __launch_bounds__(256) void k_sink_rows(const float* __restrict__ Zb,
 // Column reduction of the block partials of every pair: v_j = log2 nu_j -
 // lse2_g P[g][j] (write_v), and after the last iteration the column argmax
 // over the real rows (idx1) plus the default (-1 / 0) side-B outputs.
-// A workgroup takes 64 columns of one pair (16 lanes x float4, so that each
-// partial row is read in whole 256-byte runs); its 16 row lanes
-// (threadIdx / 16) take the partial rows g = gl (mod 16).
-__device__ __forceinline__ void set4(float4& a, int c, float v) {
-  if (c == 0) a.x = v;
-  else if (c == 1) a.y = v;
-  else if (c == 2) a.z = v;
-  else a.w = v;
-}
-
+// A workgroup takes 64 real columns of one pair (16 lanes x float4, so that
+// each partial row is read in whole 256-byte runs); its 16 row lanes
+// (threadIdx / 16) take the partial rows g = gl (mod 16).  Loads are
+// unconditional at clamped addresses and masked afterwards, so that all of a
+// thread's loads are in flight together.  The workgroup that holds column N
+// also reduces the dustbin column's partials Pd.
 template <bool ARG>
 __global__ __launch_bounds__(256) void k_sink_cols(PairTable pt, const float* __restrict__ P,
                                                    const float* __restrict__ Pd,
@@ -258,23 +254,21 @@ __global__ __launch_bounds__(256) void k_sink_cols(PairTable pt, const float* __
                                                    const int* __restrict__ PI, int* __restrict__ idx1,
                                                    int write_v, int Npad, int32_t* __restrict__ m1,
                                                    float* __restrict__ s1) {
-  constexpr int GL = 16, U = 8;
+  constexpr int GL = 16, U = ARG ? 8 : 16;
   __shared__ float sm_m[GL][64], sm_s[GL][64], sm_b[GL][64];
   __shared__ int sm_i[GL][64];
   const int b = blockIdx.y;
   const int M = pt.M[b], N = pt.N[b];
   if (blockIdx.x * 64 > N) return;
   const int G = pt.gpre[b + 1] - pt.gpre[b];
-  const int cl = threadIdx.x % 16, gl = threadIdx.x / 16;
+  const int tid = threadIdx.x;
+  const int cl = tid % 16, gl = tid / 16;
   const int js = blockIdx.x * 64 + 4 * cl;  // first of this lane's four columns
   const int ldp = ld4(N);
-  const float* pp = P + pt.p_off[b];
-  const float* pd = Pd + pt.gpre[b];
-  const bool real = js < N;  // the float4 at js lies inside the padded row
-  const int dpos = N - js;   // the dustbin column's place in the group, if 0..3
-  const bool dust = dpos >= 0 && dpos < 4;
-  const bool want_a = ARG && real;
-  const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  const bool real = js < N;
+  const int jsc = real ? js : max(ldp - 4, 0);  // an in-bounds address for the masked lanes
+  const float* pp = P + pt.p_off[b] + jsc;
+  const float lmn = log2f((float)(M + N));
   float mx[4], s[4], best[4];
   int bi[4];
 #pragma unroll
@@ -284,40 +278,39 @@ __global__ __launch_bounds__(256) void k_sink_cols(PairTable pt, const float* __
     best[c] = -INFINITY;
     bi[c] = 0x7fffffff;
   }
-  for (int g0 = gl; g0 < G; g0 += GL * U) {
-    constexpr int UA = ARG ? U : 1;
-    float4 xs[U], bv[UA];
-    int4 bx[UA];
+  if (N > 0 && (write_v || ARG)) {
+    for (int g0 = gl; g0 < G; g0 += GL * U) {
+      float4 xs[U];
+      int4 bx[ARG ? U : 1];
+      float4 bv[ARG ? U : 1];
 #pragma unroll
-    for (int q = 0; q < U; ++q) {
-      const int g = g0 + GL * q;
-      const bool ok = g < G;
-      const size_t o = (size_t)g * ldp + js;
-      xs[q] = ok && write_v && real ? *reinterpret_cast<const float4*>(pp + o) : ninf;
-      if (ok && write_v && dust) set4(xs[q], dpos, pd[g]);
-      if constexpr (ARG) {
-        bv[q] = ok && want_a ? *reinterpret_cast<const float4*>(PV + pt.p_off[b] + o) : ninf;
-        bx[q] = ok && want_a ? *reinterpret_cast<const int4*>(PI + pt.p_off[b] + o)
-                             : make_int4(0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff);
+      for (int q = 0; q < U; ++q) {
+        const size_t o = (size_t)min(g0 + GL * q, G - 1) * ldp;
+        xs[q] = *reinterpret_cast<const float4*>(pp + o);
+        if constexpr (ARG) {
+          bv[q] = *reinterpret_cast<const float4*>(PV + pt.p_off[b] + jsc + o);
+          bx[q] = *reinterpret_cast<const int4*>(PI + pt.p_off[b] + jsc + o);
+        }
       }
-    }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float m2 = mx[c];
+      for (int c = 0; c < 4; ++c) {
+        float m2 = mx[c];
 #pragma unroll
-      for (int q = 0; q < U; ++q) m2 = fmaxf(m2, f4c(xs[q], c));
-      if (m2 != -INFINITY) {
+        for (int q = 0; q < U; ++q)
+          if (g0 + GL * q < G) m2 = fmaxf(m2, f4c(xs[q], c));
         float t = mx[c] == -INFINITY ? 0.f : s[c] * exp2_fast(mx[c] - m2);
 #pragma unroll
-        for (int q = 0; q < U; ++q) t += exp2_fast(f4c(xs[q], c) - m2);
+        for (int q = 0; q < U; ++q)
+          if (g0 + GL * q < G) t += exp2_fast(f4c(xs[q], c) - m2);
         s[c] = t;
         mx[c] = m2;
-      }
-      if constexpr (ARG) {
+        if constexpr (ARG) {
 #pragma unroll
-        for (int q = 0; q < UA; ++q) {
-          const int4 ix = bx[q];
-          argmax_merge(best[c], bi[c], f4c(bv[q], c), c == 0 ? ix.x : c == 1 ? ix.y : c == 2 ? ix.z : ix.w);
+          for (int q = 0; q < U; ++q)
+            if (g0 + GL * q < G) {
+              const int4 ix = bx[q];
+              argmax_merge(best[c], bi[c], f4c(bv[q], c), c == 0 ? ix.x : c == 1 ? ix.y : c == 2 ? ix.z : ix.w);
+            }
         }
       }
     }
@@ -330,28 +323,53 @@ __global__ __launch_bounds__(256) void k_sink_cols(PairTable pt, const float* __
     sm_i[gl][4 * cl + c] = bi[c];
   }
   __syncthreads();
-  const int t = threadIdx.x;
+  const int t = tid;
   const int j = blockIdx.x * 64 + t;
-  if (t >= 64 || j > N) return;
-  float mm = -INFINITY;
+  if (t < 64 && j < N) {
+    float mm = -INFINITY;
 #pragma unroll
-  for (int q = 0; q < GL; ++q) mm = fmaxf(mm, sm_m[q][t]);
-  float ss = 0.f, bb = -INFINITY;
-  int ii = 0x7fffffff;
+    for (int q = 0; q < GL; ++q) mm = fmaxf(mm, sm_m[q][t]);
+    float ss = 0.f, bb = -INFINITY;
+    int ii = 0x7fffffff;
 #pragma unroll
-  for (int q = 0; q < GL; ++q) {
-    if (sm_m[q][t] != -INFINITY) ss += sm_s[q][t] * exp2_fast(sm_m[q][t] - mm);
-    argmax_merge(bb, ii, sm_b[q][t], sm_i[q][t]);
+    for (int q = 0; q < GL; ++q) {
+      if (sm_m[q][t] != -INFINITY) ss += sm_s[q][t] * exp2_fast(sm_m[q][t] - mm);
+      argmax_merge(bb, ii, sm_b[q][t], sm_i[q][t]);
+    }
+    if (write_v) v_out[pt.voff[b] + j] = -lmn - (mm + log2_fast(ss));
+    if (ARG) {
+      idx1[pt.vpre[b] - b + j] = ii;
+      if (m1) {
+        m1[(size_t)b * Npad + j] = -1;
+        if (s1) s1[(size_t)b * Npad + j] = 0.f;
+      }
+    }
   }
-  if (write_v) {
-    const float ln = (j < N ? 0.f : log2f((float)M)) - log2f((float)(M + N));
-    v_out[pt.voff[b] + j] = ln - (mm + log2_fast(ss));
-  }
-  if (ARG && j < N) {
-    idx1[pt.vpre[b] - b + j] = ii;
-    if (m1) {
-      m1[(size_t)b * Npad + j] = -1;
-      if (s1) s1[(size_t)b * Npad + j] = 0.f;
+  // the dustbin column: v_N = log2 M - log2(M+N) - lse2_g Pd[g]
+  if (write_v && blockIdx.x == N / 64) {
+    __syncthreads();
+    const float* pd = Pd + pt.gpre[b];
+    float m = -INFINITY, sum = 0.f;
+    for (int g = tid; g < G; g += 256) {
+      const float x = pd[g];
+      const float m2 = fmaxf(m, x);
+      sum = (m == -INFINITY ? 0.f : sum * exp2_fast(m - m2)) + exp2_fast(x - m2);
+      m = m2;
+    }
+    const float wm = wave_max(m);
+    sum = wave_sum(m == -INFINITY ? 0.f : sum * exp2_fast(m - wm));
+    if ((tid & 63) == 0) {
+      sm_m[0][tid >> 6] = wm;
+      sm_s[0][tid >> 6] = sum;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float mm = -INFINITY;
+      for (int w = 0; w < 4; ++w) mm = fmaxf(mm, sm_m[0][w]);
+      float ss = 0.f;
+      for (int w = 0; w < 4; ++w)
+        if (sm_m[0][w] != -INFINITY) ss += sm_s[0][w] * exp2_fast(sm_m[0][w] - mm);
+      v_out[pt.voff[b] + N] = log2f((float)M) - lmn - (mm + log2_fast(ss));
     }
   }
 }

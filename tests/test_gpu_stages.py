@@ -100,6 +100,8 @@ def test_encoder_parity(cid, n, bias_on):
     (3, 2048, 1536, (0, 2), 1e-5),
     (2, 1024, 1024, (0, 2), 5e-3),
     (2, 300, 45, (3, 5), 5e-3),
+    (2, 33, 1, (0, 3), 5e-3),
+    (2, 68, 2000, (6, 9), 5e-3),
 ])
 def test_gnn_stage_parity(cid, M, N, stages, tol):
     cfg = synth.CONFIGS[cid]
