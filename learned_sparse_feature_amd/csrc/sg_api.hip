@@ -122,7 +122,7 @@ sg_status check_weights(const sg_weights* w, WLayout* out) {
 // ---------------------------------------------------------- workspace layout
 
 struct WsLayout {
-  size_t X, H0, H1, QK, VT, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, IDX1, total;
+  size_t X, H0, H1, QK, VT, KS, VS, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, IDX1, total;
   int ldvt, ldqk;
 };
 
@@ -131,15 +131,20 @@ WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, l
   WsLayout L;
   // row strides are kept off powers of two (+64 / +16 bytes) so that the
   // strided accesses of the attention kernel spread over the L2 channels
+  // fp32 networks keep q | k row-major and v transposed (VT); bf16 networks
+  // keep q row-major and k, v in the tile-swizzled KS, VS (see AttnArgs)
+  const bool bf = os == 2;
   L.ldvt = (int)((R + 63) & ~63L) + 32;
-  L.ldqk = (int)(2 * D + 8);
+  L.ldqk = (int)((bf ? 1 : 2) * D + 8);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   L.X = take((size_t)R * D * 4);
   L.H0 = take((size_t)R * maxw * 4);
   L.H1 = take((size_t)R * maxw * 4);
   L.QK = take((size_t)R * L.ldqk * os);
-  L.VT = take((size_t)D * L.ldvt * os);
+  L.VT = take(bf ? 0 : (size_t)D * L.ldvt * os);
+  L.KS = take(bf ? (size_t)R * D * os : 0);
+  L.VS = take(bf ? (size_t)R * D * os : 0);
   L.MB = take((size_t)R * D * os);
   L.M2 = take((size_t)R * D * os);
   L.HB = take((size_t)R * 2 * D * os);
@@ -365,7 +370,7 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       memset(&g, 0, sizeof(g));
       g.A0 = X; g.lda0 = D; g.K0 = D; g.K = D;
       g.W = atv(w, L, base); g.ldw = D; g.bias = atv(w, L, base + 1);
-      g.C = QK; g.C2 = VT; g.split = 2 * D;
+      g.C = QK; g.C2 = op == SG_BF16 ? ws + wl.VS : VT; g.C3 = ws + wl.KS; g.split = 2 * D;
       GemmBatch b = single(R, 3 * D, wl.ldqk);
       b.p[0].ldct = wl.ldvt;
       HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, 0, EPI_QKV, g, b, R, 3 * D, st); }), "qkv GEMM");
@@ -373,7 +378,8 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
     // multi-head attention: self on even stages, cross on odd stages
     {
       AttnArgs a;
-      a.qk = QK; a.vt = VT; a.out = MB; a.D = D; a.ldvt = wl.ldvt; a.ldqk = wl.ldqk; a.cross = s & 1;
+      a.qk = QK; a.vt = VT; a.ks = ws + wl.KS; a.vs = ws + wl.VS;
+      a.out = MB; a.D = D; a.ldvt = wl.ldvt; a.ldqk = wl.ldqk; a.cross = s & 1;
       a.heads = w->H;
       const int dh = D / w->H;
       a.scale2 = log2e / sqrtf((float)dh);
@@ -842,6 +848,10 @@ sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weig
   float* X = reinterpret_cast<float*>(ws + wl.X);
   if (M) HIPCHK(hipMemcpyAsync(X, xA, M * rb, hipMemcpyDeviceToDevice, st), "copy xA");
   if (N) HIPCHK(hipMemcpyAsync(X + (size_t)pl.seg.row0[1] * weights->D, xB, N * rb, hipMemcpyDeviceToDevice, st), "copy xB");
+  // the 32-row padding of each image is zero, as the encoder leaves it
+  HIPCHK(launch_fill_f32(X + (size_t)M * weights->D, 0.f, (pl.seg.row0[1] - M) * weights->D, st), "zero padding A");
+  HIPCHK(launch_fill_f32(X + (size_t)(pl.seg.row0[1] + N) * weights->D, 0.f, (pl.R - pl.seg.row0[1] - N) * weights->D, st),
+         "zero padding B");
   Timer tm{opts, st};
   if ((s = run_gnn(pl, weights, WL, s0, s1, ws, wl, opts ? opts->flags : 0, tm, st)) != SG_OK) return s;
   if (M) HIPCHK(hipMemcpyAsync(xA, X, M * rb, hipMemcpyDeviceToDevice, st), "copy xA back");

@@ -16,8 +16,9 @@ namespace sg {
 template <typename OpT, int DH, int NW>
 __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg) {
   constexpr bool BF = std::is_same<OpT, bf16>::value;
-  constexpr int NCB = (DH + 31) / 32;  // 32-channel blocks of the output
-  constexpr int QS = BF ? DH / 16 : DH / 8;  // Q / K registers: bf16x8 or float4 per lane
+  constexpr int NCB = (DH + 31) / 32;        // 32-channel blocks of the output
+  constexpr int QS = BF ? DH / 16 : DH / 8;  // Q / K registers per 32 keys: bf16x8 or float4 per lane
+  constexpr int KB = BF ? 2 : 1;             // 32-key blocks per key tile (64 keys in bf16)
   __shared__ float sm_m[NW][32], sm_l[NW][32];
   __shared__ float sm_o[NW][DH][33];
 
@@ -31,68 +32,68 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
   const int src = a.cross ? seg.partner[s] : s;
   const int nk = seg.n[src], krow0 = seg.row0[src];
   const int h = blockIdx.x % H;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hi = lane >> 5, lq = lane & 31;
+  const int lane = threadIdx.x & 63, w = wave_id(), hi = lane >> 5, lq = lane & 31;
   const int D = a.D, ld2 = a.ldqk;
   const OpT* __restrict__ qk = reinterpret_cast<const OpT*>(a.qk);
   const OpT* __restrict__ vt = reinterpret_cast<const OpT*>(a.vt);
 
   typedef typename std::conditional<BF, bf16x8, float4>::type KT;
-  typedef typename std::conditional<BF, bf16x4, float4>::type VT;
-  constexpr int NV = BF ? 4 * NCB : 4 * NCB;  // V registers per lane per tile
+  typedef typename std::conditional<BF, bf16x8, float4>::type VT;
+  constexpr int NV = BF ? 2 * NCB : 4 * NCB;  // V registers per lane per 32 keys
 
+  // Every image occupies a whole number of 32-row tiles of the row space, so
+  // Q, K and V^T loads of any 32-key block of the image stay in bounds
+  // without masks; scores and values of keys past the image are masked, and
+  // queries past the image are not stored.
   // Q^T operand, kept in registers for the whole key loop.  bf16: lane half
   // hi holds dims 16 i + 8 hi .. +7; fp32: dims hi*DH/2 + 4 i .. +3.
-  const int qi = q0 + lq;
-  const bool qvalid = qi < nq;
   KT Qr[QS];
   {
-    const OpT* qp = qk + (size_t)(qrow0 + (qvalid ? qi : 0)) * ld2 + h * DH;
+    const OpT* qp = qk + (size_t)(qrow0 + q0 + lq) * ld2 + h * DH;
 #pragma unroll
-    for (int i = 0; i < QS; ++i) {
-      KT v = BF ? *reinterpret_cast<const KT*>(qp + i * 16 + hi * 8)
-                : *reinterpret_cast<const KT*>(qp + hi * (DH / 2) + 4 * i);
-      if (!qvalid) v = (KT)(OpT)0.f;
-      Qr[i] = v;
-    }
+    for (int i = 0; i < QS; ++i)
+      Qr[i] = BF ? *reinterpret_cast<const KT*>(qp + i * 16 + hi * 8)
+                 : *reinterpret_cast<const KT*>(qp + hi * (DH / 2) + 4 * i);
   }
 
-  // K / V registers of one key tile (32 keys from k0).  V for channel block
-  // cb: bf16: keys k0 + 16 j + 4 hi .. +3 and +8 .. +11 (index 2 (2 cb + j) + 0/1);
-  // fp32: keys k0 + 8 g + 4 hi .. +3 (index 4 cb + g).
-  auto load_tile = [&](int kt, KT* kr, VT* vr) {
-    const int k0 = kt * 32;
-    const bool tail = k0 + 32 > nk;
-    const int ki = k0 + lq;
-    const bool kvalid = ki < nk;
-    const OpT* kp = qk + (size_t)(krow0 + (kvalid ? ki : 0)) * ld2 + D + h * DH;
+  // K / V registers of one 32-key block from key k0.  bf16: the swizzled
+  // blocks of ks / vs give each lane its MFMA operand as one 16-byte load:
+  // K chunk i (dims 16 i.. of the head), V chunk 2 cb + j (output rows =
+  // the 32 features of block f = (h DH + 32 cb) / 32, keys 16 j..).  fp32:
+  // K row-major (dims hi*DH/2 + 4 i), V^T rows, keys 8 g + 4 hi .. +3 (index
+  // 4 cb + g); channels past DH (DH < 32) read channel DH - 1 and are zeroed.
+  auto load_block = [&](int k0, KT* kr, VT* vr) {
+    if constexpr (BF) {
+      const size_t tile = (size_t)((krow0 + k0) >> 5);
+      const bf16* kp = reinterpret_cast<const bf16*>(a.ks) + (tile * (D / 16) + h * (DH / 16)) * 512 + lane * 8;
 #pragma unroll
-    for (int i = 0; i < QS; ++i) {
-      KT v = BF ? *reinterpret_cast<const KT*>(kp + i * 16 + hi * 8)
-                : *reinterpret_cast<const KT*>(kp + hi * (DH / 2) + 4 * i);
-      if (!kvalid) v = (KT)(OpT)0.f;
-      kr[i] = v;
-    }
+      for (int i = 0; i < QS; ++i) kr[i] = *reinterpret_cast<const bf16x8*>(kp + i * 512);
+      const bf16* vp = reinterpret_cast<const bf16*>(a.vs) + (tile * (D / 32) + (h * DH) / 32) * 1024 + lane * 8;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const int c = cb * 32 + lq;
-      const bool cvalid = c < DH;
-      const OpT* vp = vt + (size_t)(h * DH + (cvalid ? c : 0)) * a.ldvt + krow0 + k0;
+      for (int e = 0; e < NV; ++e) vr[e] = *reinterpret_cast<const bf16x8*>(vp + e * 512);
+    } else {
+      const OpT* kp = qk + (size_t)(krow0 + k0 + lq) * ld2 + D + h * DH;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // bf16: e = 2 j + half -> keys 16 j + 8 half + 4 hi; fp32: e = g -> keys 8 g + 4 hi
-        const int koff = BF ? 16 * (e >> 1) + 8 * (e & 1) + 4 * hi : 8 * e + 4 * hi;
-        VT v = (VT)(OpT)0.f;
-        if (cvalid) {
-          if (!tail) {
-            v = *reinterpret_cast<const VT*>(vp + koff);
-          } else {
+      for (int i = 0; i < QS; ++i) kr[i] = *reinterpret_cast<const KT*>(kp + hi * (DH / 2) + 4 * i);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) v[x] = k0 + koff + x < nk ? vp[koff + x] : (OpT)0.f;
-          }
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int c = cb * 32 + lq;
+        const OpT* vp = vt + (size_t)(h * DH + min(c, DH - 1)) * a.ldvt + krow0 + k0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          VT v = *reinterpret_cast<const VT*>(vp + 8 * e + 4 * hi);
+          if (DH < 32 && c >= DH) v = (VT)(OpT)0.f;
+          vr[4 * cb + e] = v;
         }
-        vr[4 * cb + e] = v;
       }
     }
+  };
+  // a key tile = KB blocks; a block past the image (possible in the last
+  // tile) re-reads the image's last block and is fully masked below
+  const int nkb = (nk + 31) >> 5;
+  auto load_tile = [&](int kt, KT (*kr)[QS], VT (*vr)[NV]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) load_block(32 * min(kt * KB + kb, nkb - 1), kr[kb], vr[kb]);
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -100,95 +101,137 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
 #pragma unroll
   for (int c = 0; c < NCB; ++c) O[c] = zero16();
 
-  const int ntk = (nk + 31) >> 5;
-  // PT tiles of this wave are in flight at once (register slots 0..PT-1):
-  // slot j holds tile w + NW (base + j); after it is processed the slot is
-  // refilled with the tile PT rounds ahead.
-  constexpr int PT = BF ? 4 : 2;
-  KT kr[PT][QS];
-  VT vr[PT][NV];
+  // one key tile: S^T = K Q^T per block, online softmax (base 2) over the
+  // tile's 64 keys, O^T += V^T P^T
+  auto process = [&](KT (*kc)[QS], VT (*vc)[NV], int kt) {
+    f32x16 S[KB];
 #pragma unroll
-  for (int j = 0; j < PT; ++j)
-    if (w + NW * j < ntk) load_tile(w + NW * j, kr[j], vr[j]);
-  for (int base = 0; w + NW * base < ntk; base += PT) {
-#pragma unroll
-  for (int j = 0; j < PT; ++j) {
-    const int kt = w + NW * (base + j);
-    if (kt >= ntk) break;
-    const KT* kc = kr[j];
-    const VT* vc = vr[j];
-    const int k0 = kt * 32;
-    f32x16 S = zero16();
+    for (int kb = 0; kb < KB; ++kb) S[kb] = zero16();
     if constexpr (BF) {
 #pragma unroll
-      for (int i = 0; i < QS; ++i) S = mfma(kc[i], Qr[i], S);
+      for (int i = 0; i < QS; ++i)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) S[kb] = mfma(kc[kb][i], Qr[i], S[kb]);
     } else {
 #pragma unroll
-      for (int i = 0; i < QS; ++i) {
-        S = mfma(kc[i].x, Qr[i].x, S);
-        S = mfma(kc[i].y, Qr[i].y, S);
-        S = mfma(kc[i].z, Qr[i].z, S);
-        S = mfma(kc[i].w, Qr[i].w, S);
+      for (int i = 0; i < QS; ++i)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          S[kb] = mfma(kc[kb][i].x, Qr[i].x, S[kb]);
+          S[kb] = mfma(kc[kb][i].y, Qr[i].y, S[kb]);
+          S[kb] = mfma(kc[kb][i].z, Qr[i].z, S[kb]);
+          S[kb] = mfma(kc[kb][i].w, Qr[i].w, S[kb]);
+        }
+    }
+    const int k0 = kt * 32 * KB;
+    // keys past the image (partial last tile): scores -inf, values 0 (padding
+    // rows of V may hold anything a caller staged there)
+    VT vm[KB][NV];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < NV; ++e) vm[kb][e] = vc[kb][e];
+    if (k0 + 32 * KB > nk) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (k0 + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3) >= nk) S[kb][i] = -INFINITY;
+        if constexpr (BF) {
+          // element t of chunk 2 cb + j: key 16 j + 8 (t / 4) + 4 hi + t % 4
+#pragma unroll
+          for (int e = 0; e < NV; ++e)
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+              if (k0 + 32 * kb + 16 * (e & 1) + 8 * (x >> 2) + 4 * hi + (x & 3) >= nk) vm[kb][e][x] = (OpT)0.f;
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int x = 0; x < 4; ++x)
+                if (k0 + 32 * kb + 8 * e + 4 * hi + x >= nk) vm[kb][4 * cb + e][x] = (OpT)0.f;
+        }
       }
     }
-    float e[16], tmax = -INFINITY;
-    if (k0 + 32 <= nk) {
+    float tmax = S[0][0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        e[i] = S[i] * a.scale2;
-        tmax = fmaxf(tmax, e[i]);
-      }
-    } else {  // the last, partial tile: keys past the image are masked
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = k0 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        e[i] = kk < nk ? S[i] * a.scale2 : -INFINITY;
-        tmax = fmaxf(tmax, e[i]);
-      }
-    }
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, S[kb][i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float corr = exp2_fast(m_run - m_new);
-    float p[16], psum = 0.f;
+    const float m_new = fmaxf(m_run, tmax * a.scale2);
+    // rescale the running output only when some query's maximum moved
+    if (__ballot(m_new != m_run)) {
+      const float corr = exp2_fast(m_run - m_new);
+      l_run *= corr;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[i] = exp2_fast(e[i] - m_new);
-      psum += p[i];
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[c][i] *= corr;
+      m_run = m_new;
     }
-    l_run = l_run * corr + psum;
-    m_run = m_new;
 #pragma unroll
-    for (int c = 0; c < NCB; ++c)
+    for (int kb = 0; kb < KB; ++kb) {
+      float p[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) O[c][i] *= corr;
-    if constexpr (BF) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bf16x8 pb;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = (bf16)p[8 * j + i];
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const bf16x4 x0 = vc[4 * cb + 2 * j], x1 = vc[4 * cb + 2 * j + 1];
-          const bf16x8 va = (bf16x8){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          O[cb] = mfma(va, pb, O[cb]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        p[i] = exp2_fast(fmaf(S[kb][i], a.scale2, -m_run));
+        l_run += p[i];
       }
-    } else {
+      if constexpr (BF) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
+        for (int j = 0; j < 2; ++j) {
+          bf16x8 pb;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 v = vc[4 * cb + g4];
-          O[cb] = mfma(v.x, p[4 * g4], O[cb]);
-          O[cb] = mfma(v.y, p[4 * g4 + 1], O[cb]);
-          O[cb] = mfma(v.z, p[4 * g4 + 2], O[cb]);
-          O[cb] = mfma(v.w, p[4 * g4 + 3], O[cb]);
+          for (int i = 0; i < 8; ++i) pb[i] = (bf16)p[8 * j + i];
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) O[cb] = mfma(vm[kb][2 * cb + j], pb, O[cb]);
         }
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 v = vm[kb][4 * cb + g4];
+            O[cb] = mfma(v.x, p[4 * g4], O[cb]);
+            O[cb] = mfma(v.y, p[4 * g4 + 1], O[cb]);
+            O[cb] = mfma(v.z, p[4 * g4 + 2], O[cb]);
+            O[cb] = mfma(v.w, p[4 * g4 + 3], O[cb]);
+          }
+      }
     }
-    const int kt_next = kt + NW * PT;
-    if (kt_next < ntk) load_tile(kt_next, kr[j], vr[j]);
-  }
+  };
+
+  // Wave w takes key tiles w, w + NW, ...  PT of them are in flight: slot j
+  // of round r holds the wave's tile PT r + j.  Rounds whose refills are all
+  // needed run unconditionally (so every path keeps the same loads in
+  // flight); the last one or two rounds drain the ring.
+  const int ntk = (nk + 32 * KB - 1) / (32 * KB);
+  const int mine = ntk > w ? (ntk - w + NW - 1) / NW : 0;
+  constexpr int PT = 2;
+  if (mine > 0) {
+    KT kr[PT][KB][QS];
+    VT vr[PT][KB][NV];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) load_tile(w + NW * min(j, mine - 1), kr[j], vr[j]);
+    int r0 = 0;
+    for (; r0 + 2 * PT <= mine; r0 += PT) {
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        process(kr[j], vr[j], w + NW * (r0 + j));
+        load_tile(w + NW * (r0 + j + PT), kr[j], vr[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      if (r0 + j < mine) process(kr[j], vr[j], w + NW * (r0 + j));
+      if (r0 + j + PT < mine) load_tile(w + NW * (r0 + j + PT), kr[j], vr[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < PT; ++j)
+      if (r0 + PT + j < mine) process(kr[j], vr[j], w + NW * (r0 + PT + j));
   }
 
   l_run += __shfl_xor(l_run, 32);
@@ -196,12 +239,16 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
     sm_m[w][lq] = m_run;
     sm_l[w][lq] = l_run;
   }
+  // output row rho of channel block cb is channel 32 cb + rho of the head
+  // (bf16 with DH < 32: the V block's 32 features start at a multiple of 32,
+  // so head h's channels are rows (h DH) % 32 ..)
+  const int row_off = (BF && DH < 32) ? (h * DH) % 32 : 0;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int c = cb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-      if (c < DH) sm_o[w][c][lq] = O[cb][i];
+      const int c = cb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3) - row_off;
+      if (c >= 0 && c < DH) sm_o[w][c][lq] = O[cb][i];
     }
   __syncthreads();
   OpT* out = reinterpret_cast<OpT*>(a.out);
@@ -224,17 +271,17 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
 
 // Throughput variant (bf16, many workgroups): 128 queries of one image and
 // one head per workgroup, one wave per 32 queries, every wave running over
-// all keys.  64-key tiles of K and of V^T are staged through LDS with
-// coalesced 16-byte loads (double buffered: the next tile is in flight while
-// the current one is consumed) and shared by the four waves.
+// all keys.  64-key tiles of K and V are staged through LDS as their
+// swizzled 1 KB blocks (contiguous 16-byte loads; double buffered: the next
+// tile is in flight while the current one is consumed) and shared by the
+// four waves, which read their MFMA operands as one 16-byte LDS load each.
 template <int DH>
 __global__ __launch_bounds__(256) void k_attention_wide(AttnArgs a, SegTable seg) {
   constexpr int BQ = 128, BKEY = 64;
-  constexpr int KP = DH + 8;    // K tile row pitch (keys x dims)
-  constexpr int VP = BKEY + 8;  // V^T tile row pitch (dims x keys)
-  constexpr int KCH = BKEY * DH / 8 / 256;  // 16-byte chunks per thread per K (and V) tile
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BKEY * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][DH * VP];
+  constexpr int KBLK = DH / 16, VBLK = DH / 16;  // 512-element blocks per 32 keys (K: dim chunks; V: 2 j x DH/32)
+  constexpr int TILE = (BKEY / 32) * (KBLK + VBLK) * 512;  // elements of one staged tile
+  constexpr int KCH = TILE / 8 / 256;                      // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) bf16 Ts[2][TILE];
 
   const int H = a.heads;
   int t = blockIdx.x / H;
@@ -249,10 +296,11 @@ __global__ __launch_bounds__(256) void k_attention_wide(AttnArgs a, SegTable seg
   const int q0 = t * BQ, nq = seg.n[s], qrow0 = seg.row0[s];
   const int src = a.cross ? seg.partner[s] : s;
   const int nk = seg.n[src], krow0 = seg.row0[src];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), hi = lane >> 5, lq = lane & 31;
   const int D = a.D, ldq = a.ldqk;
   const bf16* __restrict__ qk = reinterpret_cast<const bf16*>(a.qk);
-  const bf16* __restrict__ vt = reinterpret_cast<const bf16*>(a.vt);
+  const bf16* __restrict__ ks = reinterpret_cast<const bf16*>(a.ks);
+  const bf16* __restrict__ vs = reinterpret_cast<const bf16*>(a.vs);
 
   const int qi = q0 + 32 * w + lq;
   const bool qvalid = qi < nq;
@@ -267,35 +315,26 @@ __global__ __launch_bounds__(256) void k_attention_wide(AttnArgs a, SegTable seg
     }
   }
 
-  // cooperative tile loads: K chunk c -> key c / (DH/8), dims (c % (DH/8)) * 8;
-  // V^T chunk c -> dim c / 8, keys (c % 8) * 8
-  bf16x8 kreg[KCH], vreg[KCH];
+  // Staged tile layout: for each 32-key block kb, the head's KBLK K blocks,
+  // then its VBLK V blocks (2 cb + j), 512 elements each.  Chunk c of the
+  // tile is element 8 c; a 32-key block past the image's last one re-reads
+  // that block (its keys are masked).
+  const int nkb = (nk + 31) >> 5;
+  bf16x8 treg[KCH];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + 256 * i;
-      const int key = c / (DH / 8), part = c % (DH / 8);
-      bf16x8 v = (bf16x8)(bf16)0.f;
-      if (k0 + key < nk) v = *reinterpret_cast<const bf16x8*>(qk + (size_t)(krow0 + k0 + key) * ldq + D + h * DH + part * 8);
-      kreg[i] = v;
-      const int dim = c / 8, kp = (c % 8) * 8;
-      const bf16* vp = vt + (size_t)(h * DH + dim) * a.ldvt + krow0 + k0 + kp;
-      if (k0 + kp + 8 <= nk) {
-        v = *reinterpret_cast<const bf16x8*>(vp);
-      } else {
-#pragma unroll
-        for (int x = 0; x < 8; ++x) v[x] = k0 + kp + x < nk ? vp[x] : (bf16)0.f;
-      }
-      vreg[i] = v;
+      const int kb = c / ((KBLK + VBLK) * 64), r = c % ((KBLK + VBLK) * 64);
+      const size_t tile = (size_t)((krow0 + 32 * min(k0 / 32 + kb, nkb - 1)) >> 5);
+      const bf16* src = r < KBLK * 64 ? ks + (tile * (D / 16) + h * (DH / 16)) * 512 + 8 * r
+                                      : vs + (tile * (D / 32) + (h * DH) / 32) * 1024 + 8 * (r - KBLK * 64);
+      treg[i] = *reinterpret_cast<const bf16x8*>(src);
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<bf16x8*>(&Ks[buf][(c / (DH / 8)) * KP + (c % (DH / 8)) * 8]) = kreg[i];
-      *reinterpret_cast<bf16x8*>(&Vs[buf][(c / 8) * VP + (c % 8) * 8]) = vreg[i];
-    }
+    for (int i = 0; i < KCH; ++i) *reinterpret_cast<bf16x8*>(&Ts[buf][8 * (tid + 256 * i)]) = treg[i];
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -314,12 +353,10 @@ __global__ __launch_bounds__(256) void k_attention_wide(AttnArgs a, SegTable seg
     for (int kb = 0; kb < BKEY / 32; ++kb) {
       const int k0 = kt * BKEY + kb * 32;
       if (k0 >= nk) break;
+      const bf16* tb = &Ts[cur][kb * (KBLK + VBLK) * 512 + lane * 8];
       f32x16 S = zero16();
 #pragma unroll
-      for (int i = 0; i < DH / 16; ++i) {
-        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&Ks[cur][(kb * 32 + lq) * KP + i * 16 + hi * 8]);
-        S = mfma(kv, Qr[i], S);
-      }
+      for (int i = 0; i < DH / 16; ++i) S = mfma(*reinterpret_cast<const bf16x8*>(tb + i * 512), Qr[i], S);
       float e[16], tmax = -INFINITY;
       if (k0 + 32 <= nk) {
 #pragma unroll
@@ -354,14 +391,19 @@ __global__ __launch_bounds__(256) void k_attention_wide(AttnArgs a, SegTable seg
 #pragma unroll
           for (int i = 0; i < 16; ++i) O[c][i] *= corr;
       }
+      // values of keys past the image are zeroed (their P is 0, but padding
+      // rows may hold anything a caller staged there)
+      const bool vtail = k0 + 32 > nk;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int cb = 0; cb < DH / 32; ++cb) {
-          const bf16* vp = &Vs[cur][(cb * 32 + lq) * VP + kb * 32 + 16 * j + 4 * hi];
-          const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(vp);
-          const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(vp + 8);
-          const bf16x8 va = (bf16x8){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          bf16x8 va = *reinterpret_cast<const bf16x8*>(tb + (KBLK + 2 * cb + j) * 512);
+          if (vtail) {
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+              if (k0 + 16 * j + 8 * (x >> 2) + 4 * hi + (x & 3) >= nk) va[x] = (bf16)0.f;
+          }
           O[cb] = mfma(va, pb[j], O[cb]);
         }
     }
@@ -399,7 +441,8 @@ hipError_t launch_attention(int op, int dh, const AttnArgs& a, const SegTable& s
     hipLaunchKernelGGL((k_attention_wide<64>), dim3(wide_tiles * heads), dim3(256), 0, st, a, seg);
     return hipGetLastError();
   }
-  constexpr int NW = 8;
+  // four waves (one per SIMD, up to 512 registers each) split the key tiles
+  constexpr int NW = 4;
   dim3 grid(tiles * heads);
   if (op == SG_BF16) {
     if (dh == 64) hipLaunchKernelGGL((k_attention<bf16, 64, NW>), grid, dim3(64 * NW), 0, st, a, seg);

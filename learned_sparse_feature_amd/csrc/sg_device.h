@@ -29,6 +29,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
+// Index of this thread's wave in the workgroup, as a scalar: deriving loop
+// bounds and addresses from it keeps wave-uniform control flow on the scalar
+// unit instead of exec-mask branches.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // Cross-lane moves inside each row of 16 lanes (DPP): quad_perm [1,0,3,2]
 // and [2,3,0,1] swap neighbours and pairs, row_half_mirror (0x141) and
 // row_mirror (0x140) reverse 8- and 16-lane groups.

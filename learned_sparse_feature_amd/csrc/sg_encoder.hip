@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void k_encoder(EncArgs e, SegTable seg) {
   const float* de = e.desc[isA ? 0 : 1] + (size_t)e.D * (seg.in_off[s] + p0);
   const float iw = e.img[isA ? 0 : 2], ih = e.img[isA ? 1 : 3];
   const size_t row0 = (size_t)seg.row0[s] + p0;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
 
   // layer 0 (3 -> w1) with ReLU; rows past the image are zero
   {

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   const GemmProblem P = bt.p[tz];
   const int r0 = tx * BM, n0 = ty * BN;
   if (r0 >= P.rows || n0 >= P.n_out) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
 
   // chunk c = tid + 256 h of a tile covers row c / 8, columns (c % 8) * CH;
@@ -177,6 +177,65 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
     }
   }
 
+  if constexpr (EPI == EPI_QKV && BF) {
+    // bf16 q | k | v, per 32x32 block: q row-major into C; k through a
+    // wave-private LDS transposition into the tile-swizzled C3; v straight
+    // from the accumulators into the tile-swizzled C2 (its layout is the
+    // accumulator layout).  Column ranges: q [0, D), k [D, 2D), v [2D, 3D)
+    // with D = split / 2; the QKV GEMM covers the whole row space, so the
+    // problem's rows are the compact rows (32-row tiles stay aligned).
+    const int Dm = g.split / 2;
+    constexpr int TP = 32 + 8;
+    bf16* tt = reinterpret_cast<bf16*>(&As[0][0]) + wave * 32 * TP;
+    bf16* const cq = reinterpret_cast<bf16*>(g.C);
+    bf16* const cv = reinterpret_cast<bf16*>(g.C2);
+    bf16* const ck = reinterpret_cast<bf16*>(g.C3);
+    const int nl = lane & 31;
+    __syncthreads();  // every wave is done with the A tiles: As is scratch now
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int rr0 = r0 + wm * (BM / 2) + i * 32, nn0 = n0 + wn * (BN / 2) + j * 32;
+        if (rr0 >= P.rows || nn0 >= P.n_out) continue;
+        const float bias = g.bias ? (float)reinterpret_cast<const WT*>(g.bias)[nn0 + nl] : 0.f;
+        const int tile = rr0 >> 5;
+        if (nn0 < Dm) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = rr0 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            cq[P.c_off + (size_t)r * P.ldc + nn0 + nl] = (bf16)(acc[i][j][e] + bias);
+          }
+        } else if (nn0 < 2 * Dm) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            tt[nl * TP + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)] = (bf16)(acc[i][j][e] + bias);
+          __builtin_amdgcn_wave_barrier();
+          // chunk c: 16-dim half `which` of the block's 32 columns, lane slot L
+#pragma unroll
+          for (int c = lane; c < 128; c += 64) {
+            const int L = c & 63, which = c >> 6;
+            bf16x8 v;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = tt[(16 * which + 8 * (L >> 5) + t) * TP + (L & 31)];
+            const size_t blk = (size_t)tile * (Dm / 16) + (nn0 - Dm) / 16 + which;
+            *reinterpret_cast<bf16x8*>(ck + blk * 512 + L * 8) = v;
+          }
+          __builtin_amdgcn_wave_barrier();
+        } else {
+          bf16* base = cv + ((size_t)tile * (Dm / 32) + (nn0 - 2 * Dm) / 32) * 1024 + lane * 8;
+          bf16x8 lo, hi8;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            lo[x] = (bf16)(acc[i][j][x] + bias);
+            hi8[x] = (bf16)(acc[i][j][8 + x] + bias);
+          }
+          *reinterpret_cast<bf16x8*>(base) = lo;
+          *reinterpret_cast<bf16x8*>(base + 512) = hi8;
+        }
+      }
+    return;
+  }
   if constexpr (EPI == EPI_QKV) {
     if (n0 >= g.split) {
       // V columns: written transposed (VT [n - split][r]).  Each 32x32 block

@@ -67,7 +67,8 @@ struct GemmArgs {
   const void* W; int ldw;            // weights [n_out][K]
   const void* bias;                  // [n_out] or null
   int K;
-  void* C; void* C2;                 // outputs (C2: VT or ZT)
+  void* C; void* C2;                 // outputs (C2: VT / VS or ZT)
+  void* C3;                          // EPI_QKV, bf16: KS
   float scale;
   int split;                         // EPI_QKV: first column that goes to VT
   int gx, gy;                        // row and column tiles (set by the launcher)
@@ -87,9 +88,21 @@ struct EncArgs {
   float* X;              // states [R][ldx]
 };
 
+// Attention operands.  fp32 networks: qk [R][ldqk] holds q (columns
+// h*dh..) and k (columns D + h*dh..), vt [D][ldvt] holds v transposed.
+// bf16 networks: qk holds q only; k and v are tile-swizzled so that every
+// MFMA operand fragment is 16 contiguous bytes per lane (one 1 KB load per
+// wave):
+//   ks: [R/32][D/16][64][8]: block (tile, c) holds rows 32 tile.. and
+//       columns 16 c..; lane L, element t is k[32 tile + L%32][16 c + 8 (L/32) + t];
+//   vs: [R/32][D/32][2][64][8]: block (tile, f, j), lane L, element t is
+//       v[32 tile + 16 j + 8 (t/4) + 4 (L/32) + t%4][32 f + L%32], which is
+//       the accumulator layout of a 32x32 MFMA block (elements 8j..8j+7).
 struct AttnArgs {
-  const void* qk;    // [R][2D]: q at columns h*dh.., k at D + h*dh..
-  const void* vt;    // [D][ldvt]: v transposed
+  const void* qk;
+  const void* vt;    // fp32
+  const void* ks;    // bf16
+  const void* vs;    // bf16
   void* out;         // [R][D] message (heads concatenated)
   int D, ldvt, ldqk, cross, heads;
   float scale2;      // log2(e) / sqrt(dh)

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void k_sink_rows(const float* __restrict__ Zb,
   const int gb = blockIdx.x - pt.gpre[b];
   const int M = pt.M[b], N = pt.N[b];
   const int i0 = gb * RB;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int ldz = ld4(N);
   const float* zp = Zb + pt.z_off[b];
   const float* vv = v_in ? v_in + pt.voff[b] : nullptr;
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(256) void k_lse(const float* __restrict__ Zbase, Pa
                                              const float* __restrict__ alpha_dev) {
   if (alpha_dev) alpha2 = alpha_dev[0] * kLog2e;
   const int lane = threadIdx.x & 63;
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int g = blockIdx.x * 4 + wave_id();
   const int* pre = which ? pt.vpre : pt.upre;
   const int b = find_pair(pre, pt.n_pairs, g);
   if (b >= pt.n_pairs) return;
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256) void k_col_argmax(const float* __restrict__ ZT
                                                     int* __restrict__ idx1, int Npad,
                                                     int32_t* __restrict__ m1, float* __restrict__ s1) {
   const int lane = threadIdx.x & 63;
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int g = blockIdx.x * 4 + wave_id();
   // flattened real columns: the prefix of N over the pairs is vpre[b] - b
   int b = 0;
   while (b < pt.n_pairs && g >= pt.vpre[b + 1] - (b + 1)) ++b;
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(256) void k_sink_extract(const float* __restrict__ 
                                                       float* __restrict__ s1) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x * 4 + wave_id();
   const int M = pt.M[b], N = pt.N[b];
   const bool empty = M == 0 || N == 0;
   if (m1 && t >= N && t < Npad && lane == 0) {  // padded side-B entries
