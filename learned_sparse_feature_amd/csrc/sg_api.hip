@@ -263,6 +263,13 @@ void make_plan(const Problem& p, Plan& pl) {
   int R = 0;
   long zf = 0, ztf = 0, pf = 0;
   pl.pt.n_pairs = p.B;
+  // Sinkhorn schedule: forced by a flag, else by the score matrices' size:
+  // two sweeps up to SG_TWO_SWEEP_MAX_BYTES, one pass with a column
+  // reduction beyond
+  long zbytes = 0;
+  for (int b = 0; b < p.B; ++b) zbytes += 4L * p.M[b] * ld4(p.N[b]);
+  pl.two_sweep = (p.flags & SG_FLAG_SINKHORN_TWO_SWEEP) ||
+                 (!(p.flags & SG_FLAG_SINKHORN_ONE_SWEEP) && zbytes <= (long)SG_TWO_SWEEP_MAX_BYTES);
   pl.pt.rb = sink_rows_per_block(p.M.data(), p.N.data(), p.B);
   pl.seg.n_seg = 2 * p.B;
   for (int b = 0; b < p.B; ++b) {
@@ -291,8 +298,6 @@ void make_plan(const Problem& p, Plan& pl) {
   }
   pl.R = R;
   pl.zf = zf; pl.pf = pf; pl.pd = pl.pt.gpre[p.B];
-  pl.two_sweep = (p.flags & SG_FLAG_SINKHORN_TWO_SWEEP) ||
-                 (!(p.flags & SG_FLAG_SINKHORN_ONE_SWEEP) && zf * 4 <= (long)SG_TWO_SWEEP_MAX_BYTES);
   pl.ztf = pl.two_sweep ? ztf : 0;
   pl.ru = pl.pt.upre[p.B]; pl.rv = pl.pt.vpre[p.B];
   pl.nb = pl.rv - p.B;
@@ -697,13 +702,14 @@ size_t sg_workspace_size(const sg_weights* w, int32_t Mmax, int32_t Nmax, int32_
   if (check_config(w) != SG_OK || Mmax < 0 || Nmax < 0 || batch < 1) return 0;
   const long B = batch;
   const long R = B * (round32(Mmax) + round32(Nmax));
-  // column partials: at most ceil((Mmax+1)/4) row blocks per pair
   // the transposed scores exist only for the two-sweep schedule, which the
   // default rule picks for at most SG_TWO_SWEEP_MAX_BYTES of Z (ZT exceeds Z
   // by at most its row padding)
   const long ztf = std::min(B * Nmax * ld4(Mmax), (long)(SG_TWO_SWEEP_MAX_BYTES / 4) + 3 * B * Nmax);
-  WsLayout wl = ws_layout(w, R, B * Mmax * ld4(Nmax), ztf, B * ((Mmax + 4) / 4) * ld4(Nmax), B * ((Mmax + 4) / 4),
-                          B * ld4(Mmax + 1), B * ld4(Nmax + 1), B * Nmax);
+  // column partials: at most ceil((Mmax+1)/4) row blocks per pair
+  const long G = (Mmax + 4) / 4;
+  WsLayout wl = ws_layout(w, R, B * Mmax * ld4(Nmax), ztf, B * G * ld4(Nmax), B * G, B * ld4(Mmax + 1),
+                          B * ld4(Nmax + 1), B * Nmax);
   return wl.total;
 }
 
@@ -711,9 +717,8 @@ size_t sg_stage_match_workspace_size(int32_t M, int32_t N, int32_t D) {
   if (M < 0 || N < 0 || D <= 0) return 0;
   const long R = round32(M) + round32(N);
   const long ztf = std::min((long)N * ld4(M), (long)(SG_TWO_SWEEP_MAX_BYTES / 4) + 3L * N);
-  return ws_layout_raw(D, 4, 0, R, (long)M * ld4(N), ztf, (long)((M + 4) / 4) * ld4(N), (M + 4) / 4, ld4(M + 1),
-                       ld4(N + 1), N)
-      .total;
+  const long G = (M + 4) / 4;
+  return ws_layout_raw(D, 4, 0, R, (long)M * ld4(N), ztf, G * ld4(N), G, ld4(M + 1), ld4(N + 1), N).total;
 }
 
 sg_status sg_match(const float* kptsA, const float* descA, const float* confA, int32_t M,

@@ -40,6 +40,7 @@ __device__ __forceinline__ float f4c(const float4& q, int c) {
 // dustbin column (flattened over pairs by gpre).  ARG: also the per-block
 // column argmax of Z + u over the real rows into PV / PI.  update_u = 0
 // (no Sinkhorn iteration) takes u = 0 and writes only PV / PI.
+
 template <int RPW, int NV4, bool ARG>
 __global__ __launch_bounds__(256) void k_sink_rows(const float* __restrict__ Zb, PairTable pt,
                                                    const float* __restrict__ v_in,
@@ -60,8 +61,8 @@ __global__ __launch_bounds__(256) void k_sink_rows(const float* __restrict__ Zb,
   const int lane = threadIdx.x & 63, w = wave_id();
   const int ldz = ld4(N);
   const float* zp = Zb + pt.z_off[b];
-  const float* vv = v_in ? v_in + pt.voff[b] : nullptr;
   const float lmn = log2f((float)(M + N));
+  const float* vv = v_in ? v_in + pt.voff[b] : nullptr;
 
   float vc[NV4][4];
 #pragma unroll
@@ -76,6 +77,22 @@ __global__ __launch_bounds__(256) void k_sink_rows(const float* __restrict__ Zb,
   // ---- row update of the wave's rows; e keeps 2^(t - m)
   float e[RPW][NV4][4], wgt[RPW];
   float dT = 0.f;  // lane 0: this wave's dustbin-column partial
+  // all of the wave's row loads are issued before any row is reduced (at a
+  // real row and column, clamped in bounds; replaced below where the entry
+  // is the dustbin row, a masked column or a row past it)
+  if (M > 0 && N > 0) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int ic = min(i0 + w * RPW + r, M - 1);
+#pragma unroll
+      for (int k = 0; k < NV4; ++k) {
+        const float4 q = *reinterpret_cast<const float4*>(zp + (size_t)ic * ldz + min(4 * (lane + 64 * k), ldz - 4));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) e[r][k][c] = f4c(q, c);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int i = i0 + w * RPW + r;
@@ -91,10 +108,8 @@ __global__ __launch_bounds__(256) void k_sink_rows(const float* __restrict__ Zb,
 #pragma unroll
     for (int k = 0; k < NV4; ++k) {
       const int j = 4 * (lane + 64 * k);
-      float4 q = make_float4(alpha2, alpha2, alpha2, alpha2);
-      if (i < M && j < N) q = *reinterpret_cast<const float4*>(zp + (size_t)i * ldz + j);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) e[r][k][c] = j + c < N ? f4c(q, c) + vc[k][c] : -INFINITY;
+      for (int c = 0; c < 4; ++c) e[r][k][c] = j + c < N ? (i < M ? e[r][k][c] : alpha2) + vc[k][c] : -INFINITY;
     }
     float mx = lane == 0 ? alpha2 + vN : -INFINITY;
 #pragma unroll

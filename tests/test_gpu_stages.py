@@ -131,8 +131,9 @@ def test_final_projection_parity(cid, n):
 
 # --------------------------------------------- scores + Sinkhorn + extraction
 
-# Both Sinkhorn schedules ("two": sweeps over Z and its transpose; "one": a
-# single pass over Z with per-block column partials) run every case.
+# Both Sinkhorn schedules run every case: "two" (sweeps over Z and its
+# transpose) and "one" (one pass over Z with per-block column partials, then
+# a column reduction).
 SCHEDULES = ["two", "one"]
 
 
