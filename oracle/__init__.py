@@ -25,7 +25,12 @@ Readings taken where the pages are silent (each also pinned by a test):
 * both images are updated from the pre-stage states of a stage;
 * argmax ties go to the lowest index; the match threshold is strict '>';
 * masked (padded) keys and points are simply absent: a padded pair is the
-  unpadded pair.
+  unpadded pair;
+* double-softmax head ([LightGlue-review] section 2.4): the similarity is
+  the same S = f_A f_B^T / sqrt(D) (the page divides each projected
+  descriptor by D^(1/4)); the matchability logit reads the last GNN states
+  x^(L), not the projected f; the log assignment is extracted with the same
+  mutual argmax and threshold as the Sinkhorn head.
 
 Parity status: every function below is pinned by `tests/test_oracle_*.py`
 except the end-to-end composition with trained weights, which no page prints
@@ -41,6 +46,8 @@ __all__ = [
     "score_matrix", "logsumexp", "log_sinkhorn_iterations",
     "log_optimal_transport", "extract_matches", "superglue_match",
     "superglue_descriptors", "sinkhorn_knopp_exp", "match_from_descriptors",
+    "log_sigmoid", "matchability", "double_softmax_assignment",
+    "double_softmax_from_descriptors", "double_softmax_match",
 ]
 
 
@@ -267,3 +274,65 @@ def sinkhorn_knopp_exp(Zbar, a, b, iters):
         P = P * (a / P.sum(axis=1))[:, None]
         P = P * (b / P.sum(axis=0))[None, :]
     return P
+
+
+# ------------------------------------------------- double-softmax head
+# [LightGlue-review] section 2.4 (the matching head that replaces the
+# optimal-transport layer with a closed form).
+
+
+def log_sigmoid(z):
+    """log(1 / (1 + exp(-z))), written as min(z, 0) - log(1 + exp(-|z|)) so
+    that it is finite for any finite z."""
+    z = _f64(z)
+    return np.minimum(z, 0.0) - np.log1p(np.exp(-np.abs(z)))
+
+
+def matchability(x, wz, bz):
+    """[LightGlue-review] section 2.4: a unary matchability logit per point,
+    a Linear(D, 1) of its state: z_i = <w, x_i> + b."""
+    return _f64(x) @ _f64(wz).reshape(-1) + float(bz)
+
+
+def double_softmax_assignment(S, z0, z1):
+    """[LightGlue-review] section 2.4: the (M+1) x (N+1) log assignment.
+    Real block: the log-softmax of S over j (each row) plus the log-softmax
+    of S over i (each column) plus log sigmoid(z0_i) + log sigmoid(z1_j).
+    Last column (i < M): log sigmoid(-z0_i); last row (j < N):
+    log sigmoid(-z1_j); the corner stays 0."""
+    S = _f64(S)
+    M, N = S.shape
+    z0, z1 = _f64(z0).reshape(M), _f64(z1).reshape(N)
+    row_term = S - logsumexp(S, axis=1)[:, None]
+    col_term = S - logsumexp(S, axis=0)[None, :]
+    out = np.zeros((M + 1, N + 1))
+    out[:M, :N] = row_term + col_term + log_sigmoid(z0)[:, None] + log_sigmoid(z1)[None, :]
+    out[:M, N] = log_sigmoid(-z0)
+    out[M, :N] = log_sigmoid(-z1)
+    return out
+
+
+def double_softmax_from_descriptors(fA, fB, xA, xB, wz, bz, threshold=0.0):
+    """Similarity, matchability, log assignment and extraction of the
+    double-softmax head from matching descriptors f and last states x."""
+    S = score_matrix(fA, fB)
+    z0, z1 = matchability(xA, wz, bz), matchability(xB, wz, bz)
+    logP = double_softmax_assignment(S, z0, z1)
+    m0, s0, m1, s1 = extract_matches(logP, threshold)
+    return {"S": S, "z0": z0, "z1": z1, "logP": logP,
+            "matches0": m0, "scores0": s0, "matches1": m1, "scores1": s1}
+
+
+def double_softmax_match(pair, weights, L=None, threshold=0.0):
+    """The whole forward pass with the double-softmax head for one pair: the
+    encoder and GNN of superglue_descriptors, then the head above with
+    weights["wz"] ([D]) and weights["bz"] (scalar)."""
+    M = len(pair["kpts0"])
+    N = len(pair["kpts1"])
+    if M == 0 or N == 0:
+        return {"matches0": -np.ones(M, np.int32), "scores0": np.zeros(M),
+                "matches1": -np.ones(N, np.int32), "scores1": np.zeros(N)}
+    out = superglue_descriptors(pair, weights, L)
+    out.update(double_softmax_from_descriptors(out["f0"], out["f1"], out["xL_0"], out["xL_1"],
+                                               weights["wz"], weights["bz"], threshold))
+    return out

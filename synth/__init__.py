@@ -93,7 +93,8 @@ def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
     last encoder bias and the last bias of every update MLP, which stay zero.
     For a bf16 network every value is rounded to bf16.  Draw order: encoder
     layers, then per stage q, k, v, merge, mlp1, mlp2 (each W then b), then the
-    final projection.  The dustbin score is `alpha`.
+    final projection, then the matchability weight and bias of the
+    double-softmax head ("wz" [D], "bz").  The dustbin score is `alpha`.
     """
     if seed is None:
         seed = (BIAS_ON_SEED_BASE if bias_on else WEIGHT_SEED_BASE) + cfg.cid
@@ -117,12 +118,18 @@ def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
         stages.append(st)
     Wf = _xavier(rng, D, D)
     bf = _bias(rng, D, D, bias_on, zero=False)
+    # matchability Linear(D, 1) of the double-softmax head, drawn last so
+    # that every earlier tensor is the same with or without it
+    wz = _xavier(rng, 1, D)[0]
+    bz = _bias(rng, 1, D, bias_on, zero=False)[0]
     w = {"enc": enc, "stages": stages, "Wf": Wf, "bf": bf, "alpha": float(alpha),
-         "D": D, "H": cfg.H, "L": L, "dtype": cfg.dtype}
+         "wz": wz, "bz": float(bz), "D": D, "H": cfg.H, "L": L, "dtype": cfg.dtype}
     if cfg.dtype == "bf16":
         w["enc"] = [(round_to_bf16(W), round_to_bf16(b)) for W, b in w["enc"]]
         w["stages"] = [{k: round_to_bf16(v) for k, v in st.items()} for st in w["stages"]]
         w["Wf"], w["bf"] = round_to_bf16(w["Wf"]), round_to_bf16(w["bf"])
+        w["wz"] = round_to_bf16(w["wz"])
+        w["bz"] = float(round_to_bf16(np.array([w["bz"]], np.float32))[0])
     return w
 
 
