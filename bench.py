@@ -7,7 +7,10 @@ T = 100, bf16 GNN operands with fp32 accumulation, fp32 Sinkhorn), inputs
 resident in HBM before the timed region.  Prints one JSON line on stdout;
 progress goes to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--head ds]
+
+--head ds replaces the Sinkhorn head by the double-softmax + matchability
+head (section 2.4 of the LightGlue review) on the same network and pair.
 """
 from __future__ import annotations
 
@@ -22,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "image pairs/sec (L=9 GNN + T=100 Sinkhorn) at M=N=1024; MFMA util %"
+METRIC_DS = "image pairs/sec (L=9 GNN + double-softmax head) at M=N=1024"
 PEAK = {"hbm_GBps": 8000.0, "bf16_TFLOPs": 2500.0, "f32_TFLOPs": 157.3}
 
 
@@ -53,6 +57,13 @@ def sinkhorn_bytes(M, N, T):
     return [4.0 * (M + 1) * (N + 1)] * (2 * T)
 
 
+def ds_bytes(M, N, D):
+    """One launch of the double-softmax statistics: Z and its transpose read
+    once, every point's fp32 state read once, u, v and the dustbin entries
+    written."""
+    return [8.0 * M * N + 4.0 * D * (M + N) + 8.0 * (M + N)]
+
+
 def profiled_traffic(kernel, profile="superglue_pair1024_bf16_hbm_traffic.txt"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary, or None when it is missing or the kernel's source has
@@ -76,7 +87,7 @@ def profiled_traffic(kernel, profile="superglue_pair1024_bf16_hbm_traffic.txt"):
     return None
 
 
-def cpu_baseline(cfg, w, pair, budget_s=12.0, max_pairs=3):
+def cpu_baseline(cfg, w, pair, head="sinkhorn", budget_s=12.0, max_pairs=3):
     import oracle
     try:
         import threadpoolctl
@@ -86,13 +97,17 @@ def cpu_baseline(cfg, w, pair, budget_s=12.0, max_pairs=3):
     t0 = time.perf_counter()
     n = 0
     while n < max_pairs:
-        oracle.superglue_match(pair, w, T=cfg.T)
+        if head == "ds":
+            oracle.double_softmax_match(pair, w)
+        else:
+            oracle.superglue_match(pair, w, T=cfg.T)
         n += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} full passes of the same 1024x1024 pair (L=9, T=100) by the float64 numpy "
+            "sample": f"{n} full passes of the same 1024x1024 pair (L=9, "
+                      f"{'double-softmax head' if head == 'ds' else 'T=100'}) by the float64 numpy "
                       f"oracle, {dt:.1f} s wall"}
 
 
@@ -107,6 +122,8 @@ def main():
                     help="also time sg_match_batch on this many 1024x1024 pairs per call (0: skip)")
     ap.add_argument("--sinkhorn", choices=["auto", "two", "one"], default="auto",
                     help="Sinkhorn schedule (default: chosen by problem size)")
+    ap.add_argument("--head", choices=["sinkhorn", "ds"], default="sinkhorn",
+                    help="matching head: Sinkhorn (default) or double softmax + matchability")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="before the steps, copy this many MiB with a plain device copy (counter scaling)")
     args = ap.parse_args()
@@ -126,7 +143,10 @@ def main():
     cfg = synth.CONFIGS[2]
     w = synth.make_weights(cfg)
     pair = synth.make_pair(cfg)
-    W = sg.pack_weights(w, device=dev)
+    W = sg.pack_weights(w, device=dev, head=args.head)
+    ds = args.head == "ds"
+    # launches and algorithmic bytes of the head's normalisation kernels
+    norm_work = ds_bytes(cfg.M, cfg.N, cfg.D) if ds else sinkhorn_bytes(cfg.M, cfg.N, cfg.T)
     keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
     t = [torch.from_numpy(pair[k]).to(dev) for k in keys]
     img = (*pair["image_size0"], *pair["image_size1"])
@@ -172,7 +192,7 @@ def main():
         step(stage_events=ev)
         torch.cuda.synchronize()
         acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(sg.SG_N_STAGE_EVENTS - 1)]
-    names = ["encoder", "gnn", "projection_scores", "sinkhorn", "extraction"]
+    names = ["encoder", "gnn", "projection_scores", "ds_stats" if ds else "sinkhorn", "extraction"]
     stages = {n: round(float(v / nrep), 4) for n, v in zip(names, acc)}
     log(f"stages (ms): {stages}")
 
@@ -180,7 +200,7 @@ def main():
     roofline = None
     if not args.no_kernel_timing:
         specs = {
-            "sinkhorn": (sg.SG_K_SINKHORN, sinkhorn_bytes(M, N, cfg.T)),
+            "sinkhorn": (sg.SG_K_SINKHORN, norm_work),
             "attention": (sg.SG_K_ATTENTION, attention_flops(cfg, M, N)),
             "gemm": (sg.SG_K_GEMM, [f for _, f in gemm_flops(cfg, M, N)]),
         }
@@ -209,14 +229,21 @@ def main():
         # Sinkhorn stage time (stage events, no event between the launches)
         # over the 2T launches.  Bracketing each launch with its own pair of
         # events adds the event and dispatch latency (~2.5 us) to every launch.
-        per = stages["sinkhorn"] * 1e3 / (2 * cfg.T)
+        # (the double-softmax head has one such launch: its stage time)
+        nn = len(norm_work)
+        per = stages["ds_stats" if ds else "sinkhorn"] * 1e3 / nn
         kernels["sinkhorn"]["bracketed_avg_us"] = kernels["sinkhorn"]["avg_us"]
         kernels["sinkhorn"]["avg_us"] = round(per, 3)
-        kernels["sinkhorn"]["total_us"] = round(per * 2 * cfg.T, 2)
-        kernels["sinkhorn"]["achieved_GBps"] = round(sinkhorn_bytes(M, N, cfg.T)[0] / (per * 1e-6) / 1e9, 1)
+        kernels["sinkhorn"]["total_us"] = round(per * nn, 2)
+        kernels["sinkhorn"]["achieved_GBps"] = round(norm_work[0] / (per * 1e-6) / 1e9, 1)
+        kernels["sinkhorn"]["frac_hbm"] = round(norm_work[0] / (per * 1e-6) / 1e9 / PEAK["hbm_GBps"], 4)
+        if ds:
+            kernels["ds_stats"] = kernels.pop("sinkhorn")
+            kernels["ds_stats"]["kernel"] = "k_ds_stats (row / column lse over Z and Z^T + matchability)"
         # the same bracketing latency, measured here on the Sinkhorn launches,
         # is removed from the other classes' bracketed launch times
-        over = max(0.0, kernels["sinkhorn"]["bracketed_avg_us"] - per)
+        nk = "ds_stats" if ds else "sinkhorn"
+        over = max(0.0, kernels[nk]["bracketed_avg_us"] - per)
         for k in ("attention", "gemm"):
             kk = kernels[k]
             kk["bracketed_avg_us"] = kk["avg_us"]
@@ -227,9 +254,16 @@ def main():
                 if f in kk:
                     kk[f] = round(kk[f] * scale, 2)
         kernels["bracket_latency_us"] = round(over, 3)
-        dom = max(("sinkhorn", "attention", "gemm"), key=lambda k: kernels[k]["total_us"])
-        if dom == "sinkhorn":
-            per_launch = sinkhorn_bytes(M, N, cfg.T)[0]
+        dom = max((nk, "attention", "gemm"), key=lambda k: kernels[k]["total_us"])
+        if dom == "ds_stats":
+            per_launch = norm_work[0]
+            ach = per_launch / (kernels[dom]["avg_us"] * 1e-6) / 1e9
+            roofline = {"kernel": kernels[dom]["kernel"], "bound": "hbm", "achieved": round(ach, 1),
+                        "peak": PEAK["hbm_GBps"], "unit": "GB/s", "frac": round(ach / PEAK["hbm_GBps"], 4),
+                        "traffic": None, "algorithmic_bytes_per_launch": per_launch,
+                        "avg_launch_us": kernels[dom]["avg_us"]}
+        elif dom == "sinkhorn":
+            per_launch = norm_work[0]
             ach = per_launch / (kernels[dom]["avg_us"] * 1e-6) / 1e9
             tr = profiled_traffic("k_lse") if args.sinkhorn != "one" else None
             roofline = {"kernel": "k_lse (Sinkhorn sweep over Z or Z^T)", "bound": "hbm", "achieved": round(ach, 1),
@@ -277,17 +311,20 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(cfg, w, pair)
+        cpu = cpu_baseline(cfg, w, pair, head=args.head)
         log(f"cpu: {cpu}")
 
     rec = {
-        "metric": METRIC, "value": round(value, 3), "unit": "pairs/s", "n_gpus": 1,
+        "metric": METRIC_DS if ds else METRIC, "value": round(value, 3), "unit": "pairs/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded planted-homography pair, random Xavier weights)",
-        "config": {"workload": "one 1024x1024 keypoint pair per step: D=256, H=4, L=9 (18 stages), T=100, "
-                               "bf16 GNN operands / fp32 accumulation, fp32 scores + Sinkhorn",
-                   "pairs_per_step": 1, "M": M, "N": N, "D": cfg.D, "L": cfg.L, "T": cfg.T},
+        "config": {"workload": ("one 1024x1024 keypoint pair per step: D=256, H=4, L=9 (18 stages), "
+                                + ("double-softmax + matchability head, " if ds else "T=100, ")
+                                + "bf16 GNN operands / fp32 accumulation, fp32 scores + "
+                                + ("head" if ds else "Sinkhorn")),
+                   "pairs_per_step": 1, "M": M, "N": N, "D": cfg.D, "L": cfg.L, "T": None if ds else cfg.T,
+                   "head": args.head},
         "roofline": roofline, "cpu_baseline": cpu, "stages_ms": stages, "kernels": kernels,
         "batch_throughput": batch,
         "baseline_context": {"pages_ms_per_pair": {"GTX1080_1024kp": 87.0, "unstated_hw_2048kp": 70.0},

@@ -9,7 +9,9 @@
  *   "SuperGlue 的注意力图神经网络怎样传递信息" (huluoboge.top blog),
  *   "SuperGlue:Learning Feature Matching with Graph Neural Networks论文阅读"
  *   (realcat.vercel.app notes), "SuperGlue_model_forward_learning"
- *   (SuperGlue_Code_Learning notes).
+ *   (SuperGlue_Code_Learning notes).  The optional double-softmax head
+ *   (sg_weights.head) follows section 2.4 of "论文解读:LightGlue,让稀疏特征
+ *   匹配随难度自适应地快" (vincentqin.tech review of LightGlue).
  *
  * Conventions shared by every entry point:
  *  - Pointers are DEVICE pointers unless marked "host".  All buffers belong
@@ -58,6 +60,19 @@ typedef enum {
 
 typedef enum { SG_F32 = 0, SG_BF16 = 1 } sg_dtype;
 
+/* Matching head (sg_weights.head).
+ * SG_HEAD_SINKHORN: the score matrix with a dustbin row and column of score
+ *   alpha, T log-domain Sinkhorn iterations (SuperGlue).
+ * SG_HEAD_DOUBLE_SOFTMAX: no iteration (T is ignored): the log assignment is
+ *   log_softmax_j(S_ij) + log_softmax_i(S_ij) + log sigmoid(z_A,i) +
+ *   log sigmoid(z_B,j) on the real block, log sigmoid(-z_A,i) in the dustbin
+ *   column, log sigmoid(-z_B,j) in the dustbin row, 0 in the corner, where
+ *   z = <w_z, x> + b_z is the matchability logit of a point's last GNN state
+ *   x (section 2.4 of the LightGlue review).  S is the same S = f_A f_B^T /
+ *   sqrt(D) as for the Sinkhorn head; extraction is the same mutual argmax
+ *   with threshold. */
+typedef enum { SG_HEAD_SINKHORN = 0, SG_HEAD_DOUBLE_SOFTMAX = 1 } sg_head;
+
 #define SG_MAX_ENC 8     /* hidden layers of the keypoint encoder          */
 #define SG_MAX_BATCH 64  /* pairs per sg_match_batch call                  */
 
@@ -82,6 +97,8 @@ typedef enum { SG_F32 = 0, SG_BF16 = 1 } sg_dtype;
  *     W_2 [D][2D], b_2 [D]
  *   W_f [D][D], b_f [D]            (final projection)
  *   alpha: one float32             (dustbin score, always fp32)
+ *   SG_HEAD_DOUBLE_SOFTMAX only:
+ *   w_z [1][D], b_z [1]            (matchability Linear(D, 1))
  * Head h owns channels [h*D/H, (h+1)*D/H) of q, k, v and of the merge input.
  */
 typedef struct {
@@ -90,6 +107,7 @@ typedef struct {
   int32_t enc[SG_MAX_ENC];
   int32_t L_max;
   int32_t dtype;       /* sg_dtype */
+  int32_t head;        /* sg_head */
   const void* blob;    /* device pointer, caller-owned */
   size_t blob_bytes;
 } sg_weights;
@@ -100,12 +118,15 @@ enum {
   SG_EV_ENCODED = 1,   /* after the encoder                        */
   SG_EV_GNN = 2,       /* after the 2L stages                      */
   SG_EV_SCORES = 3,    /* after final projection + score matrix    */
-  SG_EV_SINKHORN = 4,  /* after the T iterations                   */
+  SG_EV_SINKHORN = 4,  /* after the T iterations (double-softmax head:
+                          after its row / column statistics)         */
   SG_EV_END = 5,       /* after extraction (and optional outputs)  */
   SG_N_STAGE_EVENTS = 6
 };
 enum { /* kernel classes that can be bracketed by kernel_events */
-  SG_K_NONE = 0, SG_K_GEMM = 1, SG_K_ATTENTION = 2, SG_K_SINKHORN = 3
+  SG_K_NONE = 0, SG_K_GEMM = 1, SG_K_ATTENTION = 2,
+  SG_K_SINKHORN = 3 /* the head's normalisation: Sinkhorn sweeps, or the
+                       double-softmax statistics kernel */
 };
 
 typedef struct {
@@ -138,7 +159,8 @@ typedef struct {
  * partials, then a column reduction).  Both compute the same iteration of
  * the page's algorithm; these flags force one schedule (setting both is
  * SG_ERR_INVALID_ARG).  A forced two-sweep schedule above the threshold
- * needs a workspace beyond sg_workspace_size(). */
+ * needs a workspace beyond sg_workspace_size().  The double-softmax head
+ * always reads Z and its transpose once and ignores these flags. */
 #define SG_FLAG_SINKHORN_TWO_SWEEP 2
 #define SG_FLAG_SINKHORN_ONE_SWEEP 4
 #define SG_TWO_SWEEP_MAX_BYTES (48u << 20)
@@ -210,6 +232,20 @@ sg_status sg_stage_match(const float* fA, int32_t M, const float* fB, int32_t N,
 
 /* Workspace bytes of sg_stage_match for M x N points of dimension D. */
 size_t sg_stage_match_workspace_size(int32_t M, int32_t N, int32_t D);
+
+/* The double-softmax head (SG_HEAD_DOUBLE_SOFTMAX above) from matching
+   descriptors fA [M][D], fB [N][D] and last GNN states xA [M][D], xB [N][D]
+   (all fp32): S = fA fB^T / sqrt(D), matchability z = x w_z + b_z with w_z a
+   DEVICE fp32 [D] vector and b_z a host value, the log assignment and the
+   mutual-argmax extraction (section 2.4 of the LightGlue review).  Outputs
+   and options as sg_stage_match (out_logP: the (M+1) x (N+1) log
+   assignment); D must be a positive multiple of 8. */
+sg_status sg_stage_match_ds(const float* fA, const float* xA, int32_t M, const float* fB,
+                            const float* xB, int32_t N, int32_t D, const float* w_z, float b_z,
+                            int32_t* out_matches, float* out_scores, const sg_opts* opts);
+
+/* Workspace bytes of sg_stage_match_ds for M x N points of dimension D. */
+size_t sg_stage_match_ds_workspace_size(int32_t M, int32_t N, int32_t D);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* sg_last_error(void);

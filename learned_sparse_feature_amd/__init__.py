@@ -14,12 +14,12 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import (SG_BF16, SG_F32, SG_K_ATTENTION, SG_K_GEMM, SG_K_NONE, SG_K_SINKHORN,
-                   SG_MAX_BATCH, SG_N_STAGE_EVENTS, SgError, SgOpts, SgWeights)
+from ._lib import (SG_BF16, SG_F32, SG_HEAD_DOUBLE_SOFTMAX, SG_HEAD_SINKHORN, SG_K_ATTENTION, SG_K_GEMM,
+                   SG_K_NONE, SG_K_SINKHORN, SG_MAX_BATCH, SG_N_STAGE_EVENTS, SgError, SgOpts, SgWeights)
 
 __all__ = ["Weights", "weights_config", "pack_weights", "workspace_size", "sg_match",
            "sg_match_batch", "sg_stage_encode", "sg_stage_gnn", "sg_stage_project",
-           "sg_stage_match", "lib", "SgError", "SG_K_GEMM", "SG_K_ATTENTION", "SG_K_SINKHORN",
+           "sg_stage_match", "sg_stage_match_ds", "lib", "SgError", "SG_K_GEMM", "SG_K_ATTENTION", "SG_K_SINKHORN",
            "SG_N_STAGE_EVENTS"]
 
 
@@ -31,9 +31,15 @@ def _dtype_code(dtype: str) -> int:
     return {"f32": SG_F32, "bf16": SG_BF16}[dtype]
 
 
-def weights_config(D: int, H: int, enc: Sequence[int], L_max: int, dtype: str = "f32") -> SgWeights:
+_HEADS = {"sinkhorn": SG_HEAD_SINKHORN, "ds": SG_HEAD_DOUBLE_SOFTMAX}
+
+
+def weights_config(D: int, H: int, enc: Sequence[int], L_max: int, dtype: str = "f32",
+                   head: str = "sinkhorn") -> SgWeights:
+    """head: "sinkhorn" (optimal transport) or "ds" (double softmax + matchability)."""
     st = SgWeights()
     st.D, st.H, st.n_enc, st.L_max, st.dtype = D, H, len(enc), L_max, _dtype_code(dtype)
+    st.head = _HEADS[head]
     for i, e in enumerate(enc):
         st.enc[i] = e
     return st
@@ -57,8 +63,12 @@ class Weights:
     def D(self):
         return self.struct.D
 
+    @property
+    def head(self):
+        return "ds" if self.struct.head == SG_HEAD_DOUBLE_SOFTMAX else "sinkhorn"
 
-def _ordered_tensors(w: dict):
+
+def _ordered_tensors(w: dict, head: str):
     out = []
     for W, b in w["enc"]:
         out += [W, b]
@@ -66,21 +76,25 @@ def _ordered_tensors(w: dict):
         out += [np.concatenate([st["Wq"], st["Wk"], st["Wv"]]), np.concatenate([st["bq"], st["bk"], st["bv"]]),
                 st["Wm"], st["bm"], st["W1"], st["b1"], st["W2"], st["b2"]]
     out += [w["Wf"], w["bf"], np.array([w["alpha"]], dtype=np.float32)]
+    if head == "ds":
+        out += [np.asarray(w["wz"]).reshape(1, -1), np.array([w["bz"]], dtype=np.float32)]
     return out
 
 
-def pack_weights(w: dict, device="cuda") -> Weights:
+def pack_weights(w: dict, device="cuda", head: str = "sinkhorn") -> Weights:
     """Lay the weight dictionary (row-major [out][in] matrices) out as the
-    library's blob, in the blob dtype, and upload it."""
+    library's blob, in the blob dtype, and upload it.  head="ds" selects the
+    double-softmax head and appends the matchability weights wz, bz."""
     enc = [W.shape[0] for W, _ in w["enc"][:-1]]
     L_max = len(w["stages"]) // 2
-    st = weights_config(w["D"], w["H"], enc, L_max, w["dtype"])
+    st = weights_config(w["D"], w["H"], enc, L_max, w["dtype"], head)
     L = lib()
     nbytes = L.sg_weights_bytes(C.byref(st))
     count = L.sg_weights_count(C.byref(st))
     if nbytes == 0 or count <= 0:
         raise SgError(-1, "sg_weights_bytes")
-    tensors = _ordered_tensors(w)
+    tensors = _ordered_tensors(w, head)
+    alpha_index = count - (3 if head == "ds" else 1)  # alpha is always float32
     if len(tensors) != count:
         raise ValueError(f"weight dictionary has {len(tensors)} tensors, the layout {count}")
     host = torch.zeros(nbytes, dtype=torch.uint8)
@@ -92,7 +106,7 @@ def pack_weights(w: dict, device="cuda") -> Weights:
         arr = np.ascontiguousarray(arr, dtype=np.float32).reshape(-1)
         if arr.size != rows.value * cols.value:
             raise ValueError(f"tensor {i}: {arr.size} values, layout {rows.value}x{cols.value}")
-        t = torch.from_numpy(arr).to(torch.float32 if i == count - 1 else tdt)
+        t = torch.from_numpy(arr).to(torch.float32 if i == alpha_index else tdt)
         raw = t.view(torch.uint8)
         host[off.value: off.value + raw.numel()] = raw
     return Weights(st, host.to(device), L_max)
@@ -334,5 +348,34 @@ def sg_stage_match(fA, fB, alpha: float, T: int, *, threshold: float = 0.0, want
                            timed_kernel=timed_kernel, kernel_events=kernel_events, sinkhorn=sinkhorn)
     _lib.check(lib().sg_stage_match(_ptr(fA), M, _ptr(fB), N, D, float(alpha), T, _ptr(out["matches0"]),
                                     _ptr(out["scores0"]), C.byref(o)), "sg_stage_match")
+    out["n_kernel_launches"] = count.value
+    return out
+
+
+def sg_stage_match_ds(fA, fB, xA, xB, wz, bz: float, *, threshold: float = 0.0, want_logP=True,
+                      workspace=None, stage_events=None, timed_kernel=SG_K_NONE, kernel_events=None) -> dict:
+    """Double-softmax head from matching descriptors f and last states x (float32
+    CUDA tensors [n][D]) with matchability weights wz (float32 CUDA [D]) and bz."""
+    M, N, D = fA.shape[0], fB.shape[0], fA.shape[1]
+    _check_tensor(fA, "fA", torch.float32, (M, D))
+    _check_tensor(fB, "fB", torch.float32, (N, D))
+    _check_tensor(xA, "xA", torch.float32, (M, D))
+    _check_tensor(xB, "xB", torch.float32, (N, D))
+    _check_tensor(wz, "wz", torch.float32, (D,))
+    dev = fA.device
+    out = {"matches0": torch.empty(M, dtype=torch.int32, device=dev),
+           "scores0": torch.empty(M, dtype=torch.float32, device=dev),
+           "matches1": torch.empty(N, dtype=torch.int32, device=dev),
+           "scores1": torch.empty(N, dtype=torch.float32, device=dev)}
+    if want_logP:
+        out["logP"] = torch.empty((M + 1, N + 1), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib().sg_stage_match_ds_workspace_size(M, N, D)))
+    o, keep, count = _opts(dev, threshold=threshold, workspace=workspace, m1=out["matches1"], s1=out["scores1"],
+                           logP=out.get("logP"), logP_ld=N + 1, stage_events=stage_events,
+                           timed_kernel=timed_kernel, kernel_events=kernel_events)
+    _lib.check(lib().sg_stage_match_ds(_ptr(fA), _ptr(xA), M, _ptr(fB), _ptr(xB), N, D, _ptr(wz), float(bz),
+                                       _ptr(out["matches0"]), _ptr(out["scores0"]), C.byref(o)),
+               "sg_stage_match_ds")
     out["n_kernel_launches"] = count.value
     return out

@@ -49,6 +49,7 @@ struct WLayout {
   int stage_first = 0;  // index of stage 0 W_qkv
   int final_first = 0;  // index of W_f
   int alpha = 0;        // index of alpha
+  int wz = -1;          // index of the matchability weight (double-softmax head)
 };
 
 constexpr int kPerStage = 8;  // W_qkv, b_qkv, W_m, b_m, W_1, b_1, W_2, b_2
@@ -63,6 +64,8 @@ sg_status check_config(const sg_weights* w) {
     if (w->enc[i] <= 0) return fail(SG_ERR_INVALID_ARG, "encoder width %d is not positive", i);
   if (w->L_max < 1) return fail(SG_ERR_INVALID_ARG, "L_max must be >= 1");
   if (w->dtype != SG_F32 && w->dtype != SG_BF16) return fail(SG_ERR_INVALID_ARG, "unknown dtype %d", w->dtype);
+  if (w->head != SG_HEAD_SINKHORN && w->head != SG_HEAD_DOUBLE_SOFTMAX)
+    return fail(SG_ERR_INVALID_ARG, "unknown head %d", w->head);
   const int dh = w->D / w->H;
   if (dh != 16 && dh != 64) return fail(SG_ERR_UNSUPPORTED, "head dimension %d (supported: 16, 64)", dh);
   if (w->D % 32 || w->D > 1024) return fail(SG_ERR_UNSUPPORTED, "D = %d (supported: multiples of 32 up to 1024)", w->D);
@@ -104,6 +107,11 @@ WLayout layout_of(const sg_weights* w) {
   add(1, D, es);
   L.alpha = (int)L.t.size();
   add(1, 1, 4);
+  if (w->head == SG_HEAD_DOUBLE_SOFTMAX) {
+    L.wz = (int)L.t.size();
+    add(1, D, es);
+    add(1, 1, es);
+  }
   L.bytes = off;
   return L;
 }
@@ -122,7 +130,7 @@ sg_status check_weights(const sg_weights* w, WLayout* out) {
 // ---------------------------------------------------------- workspace layout
 
 struct WsLayout {
-  size_t X, H0, H1, QK, VT, KS, VS, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, IDX1, total;
+  size_t X, H0, H1, QK, VT, KS, VS, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, total;
   int ldvt, ldqk;
 };
 
@@ -157,6 +165,8 @@ WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, l
   L.PI = take((size_t)pf * 4);
   L.U = take((size_t)uf * 4);
   L.V = take((size_t)vf * 4);
+  L.UD = take((size_t)uf * 4);  // dustbin entries of the double-softmax head
+  L.VD = take((size_t)vf * 4);
   L.IDX1 = take((size_t)nb * 4);
   L.total = o;
   return L;
@@ -240,6 +250,7 @@ struct Timer {
 struct Problem {
   int B = 1, Mpad = 0, Npad = 0;
   int flags = 0;  // SG_FLAG_*
+  int head = SG_HEAD_SINKHORN;
   std::vector<int> M, N;
   const float *kp[2] = {nullptr, nullptr}, *cf[2] = {nullptr, nullptr}, *de[2] = {nullptr, nullptr};
   float img[4] = {0, 0, 0, 0};
@@ -268,7 +279,8 @@ void make_plan(const Problem& p, Plan& pl) {
   // reduction beyond
   long zbytes = 0;
   for (int b = 0; b < p.B; ++b) zbytes += 4L * p.M[b] * ld4(p.N[b]);
-  pl.two_sweep = (p.flags & SG_FLAG_SINKHORN_TWO_SWEEP) ||
+  // (the double-softmax head reads Z and ZT once each, whatever their size)
+  pl.two_sweep = p.head == SG_HEAD_DOUBLE_SOFTMAX || (p.flags & SG_FLAG_SINKHORN_TWO_SWEEP) ||
                  (!(p.flags & SG_FLAG_SINKHORN_ONE_SWEEP) && zbytes <= (long)SG_TWO_SWEEP_MAX_BYTES);
   pl.pt.rb = sink_rows_per_block(p.M.data(), p.N.data(), p.B);
   pl.seg.n_seg = 2 * p.B;
@@ -299,6 +311,7 @@ void make_plan(const Problem& p, Plan& pl) {
   pl.R = R;
   pl.zf = zf; pl.pf = pf; pl.pd = pl.pt.gpre[p.B];
   pl.ztf = pl.two_sweep ? ztf : 0;
+  if (p.head == SG_HEAD_DOUBLE_SOFTMAX) pl.pf = pl.pd = 0;  // no column partials
   pl.ru = pl.pt.upre[p.B]; pl.rv = pl.pt.vpre[p.B];
   pl.nb = pl.rv - p.B;
 }
@@ -438,9 +451,21 @@ sg_status run_project(const Plan& pl, const sg_weights* w, const WLayout& L, con
   return SG_OK;
 }
 
-// Scores, Sinkhorn and extraction from F (rows of the plan).
+// Inputs of the double-softmax head: the last states X [R][D] (fp32, rows
+// of the plan) and the matchability weights (w_dtype) with the bias at
+// bz_dev, or the host value bz when bz_dev is null.
+struct DsHead {
+  const float* X = nullptr;
+  int w_dtype = SG_F32;
+  const void* wz = nullptr;
+  const void* bz_dev = nullptr;
+  float bz = 0.f;
+};
+
+// Scores, the head (Sinkhorn or double softmax) and extraction from F (rows
+// of the plan).  ds == nullptr: Sinkhorn.
 sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, const float* alpha_dev,
-                       int T, float thr,
+                       int T, float thr, const DsHead* ds,
                        const float* F, char* ws, const WsLayout& wl, const Outputs& out, Timer& tm,
                        hipStream_t st) {
   const float log2e = 1.4426950408889634f;
@@ -475,6 +500,23 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
     HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(SG_F32, 1, SG_F32, 1, EPI_SCORE, g, b, mr, mn, st); }), "score GEMM");
   }
   tm.stage(SG_EV_SCORES);
+  if (ds) {
+    // one sweep over the rows of Z and of ZT: row / column log-sum-exp and
+    // matchability; then the same extraction with the real block 2 Z + u + v
+    float* UD = reinterpret_cast<float*>(ws + wl.UD);
+    float* VD = reinterpret_cast<float*>(ws + wl.VD);
+    HIPCHK(tm.run(SG_K_SINKHORN, [&] {
+             return launch_ds_stats(Z, ZT, pl.pt, ds->X, D, ds->w_dtype, ds->wz, ds->bz_dev, ds->bz, U, V, UD, VD, st);
+           }), "double-softmax statistics");
+    tm.stage(SG_EV_SINKHORN);
+    HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, 1, st), "column argmax");
+    HIPCHK(launch_sink_extract(Z, pl.pt, U, V, idx1, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, 1, st),
+           "extract");
+    if (out.logP)
+      HIPCHK(launch_ds_write_logp(Z, pl.pt, U, V, UD, VD, out.logP, out.logP_ld, out.logP_stride, pl.ru, st),
+             "logP");
+    return SG_OK;
+  }
   if (pl.two_sweep) {
     // T iterations: u = log mu - lse_j(Z + v) over the rows of Z, then
     // v = log nu - lse_i(Z + u) over the rows of ZT
@@ -489,7 +531,7 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
       HIPCHK(launch_fill_f32(V, 0.f, (int)pl.vf, st), "zero v");
     }
     tm.stage(SG_EV_SINKHORN);
-    HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, st), "column argmax");
+    HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, 0, st), "column argmax");
   } else {
     // T iterations: u = log mu - lse_j(Z + v) with the column partials of
     // Z + u in the same pass; then v = log nu - lse over the partials.  The
@@ -513,7 +555,7 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
     }
     tm.stage(SG_EV_SINKHORN);
   }
-  HIPCHK(launch_sink_extract(Z, pl.pt, U, V, idx1, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, st),
+  HIPCHK(launch_sink_extract(Z, pl.pt, U, V, idx1, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, 0, st),
          "extract");
   if (out.logP)
     HIPCHK(launch_write_logp(Z, pl.pt, U, V, alpha2, alpha_dev, out.logP, out.logP_ld, out.logP_stride, pl.ru, st),
@@ -617,7 +659,7 @@ std::string call_key(int kind, const Problem& p, const sg_weights* w, int Lst, i
   if (w) {
     put(k, w->D); put(k, w->H); put(k, w->n_enc);
     for (int i = 0; i < w->n_enc; ++i) put(k, w->enc[i]);
-    put(k, w->L_max); put(k, w->dtype); put(k, w->blob); put(k, w->blob_bytes);
+    put(k, w->L_max); put(k, w->dtype); put(k, w->head); put(k, w->blob); put(k, w->blob_bytes);
   }
   put(k, Lst); put(k, T); put(k, out);
   put(k, o ? o->match_threshold : 0.f);
@@ -664,7 +706,16 @@ sg_status enqueue_full(const Problem& p, const Plan& pl, const WsLayout& wl, cha
                             (size_t)p.N[b] * w->D * 4, hipMemcpyDeviceToDevice, st), "copy f_B");
   }
   const float thr = o ? o->match_threshold : 0.f;
-  if ((s = run_matching(p, pl, w->D, 0.f, alpha_dev, T, thr, F, ws, wl, out, tm, st)) != SG_OK) return s;
+  DsHead ds;
+  if (w->head == SG_HEAD_DOUBLE_SOFTMAX) {
+    ds.X = reinterpret_cast<const float*>(ws + wl.X);
+    ds.w_dtype = w->dtype;
+    ds.wz = atv(w, L, L.wz);
+    ds.bz_dev = atv(w, L, L.wz + 1);
+  }
+  if ((s = run_matching(p, pl, w->D, 0.f, alpha_dev, T, thr, w->head == SG_HEAD_DOUBLE_SOFTMAX ? &ds : nullptr, F,
+                        ws, wl, out, tm, st)) != SG_OK)
+    return s;
   tm.stage(SG_EV_END);
   tm.finish();
   return SG_OK;
@@ -704,12 +755,15 @@ size_t sg_workspace_size(const sg_weights* w, int32_t Mmax, int32_t Nmax, int32_
   const long R = B * (round32(Mmax) + round32(Nmax));
   // the transposed scores exist only for the two-sweep schedule, which the
   // default rule picks for at most SG_TWO_SWEEP_MAX_BYTES of Z (ZT exceeds Z
-  // by at most its row padding)
-  const long ztf = std::min(B * Nmax * ld4(Mmax), (long)(SG_TWO_SWEEP_MAX_BYTES / 4) + 3 * B * Nmax);
+  // by at most its row padding), and for the double-softmax head
+  const long ztf = w->head == SG_HEAD_DOUBLE_SOFTMAX
+                       ? B * Nmax * ld4(Mmax)
+                       : std::min(B * Nmax * ld4(Mmax), (long)(SG_TWO_SWEEP_MAX_BYTES / 4) + 3 * B * Nmax);
   // column partials: at most ceil((Mmax+1)/4) row blocks per pair
   const long G = (Mmax + 4) / 4;
-  WsLayout wl = ws_layout(w, R, B * Mmax * ld4(Nmax), ztf, B * G * ld4(Nmax), B * G, B * ld4(Mmax + 1),
-                          B * ld4(Nmax + 1), B * Nmax);
+  const bool ds = w->head == SG_HEAD_DOUBLE_SOFTMAX;  // no column partials
+  WsLayout wl = ws_layout(w, R, B * Mmax * ld4(Nmax), ztf, ds ? 0 : B * G * ld4(Nmax), ds ? 0 : B * G,
+                          B * ld4(Mmax + 1), B * ld4(Nmax + 1), B * Nmax);
   return wl.total;
 }
 
@@ -746,6 +800,7 @@ sg_status sg_match(const float* kptsA, const float* descA, const float* confA, i
   }
   Problem p;
   p.flags = opts ? opts->flags : 0;
+  p.head = weights->head;
   p.B = 1; p.Mpad = M; p.Npad = N;
   p.M = {M}; p.N = {N};
   p.kp[0] = kptsA; p.cf[0] = confA; p.de[0] = descA;
@@ -784,6 +839,7 @@ sg_status sg_match_batch(int32_t B, int32_t Mpad, int32_t Npad, const int32_t* M
   if (opts && opts->out_logP && opts->logP_ld < Npad + 1) return fail(SG_ERR_INVALID_ARG, "logP_ld < Npad+1");
   Problem p;
   p.flags = opts ? opts->flags : 0;
+  p.head = weights->head;
   p.B = B; p.Mpad = Mpad; p.Npad = Npad;
   p.M.assign(M, M + B); p.N.assign(N, N + B);
   p.kp[0] = kptsA; p.cf[0] = confA; p.de[0] = descA;
@@ -927,7 +983,74 @@ sg_status sg_stage_match(const float* fA, int32_t M, const float* fB, int32_t N,
            "copy fB");
     Timer tm{opts, cs};
     tm.stage(SG_EV_GNN);
-    sg_status r = run_matching(p, pl, D, alpha, nullptr, T, opts ? opts->match_threshold : 0.f, F, ws, wl, out, tm, cs);
+    sg_status r = run_matching(p, pl, D, alpha, nullptr, T, opts ? opts->match_threshold : 0.f, nullptr, F, ws, wl,
+                               out, tm, cs);
+    if (r != SG_OK) return r;
+    tm.stage(SG_EV_END);
+    tm.finish();
+    return SG_OK;
+  });
+}
+
+size_t sg_stage_match_ds_workspace_size(int32_t M, int32_t N, int32_t D) {
+  if (M < 0 || N < 0 || D <= 0) return 0;
+  const long R = round32(M) + round32(N);
+  return ws_layout_raw(D, 4, 0, R, (long)M * ld4(N), (long)N * ld4(M), 0, 0, ld4(M + 1), ld4(N + 1), N).total;
+}
+
+sg_status sg_stage_match_ds(const float* fA, const float* xA, int32_t M, const float* fB, const float* xB,
+                            int32_t N, int32_t D, const float* w_z, float b_z, int32_t* out_matches,
+                            float* out_scores, const sg_opts* opts) {
+  g_err.clear();
+  sg_status s;
+  if ((s = check_opts(opts)) != SG_OK) return s;
+  if (M < 0 || N < 0) return fail(SG_ERR_INVALID_ARG, "negative point count");
+  if (M > 4096 || N > 4096) return fail(SG_ERR_UNSUPPORTED, "more than 4096 points per image");
+  if (D <= 0 || D % 8) return fail(SG_ERR_UNSUPPORTED, "D = %d (must be a positive multiple of 8)", D);
+  if (M > 0 && (!out_matches || !out_scores)) return fail(SG_ERR_INVALID_ARG, "NULL output");
+  if (M > 0 && N > 0 && (!fA || !fB || !xA || !xB || !w_z)) return fail(SG_ERR_INVALID_ARG, "NULL input");
+  if (opts && opts->out_logP && opts->logP_ld < N + 1) return fail(SG_ERR_INVALID_ARG, "logP_ld < N+1");
+  hipStream_t st = stream_of(opts);
+  if (M == 0 || N == 0) {
+    HIPCHK(launch_fill_empty(out_matches, out_scores, M, st), "empty output");
+    if (opts && opts->out_matches1) HIPCHK(launch_fill_empty(opts->out_matches1, opts->out_scores1, N, st), "empty output");
+    return SG_OK;
+  }
+  Problem p;
+  p.flags = opts ? opts->flags : 0;
+  p.head = SG_HEAD_DOUBLE_SOFTMAX;
+  p.B = 1; p.Mpad = M; p.Npad = N; p.M = {M}; p.N = {N};
+  Plan pl;
+  make_plan(p, pl);
+  // f and x are staged into the compact F and X rows of the workspace
+  WsLayout wl = ws_layout_raw(D, 4, 0, pl.R, pl.zf, pl.ztf, pl.pf, pl.pd, pl.uf, pl.vf, pl.nb);
+  void* wsp;
+  if ((s = get_workspace(opts, wl.total, &wsp)) != SG_OK) return s;
+  char* ws = reinterpret_cast<char*>(wsp);
+  float* F = reinterpret_cast<float*>(ws + wl.F);
+  float* X = reinterpret_cast<float*>(ws + wl.X);
+  Outputs out;
+  out.m0 = out_matches; out.s0 = out_scores;
+  if (opts) {
+    out.m1 = opts->out_matches1; out.s1 = opts->out_scores1;
+    out.logP = opts->out_logP; out.logP_ld = opts->logP_ld;
+  }
+  p.kp[0] = fA; p.kp[1] = fB; p.cf[0] = xA; p.cf[1] = xB; p.de[0] = w_z;  // part of the replay key
+  std::string key = call_key(2, p, nullptr, D, 0, out, opts, wsp);
+  key.append(reinterpret_cast<const char*>(&b_z), sizeof(b_z));
+  DsHead ds;
+  ds.X = X; ds.w_dtype = SG_F32; ds.wz = w_z; ds.bz = b_z;
+  return run_maybe_graph(key, opts, st, [&](hipStream_t cs) -> sg_status {
+    const size_t rb = (size_t)D * 4;
+    const size_t rowB = (size_t)pl.seg.row0[1] * D;
+    HIPCHK(hipMemcpyAsync(F, fA, M * rb, hipMemcpyDeviceToDevice, cs), "copy fA");
+    HIPCHK(hipMemcpyAsync(F + rowB, fB, N * rb, hipMemcpyDeviceToDevice, cs), "copy fB");
+    HIPCHK(hipMemcpyAsync(X, xA, M * rb, hipMemcpyDeviceToDevice, cs), "copy xA");
+    HIPCHK(hipMemcpyAsync(X + rowB, xB, N * rb, hipMemcpyDeviceToDevice, cs), "copy xB");
+    Timer tm{opts, cs};
+    tm.stage(SG_EV_GNN);
+    sg_status r = run_matching(p, pl, D, 0.f, nullptr, 0, opts ? opts->match_threshold : 0.f, &ds, F, ws, wl, out,
+                               tm, cs);
     if (r != SG_OK) return r;
     tm.stage(SG_EV_END);
     tm.finish();

@@ -127,14 +127,24 @@ hipError_t launch_sink_cols(const PairTable& pt, const float* P, const float* Pd
                             hipStream_t st);
 hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const float* w_in, float* w_out,
                       float alpha2, const float* alpha_dev, int total_rows, hipStream_t st);
+// ds = 1: the double-softmax head (real block 2 Z + u + v, see sg_double_softmax.hip)
 hipError_t launch_col_argmax(const float* ZT, const PairTable& pt, const float* u, int* idx1, int Npad,
-                             int32_t* m1, float* s1, hipStream_t st);
+                             int32_t* m1, float* s1, int ds, hipStream_t st);
 hipError_t launch_sink_extract(const float* Z, const PairTable& pt, const float* u, const float* v,
                                const int* idx1, int Mpad, int Npad, float thr, int32_t* m0, float* s0,
-                               int32_t* m1, float* s1, hipStream_t st);
+                               int32_t* m1, float* s1, int ds, hipStream_t st);
 hipError_t launch_write_logp(const float* Z, const PairTable& pt, const float* u, const float* v,
                              float alpha2, const float* alpha_dev, float* logP, int64_t ld,
                              int64_t pair_stride, int total_rows, hipStream_t st);
+// Double-softmax head: u, v (base-2 row / column terms) and ud, vd (dustbin
+// entries) from Z, ZT and the states X [R][D] with the matchability weights
+// wz [D], bias at bz_dev (device, w_dtype) or bz (bz_dev == nullptr).
+hipError_t launch_ds_stats(const float* Z, const float* ZT, const PairTable& pt, const float* X, int D,
+                           int w_dtype, const void* wz, const void* bz_dev, float bz, float* u, float* v,
+                           float* ud, float* vd, hipStream_t st);
+hipError_t launch_ds_write_logp(const float* Z, const PairTable& pt, const float* u, const float* v,
+                                const float* ud, const float* vd, float* logP, int64_t ld, int64_t pair_stride,
+                                int total_rows, hipStream_t st);
 hipError_t launch_fill_f32(float* p, float v, int n, hipStream_t st);
 hipError_t launch_fill_empty(int32_t* m, float* s, int n, hipStream_t st);
 

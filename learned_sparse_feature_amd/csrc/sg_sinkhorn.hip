@@ -448,8 +448,9 @@ __global__ __launch_bounds__(256) void k_lse(const float* __restrict__ Zbase, Pa
 
 // Column argmax over the real rows (argmax_i Z2_ij + u_i, lowest index on
 // ties) from the rows of ZT, one wave per column; also the default (-1 / 0)
-// side-B outputs that the extraction overwrites for mutual matches.
-template <int NV4>
+// side-B outputs that the extraction overwrites for mutual matches.  DS: the
+// double-softmax head, whose real block is 2 Z2 + u + v.
+template <int NV4, bool DS>
 __global__ __launch_bounds__(256) void k_col_argmax(const float* __restrict__ ZTb, PairTable pt,
                                                     const float* __restrict__ u,
                                                     int* __restrict__ idx1, int Npad,
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(256) void k_col_argmax(const float* __restrict__ ZT
       const float4 q = *reinterpret_cast<const float4*>(uu + i);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float y = f4c(z, c) + f4c(q, c);
+        const float y = (DS ? 2.f * f4c(z, c) : f4c(z, c)) + f4c(q, c);
         if (i + c < M && y > best) {
           best = y;
           bi = i + c;
@@ -494,8 +495,9 @@ __global__ __launch_bounds__(256) void k_col_argmax(const float* __restrict__ ZT
 
 // Row argmax of the final log assignment (argmax_j Z_ij + v_j; lowest index
 // on ties), mutual check against idx1, score exp(logP), threshold; side-B
-// outputs of mutual pairs; -1 / 0 for padded entries and empty pairs.
-template <int NV4>
+// outputs of mutual pairs; -1 / 0 for padded entries and empty pairs.  DS:
+// the double-softmax head (2 Z + u + v, no marginal normalisation to undo).
+template <int NV4, bool DS>
 __global__ __launch_bounds__(256) void k_sink_extract(const float* __restrict__ Zb, PairTable pt,
                                                       const float* __restrict__ u,
                                                       const float* __restrict__ v,
@@ -536,7 +538,8 @@ __global__ __launch_bounds__(256) void k_sink_extract(const float* __restrict__ 
     if (j < N) {
       const float4 z = *reinterpret_cast<const float4*>(row + j);
       const float4 q = *reinterpret_cast<const float4*>(vv + j);
-      const float x[4] = {z.x + q.x, z.y + q.y, z.z + q.z, z.w + q.w};
+      const float zm = DS ? 2.f : 1.f;
+      const float x[4] = {zm * z.x + q.x, zm * z.y + q.y, zm * z.z + q.z, zm * z.w + q.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (j + e < N && x[e] > best) { best = x[e]; bj = j + e; }
@@ -549,7 +552,7 @@ __global__ __launch_bounds__(256) void k_sink_extract(const float* __restrict__ 
   float score = 0.f;
   int mo = -1;
   if (mutual) {
-    const float lp2 = best + u[pt.uoff[b] + t] + log2f((float)(M + N));
+    const float lp2 = best + u[pt.uoff[b] + t] + (DS ? 0.f : log2f((float)(M + N)));
     score = exp2f(lp2);
     // exp(logP) > thr decided in the log domain (exact for any finite logP:
     // exp never reaches 0, so a non-positive threshold accepts every mutual match)
@@ -674,7 +677,7 @@ hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const floa
 }
 
 hipError_t launch_col_argmax(const float* ZT, const PairTable& pt, const float* u, int* idx1, int Npad,
-                             int32_t* m1, float* s1, hipStream_t st) {
+                             int32_t* m1, float* s1, int ds, hipStream_t st) {
   int cols = 0, mr = 0;
   for (int b = 0; b < pt.n_pairs; ++b) {
     cols += pt.N[b];
@@ -683,8 +686,12 @@ hipError_t launch_col_argmax(const float* ZT, const PairTable& pt, const float* 
   if (cols <= 0) return hipSuccess;
   const int nv4 = sink_nv4(mr);
   dim3 grid((cols + 3) / 4);
-#define SG_CA(NV) \
-  if (nv4 == NV) { hipLaunchKernelGGL(k_col_argmax<NV>, grid, dim3(256), 0, st, ZT, pt, u, idx1, Npad, m1, s1); return hipGetLastError(); }
+#define SG_CA(NV)                                                                                          \
+  if (nv4 == NV) {                                                                                         \
+    if (ds) hipLaunchKernelGGL((k_col_argmax<NV, true>), grid, dim3(256), 0, st, ZT, pt, u, idx1, Npad, m1, s1); \
+    else hipLaunchKernelGGL((k_col_argmax<NV, false>), grid, dim3(256), 0, st, ZT, pt, u, idx1, Npad, m1, s1); \
+    return hipGetLastError();                                                                              \
+  }
   SG_CA(1) SG_CA(2) SG_CA(4) SG_CA(8) SG_CA(16)
 #undef SG_CA
   return hipErrorInvalidValue;
@@ -692,13 +699,17 @@ hipError_t launch_col_argmax(const float* ZT, const PairTable& pt, const float* 
 
 hipError_t launch_sink_extract(const float* Z, const PairTable& pt, const float* u, const float* v,
                                const int* idx1, int Mpad, int Npad, float thr, int32_t* m0, float* s0,
-                               int32_t* m1, float* s1, hipStream_t st) {
+                               int32_t* m1, float* s1, int ds, hipStream_t st) {
   const int n = std::max(Mpad, m1 ? Npad : 0);
   if (n <= 0 || pt.n_pairs <= 0) return hipSuccess;
   const int nc = max_n(pt);
   const int nv4 = (nc + 255) / 256;
   dim3 grid((n + 3) / 4, pt.n_pairs);
-#define SG_EXT(NV) hipLaunchKernelGGL(k_sink_extract<NV>, grid, dim3(256), 0, st, Z, pt, u, v, idx1, Mpad, Npad, thr, m0, s0, m1, s1)
+#define SG_EXT(NV)                                                                                            \
+  if (ds) hipLaunchKernelGGL((k_sink_extract<NV, true>), grid, dim3(256), 0, st, Z, pt, u, v, idx1, Mpad, Npad, \
+                             thr, m0, s0, m1, s1);                                                            \
+  else hipLaunchKernelGGL((k_sink_extract<NV, false>), grid, dim3(256), 0, st, Z, pt, u, v, idx1, Mpad, Npad, \
+                          thr, m0, s0, m1, s1)
   if (nv4 <= 1) SG_EXT(1);
   else if (nv4 <= 2) SG_EXT(2);
   else if (nv4 <= 4) SG_EXT(4);

@@ -119,3 +119,37 @@ def test_stage_entry_points_validate_on_host():
     assert lib.sg_stage_match(fake, 4, fake, 4, 64, 1.0, -1, fake, fake, None) == _lib.SG_ERR_INVALID_ARG
     assert lib.sg_stage_encode(fake, fake, fake, -1, 0.0, 0.0, C.byref(good), fake, None) == _lib.SG_ERR_INVALID_ARG
     assert lib.sg_stage_match_workspace_size(1024, 1024, 256) > 1024 * 1024 * 8
+
+
+def test_double_softmax_head_layout_and_validation():
+    """The double-softmax head appends the matchability Linear(D, 1) (D + 1
+    parameters) after alpha; an unknown head is rejected; the stage entry
+    point validates on the host; its workspace holds the full transpose."""
+    lib = _lib.load()
+    w = _cfg()
+    wd = _cfg()
+    wd.head = _lib.SG_HEAD_DOUBLE_SOFTMAX
+    n, nd = lib.sg_weights_count(C.byref(w)), lib.sg_weights_count(C.byref(wd))
+    assert nd == n + 2
+    off, r, c = C.c_size_t(), C.c_int32(), C.c_int32()
+    shapes = []
+    for i in (n, n + 1):
+        assert lib.sg_weights_tensor(C.byref(wd), i, C.byref(off), C.byref(r), C.byref(c)) == 0
+        shapes.append((r.value, c.value))
+    assert shapes == [(1, 256), (1, 1)]
+    assert lib.sg_weights_bytes(C.byref(wd)) > lib.sg_weights_bytes(C.byref(w))
+    bad = _cfg()
+    bad.head = 7
+    assert lib.sg_weights_count(C.byref(bad)) == -1
+    fake = C.c_void_p(0x1000)
+    bad.blob, bad.blob_bytes = fake, 1 << 30
+    assert _match(lib, bad) == _lib.SG_ERR_INVALID_ARG and "head" in lib.sg_last_error().decode()
+    f = fake
+    assert lib.sg_stage_match_ds(f, f, 4, f, f, 4, 12, f, 0.0, f, f, None) == _lib.SG_ERR_UNSUPPORTED
+    assert lib.sg_stage_match_ds(f, f, -1, f, f, 4, 64, f, 0.0, f, f, None) == _lib.SG_ERR_INVALID_ARG
+    assert lib.sg_stage_match_ds(f, None, 4, f, f, 4, 64, f, 0.0, f, f, None) == _lib.SG_ERR_INVALID_ARG
+    assert lib.sg_stage_match_ds(f, f, 4, f, f, 4, 64, None, 0.0, f, f, None) == _lib.SG_ERR_INVALID_ARG
+    # Z and its full transpose at any size (the Sinkhorn workspace caps the transpose)
+    big = lib.sg_stage_match_ds_workspace_size(4096, 4096, 256)
+    assert 2 * 4096 * 4096 * 4 < big < 4 * 4096 * 4096 * 4
+    assert lib.sg_workspace_size(C.byref(wd), 4096, 4096, 8) > 2 * 8 * 4096 * 4096 * 4
