@@ -46,6 +46,7 @@ __all__ = [
     "score_matrix", "logsumexp", "log_sinkhorn_iterations",
     "log_optimal_transport", "extract_matches", "superglue_match",
     "superglue_descriptors", "sinkhorn_knopp_exp", "match_from_descriptors",
+    "bidirectional_cross_attention",
     "log_sigmoid", "matchability", "double_softmax_assignment",
     "double_softmax_from_descriptors", "double_softmax_match",
 ]
@@ -110,14 +111,49 @@ def multi_head_attention(x, src, st, heads):
     return msg @ _f64(st["Wm"]).T + _f64(st["bm"])
 
 
+def bidirectional_cross_attention(x0, x1, st, heads):
+    """Messages (m0, m1) of both images from one shared similarity.
+
+    [LightGlue-review] section 2.3 (bidirectional cross-attention): each image
+    has a single projection qk = W_qk x + b_qk (no separate query) and a value
+    projection v = W_v x + b_v; per head the similarity sim_ij =
+    qk0_i^T qk1_j / sqrt(d_h) is formed once; its softmax over j (each row)
+    aggregates image 1's values into m0, its softmax over i (each column)
+    aggregates image 0's values into m1.  Heads as in multi_head_attention,
+    then the merge projection W_m m + b_m.  Stage weights `st` hold
+    Wqk,bqk,Wv,bv,Wm,bm.
+    """
+    x0, x1 = _f64(x0), _f64(x1)
+    D = x0.shape[1]
+    dh = D // heads
+    qk0 = x0 @ _f64(st["Wqk"]).T + _f64(st["bqk"])
+    qk1 = x1 @ _f64(st["Wqk"]).T + _f64(st["bqk"])
+    v0 = x0 @ _f64(st["Wv"]).T + _f64(st["bv"])
+    v1 = x1 @ _f64(st["Wv"]).T + _f64(st["bv"])
+    m0 = np.zeros((x0.shape[0], D))
+    m1 = np.zeros((x1.shape[0], D))
+    for h in range(heads):
+        c = slice(h * dh, (h + 1) * dh)
+        sim = (qk0[:, c] @ qk1[:, c].T) / np.sqrt(dh)
+        m0[:, c] = _softmax_rows(sim) @ v1[:, c]
+        m1[:, c] = _softmax_rows(sim.T) @ v0[:, c]
+    merge = lambda m: m @ _f64(st["Wm"]).T + _f64(st["bm"])
+    return merge(m0), merge(m1)
+
+
+def _update_mlp(x, m, st):
+    """[realcat] section "多层GNN" (AttentionalPropagation): MLP([x || m]) with
+    channels [2D, 2D, D], ReLU between the two layers."""
+    h = np.concatenate([_f64(x), m], axis=1) @ _f64(st["W1"]).T + _f64(st["b1"])
+    h = np.maximum(h, 0.0)
+    return h @ _f64(st["W2"]).T + _f64(st["b2"])
+
+
 def attentional_propagation(x, src, st, heads):
     """[realcat] section "多层GNN" (AttentionalPropagation): the residual
     update MLP([x || m]) with channels [2D, 2D, D], ReLU between the two
     layers.  Returns the update (delta), not x + delta."""
-    m = multi_head_attention(x, src, st, heads)
-    h = np.concatenate([_f64(x), m], axis=1) @ _f64(st["W1"]).T + _f64(st["b1"])
-    h = np.maximum(h, 0.0)
-    return h @ _f64(st["W2"]).T + _f64(st["b2"])
+    return _update_mlp(x, multi_head_attention(x, src, st, heads), st)
 
 
 def attentional_gnn(xA, xB, stages, heads, first_stage=0):
@@ -126,15 +162,22 @@ def attentional_gnn(xA, xB, stages, heads, first_stage=0):
     and cross (sources = the other image), self first; each stage has its own
     weights, shared by both images, and both deltas are computed from the
     states before the stage, then added.  `stages` may be a slice of the
-    network starting at stage index `first_stage` (even = self)."""
+    network starting at stage index `first_stage` (even = self).  A cross
+    stage whose weights hold "Wqk" uses bidirectional_cross_attention
+    ([LightGlue-review] section 2.3) for both messages, followed by the same
+    update MLP."""
     xA, xB = _f64(xA).copy(), _f64(xB).copy()
     for s, st in enumerate(stages, start=first_stage):
-        if s % 2 == 0:          # self
-            srcA, srcB = xA, xB
-        else:                   # cross
-            srcA, srcB = xB, xA
-        dA = attentional_propagation(xA, srcA, st, heads)
-        dB = attentional_propagation(xB, srcB, st, heads)
+        if s % 2 == 1 and "Wqk" in st:   # bidirectional cross
+            mA, mB = bidirectional_cross_attention(xA, xB, st, heads)
+            dA, dB = _update_mlp(xA, mA, st), _update_mlp(xB, mB, st)
+        else:
+            if s % 2 == 0:          # self
+                srcA, srcB = xA, xB
+            else:                   # cross
+                srcA, srcB = xB, xA
+            dA = attentional_propagation(xA, srcA, st, heads)
+            dB = attentional_propagation(xB, srcB, st, heads)
         xA, xB = xA + dA, xB + dB
     return xA, xB
 

@@ -85,7 +85,7 @@ def _bias(rng: np.random.Generator, n_out: int, n_in: int, bias_on: bool, zero: 
 
 
 def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
-                 L: Optional[int] = None, alpha: float = 1.0) -> dict:
+                 L: Optional[int] = None, alpha: float = 1.0, cross: str = "standard") -> dict:
     """Draw the network weights of `cfg` (row-major [out][in] matrices).
 
     Every matrix is Xavier-uniform U(+-sqrt(6/(fan_in+fan_out))).  Biases are
@@ -95,10 +95,14 @@ def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
     layers, then per stage q, k, v, merge, mlp1, mlp2 (each W then b), then the
     final projection, then the matchability weight and bias of the
     double-softmax head ("wz" [D], "bz").  The dustbin score is `alpha`.
+    cross="bidirectional": every cross stage draws one shared query/key
+    projection ("Wqk", "bqk") and "Wv", "bv" instead of q, k, v.
     """
     if seed is None:
         seed = (BIAS_ON_SEED_BASE if bias_on else WEIGHT_SEED_BASE) + cfg.cid
     L = cfg.L if L is None else L
+    if cross not in ("standard", "bidirectional"):
+        raise ValueError(f"cross = {cross!r}")
     rng = np.random.Generator(np.random.PCG64(seed))
     D = cfg.D
     widths = [3] + list(cfg.enc) + [D]
@@ -108,11 +112,12 @@ def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
         b = _bias(rng, widths[i + 1], widths[i], bias_on, zero=(i == len(widths) - 2))
         enc.append((W, b))
     stages = []
-    for _ in range(2 * L):
+    for s in range(2 * L):
         st = {}
-        for name, n_out, n_in, zero in (("q", D, D, False), ("k", D, D, False), ("v", D, D, False),
-                                        ("m", D, D, False), ("1", 2 * D, 2 * D, False),
-                                        ("2", D, 2 * D, True)):
+        attn = ((("qk", D, D, False), ("v", D, D, False)) if cross == "bidirectional" and s % 2 == 1
+                else (("q", D, D, False), ("k", D, D, False), ("v", D, D, False)))
+        for name, n_out, n_in, zero in attn + (("m", D, D, False), ("1", 2 * D, 2 * D, False),
+                                               ("2", D, 2 * D, True)):
             st["W" + name] = _xavier(rng, n_out, n_in)
             st["b" + name] = _bias(rng, n_out, n_in, bias_on, zero)
         stages.append(st)
@@ -123,7 +128,7 @@ def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
     wz = _xavier(rng, 1, D)[0]
     bz = _bias(rng, 1, D, bias_on, zero=False)[0]
     w = {"enc": enc, "stages": stages, "Wf": Wf, "bf": bf, "alpha": float(alpha),
-         "wz": wz, "bz": float(bz), "D": D, "H": cfg.H, "L": L, "dtype": cfg.dtype}
+         "wz": wz, "bz": float(bz), "D": D, "H": cfg.H, "L": L, "dtype": cfg.dtype, "cross": cross}
     if cfg.dtype == "bf16":
         w["enc"] = [(round_to_bf16(W), round_to_bf16(b)) for W, b in w["enc"]]
         w["stages"] = [{k: round_to_bf16(v) for k, v in st.items()} for st in w["stages"]]
