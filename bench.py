@@ -10,7 +10,9 @@ progress goes to stderr.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--head ds]
 
 --head ds replaces the Sinkhorn head by the double-softmax + matchability
-head (section 2.4 of the LightGlue review) on the same network and pair.
+head (section 2.4 of the LightGlue review) on the same network and pair;
+--cross bidirectional gives the cross stages one shared query/key projection
+(section 2.3 of the review).
 """
 from __future__ import annotations
 
@@ -33,13 +35,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def gemm_flops(cfg, M, N):
+def gemm_flops(cfg, M, N, cross="standard"):
     """Algorithmic flops of every GEMM launch of one pass, in launch order,
-    with the operand dtype of each (real rows only)."""
+    with the operand dtype of each (real rows only).  Bidirectional cross
+    stages project qk | v (2D outputs) instead of q | k | v."""
     R, D = M + N, cfg.D
     out = []
-    for _ in range(2 * cfg.L):
-        out += [(cfg.dtype, 2.0 * R * D * 3 * D), (cfg.dtype, 2.0 * R * D * D),
+    for s in range(2 * cfg.L):
+        nqkv = 2 if (s % 2 == 1 and cross == "bidirectional") else 3
+        out += [(cfg.dtype, 2.0 * R * D * nqkv * D), (cfg.dtype, 2.0 * R * D * D),
                 (cfg.dtype, 2.0 * R * 2 * D * 2 * D), (cfg.dtype, 2.0 * R * 2 * D * D)]
     out.append((cfg.dtype, 2.0 * R * D * D))     # final projection
     out.append(("f32", 2.0 * M * N * D))         # scores
@@ -124,6 +128,8 @@ def main():
                     help="Sinkhorn schedule (default: chosen by problem size)")
     ap.add_argument("--head", choices=["sinkhorn", "ds"], default="sinkhorn",
                     help="matching head: Sinkhorn (default) or double softmax + matchability")
+    ap.add_argument("--cross", choices=["standard", "bidirectional"], default="standard",
+                    help="cross-attention of the odd stages")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="before the steps, copy this many MiB with a plain device copy (counter scaling)")
     args = ap.parse_args()
@@ -141,7 +147,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[2]
-    w = synth.make_weights(cfg)
+    w = synth.make_weights(cfg, cross=args.cross)
     pair = synth.make_pair(cfg)
     W = sg.pack_weights(w, device=dev, head=args.head)
     ds = args.head == "ds"
@@ -202,7 +208,7 @@ def main():
         specs = {
             "sinkhorn": (sg.SG_K_SINKHORN, norm_work),
             "attention": (sg.SG_K_ATTENTION, attention_flops(cfg, M, N)),
-            "gemm": (sg.SG_K_GEMM, [f for _, f in gemm_flops(cfg, M, N)]),
+            "gemm": (sg.SG_K_GEMM, [f for _, f in gemm_flops(cfg, M, N, args.cross)]),
         }
         durs = {}
         for name, (kind, work) in specs.items():
@@ -224,7 +230,7 @@ def main():
             elif name == "attention":
                 kernels[name]["achieved_TFLOPs"] = round(float(sum(work) / dur.sum() / 1e9), 2)
             else:
-                bf = [(f, d) for (dt_, f), d in zip(gemm_flops(cfg, M, N), dur) if dt_ == "bf16"]
+                bf = [(f, d) for (dt_, f), d in zip(gemm_flops(cfg, M, N, args.cross), dur) if dt_ == "bf16"]
                 kernels[name]["achieved_TFLOPs_bf16"] = round(float(sum(f for f, _ in bf) / sum(d for _, d in bf) / 1e9), 2)
             log(f"{name}: {kernels[name]}")
         # Sinkhorn sweeps run back to back: their average launch time is the
@@ -333,11 +339,12 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded planted-homography pair, random Xavier weights)",
         "config": {"workload": ("one 1024x1024 keypoint pair per step: D=256, H=4, L=9 (18 stages), "
+                                + ("bidirectional cross-attention, " if args.cross == "bidirectional" else "")
                                 + ("double-softmax + matchability head, " if ds else "T=100, ")
                                 + "bf16 GNN operands / fp32 accumulation, fp32 scores + "
                                 + ("head" if ds else "Sinkhorn")),
                    "pairs_per_step": 1, "M": M, "N": N, "D": cfg.D, "L": cfg.L, "T": None if ds else cfg.T,
-                   "head": args.head},
+                   "head": args.head, "cross_attention": args.cross},
         "roofline": roofline, "cpu_baseline": cpu, "stages_ms": stages, "kernels": kernels,
         "batch_throughput": batch,
         "baseline_context": {"pages_ms_per_pair": {"GTX1080_1024kp": 87.0, "unstated_hw_2048kp": 70.0},

@@ -73,6 +73,17 @@ typedef enum { SG_F32 = 0, SG_BF16 = 1 } sg_dtype;
  *   with threshold. */
 typedef enum { SG_HEAD_SINKHORN = 0, SG_HEAD_DOUBLE_SOFTMAX = 1 } sg_head;
 
+/* Cross-attention of the odd stages (sg_weights.cross).
+ * SG_CROSS_STANDARD: q from the query image, k and v from the other image,
+ *   three projections per stage (SuperGlue).
+ * SG_CROSS_BIDIRECTIONAL: one shared query/key projection qk = W_qk x + b_qk
+ *   and v = W_v x + b_v per image; per head the similarity
+ *   qk_A,i . qk_B,j / sqrt(d_h) is shared by both directions: its softmax
+ *   over j gives A's messages, its softmax over i gives B's (section 2.3 of
+ *   the LightGlue review).  Each direction is evaluated as attention with
+ *   the query and key projections tied, which computes the same messages. */
+typedef enum { SG_CROSS_STANDARD = 0, SG_CROSS_BIDIRECTIONAL = 1 } sg_cross;
+
 #define SG_MAX_ENC 8     /* hidden layers of the keypoint encoder          */
 #define SG_MAX_BATCH 64  /* pairs per sg_match_batch call                  */
 
@@ -91,7 +102,9 @@ typedef enum { SG_HEAD_SINKHORN = 0, SG_HEAD_DOUBLE_SOFTMAX = 1 } sg_head;
  * aligned offset (sg_weights_tensor() enumerates offsets and shapes):
  *   encoder layer i = 0..n_enc: W [w_{i+1}][w_i], b [w_{i+1}]
  *   stage s = 0..2*L_max-1 (even s = self, odd s = cross):
- *     W_qkv [3D][D] (rows: q, then k, then v), b_qkv [3D],
+ *     W_qkv [3D][D] (rows: q, then k, then v), b_qkv [3D]
+ *       (SG_CROSS_BIDIRECTIONAL cross stages: W_qkv [2D][D], rows qk then v,
+ *       b_qkv [2D]),
  *     W_m [D][D], b_m [D]          (merge of the concatenated heads),
  *     W_1 [2D][2D], b_1 [2D]       (columns 0..D-1 multiply x, D..2D-1 m),
  *     W_2 [D][2D], b_2 [D]
@@ -108,6 +121,7 @@ typedef struct {
   int32_t L_max;
   int32_t dtype;       /* sg_dtype */
   int32_t head;        /* sg_head */
+  int32_t cross;       /* sg_cross */
   const void* blob;    /* device pointer, caller-owned */
   size_t blob_bytes;
 } sg_weights;

@@ -14,7 +14,8 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import (SG_BF16, SG_F32, SG_HEAD_DOUBLE_SOFTMAX, SG_HEAD_SINKHORN, SG_K_ATTENTION, SG_K_GEMM,
+from ._lib import (SG_BF16, SG_CROSS_BIDIRECTIONAL, SG_CROSS_STANDARD, SG_F32, SG_HEAD_DOUBLE_SOFTMAX,
+                   SG_HEAD_SINKHORN, SG_K_ATTENTION, SG_K_GEMM,
                    SG_K_NONE, SG_K_SINKHORN, SG_MAX_BATCH, SG_N_STAGE_EVENTS, SgError, SgOpts, SgWeights)
 
 __all__ = ["Weights", "weights_config", "pack_weights", "workspace_size", "sg_match",
@@ -32,14 +33,17 @@ def _dtype_code(dtype: str) -> int:
 
 
 _HEADS = {"sinkhorn": SG_HEAD_SINKHORN, "ds": SG_HEAD_DOUBLE_SOFTMAX}
+_CROSS = {"standard": SG_CROSS_STANDARD, "bidirectional": SG_CROSS_BIDIRECTIONAL}
 
 
 def weights_config(D: int, H: int, enc: Sequence[int], L_max: int, dtype: str = "f32",
-                   head: str = "sinkhorn") -> SgWeights:
-    """head: "sinkhorn" (optimal transport) or "ds" (double softmax + matchability)."""
+                   head: str = "sinkhorn", cross: str = "standard") -> SgWeights:
+    """head: "sinkhorn" (optimal transport) or "ds" (double softmax + matchability);
+    cross: "standard" or "bidirectional" cross-attention."""
     st = SgWeights()
     st.D, st.H, st.n_enc, st.L_max, st.dtype = D, H, len(enc), L_max, _dtype_code(dtype)
     st.head = _HEADS[head]
+    st.cross = _CROSS[cross]
     for i, e in enumerate(enc):
         st.enc[i] = e
     return st
@@ -73,8 +77,11 @@ def _ordered_tensors(w: dict, head: str):
     for W, b in w["enc"]:
         out += [W, b]
     for st in w["stages"]:
-        out += [np.concatenate([st["Wq"], st["Wk"], st["Wv"]]), np.concatenate([st["bq"], st["bk"], st["bv"]]),
-                st["Wm"], st["bm"], st["W1"], st["b1"], st["W2"], st["b2"]]
+        if "Wqk" in st:   # bidirectional cross stage: qk | v
+            out += [np.concatenate([st["Wqk"], st["Wv"]]), np.concatenate([st["bqk"], st["bv"]])]
+        else:
+            out += [np.concatenate([st["Wq"], st["Wk"], st["Wv"]]), np.concatenate([st["bq"], st["bk"], st["bv"]])]
+        out += [st["Wm"], st["bm"], st["W1"], st["b1"], st["W2"], st["b2"]]
     out += [w["Wf"], w["bf"], np.array([w["alpha"]], dtype=np.float32)]
     if head == "ds":
         out += [np.asarray(w["wz"]).reshape(1, -1), np.array([w["bz"]], dtype=np.float32)]
@@ -87,7 +94,7 @@ def pack_weights(w: dict, device="cuda", head: str = "sinkhorn") -> Weights:
     double-softmax head and appends the matchability weights wz, bz."""
     enc = [W.shape[0] for W, _ in w["enc"][:-1]]
     L_max = len(w["stages"]) // 2
-    st = weights_config(w["D"], w["H"], enc, L_max, w["dtype"], head)
+    st = weights_config(w["D"], w["H"], enc, L_max, w["dtype"], head, w.get("cross", "standard"))
     L = lib()
     nbytes = L.sg_weights_bytes(C.byref(st))
     count = L.sg_weights_count(C.byref(st))

@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(PKG, "libsg.so")
 SG_OK, SG_ERR_INVALID_ARG, SG_ERR_UNSUPPORTED, SG_ERR_WEIGHTS, SG_ERR_WORKSPACE, SG_ERR_HIP = 0, -1, -2, -3, -4, -5
 SG_F32, SG_BF16 = 0, 1
 SG_HEAD_SINKHORN, SG_HEAD_DOUBLE_SOFTMAX = 0, 1
+SG_CROSS_STANDARD, SG_CROSS_BIDIRECTIONAL = 0, 1
 SG_MAX_ENC = 8
 SG_MAX_BATCH = 64
 SG_N_STAGE_EVENTS = 6
@@ -25,7 +26,7 @@ STATUS_NAMES = {0: "SG_OK", -1: "SG_ERR_INVALID_ARG", -2: "SG_ERR_UNSUPPORTED", 
 class SgWeights(C.Structure):
     _fields_ = [("D", C.c_int32), ("H", C.c_int32), ("n_enc", C.c_int32),
                 ("enc", C.c_int32 * SG_MAX_ENC), ("L_max", C.c_int32), ("dtype", C.c_int32),
-                ("head", C.c_int32),
+                ("head", C.c_int32), ("cross", C.c_int32),
                 ("blob", C.c_void_p), ("blob_bytes", C.c_size_t)]
 
 

@@ -66,6 +66,8 @@ sg_status check_config(const sg_weights* w) {
   if (w->dtype != SG_F32 && w->dtype != SG_BF16) return fail(SG_ERR_INVALID_ARG, "unknown dtype %d", w->dtype);
   if (w->head != SG_HEAD_SINKHORN && w->head != SG_HEAD_DOUBLE_SOFTMAX)
     return fail(SG_ERR_INVALID_ARG, "unknown head %d", w->head);
+  if (w->cross != SG_CROSS_STANDARD && w->cross != SG_CROSS_BIDIRECTIONAL)
+    return fail(SG_ERR_INVALID_ARG, "unknown cross-attention variant %d", w->cross);
   const int dh = w->D / w->H;
   if (dh != 16 && dh != 64) return fail(SG_ERR_UNSUPPORTED, "head dimension %d (supported: 16, 64)", dh);
   if (w->D % 32 || w->D > 1024) return fail(SG_ERR_UNSUPPORTED, "D = %d (supported: multiples of 32 up to 1024)", w->D);
@@ -97,7 +99,8 @@ WLayout layout_of(const sg_weights* w) {
   }
   L.stage_first = (int)L.t.size();
   for (int s = 0; s < 2 * w->L_max; ++s) {
-    add(3 * D, D, es); add(1, 3 * D, es);
+    const int nqkv = (s & 1) && w->cross == SG_CROSS_BIDIRECTIONAL ? 2 : 3;  // projections of the stage
+    add(nqkv * D, D, es); add(1, nqkv * D, es);
     add(D, D, es); add(1, D, es);
     add(2 * D, 2 * D, es); add(1, 2 * D, es);
     add(D, 2 * D, es); add(1, D, es);
@@ -382,16 +385,20 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
   const float log2e = 1.4426950408889634f;
   for (int s = s0; s < s1; ++s) {
     const int base = L.stage_first + kPerStage * s;
-    // q | k | v = x W_qkv^T + b_qkv  (v written transposed)
+    // q | k | v = x W_qkv^T + b_qkv  (v written transposed or swizzled); a
+    // bidirectional cross stage projects qk | v and writes qk as both q and k
     {
+      const bool tied = (s & 1) && w->cross == SG_CROSS_BIDIRECTIONAL;
+      const int nout = (tied ? 2 : 3) * D;
       GemmArgs g;
       memset(&g, 0, sizeof(g));
       g.A0 = X; g.lda0 = D; g.K0 = D; g.K = D;
       g.W = atv(w, L, base); g.ldw = D; g.bias = atv(w, L, base + 1);
-      g.C = QK; g.C2 = op == SG_BF16 ? ws + wl.VS : VT; g.C3 = ws + wl.KS; g.split = 2 * D;
-      GemmBatch b = single(R, 3 * D, wl.ldqk);
+      g.C = QK; g.C2 = op == SG_BF16 ? ws + wl.VS : VT; g.C3 = ws + wl.KS;
+      g.split = nout - D; g.tied = tied;
+      GemmBatch b = single(R, nout, wl.ldqk);
       b.p[0].ldct = wl.ldvt;
-      HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, 0, EPI_QKV, g, b, R, 3 * D, st); }), "qkv GEMM");
+      HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, 0, EPI_QKV, g, b, R, nout, st); }), "qkv GEMM");
     }
     // multi-head attention: self on even stages, cross on odd stages
     {
@@ -659,7 +666,7 @@ std::string call_key(int kind, const Problem& p, const sg_weights* w, int Lst, i
   if (w) {
     put(k, w->D); put(k, w->H); put(k, w->n_enc);
     for (int i = 0; i < w->n_enc; ++i) put(k, w->enc[i]);
-    put(k, w->L_max); put(k, w->dtype); put(k, w->head); put(k, w->blob); put(k, w->blob_bytes);
+    put(k, w->L_max); put(k, w->dtype); put(k, w->head); put(k, w->cross); put(k, w->blob); put(k, w->blob_bytes);
   }
   put(k, Lst); put(k, T); put(k, out);
   put(k, o ? o->match_threshold : 0.f);

@@ -182,9 +182,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
     // wave-private LDS transposition into the tile-swizzled C3; v straight
     // from the accumulators into the tile-swizzled C2 (its layout is the
     // accumulator layout).  Column ranges: q [0, D), k [D, 2D), v [2D, 3D)
-    // with D = split / 2; the QKV GEMM covers the whole row space, so the
-    // problem's rows are the compact rows (32-row tiles stay aligned).
-    const int Dm = g.split / 2;
+    // with D = split / 2; tied (one shared query/key projection): qk [0, D)
+    // written as both q and k, v [D, 2D) with D = split.  The QKV GEMM covers
+    // the whole row space, so the problem's rows are the compact rows (32-row
+    // tiles stay aligned).
+    const int Dm = g.tied ? g.split : g.split / 2;
     constexpr int TP = 32 + 8;
     bf16* tt = reinterpret_cast<bf16*>(&As[0][0]) + wave * 32 * TP;
     bf16* const cq = reinterpret_cast<bf16*>(g.C);
@@ -206,7 +208,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
             const int r = rr0 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
             cq[P.c_off + (size_t)r * P.ldc + nn0 + nl] = (bf16)(acc[i][j][e] + bias);
           }
-        } else if (nn0 < 2 * Dm) {
+        }
+        if (nn0 < g.split && (g.tied || nn0 >= Dm)) {
+          const int kc = g.tied ? nn0 : nn0 - Dm;  // column of k
 #pragma unroll
           for (int e = 0; e < 16; ++e)
             tt[nl * TP + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)] = (bf16)(acc[i][j][e] + bias);
@@ -218,12 +222,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
             bf16x8 v;
 #pragma unroll
             for (int t = 0; t < 8; ++t) v[t] = tt[(16 * which + 8 * (L >> 5) + t) * TP + (L & 31)];
-            const size_t blk = (size_t)tile * (Dm / 16) + (nn0 - Dm) / 16 + which;
+            const size_t blk = (size_t)tile * (Dm / 16) + kc / 16 + which;
             *reinterpret_cast<bf16x8*>(ck + blk * 512 + L * 8) = v;
           }
           __builtin_amdgcn_wave_barrier();
-        } else {
-          bf16* base = cv + ((size_t)tile * (Dm / 32) + (nn0 - 2 * Dm) / 32) * 1024 + lane * 8;
+        } else if (nn0 >= g.split) {
+          bf16* base = cv + ((size_t)tile * (Dm / 32) + (nn0 - g.split) / 32) * 1024 + lane * 8;
           bf16x8 lo, hi8;
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
@@ -290,6 +294,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
         if constexpr (EPI == EPI_BIAS || EPI == EPI_RELU || EPI == EPI_QKV) {
           if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
           reinterpret_cast<OutT*>(g.C)[P.c_off + (size_t)r * P.ldc + n] = (OutT)v;
+          // tied query/key projection: the same column is k as well (k at +split)
+          if (EPI == EPI_QKV && g.tied) reinterpret_cast<OutT*>(g.C)[P.c_off + (size_t)r * P.ldc + n + g.split] = (OutT)v;
         } else if constexpr (EPI == EPI_RESID) {
           float* c = reinterpret_cast<float*>(g.C) + P.c_off + (size_t)r * P.ldc + n;
           *c = *c + v;
@@ -307,7 +313,8 @@ static void gemm_go(const GemmArgs& g, const GemmBatch& b, int max_rows, int max
   // large problems (several tiles per CU even at 128 x 128): the LDS-efficient shape
   const long big_tiles = (long)((max_rows + 127) / 128) * ((max_n + 127) / 128) * b.n;
   GemmArgs a = g;
-  if (big_tiles >= 1024) {
+  // (a QKV split must fall on a tile edge: 128-wide tiles need it at a multiple of 128)
+  if (big_tiles >= 1024 && !(EPI == EPI_QKV && g.split % 128)) {
     a.gx = (max_rows + 127) / 128;
     a.gy = (max_n + 127) / 128;
     const int T = a.gx * a.gy * b.n;
@@ -324,7 +331,7 @@ hipError_t launch_gemm(int op, int a0f, int wd, int outf, int epi, const GemmArg
                        const GemmBatch& b, int max_rows, int max_n, hipStream_t st) {
   if (max_rows <= 0 || max_n <= 0 || b.n <= 0) return hipSuccess;
   if (g.K % 8 || g.K0 % 8) return hipErrorInvalidValue;
-  if (epi == EPI_QKV && g.split % 128) return hipErrorInvalidValue;  // V columns start on a tile edge
+  if (epi == EPI_QKV && g.split % 64) return hipErrorInvalidValue;  // V columns start on a tile edge
 #define SG_GO(O, A, W, OUT, E) gemm_go<O, A, W, OUT, E>(g, b, max_rows, max_n, st)
   // The operand-type / epilogue combinations the pipeline uses.
   if (op == SG_F32) {

@@ -57,7 +57,7 @@ enum Epilogue {
   EPI_BIAS = 0,   // C = A W^T + b
   EPI_RELU = 1,   // C = max(A W^T + b, 0)
   EPI_RESID = 2,  // C (fp32) = C + A W^T + b   (in place residual add)
-  EPI_QKV = 3,    // columns < split: QK = A W^T + b; others: VT (transposed)
+  EPI_QKV = 3,    // columns < split: QK = A W^T + b (tied: q and k); others: VT / VS
   EPI_SCORE = 4   // C = scale * A W^T and CT = its transpose (fp32)
 };
 
@@ -70,7 +70,8 @@ struct GemmArgs {
   void* C; void* C2;                 // outputs (C2: VT / VS or ZT)
   void* C3;                          // EPI_QKV, bf16: KS
   float scale;
-  int split;                         // EPI_QKV: first column that goes to VT
+  int split;                         // EPI_QKV: first column that goes to VT (VS)
+  int tied;                          // EPI_QKV: columns [0, split) are both q and k
   int gx, gy;                        // row and column tiles (set by the launcher)
 };
 

@@ -153,3 +153,25 @@ def test_double_softmax_head_layout_and_validation():
     big = lib.sg_stage_match_ds_workspace_size(4096, 4096, 256)
     assert 2 * 4096 * 4096 * 4 < big < 4 * 4096 * 4096 * 4
     assert lib.sg_workspace_size(C.byref(wd), 4096, 4096, 8) > 2 * 8 * 4096 * 4096 * 4
+
+
+def test_bidirectional_cross_layout_and_validation():
+    """Bidirectional cross stages store W_qk | W_v ([2D][D]) and their bias
+    [2D]: D^2 + D fewer parameters per cross stage; an unknown variant is
+    rejected."""
+    lib = _lib.load()
+    w, wb = _cfg(), _cfg()
+    wb.cross = _lib.SG_CROSS_BIDIRECTIONAL
+    assert lib.sg_weights_count(C.byref(wb)) == lib.sg_weights_count(C.byref(w))
+
+    def params(cfg):
+        off, r, c = C.c_size_t(), C.c_int32(), C.c_int32()
+        total = 0
+        for i in range(lib.sg_weights_count(C.byref(cfg))):
+            assert lib.sg_weights_tensor(C.byref(cfg), i, C.byref(off), C.byref(r), C.byref(c)) == 0
+            total += r.value * c.value
+        return total
+    assert params(w) - params(wb) == 9 * (256 * 256 + 256)
+    bad = _cfg()
+    bad.cross = 2
+    assert lib.sg_weights_count(C.byref(bad)) == -1
