@@ -26,6 +26,9 @@ Readings taken where the pages are silent (each also pinned by a test):
 * argmax ties go to the lowest index; the match threshold is strict '>';
 * masked (padded) keys and points are simply absent: a padded pair is the
   unpadded pair;
+* rotary encoding ([LightGlue-review] section 2.2): positions are the
+  normalised keypoints above; channel pairs (2k, 2k+1) inside each head
+  share angle k, the same for every head;
 * double-softmax head ([LightGlue-review] section 2.4): the similarity is
   the same S = f_A f_B^T / sqrt(D) (the page divides each projected
   descriptor by D^(1/4)); the matchability logit reads the last GNN states
@@ -46,7 +49,7 @@ __all__ = [
     "score_matrix", "logsumexp", "log_sinkhorn_iterations",
     "log_optimal_transport", "extract_matches", "superglue_match",
     "superglue_descriptors", "sinkhorn_knopp_exp", "match_from_descriptors",
-    "bidirectional_cross_attention",
+    "bidirectional_cross_attention", "rope_angles", "rotate_pairs",
     "log_sigmoid", "matchability", "double_softmax_assignment",
     "double_softmax_from_descriptors", "double_softmax_match",
 ]
@@ -86,7 +89,32 @@ def _softmax_rows(e):
     return a / a.sum(axis=1, keepdims=True)
 
 
-def multi_head_attention(x, src, st, heads):
+def rope_angles(pos, basis):
+    """[LightGlue-review] section 2.2 (relative positions in self-attention):
+    the per-head channels form d_h/2 two-dimensional subspaces; subspace k
+    maps a point's position p onto its learned 2-D basis vector b_k, giving
+    the angle theta_k = <b_k, p>.  Returns [n][d_h/2]."""
+    return _f64(pos) @ _f64(basis).T
+
+
+def rotate_pairs(t, theta, heads):
+    """[LightGlue-review] section 2.2: rotate each 2-D subspace of every head
+    by its angle: channels (2k, 2k+1) of head h (offset h*d_h) map
+    (a, b) -> (a cos theta_k - b sin theta_k, a sin theta_k + b cos theta_k).
+    Every head uses the same angles."""
+    t = _f64(t).copy()
+    D = t.shape[1]
+    dh = D // heads
+    c, s = np.cos(theta), np.sin(theta)
+    for h in range(heads):
+        a = t[:, h * dh:(h + 1) * dh:2].copy()
+        b = t[:, h * dh + 1:(h + 1) * dh:2].copy()
+        t[:, h * dh:(h + 1) * dh:2] = a * c - b * s
+        t[:, h * dh + 1:(h + 1) * dh:2] = a * s + b * c
+    return t
+
+
+def multi_head_attention(x, src, st, heads, rope=None):
     """Message m for every query point of `x` from the source points `src`.
 
     [realcat] section "Attentional Aggregation": q_i = W1 x_i^Q + b1 from the
@@ -96,6 +124,8 @@ def multi_head_attention(x, src, st, heads):
     sqrt(d_k), d_k the per-head dimension.  Heads split D into contiguous
     blocks; the concatenated heads then pass the merge projection
     W_m m + b_m.  Stage weights `st` hold Wq,bq,Wk,bk,Wv,bv,Wm,bm.
+    rope = (theta_x, theta_src): [LightGlue-review] section 2.2, q and k (not
+    v) rotated by their points' angles after the projection.
     """
     x, src = _f64(x), _f64(src)
     D = x.shape[1]
@@ -103,6 +133,9 @@ def multi_head_attention(x, src, st, heads):
     q = x @ _f64(st["Wq"]).T + _f64(st["bq"])
     k = src @ _f64(st["Wk"]).T + _f64(st["bk"])
     v = src @ _f64(st["Wv"]).T + _f64(st["bv"])
+    if rope is not None:
+        q = rotate_pairs(q, rope[0], heads)
+        k = rotate_pairs(k, rope[1], heads)
     msg = np.zeros((x.shape[0], D))
     for h in range(heads):
         c = slice(h * dh, (h + 1) * dh)
@@ -149,14 +182,14 @@ def _update_mlp(x, m, st):
     return h @ _f64(st["W2"]).T + _f64(st["b2"])
 
 
-def attentional_propagation(x, src, st, heads):
+def attentional_propagation(x, src, st, heads, rope=None):
     """[realcat] section "多层GNN" (AttentionalPropagation): the residual
     update MLP([x || m]) with channels [2D, 2D, D], ReLU between the two
     layers.  Returns the update (delta), not x + delta."""
-    return _update_mlp(x, multi_head_attention(x, src, st, heads), st)
+    return _update_mlp(x, multi_head_attention(x, src, st, heads, rope), st)
 
 
-def attentional_gnn(xA, xB, stages, heads, first_stage=0):
+def attentional_gnn(xA, xB, stages, heads, first_stage=0, rope=None):
     """[realcat] section "多层GNN" (AttentionalGNN) and [GNN-blog] section
     "多轮消息怎样回到同一幅图": stages alternate self (sources = own image)
     and cross (sources = the other image), self first; each stage has its own
@@ -165,19 +198,24 @@ def attentional_gnn(xA, xB, stages, heads, first_stage=0):
     network starting at stage index `first_stage` (even = self).  A cross
     stage whose weights hold "Wqk" uses bidirectional_cross_attention
     ([LightGlue-review] section 2.3) for both messages, followed by the same
-    update MLP."""
+    update MLP.  rope = (theta_A, theta_B) (rope_angles of each image's
+    points): self stages rotate q and k ([LightGlue-review] section 2.2: the
+    encoding is the same for every layer and never enters cross stages)."""
     xA, xB = _f64(xA).copy(), _f64(xB).copy()
     for s, st in enumerate(stages, start=first_stage):
         if s % 2 == 1 and "Wqk" in st:   # bidirectional cross
             mA, mB = bidirectional_cross_attention(xA, xB, st, heads)
             dA, dB = _update_mlp(xA, mA, st), _update_mlp(xB, mB, st)
         else:
+            ropeA = ropeB = None
             if s % 2 == 0:          # self
                 srcA, srcB = xA, xB
+                if rope is not None:
+                    ropeA, ropeB = (rope[0], rope[0]), (rope[1], rope[1])
             else:                   # cross
                 srcA, srcB = xB, xA
-            dA = attentional_propagation(xA, srcA, st, heads)
-            dB = attentional_propagation(xB, srcB, st, heads)
+            dA = attentional_propagation(xA, srcA, st, heads, ropeA)
+            dB = attentional_propagation(xB, srcB, st, heads, ropeB)
         xA, xB = xA + dA, xB + dB
     return xA, xB
 
@@ -268,14 +306,17 @@ def superglue_descriptors(pair, weights, L=None):
     L = weights["L"] if L is None else L
     H = weights["H"]
     out = {}
-    xs = []
+    xs, thetas = [], []
     for side in ("0", "1"):
         w, h = pair["image_size" + side]
         kn = normalize_keypoints(pair["kpts" + side], w, h)
         x0 = _f64(pair["desc" + side]) + keypoint_encoder(kn, pair["conf" + side], weights["enc"])
         xs.append(x0)
         out["x0_" + side] = x0
-    xA, xB = attentional_gnn(xs[0], xs[1], weights["stages"][:2 * L], H)
+        if weights.get("rope_basis") is not None:
+            thetas.append(rope_angles(kn, weights["rope_basis"]))
+    rope = tuple(thetas) if thetas else None
+    xA, xB = attentional_gnn(xs[0], xs[1], weights["stages"][:2 * L], H, rope=rope)
     out["xL_0"], out["xL_1"] = xA, xB
     out["f0"] = final_projection(xA, weights["Wf"], weights["bf"])
     out["f1"] = final_projection(xB, weights["Wf"], weights["bf"])

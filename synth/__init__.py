@@ -85,7 +85,8 @@ def _bias(rng: np.random.Generator, n_out: int, n_in: int, bias_on: bool, zero: 
 
 
 def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
-                 L: Optional[int] = None, alpha: float = 1.0, cross: str = "standard") -> dict:
+                 L: Optional[int] = None, alpha: float = 1.0, cross: str = "standard",
+                 rope: bool = False) -> dict:
     """Draw the network weights of `cfg` (row-major [out][in] matrices).
 
     Every matrix is Xavier-uniform U(+-sqrt(6/(fan_in+fan_out))).  Biases are
@@ -97,6 +98,7 @@ def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
     double-softmax head ("wz" [D], "bz").  The dustbin score is `alpha`.
     cross="bidirectional": every cross stage draws one shared query/key
     projection ("Wqk", "bqk") and "Wv", "bv" instead of q, k, v.
+    rope=True: a rotary basis "rope_basis" [d_h/2][2] ~ N(0, 1) (kept fp32).
     """
     if seed is None:
         seed = (BIAS_ON_SEED_BASE if bias_on else WEIGHT_SEED_BASE) + cfg.cid
@@ -127,8 +129,11 @@ def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
     # that every earlier tensor is the same with or without it
     wz = _xavier(rng, 1, D)[0]
     bz = _bias(rng, 1, D, bias_on, zero=False)[0]
+    # rotary basis of self-attention ([d_h/2][2], N(0, 1)), drawn last
+    basis = rng.standard_normal((D // cfg.H // 2, 2)).astype(np.float32) if rope else None
     w = {"enc": enc, "stages": stages, "Wf": Wf, "bf": bf, "alpha": float(alpha),
-         "wz": wz, "bz": float(bz), "D": D, "H": cfg.H, "L": L, "dtype": cfg.dtype, "cross": cross}
+         "wz": wz, "bz": float(bz), "D": D, "H": cfg.H, "L": L, "dtype": cfg.dtype, "cross": cross,
+         "rope_basis": basis}
     if cfg.dtype == "bf16":
         w["enc"] = [(round_to_bf16(W), round_to_bf16(b)) for W, b in w["enc"]]
         w["stages"] = [{k: round_to_bf16(v) for k, v in st.items()} for st in w["stages"]]
