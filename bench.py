@@ -12,7 +12,8 @@ progress goes to stderr.
 --head ds replaces the Sinkhorn head by the double-softmax + matchability
 head (section 2.4 of the LightGlue review) on the same network and pair;
 --cross bidirectional gives the cross stages one shared query/key projection
-(section 2.3 of the review).
+(section 2.3 of the review); --rope rotates q and k of the self stages by the
+keypoints' positions (section 2.2).
 """
 from __future__ import annotations
 
@@ -130,6 +131,7 @@ def main():
                     help="matching head: Sinkhorn (default) or double softmax + matchability")
     ap.add_argument("--cross", choices=["standard", "bidirectional"], default="standard",
                     help="cross-attention of the odd stages")
+    ap.add_argument("--rope", action="store_true", help="rotary position encoding in self-attention")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="before the steps, copy this many MiB with a plain device copy (counter scaling)")
     args = ap.parse_args()
@@ -147,7 +149,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[2]
-    w = synth.make_weights(cfg, cross=args.cross)
+    w = synth.make_weights(cfg, cross=args.cross, rope=args.rope)
     pair = synth.make_pair(cfg)
     W = sg.pack_weights(w, device=dev, head=args.head)
     ds = args.head == "ds"
@@ -340,11 +342,12 @@ def main():
         "data": "synthetic (seeded planted-homography pair, random Xavier weights)",
         "config": {"workload": ("one 1024x1024 keypoint pair per step: D=256, H=4, L=9 (18 stages), "
                                 + ("bidirectional cross-attention, " if args.cross == "bidirectional" else "")
+                                + ("rotary self-attention, " if args.rope else "")
                                 + ("double-softmax + matchability head, " if ds else "T=100, ")
                                 + "bf16 GNN operands / fp32 accumulation, fp32 scores + "
                                 + ("head" if ds else "Sinkhorn")),
                    "pairs_per_step": 1, "M": M, "N": N, "D": cfg.D, "L": cfg.L, "T": None if ds else cfg.T,
-                   "head": args.head, "cross_attention": args.cross},
+                   "head": args.head, "cross_attention": args.cross, "rope": args.rope},
         "roofline": roofline, "cpu_baseline": cpu, "stages_ms": stages, "kernels": kernels,
         "batch_throughput": batch,
         "baseline_context": {"pages_ms_per_pair": {"GTX1080_1024kp": 87.0, "unstated_hw_2048kp": 70.0},

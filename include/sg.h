@@ -84,6 +84,14 @@ typedef enum { SG_HEAD_SINKHORN = 0, SG_HEAD_DOUBLE_SOFTMAX = 1 } sg_head;
  *   the query and key projections tied, which computes the same messages. */
 typedef enum { SG_CROSS_STANDARD = 0, SG_CROSS_BIDIRECTIONAL = 1 } sg_cross;
 
+/* Rotary position encoding of the self stages (sg_weights.rope = 1), after
+ * section 2.2 of the LightGlue review: inside each head, channel pairs
+ * (2k, 2k+1) of q and k (never v, never in cross stages) are rotated by the
+ * angle theta_k = <b_k, p>, where p is the point's position normalised as
+ * for the encoder and b_k (k < d_h / 2) is a learned 2-D basis stored in
+ * the blob.  Every head and every self stage uses the same angles; the
+ * (cos, sin) table is computed once per call. */
+
 #define SG_MAX_ENC 8     /* hidden layers of the keypoint encoder          */
 #define SG_MAX_BATCH 64  /* pairs per sg_match_batch call                  */
 
@@ -112,6 +120,8 @@ typedef enum { SG_CROSS_STANDARD = 0, SG_CROSS_BIDIRECTIONAL = 1 } sg_cross;
  *   alpha: one float32             (dustbin score, always fp32)
  *   SG_HEAD_DOUBLE_SOFTMAX only:
  *   w_z [1][D], b_z [1]            (matchability Linear(D, 1))
+ *   rope = 1 only:
+ *   B_rot [D/H/2][2]               (rotary basis, always fp32)
  * Head h owns channels [h*D/H, (h+1)*D/H) of q, k, v and of the merge input.
  */
 typedef struct {
@@ -122,6 +132,7 @@ typedef struct {
   int32_t dtype;       /* sg_dtype */
   int32_t head;        /* sg_head */
   int32_t cross;       /* sg_cross */
+  int32_t rope;        /* 1: rotary encoding in self-attention */
   const void* blob;    /* device pointer, caller-owned */
   size_t blob_bytes;
 } sg_weights;
@@ -233,6 +244,13 @@ sg_status sg_stage_encode(const float* kpts, const float* conf, const float* des
 /* Stages s0 .. s1-1 of the GNN, in place on the fp32 states xA [M][D], xB [N][D]. */
 sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weights* weights,
                        int32_t s0, int32_t s1, const sg_opts* opts);
+
+/* As sg_stage_gnn, with the point positions posA [M][2], posB [N][2] that
+   rotary self-attention needs (normalised, or pixels when
+   opts->image_size is set); they may be NULL for weights without rope.
+   sg_stage_gnn is this call with NULL positions. */
+sg_status sg_stage_gnn_pos(float* xA, const float* posA, int32_t M, float* xB, const float* posB, int32_t N,
+                           const sg_weights* weights, int32_t s0, int32_t s1, const sg_opts* opts);
 
 /* Final projection f [n][D] fp32 = W_f x + b_f. */
 sg_status sg_stage_project(const float* x, int32_t n, const sg_weights* weights, float* f_out,

@@ -37,13 +37,15 @@ _CROSS = {"standard": SG_CROSS_STANDARD, "bidirectional": SG_CROSS_BIDIRECTIONAL
 
 
 def weights_config(D: int, H: int, enc: Sequence[int], L_max: int, dtype: str = "f32",
-                   head: str = "sinkhorn", cross: str = "standard") -> SgWeights:
+                   head: str = "sinkhorn", cross: str = "standard", rope: bool = False) -> SgWeights:
     """head: "sinkhorn" (optimal transport) or "ds" (double softmax + matchability);
-    cross: "standard" or "bidirectional" cross-attention."""
+    cross: "standard" or "bidirectional" cross-attention; rope: rotary encoding
+    in self-attention."""
     st = SgWeights()
     st.D, st.H, st.n_enc, st.L_max, st.dtype = D, H, len(enc), L_max, _dtype_code(dtype)
     st.head = _HEADS[head]
     st.cross = _CROSS[cross]
+    st.rope = 1 if rope else 0
     for i, e in enumerate(enc):
         st.enc[i] = e
     return st
@@ -85,6 +87,8 @@ def _ordered_tensors(w: dict, head: str):
     out += [w["Wf"], w["bf"], np.array([w["alpha"]], dtype=np.float32)]
     if head == "ds":
         out += [np.asarray(w["wz"]).reshape(1, -1), np.array([w["bz"]], dtype=np.float32)]
+    if w.get("rope_basis") is not None:
+        out.append(np.asarray(w["rope_basis"]))
     return out
 
 
@@ -94,14 +98,17 @@ def pack_weights(w: dict, device="cuda", head: str = "sinkhorn") -> Weights:
     double-softmax head and appends the matchability weights wz, bz."""
     enc = [W.shape[0] for W, _ in w["enc"][:-1]]
     L_max = len(w["stages"]) // 2
-    st = weights_config(w["D"], w["H"], enc, L_max, w["dtype"], head, w.get("cross", "standard"))
+    rope = w.get("rope_basis") is not None
+    st = weights_config(w["D"], w["H"], enc, L_max, w["dtype"], head, w.get("cross", "standard"), rope)
     L = lib()
     nbytes = L.sg_weights_bytes(C.byref(st))
     count = L.sg_weights_count(C.byref(st))
     if nbytes == 0 or count <= 0:
         raise SgError(-1, "sg_weights_bytes")
     tensors = _ordered_tensors(w, head)
-    alpha_index = count - (3 if head == "ds" else 1)  # alpha is always float32
+    # alpha and the rotary basis are always float32
+    alpha_index = count - (3 if head == "ds" else 1) - (1 if rope else 0)
+    f32_index = {alpha_index, count - 1} if rope else {alpha_index}
     if len(tensors) != count:
         raise ValueError(f"weight dictionary has {len(tensors)} tensors, the layout {count}")
     host = torch.zeros(nbytes, dtype=torch.uint8)
@@ -113,7 +120,7 @@ def pack_weights(w: dict, device="cuda", head: str = "sinkhorn") -> Weights:
         arr = np.ascontiguousarray(arr, dtype=np.float32).reshape(-1)
         if arr.size != rows.value * cols.value:
             raise ValueError(f"tensor {i}: {arr.size} values, layout {rows.value}x{cols.value}")
-        t = torch.from_numpy(arr).to(torch.float32 if i == alpha_index else tdt)
+        t = torch.from_numpy(arr).to(torch.float32 if i in f32_index else tdt)
         raw = t.view(torch.uint8)
         host[off.value: off.value + raw.numel()] = raw
     return Weights(st, host.to(device), L_max)
@@ -311,16 +318,22 @@ def sg_stage_encode(kpts, conf, desc, weights: Weights, image_size=(0.0, 0.0), w
 
 
 def sg_stage_gnn(xA, xB, weights: Weights, s0: int, s1: int, workspace=None, timed_kernel=SG_K_NONE,
-                 kernel_events=None):
-    """Runs stages [s0, s1) in place on float32 states xA [M][D], xB [N][D]."""
+                 kernel_events=None, posA=None, posB=None, image_size=None):
+    """Runs stages [s0, s1) in place on float32 states xA [M][D], xB [N][D].
+    posA [M][2], posB [N][2]: point positions (rotary self-attention), normalised,
+    or pixels with image_size=(wA, hA, wB, hB)."""
     M, N, D = xA.shape[0], xB.shape[0], weights.D
     _check_tensor(xA, "xA", torch.float32, (M, D))
     _check_tensor(xB, "xB", torch.float32, (N, D))
+    if posA is not None:
+        _check_tensor(posA, "posA", torch.float32, (M, 2))
+        _check_tensor(posB, "posB", torch.float32, (N, 2))
     if workspace is None:
         workspace = _workspace(xA.device, workspace_size(weights, M, N, 1))
     o, keep, count = _opts(xA.device, workspace=workspace, timed_kernel=timed_kernel,
-                           kernel_events=kernel_events)
-    _lib.check(lib().sg_stage_gnn(_ptr(xA), M, _ptr(xB), N, weights.ref, s0, s1, C.byref(o)), "sg_stage_gnn")
+                           kernel_events=kernel_events, image_size=image_size)
+    _lib.check(lib().sg_stage_gnn_pos(_ptr(xA), _ptr(posA), M, _ptr(xB), _ptr(posB), N, weights.ref, s0, s1,
+                                      C.byref(o)), "sg_stage_gnn_pos")
     return count.value
 
 

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "SG_OK", -1: "SG_ERR_INVALID_ARG", -2: "SG_ERR_UNSUPPORTED", 
 class SgWeights(C.Structure):
     _fields_ = [("D", C.c_int32), ("H", C.c_int32), ("n_enc", C.c_int32),
                 ("enc", C.c_int32 * SG_MAX_ENC), ("L_max", C.c_int32), ("dtype", C.c_int32),
-                ("head", C.c_int32), ("cross", C.c_int32),
+                ("head", C.c_int32), ("cross", C.c_int32), ("rope", C.c_int32),
                 ("blob", C.c_void_p), ("blob_bytes", C.c_size_t)]
 
 
@@ -58,6 +58,7 @@ SIGNATURES = {
                             _P, _P, _O]),
     "sg_stage_encode": (_I, [_P, _P, _P, _I, _F, _F, _W, _P, _O]),
     "sg_stage_gnn": (_I, [_P, _I, _P, _I, _W, _I, _I, _O]),
+    "sg_stage_gnn_pos": (_I, [_P, _P, _I, _P, _P, _I, _W, _I, _I, _O]),
     "sg_stage_project": (_I, [_P, _I, _W, _P, _O]),
     "sg_stage_match": (_I, [_P, _I, _P, _I, _I, _F, _I, _P, _P, _O]),
     "sg_stage_match_workspace_size": (C.c_size_t, [_I, _I, _I]),

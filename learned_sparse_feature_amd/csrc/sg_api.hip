@@ -50,6 +50,7 @@ struct WLayout {
   int final_first = 0;  // index of W_f
   int alpha = 0;        // index of alpha
   int wz = -1;          // index of the matchability weight (double-softmax head)
+  int rope = -1;        // index of the rotary basis
 };
 
 constexpr int kPerStage = 8;  // W_qkv, b_qkv, W_m, b_m, W_1, b_1, W_2, b_2
@@ -68,6 +69,7 @@ sg_status check_config(const sg_weights* w) {
     return fail(SG_ERR_INVALID_ARG, "unknown head %d", w->head);
   if (w->cross != SG_CROSS_STANDARD && w->cross != SG_CROSS_BIDIRECTIONAL)
     return fail(SG_ERR_INVALID_ARG, "unknown cross-attention variant %d", w->cross);
+  if (w->rope != 0 && w->rope != 1) return fail(SG_ERR_INVALID_ARG, "rope must be 0 or 1 (got %d)", w->rope);
   const int dh = w->D / w->H;
   if (dh != 16 && dh != 64) return fail(SG_ERR_UNSUPPORTED, "head dimension %d (supported: 16, 64)", dh);
   if (w->D % 32 || w->D > 1024) return fail(SG_ERR_UNSUPPORTED, "D = %d (supported: multiples of 32 up to 1024)", w->D);
@@ -115,6 +117,10 @@ WLayout layout_of(const sg_weights* w) {
     add(1, D, es);
     add(1, 1, es);
   }
+  if (w->rope) {
+    L.rope = (int)L.t.size();
+    add(D / w->H / 2, 2, 4);  // always fp32
+  }
   L.bytes = off;
   return L;
 }
@@ -133,12 +139,12 @@ sg_status check_weights(const sg_weights* w, WLayout* out) {
 // ---------------------------------------------------------- workspace layout
 
 struct WsLayout {
-  size_t X, H0, H1, QK, VT, KS, VS, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, total;
+  size_t X, H0, H1, QK, VT, KS, VS, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, ROPE, total;
   int ldvt, ldqk;
 };
 
 WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, long pf, long pd, long uf, long vf,
-                       long nb) {
+                       long nb, long ropef = 0) {
   WsLayout L;
   // row strides are kept off powers of two (+64 / +16 bytes) so that the
   // strided accesses of the attention kernel spread over the L2 channels
@@ -171,6 +177,7 @@ WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, l
   L.UD = take((size_t)uf * 4);  // dustbin entries of the double-softmax head
   L.VD = take((size_t)vf * 4);
   L.IDX1 = take((size_t)nb * 4);
+  L.ROPE = take((size_t)ropef * 8);  // (cos, sin) per row and rotary pair
   L.total = o;
   return L;
 }
@@ -178,7 +185,8 @@ WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, l
 WsLayout ws_layout(const sg_weights* w, long R, long zf, long ztf, long pf, long pd, long uf, long vf, long nb) {
   int maxw = 0;
   for (int i = 0; i < w->n_enc; ++i) maxw = std::max(maxw, w->enc[i]);
-  return ws_layout_raw(w->D, w->dtype == SG_BF16 ? 2 : 4, maxw, R, zf, ztf, pf, pd, uf, vf, nb);
+  return ws_layout_raw(w->D, w->dtype == SG_BF16 ? 2 : 4, maxw, R, zf, ztf, pf, pd, uf, vf, nb,
+                       w->rope ? R * (w->D / w->H / 2) : 0);
 }
 
 // ----------------------------------------------------------- library workspace
@@ -371,6 +379,18 @@ sg_status run_encoder(const Problem& p, const Plan& pl, const sg_weights* w, con
   return SG_OK;
 }
 
+// Rotary table of the self stages from the positions of the problem.
+sg_status run_rope_table(const Problem& p, const Plan& pl, const sg_weights* w, const WLayout& L, char* ws,
+                         const WsLayout& wl, hipStream_t st) {
+  EncArgs e;
+  memset(&e, 0, sizeof(e));
+  for (int i = 0; i < 2; ++i) e.kpts[i] = p.kp[i];
+  memcpy(e.img, p.img, sizeof(e.img));
+  HIPCHK(launch_rope_table(e, pl.seg, at<float>(w, L, L.rope), w->D / w->H, pl.R,
+                           reinterpret_cast<float2*>(ws + wl.ROPE), st), "rotary table");
+  return SG_OK;
+}
+
 // Stages [s0, s1) in place on X (compact rows of every image of the plan).
 sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0, int s1, char* ws,
                   const WsLayout& wl, int flags, Timer& tm, hipStream_t st) {
@@ -396,6 +416,10 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       g.W = atv(w, L, base); g.ldw = D; g.bias = atv(w, L, base + 1);
       g.C = QK; g.C2 = op == SG_BF16 ? ws + wl.VS : VT; g.C3 = ws + wl.KS;
       g.split = nout - D; g.tied = tied;
+      if (w->rope && !(s & 1)) {  // self stage: rotate q and k
+        g.rope = reinterpret_cast<const float2*>(ws + wl.ROPE);
+        g.rope_dh = D / w->H;
+      }
       GemmBatch b = single(R, nout, wl.ldqk);
       b.p[0].ldct = wl.ldvt;
       HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, 0, EPI_QKV, g, b, R, nout, st); }), "qkv GEMM");
@@ -666,7 +690,8 @@ std::string call_key(int kind, const Problem& p, const sg_weights* w, int Lst, i
   if (w) {
     put(k, w->D); put(k, w->H); put(k, w->n_enc);
     for (int i = 0; i < w->n_enc; ++i) put(k, w->enc[i]);
-    put(k, w->L_max); put(k, w->dtype); put(k, w->head); put(k, w->cross); put(k, w->blob); put(k, w->blob_bytes);
+    put(k, w->L_max); put(k, w->dtype); put(k, w->head); put(k, w->cross); put(k, w->rope);
+    put(k, w->blob); put(k, w->blob_bytes);
   }
   put(k, Lst); put(k, T); put(k, out);
   put(k, o ? o->match_threshold : 0.f);
@@ -699,6 +724,7 @@ sg_status enqueue_full(const Problem& p, const Plan& pl, const WsLayout& wl, cha
   const float* alpha_dev = at<float>(w, L, L.alpha);
   tm.stage(SG_EV_START);
   if ((s = run_encoder(p, pl, w, L, ws, wl, tm, st)) != SG_OK) return s;
+  if (w->rope && (s = run_rope_table(p, pl, w, L, ws, wl, st)) != SG_OK) return s;
   tm.stage(SG_EV_ENCODED);
   if ((s = run_gnn(pl, w, L, 0, 2 * Lst, ws, wl, o ? o->flags : 0, tm, st)) != SG_OK) return s;
   tm.stage(SG_EV_GNN);
@@ -892,8 +918,8 @@ sg_status sg_stage_encode(const float* kpts, const float* conf, const float* des
   return SG_OK;
 }
 
-sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weights* weights, int32_t s0,
-                       int32_t s1, const sg_opts* opts) {
+sg_status sg_stage_gnn_pos(float* xA, const float* posA, int32_t M, float* xB, const float* posB, int32_t N,
+                           const sg_weights* weights, int32_t s0, int32_t s1, const sg_opts* opts) {
   g_err.clear();
   WLayout WL;
   sg_status s = check_weights(weights, &WL);
@@ -902,9 +928,13 @@ sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weig
   if (M < 0 || N < 0 || M > 4096 || N > 4096) return fail(SG_ERR_INVALID_ARG, "counts outside [0, 4096]");
   if (s0 < 0 || s1 < s0 || s1 > 2 * weights->L_max) return fail(SG_ERR_INVALID_ARG, "stage range [%d, %d) invalid", s0, s1);
   if ((M && !xA) || (N && !xB)) return fail(SG_ERR_INVALID_ARG, "NULL state pointer");
+  if (weights->rope && ((M && !posA) || (N && !posB)))
+    return fail(SG_ERR_INVALID_ARG, "rotary self-attention needs the point positions");
   Problem p;
   p.flags = opts ? opts->flags : 0;
   p.B = 1; p.Mpad = M; p.Npad = N; p.M = {M}; p.N = {N};
+  p.kp[0] = posA; p.kp[1] = posB;
+  if (opts) memcpy(p.img, opts->image_size, sizeof(p.img));
   Plan pl;
   make_plan(p, pl);
   WsLayout wl = ws_layout(weights, pl.R, 0, 0, 0, 0, 0, 0, 0);
@@ -920,12 +950,18 @@ sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weig
   HIPCHK(launch_fill_f32(X + (size_t)M * weights->D, 0.f, (pl.seg.row0[1] - M) * weights->D, st), "zero padding A");
   HIPCHK(launch_fill_f32(X + (size_t)(pl.seg.row0[1] + N) * weights->D, 0.f, (pl.R - pl.seg.row0[1] - N) * weights->D, st),
          "zero padding B");
+  if (weights->rope && (s = run_rope_table(p, pl, weights, WL, ws, wl, st)) != SG_OK) return s;
   Timer tm{opts, st};
   if ((s = run_gnn(pl, weights, WL, s0, s1, ws, wl, opts ? opts->flags : 0, tm, st)) != SG_OK) return s;
   if (M) HIPCHK(hipMemcpyAsync(xA, X, M * rb, hipMemcpyDeviceToDevice, st), "copy xA back");
   if (N) HIPCHK(hipMemcpyAsync(xB, X + (size_t)pl.seg.row0[1] * weights->D, N * rb, hipMemcpyDeviceToDevice, st), "copy xB back");
   tm.finish();
   return SG_OK;
+}
+
+sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weights* weights, int32_t s0,
+                       int32_t s1, const sg_opts* opts) {
+  return sg_stage_gnn_pos(xA, nullptr, M, xB, nullptr, N, weights, s0, s1, opts);
 }
 
 sg_status sg_stage_project(const float* x, int32_t n, const sg_weights* weights, float* f_out, const sg_opts* opts) {

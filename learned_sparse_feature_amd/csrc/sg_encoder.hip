@@ -114,6 +114,46 @@ __global__ __launch_bounds__(256) void k_encoder(EncArgs e, SegTable seg) {
   }
 }
 
+// Rotary table of self-attention (section 2.2 of the LightGlue review):
+// for every compact row, (cos, sin) of theta_k = <b_k, p> for k < d_h / 2,
+// with p the point's position normalised as for the encoder; padding rows
+// get angle 0.  Computed once per call and read by every self stage's QKV
+// epilogue.
+__global__ __launch_bounds__(256) void k_rope_table(EncArgs e, SegTable seg, const float* __restrict__ basis,
+                                                    int hp, int R, float2* __restrict__ table) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= R * hp) return;
+  const int r = idx / hp, k = idx % hp;
+  // the image of row r: the last segment starting at or before it
+  int s = 0;
+  while (s + 1 < seg.n_seg && seg.row0[s + 1] <= r) ++s;
+  const int p = r - seg.row0[s];
+  float th = 0.f;
+  if (p < seg.n[s]) {
+    const bool isA = seg.side[s] == 0;
+    const float* kp = e.kpts[isA ? 0 : 1] + 2 * (size_t)(seg.in_off[s] + p);
+    const float iw = e.img[isA ? 0 : 2], ih = e.img[isA ? 1 : 3];
+    float x = kp[0], y = kp[1];
+    if (iw > 0.f) {
+      const float sc = 0.7f * fmaxf(iw, ih);
+      x = (x - 0.5f * iw) / sc;
+      y = (y - 0.5f * ih) / sc;
+    }
+    th = fmaf(basis[2 * k], x, basis[2 * k + 1] * y);
+  }
+  float sn, cs;
+  sincosf(th, &sn, &cs);
+  table[idx] = make_float2(cs, sn);
+}
+
+hipError_t launch_rope_table(const EncArgs& e, const SegTable& seg, const float* basis, int dh, int R,
+                             float2* table, hipStream_t st) {
+  const int hp = dh / 2;
+  if (R <= 0 || hp <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_table, dim3((R * hp + 255) / 256), dim3(256), 0, st, e, seg, basis, hp, R, table);
+  return hipGetLastError();
+}
+
 hipError_t launch_encoder(int op, int wd, const EncArgs& e, const SegTable& seg, hipStream_t st) {
   int tiles = 0;
   for (int s = 0; s < seg.n_seg; ++s) tiles += (seg.n[s] + 31) / 32;

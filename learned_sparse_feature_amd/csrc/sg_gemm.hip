@@ -177,6 +177,36 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
     }
   }
 
+  if constexpr (EPI == EPI_QKV) {
+    // The bias is added to the accumulators here, once.  Self stages with a
+    // rotary table then rotate every channel pair (2c, 2c+1) of q and k
+    // (columns [0, 2D)) by the row's angle c mod d_h / 2: the pair's other
+    // column sits in the neighbouring lane (same row), one DPP swap away.
+    const int Dq = g.tied ? g.split : g.split / 2;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int rr0 = r0 + wm * (BM / 2) + i * 32, nn0 = n0 + wn * (BN / 2) + j * 32;
+        if (rr0 >= P.rows || nn0 >= P.n_out) continue;
+        const int n = nn0 + (lane & 31);
+        const float bias = g.bias ? (float)reinterpret_cast<const WT*>(g.bias)[n] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] += bias;
+        if (g.rope && nn0 < 2 * Dq) {
+          const int hp = g.rope_dh / 2, kc = (n % g.rope_dh) >> 1;
+          const float sg = (n & 1) ? 1.f : -1.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = rr0 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const float2 cs = g.rope[(size_t)r * hp + kc];
+            const float other = dpp_f<kDppXor1>(acc[i][j][e]);
+            acc[i][j][e] = fmaf(sg * other, cs.y, acc[i][j][e] * cs.x);
+          }
+        }
+      }
+  }
+
   if constexpr (EPI == EPI_QKV && BF) {
     // bf16 q | k | v, per 32x32 block: q row-major into C; k through a
     // wave-private LDS transposition into the tile-swizzled C3; v straight
@@ -200,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
       for (int j = 0; j < NB; ++j) {
         const int rr0 = r0 + wm * (BM / 2) + i * 32, nn0 = n0 + wn * (BN / 2) + j * 32;
         if (rr0 >= P.rows || nn0 >= P.n_out) continue;
-        const float bias = g.bias ? (float)reinterpret_cast<const WT*>(g.bias)[nn0 + nl] : 0.f;
+        const float bias = 0.f;  // added to the accumulators above
         const int tile = rr0 >> 5;
         if (nn0 < Dm) {
 #pragma unroll
@@ -253,8 +283,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const int nl = lane & 31;
-          const int nn = n0 + wn * (BN / 2) + j * 32 + nl;
-          const float bias = g.bias && nn < P.n_out ? (float)reinterpret_cast<const WT*>(g.bias)[nn] : 0.f;
+          const float bias = 0.f;  // added to the accumulators above
           __syncthreads();
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
@@ -283,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
     const int n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
     if (n >= P.n_out) continue;
     float bias = 0.f;
-    if (EPI != EPI_SCORE && g.bias) bias = (float)reinterpret_cast<const WT*>(g.bias)[n];
+    if (EPI != EPI_SCORE && EPI != EPI_QKV && g.bias) bias = (float)reinterpret_cast<const WT*>(g.bias)[n];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll

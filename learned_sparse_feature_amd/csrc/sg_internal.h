@@ -72,6 +72,8 @@ struct GemmArgs {
   float scale;
   int split;                         // EPI_QKV: first column that goes to VT (VS)
   int tied;                          // EPI_QKV: columns [0, split) are both q and k
+  const float2* rope;                // EPI_QKV: per-row (cos, sin) of the rotary angles, [rows][rope_dh/2], or null
+  int rope_dh;                       // head dimension of the rotary table
   int gx, gy;                        // row and column tiles (set by the launcher)
 };
 
@@ -112,6 +114,10 @@ struct AttnArgs {
 // Host-side launchers (sg_kernels.hip).
 hipError_t launch_encoder(int op_dtype, int w_dtype, const EncArgs& e, const SegTable& seg,
                           hipStream_t st);
+// (cos, sin) of the rotary angles of every compact row ([R][dh/2]) from the
+// positions in e.kpts / e.img (normalised as for the encoder).
+hipError_t launch_rope_table(const EncArgs& e, const SegTable& seg, const float* basis, int dh, int R,
+                             float2* table, hipStream_t st);
 hipError_t launch_gemm(int op_dtype, int a0_is_f32, int w_dtype, int out_is_f32, int epi,
                        const GemmArgs& g, const GemmBatch& b, int max_rows, int max_n,
                        hipStream_t st);

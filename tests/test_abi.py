@@ -175,3 +175,24 @@ def test_bidirectional_cross_layout_and_validation():
     bad = _cfg()
     bad.cross = 2
     assert lib.sg_weights_count(C.byref(bad)) == -1
+
+
+def test_rope_layout_and_validation():
+    """Rotary weights append one fp32 [d_h/2][2] basis; the GNN stage entry
+    point refuses them without positions (host validation, before any HIP
+    call)."""
+    lib = _lib.load()
+    w, wr = _cfg(), _cfg()
+    wr.rope = 1
+    n = lib.sg_weights_count(C.byref(w))
+    assert lib.sg_weights_count(C.byref(wr)) == n + 1
+    off, r, c = C.c_size_t(), C.c_int32(), C.c_int32()
+    assert lib.sg_weights_tensor(C.byref(wr), n, C.byref(off), C.byref(r), C.byref(c)) == 0
+    assert (r.value, c.value) == (32, 2)
+    bad = _cfg()
+    bad.rope = 3
+    assert lib.sg_weights_count(C.byref(bad)) == -1
+    fake = C.c_void_p(0x1000)
+    wr.blob, wr.blob_bytes = fake, 1 << 30
+    assert lib.sg_stage_gnn(fake, 4, fake, 4, C.byref(wr), 0, 2, None) == _lib.SG_ERR_INVALID_ARG
+    assert "positions" in lib.sg_last_error().decode()
