@@ -52,6 +52,7 @@ __all__ = [
     "bidirectional_cross_attention", "rope_angles", "rotate_pairs",
     "log_sigmoid", "matchability", "double_softmax_assignment",
     "double_softmax_from_descriptors", "double_softmax_match",
+    "confidence_threshold", "token_confidence", "layer_head", "adaptive_match",
 ]
 
 
@@ -419,4 +420,109 @@ def double_softmax_match(pair, weights, L=None, threshold=0.0):
     out = superglue_descriptors(pair, weights, L)
     out.update(double_softmax_from_descriptors(out["f0"], out["f1"], out["xL_0"], out["xL_1"],
                                                weights["wz"], weights["bz"], threshold))
+    return out
+
+
+# ------------------------------------------------ adaptive depth and width
+# [LightGlue-review] sections 2.6 (adaptive depth) and 2.7 (adaptive width).
+# A "layer" is one self stage followed by one cross stage.
+
+
+def confidence_threshold(layer, n_layers):
+    """[LightGlue-review] section 2.6: the per-layer confidence threshold
+    lambda_l = 0.8 + 0.1 exp(-4 l / L), clipped to [0, 1]."""
+    return float(np.clip(0.8 + 0.1 * np.exp(-4.0 * layer / n_layers), 0.0, 1.0))
+
+
+def token_confidence(x, wc, bc):
+    """[LightGlue-review] section 2.5: a linear layer plus sigmoid on a point's
+    current state: c_i = sigmoid(<w, x_i> + b)."""
+    return np.exp(log_sigmoid(_f64(x) @ _f64(wc).reshape(-1) + float(bc)))
+
+
+def layer_head(weights, layer):
+    """The matching head of layer `layer`: its own (W_f, b_f, w_z, b_z) for
+    every layer but the network's last stored one, which uses the main head
+    ([LightGlue-review] section 2.5: every layer has a head)."""
+    heads = weights.get("heads") or []
+    if layer < len(heads):
+        return heads[layer]
+    return weights["Wf"], weights["bf"], weights["wz"], weights["bz"]
+
+
+def adaptive_match(pair, weights, L=None, depth_confidence=0.95, width_confidence=0.99,
+                   prune_min=1024, early_exit=True, prune=True, threshold=0.0):
+    """[LightGlue-review] sections 2.6 and 2.7 with the double-softmax head
+    of section 2.4, for one pair.
+
+    Layer l runs stages 2l (self) and 2l+1 (cross) on the points that remain.
+    After every layer but the last: if early_exit, each point's confidence
+    c = token_confidence(x, weights["conf"][l]) and lambda_l; the pass stops
+    when 1 - (number of remaining points with c < lambda_l) / (M + N) exceeds
+    depth_confidence (M, N the original counts).  Otherwise, if prune, an
+    image with more than prune_min remaining points keeps the points whose
+    matchability sigmoid(z) (the layer's own head) exceeds 1 -
+    width_confidence, or whose confidence is at most lambda_l (when
+    early_exit computes it).  An image left without points ends the pass.
+    The head of the last layer run gives the log assignment of the
+    remaining points; matches map back to the original indices and pruned
+    points get -1 / 0.  Also returns "exit_layer" and "prune0"/"prune1"
+    (1 + the number of pruning steps each point survived)."""
+    L = weights["L"] if L is None else L
+    H = weights["H"]
+    M, N = len(pair["kpts0"]), len(pair["kpts1"])
+    out = {"matches0": -np.ones(M, np.int32), "scores0": np.zeros(M),
+           "matches1": -np.ones(N, np.int32), "scores1": np.zeros(N),
+           "prune0": np.ones(M, np.int32), "prune1": np.ones(N, np.int32), "exit_layer": -1}
+    if M == 0 or N == 0:
+        return out
+    xs, pos = [], []
+    for side in ("0", "1"):
+        w, h = pair["image_size" + side]
+        kn = normalize_keypoints(pair["kpts" + side], w, h)
+        pos.append(kn)
+        xs.append(_f64(pair["desc" + side]) + keypoint_encoder(kn, pair["conf" + side], weights["enc"]))
+    ind = [np.arange(M), np.arange(N)]
+    basis = weights.get("rope_basis")
+    layer = 0
+    for layer in range(L):
+        rope = None
+        if basis is not None:
+            rope = (rope_angles(pos[0][ind[0]], basis), rope_angles(pos[1][ind[1]], basis))
+        xs[0], xs[1] = attentional_gnn(xs[0], xs[1], weights["stages"][2 * layer:2 * layer + 2], H,
+                                       first_stage=2 * layer, rope=rope)
+        if layer == L - 1:
+            break
+        lam = confidence_threshold(layer, L)
+        conf = None
+        if early_exit:
+            wc, bc = weights["conf"][layer]
+            conf = [token_confidence(x, wc, bc) for x in xs]
+            unconfident = sum(int((c < lam).sum()) for c in conf)
+            if 1.0 - unconfident / (M + N) > depth_confidence:
+                break
+        if prune:
+            _, _, wz, bz = layer_head(weights, layer)
+            for k in (0, 1):
+                if len(ind[k]) <= prune_min:
+                    continue
+                keep = np.exp(log_sigmoid(matchability(xs[k], wz, bz))) > 1.0 - width_confidence
+                if conf is not None:
+                    keep |= conf[k] <= lam
+                xs[k], ind[k] = xs[k][keep], ind[k][keep]
+                out["prune%d" % k][ind[k]] += 1
+        if len(ind[0]) == 0 or len(ind[1]) == 0:
+            break
+    out["exit_layer"] = layer
+    if len(ind[0]) == 0 or len(ind[1]) == 0:
+        return out
+    Wf, bf, wz, bz = layer_head(weights, layer)
+    f0, f1 = final_projection(xs[0], Wf, bf), final_projection(xs[1], Wf, bf)
+    r = double_softmax_from_descriptors(f0, f1, xs[0], xs[1], wz, bz, threshold)
+    i0, i1 = ind
+    out["matches0"][i0] = np.where(r["matches0"] >= 0, i1[np.maximum(r["matches0"], 0)], -1)
+    out["scores0"][i0] = r["scores0"]
+    out["matches1"][i1] = np.where(r["matches1"] >= 0, i0[np.maximum(r["matches1"], 0)], -1)
+    out["scores1"][i1] = r["scores1"]
+    out.update({"kept0": i0, "kept1": i1, "logP": r["logP"], "f0": f0, "f1": f1})
     return out

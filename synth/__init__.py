@@ -86,7 +86,7 @@ def _bias(rng: np.random.Generator, n_out: int, n_in: int, bias_on: bool, zero: 
 
 def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
                  L: Optional[int] = None, alpha: float = 1.0, cross: str = "standard",
-                 rope: bool = False) -> dict:
+                 rope: bool = False, adaptive: bool = False) -> dict:
     """Draw the network weights of `cfg` (row-major [out][in] matrices).
 
     Every matrix is Xavier-uniform U(+-sqrt(6/(fan_in+fan_out))).  Biases are
@@ -99,6 +99,8 @@ def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
     cross="bidirectional": every cross stage draws one shared query/key
     projection ("Wqk", "bqk") and "Wv", "bv" instead of q, k, v.
     rope=True: a rotary basis "rope_basis" [d_h/2][2] ~ N(0, 1) (kept fp32).
+    adaptive=True: "conf" [(w_c, b_c)] and "heads" [(W_f, b_f, w_z, b_z)] for
+    every layer but the last (adaptive depth and width).
     """
     if seed is None:
         seed = (BIAS_ON_SEED_BASE if bias_on else WEIGHT_SEED_BASE) + cfg.cid
@@ -131,15 +133,27 @@ def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
     bz = _bias(rng, 1, D, bias_on, zero=False)[0]
     # rotary basis of self-attention ([d_h/2][2], N(0, 1)), drawn last
     basis = rng.standard_normal((D // cfg.H // 2, 2)).astype(np.float32) if rope else None
+    # adaptive depth / width: per layer but the last, a confidence Linear(D, 1)
+    # and a matching head (W_f, b_f, w_z, b_z), drawn last
+    conf, heads = [], []
+    if adaptive:
+        for _ in range(L - 1):
+            conf.append((_xavier(rng, 1, D)[0], float(_bias(rng, 1, D, bias_on, zero=False)[0])))
+            heads.append((_xavier(rng, D, D), _bias(rng, D, D, bias_on, zero=False),
+                          _xavier(rng, 1, D)[0], float(_bias(rng, 1, D, bias_on, zero=False)[0])))
     w = {"enc": enc, "stages": stages, "Wf": Wf, "bf": bf, "alpha": float(alpha),
          "wz": wz, "bz": float(bz), "D": D, "H": cfg.H, "L": L, "dtype": cfg.dtype, "cross": cross,
-         "rope_basis": basis}
+         "rope_basis": basis, "conf": conf if adaptive else None, "heads": heads if adaptive else None}
     if cfg.dtype == "bf16":
         w["enc"] = [(round_to_bf16(W), round_to_bf16(b)) for W, b in w["enc"]]
         w["stages"] = [{k: round_to_bf16(v) for k, v in st.items()} for st in w["stages"]]
         w["Wf"], w["bf"] = round_to_bf16(w["Wf"]), round_to_bf16(w["bf"])
         w["wz"] = round_to_bf16(w["wz"])
         w["bz"] = float(round_to_bf16(np.array([w["bz"]], np.float32))[0])
+        r1 = lambda v: float(round_to_bf16(np.array([v], np.float32))[0])
+        if adaptive:
+            w["conf"] = [(round_to_bf16(a), r1(b)) for a, b in w["conf"]]
+            w["heads"] = [(round_to_bf16(a), round_to_bf16(b), round_to_bf16(c), r1(d)) for a, b, c, d in w["heads"]]
     return w
 
 

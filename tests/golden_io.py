@@ -28,3 +28,8 @@ def sinkhorn_demo():
     S = np.array([r[1:] for r in rows if r[0] == "S"], dtype=np.float64)
     dust = float([r for r in rows if r[0] == "dust"][0][1])
     return S, dust
+
+
+def confidence_threshold_example():
+    """(layer, n_layers, threshold) rows of the page's adaptive-depth example."""
+    return [(int(a), int(b), float(c)) for a, b, c in _lines("confidence_threshold_example.txt")]
