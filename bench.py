@@ -13,7 +13,8 @@ progress goes to stderr.
 head (section 2.4 of the LightGlue review) on the same network and pair;
 --cross bidirectional gives the cross stages one shared query/key projection
 (section 2.3 of the review); --rope rotates q and k of the self stages by the
-keypoints' positions (section 2.2).
+keypoints' positions (section 2.2).  --adaptive adds the adaptive depth /
+width measurements (sections 2.6 and 2.7) beside the headline number.
 """
 from __future__ import annotations
 
@@ -116,6 +117,73 @@ def cpu_baseline(cfg, w, pair, head="sinkhorn", budget_s=12.0, max_pairs=3):
                       f"oracle, {dt:.1f} s wall"}
 
 
+def adaptive_bench(args, cfg, dev, sg, synth, np, torch):
+    """Adaptive depth and width of one pair with the double-softmax head:
+    the same pass with the confidence forced low (no exit: the per-layer
+    statistics and synchronisations are pure overhead), forced high from a
+    given layer (exit after it), and point pruning on a 2048 x 2048 pair whose
+    matchability drops about a quarter of the points after layer 0.  Adaptive
+    calls run eagerly, so the plain pass is timed eagerly too."""
+    import copy
+    keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t0) / reps
+
+    reps = max(5, min(30, args.steps // 3))
+    base = synth.make_weights(cfg, adaptive=True, cross=args.cross, rope=args.rope)
+    pair = synth.make_pair(cfg)
+    t = [torch.from_numpy(pair[k]).to(dev) for k in keys]
+    img = (*pair["image_size0"], *pair["image_size1"])
+    res = {"pair": "1024x1024, L=9"}
+
+    def with_conf(w, first_confident):
+        w = copy.deepcopy(w)
+        w["conf"] = [(0 * wc, 40.0 if l >= first_confident else -40.0) for l, (wc, _) in enumerate(w["conf"])]
+        return sg.pack_weights(w, device=dev, head="ds")
+
+    Wn = with_conf(base, cfg.L)  # never confident
+    res["plain_graph_ms"] = round(timed(lambda: sg.sg_match(*t, Wn, cfg.L, cfg.T, image_size=img), reps), 4)
+    res["plain_eager_ms"] = round(timed(lambda: sg.sg_match(*t, Wn, cfg.L, cfg.T, image_size=img, graph=False), reps), 4)
+    res["adaptive_no_exit_ms"] = round(timed(lambda: sg.sg_match(*t, Wn, cfg.L, cfg.T, image_size=img,
+                                                                  adaptive={"prune": False}), reps), 4)
+    for k in (1, 4):
+        Wk = with_conf(base, k)
+        o = sg.sg_match(*t, Wk, cfg.L, cfg.T, image_size=img, adaptive={"prune": False})
+        assert o["exit_layer"] == k, o["exit_layer"]
+        res[f"exit_after_layer_{k}_ms"] = round(timed(lambda: sg.sg_match(*t, Wk, cfg.L, cfg.T, image_size=img,
+                                                                           adaptive={"prune": False}), reps), 4)
+    # pruning: states frozen through layer 0's decision are not needed; the
+    # matchability of layer 0 reads one descriptor channel scaled so that a
+    # quarter of the points are confidently unmatchable
+    big = synth.make_pair(cfg, M=2048, N=2048, seed=77)
+    tb = [torch.from_numpy(big[k]).to(dev) for k in keys]
+    wp = copy.deepcopy(base)
+    e = np.eye(cfg.D, dtype=np.float32)
+    wp["conf"] = [(2000.0 * e[0], 0.0)] + [(0 * wc, -40.0) for wc, _ in wp["conf"][1:]]
+    wp["heads"] = [(h[0], h[1], 2000.0 * e[1] if l == 0 else 0 * h[2], 0.0 if l == 0 else 40.0)
+                   for l, h in enumerate(wp["heads"])]
+    Wp = sg.pack_weights(wp, device=dev, head="ds")
+    ws = torch.empty(sg.workspace_size(Wp, 2048, 2048, 1), dtype=torch.uint8, device=dev)
+    o = sg.sg_match(*tb, Wp, cfg.L, cfg.T, image_size=img, adaptive={}, workspace=ws)
+    kept = (int((o["prune0"] > 1).sum().item()), int((o["prune1"] > 1).sum().item()))
+    res["prune_pair"] = "2048x2048, L=9, layer 0 drops confident unmatchable points"
+    res["prune_kept_points"] = kept
+    res["prune_plain_eager_ms"] = round(timed(lambda: sg.sg_match(*tb, Wp, cfg.L, cfg.T, image_size=img,
+                                                                   graph=False, workspace=ws), reps), 4)
+    res["prune_adaptive_ms"] = round(timed(lambda: sg.sg_match(*tb, Wp, cfg.L, cfg.T, image_size=img,
+                                                                adaptive={}, workspace=ws), reps), 4)
+    log(f"adaptive: {res}")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +200,8 @@ def main():
     ap.add_argument("--cross", choices=["standard", "bidirectional"], default="standard",
                     help="cross-attention of the odd stages")
     ap.add_argument("--rope", action="store_true", help="rotary position encoding in self-attention")
+    ap.add_argument("--adaptive", action="store_true",
+                    help="also time adaptive depth / width (forced exits and pruning) with the double-softmax head")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="before the steps, copy this many MiB with a plain device copy (counter scaling)")
     args = ap.parse_args()
@@ -329,6 +399,8 @@ def main():
                  "pairs_per_s": round(nb * Bn / dtb, 2)}
         log(f"batch: {batch}")
 
+    adaptive = adaptive_bench(args, cfg, dev, sg, synth, np, torch) if args.adaptive else None
+
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
@@ -350,6 +422,7 @@ def main():
                    "head": args.head, "cross_attention": args.cross, "rope": args.rope},
         "roofline": roofline, "cpu_baseline": cpu, "stages_ms": stages, "kernels": kernels,
         "batch_throughput": batch,
+        "adaptive": adaptive,
         "baseline_context": {"pages_ms_per_pair": {"GTX1080_1024kp": 87.0, "unstated_hw_2048kp": 70.0},
                              "pages_pairs_per_s": {"GTX1080_1024kp": 11.5, "unstated_hw_aachen_4096kp": 6.5}},
     }

@@ -92,6 +92,23 @@ typedef enum { SG_CROSS_STANDARD = 0, SG_CROSS_BIDIRECTIONAL = 1 } sg_cross;
  * the blob.  Every head and every self stage uses the same angles; the
  * (cos, sin) table is computed once per call. */
 
+/* Adaptive depth and width (sg_weights.adaptive = 1, double-softmax head
+ * only), after sections 2.6 and 2.7 of the LightGlue review.  A layer is one
+ * self stage and one cross stage.  After every layer l but the last, each
+ * remaining point gets a confidence c = sigmoid(<w_c,l, x> + b_c,l) and the
+ * threshold is lambda_l = 0.8 + 0.1 exp(-4 l / L).  With SG_FLAG_EARLY_EXIT
+ * the pass stops when 1 - (remaining points with c < lambda_l) / (M + N)
+ * exceeds opts->depth_confidence.  Otherwise, with SG_FLAG_PRUNE, an image
+ * with more than opts->prune_min_points remaining points drops the points
+ * whose matchability sigmoid(<w_z,l, x> + b_z,l) (layer l's head) is at most
+ * 1 - opts->width_confidence, unless (with SG_FLAG_EARLY_EXIT) their
+ * confidence is at most lambda_l; an image left without points ends the
+ * pass.  The head of the last layer run (W_f,l, w_z,l; the main head for
+ * layer L_max - 1) matches the remaining points; pruned points get -1 / 0.
+ * Adaptive calls exist for sg_match only.  They read a few counters back
+ * after every layer (one stream synchronisation per layer), always run
+ * eagerly (never captured into a graph) and are refused on a stream that the
+ * caller is capturing. */
 #define SG_MAX_ENC 8     /* hidden layers of the keypoint encoder          */
 #define SG_MAX_BATCH 64  /* pairs per sg_match_batch call                  */
 
@@ -122,6 +139,9 @@ typedef enum { SG_CROSS_STANDARD = 0, SG_CROSS_BIDIRECTIONAL = 1 } sg_cross;
  *   w_z [1][D], b_z [1]            (matchability Linear(D, 1))
  *   rope = 1 only:
  *   B_rot [D/H/2][2]               (rotary basis, always fp32)
+ *   adaptive = 1 only, for each layer l = 0..L_max-2:
+ *     w_c [1][D], b_c [1]          (token confidence Linear(D, 1))
+ *     W_f [D][D], b_f [D], w_z [1][D], b_z [1]   (layer l's matching head)
  * Head h owns channels [h*D/H, (h+1)*D/H) of q, k, v and of the merge input.
  */
 typedef struct {
@@ -133,6 +153,7 @@ typedef struct {
   int32_t head;        /* sg_head */
   int32_t cross;       /* sg_cross */
   int32_t rope;        /* 1: rotary encoding in self-attention */
+  int32_t adaptive;    /* 1: per-layer confidence and heads (adaptive depth / width) */
   const void* blob;    /* device pointer, caller-owned */
   size_t blob_bytes;
 } sg_weights;
@@ -173,6 +194,14 @@ typedef struct {
   int32_t n_kernel_events;     /* capacity; launches beyond it are not bracketed */
   int32_t* n_kernel_launches;  /* host: receives the number of bracketed launches */
   int32_t flags;               /* SG_FLAG_* */
+  /* adaptive calls (SG_FLAG_EARLY_EXIT / SG_FLAG_PRUNE with adaptive weights):
+     0 selects the default in brackets */
+  float depth_confidence;      /* stop when the confident share exceeds it [0.95] */
+  float width_confidence;      /* prune points with matchability <= 1 - it [0.99] */
+  int32_t prune_min_points;    /* prune only images with more points [1024] */
+  int32_t* out_exit_layer;     /* host, optional: the layer whose head matched */
+  int32_t* out_prune0;         /* optional [M]: 1 + pruning steps each point of A survived */
+  int32_t* out_prune1;         /* optional [N] */
 } sg_opts;
 
 /* sg_opts.flags: run eagerly instead of replaying the captured HIP graph. */
@@ -189,6 +218,12 @@ typedef struct {
 #define SG_FLAG_SINKHORN_TWO_SWEEP 2
 #define SG_FLAG_SINKHORN_ONE_SWEEP 4
 #define SG_TWO_SWEEP_MAX_BYTES (48u << 20)
+/* sg_opts.flags: adaptive depth and width (see sg_weights.adaptive).  In an
+ * adaptive call out_logP, out_desc_A and out_desc_B hold the exit layer's
+ * values for the remaining points, in the original order; the rows and
+ * columns of pruned points are left untouched. */
+#define SG_FLAG_EARLY_EXIT 8
+#define SG_FLAG_PRUNE 16
 
 /* Number of tensors in the blob (the alpha scalar counts as one). */
 int32_t sg_weights_count(const sg_weights* w);

@@ -37,7 +37,8 @@ _CROSS = {"standard": SG_CROSS_STANDARD, "bidirectional": SG_CROSS_BIDIRECTIONAL
 
 
 def weights_config(D: int, H: int, enc: Sequence[int], L_max: int, dtype: str = "f32",
-                   head: str = "sinkhorn", cross: str = "standard", rope: bool = False) -> SgWeights:
+                   head: str = "sinkhorn", cross: str = "standard", rope: bool = False,
+                   adaptive: bool = False) -> SgWeights:
     """head: "sinkhorn" (optimal transport) or "ds" (double softmax + matchability);
     cross: "standard" or "bidirectional" cross-attention; rope: rotary encoding
     in self-attention."""
@@ -46,6 +47,7 @@ def weights_config(D: int, H: int, enc: Sequence[int], L_max: int, dtype: str = 
     st.head = _HEADS[head]
     st.cross = _CROSS[cross]
     st.rope = 1 if rope else 0
+    st.adaptive = 1 if adaptive else 0
     for i, e in enumerate(enc):
         st.enc[i] = e
     return st
@@ -89,6 +91,10 @@ def _ordered_tensors(w: dict, head: str):
         out += [np.asarray(w["wz"]).reshape(1, -1), np.array([w["bz"]], dtype=np.float32)]
     if w.get("rope_basis") is not None:
         out.append(np.asarray(w["rope_basis"]))
+    if head == "ds" and w.get("conf"):
+        for (wc, bc), (Wf, bf, wz, bz) in zip(w["conf"], w["heads"]):
+            out += [np.asarray(wc).reshape(1, -1), np.array([bc], np.float32), Wf, bf,
+                    np.asarray(wz).reshape(1, -1), np.array([bz], np.float32)]
     return out
 
 
@@ -99,7 +105,8 @@ def pack_weights(w: dict, device="cuda", head: str = "sinkhorn") -> Weights:
     enc = [W.shape[0] for W, _ in w["enc"][:-1]]
     L_max = len(w["stages"]) // 2
     rope = w.get("rope_basis") is not None
-    st = weights_config(w["D"], w["H"], enc, L_max, w["dtype"], head, w.get("cross", "standard"), rope)
+    adaptive = head == "ds" and bool(w.get("conf"))
+    st = weights_config(w["D"], w["H"], enc, L_max, w["dtype"], head, w.get("cross", "standard"), rope, adaptive)
     L = lib()
     nbytes = L.sg_weights_bytes(C.byref(st))
     count = L.sg_weights_count(C.byref(st))
@@ -107,8 +114,9 @@ def pack_weights(w: dict, device="cuda", head: str = "sinkhorn") -> Weights:
         raise SgError(-1, "sg_weights_bytes")
     tensors = _ordered_tensors(w, head)
     # alpha and the rotary basis are always float32
-    alpha_index = count - (3 if head == "ds" else 1) - (1 if rope else 0)
-    f32_index = {alpha_index, count - 1} if rope else {alpha_index}
+    n_adapt = 6 * (L_max - 1) if adaptive else 0
+    alpha_index = count - n_adapt - (3 if head == "ds" else 1) - (1 if rope else 0)
+    f32_index = {alpha_index, alpha_index + (3 if head == "ds" else 1)} if rope else {alpha_index}
     if len(tensors) != count:
         raise ValueError(f"weight dictionary has {len(tensors)} tensors, the layout {count}")
     host = torch.zeros(nbytes, dtype=torch.uint8)
@@ -183,9 +191,15 @@ def _transposed_extra(sinkhorn, B, M, N):
 
 def _opts(device, *, threshold=0.0, image_size=None, workspace=None, ws_bytes=0, m1=None, s1=None,
           fA=None, fB=None, logP=None, logP_ld=0, stage_events=None, timed_kernel=SG_K_NONE,
-          kernel_events=None, stream=None, graph=True, sinkhorn="auto"):
+          kernel_events=None, stream=None, graph=True, sinkhorn="auto", adaptive=None):
     o = SgOpts()
     o.flags = (0 if graph else _lib.SG_FLAG_NO_GRAPH) | _SINKHORN_FLAGS[sinkhorn]
+    if adaptive is not None:
+        o.flags |= (_lib.SG_FLAG_EARLY_EXIT if adaptive.get("early_exit", True) else 0)
+        o.flags |= (_lib.SG_FLAG_PRUNE if adaptive.get("prune", True) else 0)
+        o.depth_confidence = float(adaptive.get("depth_confidence", 0.0))
+        o.width_confidence = float(adaptive.get("width_confidence", 0.0))
+        o.prune_min_points = int(adaptive.get("prune_min", 0))
     s = stream if stream is not None else torch.cuda.current_stream(device)
     o.stream = s.cuda_stream
     if workspace is not None:
@@ -221,11 +235,14 @@ def sg_match(kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int,
              threshold: float = 0.0, image_size=None, want_matches1=True, want_logP=False,
              want_desc=False, workspace=None, stage_events=None, timed_kernel=SG_K_NONE,
              kernel_events=None, stream=None, graph=True, out: Optional[dict] = None,
-             sinkhorn: str = "auto") -> dict:
+             sinkhorn: str = "auto", adaptive: Optional[dict] = None) -> dict:
     """One pair.  kpts [n][2] (pixels if image_size=(wA, hA, wB, hB) is given),
     desc [n][D], conf [n]: float32 CUDA tensors.  Returns device tensors;
     `out` may supply them (same keys) so that repeated calls reuse buffers.
-    sinkhorn: "auto", or "two" / "one" to force a Sinkhorn schedule."""
+    sinkhorn: "auto", or "two" / "one" to force a Sinkhorn schedule.
+    adaptive (adaptive weights only): {"early_exit": bool, "prune": bool,
+    "depth_confidence": a, "width_confidence": b, "prune_min": n} (0 = the
+    library's default); adds "exit_layer", "prune0", "prune1" to the result."""
     dev = descA.device
     M, N, D = kptsA.shape[0], kptsB.shape[0], weights.D
     for t, nm, shp in ((kptsA, "kptsA", (M, 2)), (descA, "descA", (M, D)), (confA, "confA", (M,)),
@@ -256,11 +273,20 @@ def sg_match(kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int,
                            m1=out.get("matches1"), s1=out.get("scores1"), fA=out.get("f0"),
                            fB=out.get("f1"), logP=out.get("logP"), logP_ld=N + 1,
                            stage_events=stage_events, timed_kernel=timed_kernel,
-                           kernel_events=kernel_events, stream=stream, graph=graph, sinkhorn=sinkhorn)
+                           kernel_events=kernel_events, stream=stream, graph=graph, sinkhorn=sinkhorn,
+                           adaptive=adaptive)
+    exit_layer = C.c_int32(-1)
+    if adaptive is not None:
+        out["prune0"] = torch.empty(M, dtype=torch.int32, device=dev)
+        out["prune1"] = torch.empty(N, dtype=torch.int32, device=dev)
+        o.out_prune0, o.out_prune1 = out["prune0"].data_ptr(), out["prune1"].data_ptr()
+        o.out_exit_layer = C.pointer(exit_layer)
     st = lib().sg_match(_ptr(kptsA), _ptr(descA), _ptr(confA), M, _ptr(kptsB), _ptr(descB), _ptr(confB), N,
                         weights.ref, L, T, _ptr(out["matches0"]), _ptr(out["scores0"]), C.byref(o))
     _lib.check(st, "sg_match")
     out["n_kernel_launches"] = count.value
+    if adaptive is not None:
+        out["exit_layer"] = exit_layer.value
     return out
 
 

@@ -18,6 +18,8 @@ SG_K_NONE, SG_K_GEMM, SG_K_ATTENTION, SG_K_SINKHORN = 0, 1, 2, 3
 SG_FLAG_NO_GRAPH = 1
 SG_FLAG_SINKHORN_TWO_SWEEP = 2
 SG_FLAG_SINKHORN_ONE_SWEEP = 4
+SG_FLAG_EARLY_EXIT = 8
+SG_FLAG_PRUNE = 16
 
 STATUS_NAMES = {0: "SG_OK", -1: "SG_ERR_INVALID_ARG", -2: "SG_ERR_UNSUPPORTED", -3: "SG_ERR_WEIGHTS",
                 -4: "SG_ERR_WORKSPACE", -5: "SG_ERR_HIP"}
@@ -26,7 +28,7 @@ STATUS_NAMES = {0: "SG_OK", -1: "SG_ERR_INVALID_ARG", -2: "SG_ERR_UNSUPPORTED", 
 class SgWeights(C.Structure):
     _fields_ = [("D", C.c_int32), ("H", C.c_int32), ("n_enc", C.c_int32),
                 ("enc", C.c_int32 * SG_MAX_ENC), ("L_max", C.c_int32), ("dtype", C.c_int32),
-                ("head", C.c_int32), ("cross", C.c_int32), ("rope", C.c_int32),
+                ("head", C.c_int32), ("cross", C.c_int32), ("rope", C.c_int32), ("adaptive", C.c_int32),
                 ("blob", C.c_void_p), ("blob_bytes", C.c_size_t)]
 
 
@@ -39,7 +41,9 @@ class SgOpts(C.Structure):
                 ("stage_events", C.c_void_p), ("n_stage_events", C.c_int32),
                 ("timed_kernel", C.c_int32), ("kernel_events", C.c_void_p),
                 ("n_kernel_events", C.c_int32), ("n_kernel_launches", C.POINTER(C.c_int32)),
-                ("flags", C.c_int32)]
+                ("flags", C.c_int32), ("depth_confidence", C.c_float), ("width_confidence", C.c_float),
+                ("prune_min_points", C.c_int32), ("out_exit_layer", C.POINTER(C.c_int32)),
+                ("out_prune0", C.c_void_p), ("out_prune1", C.c_void_p)]
 
 
 _P = C.c_void_p

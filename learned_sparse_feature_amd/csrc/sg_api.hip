@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <mutex>
 #include <string>
@@ -51,7 +52,10 @@ struct WLayout {
   int alpha = 0;        // index of alpha
   int wz = -1;          // index of the matchability weight (double-softmax head)
   int rope = -1;        // index of the rotary basis
+  int adapt = -1;       // index of layer 0's confidence weight (6 tensors per layer)
 };
+
+constexpr int kPerLayerAdaptive = 6;  // w_c, b_c, W_f, b_f, w_z, b_z
 
 constexpr int kPerStage = 8;  // W_qkv, b_qkv, W_m, b_m, W_1, b_1, W_2, b_2
 
@@ -70,6 +74,10 @@ sg_status check_config(const sg_weights* w) {
   if (w->cross != SG_CROSS_STANDARD && w->cross != SG_CROSS_BIDIRECTIONAL)
     return fail(SG_ERR_INVALID_ARG, "unknown cross-attention variant %d", w->cross);
   if (w->rope != 0 && w->rope != 1) return fail(SG_ERR_INVALID_ARG, "rope must be 0 or 1 (got %d)", w->rope);
+  if (w->adaptive != 0 && w->adaptive != 1)
+    return fail(SG_ERR_INVALID_ARG, "adaptive must be 0 or 1 (got %d)", w->adaptive);
+  if (w->adaptive && w->head != SG_HEAD_DOUBLE_SOFTMAX)
+    return fail(SG_ERR_INVALID_ARG, "adaptive depth / width needs the double-softmax head");
   const int dh = w->D / w->H;
   if (dh != 16 && dh != 64) return fail(SG_ERR_UNSUPPORTED, "head dimension %d (supported: 16, 64)", dh);
   if (w->D % 32 || w->D > 1024) return fail(SG_ERR_UNSUPPORTED, "D = %d (supported: multiples of 32 up to 1024)", w->D);
@@ -121,6 +129,14 @@ WLayout layout_of(const sg_weights* w) {
     L.rope = (int)L.t.size();
     add(D / w->H / 2, 2, 4);  // always fp32
   }
+  if (w->adaptive) {
+    L.adapt = (int)L.t.size();
+    for (int l = 0; l + 1 < w->L_max; ++l) {
+      add(1, D, es); add(1, 1, es);   // token confidence
+      add(D, D, es); add(1, D, es);   // layer l's final projection
+      add(1, D, es); add(1, 1, es);   // layer l's matchability
+    }
+  }
   L.bytes = off;
   return L;
 }
@@ -139,12 +155,12 @@ sg_status check_weights(const sg_weights* w, WLayout* out) {
 // ---------------------------------------------------------- workspace layout
 
 struct WsLayout {
-  size_t X, H0, H1, QK, VT, KS, VS, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, ROPE, total;
+  size_t X, H0, H1, QK, VT, KS, VS, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, ROPE, ADAPT, total;
   int ldvt, ldqk;
 };
 
 WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, long pf, long pd, long uf, long vf,
-                       long nb, long ropef = 0) {
+                       long nb, long ropef = 0, bool adaptive = false) {
   WsLayout L;
   // row strides are kept off powers of two (+64 / +16 bytes) so that the
   // strided accesses of the attention kernel spread over the L2 channels
@@ -178,6 +194,9 @@ WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, l
   L.VD = take((size_t)vf * 4);
   L.IDX1 = take((size_t)nb * 4);
   L.ROPE = take((size_t)ropef * 8);  // (cos, sin) per row and rotary pair
+  // adaptive calls: 10 per-row int / float arrays, the stop flag and the
+  // exit head's (M+1) x (N+1) log assignment (at most zf + R + 1 floats)
+  L.ADAPT = take(adaptive ? (size_t)(10 * R + 128 + zf + R + 1) * 4 : 0);
   L.total = o;
   return L;
 }
@@ -186,7 +205,7 @@ WsLayout ws_layout(const sg_weights* w, long R, long zf, long ztf, long pf, long
   int maxw = 0;
   for (int i = 0; i < w->n_enc; ++i) maxw = std::max(maxw, w->enc[i]);
   return ws_layout_raw(w->D, w->dtype == SG_BF16 ? 2 : 4, maxw, R, zf, ztf, pf, pd, uf, vf, nb,
-                       w->rope ? R * (w->D / w->H / 2) : 0);
+                       w->rope ? R * (w->D / w->H / 2) : 0, w->adaptive != 0);
 }
 
 // ----------------------------------------------------------- library workspace
@@ -381,19 +400,19 @@ sg_status run_encoder(const Problem& p, const Plan& pl, const sg_weights* w, con
 
 // Rotary table of the self stages from the positions of the problem.
 sg_status run_rope_table(const Problem& p, const Plan& pl, const sg_weights* w, const WLayout& L, char* ws,
-                         const WsLayout& wl, hipStream_t st) {
+                         const WsLayout& wl, hipStream_t st, const int* ind = nullptr) {
   EncArgs e;
   memset(&e, 0, sizeof(e));
   for (int i = 0; i < 2; ++i) e.kpts[i] = p.kp[i];
   memcpy(e.img, p.img, sizeof(e.img));
-  HIPCHK(launch_rope_table(e, pl.seg, at<float>(w, L, L.rope), w->D / w->H, pl.R,
+  HIPCHK(launch_rope_table(e, pl.seg, at<float>(w, L, L.rope), w->D / w->H, pl.R, ind,
                            reinterpret_cast<float2*>(ws + wl.ROPE), st), "rotary table");
   return SG_OK;
 }
 
 // Stages [s0, s1) in place on X (compact rows of every image of the plan).
 sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0, int s1, char* ws,
-                  const WsLayout& wl, int flags, Timer& tm, hipStream_t st) {
+                  const WsLayout& wl, int flags, Timer& tm, hipStream_t st, const int* stop = nullptr) {
   const int D = w->D, op = w->dtype, R = pl.R;
   (void)flags;
   float* X = reinterpret_cast<float*>(ws + wl.X);
@@ -415,7 +434,7 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       g.A0 = X; g.lda0 = D; g.K0 = D; g.K = D;
       g.W = atv(w, L, base); g.ldw = D; g.bias = atv(w, L, base + 1);
       g.C = QK; g.C2 = op == SG_BF16 ? ws + wl.VS : VT; g.C3 = ws + wl.KS;
-      g.split = nout - D; g.tied = tied;
+      g.split = nout - D; g.tied = tied; g.stop = stop;
       if (w->rope && !(s & 1)) {  // self stage: rotate q and k
         g.rope = reinterpret_cast<const float2*>(ws + wl.ROPE);
         g.rope_dh = D / w->H;
@@ -428,7 +447,7 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
     {
       AttnArgs a;
       a.qk = QK; a.vt = VT; a.ks = ws + wl.KS; a.vs = ws + wl.VS;
-      a.out = MB; a.D = D; a.ldvt = wl.ldvt; a.ldqk = wl.ldqk; a.cross = s & 1;
+      a.out = MB; a.D = D; a.ldvt = wl.ldvt; a.ldqk = wl.ldqk; a.cross = s & 1; a.stop = stop;
       a.heads = w->H;
       const int dh = D / w->H;
       a.scale2 = log2e / sqrtf((float)dh);
@@ -440,7 +459,7 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       memset(&g, 0, sizeof(g));
       g.A0 = MB; g.lda0 = D; g.K0 = D; g.K = D;
       g.W = atv(w, L, base + 2); g.ldw = D; g.bias = atv(w, L, base + 3);
-      g.C = M2;
+      g.C = M2; g.stop = stop;
       GemmBatch b = single(R, D, D);
       HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, op == SG_F32, op, op == SG_F32, EPI_BIAS, g, b, R, D, st); }), "merge GEMM");
     }
@@ -450,7 +469,7 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       memset(&g, 0, sizeof(g));
       g.A0 = X; g.lda0 = D; g.K0 = D; g.A1 = M2; g.lda1 = D; g.K = 2 * D;
       g.W = atv(w, L, base + 4); g.ldw = 2 * D; g.bias = atv(w, L, base + 5);
-      g.C = HB;
+      g.C = HB; g.stop = stop;
       GemmBatch b = single(R, 2 * D, 2 * D);
       HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, op == SG_F32, EPI_RELU, g, b, R, 2 * D, st); }), "mlp1 GEMM");
     }
@@ -460,7 +479,7 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       memset(&g, 0, sizeof(g));
       g.A0 = HB; g.lda0 = 2 * D; g.K0 = 2 * D; g.K = 2 * D;
       g.W = atv(w, L, base + 6); g.ldw = 2 * D; g.bias = atv(w, L, base + 7);
-      g.C = X;
+      g.C = X; g.stop = stop;
       GemmBatch b = single(R, D, D);
       HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, op == SG_F32, op, 1, EPI_RESID, g, b, R, D, st); }), "mlp2 GEMM");
     }
@@ -470,12 +489,13 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
 
 // Final projection of every row of X into F (fp32).
 sg_status run_project(const Plan& pl, const sg_weights* w, const WLayout& L, const float* X, float* F,
-                      Timer& tm, hipStream_t st) {
+                      Timer& tm, hipStream_t st, int wf_index = -1) {
   const int D = w->D, op = w->dtype;
+  if (wf_index < 0) wf_index = L.final_first;
   GemmArgs g;
   memset(&g, 0, sizeof(g));
   g.A0 = X; g.lda0 = D; g.K0 = D; g.K = D;
-  g.W = atv(w, L, L.final_first); g.ldw = D; g.bias = atv(w, L, L.final_first + 1);
+  g.W = atv(w, L, wf_index); g.ldw = D; g.bias = atv(w, L, wf_index + 1);
   g.C = F;
   GemmBatch b = single(pl.R, D, D);
   HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, 1, EPI_BIAS, g, b, pl.R, D, st); }), "final projection");
@@ -600,6 +620,8 @@ sg_status check_opts(const sg_opts* o) {
   if (o->kernel_events && o->n_kernel_events < 0) return fail(SG_ERR_INVALID_ARG, "n_kernel_events < 0");
   if ((o->flags & SG_FLAG_SINKHORN_TWO_SWEEP) && (o->flags & SG_FLAG_SINKHORN_ONE_SWEEP))
     return fail(SG_ERR_INVALID_ARG, "both Sinkhorn schedules forced");
+  if (o->depth_confidence < 0.f || o->width_confidence < 0.f || o->width_confidence > 1.f || o->prune_min_points < 0)
+    return fail(SG_ERR_INVALID_ARG, "adaptive options out of range");
   return SG_OK;
 }
 
@@ -690,7 +712,7 @@ std::string call_key(int kind, const Problem& p, const sg_weights* w, int Lst, i
   if (w) {
     put(k, w->D); put(k, w->H); put(k, w->n_enc);
     for (int i = 0; i < w->n_enc; ++i) put(k, w->enc[i]);
-    put(k, w->L_max); put(k, w->dtype); put(k, w->head); put(k, w->cross); put(k, w->rope);
+    put(k, w->L_max); put(k, w->dtype); put(k, w->head); put(k, w->cross); put(k, w->rope); put(k, w->adaptive);
     put(k, w->blob); put(k, w->blob_bytes);
   }
   put(k, Lst); put(k, T); put(k, out);
@@ -749,6 +771,192 @@ sg_status enqueue_full(const Problem& p, const Plan& pl, const WsLayout& wl, cha
   if ((s = run_matching(p, pl, w->D, 0.f, alpha_dev, T, thr, w->head == SG_HEAD_DOUBLE_SOFTMAX ? &ds : nullptr, F,
                         ws, wl, out, tm, st)) != SG_OK)
     return s;
+  tm.stage(SG_EV_END);
+  tm.finish();
+  return SG_OK;
+}
+
+// ------------------------------------------------- adaptive depth and width
+//
+// One pair, eager, with one stream synchronisation per layer: the stop
+// decision and the kept counts come back to the host, which re-plans the row
+// space when points are dropped (as the page's own loop does with its Python
+// control flow).
+
+std::mutex g_pin_mu;
+int* g_pin[64] = {};      // host-visible, coherent post box per device
+int* g_pin_dev[64] = {};  // its device address
+int g_adaptive_calls = 0;
+
+sg_status post_box(int** host, int** dev_ptr) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(SG_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_pin_mu);
+  if (!g_pin[dev]) {
+    HIPCHK(hipHostMalloc((void**)&g_pin[dev], 64 * sizeof(int), hipHostMallocMapped | hipHostMallocCoherent),
+           "hipHostMalloc");
+    HIPCHK(hipHostGetDevicePointer((void**)&g_pin_dev[dev], g_pin[dev], 0), "hipHostGetDevicePointer");
+    g_pin[dev][0] = -1;
+  }
+  *host = g_pin[dev];
+  *dev_ptr = g_pin_dev[dev];
+  return SG_OK;
+}
+
+// Spins until the statistics kernel of the layer posts `seq` (bounded: an
+// error after ten seconds).
+sg_status wait_post(volatile int* box, int seq, hipStream_t st) {
+  const auto t0 = std::chrono::steady_clock::now();
+  long n = 0;
+  while (box[0] != seq) {
+    if ((++n & 0xFFFF) == 0) {
+      const hipError_t e = hipStreamQuery(st);
+      if (e != hipSuccess && e != hipErrorNotReady) return hip_fail(e, "adaptive statistics");
+      if (e == hipSuccess && box[0] != seq) return fail(SG_ERR_HIP, "adaptive statistics did not post");
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(10))
+        return fail(SG_ERR_HIP, "adaptive statistics: no post after 10 s");
+    }
+  }
+  return SG_OK;
+}
+
+sg_status run_adaptive(const Problem& p0, const sg_weights* w, const WLayout& L, int Lst, const Outputs& out,
+                       const sg_opts* o) {
+  hipStream_t st = stream_of(o);
+  if (st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+      return fail(SG_ERR_INVALID_ARG, "adaptive calls synchronise their stream and cannot be captured");
+  }
+  const bool depth = o->flags & SG_FLAG_EARLY_EXIT, width = o->flags & SG_FLAG_PRUNE;
+  const float alpha = o->depth_confidence > 0.f ? o->depth_confidence : 0.95f;
+  const float beta = o->width_confidence > 0.f ? o->width_confidence : 0.99f;
+  const int pmin = o->prune_min_points > 0 ? o->prune_min_points : 1024;
+  Plan pl;
+  make_plan(p0, pl);
+  WsLayout wl = ws_layout(w, pl.R, pl.zf, pl.ztf, pl.pf, pl.pd, pl.uf, pl.vf, pl.nb);
+  void* wsp = nullptr;
+  sg_status s = get_workspace(o, wl.total, &wsp);
+  if (s != SG_OK) return s;
+  int *box = nullptr, *box_dev = nullptr;
+  if ((s = post_box(&box, &box_dev)) != SG_OK) return s;
+  char* ws = reinterpret_cast<char*>(wsp);
+  const int M = p0.M[0], N = p0.N[0], D = w->D, R0 = pl.R;
+  float* X = reinterpret_cast<float*>(ws + wl.X);
+  int* IND = reinterpret_cast<int*>(ws + wl.ADAPT);
+  int* IND2 = IND + R0;
+  int* KEEP = IND + 2 * R0;
+  int* NEWIDX = IND + 3 * R0;
+  int* CNT = IND + 4 * R0;  // the stop flag at [0]
+  int* STOP = CNT;
+  int* PART = CNT + 64;      // per-workgroup counts: 4 per 4 points, at most R0 + 4
+  int* PR = PART + R0 + 64;
+  int32_t* TM0 = PR + R0;
+  float* TS0 = reinterpret_cast<float*>(TM0 + R0);
+  int32_t* TM1 = reinterpret_cast<int32_t*>(TS0 + R0);
+  float* TS1 = reinterpret_cast<float*>(TM1 + R0);
+  float* LT = TS1 + R0;
+  Timer tm{o, st};
+  tm.stage(SG_EV_START);
+  HIPCHK(launch_fill_empty(out.m0, out.s0, M, st), "empty output");
+  if (out.m1) HIPCHK(launch_fill_empty(out.m1, out.s1, N, st), "empty output");
+  HIPCHK(launch_fill_i32(PR, 1, M + N, st), "prune counts");
+  HIPCHK(launch_fill_i32(CNT, 0, 64, st), "counters and stop flag");
+  if ((s = run_encoder(p0, pl, w, L, ws, wl, tm, st)) != SG_OK) return s;
+  HIPCHK(launch_iota_rows(pl.seg, R0, IND, st), "row index");
+  if (w->rope && (s = run_rope_table(p0, pl, w, L, ws, wl, st, IND)) != SG_OK) return s;
+  tm.stage(SG_EV_ENCODED);
+  const int call = ++g_adaptive_calls & 0xFFFFF;
+  const int stat_flags = (depth ? 1 : 0) | (width ? 2 : 0);
+  Problem pc = p0;
+  Plan cur = pl;
+  // Layer l's stages, then (all layers but the last) its statistics, which
+  // post their counters and set the device stop flag; every kernel of a
+  // later layer checks that flag, so the host may enqueue layer l + 1 before
+  // layer l's decision arrives whenever no pruning can reshape the rows.
+  auto enqueue_layer = [&](int l) -> sg_status {
+    sg_status r = run_gnn(cur, w, L, 2 * l, 2 * l + 2, ws, wl, o->flags, tm, st, STOP);
+    if (r != SG_OK || l == Lst - 1 || !stat_flags) return r;
+    const int base = L.adapt + kPerLayerAdaptive * l;
+    const float lam = std::min(1.f, std::max(0.f, 0.8f + 0.1f * std::exp(-4.f * l / Lst)));
+    HIPCHK(launch_adaptive_stats(X, cur.seg, D, w->dtype, atv(w, L, base), atv(w, L, base + 1),
+                                 atv(w, L, base + 4), atv(w, L, base + 5), lam, 1.f - beta, stat_flags, alpha, M + N,
+                                 (call << 8) | l, KEEP, PART, STOP, box_dev, st), "confidence");
+    return SG_OK;
+  };
+  int exit_layer = Lst - 1;
+  bool empty = false;
+  if ((s = enqueue_layer(0)) != SG_OK) return s;
+  for (int l = 0; l + 1 < Lst; ++l) {
+    // layer l (and its statistics) are enqueued
+    if (!stat_flags) {
+      if ((s = enqueue_layer(l + 1)) != SG_OK) return s;
+      continue;
+    }
+    const int curM = pc.M[0], curN = pc.N[0];
+    const bool may_prune = width && (curM > pmin || curN > pmin);
+    if (!may_prune && (s = enqueue_layer(l + 1)) != SG_OK) return s;  // speculative
+    if ((s = wait_post(box, (call << 8) | l, st)) != SG_OK) return s;
+    const int stopped = box[1], kA = box[3], kB = box[5];
+    if (stopped) {
+      exit_layer = l;
+      break;
+    }
+    if (may_prune) {
+      const bool pA = curM > pmin && kA < curM, pB = curN > pmin && kB < curN;
+      if (pA || pB) {
+        const int mask = (pA ? 1 : 0) | (pB ? 2 : 0);
+        Problem pn = pc;
+        pn.M = {pA ? kA : curM};
+        pn.N = {pB ? kB : curN};
+        pn.Mpad = pn.M[0];
+        pn.Npad = pn.N[0];
+        Plan nx;
+        make_plan(pn, nx);
+        float* XT = reinterpret_cast<float*>(ws + wl.HB);  // free between layers, at least R D floats
+        HIPCHK(launch_prune_scan(cur.seg, KEEP, mask, NEWIDX, st), "prune scan");
+        HIPCHK(launch_compact_rows(X, IND, NEWIDX, cur.seg, nx.seg, cur.R, nx.R, D, mask, M, XT, IND2, PR, st),
+               "compact rows");
+        if (nx.R > 0) {
+          HIPCHK(hipMemcpyAsync(X, XT, (size_t)nx.R * D * 4, hipMemcpyDeviceToDevice, st), "copy states");
+          HIPCHK(hipMemcpyAsync(IND, IND2, (size_t)nx.R * 4, hipMemcpyDeviceToDevice, st), "copy index");
+        }
+        pc = pn;
+        cur = nx;
+        if (w->rope && (s = run_rope_table(pc, cur, w, L, ws, wl, st, IND)) != SG_OK) return s;
+      }
+      if (pc.M[0] == 0 || pc.N[0] == 0) {
+        exit_layer = l;
+        empty = true;
+        break;
+      }
+      if ((s = enqueue_layer(l + 1)) != SG_OK) return s;
+    }
+  }
+  tm.stage(SG_EV_GNN);
+  if (!empty) {
+    const bool own = exit_layer < w->L_max - 1;  // the layer's own head, else the main one
+    const int hb = L.adapt + kPerLayerAdaptive * exit_layer;
+    float* F = reinterpret_cast<float*>(ws + wl.F);
+    if ((s = run_project(cur, w, L, X, F, tm, st, own ? hb + 2 : L.final_first)) != SG_OK) return s;
+    DsHead ds;
+    ds.X = X;
+    ds.w_dtype = w->dtype;
+    ds.wz = atv(w, L, own ? hb + 4 : L.wz);
+    ds.bz_dev = atv(w, L, own ? hb + 5 : L.wz + 1);
+    Outputs to;
+    to.m0 = TM0; to.s0 = TS0; to.m1 = TM1; to.s1 = TS1;
+    to.logP = out.logP ? LT : nullptr;
+    to.logP_ld = pc.N[0] + 1;
+    if ((s = run_matching(pc, cur, D, 0.f, nullptr, 0, o->match_threshold, &ds, F, ws, wl, to, tm, st)) != SG_OK)
+      return s;
+    HIPCHK(launch_scatter_outputs(cur.seg, IND, TM0, TS0, TM1, TS1, out.m0, out.s0, out.m1, out.s1, F, D, out.descA,
+                                  out.descB, to.logP, M, N, out.logP, out.logP_ld, cur.R, st), "scatter outputs");
+  }
+  if (o->out_prune0 && M) HIPCHK(hipMemcpyAsync(o->out_prune0, PR, (size_t)M * 4, hipMemcpyDeviceToDevice, st), "prune0");
+  if (o->out_prune1 && N) HIPCHK(hipMemcpyAsync(o->out_prune1, PR + M, (size_t)N * 4, hipMemcpyDeviceToDevice, st), "prune1");
+  if (o->out_exit_layer) *o->out_exit_layer = exit_layer;
   tm.stage(SG_EV_END);
   tm.finish();
   return SG_OK;
@@ -846,6 +1054,10 @@ sg_status sg_match(const float* kptsA, const float* descA, const float* confA, i
     out.descA = opts->out_desc_A; out.descB = opts->out_desc_B;
     out.logP = opts->out_logP; out.logP_ld = opts->logP_ld; out.logP_stride = 0;
   }
+  if (opts && (opts->flags & (SG_FLAG_EARLY_EXIT | SG_FLAG_PRUNE))) {
+    if (!weights->adaptive) return fail(SG_ERR_INVALID_ARG, "adaptive flags need adaptive weights");
+    return run_adaptive(p, weights, WL, L, out, opts);
+  }
   return run_full(p, weights, WL, L, T, out, opts);
 }
 
@@ -860,6 +1072,8 @@ sg_status sg_match_batch(int32_t B, int32_t Mpad, int32_t Npad, const int32_t* M
   if (s != SG_OK) return s;
   if ((s = check_opts(opts)) != SG_OK) return s;
   if (B < 1 || B > SG_MAX_BATCH) return fail(SG_ERR_INVALID_ARG, "B = %d outside [1, %d]", B, SG_MAX_BATCH);
+  if (opts && (opts->flags & (SG_FLAG_EARLY_EXIT | SG_FLAG_PRUNE)))
+    return fail(SG_ERR_UNSUPPORTED, "adaptive depth / width runs one pair per call (sg_match)");
   if (!M || !N) return fail(SG_ERR_INVALID_ARG, "M/N host arrays are NULL");
   if (Mpad < 0 || Npad < 0 || Mpad > 4096 || Npad > 4096) return fail(SG_ERR_UNSUPPORTED, "Mpad/Npad outside [0, 4096]");
   for (int b = 0; b < B; ++b)

@@ -15,6 +15,7 @@ namespace sg {
 
 template <typename OpT, int DH, int NW>
 __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg) {
+  if (a.stop && *a.stop) return;  // a later layer of a pass that has already stopped
   constexpr bool BF = std::is_same<OpT, bf16>::value;
   constexpr int NCB = (DH + 31) / 32;        // 32-channel blocks of the output
   constexpr int QS = BF ? DH / 16 : DH / 8;  // Q / K registers per 32 keys: bf16x8 or float4 per lane
@@ -277,6 +278,7 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
 // four waves, which read their MFMA operands as one 16-byte LDS load each.
 template <int DH>
 __global__ __launch_bounds__(256) void k_attention_wide(AttnArgs a, SegTable seg) {
+  if (a.stop && *a.stop) return;  // a later layer of a pass that has already stopped
   constexpr int BQ = 128, BKEY = 64;
   constexpr int KBLK = DH / 16, VBLK = DH / 16;  // 512-element blocks per 32 keys (K: dim chunks; V: 2 j x DH/32)
   constexpr int TILE = (BKEY / 32) * (KBLK + VBLK) * 512;  // elements of one staged tile

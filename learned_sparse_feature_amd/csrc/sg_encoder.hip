@@ -120,16 +120,19 @@ __global__ __launch_bounds__(256) void k_encoder(EncArgs e, SegTable seg) {
 // get angle 0.  Computed once per call and read by every self stage's QKV
 // epilogue.
 __global__ __launch_bounds__(256) void k_rope_table(EncArgs e, SegTable seg, const float* __restrict__ basis,
-                                                    int hp, int R, float2* __restrict__ table) {
+                                                    int hp, int R, const int* __restrict__ ind,
+                                                    float2* __restrict__ table) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= R * hp) return;
   const int r = idx / hp, k = idx % hp;
   // the image of row r: the last segment starting at or before it
   int s = 0;
   while (s + 1 < seg.n_seg && seg.row0[s + 1] <= r) ++s;
-  const int p = r - seg.row0[s];
+  // the point's index in the caller's arrays: its row within the image, or
+  // the map `ind` once points have been dropped
+  const int p = ind ? ind[r] : (r - seg.row0[s] < seg.n[s] ? r - seg.row0[s] : -1);
   float th = 0.f;
-  if (p < seg.n[s]) {
+  if (p >= 0) {
     const bool isA = seg.side[s] == 0;
     const float* kp = e.kpts[isA ? 0 : 1] + 2 * (size_t)(seg.in_off[s] + p);
     const float iw = e.img[isA ? 0 : 2], ih = e.img[isA ? 1 : 3];
@@ -147,10 +150,10 @@ __global__ __launch_bounds__(256) void k_rope_table(EncArgs e, SegTable seg, con
 }
 
 hipError_t launch_rope_table(const EncArgs& e, const SegTable& seg, const float* basis, int dh, int R,
-                             float2* table, hipStream_t st) {
+                             const int* ind, float2* table, hipStream_t st) {
   const int hp = dh / 2;
   if (R <= 0 || hp <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rope_table, dim3((R * hp + 255) / 256), dim3(256), 0, st, e, seg, basis, hp, R, table);
+  hipLaunchKernelGGL(k_rope_table, dim3((R * hp + 255) / 256), dim3(256), 0, st, e, seg, basis, hp, R, ind, table);
   return hipGetLastError();
 }
 

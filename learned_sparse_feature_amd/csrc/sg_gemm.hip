@@ -68,6 +68,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   __shared__ __attribute__((aligned(16))) OpT As[2][BM * PITCH];
   __shared__ __attribute__((aligned(16))) OpT Ws[2][BN * PITCH];
 
+  if (g.stop && *g.stop) return;  // a later layer of a pass that has already stopped
   const int T = g.gx * g.gy * bt.n;
   const int t = (int)(blockIdx.x % 8) * ((T + 7) / 8) + (int)(blockIdx.x / 8);
   if (t >= T) return;

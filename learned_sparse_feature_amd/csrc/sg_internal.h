@@ -74,6 +74,7 @@ struct GemmArgs {
   int tied;                          // EPI_QKV: columns [0, split) are both q and k
   const float2* rope;                // EPI_QKV: per-row (cos, sin) of the rotary angles, [rows][rope_dh/2], or null
   int rope_dh;                       // head dimension of the rotary table
+  const int* stop;                   // or null: the launch does nothing when *stop != 0 (adaptive depth)
   int gx, gy;                        // row and column tiles (set by the launcher)
 };
 
@@ -109,15 +110,17 @@ struct AttnArgs {
   void* out;         // [R][D] message (heads concatenated)
   int D, ldvt, ldqk, cross, heads;
   float scale2;      // log2(e) / sqrt(dh)
+  const int* stop;   // or null: the launch does nothing when *stop != 0 (adaptive depth)
 };
 
 // Host-side launchers (sg_kernels.hip).
 hipError_t launch_encoder(int op_dtype, int w_dtype, const EncArgs& e, const SegTable& seg,
                           hipStream_t st);
 // (cos, sin) of the rotary angles of every compact row ([R][dh/2]) from the
-// positions in e.kpts / e.img (normalised as for the encoder).
+// positions in e.kpts / e.img (normalised as for the encoder); ind (or
+// null): the caller's point index of every row, -1 on padding.
 hipError_t launch_rope_table(const EncArgs& e, const SegTable& seg, const float* basis, int dh, int R,
-                             float2* table, hipStream_t st);
+                             const int* ind, float2* table, hipStream_t st);
 hipError_t launch_gemm(int op_dtype, int a0_is_f32, int w_dtype, int out_is_f32, int epi,
                        const GemmArgs& g, const GemmBatch& b, int max_rows, int max_n,
                        hipStream_t st);
@@ -153,6 +156,26 @@ hipError_t launch_ds_write_logp(const float* Z, const PairTable& pt, const float
                                 const float* ud, const float* vd, float* logP, int64_t ld, int64_t pair_stride,
                                 int total_rows, hipStream_t st);
 hipError_t launch_fill_f32(float* p, float v, int n, hipStream_t st);
+
+// Adaptive depth and width of one pair (sg_adaptive.hip).
+hipError_t launch_iota_rows(const SegTable& seg, int R, int* ind, hipStream_t st);
+hipError_t launch_fill_i32(int* p, int v, int n, hipStream_t st);
+// Per-point statistics (keep flags, per-workgroup counts in part[4 nb]),
+// then one workgroup that decides the stop (1 - unconfident / total > alpha
+// with flags bit 1) into *stop and posts seq, stop and the counts to the
+// host-visible post[0..5] (seq last).  Nothing runs once *stop is set.
+hipError_t launch_adaptive_stats(const float* X, const SegTable& seg, int D, int w_dtype, const void* wc,
+                                 const void* bc, const void* wz, const void* bz, float lam, float min_match,
+                                 int flags, float alpha, int total, int seq, int* keep, int* part, int* stop,
+                                 int* post, hipStream_t st);
+hipError_t launch_prune_scan(const SegTable& seg, const int* keep, int prune_mask, int* newidx, hipStream_t st);
+hipError_t launch_compact_rows(const float* Xo, const int* ind_o, const int* newidx, const SegTable& so,
+                               const SegTable& sn, int R_old, int R_new, int D, int prune_mask, int M, float* Xn,
+                               int* ind_n, int* pr, hipStream_t st);
+hipError_t launch_scatter_outputs(const SegTable& seg, const int* ind, const int32_t* tm0, const float* ts0,
+                                  const int32_t* tm1, const float* ts1, int32_t* m0, float* s0, int32_t* m1,
+                                  float* s1, const float* F, int D, float* fA, float* fB, const float* lt, int M,
+                                  int N, float* logP, int64_t ld, int R, hipStream_t st);
 hipError_t launch_fill_empty(int32_t* m, float* s, int n, hipStream_t st);
 
 }  // namespace sg

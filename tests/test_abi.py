@@ -196,3 +196,32 @@ def test_rope_layout_and_validation():
     wr.blob, wr.blob_bytes = fake, 1 << 30
     assert lib.sg_stage_gnn(fake, 4, fake, 4, C.byref(wr), 0, 2, None) == _lib.SG_ERR_INVALID_ARG
     assert "positions" in lib.sg_last_error().decode()
+
+
+def test_adaptive_layout_and_validation():
+    """Adaptive weights append, per layer but the last, the confidence and
+    the layer's head (6 tensors); they need the double-softmax head; the
+    batch entry point refuses adaptive calls; bad adaptive options are
+    rejected on the host."""
+    lib = _lib.load()
+    w = _cfg()
+    w.head = _lib.SG_HEAD_DOUBLE_SOFTMAX
+    wa = _cfg()
+    wa.head, wa.adaptive = _lib.SG_HEAD_DOUBLE_SOFTMAX, 1
+    assert lib.sg_weights_count(C.byref(wa)) == lib.sg_weights_count(C.byref(w)) + 6 * 8
+    bad = _cfg()
+    bad.adaptive = 1
+    assert lib.sg_weights_count(C.byref(bad)) == -1
+    fake = C.c_void_p(0x1000)
+    wa.blob, wa.blob_bytes = fake, 1 << 30
+    o = _lib.SgOpts()
+    o.flags = _lib.SG_FLAG_EARLY_EXIT
+    Ms = (C.c_int32 * 1)(8)
+    st = lib.sg_match_batch(1, 8, 8, Ms, Ms, *([fake] * 6), C.byref(wa), 1, 5, fake, fake, C.byref(o))
+    assert st == _lib.SG_ERR_UNSUPPORTED
+    o.width_confidence = 1.5
+    assert _match(lib, wa, opts=C.byref(o)) == _lib.SG_ERR_INVALID_ARG
+    plain = _cfg(blob=fake, nbytes=1 << 30)
+    o2 = _lib.SgOpts()
+    o2.flags = _lib.SG_FLAG_PRUNE
+    assert _match(lib, plain, opts=C.byref(o2)) == _lib.SG_ERR_INVALID_ARG
