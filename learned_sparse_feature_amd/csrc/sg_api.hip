@@ -155,7 +155,7 @@ sg_status check_weights(const sg_weights* w, WLayout* out) {
 // ---------------------------------------------------------- workspace layout
 
 struct WsLayout {
-  size_t X, H0, H1, QK, VT, KS, VS, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, ROPE, ADAPT, total;
+  size_t X, XB, H0, H1, QK, VT, KS, VS, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, ROPE, ADAPT, total;
   int ldvt, ldqk;
 };
 
@@ -172,6 +172,7 @@ WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, l
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   L.X = take((size_t)R * D * 4);
+  L.XB = take(bf ? (size_t)R * D * 2 : 0);  // bf16 copy of X: the operand of the QKV and MLP GEMMs
   L.H0 = take((size_t)R * maxw * 4);
   L.H1 = take((size_t)R * maxw * 4);
   L.QK = take((size_t)R * L.ldqk * os);
@@ -394,6 +395,7 @@ sg_status run_encoder(const Problem& p, const Plan& pl, const sg_weights* w, con
     e.b[i] = atv(w, L, L.enc_first + 2 * i + 1);
   }
   e.X = reinterpret_cast<float*>(ws + wl.X);
+  e.XB = w->dtype == SG_BF16 ? ws + wl.XB : nullptr;
   HIPCHK(launch_encoder(w->dtype, w->dtype, e, pl.seg, st), "encoder");
   return SG_OK;
 }
@@ -411,11 +413,18 @@ sg_status run_rope_table(const Problem& p, const Plan& pl, const sg_weights* w, 
 }
 
 // Stages [s0, s1) in place on X (compact rows of every image of the plan).
+// xb_valid: the bf16 copy XB of the states is current (the encoder writes
+// it); otherwise bf16 networks refresh it first.
 sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0, int s1, char* ws,
-                  const WsLayout& wl, int flags, Timer& tm, hipStream_t st, const int* stop = nullptr) {
+                  const WsLayout& wl, int flags, Timer& tm, hipStream_t st, const int* stop = nullptr,
+                  bool xb_valid = false) {
   const int D = w->D, op = w->dtype, R = pl.R;
   (void)flags;
   float* X = reinterpret_cast<float*>(ws + wl.X);
+  // bf16 networks read the states as bf16 (the QKV and MLP GEMMs would round
+  // them on load anyway); the residual GEMM keeps the copy current
+  void* XB = op == SG_BF16 ? ws + wl.XB : nullptr;
+  if (XB && !xb_valid && s0 < s1) HIPCHK(launch_to_bf16(X, XB, R * D, st), "bf16 states");
   void* QK = ws + wl.QK;
   void* VT = ws + wl.VT;
   void* MB = ws + wl.MB;
@@ -431,7 +440,7 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       const int nout = (tied ? 2 : 3) * D;
       GemmArgs g;
       memset(&g, 0, sizeof(g));
-      g.A0 = X; g.lda0 = D; g.K0 = D; g.K = D;
+      g.A0 = XB ? XB : X; g.lda0 = D; g.K0 = D; g.K = D;
       g.W = atv(w, L, base); g.ldw = D; g.bias = atv(w, L, base + 1);
       g.C = QK; g.C2 = op == SG_BF16 ? ws + wl.VS : VT; g.C3 = ws + wl.KS;
       g.split = nout - D; g.tied = tied; g.stop = stop;
@@ -441,7 +450,8 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       }
       GemmBatch b = single(R, nout, wl.ldqk);
       b.p[0].ldct = wl.ldvt;
-      HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, 0, EPI_QKV, g, b, R, nout, st); }), "qkv GEMM");
+      HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, XB == nullptr, op, 0, EPI_QKV, g, b, R, nout, st); }),
+             "qkv GEMM");
     }
     // multi-head attention: self on even stages, cross on odd stages
     {
@@ -467,11 +477,12 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
     {
       GemmArgs g;
       memset(&g, 0, sizeof(g));
-      g.A0 = X; g.lda0 = D; g.K0 = D; g.A1 = M2; g.lda1 = D; g.K = 2 * D;
+      g.A0 = XB ? XB : X; g.lda0 = D; g.K0 = D; g.A1 = M2; g.lda1 = D; g.K = 2 * D;
       g.W = atv(w, L, base + 4); g.ldw = 2 * D; g.bias = atv(w, L, base + 5);
       g.C = HB; g.stop = stop;
       GemmBatch b = single(R, 2 * D, 2 * D);
-      HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, 1, op, op == SG_F32, EPI_RELU, g, b, R, 2 * D, st); }), "mlp1 GEMM");
+      HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, XB == nullptr, op, op == SG_F32, EPI_RELU, g, b, R, 2 * D, st); }),
+             "mlp1 GEMM");
     }
     // x += W_2 h + b_2
     {
@@ -479,7 +490,7 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       memset(&g, 0, sizeof(g));
       g.A0 = HB; g.lda0 = 2 * D; g.K0 = 2 * D; g.K = 2 * D;
       g.W = atv(w, L, base + 6); g.ldw = 2 * D; g.bias = atv(w, L, base + 7);
-      g.C = X; g.stop = stop;
+      g.C = X; g.C2 = XB; g.stop = stop;
       GemmBatch b = single(R, D, D);
       HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, op == SG_F32, op, 1, EPI_RESID, g, b, R, D, st); }), "mlp2 GEMM");
     }
@@ -748,7 +759,7 @@ sg_status enqueue_full(const Problem& p, const Plan& pl, const WsLayout& wl, cha
   if ((s = run_encoder(p, pl, w, L, ws, wl, tm, st)) != SG_OK) return s;
   if (w->rope && (s = run_rope_table(p, pl, w, L, ws, wl, st)) != SG_OK) return s;
   tm.stage(SG_EV_ENCODED);
-  if ((s = run_gnn(pl, w, L, 0, 2 * Lst, ws, wl, o ? o->flags : 0, tm, st)) != SG_OK) return s;
+  if ((s = run_gnn(pl, w, L, 0, 2 * Lst, ws, wl, o ? o->flags : 0, tm, st, nullptr, true)) != SG_OK) return s;
   tm.stage(SG_EV_GNN);
   float* F = reinterpret_cast<float*>(ws + wl.F);
   if ((s = run_project(pl, w, L, reinterpret_cast<float*>(ws + wl.X), F, tm, st)) != SG_OK) return s;
@@ -875,8 +886,10 @@ sg_status run_adaptive(const Problem& p0, const sg_weights* w, const WLayout& L,
   // post their counters and set the device stop flag; every kernel of a
   // later layer checks that flag, so the host may enqueue layer l + 1 before
   // layer l's decision arrives whenever no pruning can reshape the rows.
+  bool xb_ok = true;  // the bf16 copy of the states matches X (compaction moves X only)
   auto enqueue_layer = [&](int l) -> sg_status {
-    sg_status r = run_gnn(cur, w, L, 2 * l, 2 * l + 2, ws, wl, o->flags, tm, st, STOP);
+    sg_status r = run_gnn(cur, w, L, 2 * l, 2 * l + 2, ws, wl, o->flags, tm, st, STOP, xb_ok);
+    xb_ok = true;
     if (r != SG_OK || l == Lst - 1 || !stat_flags) return r;
     const int base = L.adapt + kPerLayerAdaptive * l;
     const float lam = std::min(1.f, std::max(0.f, 0.8f + 0.1f * std::exp(-4.f * l / Lst)));
@@ -924,6 +937,7 @@ sg_status run_adaptive(const Problem& p0, const sg_weights* w, const WLayout& L,
         }
         pc = pn;
         cur = nx;
+        xb_ok = false;
         if (w->rope && (s = run_rope_table(pc, cur, w, L, ws, wl, st, IND)) != SG_OK) return s;
       }
       if (pc.M[0] == 0 || pc.N[0] == 0) {

@@ -105,7 +105,9 @@ __global__ __launch_bounds__(256) void k_encoder(EncArgs e, SegTable seg) {
         } else {
           // rows past the image (the tile's padding) are zero, so that every
           // later product over the padded row space stays finite
-          e.X[(row0 + r) * e.ldx + n] = r < np ? de[(size_t)r * e.D + n] + v : 0.f;
+          const float xv = r < np ? de[(size_t)r * e.D + n] + v : 0.f;
+          e.X[(row0 + r) * e.ldx + n] = xv;
+          if (e.XB) static_cast<bf16*>(e.XB)[(row0 + r) * e.ldx + n] = (bf16)xv;
         }
       }
     }

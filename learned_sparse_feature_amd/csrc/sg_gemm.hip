@@ -328,7 +328,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
           if (EPI == EPI_QKV && g.tied) reinterpret_cast<OutT*>(g.C)[P.c_off + (size_t)r * P.ldc + n + g.split] = (OutT)v;
         } else if constexpr (EPI == EPI_RESID) {
           float* c = reinterpret_cast<float*>(g.C) + P.c_off + (size_t)r * P.ldc + n;
-          *c = *c + v;
+          const float x = *c + v;
+          *c = x;
+          // bf16 shadow of the states (the operand the next GEMMs read)
+          if (g.C2) reinterpret_cast<bf16*>(g.C2)[P.c_off + (size_t)r * P.ldc + n] = (bf16)x;
         } else {  // EPI_SCORE
           v = acc[i][j][e] * g.scale;
           reinterpret_cast<float*>(g.C)[P.c_off + (size_t)r * P.ldc + n] = v;
@@ -336,6 +339,22 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
         }
       }
   }
+}
+
+__global__ void k_to_bf16(const float* __restrict__ x, bf16* __restrict__ y, int n4) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= n4) return;
+  const float4 v = reinterpret_cast<const float4*>(x)[t];
+  bf16x4 o;
+  o[0] = (bf16)v.x; o[1] = (bf16)v.y; o[2] = (bf16)v.z; o[3] = (bf16)v.w;
+  reinterpret_cast<bf16x4*>(y)[t] = o;
+}
+
+hipError_t launch_to_bf16(const float* x, void* y, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_to_bf16, dim3((n / 4 + 255) / 256), dim3(256), 0, st, x, static_cast<bf16*>(y), n / 4);
+  return hipGetLastError();
 }
 
 template <typename OpT, typename A0T, typename WT, typename OutT, int EPI>
@@ -390,6 +409,8 @@ hipError_t launch_gemm(int op, int a0f, int wd, int outf, int epi, const GemmArg
       switch (epi) {
         case EPI_BIAS: SG_GO(bf16, bf16, bf16, bf16, EPI_BIAS); break;
         case EPI_RESID: SG_GO(bf16, bf16, bf16, float, EPI_RESID); break;
+        case EPI_QKV: SG_GO(bf16, bf16, bf16, bf16, EPI_QKV); break;
+        case EPI_RELU: SG_GO(bf16, bf16, bf16, bf16, EPI_RELU); break;
         default: return hipErrorInvalidValue;
       }
     }

@@ -67,7 +67,7 @@ struct GemmArgs {
   const void* W; int ldw;            // weights [n_out][K]
   const void* bias;                  // [n_out] or null
   int K;
-  void* C; void* C2;                 // outputs (C2: VT / VS or ZT)
+  void* C; void* C2;                 // outputs (C2: VT / VS, ZT, or the bf16 shadow of C for EPI_RESID)
   void* C3;                          // EPI_QKV, bf16: KS
   float scale;
   int split;                         // EPI_QKV: first column that goes to VT (VS)
@@ -90,6 +90,7 @@ struct EncArgs {
   const void* W[SG_MAX_ENC + 1];
   const void* b[SG_MAX_ENC + 1];
   float* X;              // states [R][ldx]
+  void* XB;              // or null: their bf16 copy [R][ldx] (bf16 networks)
 };
 
 // Attention operands.  fp32 networks: qk [R][ldqk] holds q (columns
@@ -124,6 +125,8 @@ hipError_t launch_rope_table(const EncArgs& e, const SegTable& seg, const float*
 hipError_t launch_gemm(int op_dtype, int a0_is_f32, int w_dtype, int out_is_f32, int epi,
                        const GemmArgs& g, const GemmBatch& b, int max_rows, int max_n,
                        hipStream_t st);
+// y (bf16) = x (fp32) rounded to nearest even, n a multiple of 4.
+hipError_t launch_to_bf16(const float* x, void* y, int n, hipStream_t st);
 hipError_t launch_attention(int op_dtype, int dh, const AttnArgs& a, const SegTable& seg,
                             int heads, hipStream_t st);
 // alpha_dev (device pointer to the dustbin score) overrides alpha2 when non-null.
