@@ -161,6 +161,28 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = zero16();
+  // The residual tile is requested all at once, not one element after
+  // another behind the epilogue's stores (which the compiler may not move
+  // the loads past): before the main loop for the small tiles, where its
+  // latency then overlaps the K loop, and after it for the large ones, whose
+  // main loop has no registers to spare.
+  constexpr int RM = EPI == EPI_RESID ? MB : 1, RN = EPI == EPI_RESID ? NB : 1;
+  float cres[RM][RN][16];
+  auto load_resid = [&]() {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = r0 + wm * (BM / 2) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          cres[i][j][e] = (r < P.rows && n < P.n_out)
+                              ? reinterpret_cast<const float*>(g.C)[P.c_off + (size_t)r * P.ldc + n] : 0.f;
+        }
+    }
+  };
+  if constexpr (EPI == EPI_RESID && PF > 2) load_resid();
   const int nk = (g.K + BK - 1) / BK;
 #pragma unroll
   for (int q = 0; q < PF; ++q)
@@ -178,6 +200,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
     }
   }
 
+  if constexpr (EPI == EPI_RESID && PF <= 2) load_resid();
   if constexpr (EPI == EPI_QKV) {
     // The bias is added to the accumulators here, once.  Self stages with a
     // rotary table then rotate every channel pair (2c, 2c+1) of q and k
@@ -327,9 +350,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
           // tied query/key projection: the same column is k as well (k at +split)
           if (EPI == EPI_QKV && g.tied) reinterpret_cast<OutT*>(g.C)[P.c_off + (size_t)r * P.ldc + n + g.split] = (OutT)v;
         } else if constexpr (EPI == EPI_RESID) {
-          float* c = reinterpret_cast<float*>(g.C) + P.c_off + (size_t)r * P.ldc + n;
-          const float x = *c + v;
-          *c = x;
+          const float x = cres[i][j][e] + v;
+          reinterpret_cast<float*>(g.C)[P.c_off + (size_t)r * P.ldc + n] = x;
           // bf16 shadow of the states (the operand the next GEMMs read)
           if (g.C2) reinterpret_cast<bf16*>(g.C2)[P.c_off + (size_t)r * P.ldc + n] = (bf16)x;
         } else {  // EPI_SCORE
