@@ -184,6 +184,74 @@ def adaptive_bench(args, cfg, dev, sg, synth, np, torch):
     return res
 
 
+def batch_kernels(args, cfg, sg, np, torch, bstep, B, M, N, ds):
+    """Per kernel class of one batched call: launches, time, and the fraction
+    of the MFMA or HBM peak.  Launches here run 25-200 us, so the ~2.5 us of
+    the events bracketing each launch is left in."""
+    classes = {"gemm": sg.SG_K_GEMM, "attention": sg.SG_K_ATTENTION, "sinkhorn": sg.SG_K_SINKHORN}
+    res = {}
+    evs = sg.make_events(1024)
+    for name, kind in classes.items():
+        tot, nl = None, None
+        reps = 3
+        for _ in range(reps):
+            o = bstep(timed_kernel=kind, kernel_events=evs)
+            torch.cuda.synchronize()
+            nl = o["n_kernel_launches"]
+            assert 0 < nl < 512, (name, nl)
+            d = np.array([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(nl)])
+            tot = d if tot is None else tot + d
+        dur_us = tot / reps * 1e3
+        r = {"launches": nl, "total_us": round(float(dur_us.sum()), 1), "avg_us": round(float(dur_us.mean()), 2)}
+        if name == "gemm":
+            fl = gemm_flops(cfg, M, N, args.cross)
+            assert nl == len(fl), ("batched GEMM launches", nl, len(fl))
+            bf = [(f * B, d) for (dt_, f), d in zip(fl, dur_us) if dt_ == "bf16"]
+            ach = sum(f for f, _ in bf) / sum(d for _, d in bf) / 1e6
+            r.update(achieved_TFLOPs_bf16=round(ach, 1), frac_mfma=round(ach / PEAK["bf16_TFLOPs"], 4))
+            per = {"qkv": dur_us[0:8 * cfg.L:4], "merge": dur_us[1:8 * cfg.L:4], "mlp1": dur_us[2:8 * cfg.L:4],
+                   "mlp2_residual": dur_us[3:8 * cfg.L:4]}
+            fls = {"qkv": fl[0][1], "merge": fl[1][1], "mlp1": fl[2][1], "mlp2_residual": fl[3][1]}
+            r["per_projection"] = {k: {"avg_us": round(float(v.mean()), 2),
+                                       "frac_mfma": round(fls[k] * B / (float(v.mean()) * 1e6) / PEAK["bf16_TFLOPs"], 4)}
+                                   for k, v in per.items()}
+        elif name == "attention":
+            fl = attention_flops(cfg, M, N)
+            assert nl == len(fl), ("batched attention launches", nl, len(fl))
+            ach = sum(fl) * B / dur_us.sum() / 1e6
+            r.update(achieved_TFLOPs=round(ach, 1), frac_mfma=round(ach / PEAK["bf16_TFLOPs"], 4))
+        elif ds:
+            r["kernel"] = "k_ds_stats"
+            byt = ds_bytes(M, N, cfg.D)[0] * B
+            r.update(achieved_GBps=round(byt / dur_us.sum() / 1e3, 1),
+                     frac_hbm=round(byt / dur_us.sum() / 1e3 / PEAK["hbm_GBps"], 4))
+        else:
+            # one read of every pair's couplings per iteration, over the time
+            # of the iteration's launches (row pass + column reduction)
+            byt = 4.0 * (M + 1) * (N + 1) * B * cfg.T
+            r.update(bytes_per_iteration=4.0 * (M + 1) * (N + 1) * B,
+                     achieved_GBps=round(byt / dur_us.sum() / 1e3, 1),
+                     frac_hbm=round(byt / dur_us.sum() / 1e3 / PEAK["hbm_GBps"], 4))
+        res[name] = r
+    return res
+
+
+def latency_percentiles(step, sg, torch, n):
+    """p10 / p50 / p90 of single-pass latency: each pass bracketed by its own
+    pair of events on the library's stream, one pass at a time."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    ts = []
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    q = lambda f: round(ts[min(n - 1, int(f * n))], 4)
+    return {"passes": n, "p10_ms": q(0.1), "p50_ms": q(0.5), "p90_ms": q(0.9)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +328,8 @@ def main():
     ms = 1e3 * dt / args.steps
     value = args.steps / dt
     log(f"{ms:.3f} ms/step, {value:.1f} pairs/s; matches {(out['matches0'] >= 0).sum().item()}")
+    latency = latency_percentiles(step, sg, torch, max(10, min(100, args.steps)))
+    log(f"latency: {latency}")
 
     # per-stage times (a separate pass: stage events perturb the stream slightly)
     stages = {}
@@ -383,9 +453,9 @@ def main():
         bbufs = {"matches0": torch.empty((Bn, M), dtype=torch.int32, device=dev),
                  "scores0": torch.empty((Bn, M), dtype=torch.float32, device=dev)}
 
-        def bstep():
+        def bstep(**kw):
             return sg.sg_match_batch(Ms, Ns, *[bt[k] for k in keys], W, cfg.L, cfg.T, image_size=img,
-                                     workspace=wsb, want_matches1=False, sinkhorn=args.sinkhorn)
+                                     workspace=wsb, want_matches1=False, sinkhorn=args.sinkhorn, **kw)
         for _ in range(max(2, args.warmup)):
             bstep()
         torch.cuda.synchronize()
@@ -397,6 +467,8 @@ def main():
         dtb = time.perf_counter() - t0
         batch = {"pairs_per_call": Bn, "calls": nb, "ms_per_call": round(1e3 * dtb / nb, 3),
                  "pairs_per_s": round(nb * Bn / dtb, 2)}
+        if not args.no_kernel_timing:
+            batch["kernels"] = batch_kernels(args, cfg, sg, np, torch, bstep, Bn, M, N, ds)
         log(f"batch: {batch}")
 
     adaptive = adaptive_bench(args, cfg, dev, sg, synth, np, torch) if args.adaptive else None
@@ -420,7 +492,7 @@ def main():
                                 + ("head" if ds else "Sinkhorn")),
                    "pairs_per_step": 1, "M": M, "N": N, "D": cfg.D, "L": cfg.L, "T": None if ds else cfg.T,
                    "head": args.head, "cross_attention": args.cross, "rope": args.rope},
-        "roofline": roofline, "cpu_baseline": cpu, "stages_ms": stages, "kernels": kernels,
+        "roofline": roofline, "cpu_baseline": cpu, "latency": latency, "stages_ms": stages, "kernels": kernels,
         "batch_throughput": batch,
         "adaptive": adaptive,
         "baseline_context": {"pages_ms_per_pair": {"GTX1080_1024kp": 87.0, "unstated_hw_2048kp": 70.0},

@@ -798,6 +798,10 @@ std::mutex g_pin_mu;
 int* g_pin[64] = {};      // host-visible, coherent post box per device
 int* g_pin_dev[64] = {};  // its device address
 int g_adaptive_calls = 0;
+// Post slots: layer l posts into slot l % kPostSlots, so that the layer
+// enqueued ahead of the host's wait cannot overwrite the post being waited
+// for (the host may be descheduled for longer than a layer takes).
+constexpr int kPostSlots = 64, kPostSlotInts = 16;
 
 sg_status post_box(int** host, int** dev_ptr) {
   int dev = 0;
@@ -805,10 +809,11 @@ sg_status post_box(int** host, int** dev_ptr) {
   if (dev < 0 || dev >= 64) return fail(SG_ERR_UNSUPPORTED, "device index %d", dev);
   std::lock_guard<std::mutex> lk(g_pin_mu);
   if (!g_pin[dev]) {
-    HIPCHK(hipHostMalloc((void**)&g_pin[dev], 64 * sizeof(int), hipHostMallocMapped | hipHostMallocCoherent),
+    HIPCHK(hipHostMalloc((void**)&g_pin[dev], kPostSlots * kPostSlotInts * sizeof(int),
+                         hipHostMallocMapped | hipHostMallocCoherent),
            "hipHostMalloc");
     HIPCHK(hipHostGetDevicePointer((void**)&g_pin_dev[dev], g_pin[dev], 0), "hipHostGetDevicePointer");
-    g_pin[dev][0] = -1;
+    for (int k = 0; k < kPostSlots; ++k) g_pin[dev][k * kPostSlotInts] = -1;
   }
   *host = g_pin[dev];
   *dev_ptr = g_pin_dev[dev];
@@ -895,7 +900,8 @@ sg_status run_adaptive(const Problem& p0, const sg_weights* w, const WLayout& L,
     const float lam = std::min(1.f, std::max(0.f, 0.8f + 0.1f * std::exp(-4.f * l / Lst)));
     HIPCHK(launch_adaptive_stats(X, cur.seg, D, w->dtype, atv(w, L, base), atv(w, L, base + 1),
                                  atv(w, L, base + 4), atv(w, L, base + 5), lam, 1.f - beta, stat_flags, alpha, M + N,
-                                 (call << 8) | l, KEEP, PART, STOP, box_dev, st), "confidence");
+                                 (call << 8) | l, KEEP, PART, STOP, box_dev + kPostSlotInts * (l % kPostSlots), st),
+           "confidence");
     return SG_OK;
   };
   int exit_layer = Lst - 1;
@@ -910,8 +916,9 @@ sg_status run_adaptive(const Problem& p0, const sg_weights* w, const WLayout& L,
     const int curM = pc.M[0], curN = pc.N[0];
     const bool may_prune = width && (curM > pmin || curN > pmin);
     if (!may_prune && (s = enqueue_layer(l + 1)) != SG_OK) return s;  // speculative
-    if ((s = wait_post(box, (call << 8) | l, st)) != SG_OK) return s;
-    const int stopped = box[1], kA = box[3], kB = box[5];
+    volatile int* slot = box + kPostSlotInts * (l % kPostSlots);
+    if ((s = wait_post(slot, (call << 8) | l, st)) != SG_OK) return s;
+    const int stopped = slot[1], kA = slot[3], kB = slot[5];
     if (stopped) {
       exit_layer = l;
       break;

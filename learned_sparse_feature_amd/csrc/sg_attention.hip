@@ -13,7 +13,9 @@
 
 namespace sg {
 
-template <typename OpT, int DH, int NW>
+// PAIR1: the two segments of a single pair (each the other's partner),
+// whose entries then sit at fixed argument offsets.
+template <typename OpT, int DH, int NW, bool PAIR1>
 __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg) {
   if (a.stop && *a.stop) return;  // a later layer of a pass that has already stopped
   constexpr bool BF = std::is_same<OpT, bf16>::value;
@@ -27,11 +29,27 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
   // with 4 heads an XCD serves one head and keeps that head's K/V in its L2.
   const int H = a.heads;
   int t = blockIdx.x / H;
-  const int s = find_segment(seg, &t);
-  if (s >= seg.n_seg) return;
-  const int q0 = t * 32, nq = seg.n[s], qrow0 = seg.row0[s];
-  const int src = a.cross ? seg.partner[s] : s;
-  const int nk = seg.n[src], krow0 = seg.row0[src];
+  int nq, qrow0, nk, krow0;
+  if constexpr (PAIR1) {
+    const int n0 = seg.n[0], n1 = seg.n[1], nt0 = (n0 + 31) >> 5;
+    if (t >= nt0 + ((n1 + 31) >> 5)) return;
+    const bool s1 = t >= nt0;
+    if (s1) t -= nt0;
+    const bool k1 = a.cross ? !s1 : s1;
+    nq = s1 ? n1 : n0;
+    qrow0 = s1 ? seg.row0[1] : seg.row0[0];
+    nk = k1 ? n1 : n0;
+    krow0 = k1 ? seg.row0[1] : seg.row0[0];
+  } else {
+    const int s = find_segment(seg, &t);
+    if (s >= seg.n_seg) return;
+    nq = seg.n[s];
+    qrow0 = seg.row0[s];
+    const int src = a.cross ? seg.partner[s] : s;
+    nk = seg.n[src];
+    krow0 = seg.row0[src];
+  }
+  const int q0 = t * 32;
   const int h = blockIdx.x % H;
   const int lane = threadIdx.x & 63, w = wave_id(), hi = lane >> 5, lq = lane & 31;
   const int D = a.D, ld2 = a.ldqk;
@@ -446,15 +464,20 @@ hipError_t launch_attention(int op, int dh, const AttnArgs& a, const SegTable& s
   // four waves (one per SIMD, up to 512 registers each) split the key tiles
   constexpr int NW = 4;
   dim3 grid(tiles * heads);
+  const bool one = seg.n_seg == 2;  // a single pair
+#define SG_ATT(T, DHV)                                                                            \
+  if (one) hipLaunchKernelGGL((k_attention<T, DHV, NW, true>), grid, dim3(64 * NW), 0, st, a, seg); \
+  else hipLaunchKernelGGL((k_attention<T, DHV, NW, false>), grid, dim3(64 * NW), 0, st, a, seg)
   if (op == SG_BF16) {
-    if (dh == 64) hipLaunchKernelGGL((k_attention<bf16, 64, NW>), grid, dim3(64 * NW), 0, st, a, seg);
-    else if (dh == 16) hipLaunchKernelGGL((k_attention<bf16, 16, NW>), grid, dim3(64 * NW), 0, st, a, seg);
+    if (dh == 64) SG_ATT(bf16, 64);
+    else if (dh == 16) SG_ATT(bf16, 16);
     else return hipErrorInvalidValue;
   } else {
-    if (dh == 64) hipLaunchKernelGGL((k_attention<float, 64, NW>), grid, dim3(64 * NW), 0, st, a, seg);
-    else if (dh == 16) hipLaunchKernelGGL((k_attention<float, 16, NW>), grid, dim3(64 * NW), 0, st, a, seg);
+    if (dh == 64) SG_ATT(float, 64);
+    else if (dh == 16) SG_ATT(float, 16);
     else return hipErrorInvalidValue;
   }
+#undef SG_ATT
   return hipGetLastError();
 }
 

@@ -56,7 +56,9 @@ __device__ __forceinline__ typename Chunk<OpT, CH>::type load_chunk(const SrcT* 
 
 }  // namespace
 
-template <typename OpT, typename A0T, typename WT, typename OutT, int EPI, int BM, int BN, int PF>
+// ONE: a single problem, whose descriptor then sits at fixed argument
+// offsets (no indexed lookup ahead of the first load).
+template <typename OpT, typename A0T, typename WT, typename OutT, int EPI, int BM, int BN, int PF, bool ONE>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   constexpr bool BF = std::is_same<OpT, bf16>::value;
   constexpr int CH = BF ? 8 : 4;   // elements per 16-byte chunk
@@ -69,10 +71,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   __shared__ __attribute__((aligned(16))) OpT Ws[2][BN * PITCH];
 
   if (g.stop && *g.stop) return;  // a later layer of a pass that has already stopped
-  const int T = g.gx * g.gy * bt.n;
+  const int T = g.gx * g.gy * (ONE ? 1 : bt.n);
   const int t = (int)(blockIdx.x % 8) * ((T + 7) / 8) + (int)(blockIdx.x / 8);
   if (t >= T) return;
-  const int ty = t % g.gy, tx = (t / g.gy) % g.gx, tz = t / (g.gy * g.gx);
+  const int ty = t % g.gy, tx = (t / g.gy) % g.gx, tz = ONE ? 0 : t / (g.gy * g.gx);
   const GemmProblem P = bt.p[tz];
   const int r0 = tx * BM, n0 = ty * BN;
   if (r0 >= P.rows || n0 >= P.n_out) return;
@@ -389,12 +391,15 @@ static void gemm_go(const GemmArgs& g, const GemmBatch& b, int max_rows, int max
     a.gx = (max_rows + 127) / 128;
     a.gy = (max_n + 127) / 128;
     const int T = a.gx * a.gy * b.n;
-    hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 128, 128, 2>), dim3(8 * ((T + 7) / 8)), dim3(256), 0, st, a, b);
+    hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 128, 128, 2, false>), dim3(8 * ((T + 7) / 8)), dim3(256), 0, st, a, b);
   } else {
     a.gx = (max_rows + 63) / 64;
     a.gy = (max_n + 63) / 64;
     const int T = a.gx * a.gy * b.n;
-    hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 64, 64, 8>), dim3(8 * ((T + 7) / 8)), dim3(256), 0, st, a, b);
+    if (b.n == 1)
+      hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 64, 64, 8, true>), dim3(8 * ((T + 7) / 8)), dim3(256), 0, st, a, b);
+    else
+      hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 64, 64, 8, false>), dim3(8 * ((T + 7) / 8)), dim3(256), 0, st, a, b);
   }
 }
 

@@ -25,6 +25,7 @@
 // over the real rows) are reduced the same way, and k_sink_extract takes the
 // row argmax, the mutual check, the scores and the threshold.
 #include <algorithm>
+#include <cmath>
 
 #include "sg_device.h"
 
@@ -399,35 +400,23 @@ __global__ __launch_bounds__(256) void k_sink_cols(PairTable pt, const float* __
 // with the dustbin row/column equal to alpha2 and the base-2 marginals
 // -log2(M+N) (real rows) and log2(count of the other side) - log2(M+N)
 // (dustbin).  w_in == nullptr stands for w = 0 (the first iteration).
+// The row statistics of one sweep for one row i of Z (WHICH = 0) or ZT
+// (WHICH = 1): lane-owned float4 groups zq / wq of the row and of the
+// other side's duals (columns 4*(lane + 64 k) .. +3, loaded clamped in
+// bounds: entries past nc and the dustbin row i == nr are replaced here).
 template <int NV4>
-__global__ __launch_bounds__(256) void k_lse(const float* __restrict__ Zbase, PairTable pt,
-                                             int which, const float* __restrict__ w_in,
-                                             float* __restrict__ w_out, float alpha2,
-                                             const float* __restrict__ alpha_dev) {
-  if (alpha_dev) alpha2 = alpha_dev[0] * kLog2e;
-  const int lane = threadIdx.x & 63;
-  const int g = blockIdx.x * 4 + wave_id();
-  const int* pre = which ? pt.vpre : pt.upre;
-  const int b = find_pair(pre, pt.n_pairs, g);
-  if (b >= pt.n_pairs) return;
-  const int i = g - pre[b];
-  const int M = pt.M[b], N = pt.N[b];
-  const int nr = which ? N : M, nc = which ? M : N;
-  const float* wv = w_in ? w_in + (which ? pt.uoff[b] : pt.voff[b]) : nullptr;
-  const float* row = which ? Zbase + pt.zt_off[b] + (size_t)i * ld4(M) : Zbase + pt.z_off[b] + (size_t)i * ld4(N);
-  // every lane owns NV4 float4 groups of the row: columns 4*(lane + 64 k) .. +3
+__device__ __forceinline__ float lse_row(const float4 (&zq)[NV4], const float4 (&wq)[NV4], float wd, float alpha2,
+                                         int i, int nr, int nc, int lane) {
   float x[NV4][4];
 #pragma unroll
   for (int k = 0; k < NV4; ++k) {
     const int j = 4 * (lane + 64 * k);
-    float4 z = make_float4(alpha2, alpha2, alpha2, alpha2);  // the dustbin row
-    if (i < nr && j < nc) z = *reinterpret_cast<const float4*>(row + j);
-    const float4 w = (wv && j < nc) ? *reinterpret_cast<const float4*>(wv + j) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) x[k][c] = j + c < nc ? f4c(z, c) + f4c(w, c) : -INFINITY;
+    for (int c = 0; c < 4; ++c)
+      x[k][c] = j + c < nc ? (i < nr ? f4c(zq[k], c) : alpha2) + f4c(wq[k], c) : -INFINITY;
   }
   // the dustbin column (j = nc) is alpha for every row
-  const float xd = alpha2 + (wv ? wv[nc] : 0.f);
+  const float xd = alpha2 + wd;
   float mx = xd;
 #pragma unroll
   for (int k = 0; k < NV4; ++k)
@@ -440,10 +429,74 @@ __global__ __launch_bounds__(256) void k_lse(const float* __restrict__ Zbase, Pa
 #pragma unroll
     for (int c = 0; c < 4; ++c) sum += exp2_fast(x[k][c] - mx);
   sum = wave_sum(sum);
+  return mx + log2_fast(sum);
+}
+
+// Loads of lse_row's operands, unconditional at a real row and column
+// clamped in bounds (the dustbin row reads the last real row), so that all
+// of them are in flight together.  row: the row's first entry; wv: the
+// duals (nullptr: zero).
+template <int NV4>
+__device__ __forceinline__ void lse_loads(const float* row, const float* wv, int nr, int nc, int lane,
+                                          float4 (&zq)[NV4], float4 (&wq)[NV4]) {
+  const int ldz = ld4(nc);
+#pragma unroll
+  for (int k = 0; k < NV4; ++k) zq[k] = wq[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (nc <= 0) return;  // (wave-uniform conditions)
+#pragma unroll
+  for (int k = 0; k < NV4; ++k) {
+    const int jc = min(4 * (lane + 64 * k), ldz - 4);
+    if (nr > 0) zq[k] = *reinterpret_cast<const float4*>(row + jc);
+    if (wv) wq[k] = *reinterpret_cast<const float4*>(wv + jc);
+  }
+}
+
+// WHICH: the sweep (0: rows of Z, 1: rows of ZT), fixed at compile time so
+// that the table entries sit at fixed offsets once the pair is known.
+template <int NV4, int WHICH>
+__global__ __launch_bounds__(256) void k_lse(const float* __restrict__ Zbase, PairTable pt,
+                                             const float* __restrict__ w_in, float* __restrict__ w_out,
+                                             float alpha2, const float* __restrict__ alpha_dev) {
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + wave_id();
+  const int* pre = WHICH ? pt.vpre : pt.upre;
+  const int b = find_pair(pre, pt.n_pairs, g);
+  if (b >= pt.n_pairs) return;
+  const int i = g - pre[b];
+  const int M = pt.M[b], N = pt.N[b];
+  const int nr = WHICH ? N : M, nc = WHICH ? M : N;
+  const float* wv = w_in ? w_in + (WHICH ? pt.uoff[b] : pt.voff[b]) : nullptr;
+  float4 zq[NV4], wq[NV4];
+  lse_loads<NV4>(Zbase + (WHICH ? pt.zt_off[b] : pt.z_off[b]) + (size_t)max(min(i, nr - 1), 0) * ld4(nc), wv, nr, nc,
+                 lane, zq, wq);
+  const float wd = wv ? wv[nc] : 0.f;
+  if (alpha_dev) alpha2 = alpha_dev[0] * kLog2e;  // needed only once the row loads are in flight
+  const float l = lse_row<NV4>(zq, wq, wd, alpha2, i, nr, nc, lane);
   if (lane == 0) {
     const float lm = (i < nr ? 0.f : log2f((float)nc)) - log2f((float)(M + N));
-    w_out[(which ? pt.voff[b] : pt.uoff[b]) + i] = lm - (mx + log2_fast(sum));
+    w_out[(WHICH ? pt.voff[b] : pt.uoff[b]) + i] = lm - l;
   }
+}
+
+// The same sweep for a single pair, with its sizes and offsets as plain
+// arguments: every scalar the row loads need arrives in one round of
+// argument loads (no pair search, no table lookups ahead of them).
+// Z: the pair's Z or ZT; wv / w_out: the duals read / written (offsets
+// applied); nr: rows (the dustbin row is nr); nc: columns; lmn = log2(M+N).
+template <int NV4>
+__global__ __launch_bounds__(256) void k_lse_one(const float* __restrict__ Z, const float* __restrict__ wv,
+                                                 float* __restrict__ w_out, int nr, int nc, float alpha2,
+                                                 const float* __restrict__ alpha_dev, float lm_real,
+                                                 float lm_dust) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave_id();
+  if (i > nr) return;
+  float4 zq[NV4], wq[NV4];
+  lse_loads<NV4>(Z + (size_t)max(min(i, nr - 1), 0) * ld4(nc), wv, nr, nc, lane, zq, wq);
+  const float wd = wv ? wv[nc] : 0.f;
+  if (alpha_dev) alpha2 = alpha_dev[0] * kLog2e;
+  const float l = lse_row<NV4>(zq, wq, wd, alpha2, i, nr, nc, lane);
+  if (lane == 0) w_out[i] = (i < nr ? lm_real : lm_dust) - l;
 }
 
 // Column argmax over the real rows (argmax_i Z2_ij + u_i, lowest index on
@@ -669,8 +722,29 @@ hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const floa
   for (int b = 0; b < pt.n_pairs; ++b) nc = std::max(nc, which ? pt.M[b] : pt.N[b]);
   const int nv4 = sink_nv4(nc);
   dim3 grid((total_rows + 3) / 4);
-#define SG_LSE(NV) \
-  if (nv4 == NV) { hipLaunchKernelGGL(k_lse<NV>, grid, dim3(256), 0, st, Z, pt, which, w_in, w_out, alpha2, alpha_dev); return hipGetLastError(); }
+  if (pt.n_pairs == 1) {
+    const int M = pt.M[0], N = pt.N[0], nr = which ? N : M;
+    const float* zp = Z + (which ? pt.zt_off[0] : pt.z_off[0]);
+    const float* wv = w_in ? w_in + (which ? pt.uoff[0] : pt.voff[0]) : nullptr;
+    float* wo = w_out + (which ? pt.voff[0] : pt.uoff[0]);
+    // the same single-precision logarithms as the pair-table kernel
+    const float lmn = std::log2((float)(M + N));
+    const float lr = 0.f - lmn, ld = std::log2((float)nc) - lmn;
+#define SG_LSE(NV)                                                                                                  \
+    if (nv4 == NV) {                                                                                                \
+      hipLaunchKernelGGL(k_lse_one<NV>, grid, dim3(256), 0, st, zp, wv, wo, nr, nc, alpha2, alpha_dev, lr, ld);     \
+      return hipGetLastError();                                                                                     \
+    }
+    SG_LSE(1) SG_LSE(2) SG_LSE(4) SG_LSE(8) SG_LSE(16)
+#undef SG_LSE
+    return hipErrorInvalidValue;
+  }
+#define SG_LSE(NV)                                                                                            \
+  if (nv4 == NV) {                                                                                            \
+    if (which) hipLaunchKernelGGL((k_lse<NV, 1>), grid, dim3(256), 0, st, Z, pt, w_in, w_out, alpha2, alpha_dev); \
+    else hipLaunchKernelGGL((k_lse<NV, 0>), grid, dim3(256), 0, st, Z, pt, w_in, w_out, alpha2, alpha_dev);       \
+    return hipGetLastError();                                                                                 \
+  }
   SG_LSE(1) SG_LSE(2) SG_LSE(4) SG_LSE(8) SG_LSE(16)
 #undef SG_LSE
   return hipErrorInvalidValue;
