@@ -17,6 +17,9 @@ namespace sg {
 // whose entries then sit at fixed argument offsets.
 template <typename OpT, int DH, int NW, bool PAIR1>
 __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg) {
+  if constexpr (PAIR1)
+    args_in_sgprs(a.qk, a.vt, a.ks, a.vs, a.D, a.ldqk, a.ldvt, a.cross, a.heads, a.scale2, a.stop, seg.n[0],
+                  seg.n[1], seg.row0[0], seg.row0[1]);
   if (a.stop && *a.stop) return;  // a later layer of a pass that has already stopped
   constexpr bool BF = std::is_same<OpT, bf16>::value;
   constexpr int NCB = (DH + 31) / 32;        // 32-channel blocks of the output

@@ -121,6 +121,20 @@ __device__ __forceinline__ int find_segment(const SegTable& seg, int* t) {
   return s;
 }
 
+// Pins kernel arguments in scalar registers at this point, so that their
+// loads are issued together, in one round, ahead of a kernel's first early
+// exit.  (Left alone, the compiler sinks each load past the exits that
+// precede its first use; every round then waits on a miss, since the
+// argument block of every launch is new to the scalar cache.)
+template <class T>
+__device__ __forceinline__ void arg_in_sgprs(const T& v) {
+  asm volatile("" ::"s"(v));
+}
+template <class... T>
+__device__ __forceinline__ void args_in_sgprs(const T&... v) {
+  (arg_in_sgprs(v), ...);
+}
+
 // Pair of a flattened row index given prefix sums `pre` of per-pair rows.
 __device__ __forceinline__ int find_pair(const int* pre, int n_pairs, int g) {
   int b = 0;

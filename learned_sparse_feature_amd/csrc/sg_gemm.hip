@@ -70,6 +70,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   __shared__ __attribute__((aligned(16))) OpT As[2][BM * PITCH];
   __shared__ __attribute__((aligned(16))) OpT Ws[2][BN * PITCH];
 
+  if constexpr (ONE)
+    args_in_sgprs(g.A0, g.A1, g.W, g.lda0, g.lda1, g.ldw, g.K0, g.K, g.gx, g.gy, g.stop, bt.p[0].a_row0,
+                  bt.p[0].w_row0, bt.p[0].rows, bt.p[0].n_out);
   if (g.stop && *g.stop) return;  // a later layer of a pass that has already stopped
   const int T = g.gx * g.gy * (ONE ? 1 : bt.n);
   const int t = (int)(blockIdx.x % 8) * ((T + 7) / 8) + (int)(blockIdx.x / 8);
