@@ -39,14 +39,17 @@ def log(*a):
 
 def gemm_flops(cfg, M, N, cross="standard"):
     """Algorithmic flops of every GEMM launch of one pass, in launch order,
-    with the operand dtype of each (real rows only).  Bidirectional cross
-    stages project qk | v (2D outputs) instead of q | k | v."""
+    with the operand dtype of each (real rows only): the merge fold of all
+    2L stages (W1[:, D:] Wm, 2D x D x D per stage), then per stage the QKV
+    projection, the first MLP layer over [x || a] (merge folded in) and the
+    second with the residual.  Bidirectional cross stages project qk | v (2D
+    outputs) instead of q | k | v."""
     R, D = M + N, cfg.D
-    out = []
+    out = [(cfg.dtype, 2.0 * 2 * cfg.L * 2 * D * D * D)]
     for s in range(2 * cfg.L):
         nqkv = 2 if (s % 2 == 1 and cross == "bidirectional") else 3
-        out += [(cfg.dtype, 2.0 * R * D * nqkv * D), (cfg.dtype, 2.0 * R * D * D),
-                (cfg.dtype, 2.0 * R * 2 * D * 2 * D), (cfg.dtype, 2.0 * R * 2 * D * D)]
+        out += [(cfg.dtype, 2.0 * R * D * nqkv * D), (cfg.dtype, 2.0 * R * 2 * D * 2 * D),
+                (cfg.dtype, 2.0 * R * 2 * D * D)]
     out.append((cfg.dtype, 2.0 * R * D * D))     # final projection
     out.append(("f32", 2.0 * M * N * D))         # scores
     return out
@@ -207,31 +210,32 @@ def batch_kernels(args, cfg, sg, np, torch, bstep, B, M, N, ds):
             fl = gemm_flops(cfg, M, N, args.cross)
             assert nl == len(fl), ("batched GEMM launches", nl, len(fl))
             bf = [(f * B, d) for (dt_, f), d in zip(fl, dur_us) if dt_ == "bf16"]
-            ach = sum(f for f, _ in bf) / sum(d for _, d in bf) / 1e6
+            ach = float(sum(f for f, _ in bf) / sum(d for _, d in bf) / 1e6)
             r.update(achieved_TFLOPs_bf16=round(ach, 1), frac_mfma=round(ach / PEAK["bf16_TFLOPs"], 4))
-            per = {"qkv": dur_us[0:8 * cfg.L:4], "merge": dur_us[1:8 * cfg.L:4], "mlp1": dur_us[2:8 * cfg.L:4],
-                   "mlp2_residual": dur_us[3:8 * cfg.L:4]}
-            fls = {"qkv": fl[0][1], "merge": fl[1][1], "mlp1": fl[2][1], "mlp2_residual": fl[3][1]}
+            e = 1 + 6 * cfg.L
+            per = {"qkv": dur_us[1:e:3], "mlp1_merge_folded": dur_us[2:e:3], "mlp2_residual": dur_us[3:e:3]}
+            fls = {"qkv": fl[1][1] * B, "mlp1_merge_folded": fl[2][1] * B, "mlp2_residual": fl[3][1] * B}
             r["per_projection"] = {k: {"avg_us": round(float(v.mean()), 2),
-                                       "frac_mfma": round(fls[k] * B / (float(v.mean()) * 1e6) / PEAK["bf16_TFLOPs"], 4)}
+                                       "frac_mfma": round(fls[k] / (float(v.mean()) * 1e6) / PEAK["bf16_TFLOPs"], 4)}
                                    for k, v in per.items()}
+            r["merge_fold_us"] = round(float(dur_us[0]), 2)
         elif name == "attention":
             fl = attention_flops(cfg, M, N)
             assert nl == len(fl), ("batched attention launches", nl, len(fl))
-            ach = sum(fl) * B / dur_us.sum() / 1e6
+            ach = float(sum(fl) * B / dur_us.sum() / 1e6)
             r.update(achieved_TFLOPs=round(ach, 1), frac_mfma=round(ach / PEAK["bf16_TFLOPs"], 4))
         elif ds:
             r["kernel"] = "k_ds_stats"
             byt = ds_bytes(M, N, cfg.D)[0] * B
-            r.update(achieved_GBps=round(byt / dur_us.sum() / 1e3, 1),
-                     frac_hbm=round(byt / dur_us.sum() / 1e3 / PEAK["hbm_GBps"], 4))
+            r.update(achieved_GBps=round(float(byt / dur_us.sum() / 1e3), 1),
+                     frac_hbm=round(float(byt / dur_us.sum() / 1e3) / PEAK["hbm_GBps"], 4))
         else:
             # one read of every pair's couplings per iteration, over the time
             # of the iteration's launches (row pass + column reduction)
             byt = 4.0 * (M + 1) * (N + 1) * B * cfg.T
             r.update(bytes_per_iteration=4.0 * (M + 1) * (N + 1) * B,
-                     achieved_GBps=round(byt / dur_us.sum() / 1e3, 1),
-                     frac_hbm=round(byt / dur_us.sum() / 1e3 / PEAK["hbm_GBps"], 4))
+                     achieved_GBps=round(float(byt / dur_us.sum() / 1e3), 1),
+                     frac_hbm=round(float(byt / dur_us.sum() / 1e3) / PEAK["hbm_GBps"], 4))
         res[name] = r
     return res
 
@@ -393,8 +397,8 @@ def main():
         # sum of their bracketed times exceeds the stage time by the bracketing
         # cost of 10L launches.
         nk = "ds_stats" if ds else "sinkhorn"
-        n_gnn = 10 * cfg.L
-        bracketed_gnn_ms = float(durs["attention"].sum() + durs["gemm"][:8 * cfg.L].sum())
+        n_gnn = 8 * cfg.L + 1  # 2L attention launches, the merge fold and 6L GEMMs
+        bracketed_gnn_ms = float(durs["attention"].sum() + durs["gemm"][:6 * cfg.L + 1].sum())
         over = max(0.0, (bracketed_gnn_ms - stages["gnn"]) * 1e3 / n_gnn)
         # the double-softmax head has a single statistics launch, whose stage
         # time holds the events' own latency: its bracketed time less the

@@ -155,12 +155,12 @@ sg_status check_weights(const sg_weights* w, WLayout* out) {
 // ---------------------------------------------------------- workspace layout
 
 struct WsLayout {
-  size_t X, XB, H0, H1, QK, VT, KS, VS, MB, M2, HB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, ROPE, ADAPT, total;
+  size_t X, XB, H0, H1, QK, VT, KS, VS, MB, HB, WF, WFB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, ROPE, ADAPT, total;
   int ldvt, ldqk;
 };
 
 WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, long pf, long pd, long uf, long vf,
-                       long nb, long ropef = 0, bool adaptive = false) {
+                       long nb, long ropef = 0, bool adaptive = false, long nstage = 0) {
   WsLayout L;
   // row strides are kept off powers of two (+64 / +16 bytes) so that the
   // strided accesses of the attention kernel spread over the L2 channels
@@ -180,8 +180,10 @@ WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, l
   L.KS = take(bf ? (size_t)R * D * os : 0);
   L.VS = take(bf ? (size_t)R * D * os : 0);
   L.MB = take((size_t)R * D * os);
-  L.M2 = take((size_t)R * D * os);
   L.HB = take((size_t)R * 2 * D * os);
+  // per stage: the update MLP's first layer with the merge projection folded in
+  L.WF = take((size_t)nstage * 4 * D * D * os);
+  L.WFB = take((size_t)nstage * 2 * D * os);
   L.F = take((size_t)R * D * 4);
   L.Z = take((size_t)zf * 4);
   L.ZT = take((size_t)ztf * 4);
@@ -206,7 +208,7 @@ WsLayout ws_layout(const sg_weights* w, long R, long zf, long ztf, long pf, long
   int maxw = 0;
   for (int i = 0; i < w->n_enc; ++i) maxw = std::max(maxw, w->enc[i]);
   return ws_layout_raw(w->D, w->dtype == SG_BF16 ? 2 : 4, maxw, R, zf, ztf, pf, pd, uf, vf, nb,
-                       w->rope ? R * (w->D / w->H / 2) : 0, w->adaptive != 0);
+                       w->rope ? R * (w->D / w->H / 2) : 0, w->adaptive != 0, 2L * w->L_max);
 }
 
 // ----------------------------------------------------------- library workspace
@@ -412,7 +414,34 @@ sg_status run_rope_table(const Problem& p, const Plan& pl, const sg_weights* w, 
   return SG_OK;
 }
 
-// Stages [s0, s1) in place on X (compact rows of every image of the plan).
+// Folds the merge projection of stages [s0, s1) into their update MLPs'
+// first layers (workspace WF / WFB, indexed by stage).  Every call redoes
+// it, so that weights changed in place between calls take effect.
+sg_status run_fold(const sg_weights* w, const WLayout& L, int s0, int s1, char* ws, const WsLayout& wl, Timer& tm,
+                   hipStream_t st) {
+  const int D = w->D;
+  const size_t os = w->dtype == SG_BF16 ? 2 : 4;
+  for (int c0 = s0; c0 < s1; c0 += kMaxFold) {
+    FoldArgs f;
+    memset(&f, 0, sizeof(f));
+    f.D = D;
+    f.n = std::min(kMaxFold, s1 - c0);
+    for (int i = 0; i < f.n; ++i) {
+      const int base = L.stage_first + kPerStage * (c0 + i);
+      f.wm[i] = atv(w, L, base + 2);
+      f.bm[i] = atv(w, L, base + 3);
+      f.w1[i] = atv(w, L, base + 4);
+      f.b1[i] = atv(w, L, base + 5);
+    }
+    f.wf = ws + wl.WF + (size_t)c0 * 4 * D * D * os;
+    f.bf = ws + wl.WFB + (size_t)c0 * 2 * D * os;
+    HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_fold_merge(w->dtype, f, st); }), "merge fold");
+  }
+  return SG_OK;
+}
+
+// Stages [s0, s1) in place on X (compact rows of every image of the plan);
+// the merge projections of these stages must have been folded (run_fold).
 // xb_valid: the bf16 copy XB of the states is current (the encoder writes
 // it); otherwise bf16 networks refresh it first.
 sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0, int s1, char* ws,
@@ -428,8 +457,8 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
   void* QK = ws + wl.QK;
   void* VT = ws + wl.VT;
   void* MB = ws + wl.MB;
-  void* M2 = ws + wl.M2;
   void* HB = ws + wl.HB;
+  const size_t os = op == SG_BF16 ? 2 : 4;
   const float log2e = 1.4426950408889634f;
   for (int s = s0; s < s1; ++s) {
     const int base = L.stage_first + kPerStage * s;
@@ -463,22 +492,13 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       a.scale2 = log2e / sqrtf((float)dh);
       HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_attention(op, dh, a, pl.seg, w->H, st); }), "attention");
     }
-    // merge projection
+    // h = ReLU(W_1 [x || m] + b_1) with m = W_m a + b_m folded in (run_fold):
+    // h = ReLU(W_f [x || a] + b_f), a = the attention output
     {
       GemmArgs g;
       memset(&g, 0, sizeof(g));
-      g.A0 = MB; g.lda0 = D; g.K0 = D; g.K = D;
-      g.W = atv(w, L, base + 2); g.ldw = D; g.bias = atv(w, L, base + 3);
-      g.C = M2; g.stop = stop;
-      GemmBatch b = single(R, D, D);
-      HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, op == SG_F32, op, op == SG_F32, EPI_BIAS, g, b, R, D, st); }), "merge GEMM");
-    }
-    // h = ReLU(W_1 [x || m] + b_1)
-    {
-      GemmArgs g;
-      memset(&g, 0, sizeof(g));
-      g.A0 = XB ? XB : X; g.lda0 = D; g.K0 = D; g.A1 = M2; g.lda1 = D; g.K = 2 * D;
-      g.W = atv(w, L, base + 4); g.ldw = 2 * D; g.bias = atv(w, L, base + 5);
+      g.A0 = XB ? XB : X; g.lda0 = D; g.K0 = D; g.A1 = MB; g.lda1 = D; g.K = 2 * D;
+      g.W = ws + wl.WF + (size_t)s * 4 * D * D * os; g.ldw = 2 * D; g.bias = ws + wl.WFB + (size_t)s * 2 * D * os;
       g.C = HB; g.stop = stop;
       GemmBatch b = single(R, 2 * D, 2 * D);
       HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(op, XB == nullptr, op, op == SG_F32, EPI_RELU, g, b, R, 2 * D, st); }),
@@ -759,6 +779,7 @@ sg_status enqueue_full(const Problem& p, const Plan& pl, const WsLayout& wl, cha
   if ((s = run_encoder(p, pl, w, L, ws, wl, tm, st)) != SG_OK) return s;
   if (w->rope && (s = run_rope_table(p, pl, w, L, ws, wl, st)) != SG_OK) return s;
   tm.stage(SG_EV_ENCODED);
+  if ((s = run_fold(w, L, 0, 2 * Lst, ws, wl, tm, st)) != SG_OK) return s;
   if ((s = run_gnn(pl, w, L, 0, 2 * Lst, ws, wl, o ? o->flags : 0, tm, st, nullptr, true)) != SG_OK) return s;
   tm.stage(SG_EV_GNN);
   float* F = reinterpret_cast<float*>(ws + wl.F);
@@ -883,6 +904,7 @@ sg_status run_adaptive(const Problem& p0, const sg_weights* w, const WLayout& L,
   HIPCHK(launch_iota_rows(pl.seg, R0, IND, st), "row index");
   if (w->rope && (s = run_rope_table(p0, pl, w, L, ws, wl, st, IND)) != SG_OK) return s;
   tm.stage(SG_EV_ENCODED);
+  if ((s = run_fold(w, L, 0, 2 * Lst, ws, wl, tm, st)) != SG_OK) return s;
   const int call = ++g_adaptive_calls & 0xFFFFF;
   const int stat_flags = (depth ? 1 : 0) | (width ? 2 : 0);
   Problem pc = p0;
@@ -1187,6 +1209,7 @@ sg_status sg_stage_gnn_pos(float* xA, const float* posA, int32_t M, float* xB, c
          "zero padding B");
   if (weights->rope && (s = run_rope_table(p, pl, weights, WL, ws, wl, st)) != SG_OK) return s;
   Timer tm{opts, st};
+  if ((s = run_fold(weights, WL, s0, s1, ws, wl, tm, st)) != SG_OK) return s;
   if ((s = run_gnn(pl, weights, WL, s0, s1, ws, wl, opts ? opts->flags : 0, tm, st)) != SG_OK) return s;
   if (M) HIPCHK(hipMemcpyAsync(xA, X, M * rb, hipMemcpyDeviceToDevice, st), "copy xA back");
   if (N) HIPCHK(hipMemcpyAsync(xB, X + (size_t)pl.seg.row0[1] * weights->D, N * rb, hipMemcpyDeviceToDevice, st), "copy xB back");

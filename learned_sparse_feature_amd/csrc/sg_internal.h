@@ -127,6 +127,23 @@ hipError_t launch_gemm(int op_dtype, int a0_is_f32, int w_dtype, int out_is_f32,
                        hipStream_t st);
 // y (bf16) = x (fp32) rounded to nearest even, n a multiple of 4.
 hipError_t launch_to_bf16(const float* x, void* y, int n, hipStream_t st);
+
+// Merge projection folded into the update MLP's first layer, per stage:
+// W1 [2D][2D] (input [x || m]), m = Wm a + bm  =>  W1 [x || m] + b1 =
+// Wf [x || a] + bf with Wf = [W1[:, :D] | W1[:, D:] Wm], bf = b1 + W1[:, D:] bm.
+// Up to kMaxFold stages per launch; wf / bf: [n][2D][2D] / [n][2D] in the
+// weights' type.
+constexpr int kMaxFold = 32;
+struct FoldArgs {
+  const void* w1[kMaxFold];
+  const void* b1[kMaxFold];
+  const void* wm[kMaxFold];
+  const void* bm[kMaxFold];
+  void* wf;
+  void* bf;
+  int D, n;
+};
+hipError_t launch_fold_merge(int w_dtype, const FoldArgs& f, hipStream_t st);
 hipError_t launch_attention(int op_dtype, int dh, const AttnArgs& a, const SegTable& seg,
                             int heads, hipStream_t st);
 // alpha_dev (device pointer to the dustbin score) overrides alpha2 when non-null.
