@@ -1,10 +1,12 @@
 // Multi-head attention of one GNN stage (self or cross) on MFMA (gfx950).
 //
 // One workgroup = 32 queries of one image and one head.  Its NW waves split
-// the 32-key tiles of the source image round robin; each wave keeps an
-// online softmax (running max, running sum, unnormalised output) in
-// registers and prefetches its next K/V tile while it works on the current
-// one.  S^T = K Q^T is formed so that every lane owns one query column: the
+// the key tiles of the source image round robin; each wave keeps an online
+// softmax (running max, running sum, unnormalised output) in registers.
+// With NW = 8 (two waves per SIMD, at most 256 registers each) a wave holds
+// one K/V tile at a time and the other wave of its SIMD covers the load
+// latency; with fewer waves each prefetches its next tile while it works on
+// the current one.  S^T = K Q^T is formed so that every lane owns one query column: the
 // softmax statistics of a query then need only the lane and its partner
 // lane l^32.  P never leaves registers: its accumulator layout is reused as
 // the B operand of O^T = V^T P^T, with V read from the transposed copy VT.
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
   // flight); the last one or two rounds drain the ring.
   const int ntk = (nk + 32 * KB - 1) / (32 * KB);
   const int mine = ntk > w ? (ntk - w + NW - 1) / NW : 0;
-  constexpr int PT = 2;
+  constexpr int PT = NW >= 8 ? 1 : 2;
   if (mine > 0) {
     KT kr[PT][KB][QS];
     VT vr[PT][KB][NV];
@@ -464,8 +466,8 @@ hipError_t launch_attention(int op, int dh, const AttnArgs& a, const SegTable& s
     hipLaunchKernelGGL((k_attention_wide<64>), dim3(wide_tiles * heads), dim3(256), 0, st, a, seg);
     return hipGetLastError();
   }
-  // four waves (one per SIMD, up to 512 registers each) split the key tiles
-  constexpr int NW = 4;
+  // eight waves (two per SIMD) split the key tiles
+  constexpr int NW = 8;
   dim3 grid(tiles * heads);
   const bool one = seg.n_seg == 2;  // a single pair
 #define SG_ATT(T, DHV)                                                                            \
