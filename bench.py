@@ -431,7 +431,7 @@ def main():
             per_launch = norm_work[0]
             ach = per_launch / (kernels[dom]["avg_us"] * 1e-6) / 1e9
             tr = profiled_traffic("k_lse") if args.sinkhorn != "one" else None
-            roofline = {"kernel": "k_lse (Sinkhorn sweep over Z or Z^T)", "bound": "hbm", "achieved": round(ach, 1),
+            roofline = {"kernel": "k_lse_one (Sinkhorn sweep over Z or Z^T, one pair)", "bound": "hbm", "achieved": round(ach, 1),
                         "peak": PEAK["hbm_GBps"], "unit": "GB/s", "frac": round(ach / PEAK["hbm_GBps"], 4),
                         "traffic": None if tr is None else round(tr), "algorithmic_bytes_per_launch": per_launch,
                         "avg_launch_us": kernels[dom]["avg_us"]}
