@@ -184,7 +184,7 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, S[kb][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = half_swap_max(tmax);
     const float m_new = fmaxf(m_run, tmax * a.scale2);
     // rescale the running output only when some query's maximum moved
     if (__ballot(m_new != m_run)) {
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
       if (r0 + PT + j < mine) process(kr[j], vr[j], w + NW * (r0 + PT + j));
   }
 
-  l_run += __shfl_xor(l_run, 32);
+  l_run = half_swap_sum(l_run);
   if (hi == 0) {
     sm_m[w][lq] = m_run;
     sm_l[w][lq] = l_run;
@@ -371,54 +371,67 @@ __global__ __launch_bounds__(256) void k_attention_wide(AttnArgs a, SegTable seg
   gload(0);
   sstore(0);
   __syncthreads();
+  // Both 32-key blocks of a tile are taken together: two independent QK^T
+  // chains, one maximum, one rescale of O and 32 exponentials per lane.
+  static_assert(BKEY == 64, "two 32-key blocks per tile");
   for (int kt = 0; kt < ntk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < ntk) gload((kt + 1) * BKEY);
+    const int k0 = kt * BKEY;
+    const bf16* tb0 = &Ts[cur][lane * 8];
+    const bf16* tb1 = tb0 + (KBLK + VBLK) * 512;
+    f32x16 S0 = zero16(), S1 = zero16();
 #pragma unroll
-    for (int kb = 0; kb < BKEY / 32; ++kb) {
-      const int k0 = kt * BKEY + kb * 32;
-      if (k0 >= nk) break;
-      const bf16* tb = &Ts[cur][kb * (KBLK + VBLK) * 512 + lane * 8];
-      f32x16 S = zero16();
-#pragma unroll
-      for (int i = 0; i < DH / 16; ++i) S = mfma(*reinterpret_cast<const bf16x8*>(tb + i * 512), Qr[i], S);
-      float e[16], tmax = -INFINITY;
-      if (k0 + 32 <= nk) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          e[i] = S[i] * a.scale2;
-          tmax = fmaxf(tmax, e[i]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kk = k0 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          e[i] = kk < nk ? S[i] * a.scale2 : -INFINITY;
-          tmax = fmaxf(tmax, e[i]);
-        }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float corr = exp2_fast(m_run - m_new);
-      float psum = 0.f;
-      bf16x8 pb[2];
+    for (int i = 0; i < DH / 16; ++i) {
+      S0 = mfma(*reinterpret_cast<const bf16x8*>(tb0 + i * 512), Qr[i], S0);
+      S1 = mfma(*reinterpret_cast<const bf16x8*>(tb1 + i * 512), Qr[i], S1);
+    }
+    float e[2][16], tmax = -INFINITY;
+    if (k0 + BKEY <= nk) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2_fast(e[i] - m_new);
+        e[0][i] = S0[i] * a.scale2;
+        e[1][i] = S1[i] * a.scale2;
+        tmax = fmaxf(tmax, fmaxf(e[0][i], e[1][i]));
+      }
+    } else {  // keys past the image (a block past it re-read the last block)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = k0 + 8 * (i >> 2) + 4 * hi + (i & 3);
+        e[0][i] = kk < nk ? S0[i] * a.scale2 : -INFINITY;
+        e[1][i] = kk + 32 < nk ? S1[i] * a.scale2 : -INFINITY;
+        tmax = fmaxf(tmax, fmaxf(e[0][i], e[1][i]));
+      }
+    }
+    tmax = half_swap_max(tmax);
+    const float m_new = fmaxf(m_run, tmax);
+    const float corr = exp2_fast(m_run - m_new);
+    float psum = 0.f;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2_fast(e[b][i] - m_new);
         psum += p;
-        pb[i >> 3][i & 7] = (bf16)p;
+        pb[b][i >> 3][i & 7] = (bf16)p;
       }
-      l_run = l_run * corr + psum;
-      m_run = m_new;
-      if (__ballot(corr != 1.f)) {
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+    if (__ballot(corr != 1.f)) {
 #pragma unroll
-        for (int c = 0; c < DH / 32; ++c)
+      for (int c = 0; c < DH / 32; ++c)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) O[c][i] *= corr;
-      }
-      // values of keys past the image are zeroed (their P is 0, but padding
-      // rows may hold anything a caller staged there)
-      const bool vtail = k0 + 32 > nk;
+        for (int i = 0; i < 16; ++i) O[c][i] *= corr;
+    }
+    // values of keys past the image are zeroed (their P is 0, but padding
+    // rows may hold anything a caller staged there)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int kb0 = k0 + 32 * b;
+      if (kb0 >= nk) break;
+      const bool vtail = kb0 + 32 > nk;
+      const bf16* tb = b ? tb1 : tb0;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -427,16 +440,16 @@ __global__ __launch_bounds__(256) void k_attention_wide(AttnArgs a, SegTable seg
           if (vtail) {
 #pragma unroll
             for (int x = 0; x < 8; ++x)
-              if (k0 + 16 * j + 8 * (x >> 2) + 4 * hi + (x & 3) >= nk) va[x] = (bf16)0.f;
+              if (kb0 + 16 * j + 8 * (x >> 2) + 4 * hi + (x & 3) >= nk) va[x] = (bf16)0.f;
           }
-          O[cb] = mfma(va, pb[j], O[cb]);
+          O[cb] = mfma(va, pb[b][j], O[cb]);
         }
     }
     if (kt + 1 < ntk) sstore(cur ^ 1);
     __syncthreads();
   }
 
-  l_run += __shfl_xor(l_run, 32);
+  l_run = half_swap_sum(l_run);
   if (qvalid) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     bf16* out = reinterpret_cast<bf16*>(a.out) + (size_t)(qrow0 + qi) * D + h * DH;

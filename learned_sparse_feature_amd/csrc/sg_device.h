@@ -68,6 +68,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 
+// The value of lane l ^ 32 combined with the lane's own, in every lane:
+// v_permlane32_swap exchanges the two 32-lane halves in one VALU
+// instruction (a cross-lane shuffle would go through the LDS crossbar).
+// Applied to (v, v) it returns (lower half of v in both halves, upper half
+// in both), so op of the two is op(v[l % 32], v[l % 32 + 32]).
+__device__ __forceinline__ float half_swap_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // (value, index) argmax over the wave: the larger value wins, the lower
 // index among equal values.  Result in every lane.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {

@@ -453,7 +453,7 @@ __global__ __launch_bounds__(64) void k_fold_merge(FoldArgs f) {
 #pragma unroll
     for (int t = 0; t < CH; ++t) acc = fmaf((float)a[t], (float)b[t], acc);
   }
-  acc += __shfl_xor(acc, 32);
+  acc = half_swap_sum(acc);
   if (hi == 0) static_cast<T*>(f.bf)[(size_t)s * D2 + n0 + lr] = (T)((float)b1[n0 + lr] + acc);
 }
 
