@@ -300,7 +300,7 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
 // tile is in flight while the current one is consumed) and shared by the
 // four waves, which read their MFMA operands as one 16-byte LDS load each.
 template <int DH>
-__global__ __launch_bounds__(256) void k_attention_wide(AttnArgs a, SegTable seg) {
+__global__ __launch_bounds__(256, 3) void k_attention_wide(AttnArgs a, SegTable seg) {
   if (a.stop && *a.stop) return;  // a later layer of a pass that has already stopped
   constexpr int BQ = 128, BKEY = 64;
   constexpr int KBLK = DH / 16, VBLK = DH / 16;  // 512-element blocks per 32 keys (K: dim chunks; V: 2 j x DH/32)
