@@ -54,6 +54,28 @@ __device__ __forceinline__ typename Chunk<OpT, CH>::type load_chunk(const SrcT* 
   return v;
 }
 
+// Stores one 32 x 32 accumulator block (value(e) for accumulator e of this
+// lane: row 8 (e / 4) + 4 (lane / 32) + e % 4, column lane % 32) as bf16
+// into row-major dst (row stride ld) at rows r0.., columns c0.. through the
+// wave-private LDS tile tt [32][40]: two 16-byte stores along rows per lane
+// instead of sixteen 2-byte ones.  Rows at or past `rows` are not stored.
+// Wave-level only: LDS operations of a wave complete in order.
+template <class F>
+__device__ __forceinline__ void store_block_bf16(bf16* tt, int lane, F value, bf16* dst, size_t ld, int r0, int c0,
+                                                 int rows) {
+  const int nl = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) tt[(8 * (e >> 2) + 4 * hi + (e & 3)) * 40 + nl] = (bf16)value(e);
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int c = lane + 64 * x, row = c >> 2, part = c & 3;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(tt + row * 40 + 8 * part);
+    if (r0 + row < rows) *reinterpret_cast<bf16x8*>(dst + (size_t)(r0 + row) * ld + c0 + 8 * part) = v;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 }  // namespace
 
 // ONE: a single problem, whose descriptor then sits at fixed argument
@@ -62,9 +84,10 @@ template <typename OpT, typename A0T, typename WT, typename OutT, int EPI, int B
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   constexpr bool BF = std::is_same<OpT, bf16>::value;
   constexpr int CH = BF ? 8 : 4;   // elements per 16-byte chunk
-  constexpr int BK = 8 * CH;       // 64 bf16 or 32 fp32 per K step
+  constexpr int KC = 8;            // chunks per tile row and K step
+  constexpr int BK = KC * CH;      // 64 bf16 or 32 fp32 per K step
   constexpr int PITCH = BK + CH;   // rows padded by 16 bytes
-  constexpr int AC = BM * 8 / 256, WC = BN * 8 / 256;  // chunks per thread per K step
+  constexpr int AC = BM * KC / 256, WC = BN * KC / 256;  // chunks per thread per K step
   constexpr int MB = BM / 64, NB = BN / 64;            // 32x32 blocks per wave
   typedef typename Chunk<OpT, CH>::type VecT;
   __shared__ __attribute__((aligned(16))) OpT As[2][BM * PITCH];
@@ -84,13 +107,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
 
-  // chunk c = tid + 256 h of a tile covers row c / 8, columns (c % 8) * CH;
+  // chunk c = tid + 256 h of a tile covers row c / KC, columns (c % KC) * CH;
   // register slot q holds K step kb + q of the current round
   VecT ra[PF][AC], rw[PF][WC];
   auto gload = [&](int k0, int q) {
 #pragma unroll
     for (int h = 0; h < AC; ++h) {
-      const int c = tid + 256 * h, row = c >> 3, k = k0 + (c & 7) * CH;
+      const int c = tid + 256 * h, row = c / KC, k = k0 + (c % KC) * CH;
       const int r = r0 + row;
       if (r < P.rows && k < g.K) {
         if (k < g.K0)
@@ -103,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
     }
 #pragma unroll
     for (int h = 0; h < WC; ++h) {
-      const int c = tid + 256 * h, row = c >> 3, k = k0 + (c & 7) * CH;
+      const int c = tid + 256 * h, row = c / KC, k = k0 + (c % KC) * CH;
       const int n = n0 + row;
       if (n < P.n_out && k < g.K)
         rw[q][h] = load_chunk<WT, OpT, CH>(reinterpret_cast<const WT*>(g.W) + (size_t)(P.w_row0 + n) * g.ldw + k);
@@ -115,12 +138,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
 #pragma unroll
     for (int h = 0; h < AC; ++h) {
       const int c = tid + 256 * h;
-      *reinterpret_cast<VecT*>(&As[buf][(c >> 3) * PITCH + (c & 7) * CH]) = ra[q][h];
+      *reinterpret_cast<VecT*>(&As[buf][(c / KC) * PITCH + (c % KC) * CH]) = ra[q][h];
     }
 #pragma unroll
     for (int h = 0; h < WC; ++h) {
       const int c = tid + 256 * h;
-      *reinterpret_cast<VecT*>(&Ws[buf][(c >> 3) * PITCH + (c & 7) * CH]) = rw[q][h];
+      *reinterpret_cast<VecT*>(&Ws[buf][(c / KC) * PITCH + (c % KC) * CH]) = rw[q][h];
     }
   };
   f32x16 acc[MB][NB];
@@ -261,13 +284,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
         if (rr0 >= P.rows || nn0 >= P.n_out) continue;
         const float bias = 0.f;  // added to the accumulators above
         const int tile = rr0 >> 5;
-        if (nn0 < Dm) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int r = rr0 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            cq[P.c_off + (size_t)r * P.ldc + nn0 + nl] = (bf16)(acc[i][j][e] + bias);
-          }
-        }
+        if (nn0 < Dm)
+          store_block_bf16(tt, lane, [&](int e) { return acc[i][j][e] + bias; }, cq + P.c_off, P.ldc, rr0, nn0,
+                           P.rows);
         if (nn0 < g.split && (g.tied || nn0 >= Dm)) {
           const int kc = g.tied ? nn0 : nn0 - Dm;  // column of k
 #pragma unroll
@@ -336,6 +355,25 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
     }
   }
 
+  if constexpr ((EPI == EPI_BIAS || EPI == EPI_RELU) && std::is_same<OutT, bf16>::value) {
+    // bf16 outputs: each 32 x 32 block through a wave-private LDS tile
+    // (the n_out of these GEMMs are multiples of 32)
+    bf16* tt = reinterpret_cast<bf16*>(&As[0][0]) + wave * 32 * 40;
+    __syncthreads();  // every wave is done with the A tiles: As is scratch now
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int rr0 = r0 + wm * (BM / 2) + i * 32, nn0 = n0 + wn * (BN / 2) + j * 32;
+        if (rr0 >= P.rows || nn0 >= P.n_out) continue;
+        const float bias = g.bias ? (float)reinterpret_cast<const WT*>(g.bias)[nn0 + (lane & 31)] : 0.f;
+        store_block_bf16(tt, lane, [&](int e) {
+          const float v = acc[i][j][e] + bias;
+          return EPI == EPI_RELU ? fmaxf(v, 0.f) : v;
+        }, reinterpret_cast<bf16*>(g.C) + P.c_off, P.ldc, rr0, nn0, P.rows);
+      }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
@@ -493,6 +531,11 @@ hipError_t launch_gemm(int op, int a0f, int wd, int outf, int epi, const GemmArg
   if (max_rows <= 0 || max_n <= 0 || b.n <= 0) return hipSuccess;
   if (g.K % 8 || g.K0 % 8) return hipErrorInvalidValue;
   if (epi == EPI_QKV && g.split % 64) return hipErrorInvalidValue;  // V columns start on a tile edge
+  // bf16 outputs are stored in 16-byte row runs of whole 32-column blocks
+  if (op == SG_BF16 && !outf && epi != EPI_RESID && epi != EPI_SCORE) {
+    for (int i = 0; i < b.n; ++i)
+      if (b.p[i].n_out % 32 || b.p[i].ldc % 8 || b.p[i].c_off % 8) return hipErrorInvalidValue;
+  }
 #define SG_GO(O, A, W, OUT, E) gemm_go<O, A, W, OUT, E>(g, b, max_rows, max_n, st)
   // The operand-type / epilogue combinations the pipeline uses.
   if (op == SG_F32) {
