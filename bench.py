@@ -236,6 +236,19 @@ def batch_kernels(args, cfg, sg, np, torch, bstep, B, M, N, ds):
             r.update(bytes_per_iteration=4.0 * (M + 1) * (N + 1) * B,
                      achieved_GBps=round(float(byt / dur_us.sum() / 1e3), 1),
                      frac_hbm=round(float(byt / dur_us.sum() / 1e3) / PEAK["hbm_GBps"], 4))
+            if nl == 2 * cfg.T:
+                # one-pass schedule: row pass (reads Z, writes the per-block
+                # column partials of ceil((M+1)/8) row blocks), then the column
+                # reduction (reads the partials); launches alternate
+                G = (M + 1 + 7) // 8
+                part = 4.0 * G * ((N + 3) // 4 * 4) * B
+                rows_b, cols_b = 4.0 * M * ((N + 3) // 4 * 4) * B + part, part
+                rp, cp = dur_us[0::2], dur_us[1::2]
+                r["row_pass"] = {"avg_us": round(float(rp.mean()), 2), "bytes": rows_b,
+                                 "achieved_GBps": round(float(rows_b / rp.mean() / 1e3), 1),
+                                 "frac_hbm": round(float(rows_b / rp.mean() / 1e3 / PEAK["hbm_GBps"]), 4)}
+                r["column_reduction"] = {"avg_us": round(float(cp.mean()), 2), "bytes": cols_b,
+                                         "achieved_GBps": round(float(cols_b / cp.mean() / 1e3), 1)}
         res[name] = r
     return res
 
