@@ -269,6 +269,65 @@ def latency_percentiles(step, sg, torch, n):
     return {"passes": n, "p10_ms": q(0.1), "p50_ms": q(0.5), "p90_ms": q(0.9)}
 
 
+def per_config(sg, synth, np, torch, dev, reps=10):
+    """Every configuration's pass (cfg 0-3 one pair per call, cfg 4 its ragged
+    32-pair batch): median wall time per call over graph replays and the stage
+    times of an eager pass with stage events (context beside the headline)."""
+    keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
+    names = ["encoder", "gnn", "projection_scores", "sinkhorn", "extraction"]
+    res = {}
+    for cid in (0, 1, 3, 4):
+        cfg = synth.CONFIGS[cid]
+        w = synth.make_weights(cfg)
+        W = sg.pack_weights(w, device=dev)
+        if cfg.batch > 1:
+            b = synth.make_batch(cfg)
+            t = [torch.from_numpy(b[k]).to(dev) for k in keys]
+            img = (*b["image_size0"], *b["image_size1"])
+            Ms, Ns = [int(x) for x in b["M"]], [int(x) for x in b["N"]]
+            ws = torch.empty(sg.workspace_size(W, cfg.pad, cfg.pad, cfg.batch), dtype=torch.uint8, device=dev)
+
+            def call(**kw):
+                return sg.sg_match_batch(Ms, Ns, *t, W, cfg.L, cfg.T, image_size=img, workspace=ws,
+                                         want_matches1=False, **kw)
+            pairs = cfg.batch
+        else:
+            pair = synth.make_pair(cfg)
+            t = [torch.from_numpy(pair[k]).to(dev) for k in keys]
+            img = (*pair["image_size0"], *pair["image_size1"])
+            ws = torch.empty(sg.workspace_size(W, cfg.M, cfg.N, 1), dtype=torch.uint8, device=dev)
+            bufs = {"matches0": torch.empty(cfg.M, dtype=torch.int32, device=dev),
+                    "scores0": torch.empty(cfg.M, dtype=torch.float32, device=dev)}
+
+            def call(**kw):
+                return sg.sg_match(*t, W, cfg.L, cfg.T, image_size=img, workspace=ws, out=bufs, **kw)
+            pairs = 1
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            e.record()
+            e.synchronize()
+            ts.append(a.elapsed_time(e))
+        ev = sg.make_events(sg.SG_N_STAGE_EVENTS)
+        acc = np.zeros(sg.SG_N_STAGE_EVENTS - 1)
+        for _ in range(3):
+            call(stage_events=ev)
+            torch.cuda.synchronize()
+            acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(sg.SG_N_STAGE_EVENTS - 1)]
+        med = float(np.median(ts))
+        res[f"cfg{cid}"] = {"M": int(cfg.M) if pairs == 1 else "U{256..2048}", "N": int(cfg.N) if pairs == 1 else "U{256..2048}",
+                            "pairs_per_call": pairs, "dtype": cfg.dtype, "T": cfg.T, "L": cfg.L,
+                            "ms_per_call_p50": round(med, 4), "pairs_per_s": round(pairs / med * 1e3, 2),
+                            "stages_ms": {n: round(float(v / 3), 4) for n, v in zip(names, acc)}}
+        log(f"cfg {cid}: {res[f'cfg{cid}']}")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,6 +346,7 @@ def main():
     ap.add_argument("--rope", action="store_true", help="rotary position encoding in self-attention")
     ap.add_argument("--adaptive", action="store_true",
                     help="also time adaptive depth / width (forced exits and pruning) with the double-softmax head")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration context timings")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="before the steps, copy this many MiB with a plain device copy (counter scaling)")
     args = ap.parse_args()
@@ -489,6 +549,9 @@ def main():
         log(f"batch: {batch}")
 
     adaptive = adaptive_bench(args, cfg, dev, sg, synth, np, torch) if args.adaptive else None
+    configs = None
+    if not args.no_configs and args.head == "sinkhorn" and args.cross == "standard" and not args.rope:
+        configs = per_config(sg, synth, np, torch, dev)
 
     cpu = None
     if not args.no_cpu:
@@ -511,6 +574,7 @@ def main():
                    "head": args.head, "cross_attention": args.cross, "rope": args.rope},
         "roofline": roofline, "cpu_baseline": cpu, "latency": latency, "stages_ms": stages, "kernels": kernels,
         "batch_throughput": batch,
+        "per_config": configs,
         "adaptive": adaptive,
         "baseline_context": {"pages_ms_per_pair": {"GTX1080_1024kp": 87.0, "unstated_hw_2048kp": 70.0},
                              "pages_pairs_per_s": {"GTX1080_1024kp": 11.5, "unstated_hw_aachen_4096kp": 6.5}},
