@@ -64,6 +64,16 @@ __global__ __launch_bounds__(256) void k_encoder(EncArgs e, SegTable seg) {
       const int n = nb * 32 + (lane & 31);
       const WT* wrow = W + (size_t)n * K;
       f32x16 acc = zero16();
+      // the last layer adds the descriptors: requested with the weights, all
+      // at once (behind the state stores the compiler could not move them)
+      float dv[16];
+      if (last) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          dv[i] = r < np ? de[(size_t)r * e.D + n] : 0.f;
+        }
+      }
       // the whole weight row slice of this lane is requested before the MFMAs
       // (the loop is bound by load latency, not by the contraction)
       constexpr int KMAX = kMaxEncWidth;
@@ -105,7 +115,7 @@ __global__ __launch_bounds__(256) void k_encoder(EncArgs e, SegTable seg) {
         } else {
           // rows past the image (the tile's padding) are zero, so that every
           // later product over the padded row space stays finite
-          const float xv = r < np ? de[(size_t)r * e.D + n] + v : 0.f;
+          const float xv = r < np ? dv[i] + v : 0.f;
           e.X[(row0 + r) * e.ldx + n] = xv;
           if (e.XB) static_cast<bf16*>(e.XB)[(row0 + r) * e.ldx + n] = (bf16)xv;
         }
