@@ -1,17 +1,20 @@
 // Keypoint encoder MLP_enc([x, y, c]) added to the descriptors (gfx950).
 //
-// One fused kernel: a 256-thread workgroup takes 32 points of one image,
+// One fused kernel: a 512-thread workgroup takes 32 points of one image,
 // normalises their positions, runs the whole MLP with the hidden
 // activations kept in LDS (layer 0 on the VALU, K = 3; the other layers on
 // MFMA in the operand type of the network), and writes x0 = d + MLP_enc(p)
-// as fp32 states.  The four waves split each layer's outputs into 32-column
-// blocks; weights stream from L2.
+// as fp32 states.  The eight waves (two per SIMD) split each layer's outputs
+// into 32-column blocks, so that a 256-wide layer is one block per wave and
+// all of its weight loads are in flight together; weights stream from L2.
 #include "sg_device.h"
 
 namespace sg {
 
+constexpr int kEncThreads = 512, kEncWaves = kEncThreads / 64;
+
 template <typename OpT, typename WT>
-__global__ __launch_bounds__(256) void k_encoder(EncArgs e, SegTable seg) {
+__global__ __launch_bounds__(kEncThreads) void k_encoder(EncArgs e, SegTable seg) {
   constexpr bool BF = std::is_same<OpT, bf16>::value;
   constexpr int PADE = BF ? 8 : 4;
   constexpr int LDH = kMaxEncWidth + PADE;
@@ -34,7 +37,7 @@ __global__ __launch_bounds__(256) void k_encoder(EncArgs e, SegTable seg) {
     const WT* W0 = reinterpret_cast<const WT*>(e.W[0]);
     const WT* b0 = reinterpret_cast<const WT*>(e.b[0]);
     const int w1 = e.width[1];
-    for (int idx = tid; idx < 32 * w1; idx += 256) {
+    for (int idx = tid; idx < 32 * w1; idx += kEncThreads) {
       const int r = idx / w1, o = idx % w1;
       float h = 0.f;
       if (r < np) {
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(256) void k_encoder(EncArgs e, SegTable seg) {
     const WT* bias = reinterpret_cast<const WT*>(e.b[l]);
     const OpT* hin = hbuf[cur];
     OpT* hout = hbuf[cur ^ 1];
-    for (int nb = wave; nb * 32 < n_out; nb += 4) {
+    for (int nb = wave; nb * 32 < n_out; nb += kEncWaves) {
       const int n = nb * 32 + (lane & 31);
       const WT* wrow = W + (size_t)n * K;
       f32x16 acc = zero16();
@@ -178,9 +181,9 @@ hipError_t launch_encoder(int op, int wd, const EncArgs& e, const SegTable& seg,
   for (int l = 1; l < e.n_layers; ++l)
     if (e.width[l] % 16 || e.width[l + 1] % 32) return hipErrorInvalidValue;
   if (op == SG_BF16 && wd == SG_BF16)
-    hipLaunchKernelGGL((k_encoder<bf16, bf16>), dim3(tiles), dim3(256), 0, st, e, seg);
+    hipLaunchKernelGGL((k_encoder<bf16, bf16>), dim3(tiles), dim3(kEncThreads), 0, st, e, seg);
   else if (op == SG_F32 && wd == SG_F32)
-    hipLaunchKernelGGL((k_encoder<float, float>), dim3(tiles), dim3(256), 0, st, e, seg);
+    hipLaunchKernelGGL((k_encoder<float, float>), dim3(tiles), dim3(kEncThreads), 0, st, e, seg);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
