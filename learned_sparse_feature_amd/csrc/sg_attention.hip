@@ -300,7 +300,7 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
 // tile is in flight while the current one is consumed) and shared by the
 // four waves, which read their MFMA operands as one 16-byte LDS load each.
 template <int DH>
-__global__ __launch_bounds__(256, 3) void k_attention_wide(AttnArgs a, SegTable seg) {
+__global__ __launch_bounds__(256, 4) void k_attention_wide(AttnArgs a, SegTable seg) {
   if (a.stop && *a.stop) return;  // a later layer of a pass that has already stopped
   constexpr int BQ = 128, BKEY = 64;
   constexpr int KBLK = DH / 16, VBLK = DH / 16;  // 512-element blocks per 32 keys (K: dim chunks; V: 2 j x DH/32)
@@ -345,8 +345,11 @@ __global__ __launch_bounds__(256, 3) void k_attention_wide(AttnArgs a, SegTable 
   // tile is element 8 c; a 32-key block past the image's last one re-reads
   // that block (its keys are masked).
   const int nkb = (nk + 31) >> 5;
-  bf16x8 treg[KCH];
-  auto gload = [&](int k0) {
+  // Tiles go from global memory straight into LDS (global_load_lds: lane
+  // l of a wave writes 16 bytes at the wave's LDS base + 16 l), so no
+  // registers hold the tile in flight; chunk c = tid + 256 i lands at
+  // element 8 c of the buffer.
+  auto gload = [&](int k0, int buf) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + 256 * i;
@@ -354,12 +357,9 @@ __global__ __launch_bounds__(256, 3) void k_attention_wide(AttnArgs a, SegTable 
       const size_t tile = (size_t)((krow0 + 32 * min(k0 / 32 + kb, nkb - 1)) >> 5);
       const bf16* src = r < KBLK * 64 ? ks + (tile * (D / 16) + h * (DH / 16)) * 512 + 8 * r
                                       : vs + (tile * (D / 32) + (h * DH) / 32) * 1024 + 8 * (r - KBLK * 64);
-      treg[i] = *reinterpret_cast<const bf16x8*>(src);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&Ts[buf][8 * (64 * w + 256 * i)],
+                                       16, 0, 0);
     }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) *reinterpret_cast<bf16x8*>(&Ts[buf][8 * (tid + 256 * i)]) = treg[i];
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -368,15 +368,15 @@ __global__ __launch_bounds__(256, 3) void k_attention_wide(AttnArgs a, SegTable 
   for (int c = 0; c < DH / 32; ++c) O[c] = zero16();
 
   const int ntk = (nk + BKEY - 1) / BKEY;
-  gload(0);
-  sstore(0);
+  gload(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // the tile is in LDS
   __syncthreads();
   // Both 32-key blocks of a tile are taken together: two independent QK^T
   // chains, one maximum, one rescale of O and 32 exponentials per lane.
   static_assert(BKEY == 64, "two 32-key blocks per tile");
   for (int kt = 0; kt < ntk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < ntk) gload((kt + 1) * BKEY);
+    if (kt + 1 < ntk) gload((kt + 1) * BKEY, cur ^ 1);  // (buffer cur ^ 1 was released by the last barrier)
     const int k0 = kt * BKEY;
     const bf16* tb0 = &Ts[cur][lane * 8];
     const bf16* tb1 = tb0 + (KBLK + VBLK) * 512;
@@ -386,25 +386,21 @@ __global__ __launch_bounds__(256, 3) void k_attention_wide(AttnArgs a, SegTable 
       S0 = mfma(*reinterpret_cast<const bf16x8*>(tb0 + i * 512), Qr[i], S0);
       S1 = mfma(*reinterpret_cast<const bf16x8*>(tb1 + i * 512), Qr[i], S1);
     }
-    float e[2][16], tmax = -INFINITY;
-    if (k0 + BKEY <= nk) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        e[0][i] = S0[i] * a.scale2;
-        e[1][i] = S1[i] * a.scale2;
-        tmax = fmaxf(tmax, fmaxf(e[0][i], e[1][i]));
-      }
-    } else {  // keys past the image (a block past it re-read the last block)
+    // the maximum is taken over the raw scores (the scale is positive) and the
+    // scale folded into the exponent's FMA
+    if (k0 + BKEY > nk) {  // keys past the image (a block past it re-read the last block)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kk = k0 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        e[0][i] = kk < nk ? S0[i] * a.scale2 : -INFINITY;
-        e[1][i] = kk + 32 < nk ? S1[i] * a.scale2 : -INFINITY;
-        tmax = fmaxf(tmax, fmaxf(e[0][i], e[1][i]));
+        if (kk >= nk) S0[i] = -INFINITY;
+        if (kk + 32 >= nk) S1[i] = -INFINITY;
       }
     }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, fmaxf(S0[i], S1[i]));
     tmax = half_swap_max(tmax);
-    const float m_new = fmaxf(m_run, tmax);
+    const float m_new = fmaxf(m_run, tmax * a.scale2);
     const float corr = exp2_fast(m_run - m_new);
     float psum = 0.f;
     bf16x8 pb[2][2];
@@ -412,7 +408,7 @@ __global__ __launch_bounds__(256, 3) void k_attention_wide(AttnArgs a, SegTable 
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2_fast(e[b][i] - m_new);
+        const float p = exp2_fast(fmaf(b ? S1[i] : S0[i], a.scale2, -m_new));
         psum += p;
         pb[b][i >> 3][i & 7] = (bf16)p;
       }
@@ -445,7 +441,7 @@ __global__ __launch_bounds__(256, 3) void k_attention_wide(AttnArgs a, SegTable 
           O[cb] = mfma(va, pb[b][j], O[cb]);
         }
     }
-    if (kt + 1 < ntk) sstore(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // the next tile is in LDS
     __syncthreads();
   }
 
