@@ -78,9 +78,20 @@ __device__ __forceinline__ void store_block_bf16(bf16* tt, int lane, F value, bf
 
 }  // namespace
 
+// Dynamic LDS of the DMA variant (below).
+extern __shared__ __attribute__((aligned(16))) unsigned char g_gemm_dyn_lds[];
+
 // ONE: a single problem, whose descriptor then sits at fixed argument
 // offsets (no indexed lookup ahead of the first load).
-template <typename OpT, typename A0T, typename WT, typename OutT, int EPI, int BM, int BN, int PF, bool ONE>
+// DMA (bf16 operands, 64 x 64 tiles, K and K0 multiples of 64): every K step
+// of the tile is requested at once straight into LDS (global_load_lds, one
+// 16-byte slot per lane), nk x 16 KB of dynamic LDS, then one barrier and
+// the whole MFMA chain.  Slot s of a step's operand holds row s / 8 and
+// 16-byte chunk (s % 8) ^ (row % 8) of the step's 64 columns (an XOR swizzle
+// instead of row padding, which a per-lane DMA slot cannot skip).  The
+// MFMA order along K is that of the staged variant, so results are equal.
+template <typename OpT, typename A0T, typename WT, typename OutT, int EPI, int BM, int BN, int PF, bool ONE,
+          bool DMA = false>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   constexpr bool BF = std::is_same<OpT, bf16>::value;
   constexpr int CH = BF ? 8 : 4;   // elements per 16-byte chunk
@@ -90,8 +101,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   constexpr int AC = BM * KC / 256, WC = BN * KC / 256;  // chunks per thread per K step
   constexpr int MB = BM / 64, NB = BN / 64;            // 32x32 blocks per wave
   typedef typename Chunk<OpT, CH>::type VecT;
-  __shared__ __attribute__((aligned(16))) OpT As[2][BM * PITCH];
-  __shared__ __attribute__((aligned(16))) OpT Ws[2][BN * PITCH];
+  static_assert(!DMA || (std::is_same<OpT, bf16>::value && std::is_same<A0T, bf16>::value &&
+                          std::is_same<WT, bf16>::value && BM == 64 && BN == 64),
+                "the DMA variant takes bf16 operands and 64 x 64 tiles");
+  __shared__ __attribute__((aligned(16))) OpT As[DMA ? 1 : 2][DMA ? 8 : BM * PITCH];
+  __shared__ __attribute__((aligned(16))) OpT Ws[DMA ? 1 : 2][DMA ? 8 : BN * PITCH];
+  // LDS scratch of the epilogues (32 x 40 elements per wave at most)
+  OpT* const scratch = DMA ? reinterpret_cast<OpT*>(g_gemm_dyn_lds) : &As[0][0];
 
   if constexpr (ONE)
     args_in_sgprs(g.A0, g.A1, g.W, g.lda0, g.lda1, g.ldw, g.K0, g.K, g.gx, g.gy, g.stop, bt.p[0].a_row0,
@@ -212,19 +228,54 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   };
   if constexpr (EPI == EPI_RESID && PF > 2) load_resid();
   const int nk = (g.K + BK - 1) / BK;
+  if constexpr (DMA) {
+    bf16* const LA = reinterpret_cast<bf16*>(g_gemm_dyn_lds);  // [nk][64 x 64]
+    bf16* const LW = LA + (size_t)nk * 4096;                    // [nk][64 x 64]
+    const bf16* const A0 = reinterpret_cast<const bf16*>(g.A0);
+    const bf16* const A1 = reinterpret_cast<const bf16*>(g.A1);
+    const bf16* const Wp = reinterpret_cast<const bf16*>(g.W);
+    for (int q = 0; q < nk; ++q) {
 #pragma unroll
-  for (int q = 0; q < PF; ++q)
-    if (q < nk) gload(q * BK, q);
-  for (int kb = 0; kb < nk; kb += PF) {
+      for (int h = 0; h < 2; ++h) {
+        // instruction h of wave w fills slots 64 (2 w + h) .. +63 of both operands
+        const int sb = 64 * (2 * wave + h), sl = sb + lane, row = sl >> 3, kc = (sl & 7) ^ (row & 7);
+        const int k = q * 64 + 8 * kc;
+        const int ra = P.a_row0 + min(r0 + row, P.rows - 1);   // rows past the end: any valid row (never stored)
+        const int rw = P.w_row0 + min(n0 + row, P.n_out - 1);
+        const bf16* srcA = k < g.K0 ? A0 + (size_t)ra * g.lda0 + k : A1 + (size_t)ra * g.lda1 + (k - g.K0);
+        __builtin_amdgcn_global_load_lds(srcA, (__attribute__((address_space(3))) void*)(LA + (size_t)q * 4096 + 8 * sb),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(Wp + (size_t)rw * g.ldw + k,
+                                         (__attribute__((address_space(3))) void*)(LW + (size_t)q * 4096 + 8 * sb), 16, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every step is in LDS
+    __syncthreads();
+    const int ar = wm * 32 + (lane & 31), wr = wn * 32 + (lane & 31);
+    for (int q = 0; q < nk; ++q) {
 #pragma unroll
-    for (int q = 0; q < PF; ++q) {
-      const int kt = kb + q;
-      if (kt >= nk) break;
-      const int cur = kt & 1;
-      sstore(cur, q);
-      __syncthreads();
-      if (kt + PF < nk) gload((kt + PF) * BK, q);
-      compute(cur);
+      for (int st = 0; st < 4; ++st) {
+        const int kc = 2 * st + (lane >> 5);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(LA + (size_t)q * 4096 + ar * 64 + 8 * (kc ^ (ar & 7)));
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(LW + (size_t)q * 4096 + wr * 64 + 8 * (kc ^ (wr & 7)));
+        acc[0][0] = mfma(a, b, acc[0][0]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < PF; ++q)
+      if (q < nk) gload(q * BK, q);
+    for (int kb = 0; kb < nk; kb += PF) {
+#pragma unroll
+      for (int q = 0; q < PF; ++q) {
+        const int kt = kb + q;
+        if (kt >= nk) break;
+        const int cur = kt & 1;
+        sstore(cur, q);
+        __syncthreads();
+        if (kt + PF < nk) gload((kt + PF) * BK, q);
+        compute(cur);
+      }
     }
   }
 
@@ -270,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
     // tiles stay aligned).
     const int Dm = g.tied ? g.split : g.split / 2;
     constexpr int TP = 32 + 8;
-    bf16* tt = reinterpret_cast<bf16*>(&As[0][0]) + wave * 32 * TP;
+    bf16* tt = reinterpret_cast<bf16*>(scratch) + wave * 32 * TP;
     bf16* const cq = reinterpret_cast<bf16*>(g.C);
     bf16* const cv = reinterpret_cast<bf16*>(g.C2);
     bf16* const ck = reinterpret_cast<bf16*>(g.C3);
@@ -323,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
       // V columns: written transposed (VT [n - split][r]).  Each 32x32 block
       // is turned around in LDS so that the stores run along rows of VT.
       constexpr int TP = 32 + 16 / (int)sizeof(OutT);
-      OutT* tt = reinterpret_cast<OutT*>(&As[0][0]) + wave * 32 * TP;
+      OutT* tt = reinterpret_cast<OutT*>(scratch) + wave * 32 * TP;
       constexpr int CO = 16 / (int)sizeof(OutT);  // elements per 16-byte store
       typedef typename Chunk<OutT, CO>::type OVec;
 #pragma unroll
@@ -358,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   if constexpr ((EPI == EPI_BIAS || EPI == EPI_RELU) && std::is_same<OutT, bf16>::value) {
     // bf16 outputs: each 32 x 32 block through a wave-private LDS tile
     // (the n_out of these GEMMs are multiples of 32)
-    bf16* tt = reinterpret_cast<bf16*>(&As[0][0]) + wave * 32 * 40;
+    bf16* tt = reinterpret_cast<bf16*>(scratch) + wave * 32 * 40;
     __syncthreads();  // every wave is done with the A tiles: As is scratch now
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -504,6 +555,8 @@ hipError_t launch_fold_merge(int w_dtype, const FoldArgs& f, hipStream_t st) {
   return hipGetLastError();
 }
 
+constexpr int kGemmDmaMaxK = 512;  // 128 KB of LDS: one workgroup per CU
+
 template <typename OpT, typename A0T, typename WT, typename OutT, int EPI>
 static void gemm_go(const GemmArgs& g, const GemmBatch& b, int max_rows, int max_n, hipStream_t st) {
   // large problems (several tiles per CU even at 128 x 128): the LDS-efficient shape
@@ -519,7 +572,20 @@ static void gemm_go(const GemmArgs& g, const GemmBatch& b, int max_rows, int max
     a.gx = (max_rows + 63) / 64;
     a.gy = (max_n + 63) / 64;
     const int T = a.gx * a.gy * b.n;
-    if (b.n == 1)
+    constexpr bool DMAOK = std::is_same<OpT, bf16>::value && std::is_same<A0T, bf16>::value &&
+                           std::is_same<WT, bf16>::value;
+    if (DMAOK && b.n == 1 && g.K % 64 == 0 && g.K0 % 64 == 0 && g.K <= kGemmDmaMaxK) {
+      // every K step in LDS: nk x 16 KB (two workgroups per CU up to K = 256)
+      const unsigned lds = (unsigned)(g.K / 64) * 16384u;
+      static bool attr = false;  // (per instantiation)
+      if (!attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<OpT, A0T, WT, OutT, EPI, 64, 64, 8, true, DMAOK>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kGemmDmaMaxK / 64 * 16384);
+        attr = true;
+      }
+      hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 64, 64, 8, true, DMAOK>), dim3(8 * ((T + 7) / 8)), dim3(256),
+                         lds, st, a, b);
+    } else if (b.n == 1)
       hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 64, 64, 8, true>), dim3(8 * ((T + 7) / 8)), dim3(256), 0, st, a, b);
     else
       hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 64, 64, 8, false>), dim3(8 * ((T + 7) / 8)), dim3(256), 0, st, a, b);
