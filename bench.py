@@ -37,22 +37,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def gemm_flops(cfg, M, N, cross="standard"):
-    """Algorithmic flops of every GEMM launch of one pass, in launch order,
-    with the operand dtype of each (real rows only): the merge fold of all
-    2L stages (W1[:, D:] Wm, 2D x D x D per stage), then per stage the QKV
+def gemm_launches(cfg, M, N, cross="standard"):
+    """(label, operand dtype, algorithmic flops) of every GEMM-class launch of
+    one pass, in launch order (real rows only): the merge fold of all 2L
+    stages (W1[:, D:] Wm, 2D x D x D per stage), then per stage the QKV
     projection, the first MLP layer over [x || a] (merge folded in) and the
-    second with the residual.  Bidirectional cross stages project qk | v (2D
-    outputs) instead of q | k | v."""
-    R, D = M + N, cfg.D
-    out = [(cfg.dtype, 2.0 * 2 * cfg.L * 2 * D * D * D)]
-    for s in range(2 * cfg.L):
-        nqkv = 2 if (s % 2 == 1 and cross == "bidirectional") else 3
-        out += [(cfg.dtype, 2.0 * R * D * nqkv * D), (cfg.dtype, 2.0 * R * 2 * D * 2 * D),
-                (cfg.dtype, 2.0 * R * 2 * D * D)]
-    out.append((cfg.dtype, 2.0 * R * D * D))     # final projection
-    out.append(("f32", 2.0 * M * N * D))         # scores
+    second with the residual, then the final projection and the scores.
+    Bidirectional cross stages project qk | v (2D outputs) instead of
+    q | k | v."""
+    R, D, S = M + N, cfg.D, 2 * cfg.L
+    out = [("merge_fold", cfg.dtype, 2.0 * S * 2 * D * D * D)]
+    for s in range(S):
+        out.append(("qkv", cfg.dtype, 2.0 * R * D * (2 if (s % 2 == 1 and cross == "bidirectional") else 3) * D))
+        out.append(("mlp1", cfg.dtype, 2.0 * R * 2 * D * 2 * D))
+        out.append(("mlp2_residual", cfg.dtype, 2.0 * R * 2 * D * D))
+    out.append(("final_projection", cfg.dtype, 2.0 * R * D * D))
+    out.append(("scores", "f32", 2.0 * M * N * D))
     return out
+
+
+def gemm_flops(cfg, M, N, cross="standard"):
+    """(operand dtype, flops) of every GEMM-class launch (see gemm_launches)."""
+    return [(d, f) for _, d, f in gemm_launches(cfg, M, N, cross)]
 
 
 def attention_flops(cfg, M, N):
@@ -207,18 +213,19 @@ def batch_kernels(args, cfg, sg, np, torch, bstep, B, M, N, ds):
         dur_us = tot / reps * 1e3
         r = {"launches": nl, "total_us": round(float(dur_us.sum()), 1), "avg_us": round(float(dur_us.mean()), 2)}
         if name == "gemm":
-            fl = gemm_flops(cfg, M, N, args.cross)
-            assert nl == len(fl), ("batched GEMM launches", nl, len(fl))
-            bf = [(f * B, d) for (dt_, f), d in zip(fl, dur_us) if dt_ == "bf16"]
+            labs = gemm_launches(cfg, M, N, args.cross)
+            assert nl == len(labs), ("batched GEMM launches", nl, len(labs))
+            mult = (lambda lab: 1 if lab == "merge_fold" else B)  # the fold works on weights only
+            bf = [(f * mult(lab), d) for (lab, dt_, f), d in zip(labs, dur_us) if dt_ == "bf16"]
             ach = float(sum(f for f, _ in bf) / sum(d for _, d in bf) / 1e6)
             r.update(achieved_TFLOPs_bf16=round(ach, 1), frac_mfma=round(ach / PEAK["bf16_TFLOPs"], 4))
-            e = 1 + 6 * cfg.L
-            per = {"qkv": dur_us[1:e:3], "mlp1_merge_folded": dur_us[2:e:3], "mlp2_residual": dur_us[3:e:3]}
-            fls = {"qkv": fl[1][1] * B, "mlp1_merge_folded": fl[2][1] * B, "mlp2_residual": fl[3][1] * B}
-            r["per_projection"] = {k: {"avg_us": round(float(v.mean()), 2),
-                                       "frac_mfma": round(fls[k] / (float(v.mean()) * 1e6) / PEAK["bf16_TFLOPs"], 4)}
-                                   for k, v in per.items()}
-            r["merge_fold_us"] = round(float(dur_us[0]), 2)
+            per = {}
+            for (lab, _, f), d in zip(labs, dur_us):
+                per.setdefault(lab, []).append((f * mult(lab), d))
+            r["per_launch_kind"] = {
+                k: {"launches": len(v), "avg_us": round(float(np.mean([d for _, d in v])), 2),
+                    "frac_mfma": round(float(sum(f for f, _ in v) / sum(d for _, d in v) / 1e6 / PEAK["bf16_TFLOPs"]), 4)}
+                for k, v in per.items() if k != "scores"}
         elif name == "attention":
             fl = attention_flops(cfg, M, N)
             assert nl == len(fl), ("batched attention launches", nl, len(fl))

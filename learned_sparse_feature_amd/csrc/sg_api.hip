@@ -155,11 +155,11 @@ sg_status check_weights(const sg_weights* w, WLayout* out) {
 // ---------------------------------------------------------- workspace layout
 
 struct WsLayout {
-  size_t X, XB, H0, H1, QK, VT, KS, VS, MB, HB, WF, WFB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, ROPE, ADAPT, total;
+  size_t X, XB, QK, VT, KS, VS, MB, HB, WF, WFB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, ROPE, ADAPT, total;
   int ldvt, ldqk;
 };
 
-WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, long pf, long pd, long uf, long vf,
+WsLayout ws_layout_raw(long D, size_t os, long R, long zf, long ztf, long pf, long pd, long uf, long vf,
                        long nb, long ropef = 0, bool adaptive = false, long nstage = 0) {
   WsLayout L;
   // row strides are kept off powers of two (+64 / +16 bytes) so that the
@@ -173,8 +173,6 @@ WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, l
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   L.X = take((size_t)R * D * 4);
   L.XB = take(bf ? (size_t)R * D * 2 : 0);  // bf16 copy of X: the operand of the QKV and MLP GEMMs
-  L.H0 = take((size_t)R * maxw * 4);
-  L.H1 = take((size_t)R * maxw * 4);
   L.QK = take((size_t)R * L.ldqk * os);
   L.VT = take(bf ? 0 : (size_t)D * L.ldvt * os);
   L.KS = take(bf ? (size_t)R * D * os : 0);
@@ -205,9 +203,7 @@ WsLayout ws_layout_raw(long D, size_t os, int maxw, long R, long zf, long ztf, l
 }
 
 WsLayout ws_layout(const sg_weights* w, long R, long zf, long ztf, long pf, long pd, long uf, long vf, long nb) {
-  int maxw = 0;
-  for (int i = 0; i < w->n_enc; ++i) maxw = std::max(maxw, w->enc[i]);
-  return ws_layout_raw(w->D, w->dtype == SG_BF16 ? 2 : 4, maxw, R, zf, ztf, pf, pd, uf, vf, nb,
+  return ws_layout_raw(w->D, w->dtype == SG_BF16 ? 2 : 4, R, zf, ztf, pf, pd, uf, vf, nb,
                        w->rope ? R * (w->D / w->H / 2) : 0, w->adaptive != 0, 2L * w->L_max);
 }
 
@@ -1056,7 +1052,7 @@ size_t sg_stage_match_workspace_size(int32_t M, int32_t N, int32_t D) {
   const long R = round32(M) + round32(N);
   const long ztf = std::min((long)N * ld4(M), (long)(SG_TWO_SWEEP_MAX_BYTES / 4) + 3L * N);
   const long G = (M + 4) / 4;
-  return ws_layout_raw(D, 4, 0, R, (long)M * ld4(N), ztf, G * ld4(N), G, ld4(M + 1), ld4(N + 1), N).total;
+  return ws_layout_raw(D, 4, R, (long)M * ld4(N), ztf, G * ld4(N), G, ld4(M + 1), ld4(N + 1), N).total;
 }
 
 sg_status sg_match(const float* kptsA, const float* descA, const float* confA, int32_t M,
@@ -1264,7 +1260,7 @@ sg_status sg_stage_match(const float* fA, int32_t M, const float* fB, int32_t N,
   Plan pl;
   make_plan(p, pl);
   // f_A and f_B are staged into the compact F rows of the workspace
-  WsLayout wl = ws_layout_raw(D, 4, 0, pl.R, pl.zf, pl.ztf, pl.pf, pl.pd, pl.uf, pl.vf, pl.nb);
+  WsLayout wl = ws_layout_raw(D, 4, pl.R, pl.zf, pl.ztf, pl.pf, pl.pd, pl.uf, pl.vf, pl.nb);
   void* wsp;
   if ((s = get_workspace(opts, wl.total, &wsp)) != SG_OK) return s;
   char* ws = reinterpret_cast<char*>(wsp);
@@ -1296,7 +1292,7 @@ sg_status sg_stage_match(const float* fA, int32_t M, const float* fB, int32_t N,
 size_t sg_stage_match_ds_workspace_size(int32_t M, int32_t N, int32_t D) {
   if (M < 0 || N < 0 || D <= 0) return 0;
   const long R = round32(M) + round32(N);
-  return ws_layout_raw(D, 4, 0, R, (long)M * ld4(N), (long)N * ld4(M), 0, 0, ld4(M + 1), ld4(N + 1), N).total;
+  return ws_layout_raw(D, 4, R, (long)M * ld4(N), (long)N * ld4(M), 0, 0, ld4(M + 1), ld4(N + 1), N).total;
 }
 
 sg_status sg_stage_match_ds(const float* fA, const float* xA, int32_t M, const float* fB, const float* xB,
@@ -1324,7 +1320,7 @@ sg_status sg_stage_match_ds(const float* fA, const float* xA, int32_t M, const f
   Plan pl;
   make_plan(p, pl);
   // f and x are staged into the compact F and X rows of the workspace
-  WsLayout wl = ws_layout_raw(D, 4, 0, pl.R, pl.zf, pl.ztf, pl.pf, pl.pd, pl.uf, pl.vf, pl.nb);
+  WsLayout wl = ws_layout_raw(D, 4, pl.R, pl.zf, pl.ztf, pl.pf, pl.pd, pl.uf, pl.vf, pl.nb);
   void* wsp;
   if ((s = get_workspace(opts, wl.total, &wsp)) != SG_OK) return s;
   char* ws = reinterpret_cast<char*>(wsp);
