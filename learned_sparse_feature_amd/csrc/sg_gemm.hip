@@ -76,6 +76,13 @@ __device__ __forceinline__ void store_block_bf16(bf16* tt, int lane, F value, bf
   __builtin_amdgcn_wave_barrier();
 }
 
+// s_waitcnt with vmcnt = N and the other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace
 
 // Dynamic LDS of the DMA variant (below).
@@ -90,8 +97,14 @@ extern __shared__ __attribute__((aligned(16))) unsigned char g_gemm_dyn_lds[];
 // 16-byte chunk (s % 8) ^ (row % 8) of the step's 64 columns (an XOR swizzle
 // instead of row padding, which a per-lane DMA slot cannot skip).  The
 // MFMA order along K is that of the staged variant, so results are equal.
+// RING (bf16 operands, 128 x 128 tiles, K and K0 multiples of 32): the K
+// loop runs in 32-wide steps through a ring of RS 16 KB LDS slots filled
+// with global_load_lds RS - 1 steps ahead of the MFMAs; slot s of an operand
+// holds row s / 4 and 16-byte chunk (s % 4) ^ ((row / 4) % 4), which keeps
+// the operand reads of 16 consecutive rows on distinct banks.  Same MFMA
+// order along K.
 template <typename OpT, typename A0T, typename WT, typename OutT, int EPI, int BM, int BN, int PF, bool ONE,
-          bool DMA = false>
+          bool DMA = false, bool RING = false>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   constexpr bool BF = std::is_same<OpT, bf16>::value;
   constexpr int CH = BF ? 8 : 4;   // elements per 16-byte chunk
@@ -104,10 +117,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   static_assert(!DMA || (std::is_same<OpT, bf16>::value && std::is_same<A0T, bf16>::value &&
                           std::is_same<WT, bf16>::value && BM == 64 && BN == 64),
                 "the DMA variant takes bf16 operands and 64 x 64 tiles");
-  __shared__ __attribute__((aligned(16))) OpT As[DMA ? 1 : 2][DMA ? 8 : BM * PITCH];
-  __shared__ __attribute__((aligned(16))) OpT Ws[DMA ? 1 : 2][DMA ? 8 : BN * PITCH];
+  static_assert(!RING || (std::is_same<OpT, bf16>::value && std::is_same<A0T, bf16>::value &&
+                           std::is_same<WT, bf16>::value && BM == 128 && BN == 128 && !DMA),
+                "the ring variant takes bf16 operands and 128 x 128 tiles");
+  constexpr bool STAGED = !DMA && !RING;
+  // ring slots (three workgroups per CU at 48 KB; the residual GEMM, whose
+  // tile count is a multiple of two per CU at batch sizes, keeps two at 64 KB)
+  constexpr int RS = EPI == EPI_RESID ? 4 : 3, RSLOT = 2 * 128 * 32;  // elements per slot: A rows, then W rows
+  __shared__ __attribute__((aligned(16))) OpT As[STAGED ? 2 : 1][STAGED ? BM * PITCH : 8];
+  __shared__ __attribute__((aligned(16))) OpT Ws[STAGED ? 2 : 1][STAGED ? BN * PITCH : 8];
+  __shared__ __attribute__((aligned(16))) bf16 Ring[RING ? RS * RSLOT : 8];
   // LDS scratch of the epilogues (32 x 40 elements per wave at most)
-  OpT* const scratch = DMA ? reinterpret_cast<OpT*>(g_gemm_dyn_lds) : &As[0][0];
+  OpT* const scratch = DMA ? reinterpret_cast<OpT*>(g_gemm_dyn_lds) : RING ? reinterpret_cast<OpT*>(Ring) : &As[0][0];
 
   if constexpr (ONE)
     args_in_sgprs(g.A0, g.A1, g.W, g.lda0, g.lda1, g.ldw, g.K0, g.K, g.gx, g.gy, g.stop, bt.p[0].a_row0,
@@ -259,6 +280,62 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(LA + (size_t)q * 4096 + ar * 64 + 8 * (kc ^ (ar & 7)));
         const bf16x8 b = *reinterpret_cast<const bf16x8*>(LW + (size_t)q * 4096 + wr * 64 + 8 * (kc ^ (wr & 7)));
         acc[0][0] = mfma(a, b, acc[0][0]);
+      }
+    }
+  } else if constexpr (RING) {
+    const bf16* const A0 = reinterpret_cast<const bf16*>(g.A0);
+    const bf16* const A1 = reinterpret_cast<const bf16*>(g.A1);
+    const bf16* const Wp = reinterpret_cast<const bf16*>(g.W);
+    const int ns = g.K / 32;
+    // step q into slot q % RS: instruction h of wave w fills slots
+    // 256 h + 64 w .. +63 of both operands
+    auto issue = [&](int q) {
+      bf16* const base = Ring + (q % RS) * RSLOT;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int sb = 256 * h + 64 * wave, sl = sb + lane, row = sl >> 2, kc = (sl & 3) ^ ((row >> 2) & 3);
+        const int k = 32 * q + 8 * kc;
+        const int ra = P.a_row0 + min(r0 + row, P.rows - 1);  // rows past the end: any valid row (never stored)
+        const int rw = P.w_row0 + min(n0 + row, P.n_out - 1);
+        const bf16* srcA = k < g.K0 ? A0 + (size_t)ra * g.lda0 + k : A1 + (size_t)ra * g.lda1 + (k - g.K0);
+        __builtin_amdgcn_global_load_lds(srcA, (__attribute__((address_space(3))) void*)(base + 8 * sb), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(Wp + (size_t)rw * g.ldw + k,
+                                         (__attribute__((address_space(3))) void*)(base + 128 * 32 + 8 * sb), 16, 0, 0);
+      }
+    };
+    for (int q = 0; q < RS - 1 && q < ns; ++q) issue(q);
+    for (int q = 0; q < ns; ++q) {
+      // step q has landed once at most the later steps' 4 instructions each are pending
+      const int later = min(ns - 1, q + RS - 2) - q;
+      if (later >= 2) wait_vm<8>();
+      else if (later == 1) wait_vm<4>();
+      else wait_vm<0>();
+      // ... in every lane; and every wave is done with step q - 1's slot.  A
+      // bare barrier: __syncthreads() would also wait for the steps still in
+      // flight (its fence covers the LDS writes of global_load_lds)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (q + RS - 1 < ns) issue(q + RS - 1);
+      const bf16* const base = Ring + (q % RS) * RSLOT;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int kc = 2 * st + (lane >> 5);
+        bf16x8 a[MB], b[NB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int ar = wm * (BM / 2) + i * 32 + (lane & 31);
+          a[i] = *reinterpret_cast<const bf16x8*>(base + ar * 32 + 8 * (kc ^ ((ar >> 2) & 3)));
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int wr = wn * (BN / 2) + j * 32 + (lane & 31);
+          b[j] = *reinterpret_cast<const bf16x8*>(base + 128 * 32 + wr * 32 + 8 * (kc ^ ((wr >> 2) & 3)));
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma(a[i], b[j], acc[i][j]);
       }
     }
   } else {
@@ -563,17 +640,22 @@ static void gemm_go(const GemmArgs& g, const GemmBatch& b, int max_rows, int max
   const long big_tiles = (long)((max_rows + 127) / 128) * ((max_n + 127) / 128) * b.n;
   GemmArgs a = g;
   // (a QKV split must fall on a tile edge: 128-wide tiles need it at a multiple of 128)
+  constexpr bool DMAOK = std::is_same<OpT, bf16>::value && std::is_same<A0T, bf16>::value &&
+                         std::is_same<WT, bf16>::value;
   if (big_tiles >= 1024 && !(EPI == EPI_QKV && g.split % 128)) {
     a.gx = (max_rows + 127) / 128;
     a.gy = (max_n + 127) / 128;
     const int T = a.gx * a.gy * b.n;
-    hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 128, 128, 2, false>), dim3(8 * ((T + 7) / 8)), dim3(256), 0, st, a, b);
+    if (DMAOK && b.n == 1 && g.K % 32 == 0 && g.K0 % 32 == 0)
+      hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 128, 128, 2, true, false, DMAOK>), dim3(8 * ((T + 7) / 8)),
+                         dim3(256), 0, st, a, b);
+    else
+      hipLaunchKernelGGL((k_gemm<OpT, A0T, WT, OutT, EPI, 128, 128, 2, false>), dim3(8 * ((T + 7) / 8)), dim3(256), 0, st,
+                         a, b);
   } else {
     a.gx = (max_rows + 63) / 64;
     a.gy = (max_n + 63) / 64;
     const int T = a.gx * a.gy * b.n;
-    constexpr bool DMAOK = std::is_same<OpT, bf16>::value && std::is_same<A0T, bf16>::value &&
-                           std::is_same<WT, bf16>::value;
     if (DMAOK && b.n == 1 && g.K % 64 == 0 && g.K0 % 64 == 0 && g.K <= kGemmDmaMaxK) {
       // every K step in LDS: nk x 16 KB (two workgroups per CU up to K = 256)
       const unsigned lds = (unsigned)(g.K / 64) * 16384u;
