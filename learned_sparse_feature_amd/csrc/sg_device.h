@@ -82,6 +82,24 @@ __device__ __forceinline__ float half_swap_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// s_waitcnt with vmcnt = N and the other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(), whose
+// release also waits for every global_load_lds still in flight: for loops
+// that keep later LDS loads in flight across the barrier and wait for the
+// ones they need with wait_vm first.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // (value, index) argmax over the wave: the larger value wins, the lower
 // index among equal values.  Result in every lane.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {

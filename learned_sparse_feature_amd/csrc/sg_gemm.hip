@@ -76,13 +76,6 @@ __device__ __forceinline__ void store_block_bf16(bf16* tt, int lane, F value, bf
   __builtin_amdgcn_wave_barrier();
 }
 
-// s_waitcnt with vmcnt = N and the other counters left alone
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 }  // namespace
 
 // Dynamic LDS of the DMA variant (below).
@@ -310,12 +303,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
       if (later >= 2) wait_vm<8>();
       else if (later == 1) wait_vm<4>();
       else wait_vm<0>();
-      // ... in every lane; and every wave is done with step q - 1's slot.  A
-      // bare barrier: __syncthreads() would also wait for the steps still in
-      // flight (its fence covers the LDS writes of global_load_lds)
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
+      // ... in every lane; and every wave is done with step q - 1's slot
+      // (__syncthreads() would also wait for the steps still in flight)
+      bare_barrier();
       if (q + RS - 1 < ns) issue(q + RS - 1);
       const bf16* const base = Ring + (q % RS) * RSLOT;
 #pragma unroll
