@@ -357,8 +357,7 @@ __global__ __launch_bounds__(256, 4) void k_attention_wide(AttnArgs a, SegTable 
       const size_t tile = (size_t)((krow0 + 32 * min(k0 / 32 + kb, nkb - 1)) >> 5);
       const bf16* src = r < KBLK * 64 ? ks + (tile * (D / 16) + h * (DH / 16)) * 512 + 8 * r
                                       : vs + (tile * (D / 32) + (h * DH) / 32) * 1024 + 8 * (r - KBLK * 64);
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&Ts[buf][8 * (64 * w + 256 * i)],
-                                       16, 0, 0);
+      lds_dma16(src, &Ts[buf][8 * (64 * w + 256 * i)]);
     }
   };
 

@@ -82,6 +82,16 @@ __device__ __forceinline__ float half_swap_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// global_load_lds of 16 bytes per lane: lane l of the wave writes the 16
+// bytes at src (its own address) to LDS at the wave-uniform lds_base + 16 l;
+// counted by vmcnt.  The source is cast to the global address space
+// explicitly: left to an implicit conversion, the host pass of some kernel
+// template instantiations drops their launch stubs without a diagnostic.
+__device__ __forceinline__ void lds_dma16(const void* src, const void* lds_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src),
+                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+
 // s_waitcnt with vmcnt = N and the other counters left alone
 template <int N>
 __device__ __forceinline__ void wait_vm() {

@@ -257,10 +257,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
         const int ra = P.a_row0 + min(r0 + row, P.rows - 1);   // rows past the end: any valid row (never stored)
         const int rw = P.w_row0 + min(n0 + row, P.n_out - 1);
         const bf16* srcA = k < g.K0 ? A0 + (size_t)ra * g.lda0 + k : A1 + (size_t)ra * g.lda1 + (k - g.K0);
-        __builtin_amdgcn_global_load_lds(srcA, (__attribute__((address_space(3))) void*)(LA + (size_t)q * 4096 + 8 * sb),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds(Wp + (size_t)rw * g.ldw + k,
-                                         (__attribute__((address_space(3))) void*)(LW + (size_t)q * 4096 + 8 * sb), 16, 0, 0);
+        lds_dma16(srcA, LA + (size_t)q * 4096 + 8 * sb);
+        lds_dma16(Wp + (size_t)rw * g.ldw + k, LW + (size_t)q * 4096 + 8 * sb);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // every step is in LDS
@@ -291,9 +289,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
         const int ra = P.a_row0 + min(r0 + row, P.rows - 1);  // rows past the end: any valid row (never stored)
         const int rw = P.w_row0 + min(n0 + row, P.n_out - 1);
         const bf16* srcA = k < g.K0 ? A0 + (size_t)ra * g.lda0 + k : A1 + (size_t)ra * g.lda1 + (k - g.K0);
-        __builtin_amdgcn_global_load_lds(srcA, (__attribute__((address_space(3))) void*)(base + 8 * sb), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(Wp + (size_t)rw * g.ldw + k,
-                                         (__attribute__((address_space(3))) void*)(base + 128 * 32 + 8 * sb), 16, 0, 0);
+        lds_dma16(srcA, base + 8 * sb);
+        lds_dma16(Wp + (size_t)rw * g.ldw + k, base + 128 * 32 + 8 * sb);
       }
     };
     for (int q = 0; q < RS - 1 && q < ns; ++q) issue(q);
