@@ -224,21 +224,25 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
   // the loads past): before the main loop for the small tiles, where its
   // latency then overlaps the K loop, and after it for the large ones, whose
   // main loop has no registers to spare.
+  // It is read in the row-major form the epilogue writes: chunk x of a
+  // 32 x 32 block is row (lane + 64 x) / 8, columns 4 ((lane + 64 x) % 8) ..
+  // +3, one 16-byte load.
   constexpr int RM = EPI == EPI_RESID ? MB : 1, RN = EPI == EPI_RESID ? NB : 1;
-  float cres[RM][RN][16];
+  float4 cres[RM][RN][4];
   auto load_resid = [&]() {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = r0 + wm * (BM / 2) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          cres[i][j][e] = (r < P.rows && n < P.n_out)
-                              ? reinterpret_cast<const float*>(g.C)[P.c_off + (size_t)r * P.ldc + n] : 0.f;
+        for (int x = 0; x < 4; ++x) {
+          const int c = lane + 64 * x;
+          const int r = r0 + wm * (BM / 2) + i * 32 + (c >> 3), n = n0 + wn * (BN / 2) + j * 32 + 4 * (c & 7);
+          cres[i][j][x] = (r < P.rows && n < P.n_out)
+                              ? *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(g.C) + P.c_off +
+                                                                 (size_t)r * P.ldc + n)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-    }
   };
   if constexpr (EPI == EPI_RESID && PF > 2) load_resid();
   const int nk = (g.K + BK - 1) / BK;
@@ -470,6 +474,45 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
     }
   }
 
+  if constexpr (EPI == EPI_RESID) {
+    // x = x + (acc + bias) and its bf16 copy: each 32 x 32 block of acc + bias
+    // goes through a wave-private fp32 LDS tile (32 rows, pitch 36), so that
+    // the residual read and both writes run along rows, 16 (8) bytes per lane
+    constexpr int TP = 36;
+    float* tt = reinterpret_cast<float*>(scratch) + wave * 32 * TP;
+    __syncthreads();  // every wave is done with the operand tiles: their LDS is scratch now
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int rr0 = r0 + wm * (BM / 2) + i * 32, nn0 = n0 + wn * (BN / 2) + j * 32;
+        if (rr0 >= P.rows || nn0 >= P.n_out) continue;
+        const float bias = g.bias ? (float)reinterpret_cast<const WT*>(g.bias)[nn0 + (lane & 31)] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tt[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * TP + (lane & 31)] = acc[i][j][e] + bias;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int c = lane + 64 * x, row = c >> 3, part = c & 7;
+          const int r = rr0 + row, n = nn0 + 4 * part;
+          if (r < P.rows && n < P.n_out) {
+            const float4 v = *reinterpret_cast<const float4*>(tt + row * TP + 4 * part);
+            const float4 res = cres[i][j][x];
+            const float4 xo = make_float4(res.x + v.x, res.y + v.y, res.z + v.z, res.w + v.w);
+            const size_t off = P.c_off + (size_t)r * P.ldc + n;
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.C) + off) = xo;
+            if (g.C2) {
+              bf16x4 xb;
+              xb[0] = (bf16)xo.x; xb[1] = (bf16)xo.y; xb[2] = (bf16)xo.z; xb[3] = (bf16)xo.w;
+              *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(g.C2) + off) = xb;
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    return;
+  }
+
   if constexpr ((EPI == EPI_BIAS || EPI == EPI_RELU) && std::is_same<OutT, bf16>::value) {
     // bf16 outputs: each 32 x 32 block through a wave-private LDS tile
     // (the n_out of these GEMMs are multiples of 32)
@@ -507,11 +550,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
           reinterpret_cast<OutT*>(g.C)[P.c_off + (size_t)r * P.ldc + n] = (OutT)v;
           // tied query/key projection: the same column is k as well (k at +split)
           if (EPI == EPI_QKV && g.tied) reinterpret_cast<OutT*>(g.C)[P.c_off + (size_t)r * P.ldc + n + g.split] = (OutT)v;
-        } else if constexpr (EPI == EPI_RESID) {
-          const float x = cres[i][j][e] + v;
-          reinterpret_cast<float*>(g.C)[P.c_off + (size_t)r * P.ldc + n] = x;
-          // bf16 shadow of the states (the operand the next GEMMs read)
-          if (g.C2) reinterpret_cast<bf16*>(g.C2)[P.c_off + (size_t)r * P.ldc + n] = (bf16)x;
         } else {  // EPI_SCORE
           v = acc[i][j][e] * g.scale;
           reinterpret_cast<float*>(g.C)[P.c_off + (size_t)r * P.ldc + n] = v;
@@ -670,6 +708,11 @@ hipError_t launch_gemm(int op, int a0f, int wd, int outf, int epi, const GemmArg
   if (op == SG_BF16 && !outf && epi != EPI_RESID && epi != EPI_SCORE) {
     for (int i = 0; i < b.n; ++i)
       if (b.p[i].n_out % 32 || b.p[i].ldc % 8 || b.p[i].c_off % 8) return hipErrorInvalidValue;
+  }
+  // the residual epilogue reads and writes 4-column row runs
+  if (epi == EPI_RESID) {
+    for (int i = 0; i < b.n; ++i)
+      if (b.p[i].n_out % 4 || b.p[i].ldc % 4 || b.p[i].c_off % 4) return hipErrorInvalidValue;
   }
 #define SG_GO(O, A, W, OUT, E) gemm_go<O, A, W, OUT, E>(g, b, max_rows, max_n, st)
   // The operand-type / epilogue combinations the pipeline uses.
