@@ -21,6 +21,8 @@
 // tiles, the column tiles of one row tile run together on one XCD, and each
 // A row tile is fetched into that XCD's L2 once instead of once per column
 // tile.
+#include <algorithm>
+
 #include "sg_device.h"
 
 namespace sg {
@@ -532,6 +534,68 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
       }
     return;
   }
+  if constexpr (EPI == EPI_SCORE || ((EPI == EPI_BIAS || EPI == EPI_RELU) && std::is_same<OutT, float>::value)) {
+    // fp32 outputs: each 32 x 32 block through a wave-private LDS tile
+    // (pitch 36), stored as 16-byte row runs; the scores' transposed copy
+    // as 16-byte runs along the rows of the transpose
+    constexpr int TP = 36;
+    float* tt = reinterpret_cast<float*>(scratch) + wave * 32 * TP;
+    __syncthreads();  // every wave is done with the operand tiles: their LDS is scratch now
+    const int nl = lane & 31;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int rr0 = r0 + wm * (BM / 2) + i * 32, nn0 = n0 + wn * (BN / 2) + j * 32;
+        if (rr0 >= P.rows || nn0 >= P.n_out) continue;
+        float bias = 0.f;
+        if (EPI != EPI_SCORE && g.bias && nn0 + nl < P.n_out) bias = (float)reinterpret_cast<const WT*>(g.bias)[nn0 + nl];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float v = EPI == EPI_SCORE ? acc[i][j][e] * g.scale : acc[i][j][e] + bias;
+          if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+          tt[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * TP + nl] = v;
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int c = lane + 64 * x, row = c >> 3, part = c & 7;
+          const int r = rr0 + row, n = nn0 + 4 * part;
+          if (r < P.rows && n < P.n_out) {
+            const float4 v = *reinterpret_cast<const float4*>(tt + row * TP + 4 * part);
+            float* dst = reinterpret_cast<float*>(g.C) + P.c_off + (size_t)r * P.ldc + n;
+            if (n + 3 < P.n_out) {
+              *reinterpret_cast<float4*>(dst) = v;
+            } else {
+              dst[0] = v.x;
+              if (n + 1 < P.n_out) dst[1] = v.y;
+              if (n + 2 < P.n_out) dst[2] = v.z;
+            }
+          }
+        }
+        if (EPI == EPI_SCORE && g.C2) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int c = lane + 64 * x, col = c >> 3, part = c & 7;
+            const int n = nn0 + col, r = rr0 + 4 * part;
+            if (n < P.n_out && r < P.rows) {
+              const float4 v = make_float4(tt[(4 * part) * TP + col], tt[(4 * part + 1) * TP + col],
+                                           tt[(4 * part + 2) * TP + col], tt[(4 * part + 3) * TP + col]);
+              float* dst = reinterpret_cast<float*>(g.C2) + P.ct_off + (size_t)n * P.ldct + r;
+              if (r + 3 < P.rows) {
+                *reinterpret_cast<float4*>(dst) = v;
+              } else {
+                dst[0] = v.x;
+                if (r + 1 < P.rows) dst[1] = v.y;
+                if (r + 2 < P.rows) dst[2] = v.z;
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
@@ -683,7 +747,8 @@ static void gemm_go(const GemmArgs& g, const GemmBatch& b, int max_rows, int max
     const int T = a.gx * a.gy * b.n;
     if (DMAOK && b.n == 1 && g.K % 64 == 0 && g.K0 % 64 == 0 && g.K <= kGemmDmaMaxK) {
       // every K step in LDS: nk x 16 KB (two workgroups per CU up to K = 256)
-      const unsigned lds = (unsigned)(g.K / 64) * 16384u;
+      // (at least the 18 KB the fp32 epilogues stage through it)
+      const unsigned lds = std::max((unsigned)(g.K / 64) * 16384u, 18432u);
       static bool attr = false;  // (per instantiation)
       if (!attr) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<OpT, A0T, WT, OutT, EPI, 64, 64, 8, true, DMAOK>),
@@ -713,6 +778,13 @@ hipError_t launch_gemm(int op, int a0f, int wd, int outf, int epi, const GemmArg
   if (epi == EPI_RESID) {
     for (int i = 0; i < b.n; ++i)
       if (b.p[i].n_out % 4 || b.p[i].ldc % 4 || b.p[i].c_off % 4) return hipErrorInvalidValue;
+  }
+  // fp32 outputs (and the scores' transposed copy) are stored in 16-byte runs
+  if (epi == EPI_SCORE || (outf && (epi == EPI_BIAS || epi == EPI_RELU))) {
+    for (int i = 0; i < b.n; ++i) {
+      if (b.p[i].ldc % 4 || b.p[i].c_off % 4) return hipErrorInvalidValue;
+      if (epi == EPI_SCORE && g.C2 && (b.p[i].ldct % 4 || b.p[i].ct_off % 4)) return hipErrorInvalidValue;
+    }
   }
 #define SG_GO(O, A, W, OUT, E) gemm_go<O, A, W, OUT, E>(g, b, max_rows, max_n, st)
   // The operand-type / epilogue combinations the pipeline uses.
