@@ -410,17 +410,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
                            P.rows);
         if (nn0 < g.split && (g.tied || nn0 >= Dm)) {
           const int kc = g.tied ? nn0 : nn0 - Dm;  // column of k
+          // the block row-major in LDS (row = key, 32 columns = dims) ...
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            tt[nl * TP + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)] = (bf16)(acc[i][j][e] + bias);
+            tt[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * TP + nl] = (bf16)(acc[i][j][e] + bias);
           __builtin_amdgcn_wave_barrier();
-          // chunk c: 16-dim half `which` of the block's 32 columns, lane slot L
+          // ... so that chunk c (16-dim half `which` of the block's 32
+          // columns, lane slot L: key L % 32, dims 16 which + 8 (L / 32) ..
+          // +7) is one 16-byte LDS read
 #pragma unroll
           for (int c = lane; c < 128; c += 64) {
             const int L = c & 63, which = c >> 6;
-            bf16x8 v;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) v[t] = tt[(16 * which + 8 * (L >> 5) + t) * TP + (L & 31)];
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(tt + (L & 31) * TP + 16 * which + 8 * (L >> 5));
             const size_t blk = (size_t)tile * (Dm / 16) + kc / 16 + which;
             *reinterpret_cast<bf16x8*>(ck + blk * 512 + L * 8) = v;
           }
@@ -534,10 +535,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
       }
     return;
   }
-  if constexpr (EPI == EPI_SCORE || ((EPI == EPI_BIAS || EPI == EPI_RELU) && std::is_same<OutT, float>::value)) {
+  if constexpr (EPI == EPI_SCORE ||
+                ((EPI == EPI_BIAS || EPI == EPI_RELU || EPI == EPI_QKV) && std::is_same<OutT, float>::value)) {
     // fp32 outputs: each 32 x 32 block through a wave-private LDS tile
     // (pitch 36), stored as 16-byte row runs; the scores' transposed copy
-    // as 16-byte runs along the rows of the transpose
+    // as 16-byte runs along the rows of the transpose.  (QKV: the q | k
+    // columns of an fp32 network, bias already in the accumulators; a tied
+    // projection writes them as k too, at + split.)
     constexpr int TP = 36;
     float* tt = reinterpret_cast<float*>(scratch) + wave * 32 * TP;
     __syncthreads();  // every wave is done with the operand tiles: their LDS is scratch now
@@ -549,7 +553,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
         const int rr0 = r0 + wm * (BM / 2) + i * 32, nn0 = n0 + wn * (BN / 2) + j * 32;
         if (rr0 >= P.rows || nn0 >= P.n_out) continue;
         float bias = 0.f;
-        if (EPI != EPI_SCORE && g.bias && nn0 + nl < P.n_out) bias = (float)reinterpret_cast<const WT*>(g.bias)[nn0 + nl];
+        if (EPI != EPI_SCORE && EPI != EPI_QKV && g.bias && nn0 + nl < P.n_out)
+          bias = (float)reinterpret_cast<const WT*>(g.bias)[nn0 + nl];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           float v = EPI == EPI_SCORE ? acc[i][j][e] * g.scale : acc[i][j][e] + bias;
@@ -566,10 +571,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
             float* dst = reinterpret_cast<float*>(g.C) + P.c_off + (size_t)r * P.ldc + n;
             if (n + 3 < P.n_out) {
               *reinterpret_cast<float4*>(dst) = v;
+              if (EPI == EPI_QKV && g.tied) *reinterpret_cast<float4*>(dst + g.split) = v;
             } else {
               dst[0] = v.x;
               if (n + 1 < P.n_out) dst[1] = v.y;
               if (n + 2 < P.n_out) dst[2] = v.z;
+              if (EPI == EPI_QKV && g.tied) {
+                dst[g.split] = v.x;
+                if (n + 1 < P.n_out) dst[g.split + 1] = v.y;
+                if (n + 2 < P.n_out) dst[g.split + 2] = v.z;
+              }
             }
           }
         }
@@ -780,7 +791,7 @@ hipError_t launch_gemm(int op, int a0f, int wd, int outf, int epi, const GemmArg
       if (b.p[i].n_out % 4 || b.p[i].ldc % 4 || b.p[i].c_off % 4) return hipErrorInvalidValue;
   }
   // fp32 outputs (and the scores' transposed copy) are stored in 16-byte runs
-  if (epi == EPI_SCORE || (outf && (epi == EPI_BIAS || epi == EPI_RELU))) {
+  if (epi == EPI_SCORE || (outf && (epi == EPI_BIAS || epi == EPI_RELU || epi == EPI_QKV))) {
     for (int i = 0; i < b.n; ++i) {
       if (b.p[i].ldc % 4 || b.p[i].c_off % 4) return hipErrorInvalidValue;
       if (epi == EPI_SCORE && g.C2 && (b.p[i].ldct % 4 || b.p[i].ct_off % 4)) return hipErrorInvalidValue;
