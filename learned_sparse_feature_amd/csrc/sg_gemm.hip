@@ -116,9 +116,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g, GemmBatch bt) {
                            std::is_same<WT, bf16>::value && BM == 128 && BN == 128 && !DMA),
                 "the ring variant takes bf16 operands and 128 x 128 tiles");
   constexpr bool STAGED = !DMA && !RING;
-  // ring slots (three workgroups per CU at 48 KB; the residual GEMM, whose
-  // tile count is a multiple of two per CU at batch sizes, keeps two at 64 KB)
-  constexpr int RS = EPI == EPI_RESID ? 4 : 3, RSLOT = 2 * 128 * 32;  // elements per slot: A rows, then W rows
+  // ring slots: three of 16 KB (48 KB of LDS, three workgroups per CU)
+  constexpr int RS = 3, RSLOT = 2 * 128 * 32;  // elements per slot: A rows, then W rows
   __shared__ __attribute__((aligned(16))) OpT As[STAGED ? 2 : 1][STAGED ? BM * PITCH : 8];
   __shared__ __attribute__((aligned(16))) OpT Ws[STAGED ? 2 : 1][STAGED ? BN * PITCH : 8];
   __shared__ __attribute__((aligned(16))) bf16 Ring[RING ? RS * RSLOT : 8];
