@@ -407,3 +407,30 @@ def test_gnn_slice_starting_at_an_odd_stage_is_cross():
     A, B = oracle.attentional_gnn(xA, xB, [_mean_stage(D)], heads=2, first_stage=1)
     np.testing.assert_allclose(A, xA + xB.mean(0), rtol=1e-13)
     np.testing.assert_allclose(B, xB + xA.mean(0), rtol=1e-13)
+
+
+def test_update_mlp_hidden_relu_and_bias_by_hand():
+    """The update MLP's hidden layer, worked by hand: [realcat] "多层GNN"
+    gives MLP([x || m]) with channels [2D, 2D, D] and a ReLU between the two
+    layers.  One self stage with D = 2, one head, uniform attention (W_q =
+    W_k = 0), v = x and merge = I, so m is the mean of the image's states.
+    W1 maps [x || m] to (-m0, -m1, x0, x1) and b1 = (1.75, 0.5, -1.5, 0.25)
+    shifts it, so that some hidden pre-activations are negative (the ReLU
+    clips them) and every hidden unit depends on b1; W2 adds units (0, 2)
+    and (1, 3).
+      A = [[1, 3], [2, -1]]: m = (1.5, 1)
+        row 0: h = (0.25, -0.5, -0.5, 3.25) -> ReLU (0.25, 0, 0, 3.25) -> (0.25, 3.25)
+        row 1: h = (0.25, -0.5,  0.5, -0.75) -> ReLU (0.25, 0, 0.5, 0) -> (0.75, 0)
+      B = [[0.5, 0.5]]: m = (0.5, 0.5)
+        h = (1.25, 0, -1, 0.75) -> ReLU (1.25, 0, 0, 0.75) -> (1.25, 0.75)
+    Dropping the ReLU or b1 changes every one of these rows."""
+    Z2, I2 = np.zeros((2, 2)), np.eye(2)
+    st = {"Wq": Z2, "bq": np.zeros(2), "Wk": Z2, "bk": np.zeros(2), "Wv": I2, "bv": np.zeros(2),
+          "Wm": I2, "bm": np.zeros(2),
+          "W1": np.block([[Z2, -I2], [I2, Z2]]), "b1": np.array([1.75, 0.5, -1.5, 0.25]),
+          "W2": np.array([[1.0, 0.0, 1.0, 0.0], [0.0, 1.0, 0.0, 1.0]]), "b2": np.zeros(2)}
+    xA = np.array([[1.0, 3.0], [2.0, -1.0]])
+    xB = np.array([[0.5, 0.5]])
+    A, B = oracle.attentional_gnn(xA, xB, [st], heads=1)
+    np.testing.assert_allclose(A - xA, [[0.25, 3.25], [0.75, 0.0]], atol=1e-14)
+    np.testing.assert_allclose(B - xB, [[1.25, 0.75]], atol=1e-14)
