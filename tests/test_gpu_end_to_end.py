@@ -3,11 +3,14 @@
 fp32 networks are compared end to end: matching descriptors within 1e-4
 relative per keypoint, log assignments within 1e-3 absolute, matches equal
 except near ties.  bf16 networks are compared end to end on the descriptors
-(2e-2 relative); their log assignments and matches are checked on the score /
-Sinkhorn / extraction stage from generator descriptors (test_gpu_stages),
-because bf16 rounding through 18 stages moves the scores by far more than the
-1e-3 log-assignment bar.
+(2e-2 relative); their log assignments and matches are checked against the
+oracle's scores, Sinkhorn and extraction run on the GPU's own descriptors f
+(the 1024 x 1024 pair and sampled pairs of the ragged 32-pair batch, under
+both Sinkhorn schedules), because bf16 rounding through 18 stages moves the
+scores by far more than the 1e-3 log-assignment bar.  A small ragged fp32
+batch (empty pairs included) is compared end to end pair by pair.
 """
+import dataclasses
 import functools
 
 import numpy as np
@@ -240,3 +243,99 @@ def test_batch_sampled_pairs_vs_oracle(pair_index):
     e = max(rel_rows(g["f0"][pair_index, :M], ref["f0"]).max(), rel_rows(g["f1"][pair_index, :N], ref["f1"]).max())
     print(f"batch pair {pair_index} ({M}x{N}): f rel err {e:.2e}")
     assert e < 2e-2
+
+
+# ------------------------------------------- batch Sinkhorn head vs the oracle
+
+_SMALL_BATCH = dataclasses.replace(synth.CONFIGS[0], cid=5, batch=7, pad=40, planted="pair",
+                                   n_range=(0, 40), frac_range=(0.2, 0.5))
+
+
+def _column_sums_ok(logP, M, N, rtol=1e-4):
+    """Column sums of exp(logP) are b = [1_N, M]: the last half-step of every
+    iteration is the column update ([realcat] "Sinkhorn Algorithm")."""
+    cs = np.exp(np.asarray(logP, np.float64)).sum(axis=0)
+    want = np.concatenate([np.ones(N), [M]])
+    np.testing.assert_allclose(cs, want, rtol=rtol)
+
+
+@pytest.mark.parametrize("sched", ["one", "two"])
+def test_batch_fp32_sinkhorn_vs_oracle(sched):
+    """A ragged fp32 batch with empty pairs under the Sinkhorn head: every pair
+    against the oracle on the unpadded pair, end to end (the marginals use
+    each pair's true M_b, N_b inside the padded buffers); padded entries
+    -1 / 0."""
+    cfg = _SMALL_BATCH
+    w = synth.make_weights(synth.CONFIGS[0], bias_on=True)
+    b = synth.make_batch(cfg, seed=408)  # pair 0 has N = 0, pair 2 has M = 0
+    assert b["N"][0] == 0 and b["M"][2] == 0
+    g = _run_batch(cfg, sg.pack_weights(w), b, sinkhorn=sched)
+    checked = 0
+    for i, p in enumerate(b["pairs"]):
+        M, N = int(b["M"][i]), int(b["N"][i])
+        assert (g["matches0"][i, M:] == -1).all() and (g["scores0"][i, M:] == 0).all()
+        assert (g["matches1"][i, N:] == -1).all() and (g["scores1"][i, N:] == 0).all()
+        if M == 0 or N == 0:
+            assert (g["matches0"][i] == -1).all() and (g["matches1"][i] == -1).all()
+            continue
+        ref = oracle.superglue_match(p, w, T=cfg.T)
+        e = max(rel_rows(g["f0"][i, :M], ref["f0"]).max(), rel_rows(g["f1"][i, :N], ref["f1"]).max())
+        assert e < 1e-4, (i, M, N, e)
+        lp = g["logP"][i, :M + 1, :N + 1]
+        dl = np.abs(lp - ref["logP"]).max()
+        assert dl < 1e-3, (i, M, N, dl)
+        check_matches(g["matches0"][i, :M], g["matches1"][i, :N], ref["logP"], ref["matches0"], ref["matches1"])
+        _column_sums_ok(lp, M, N)
+        checked += 1
+    assert checked >= 4
+
+
+def _sampled_pairs(b):
+    """Smallest, largest and most unequal pairs of a ragged batch, plus the first."""
+    M, N = b["M"].astype(int), b["N"].astype(int)
+    picks = [0, int(np.argmin(M * N)), int(np.argmax(M * N)), int(np.argmax(np.abs(M - N)))]
+    return sorted(set(picks))
+
+
+def test_batch_bf16_sinkhorn_on_gpu_descriptors():
+    """The 32-pair ragged bf16 batch (masked keys excluded from softmax and
+    Sinkhorn): for sampled pairs, the oracle's scores, dustbin, Sinkhorn and
+    extraction on the batch's own descriptors f (fp32) against the batch's
+    log assignment and matches, under both schedules.  The descriptors
+    themselves are held to the bf16 bar by test_batch_sampled_pairs_vs_oracle."""
+    cfg, w, b = _batch()
+    W = sg.pack_weights(w)
+    runs = {s: _run_batch(cfg, W, b, sinkhorn=s) for s in ("one", "two")}
+    assert np.array_equal(runs["one"]["f0"], runs["two"]["f0"])
+    for i in _sampled_pairs(b):
+        M, N = int(b["M"][i]), int(b["N"][i])
+        f0 = runs["one"]["f0"][i, :M]
+        f1 = runs["one"]["f1"][i, :N]
+        ref = oracle.match_from_descriptors(f0, f1, w["alpha"], cfg.T)
+        for s, g in runs.items():
+            lp = g["logP"][i, :M + 1, :N + 1]
+            dl = np.abs(lp - ref["logP"]).max()
+            ex = check_matches(g["matches0"][i, :M], g["matches1"][i, :N], ref["logP"], ref["matches0"],
+                               ref["matches1"])
+            print(f"pair {i} ({M}x{N}) {s}: |dlogP| {dl:.2e} (|logP| up to {np.abs(ref['logP']).max():.0f}), "
+                  f"matches {int((ref['matches0'] >= 0).sum())}, exempt {ex}")
+            assert dl < 1e-3, (i, s, dl)
+            _column_sums_ok(lp, M, N)
+            assert (g["matches0"][i, M:] == -1).all() and np.isnan(g["logP"][i, M + 1:, :]).all()
+
+
+def test_pair1024_bf16_sinkhorn_on_gpu_descriptors():
+    """The 1024 x 1024 bf16 pair: the oracle's scores, Sinkhorn and extraction
+    on sg_match's own descriptors f against its log assignment and matches."""
+    cfg = synth.CONFIGS[2]
+    w = synth.make_weights(cfg)
+    pair = synth.make_pair(cfg)
+    g = _run(pair, sg.pack_weights(w), cfg)
+    ref = oracle.match_from_descriptors(g["f0"], g["f1"], w["alpha"], cfg.T)
+    dl = np.abs(g["logP"] - ref["logP"]).max()
+    ex = check_matches(g["matches0"], g["matches1"], ref["logP"], ref["matches0"], ref["matches1"])
+    print(f"cfg2 on GPU f: |dlogP| {dl:.2e}, matches {int((ref['matches0'] >= 0).sum())}, exempt {ex}")
+    assert dl < 1e-3
+    _column_sums_ok(g["logP"], cfg.M, cfg.N)
+    ok = g["matches0"] == ref["matches0"]
+    np.testing.assert_allclose(g["scores0"][ok], ref["scores0"][ok], rtol=2e-3, atol=1e-6)
