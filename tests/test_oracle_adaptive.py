@@ -17,6 +17,13 @@ import synth
 from golden_io import confidence_threshold_example
 
 
+@pytest.fixture(autouse=True)
+def _each_oracle(oracle_impl, monkeypatch):
+    """Every pin runs against both oracle implementations (plain C, numpy)."""
+    monkeypatch.setitem(globals(), "oracle", oracle_impl)
+
+
+
 def _frozen(cfg, L=3, seed=None):
     """Adaptive weights whose GNN stages leave the states unchanged and whose
     encoder is zero: every layer's states are the descriptors."""

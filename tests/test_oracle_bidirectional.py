@@ -8,11 +8,19 @@ merge projection skipped, or the stage routed to standard attention.
 import math
 
 import numpy as np
+import pytest
 import torch
 import torch.nn.functional as F
 
 import oracle
 import synth
+
+
+@pytest.fixture(autouse=True)
+def _each_oracle(oracle_impl, monkeypatch):
+    """Every pin runs against both oracle implementations (plain C, numpy)."""
+    monkeypatch.setitem(globals(), "oracle", oracle_impl)
+
 
 
 def _rng(seed):

@@ -15,6 +15,13 @@ import oracle
 import synth
 
 
+@pytest.fixture(autouse=True)
+def _each_oracle(oracle_impl, monkeypatch):
+    """Every pin runs against both oracle implementations (plain C, numpy)."""
+    monkeypatch.setitem(globals(), "oracle", oracle_impl)
+
+
+
 def _rng(seed):
     return np.random.Generator(np.random.PCG64(seed))
 

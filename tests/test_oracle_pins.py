@@ -16,6 +16,13 @@ import synth
 from golden_io import attention_example, normalize_example, sinkhorn_demo
 
 
+@pytest.fixture(autouse=True)
+def _each_oracle(oracle_impl, monkeypatch):
+    """Every pin runs against both oracle implementations (plain C, numpy)."""
+    monkeypatch.setitem(globals(), "oracle", oracle_impl)
+
+
+
 def _rng(seed):
     return np.random.Generator(np.random.PCG64(seed))
 

@@ -8,9 +8,17 @@ import cmath
 import math
 
 import numpy as np
+import pytest
 
 import oracle
 import synth
+
+
+@pytest.fixture(autouse=True)
+def _each_oracle(oracle_impl, monkeypatch):
+    """Every pin runs against both oracle implementations (plain C, numpy)."""
+    monkeypatch.setitem(globals(), "oracle", oracle_impl)
+
 
 
 def _rng(seed):
