@@ -252,7 +252,9 @@ sg_status sg_match(const float* kptsA, const float* descA, const float* confA, i
                    int32_t* out_matches, float* out_scores, const sg_opts* opts);
 
 /*
- * B independent pairs in one call.  Inputs are padded: kptsA [B][Mpad][2],
+ * B independent pairs in one call: sg_match on every pair (the pass above;
+ * the forward walk-through of the SuperGlue_Code_Learning notes), with the
+ * pairs' point counts given separately.  Inputs are padded: kptsA [B][Mpad][2],
  * descA [B][Mpad][D], confA [B][Mpad] (B likewise with Npad); M, N are HOST
  * arrays of the true counts (0 <= M[b] <= Mpad).  Padded points are absent
  * from every softmax, from Sinkhorn (whose marginals use the true counts) and
@@ -270,13 +272,24 @@ sg_status sg_match_batch(int32_t B, int32_t Mpad, int32_t Npad, const int32_t* M
 
 /* ---- stage entry points (same conventions; for per-stage parity and timing) ---- */
 
-/* Encoder: x0 [n][D] fp32 = desc + MLP_enc(normalised kpts, conf).
-   image_w/image_h > 0: kpts in pixels; both 0: already normalised. */
+/* Encoder (realcat notes, section "特征点Encode": KeypointEncoder adds an
+   MLP of (x, y, c) to each descriptor; the keypoints are normalised as in
+   the SuperGlue_Code_Learning notes' normalize_keypoints):
+   x0 [n][D] fp32 = desc + MLP_enc(normalised kpts, conf), ReLU between the
+   layers, none after the last.  image_w/image_h > 0: kpts in pixels; both
+   0: already normalised.  kpts [n][2], conf [n], desc [n][D] fp32 inputs;
+   x_out [n][D] caller-owned.  n == 0 enqueues nothing. */
 sg_status sg_stage_encode(const float* kpts, const float* conf, const float* desc, int32_t n,
                           float image_w, float image_h, const sg_weights* weights,
                           float* x_out, const sg_opts* opts);
 
-/* Stages s0 .. s1-1 of the GNN, in place on the fp32 states xA [M][D], xB [N][D]. */
+/* Stages s0 .. s1-1 of the attentional GNN (realcat notes, sections
+   "Attentional Aggregation" and "多层GNN"; the huluoboge.top blog's
+   message-passing sections): even stages self, odd stages cross; per stage
+   multi-head attention with logits scaled by 1/sqrt(D/H), the merge
+   projection, and x += W2 ReLU(W1 [x || m] + b1) + b2 for both images from
+   their pre-stage states.  In place on the caller's fp32 states xA [M][D],
+   xB [N][D]; 0 <= s0 <= s1 <= 2 L_max (SG_ERR_INVALID_ARG otherwise). */
 sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weights* weights,
                        int32_t s0, int32_t s1, const sg_opts* opts);
 
@@ -287,12 +300,19 @@ sg_status sg_stage_gnn(float* xA, int32_t M, float* xB, int32_t N, const sg_weig
 sg_status sg_stage_gnn_pos(float* xA, const float* posA, int32_t M, float* xB, const float* posB, int32_t N,
                            const sg_weights* weights, int32_t s0, int32_t s1, const sg_opts* opts);
 
-/* Final projection f [n][D] fp32 = W_f x + b_f. */
+/* Final projection of the SuperGlue_Code_Learning notes' forward (the
+   matching descriptors, realcat notes section "Attentional Aggregation",
+   last equation): f [n][D] fp32 = W_f x + b_f from the fp32 states
+   x [n][D]; f_out caller-owned. */
 sg_status sg_stage_project(const float* x, int32_t n, const sg_weights* weights, float* f_out,
                            const sg_opts* opts);
 
-/* Scores S = fA fB^T / sqrt(D), dustbin alpha, T Sinkhorn iterations and
-   extraction, from matching descriptors fA [M][D], fB [N][D] (fp32). */
+/* The optimal-matching layer from matching descriptors fA [M][D], fB [N][D]
+   (fp32): scores S = fA fB^T / sqrt(D) (realcat notes section "匹配得分预测";
+   the forward notes' scaling), the dustbin row and column of score alpha
+   (section "遮挡以及可见性"), T log-domain Sinkhorn iterations (section
+   "Sinkhorn Algorithm") and the mutual-argmax extraction of the forward
+   notes.  Outputs and options as sg_match; D a positive multiple of 8. */
 sg_status sg_stage_match(const float* fA, int32_t M, const float* fB, int32_t N, int32_t D,
                          float alpha, int32_t T, int32_t* out_matches, float* out_scores,
                          const sg_opts* opts);
@@ -313,6 +333,49 @@ sg_status sg_stage_match_ds(const float* fA, const float* xA, int32_t M, const f
 
 /* Workspace bytes of sg_stage_match_ds for M x N points of dimension D. */
 size_t sg_stage_match_ds_workspace_size(int32_t M, int32_t N, int32_t D);
+
+/*
+ * The log-domain Sinkhorn iterations of the optimal-matching layer on
+ * caller-given couplings (realcat notes, section "Sinkhorn Algorithm":
+ * log_optimal_transport / log_sinkhorn_iterations).
+ *   Z [(M+1)][ldZ] fp32, natural log: row M and column N are the dustbin
+ *     row and column (any values; the pass itself uses the constant alpha).
+ *   Marginals: a = [1 (M times), N] and b = [1 (N times), M], each divided
+ *     by M + N.  From u = v = 0, T iterations of
+ *       u_i = log(a_i / (M+N)) - log sum_j exp(Z_ij + v_j),   i <= M,
+ *       v_j = log(b_j / (M+N)) - log sum_i exp(Z_ij + u_i),   j <= N.
+ *   Outputs (device, caller-owned): u [M+1], v [N+1] (natural log; T == 0
+ *     gives zeros) and, when logP is non-NULL, the log assignment
+ *     logP [(M+1)][ldP] = Z + u + v + log(M+N).
+ * Runs the pass's own sweep kernels (two per iteration, over Z and its
+ * transpose) in fp32 with base-2 exponentials.  Errors: M < 1 or N < 1 (the
+ * pages run the layer only on non-empty images), T < 0, NULL Z / u / v,
+ * ldZ < N+1 or (with logP) ldP < N+1 -> SG_ERR_INVALID_ARG; M or N above
+ * 4096 -> SG_ERR_UNSUPPORTED.  Workspace: sg_stage_sinkhorn_workspace_size.
+ */
+sg_status sg_stage_sinkhorn(const float* Z, int64_t ldZ, int32_t M, int32_t N, int32_t T, float* u, float* v,
+                            float* logP, int64_t ldP, const sg_opts* opts);
+
+/* Workspace bytes of sg_stage_sinkhorn and sg_stage_extract for M x N points. */
+size_t sg_stage_sinkhorn_workspace_size(int32_t M, int32_t N);
+
+/*
+ * Match extraction from a given log assignment logP [(M+1)][ldP] fp32
+ * (natural log), after the SuperGlue_Code_Learning notes' forward ("Get the
+ * matches with score above match_threshold"): on the real block, each row's
+ * best column and each column's best row (the lowest index among equal
+ * maxima); a pair is a match when each is the other's pick and exp(logP) >
+ * threshold (decided in log space; threshold <= 0 keeps every mutual pick).
+ * Outputs (device, caller-owned): out_matches0 [M] (index into B or -1),
+ * out_scores0 [M] (exp(logP) of a mutual pick, else 0); optional
+ * out_matches1 / out_scores1 [N] likewise.  M == 0 or N == 0: -1 / 0.
+ * Errors: negative counts, NULL required pointers, ldP < N+1 ->
+ * SG_ERR_INVALID_ARG; M or N above 4096 -> SG_ERR_UNSUPPORTED.  Workspace:
+ * sg_stage_sinkhorn_workspace_size(M, N).
+ */
+sg_status sg_stage_extract(const float* logP, int64_t ldP, int32_t M, int32_t N, float threshold,
+                           int32_t* out_matches0, float* out_scores0, int32_t* out_matches1, float* out_scores1,
+                           const sg_opts* opts);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* sg_last_error(void);

@@ -20,7 +20,7 @@ from ._lib import (SG_BF16, SG_CROSS_BIDIRECTIONAL, SG_CROSS_STANDARD, SG_F32, S
 
 __all__ = ["Weights", "weights_config", "pack_weights", "workspace_size", "sg_match",
            "sg_match_batch", "sg_stage_encode", "sg_stage_gnn", "sg_stage_project",
-           "sg_stage_match", "sg_stage_match_ds", "lib", "SgError", "SG_K_GEMM", "SG_K_ATTENTION", "SG_K_SINKHORN",
+           "sg_stage_match", "sg_stage_match_ds", "sg_stage_sinkhorn", "sg_stage_extract", "lib", "SgError", "SG_K_GEMM", "SG_K_ATTENTION", "SG_K_SINKHORN",
            "SG_N_STAGE_EVENTS"]
 
 
@@ -424,4 +424,48 @@ def sg_stage_match_ds(fA, fB, xA, xB, wz, bz: float, *, threshold: float = 0.0, 
                                        _ptr(out["matches0"]), _ptr(out["scores0"]), C.byref(o)),
                "sg_stage_match_ds")
     out["n_kernel_launches"] = count.value
+    return out
+
+
+def sg_stage_sinkhorn(Z, T: int, *, want_logP=True, workspace=None, stream=None, graph=True) -> dict:
+    """T log-domain Sinkhorn iterations on the couplings Z [(M+1)][N+1] (float32
+    CUDA tensor, natural log, last row and column the dustbins).  Returns the
+    duals u [M+1], v [N+1] and (want_logP) logP = Z + u + v + log(M+N)."""
+    if Z.dim() != 2:
+        raise ValueError("Z must be [(M+1)][(N+1)]")
+    M, N = Z.shape[0] - 1, Z.shape[1] - 1
+    _check_tensor(Z, "Z", torch.float32)
+    dev = Z.device
+    out = {"u": torch.empty(M + 1, dtype=torch.float32, device=dev),
+           "v": torch.empty(N + 1, dtype=torch.float32, device=dev)}
+    if want_logP:
+        out["logP"] = torch.empty((M + 1, N + 1), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib().sg_stage_sinkhorn_workspace_size(max(M, 0), max(N, 0))))
+    o, keep, _ = _opts(dev, workspace=workspace, stream=stream, graph=graph)
+    _lib.check(lib().sg_stage_sinkhorn(_ptr(Z), N + 1, M, N, int(T), _ptr(out["u"]), _ptr(out["v"]),
+                                       _ptr(out.get("logP")), N + 1, C.byref(o)), "sg_stage_sinkhorn")
+    return out
+
+
+def sg_stage_extract(logP, *, threshold: float = 0.0, want_matches1=True, workspace=None, stream=None,
+                     graph=True) -> dict:
+    """Mutual-argmax extraction from the log assignment logP [(M+1)][N+1]
+    (float32 CUDA tensor, natural log)."""
+    if logP.dim() != 2:
+        raise ValueError("logP must be [(M+1)][(N+1)]")
+    M, N = logP.shape[0] - 1, logP.shape[1] - 1
+    _check_tensor(logP, "logP", torch.float32)
+    dev = logP.device
+    out = {"matches0": torch.empty(M, dtype=torch.int32, device=dev),
+           "scores0": torch.empty(M, dtype=torch.float32, device=dev)}
+    if want_matches1:
+        out["matches1"] = torch.empty(N, dtype=torch.int32, device=dev)
+        out["scores1"] = torch.empty(N, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib().sg_stage_sinkhorn_workspace_size(max(M, 0), max(N, 0))))
+    o, keep, _ = _opts(dev, workspace=workspace, stream=stream, graph=graph)
+    _lib.check(lib().sg_stage_extract(_ptr(logP), N + 1, M, N, float(threshold), _ptr(out["matches0"]),
+                                      _ptr(out["scores0"]), _ptr(out.get("matches1")), _ptr(out.get("scores1")),
+                                      C.byref(o)), "sg_stage_extract")
     return out

@@ -587,8 +587,8 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
              return launch_ds_stats(Z, ZT, pl.pt, ds->X, D, ds->w_dtype, ds->wz, ds->bz_dev, ds->bz, U, V, UD, VD, st);
            }), "double-softmax statistics");
     tm.stage(SG_EV_SINKHORN);
-    HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, 1, st), "column argmax");
-    HIPCHK(launch_sink_extract(Z, pl.pt, U, V, idx1, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, 1, st),
+    HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, EXT_DS, st), "column argmax");
+    HIPCHK(launch_sink_extract(Z, pl.pt, U, V, idx1, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, EXT_DS, st),
            "extract");
     if (out.logP)
       HIPCHK(launch_ds_write_logp(Z, pl.pt, U, V, UD, VD, out.logP, out.logP_ld, out.logP_stride, pl.ru, st),
@@ -609,7 +609,7 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
       HIPCHK(launch_fill_f32(V, 0.f, (int)pl.vf, st), "zero v");
     }
     tm.stage(SG_EV_SINKHORN);
-    HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, 0, st), "column argmax");
+    HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, EXT_SINKHORN, st), "column argmax");
   } else {
     // T iterations: u = log mu - lse_j(Z + v) with the column partials of
     // Z + u in the same pass; then v = log nu - lse over the partials.  The
@@ -633,11 +633,101 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
     }
     tm.stage(SG_EV_SINKHORN);
   }
-  HIPCHK(launch_sink_extract(Z, pl.pt, U, V, idx1, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, 0, st),
+  HIPCHK(launch_sink_extract(Z, pl.pt, U, V, idx1, p.Mpad, p.Npad, thr, out.m0, out.s0, out.m1, out.s1, EXT_SINKHORN, st),
          "extract");
   if (out.logP)
     HIPCHK(launch_write_logp(Z, pl.pt, U, V, alpha2, alpha_dev, out.logP, out.logP_ld, out.logP_stride, pl.ru, st),
            "logP");
+  return SG_OK;
+}
+
+// ------------------------------------------- Sinkhorn / extraction stages
+//
+// The stage entry points on caller-given matrices run the pass's own sweep
+// and extraction kernels on one pair, through the same internal layout:
+// the real block in Z and ZT (base-2 scaled for Sinkhorn, as given for
+// extraction), the dustbin column and row (Sinkhorn: any values, not only
+// the constant alpha of the pass), the base-2 duals and the column argmax.
+
+struct StageWs {
+  size_t Z, ZT, BCOL, BROW, U, V, IDX1, total;
+};
+
+StageWs stage_ws(long M, long N) {
+  StageWs L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+  L.Z = take((size_t)M * ld4((int)N) * 4);
+  L.ZT = take((size_t)N * ld4((int)M) * 4);
+  L.BCOL = take((size_t)ld4((int)M + 1) * 4);
+  L.BROW = take((size_t)ld4((int)N + 1) * 4);
+  L.U = take((size_t)ld4((int)M + 1) * 4);
+  L.V = take((size_t)ld4((int)N + 1) * 4);
+  L.IDX1 = take((size_t)ld4((int)N) * 4);
+  L.total = o;
+  return L;
+}
+
+template <class T>
+T* ws_at(char* ws, size_t off) {
+  return reinterpret_cast<T*>(ws + off);
+}
+
+// T iterations on C [(M+1)][ldc] (M, N >= 1): u_i = log mu_i - lse_j, then
+// v_j = log nu_j - lse_i, with mu = [1_M, N] / (M+N), nu = [1_N, M] / (M+N)
+// (the pass's marginals); then the natural-log duals and logP.
+sg_status enqueue_stage_sinkhorn(const float* C, int64_t ldc, int M, int N, int T, float* u, float* v, float* logP,
+                                 int64_t ldp, char* ws, const StageWs& L, hipStream_t st) {
+  float* Z = ws_at<float>(ws, L.Z);
+  float* ZT = ws_at<float>(ws, L.ZT);
+  float* bcol = ws_at<float>(ws, L.BCOL);
+  float* brow = ws_at<float>(ws, L.BROW);
+  float* U = ws_at<float>(ws, L.U);
+  float* V = ws_at<float>(ws, L.V);
+  HIPCHK(launch_stage_couplings(C, ldc, M, N, 1.4426950408889634f, Z, ZT, bcol, brow, st), "stage couplings");
+  // the same single-precision logarithms as the pass's sweeps
+  const float lmn = std::log2((float)(M + N));
+  for (int it = 0; it < T; ++it) {
+    HIPCHK(launch_lse_explicit(Z, it == 0 ? nullptr : V, U, M, N, 0.f - lmn, std::log2((float)N) - lmn, bcol, brow,
+                               st),
+           "sinkhorn rows");
+    HIPCHK(launch_lse_explicit(ZT, U, V, N, M, 0.f - lmn, std::log2((float)M) - lmn, brow, bcol, st),
+           "sinkhorn cols");
+  }
+  if (T == 0) {
+    HIPCHK(launch_fill_f32(U, 0.f, M + 1, st), "zero u");
+    HIPCHK(launch_fill_f32(V, 0.f, N + 1, st), "zero v");
+  }
+  HIPCHK(launch_stage_duals(C, ldc, M, N, U, V, u, v, logP, ldp, st), "duals");
+  return SG_OK;
+}
+
+// Mutual-argmax extraction of the real block of a natural-log assignment
+// P [(M+1)][ldp] (M, N >= 1), through the pass's extraction kernels.
+sg_status enqueue_stage_extract(const float* P, int64_t ldp, int M, int N, float thr, int32_t* m0, float* s0,
+                                int32_t* m1, float* s1, char* ws, const StageWs& L, hipStream_t st) {
+  Problem p;
+  p.B = 1; p.Mpad = M; p.Npad = N; p.M = {M}; p.N = {N};
+  Plan pl;
+  make_plan(p, pl);
+  float* Z = ws_at<float>(ws, L.Z);
+  float* ZT = ws_at<float>(ws, L.ZT);
+  int* idx1 = ws_at<int>(ws, L.IDX1);
+  HIPCHK(launch_stage_couplings(P, ldp, M, N, 1.f, Z, ZT, nullptr, nullptr, st), "stage assignment");
+  HIPCHK(launch_col_argmax(ZT, pl.pt, nullptr, idx1, N, m1, s1, EXT_RAW, st), "column argmax");
+  HIPCHK(launch_sink_extract(Z, pl.pt, nullptr, nullptr, idx1, M, N, thr, m0, s0, m1, s1, EXT_RAW, st), "extract");
+  return SG_OK;
+}
+
+sg_status check_stage_sinkhorn(const float* Z, int64_t ldZ, int32_t M, int32_t N, int32_t T, const float* u,
+                               const float* v, const float* logP, int64_t ldP) {
+  if (M < 1 || N < 1)
+    return fail(SG_ERR_INVALID_ARG, "M = %d, N = %d: the optimal-matching layer runs on non-empty images", M, N);
+  if (M > 4096 || N > 4096) return fail(SG_ERR_UNSUPPORTED, "more than 4096 points per image");
+  if (T < 0) return fail(SG_ERR_INVALID_ARG, "T < 0");
+  if (!Z || !u || !v) return fail(SG_ERR_INVALID_ARG, "Z, u or v is NULL");
+  if (ldZ < (int64_t)N + 1) return fail(SG_ERR_INVALID_ARG, "ldZ < N+1");
+  if (logP && ldP < (int64_t)N + 1) return fail(SG_ERR_INVALID_ARG, "ldP < N+1");
   return SG_OK;
 }
 
@@ -1352,6 +1442,58 @@ sg_status sg_stage_match_ds(const float* fA, const float* xA, int32_t M, const f
     tm.stage(SG_EV_END);
     tm.finish();
     return SG_OK;
+  });
+}
+
+size_t sg_stage_sinkhorn_workspace_size(int32_t M, int32_t N) {
+  if (M < 0 || N < 0) return 0;
+  return stage_ws(M, N).total;
+}
+
+sg_status sg_stage_sinkhorn(const float* Z, int64_t ldZ, int32_t M, int32_t N, int32_t T, float* u, float* v,
+                            float* logP, int64_t ldP, const sg_opts* opts) {
+  g_err.clear();
+  sg_status s;
+  if ((s = check_opts(opts)) != SG_OK) return s;
+  if ((s = check_stage_sinkhorn(Z, ldZ, M, N, T, u, v, logP, ldP)) != SG_OK) return s;
+  const StageWs L = stage_ws(M, N);
+  void* wsp;
+  if ((s = get_workspace(opts, L.total, &wsp)) != SG_OK) return s;
+  std::string key;
+  put(key, 3); put(key, Z); put(key, ldZ); put(key, M); put(key, N); put(key, T); put(key, u); put(key, v);
+  put(key, logP); put(key, ldP); put(key, wsp);
+  return run_maybe_graph(key, opts, stream_of(opts), [&](hipStream_t cs) -> sg_status {
+    return enqueue_stage_sinkhorn(Z, ldZ, M, N, T, u, v, logP, ldP, reinterpret_cast<char*>(wsp), L, cs);
+  });
+}
+
+sg_status sg_stage_extract(const float* logP, int64_t ldP, int32_t M, int32_t N, float threshold,
+                           int32_t* out_matches0, float* out_scores0, int32_t* out_matches1, float* out_scores1,
+                           const sg_opts* opts) {
+  g_err.clear();
+  sg_status s;
+  if ((s = check_opts(opts)) != SG_OK) return s;
+  if (M < 0 || N < 0) return fail(SG_ERR_INVALID_ARG, "negative point count");
+  if (M > 4096 || N > 4096) return fail(SG_ERR_UNSUPPORTED, "more than 4096 points per image");
+  if (M > 0 && (!out_matches0 || !out_scores0)) return fail(SG_ERR_INVALID_ARG, "out_matches0/out_scores0 is NULL");
+  if (out_scores1 && !out_matches1) return fail(SG_ERR_INVALID_ARG, "out_scores1 without out_matches1");
+  if (M > 0 && N > 0 && !logP) return fail(SG_ERR_INVALID_ARG, "logP is NULL");
+  if (M > 0 && N > 0 && ldP < (int64_t)N + 1) return fail(SG_ERR_INVALID_ARG, "ldP < N+1");
+  hipStream_t st = stream_of(opts);
+  if (M == 0 || N == 0) {
+    HIPCHK(launch_fill_empty(out_matches0, out_scores0, M, st), "empty output");
+    if (out_matches1) HIPCHK(launch_fill_empty(out_matches1, out_scores1, N, st), "empty output");
+    return SG_OK;
+  }
+  const StageWs L = stage_ws(M, N);
+  void* wsp;
+  if ((s = get_workspace(opts, L.total, &wsp)) != SG_OK) return s;
+  std::string key;
+  put(key, 4); put(key, logP); put(key, ldP); put(key, M); put(key, N); put(key, threshold); put(key, out_matches0);
+  put(key, out_scores0); put(key, out_matches1); put(key, out_scores1); put(key, wsp);
+  return run_maybe_graph(key, opts, st, [&](hipStream_t cs) -> sg_status {
+    return enqueue_stage_extract(logP, ldP, M, N, threshold, out_matches0, out_scores0, out_matches1, out_scores1,
+                                 reinterpret_cast<char*>(wsp), L, cs);
   });
 }
 

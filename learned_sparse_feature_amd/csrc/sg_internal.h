@@ -157,12 +157,30 @@ hipError_t launch_sink_cols(const PairTable& pt, const float* P, const float* Pd
                             hipStream_t st);
 hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const float* w_in, float* w_out,
                       float alpha2, const float* alpha_dev, int total_rows, hipStream_t st);
-// ds = 1: the double-softmax head (real block 2 Z + u + v, see sg_double_softmax.hip)
+// What the extraction kernels read as the real block of the log assignment
+// (their `mode`): EXT_SINKHORN: Z2 + u + v + log2(M+N) (base 2); EXT_DS: the
+// double-softmax head, 2 Z2 + u + v (base 2, see sg_double_softmax.hip);
+// EXT_RAW: Z itself, a natural-log assignment given by the caller (u, v unused).
+enum { EXT_SINKHORN = 0, EXT_DS = 1, EXT_RAW = 2 };
 hipError_t launch_col_argmax(const float* ZT, const PairTable& pt, const float* u, int* idx1, int Npad,
-                             int32_t* m1, float* s1, int ds, hipStream_t st);
+                             int32_t* m1, float* s1, int mode, hipStream_t st);
 hipError_t launch_sink_extract(const float* Z, const PairTable& pt, const float* u, const float* v,
                                const int* idx1, int Mpad, int Npad, float thr, int32_t* m0, float* s0,
-                               int32_t* m1, float* s1, int ds, hipStream_t st);
+                               int32_t* m1, float* s1, int mode, hipStream_t st);
+// Stage entry points on caller-given (M+1) x (N+1) matrices C (leading
+// dimension ldc): the real block times `scale` into Z [M][ld4(N)] and ZT
+// [N][ld4(M)]; with bcol / brow non-null, the dustbin column (M+1 entries,
+// the corner last) and row (N+1 entries) times `scale`.
+hipError_t launch_stage_couplings(const float* C, int64_t ldc, int M, int N, float scale, float* Z, float* ZT,
+                                  float* bcol, float* brow, hipStream_t st);
+// u = ln2 u2, v = ln2 v2 and (logP non-null) logP = C + u + v + log(M+N).
+hipError_t launch_stage_duals(const float* C, int64_t ldc, int M, int N, const float* u2, const float* v2, float* u,
+                              float* v, float* logP, int64_t ldp, hipStream_t st);
+// One Sinkhorn sweep with explicit dustbins over the nr + 1 rows of Z (or
+// ZT): bown [nr + 1] the rows' dustbin-column entries (corner last), bcross
+// [ld4(nc + 1)] the dustbin row's entries.
+hipError_t launch_lse_explicit(const float* Z, const float* w_in, float* w_out, int nr, int nc, float lm_real,
+                               float lm_dust, const float* bown, const float* bcross, hipStream_t st);
 hipError_t launch_write_logp(const float* Z, const PairTable& pt, const float* u, const float* v,
                              float alpha2, const float* alpha_dev, float* logP, int64_t ld,
                              int64_t pair_stride, int total_rows, hipStream_t st);

@@ -404,19 +404,23 @@ __global__ __launch_bounds__(256) void k_sink_cols(PairTable pt, const float* __
 // (WHICH = 1): lane-owned float4 groups zq / wq of the row and of the
 // other side's duals (columns 4*(lane + 64 k) .. +3, loaded clamped in
 // bounds: entries past nc and the dustbin row i == nr are replaced here).
-template <int NV4>
+// XB (explicit dustbins, the stage entry points on caller-given couplings):
+// zq of the dustbin row holds that row's own entries and `dust` is the
+// row's dustbin-column entry (the corner for i == nr); otherwise both are
+// the constant alpha2.
+template <int NV4, bool XB = false>
 __device__ __forceinline__ float lse_row(const float4 (&zq)[NV4], const float4 (&wq)[NV4], float wd, float alpha2,
-                                         int i, int nr, int nc, int lane) {
+                                         int i, int nr, int nc, int lane, float dust = 0.f) {
   float x[NV4][4];
 #pragma unroll
   for (int k = 0; k < NV4; ++k) {
     const int j = 4 * (lane + 64 * k);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      x[k][c] = j + c < nc ? (i < nr ? f4c(zq[k], c) : alpha2) + f4c(wq[k], c) : -INFINITY;
+      x[k][c] = j + c < nc ? ((XB || i < nr) ? f4c(zq[k], c) : alpha2) + f4c(wq[k], c) : -INFINITY;
   }
-  // the dustbin column (j = nc) is alpha for every row
-  const float xd = alpha2 + wd;
+  // the dustbin column (j = nc): alpha for every row, or the row's own entry
+  const float xd = (XB ? dust : alpha2) + wd;
   float mx = xd;
 #pragma unroll
   for (int k = 0; k < NV4; ++k)
@@ -483,27 +487,32 @@ __global__ __launch_bounds__(256) void k_lse(const float* __restrict__ Zbase, Pa
 // argument loads (no pair search, no table lookups ahead of them).
 // Z: the pair's Z or ZT; wv / w_out: the duals read / written (offsets
 // applied); nr: rows (the dustbin row is nr); nc: columns; lmn = log2(M+N).
-template <int NV4>
+// XB: explicit dustbins (stage entry points): bown [nr + 1] holds each row's
+// dustbin-column entry (the corner last) and bcross [ld4(nc + 1)] the
+// dustbin row's entries; alpha2 / alpha_dev are unused.
+template <int NV4, bool XB>
 __global__ __launch_bounds__(256) void k_lse_one(const float* __restrict__ Z, const float* __restrict__ wv,
                                                  float* __restrict__ w_out, int nr, int nc, float alpha2,
                                                  const float* __restrict__ alpha_dev, float lm_real,
-                                                 float lm_dust) {
+                                                 float lm_dust, const float* __restrict__ bown,
+                                                 const float* __restrict__ bcross) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave_id();
   if (i > nr) return;
   float4 zq[NV4], wq[NV4];
-  lse_loads<NV4>(Z + (size_t)max(min(i, nr - 1), 0) * ld4(nc), wv, nr, nc, lane, zq, wq);
+  const float* row = (XB && i >= nr) ? bcross : Z + (size_t)max(min(i, nr - 1), 0) * ld4(nc);
+  lse_loads<NV4>(row, wv, XB ? 1 : nr, nc, lane, zq, wq);
   const float wd = wv ? wv[nc] : 0.f;
-  if (alpha_dev) alpha2 = alpha_dev[0] * kLog2e;
-  const float l = lse_row<NV4>(zq, wq, wd, alpha2, i, nr, nc, lane);
+  const float dust = XB ? bown[i] : 0.f;
+  if (!XB && alpha_dev) alpha2 = alpha_dev[0] * kLog2e;
+  const float l = lse_row<NV4, XB>(zq, wq, wd, alpha2, i, nr, nc, lane, dust);
   if (lane == 0) w_out[i] = (i < nr ? lm_real : lm_dust) - l;
 }
 
 // Column argmax over the real rows (argmax_i Z2_ij + u_i, lowest index on
 // ties) from the rows of ZT, one wave per column; also the default (-1 / 0)
-// side-B outputs that the extraction overwrites for mutual matches.  DS: the
-// double-softmax head, whose real block is 2 Z2 + u + v.
-template <int NV4, bool DS>
+// side-B outputs that the extraction overwrites for mutual matches.
+template <int NV4, int MODE>
 __global__ __launch_bounds__(256) void k_col_argmax(const float* __restrict__ ZTb, PairTable pt,
                                                     const float* __restrict__ u,
                                                     int* __restrict__ idx1, int Npad,
@@ -517,7 +526,7 @@ __global__ __launch_bounds__(256) void k_col_argmax(const float* __restrict__ ZT
   const int j = g - (pt.vpre[b] - b);
   const int M = pt.M[b];
   const float* row = ZTb + pt.zt_off[b] + (size_t)j * ld4(M);
-  const float* uu = u + pt.uoff[b];
+  const float* uu = MODE == EXT_RAW ? nullptr : u + pt.uoff[b];
   float best = -INFINITY;
   int bi = 0x7fffffff;
 #pragma unroll
@@ -525,10 +534,10 @@ __global__ __launch_bounds__(256) void k_col_argmax(const float* __restrict__ ZT
     const int i = 4 * (lane + 64 * k);
     if (i < M) {
       const float4 z = *reinterpret_cast<const float4*>(row + i);
-      const float4 q = *reinterpret_cast<const float4*>(uu + i);
+      const float4 q = MODE == EXT_RAW ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const float4*>(uu + i);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float y = (DS ? 2.f * f4c(z, c) : f4c(z, c)) + f4c(q, c);
+        const float y = (MODE == EXT_DS ? 2.f * f4c(z, c) : f4c(z, c)) + f4c(q, c);
         if (i + c < M && y > best) {
           best = y;
           bi = i + c;
@@ -548,9 +557,10 @@ __global__ __launch_bounds__(256) void k_col_argmax(const float* __restrict__ ZT
 
 // Row argmax of the final log assignment (argmax_j Z_ij + v_j; lowest index
 // on ties), mutual check against idx1, score exp(logP), threshold; side-B
-// outputs of mutual pairs; -1 / 0 for padded entries and empty pairs.  DS:
-// the double-softmax head (2 Z + u + v, no marginal normalisation to undo).
-template <int NV4, bool DS>
+// outputs of mutual pairs; -1 / 0 for padded entries and empty pairs.  MODE:
+// see EXT_* above (the double-softmax head has no marginal normalisation to
+// undo; a raw assignment is read as given).
+template <int NV4, int MODE>
 __global__ __launch_bounds__(256) void k_sink_extract(const float* __restrict__ Zb, PairTable pt,
                                                       const float* __restrict__ u,
                                                       const float* __restrict__ v,
@@ -582,7 +592,7 @@ __global__ __launch_bounds__(256) void k_sink_extract(const float* __restrict__ 
   }
   const int ldz = ld4(N);
   const float* row = Zb + pt.z_off[b] + (size_t)t * ldz;
-  const float* vv = v + pt.voff[b];
+  const float* vv = MODE == EXT_RAW ? nullptr : v + pt.voff[b];
   float best = -INFINITY;
   int bj = 0x7fffffff;
 #pragma unroll
@@ -590,8 +600,8 @@ __global__ __launch_bounds__(256) void k_sink_extract(const float* __restrict__ 
     const int j = 4 * (lane + 64 * k);
     if (j < N) {
       const float4 z = *reinterpret_cast<const float4*>(row + j);
-      const float4 q = *reinterpret_cast<const float4*>(vv + j);
-      const float zm = DS ? 2.f : 1.f;
+      const float4 q = MODE == EXT_RAW ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const float4*>(vv + j);
+      const float zm = MODE == EXT_DS ? 2.f : 1.f;
       const float x[4] = {zm * z.x + q.x, zm * z.y + q.y, zm * z.z + q.z, zm * z.w + q.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -605,11 +615,16 @@ __global__ __launch_bounds__(256) void k_sink_extract(const float* __restrict__ 
   float score = 0.f;
   int mo = -1;
   if (mutual) {
-    const float lp2 = best + u[pt.uoff[b] + t] + (DS ? 0.f : log2f((float)(M + N)));
-    score = exp2f(lp2);
     // exp(logP) > thr decided in the log domain (exact for any finite logP:
     // exp never reaches 0, so a non-positive threshold accepts every mutual match)
-    if (thr <= 0.f || lp2 > log2f(thr)) mo = bj;
+    if (MODE == EXT_RAW) {
+      score = expf(best);
+      if (thr <= 0.f || best > logf(thr)) mo = bj;
+    } else {
+      const float lp2 = best + u[pt.uoff[b] + t] + (MODE == EXT_DS ? 0.f : log2f((float)(M + N)));
+      score = exp2f(lp2);
+      if (thr <= 0.f || lp2 > log2f(thr)) mo = bj;
+    }
     if (m1) {
       m1[(size_t)b * Npad + bj] = mo >= 0 ? t : -1;
       if (s1) s1[(size_t)b * Npad + bj] = score;
@@ -640,6 +655,94 @@ __global__ __launch_bounds__(256) void k_write_logp(const float* __restrict__ Zb
     const float z = (i < M && j < N) ? row[j] : alpha2;
     logP[b * pair_stride + (int64_t)i * ld + j] = kLn2 * (z + ui + v[pt.voff[b] + j] + lmn);
   }
+}
+
+// ------------------------------------------------- stage entry points
+//
+// Caller-given (M+1) x (N+1) matrices C (natural log, leading dimension ldc)
+// enter the sweeps and the extraction through the same internal layout as
+// the pass: the real block scaled by `scale` into Z [M][ld4(N)] and its
+// transpose ZT [N][ld4(M)] (32 x 32 tiles through LDS, so that both sides
+// are written in whole rows); with bcol / brow non-null, the dustbin column
+// C[i][N] (i <= M, the corner last) and row C[M][j] (j <= N, the corner
+// last), scaled, for the explicit-dustbin sweeps.
+__global__ __launch_bounds__(256) void k_stage_couplings(const float* __restrict__ C, int64_t ldc, int M, int N,
+                                                         float scale, float* __restrict__ Z, float* __restrict__ ZT,
+                                                         float* __restrict__ bcol, float* __restrict__ brow) {
+  __shared__ float tile[32][33];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = i0 + ty + 8 * r, j = j0 + tx;
+    float x = 0.f;
+    if (i < M && j < N) {
+      x = C[(int64_t)i * ldc + j] * scale;
+      Z[(size_t)i * ld4(N) + j] = x;
+    }
+    tile[ty + 8 * r][tx] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int j = j0 + ty + 8 * r, i = i0 + tx;
+    if (i < M && j < N) ZT[(size_t)j * ld4(M) + i] = tile[tx][ty + 8 * r];
+  }
+  if (bcol && blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int i = threadIdx.x; i <= M; i += 256) bcol[i] = C[(int64_t)i * ldc + N] * scale;
+    for (int j = threadIdx.x; j <= N; j += 256) brow[j] = C[(int64_t)M * ldc + j] * scale;
+  }
+}
+
+// Outputs of the Sinkhorn stage entry point: the natural-log duals u = ln2 u2,
+// v = ln2 v2, and (logP non-null) logP = C + u + v + log(M+N) over the
+// (M+1) x (N+1) block, from the caller's own C.
+__global__ __launch_bounds__(256) void k_stage_duals(const float* __restrict__ C, int64_t ldc, int M, int N,
+                                                     const float* __restrict__ u2, const float* __restrict__ v2,
+                                                     float* __restrict__ u, float* __restrict__ v,
+                                                     float* __restrict__ logP, int64_t ldp, float lmn) {
+  const int i = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j > N) return;
+  const float ui = kLn2 * u2[i], vj = kLn2 * v2[j];
+  if (j == 0) u[i] = ui;
+  if (i == 0) v[j] = vj;
+  if (logP) logP[(int64_t)i * ldp + j] = C[(int64_t)i * ldc + j] + ((ui + vj) + lmn);
+}
+
+hipError_t launch_stage_couplings(const float* C, int64_t ldc, int M, int N, float scale, float* Z, float* ZT,
+                                  float* bcol, float* brow, hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_stage_couplings, dim3((N + 31) / 32, (M + 31) / 32), dim3(256), 0, st, C, ldc, M, N, scale,
+                     Z, ZT, bcol, brow);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_duals(const float* C, int64_t ldc, int M, int N, const float* u2, const float* v2, float* u,
+                              float* v, float* logP, int64_t ldp, hipStream_t st) {
+  const float lmn = logf((float)(M + N));
+  hipLaunchKernelGGL(k_stage_duals, dim3((N + 1 + 255) / 256, M + 1), dim3(256), 0, st, C, ldc, M, N, u2, v2, u, v,
+                     logP, ldp, lmn);
+  return hipGetLastError();
+}
+
+static int sink_nv4(int max_n);
+
+// One explicit-dustbin sweep (k_lse_one<.., true>) over the nr + 1 rows of Z
+// (or ZT): w_out = lm - lse2 over the row of Z2 + w_in.
+hipError_t launch_lse_explicit(const float* Z, const float* w_in, float* w_out, int nr, int nc, float lm_real,
+                               float lm_dust, const float* bown, const float* bcross, hipStream_t st) {
+  const int nv4 = sink_nv4(nc);
+  dim3 grid((nr + 1 + 3) / 4);
+#define SG_LSEX(NV)                                                                                       \
+  if (nv4 == NV) {                                                                                        \
+    hipLaunchKernelGGL((k_lse_one<NV, true>), grid, dim3(256), 0, st, Z, w_in, w_out, nr, nc, 0.f, nullptr, \
+                       lm_real, lm_dust, bown, bcross);                                                   \
+    return hipGetLastError();                                                                             \
+  }
+  SG_LSEX(1) SG_LSEX(2) SG_LSEX(4) SG_LSEX(8) SG_LSEX(16)
+#undef SG_LSEX
+  return hipErrorInvalidValue;
 }
 
 __global__ void k_fill_f32(float* p, float v, int n) {
@@ -730,10 +833,11 @@ hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const floa
     // the same single-precision logarithms as the pair-table kernel
     const float lmn = std::log2((float)(M + N));
     const float lr = 0.f - lmn, ld = std::log2((float)nc) - lmn;
-#define SG_LSE(NV)                                                                                                  \
-    if (nv4 == NV) {                                                                                                \
-      hipLaunchKernelGGL(k_lse_one<NV>, grid, dim3(256), 0, st, zp, wv, wo, nr, nc, alpha2, alpha_dev, lr, ld);     \
-      return hipGetLastError();                                                                                     \
+#define SG_LSE(NV)                                                                                             \
+    if (nv4 == NV) {                                                                                           \
+      hipLaunchKernelGGL((k_lse_one<NV, false>), grid, dim3(256), 0, st, zp, wv, wo, nr, nc, alpha2, alpha_dev, lr, \
+                         ld, nullptr, nullptr);                                                                \
+      return hipGetLastError();                                                                                \
     }
     SG_LSE(1) SG_LSE(2) SG_LSE(4) SG_LSE(8) SG_LSE(16)
 #undef SG_LSE
@@ -751,7 +855,7 @@ hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const floa
 }
 
 hipError_t launch_col_argmax(const float* ZT, const PairTable& pt, const float* u, int* idx1, int Npad,
-                             int32_t* m1, float* s1, int ds, hipStream_t st) {
+                             int32_t* m1, float* s1, int mode, hipStream_t st) {
   int cols = 0, mr = 0;
   for (int b = 0; b < pt.n_pairs; ++b) {
     cols += pt.N[b];
@@ -760,11 +864,16 @@ hipError_t launch_col_argmax(const float* ZT, const PairTable& pt, const float* 
   if (cols <= 0) return hipSuccess;
   const int nv4 = sink_nv4(mr);
   dim3 grid((cols + 3) / 4);
-#define SG_CA(NV)                                                                                          \
-  if (nv4 == NV) {                                                                                         \
-    if (ds) hipLaunchKernelGGL((k_col_argmax<NV, true>), grid, dim3(256), 0, st, ZT, pt, u, idx1, Npad, m1, s1); \
-    else hipLaunchKernelGGL((k_col_argmax<NV, false>), grid, dim3(256), 0, st, ZT, pt, u, idx1, Npad, m1, s1); \
-    return hipGetLastError();                                                                              \
+#define SG_CA(NV)                                                                                             \
+  if (nv4 == NV) {                                                                                            \
+    if (mode == EXT_DS)                                                                                       \
+      hipLaunchKernelGGL((k_col_argmax<NV, EXT_DS>), grid, dim3(256), 0, st, ZT, pt, u, idx1, Npad, m1, s1);  \
+    else if (mode == EXT_RAW)                                                                                 \
+      hipLaunchKernelGGL((k_col_argmax<NV, EXT_RAW>), grid, dim3(256), 0, st, ZT, pt, u, idx1, Npad, m1, s1); \
+    else                                                                                                      \
+      hipLaunchKernelGGL((k_col_argmax<NV, EXT_SINKHORN>), grid, dim3(256), 0, st, ZT, pt, u, idx1, Npad, m1, \
+                         s1);                                                                                 \
+    return hipGetLastError();                                                                                 \
   }
   SG_CA(1) SG_CA(2) SG_CA(4) SG_CA(8) SG_CA(16)
 #undef SG_CA
@@ -773,17 +882,22 @@ hipError_t launch_col_argmax(const float* ZT, const PairTable& pt, const float* 
 
 hipError_t launch_sink_extract(const float* Z, const PairTable& pt, const float* u, const float* v,
                                const int* idx1, int Mpad, int Npad, float thr, int32_t* m0, float* s0,
-                               int32_t* m1, float* s1, int ds, hipStream_t st) {
+                               int32_t* m1, float* s1, int mode, hipStream_t st) {
   const int n = std::max(Mpad, m1 ? Npad : 0);
   if (n <= 0 || pt.n_pairs <= 0) return hipSuccess;
   const int nc = max_n(pt);
   const int nv4 = (nc + 255) / 256;
   dim3 grid((n + 3) / 4, pt.n_pairs);
-#define SG_EXT(NV)                                                                                            \
-  if (ds) hipLaunchKernelGGL((k_sink_extract<NV, true>), grid, dim3(256), 0, st, Z, pt, u, v, idx1, Mpad, Npad, \
-                             thr, m0, s0, m1, s1);                                                            \
-  else hipLaunchKernelGGL((k_sink_extract<NV, false>), grid, dim3(256), 0, st, Z, pt, u, v, idx1, Mpad, Npad, \
-                          thr, m0, s0, m1, s1)
+#define SG_EXT(NV)                                                                                              \
+  if (mode == EXT_DS)                                                                                           \
+    hipLaunchKernelGGL((k_sink_extract<NV, EXT_DS>), grid, dim3(256), 0, st, Z, pt, u, v, idx1, Mpad, Npad, thr, \
+                       m0, s0, m1, s1);                                                                         \
+  else if (mode == EXT_RAW)                                                                                     \
+    hipLaunchKernelGGL((k_sink_extract<NV, EXT_RAW>), grid, dim3(256), 0, st, Z, pt, u, v, idx1, Mpad, Npad,    \
+                       thr, m0, s0, m1, s1);                                                                    \
+  else                                                                                                          \
+    hipLaunchKernelGGL((k_sink_extract<NV, EXT_SINKHORN>), grid, dim3(256), 0, st, Z, pt, u, v, idx1, Mpad,     \
+                       Npad, thr, m0, s0, m1, s1)
   if (nv4 <= 1) SG_EXT(1);
   else if (nv4 <= 2) SG_EXT(2);
   else if (nv4 <= 4) SG_EXT(4);

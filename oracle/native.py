@@ -219,11 +219,14 @@ def score_matrix(fA, fB):
     return S
 
 
-def log_sinkhorn_iterations(Z, log_mu, log_nu, iters):
+def log_sinkhorn_iterations(Z, log_mu, log_nu, iters, duals=False):
+    """Z + u + v after `iters` iterations; with duals=True also (u, v)."""
     Z, lm, ln = _f64(Z), _f64(log_mu), _f64(log_nu)
     out = np.empty_like(Z)
-    lib().orc_log_sinkhorn_iterations(_p(Z), Z.shape[0], Z.shape[1], _p(lm), _p(ln), int(iters), None, None, _p(out))
-    return out
+    u, v = np.empty(Z.shape[0]), np.empty(Z.shape[1])
+    lib().orc_log_sinkhorn_iterations(_p(Z), Z.shape[0], Z.shape[1], _p(lm), _p(ln), int(iters), _p(u), _p(v),
+                                      _p(out))
+    return (out, u, v) if duals else out
 
 
 def log_optimal_transport(S, alpha, iters, duals=False):

@@ -258,10 +258,12 @@ def _sinkhorn_duals(Z, log_mu, log_nu, iters):
     return rows, cols
 
 
-def log_sinkhorn_iterations(Z, log_mu, log_nu, iters):
-    """Z + u + v after `iters` iterations of _sinkhorn_duals."""
+def log_sinkhorn_iterations(Z, log_mu, log_nu, iters, duals=False):
+    """Z + u + v after `iters` iterations of _sinkhorn_duals; with
+    duals=True also (u, v)."""
     u, v = _sinkhorn_duals(Z, log_mu, log_nu, iters)
-    return _f64(Z) + u[:, None] + v[None, :]
+    out = _f64(Z) + u[:, None] + v[None, :]
+    return (out, u, v) if duals else out
 
 
 def log_optimal_transport(S, alpha, iters, duals=False):

@@ -225,3 +225,31 @@ def test_adaptive_layout_and_validation():
     o2 = _lib.SgOpts()
     o2.flags = _lib.SG_FLAG_PRUNE
     assert _match(lib, plain, opts=C.byref(o2)) == _lib.SG_ERR_INVALID_ARG
+
+
+def test_sinkhorn_and_extract_stages_validate_on_host():
+    """sg_stage_sinkhorn / sg_stage_extract refuse bad arguments before any
+    HIP call, with nothing enqueued."""
+    lib = _lib.load()
+    f = C.c_void_p(0x1000)
+    I = _lib.SG_ERR_INVALID_ARG
+    # empty images: the optimal-matching layer runs on non-empty images only
+    assert lib.sg_stage_sinkhorn(f, 5, 0, 4, 10, f, f, None, 0, None) == I
+    assert "non-empty" in lib.sg_last_error().decode()
+    assert lib.sg_stage_sinkhorn(f, 5, 3, 0, 10, f, f, None, 0, None) == I
+    assert lib.sg_stage_sinkhorn(f, 5, 3, 4, -1, f, f, None, 0, None) == I          # T < 0
+    assert lib.sg_stage_sinkhorn(f, 4, 3, 4, 10, f, f, None, 0, None) == I          # ldZ < N+1
+    assert lib.sg_stage_sinkhorn(None, 5, 3, 4, 10, f, f, None, 0, None) == I
+    assert lib.sg_stage_sinkhorn(f, 5, 3, 4, 10, None, f, None, 0, None) == I       # u NULL
+    assert lib.sg_stage_sinkhorn(f, 5, 3, 4, 10, f, None, None, 0, None) == I       # v NULL
+    assert lib.sg_stage_sinkhorn(f, 5, 3, 4, 10, f, f, f, 4, None) == I             # ldP < N+1
+    assert lib.sg_stage_sinkhorn(f, 5000, 4097, 4, 10, f, f, None, 0, None) == _lib.SG_ERR_UNSUPPORTED
+    assert lib.sg_stage_extract(f, 4, 3, 4, 0.0, f, f, None, None, None) == I        # ldP < N+1
+    assert lib.sg_stage_extract(None, 5, 3, 4, 0.0, f, f, None, None, None) == I
+    assert lib.sg_stage_extract(f, 5, 3, 4, 0.0, None, f, None, None, None) == I
+    assert lib.sg_stage_extract(f, 5, 3, 4, 0.0, f, f, None, f, None) == I           # scores1 without matches1
+    assert lib.sg_stage_extract(f, 5, -1, 4, 0.0, f, f, None, None, None) == I
+    assert lib.sg_stage_extract(f, 5, 3, 4097, 0.0, f, f, None, None, None) == _lib.SG_ERR_UNSUPPORTED
+    # the workspace holds Z, its transpose and the per-line vectors
+    assert lib.sg_stage_sinkhorn_workspace_size(1024, 1024) >= 2 * 1024 * 1024 * 4
+    assert lib.sg_stage_sinkhorn_workspace_size(-1, 3) == 0
