@@ -356,6 +356,22 @@ size_t sg_stage_match_ds_workspace_size(int32_t M, int32_t N, int32_t D);
 sg_status sg_stage_sinkhorn(const float* Z, int64_t ldZ, int32_t M, int32_t N, int32_t T, float* u, float* v,
                             float* logP, int64_t ldP, const sg_opts* opts);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, arguments and errors as sg_stage_sinkhorn, enqueued directly
+ * on `stream` (never captured into a graph by the library), with its
+ * workspace in a fixed 40 MiB device array per GPU instead of an allocation;
+ * the call allocates nothing.  Shapes whose workspace
+ * (sg_stage_sinkhorn_workspace_size) exceeds 40 MiB -> SG_ERR_UNSUPPORTED
+ * (every M, N <= 2048 fits).  All calls on one GPU share the array, which
+ * keeps the last call's contents: calls that overlap in time on one GPU
+ * (different streams, or host threads) race and must be serialised by the
+ * caller.
+ */
+sg_status sg_stage_sinkhorn_noalloc(const float* Z, int64_t ldZ, int32_t M, int32_t N, int32_t T, float* u,
+                                    float* v, float* logP, int64_t ldP, sg_stream_t stream);
+
 /* Workspace bytes of sg_stage_sinkhorn and sg_stage_extract for M x N points. */
 size_t sg_stage_sinkhorn_workspace_size(int32_t M, int32_t N);
 

@@ -20,7 +20,7 @@ from ._lib import (SG_BF16, SG_CROSS_BIDIRECTIONAL, SG_CROSS_STANDARD, SG_F32, S
 
 __all__ = ["Weights", "weights_config", "pack_weights", "workspace_size", "sg_match",
            "sg_match_batch", "sg_stage_encode", "sg_stage_gnn", "sg_stage_project",
-           "sg_stage_match", "sg_stage_match_ds", "sg_stage_sinkhorn", "sg_stage_extract", "lib", "SgError", "SG_K_GEMM", "SG_K_ATTENTION", "SG_K_SINKHORN",
+           "sg_stage_match", "sg_stage_match_ds", "sg_stage_sinkhorn", "sg_stage_sinkhorn_noalloc", "sg_stage_extract", "lib", "SgError", "SG_K_GEMM", "SG_K_ATTENTION", "SG_K_SINKHORN",
            "SG_N_STAGE_EVENTS"]
 
 
@@ -468,4 +468,29 @@ def sg_stage_extract(logP, *, threshold: float = 0.0, want_matches1=True, worksp
     _lib.check(lib().sg_stage_extract(_ptr(logP), N + 1, M, N, float(threshold), _ptr(out["matches0"]),
                                       _ptr(out["scores0"]), _ptr(out.get("matches1")), _ptr(out.get("scores1")),
                                       C.byref(o)), "sg_stage_extract")
+    return out
+
+
+def sg_stage_sinkhorn_noalloc(Z, T: int, *, u=None, v=None, logP=None, stream=None) -> dict:
+    """sg_stage_sinkhorn with the library's fixed scratch array instead of a
+    workspace: the call allocates nothing (the outputs u [M+1], v [N+1] and
+    optionally logP [(M+1)][N+1] may be passed in; omitted ones are
+    allocated here, outside the call)."""
+    if Z.dim() != 2:
+        raise ValueError("Z must be [(M+1)][(N+1)]")
+    M, N = Z.shape[0] - 1, Z.shape[1] - 1
+    _check_tensor(Z, "Z", torch.float32)
+    dev = Z.device
+    u = torch.empty(M + 1, dtype=torch.float32, device=dev) if u is None else u
+    v = torch.empty(N + 1, dtype=torch.float32, device=dev) if v is None else v
+    _check_tensor(u, "u", torch.float32, (M + 1,))
+    _check_tensor(v, "v", torch.float32, (N + 1,))
+    if logP is not None:
+        _check_tensor(logP, "logP", torch.float32, (M + 1, N + 1))
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _lib.check(lib().sg_stage_sinkhorn_noalloc(_ptr(Z), N + 1, M, N, int(T), _ptr(u), _ptr(v), _ptr(logP), N + 1,
+                                               C.c_void_p(s.cuda_stream)), "sg_stage_sinkhorn_noalloc")
+    out = {"u": u, "v": v}
+    if logP is not None:
+        out["logP"] = logP
     return out

@@ -70,6 +70,7 @@ SIGNATURES = {
     "sg_stage_match_ds_workspace_size": (C.c_size_t, [_I, _I, _I]),
     "sg_stage_sinkhorn": (_I, [_P, C.c_int64, _I, _I, _I, _P, _P, _P, C.c_int64, _O]),
     "sg_stage_sinkhorn_workspace_size": (C.c_size_t, [_I, _I]),
+    "sg_stage_sinkhorn_noalloc": (_I, [_P, C.c_int64, _I, _I, _I, _P, _P, _P, C.c_int64, _P]),
     "sg_stage_extract": (_I, [_P, C.c_int64, _I, _I, _F, _P, _P, _P, _P, _O]),
     "sg_last_error": (C.c_char_p, []),
     "sg_version": (C.c_char_p, []),

@@ -731,6 +731,35 @@ sg_status check_stage_sinkhorn(const float* Z, int64_t ldZ, int32_t M, int32_t N
   return SG_OK;
 }
 
+// ------------------------------------------ allocation-free Sinkhorn stage
+//
+// sg_stage_sinkhorn_noalloc keeps its workspace in one fixed device array
+// per GPU (held from the library's load until the process ends) instead of
+// a caller or library allocation.  In host code `scratch` only names the
+// symbol: its device address is looked up once per device with that device
+// current, and only that address reaches kernels.  Every call on a GPU
+// shares the array and overwrites what the previous call left in it.
+constexpr size_t kScratchBytes = size_t(40) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+char* g_scratch_addr[64] = {};
+
+sg_status scratch_address(char** out) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(SG_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SG_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_addr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_addr[dev];
+  return SG_OK;
+}
+
 sg_status check_opts(const sg_opts* o) {
   if (!o) return SG_OK;
   if (o->workspace && o->workspace_bytes == 0) return fail(SG_ERR_WORKSPACE, "workspace given with 0 bytes");
@@ -1495,6 +1524,20 @@ sg_status sg_stage_extract(const float* logP, int64_t ldP, int32_t M, int32_t N,
     return enqueue_stage_extract(logP, ldP, M, N, threshold, out_matches0, out_scores0, out_matches1, out_scores1,
                                  reinterpret_cast<char*>(wsp), L, cs);
   });
+}
+
+sg_status sg_stage_sinkhorn_noalloc(const float* Z, int64_t ldZ, int32_t M, int32_t N, int32_t T, float* u,
+                                    float* v, float* logP, int64_t ldP, sg_stream_t stream) {
+  g_err.clear();
+  sg_status s;
+  if ((s = check_stage_sinkhorn(Z, ldZ, M, N, T, u, v, logP, ldP)) != SG_OK) return s;
+  const StageWs L = stage_ws(M, N);
+  if (L.total > kScratchBytes)
+    return fail(SG_ERR_UNSUPPORTED, "%d x %d points need %zu bytes of scratch, the fixed array holds %zu", M, N,
+                L.total, kScratchBytes);
+  char* ws = nullptr;
+  if ((s = scratch_address(&ws)) != SG_OK) return s;
+  return enqueue_stage_sinkhorn(Z, ldZ, M, N, T, u, v, logP, ldP, ws, L, (hipStream_t)stream);
 }
 
 }  // extern "C"
