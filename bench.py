@@ -40,13 +40,15 @@ def log(*a):
 def gemm_launches(cfg, M, N, cross="standard"):
     """(label, operand dtype, algorithmic flops) of every GEMM-class launch of
     one pass, in launch order (real rows only): the merge fold of all 2L
-    stages (W1[:, D:] Wm, 2D x D x D per stage), then per stage the QKV
-    projection, the first MLP layer over [x || a] (merge folded in) and the
-    second with the residual, then the final projection and the scores.
-    Bidirectional cross stages project qk | v (2D outputs) instead of
-    q | k | v."""
+    stages, then per stage the QKV projection, the first MLP layer over
+    [x || a] (merge folded in) and the second with the residual, then the
+    final projection and the scores.  The fold launch stands in for the
+    merge projection of every stage, so it is credited with the merge's
+    algorithmic work, 2 (M+N) D^2 per stage (the fold itself multiplies
+    weights only: W1[:, D:] Wm, 2 x 2D x D x D per stage).  Bidirectional
+    cross stages project qk | v (2D outputs) instead of q | k | v."""
     R, D, S = M + N, cfg.D, 2 * cfg.L
-    out = [("merge_fold", cfg.dtype, 2.0 * S * 2 * D * D * D)]
+    out = [("merge_fold", cfg.dtype, 2.0 * R * D * D * S)]
     for s in range(S):
         out.append(("qkv", cfg.dtype, 2.0 * R * D * (2 if (s % 2 == 1 and cross == "bidirectional") else 3) * D))
         out.append(("mlp1", cfg.dtype, 2.0 * R * 2 * D * 2 * D))
@@ -68,8 +70,13 @@ def attention_flops(cfg, M, N):
 
 
 def sinkhorn_bytes(M, N, T):
-    """Per launch (half-iteration): one fp32 read of the (M+1)x(N+1) couplings."""
-    return [4.0 * (M + 1) * (N + 1)] * (2 * T)
+    """Algorithmic bytes per Sinkhorn launch.  The method's work per
+    iteration is one fused fp32 read of the (M+1)x(N+1) couplings,
+    4 (M+1)(N+1) bytes; the two-sweep schedule spends two launches on an
+    iteration (rows of Z, then rows of its transpose), so each launch is
+    credited with half of it.  Reading Z and Z^T in full is the schedule's
+    own extra traffic (traffic_ratio ~2), not algorithmic work."""
+    return [2.0 * (M + 1) * (N + 1)] * (2 * T)
 
 
 def ds_bytes(M, N, D):
@@ -102,28 +109,85 @@ def profiled_traffic(kernel, profile="superglue_pair1024_bf16_hbm_traffic.txt"):
     return None
 
 
-def cpu_baseline(cfg, w, pair, head="sinkhorn", budget_s=12.0, max_pairs=3):
-    import oracle
+def _cpu_model():
     try:
-        import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
-    except Exception:
-        threads = os.cpu_count() or 1
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def pass_flops(cfg, M, N, cross="standard"):
+    """Algorithmic flops of one pass (encoder, GNN, final projection, scores)."""
+    widths = [3] + list(cfg.enc) + [cfg.D]
+    enc = 2.0 * (M + N) * sum(a * b for a, b in zip(widths[:-1], widths[1:]))
+    gemm = sum(f for _, _, f in gemm_launches(cfg, M, N, cross))
+    return enc + gemm + sum(attention_flops(cfg, M, N))
+
+
+def cpu_baseline(cfg, w, pair, head="sinkhorn"):
+    """The plain C oracle, single-threaded, on a bounded sample of the pass:
+    the encoder of both images, one GNN layer (stage 0, self, and stage 1,
+    cross), the final projection and the whole head (scores, T Sinkhorn
+    iterations, extraction).  The L layers of the pass have identical shapes
+    and work, so the per-pair time is encoder + L x layer + head."""
+    import numpy as np
+
+    import oracle
+    oracle.set_threads(1)
+    t = {}
     t0 = time.perf_counter()
-    n = 0
-    while n < max_pairs:
-        if head == "ds":
-            oracle.double_softmax_match(pair, w)
-        else:
-            oracle.superglue_match(pair, w, T=cfg.T)
-        n += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} full passes of the same 1024x1024 pair (L=9, "
-                      f"{'double-softmax head' if head == 'ds' else 'T=100'}) by the float64 numpy "
-                      f"oracle, {dt:.1f} s wall"}
+    xs = []
+    for side in ("0", "1"):
+        wd, ht = pair["image_size" + side]
+        kn = oracle.normalize_keypoints(pair["kpts" + side], wd, ht)
+        xs.append(np.asarray(pair["desc" + side], np.float64) + oracle.keypoint_encoder(kn, pair["conf" + side], w["enc"]))
+    t["encoder"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    xa, xb = oracle.attentional_gnn(xs[0], xs[1], w["stages"][:2], w["H"])
+    t["layer"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    f0 = oracle.final_projection(xa, w["Wf"], w["bf"])
+    f1 = oracle.final_projection(xb, w["Wf"], w["bf"])
+    if head == "ds":
+        oracle.double_softmax_from_descriptors(f0, f1, xa, xb, w["wz"], w["bz"])
+    else:
+        oracle.match_from_descriptors(f0, f1, w["alpha"], cfg.T)
+    t["head"] = time.perf_counter() - t0
+    oracle.set_threads(0)
+    per_pair = t["encoder"] + cfg.L * t["layer"] + t["head"]
+    flops = pass_flops(cfg, cfg.M, cfg.N)
+    sampled = sum(t.values())
+    return {"value": round(1.0 / per_pair, 5), "unit": "pairs/s", "cores": 1, "kind": "oracle",
+            "threads": 1, "cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+            "s_per_pair": round(per_pair, 2), "gflops_per_s": round(flops / per_pair / 1e9, 3),
+            "pass_gflop": round(flops / 1e9, 2),
+            "sample": (f"plain C float64 oracle (oracle/sg_oracle.c), one thread, on the 1024x1024 pair: encoder "
+                       f"{t['encoder']:.2f} s, one self + cross layer {t['layer']:.2f} s (x L={cfg.L}), final "
+                       f"projection + {'double-softmax head' if head == 'ds' else f'scores + T={cfg.T} Sinkhorn'} + "
+                       f"extraction {t['head']:.2f} s; {sampled:.1f} s sampled")}
+
+
+def profiled_mfma_busy(profile="superglue_pair1024_bf16_mfma_busy.txt"):
+    """Counter-based MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES) per kernel of
+    the one-pair pass from the committed rocprofv3 summary, or None when it is
+    missing or a kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    out = {}
+    for line in open(path):
+        if not line.startswith("mfma_busy_frac"):
+            continue
+        kv = dict(x.split("=", 1) for x in line.split()[1:])
+        src = os.path.join(ROOT, kv["source"])
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != kv["sha256_16"]:
+            return None
+        out[kv["class"]] = float(kv["busy"])
+    return out or None
 
 
 def adaptive_bench(args, cfg, dev, sg, synth, np, torch):
@@ -215,7 +279,7 @@ def batch_kernels(args, cfg, sg, np, torch, bstep, B, M, N, ds):
         if name == "gemm":
             labs = gemm_launches(cfg, M, N, args.cross)
             assert nl == len(labs), ("batched GEMM launches", nl, len(labs))
-            mult = (lambda lab: 1 if lab == "merge_fold" else B)  # the fold works on weights only
+            mult = (lambda lab: B)  # per-pair algorithmic work (the fold credited with the merge's)
             bf = [(f * mult(lab), d) for (lab, dt_, f), d in zip(labs, dur_us) if dt_ == "bf16"]
             ach = float(sum(f for f, _ in bf) / sum(d for _, d in bf) / 1e6)
             r.update(achieved_TFLOPs_bf16=round(ach, 1), frac_mfma=round(ach / PEAK["bf16_TFLOPs"], 4))
@@ -243,19 +307,18 @@ def batch_kernels(args, cfg, sg, np, torch, bstep, B, M, N, ds):
             r.update(bytes_per_iteration=4.0 * (M + 1) * (N + 1) * B,
                      achieved_GBps=round(float(byt / dur_us.sum() / 1e3), 1),
                      frac_hbm=round(float(byt / dur_us.sum() / 1e3) / PEAK["hbm_GBps"], 4))
-            if nl == 2 * cfg.T:
-                # one-pass schedule: row pass (reads Z, writes the per-block
-                # column partials of ceil((M+1)/8) row blocks), then the column
-                # reduction (reads the partials); launches alternate
-                G = (M + 1 + 7) // 8
-                part = 4.0 * G * ((N + 3) // 4 * 4) * B
-                rows_b, cols_b = 4.0 * M * ((N + 3) // 4 * 4) * B + part, part
-                rp, cp = dur_us[0::2], dur_us[1::2]
-                r["row_pass"] = {"avg_us": round(float(rp.mean()), 2), "bytes": rows_b,
-                                 "achieved_GBps": round(float(rows_b / rp.mean() / 1e3), 1),
-                                 "frac_hbm": round(float(rows_b / rp.mean() / 1e3 / PEAK["hbm_GBps"]), 4)}
-                r["column_reduction"] = {"avg_us": round(float(cp.mean()), 2), "bytes": cols_b,
-                                         "achieved_GBps": round(float(cols_b / cp.mean() / 1e3), 1)}
+            if nl == cfg.T + 1:
+                # one-pass schedule, fused iterations: each launch reduces the
+                # previous block partials into v (every workgroup of a pair),
+                # updates u and writes its own partials from one read of Z;
+                # one column reduction follows the last iteration
+                it, fin = dur_us[:cfg.T], dur_us[cfg.T]
+                per_it = 4.0 * (M + 1) * (N + 1) * B
+                r["iteration"] = {"kernel": "k_sink_iter", "launches": cfg.T, "avg_us": round(float(it.mean()), 2),
+                                  "algorithmic_bytes": per_it,
+                                  "achieved_GBps": round(float(per_it / it.mean() / 1e3), 1),
+                                  "frac_hbm": round(float(per_it / it.mean() / 1e3 / PEAK["hbm_GBps"]), 4)}
+                r["final_column_reduction_us"] = round(float(fin), 2)
         res[name] = r
     return res
 
@@ -430,6 +493,7 @@ def main():
 
     kernels = {}
     roofline = None
+    mfma_util = None
     if not args.no_kernel_timing:
         specs = {
             "sinkhorn": (sg.SG_K_SINKHORN, norm_work),
@@ -499,6 +563,16 @@ def main():
                 if f in kk:
                     kk[f] = round(kk[f] * scale, 2)
         kernels["bracket_latency_us"] = round(over, 3)
+        # MFMA utilisation of the headline pair's contraction kernels (the
+        # metric's "MFMA util %"): algorithmic flops over the launch times
+        # above, against the bf16 dense peak
+        mfma_util = {"attention": round(100 * kernels["attention"]["achieved_TFLOPs"] / PEAK["bf16_TFLOPs"], 2),
+                     "gemm_bf16": round(100 * kernels["gemm"]["achieved_TFLOPs_bf16"] / PEAK["bf16_TFLOPs"], 2),
+                     "basis": "flop-based: algorithmic flops / (launch time x 2.5 PFLOP/s), launch times from "
+                              "HIP events on the library's stream less the bracketing latency"}
+        busy = profiled_mfma_busy()
+        if busy is not None:
+            mfma_util["counter_busy"] = {k: round(100 * v, 2) for k, v in busy.items()}
         dom = max((nk, "attention", "gemm"), key=lambda k: kernels[k]["total_us"])
         if dom == "ds_stats":
             per_launch = norm_work[0]
@@ -506,6 +580,8 @@ def main():
             roofline = {"kernel": kernels[dom]["kernel"], "bound": "hbm", "achieved": round(ach, 1),
                         "peak": PEAK["hbm_GBps"], "unit": "GB/s", "frac": round(ach / PEAK["hbm_GBps"], 4),
                         "traffic": kernels[dom]["traffic"], "algorithmic_bytes_per_launch": per_launch,
+                        "traffic_ratio": (None if kernels[dom]["traffic"] is None
+                                          else round(kernels[dom]["traffic"] / per_launch, 3)),
                         "avg_launch_us": kernels[dom]["avg_us"]}
         elif dom == "sinkhorn":
             per_launch = norm_work[0]
@@ -514,6 +590,9 @@ def main():
             roofline = {"kernel": "k_lse_one (Sinkhorn sweep over Z or Z^T, one pair)", "bound": "hbm", "achieved": round(ach, 1),
                         "peak": PEAK["hbm_GBps"], "unit": "GB/s", "frac": round(ach / PEAK["hbm_GBps"], 4),
                         "traffic": None if tr is None else round(tr), "algorithmic_bytes_per_launch": per_launch,
+                        "traffic_ratio": None if tr is None else round(tr / per_launch, 3),
+                        "algorithmic_bytes_per_iteration": 2 * per_launch,
+                        "iteration_us": round(2 * kernels[dom]["avg_us"], 3),
                         "avg_launch_us": kernels[dom]["avg_us"]}
         elif dom == "attention":
             fl = attention_flops(cfg, M, N)
@@ -579,7 +658,8 @@ def main():
                                 + ("head" if ds else "Sinkhorn")),
                    "pairs_per_step": 1, "M": M, "N": N, "D": cfg.D, "L": cfg.L, "T": None if ds else cfg.T,
                    "head": args.head, "cross_attention": args.cross, "rope": args.rope},
-        "roofline": roofline, "cpu_baseline": cpu, "latency": latency, "stages_ms": stages, "kernels": kernels,
+        "roofline": roofline, "mfma_util_pct": mfma_util, "cpu_baseline": cpu, "latency": latency,
+        "stages_ms": stages, "kernels": kernels,
         "batch_throughput": batch,
         "per_config": configs,
         "adaptive": adaptive,

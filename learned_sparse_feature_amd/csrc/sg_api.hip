@@ -155,7 +155,7 @@ sg_status check_weights(const sg_weights* w, WLayout* out) {
 // ---------------------------------------------------------- workspace layout
 
 struct WsLayout {
-  size_t X, XB, QK, VT, KS, VS, MB, HB, WF, WFB, F, Z, ZT, P, PD, PV, PI, U, V, UD, VD, IDX1, ROPE, ADAPT, total;
+  size_t X, XB, QK, VT, KS, VS, MB, HB, WF, WFB, F, Z, ZT, P, PD, P2, PD2, PV, PI, U, V, UD, VD, IDX1, ROPE, ADAPT, total;
   int ldvt, ldqk;
 };
 
@@ -187,6 +187,9 @@ WsLayout ws_layout_raw(long D, size_t os, long R, long zf, long ztf, long pf, lo
   L.ZT = take((size_t)ztf * 4);
   L.P = take((size_t)pf * 4);
   L.PD = take((size_t)pd * 4);
+  // the fused one-pass iteration reads one partial buffer and writes the other
+  L.P2 = take((size_t)pf * 4);
+  L.PD2 = take((size_t)pd * 4);
   L.PV = take((size_t)pf * 4);
   L.PI = take((size_t)pf * 4);
   L.U = take((size_t)uf * 4);
@@ -291,6 +294,7 @@ struct Plan {
   int R = 0;
   long zf = 0, ztf = 0, pf = 0, pd = 0, uf = 0, vf = 0, nb = 0;
   bool two_sweep = false;  // Sinkhorn schedule (see SG_FLAG_SINKHORN_*)
+  bool fused = false;      // one-pass schedule with the fused iteration (k_sink_iter)
   int ru = 0, rv = 0;  // flattened u rows (sum of M+1) and v rows (sum of N+1)
   std::vector<int> rowB;
 };
@@ -311,7 +315,10 @@ void make_plan(const Problem& p, Plan& pl) {
   // (the double-softmax head reads Z and ZT once each, whatever their size)
   pl.two_sweep = p.head == SG_HEAD_DOUBLE_SOFTMAX || (p.flags & SG_FLAG_SINKHORN_TWO_SWEEP) ||
                  (!(p.flags & SG_FLAG_SINKHORN_ONE_SWEEP) && zbytes <= (long)SG_TWO_SWEEP_MAX_BYTES);
-  pl.pt.rb = sink_rows_per_block(p.M.data(), p.N.data(), p.B);
+  // one-pass schedule: the fused iteration's row blocks where every row fits
+  // its registers, else the row pass + column reduction pair's
+  pl.fused = !pl.two_sweep && sink_iter_rows_per_block(p.N.data(), p.B) > 0;
+  pl.pt.rb = pl.fused ? sink_iter_rows_per_block(p.N.data(), p.B) : sink_rows_per_block(p.M.data(), p.N.data(), p.B);
   pl.seg.n_seg = 2 * p.B;
   for (int b = 0; b < p.B; ++b) {
     const int M = p.M[b], N = p.N[b];
@@ -327,7 +334,7 @@ void make_plan(const Problem& p, Plan& pl) {
     pl.pt.p_off[b] = (int)pf;
     zf += (long)M * ld4(N);
     ztf += (long)N * ld4(M);
-    const int G = (M + 1 + pl.pt.rb - 1) / pl.pt.rb;
+    const int G = pl.fused ? sink_iter_blocks(M, pl.pt.rb) : (M + 1 + pl.pt.rb - 1) / pl.pt.rb;
     pf += (long)G * ld4(N);
     pl.pt.gpre[b + 1] = pl.pt.gpre[b] + G;
     pl.pt.upre[b + 1] = pl.pt.upre[b] + M + 1;
@@ -551,6 +558,8 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
   float* ZT = reinterpret_cast<float*>(ws + wl.ZT);
   float* P = reinterpret_cast<float*>(ws + wl.P);
   float* Pd = reinterpret_cast<float*>(ws + wl.PD);
+  float* P2 = reinterpret_cast<float*>(ws + wl.P2);
+  float* Pd2 = reinterpret_cast<float*>(ws + wl.PD2);
   float* PV = reinterpret_cast<float*>(ws + wl.PV);
   int* PI = reinterpret_cast<int*>(ws + wl.PI);
   float* U = reinterpret_cast<float*>(ws + wl.U);
@@ -610,6 +619,34 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
     }
     tm.stage(SG_EV_SINKHORN);
     HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, EXT_SINKHORN, st), "column argmax");
+  } else if (pl.fused) {
+    // T fused iterations: each reduces the previous iteration's block
+    // partials into v, then updates u and writes its own partials (the two
+    // partial buffers alternate); the last one also leaves the per-block
+    // column argmax of Z + u.  One column reduction turns the last partials
+    // into v and the column argmax.
+    float* Pb[2] = {P, P2};
+    float* Pdb[2] = {Pd, Pd2};
+    for (int it = 0; it < T; ++it) {
+      const bool last = it == T - 1;
+      HIPCHK(tm.run(SG_K_SINKHORN, [&] {
+               return launch_sink_iter(Z, pl.pt, it == 0 ? nullptr : Pb[(it + 1) & 1],
+                                       it == 0 ? nullptr : Pdb[(it + 1) & 1], U, Pb[it & 1], Pdb[it & 1],
+                                       last ? PV : nullptr, last ? PI : nullptr, alpha2, alpha_dev, 1, st);
+             }), "sinkhorn iteration");
+    }
+    if (T > 0) {
+      HIPCHK(tm.run(SG_K_SINKHORN, [&] {
+               return launch_sink_cols(pl.pt, Pb[(T - 1) & 1], Pdb[(T - 1) & 1], V, PV, PI, idx1, 1, p.Npad, out.m1,
+                                       out.s1, st);
+             }), "sinkhorn cols");
+    } else {
+      HIPCHK(launch_fill_f32(U, 0.f, (int)pl.uf, st), "zero u");
+      HIPCHK(launch_fill_f32(V, 0.f, (int)pl.vf, st), "zero v");
+      HIPCHK(launch_sink_iter(Z, pl.pt, nullptr, nullptr, U, P, Pd, PV, PI, alpha2, alpha_dev, 0, st), "column argmax");
+      HIPCHK(launch_sink_cols(pl.pt, P, Pd, V, PV, PI, idx1, 0, p.Npad, out.m1, out.s1, st), "column argmax");
+    }
+    tm.stage(SG_EV_SINKHORN);
   } else {
     // T iterations: u = log mu - lse_j(Z + v) with the column partials of
     // Z + u in the same pass; then v = log nu - lse over the partials.  The

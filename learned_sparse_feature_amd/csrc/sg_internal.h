@@ -152,6 +152,16 @@ int sink_rows_per_block(const int* M, const int* N, int n_pairs);
 hipError_t launch_sink_rows(const float* Z, const PairTable& pt, const float* v_in, float* u_out,
                             float* P, float* Pd, float* PV, int* PI, float alpha2, const float* alpha_dev,
                             int update_u, hipStream_t st);
+// Fused one-pass iteration (k_sink_iter): rows per workgroup for a batch
+// (0: some row is too wide, use launch_sink_rows + launch_sink_cols), and
+// the launch.  Pin / Pdin: the previous iteration's partials (nullptr: v =
+// 0); Pout / Pdout: this iteration's (a different buffer).
+int sink_iter_rows_per_block(const int* N, int n_pairs);
+// Row blocks of a pair in the fused iteration (the last one takes the dustbin row).
+int sink_iter_blocks(int M, int rb);
+hipError_t launch_sink_iter(const float* Z, const PairTable& pt, const float* Pin, const float* Pdin, float* u_out,
+                            float* Pout, float* Pdout, float* PV, int* PI, float alpha2, const float* alpha_dev,
+                            int update_u, hipStream_t st);
 hipError_t launch_sink_cols(const PairTable& pt, const float* P, const float* Pd, float* v_out, const float* PV,
                             const int* PI, int* idx1, int write_v, int Npad, int32_t* m1, float* s1,
                             hipStream_t st);

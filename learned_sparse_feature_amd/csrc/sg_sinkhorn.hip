@@ -253,6 +253,316 @@ __global__ __launch_bounds__(256) void k_sink_rows(const float* __restrict__ Zb,
   }
 }
 
+// One fused iteration of the one-pass schedule (batches of pairs).  A
+// workgroup of W waves takes RB = W RPW consecutive rows of one pair, each
+// wave RPW of them, RS rows at a time with the next RS rows' loads in
+// flight; a pair has G = max(1, ceil(M / RB)) blocks, the last one holding
+// the dustbin row (as an extra row when M is a multiple of RB).
+//  * Phase 1: the column duals of the previous iteration, v_j = log2 nu_j -
+//    lse2_g Pin[g][j] over the pair's G block partials (Pdin: the dustbin
+//    column), into LDS.  Every workgroup of the pair repeats this small
+//    reduction (G (N+1) partials against its RB (N+1) couplings), so that no
+//    separate column launch sits between two iterations.  Pin == nullptr: v = 0
+//    (the first iteration, or no iteration at all).
+//  * Phase 2: the row update u_i and the block's column partials into Pout /
+//    Pdout, as k_sink_rows (one FMA per entry on the row exponentials, the
+//    exact per-block log-sum-exp where the sum falls below 2^-100; the
+//    dustbin column's partial always in closed form), and with ARG the
+//    per-block column argmax of Z + u into PV / PI.
+// The partials are double-buffered by the caller: iteration t reads the
+// buffer iteration t - 1 wrote and writes the other one.
+template <int W, int RPW, int NV4, int RS, bool ARG>
+__global__ __launch_bounds__(64 * W) void k_sink_iter(const float* __restrict__ Zb, PairTable pt,
+                                                      const float* __restrict__ Pin, const float* __restrict__ Pdin,
+                                                      float* __restrict__ u_out, float* __restrict__ Pout,
+                                                      float* __restrict__ Pdout, float* __restrict__ PV,
+                                                      int* __restrict__ PI, float alpha2,
+                                                      const float* __restrict__ alpha_dev, int update_u) {
+  static_assert(RPW % RS == 0, "rows per wave must be a multiple of the rows per step");
+  constexpr int NT = 64 * W;    // threads
+  constexpr int RB = W * RPW;
+  constexpr int NG = 64 * NV4;  // float4 column groups of a row held by one wave
+  constexpr int NSTEP = RPW / RS;
+  __shared__ float4 sm[W][NG];
+  __shared__ float4 vl[NG + 1];  // v of the columns; vl[NG].x: the dustbin column's
+  __shared__ float sm_u[RB + 1];  // (+1: the dustbin row may follow the block's last row)
+  if (alpha_dev) alpha2 = alpha_dev[0] * kLog2e;
+  const int b = find_pair(pt.gpre, pt.n_pairs, blockIdx.x);
+  if (b >= pt.n_pairs) return;
+  const int gb = blockIdx.x - pt.gpre[b];
+  const int G = pt.gpre[b + 1] - pt.gpre[b];
+  const int M = pt.M[b], N = pt.N[b];
+  const int i0 = gb * RB;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int ldz = ld4(N);
+  const float* zp = Zb + pt.z_off[b];
+  const float lmn = log2f((float)(M + N));
+
+  // loads of step p of the wave's rows (at a real row and column, clamped in
+  // bounds; rows at or past the dustbin row do not use them)
+  auto load_step = [&](int p, float4 (&dst)[RS][NV4]) {
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const int ic = max(min(i0 + w * RPW + p * RS + r, M - 1), 0);
+#pragma unroll
+      for (int k = 0; k < NV4; ++k)
+        dst[r][k] = (M > 0 && N > 0)
+                        ? *reinterpret_cast<const float4*>(zp + (size_t)ic * ldz + min(4 * (lane + 64 * k), ldz - 4))
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  // the first rows' loads go out before phase 1, which does not need them
+  float4 zbuf[2][RS][NV4];
+  load_step(0, zbuf[0]);
+
+  // ---- phase 1: the column duals of the previous iteration
+  if (Pin) {
+    const float* pp = Pin + pt.p_off[b];
+    constexpr int U = 8;
+    for (int q = threadIdx.x; 4 * q < N; q += NT) {
+      const int j = 4 * q;
+      float mx[4], sum[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        mx[c] = -INFINITY;
+        sum[c] = 0.f;
+      }
+      for (int g0 = 0; g0 < G; g0 += U) {
+        float4 x[U];
+#pragma unroll
+        for (int r = 0; r < U; ++r) x[r] = *reinterpret_cast<const float4*>(pp + (size_t)min(g0 + r, G - 1) * ldz + j);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float m2 = mx[c];
+#pragma unroll
+          for (int r = 0; r < U; ++r)
+            if (g0 + r < G) m2 = fmaxf(m2, f4c(x[r], c));
+          float t = mx[c] == -INFINITY ? 0.f : sum[c] * exp2_fast(mx[c] - m2);
+#pragma unroll
+          for (int r = 0; r < U; ++r)
+            if (g0 + r < G) t += exp2_fast(f4c(x[r], c) - m2);
+          sum[c] = t;
+          mx[c] = m2;
+        }
+      }
+      float o[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = j + c < N ? -lmn - (mx[c] + log2_fast(sum[c])) : 0.f;
+      vl[q] = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    if (w == 0) {  // the dustbin column: v_N = log2 M - log2(M+N) - lse2_g Pdin[g]
+      const float* pd = Pdin + pt.gpre[b];
+      float m = -INFINITY, sum = 0.f;
+      for (int g = lane; g < G; g += 64) {
+        const float x = pd[g];
+        const float m2 = fmaxf(m, x);
+        sum = (m == -INFINITY ? 0.f : sum * exp2_fast(m - m2)) + exp2_fast(x - m2);
+        m = m2;
+      }
+      const float wm = wave_max(m);
+      sum = wave_sum(m == -INFINITY ? 0.f : sum * exp2_fast(m - wm));
+      if (lane == 0) vl[NG].x = log2f((float)M) - lmn - (wm + log2_fast(sum));
+    }
+  } else {
+    for (int q = threadIdx.x; q <= NG; q += NT) vl[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+
+  // ---- phase 2: row update of the wave's rows and the block's column partials
+  // The duals of masked columns are -inf, so that t = Z + v needs no select
+  // (the loads are clamped in bounds and finite); the dustbin column (the
+  // same entry alpha + v_N for every lane) joins each row's sum once, after
+  // the wave reduction; the dustbin row is done after the real rows.
+  float vc[NV4][4];
+#pragma unroll
+  for (int k = 0; k < NV4; ++k) {
+    const float4 q = vl[lane + 64 * k];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vc[k][c] = 4 * (lane + 64 * k) + c < N ? f4c(q, c) : -INFINITY;
+  }
+  const float vN = vl[NG].x;
+  const float xd = alpha2 + vN;  // the dustbin-column entry of every row
+  float acc[NV4][4];
+#pragma unroll
+  for (int k = 0; k < NV4; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[k][c] = 0.f;
+  // one row: t = x + v (x the row's entries, or alpha for the dustbin row),
+  // its update u, and its weighted exponentials into acc
+  auto row = [&](const float4 (&zq)[NV4], bool dust, int ri) {
+    float t[NV4][4];
+    float mx = xd;
+#pragma unroll
+    for (int k = 0; k < NV4; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        t[k][c] = (dust ? alpha2 : f4c(zq[k], c)) + vc[k][c];
+        mx = fmaxf(mx, t[k][c]);
+      }
+    mx = wave_max(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV4; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        t[k][c] = exp2_fast(t[k][c] - mx);
+        sum += t[k][c];
+      }
+    const float ed = exp2_fast(xd - mx);
+    sum = wave_sum(sum) + ed;
+    const float cr = dust ? (float)N : 1.f;
+    const float ur = (dust ? log2f((float)N) - lmn : -lmn) - mx - log2_fast(sum);
+    const float wgt = cr * __builtin_amdgcn_rcpf(sum);
+#pragma unroll
+    for (int k = 0; k < NV4; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[k][c] = fmaf(t[k][c], wgt, acc[k][c]);
+    if (lane == 0) {
+      sm_u[w * RPW + ri] = update_u ? ur : 0.f;
+      if (update_u) u_out[pt.uoff[b] + i0 + w * RPW + ri] = ur;
+    }
+  };
+  const int nreal = min(max(M - (i0 + w * RPW), 0), RPW);  // the wave's real rows (a prefix of its rows)
+#pragma unroll
+  for (int p = 0; p < NSTEP; ++p) {
+    if (p + 1 < NSTEP) load_step(p + 1, zbuf[(p + 1) & 1]);
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+      if (p * RS + r < nreal) row(zbuf[p & 1][r], false, p * RS + r);
+  }
+  {
+    // the dustbin row's place among the wave's rows; a pair whose real rows
+    // fill whole blocks gets it as an extra row of its last block (last wave)
+    const int rd = M - (i0 + w * RPW);
+    if (rd >= 0 && (rd < RPW || (w == W - 1 && rd == RPW))) row(zbuf[0][0], true, rd);
+    if (lane == 0)
+      for (int r = max(rd + 1, 0); r < RPW; ++r) sm_u[w * RPW + r] = -INFINITY;  // past the dustbin row
+    if (w == W - 1 && lane == 0 && rd != RPW) sm_u[RB] = -INFINITY;
+  }
+
+  const size_t pbase = (size_t)pt.p_off[b] + (size_t)gb * ldz;
+  if (update_u) {
+#pragma unroll
+    for (int k = 0; k < NV4; ++k) sm[w][lane + 64 * k] = make_float4(acc[k][0], acc[k][1], acc[k][2], acc[k][3]);
+  }
+  __syncthreads();
+
+  // exact partial of the real column jj over the block's rows (and the
+  // dustbin row when the block takes it as an extra row)
+  auto exact = [&](int jj) -> float {
+    float mx = -INFINITY;
+    for (int r = 0; r <= RB; ++r) {
+      const int i = i0 + r;
+      if (i > M) break;
+      const float z = i < M ? zp[(size_t)i * ldz + jj] : alpha2;
+      mx = fmaxf(mx, z + sm_u[r]);
+    }
+    float sum = 0.f;
+    for (int r = 0; r <= RB; ++r) {
+      const int i = i0 + r;
+      if (i > M) break;
+      const float z = i < M ? zp[(size_t)i * ldz + jj] : alpha2;
+      sum += exp2_fast(z + sm_u[r] - mx);
+    }
+    return mx + log2_fast(sum);
+  };
+
+  if (update_u) {
+    for (int q = threadIdx.x; q < NG; q += NT) {
+      const int j = 4 * q;
+      if (j >= N) break;
+      float T[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ww = 0; ww < W; ++ww) {
+        const float4 a = sm[ww][q];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) T[c] += f4c(a, c);
+      }
+      const float4 vq = vl[q];
+      float o[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (j + c >= N) o[c] = -INFINITY;
+        else if (T[c] >= kSumFloor) o[c] = log2_fast(T[c]) - lmn - f4c(vq, c);
+        else o[c] = exact(j + c);
+      }
+      *reinterpret_cast<float4*>(Pout + pbase + j) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    if (w == 0) {
+      // the dustbin column holds alpha in every row, so its partial is
+      // exactly alpha + lse2 of the block's u (no exponential of a row's
+      // entries can lose it, however far alpha lies below the rows' maxima)
+      float mx = -INFINITY;
+      for (int r = lane; r <= RB; r += 64)
+        if (i0 + r <= M) mx = fmaxf(mx, sm_u[r]);
+      mx = wave_max(mx);
+      float sum = 0.f;
+      for (int r = lane; r <= RB; r += 64)
+        if (i0 + r <= M) sum += exp2_fast(sm_u[r] - mx);
+      sum = wave_sum(sum);
+      if (lane == 0) Pdout[pt.gpre[b] + gb] = alpha2 + mx + log2_fast(sum);
+    }
+  }
+
+  if constexpr (ARG) {
+    // column argmax of Z + u over the block's real rows (lowest row on ties):
+    // each wave over its rows, then over the waves (rows ascending with the
+    // wave index)
+    __shared__ int4 smi[W][NG];
+    __syncthreads();  // the partial sums in sm have been read
+#pragma unroll
+    for (int k = 0; k < NV4; ++k) {
+      const int j = 4 * (lane + 64 * k);
+      float bv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      int bi[4] = {-1, -1, -1, -1};
+      for (int r = 0; r < RPW; ++r) {
+        const int i = i0 + w * RPW + r;
+        if (i < M && j < N) {
+          const float4 q = *reinterpret_cast<const float4*>(zp + (size_t)i * ldz + j);
+          const float ua = sm_u[w * RPW + r];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float y = f4c(q, c) + ua;
+            if (y > bv[c]) {
+              bv[c] = y;
+              bi[c] = i;
+            }
+          }
+        }
+      }
+      sm[w][lane + 64 * k] = make_float4(bv[0], bv[1], bv[2], bv[3]);
+      smi[w][lane + 64 * k] = make_int4(bi[0], bi[1], bi[2], bi[3]);
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < NG; q += NT) {
+      const int j = 4 * q;
+      if (j >= N) break;
+      float bv[4];
+      int bi[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bv[c] = f4c(sm[0][q], c);
+        bi[c] = c == 0 ? smi[0][q].x : c == 1 ? smi[0][q].y : c == 2 ? smi[0][q].z : smi[0][q].w;
+      }
+#pragma unroll
+      for (int ww = 1; ww < W; ++ww) {
+        const float4 a = sm[ww][q];
+        const int4 ai = smi[ww][q];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float y = f4c(a, c);
+          if (y > bv[c]) {
+            bv[c] = y;
+            bi[c] = c == 0 ? ai.x : c == 1 ? ai.y : c == 2 ? ai.z : ai.w;
+          }
+        }
+      }
+      *reinterpret_cast<float4*>(PV + pbase + j) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+      *reinterpret_cast<int4*>(PI + pbase + j) = make_int4(bi[0], bi[1], bi[2], bi[3]);
+    }
+  }
+}
+
 // Column reduction of the block partials of every pair: v_j = log2 nu_j -
 // lse2_g P[g][j] (write_v), and after the last iteration the column argmax
 // over the real rows (idx1) plus the default (-1 / 0) side-B outputs.
@@ -803,6 +1113,51 @@ hipError_t launch_sink_rows(const float* Z, const PairTable& pt, const float* v_
   SG_ROWS(2, 1) SG_ROWS(2, 2) SG_ROWS(2, 4) SG_ROWS(2, 8)
   SG_ROWS(1, 1) SG_ROWS(1, 2) SG_ROWS(1, 4) SG_ROWS(1, 8) SG_ROWS(1, 16)
 #undef SG_ROWS
+  return hipErrorInvalidValue;
+}
+
+// Rows per workgroup of the fused one-pass iteration (four waves of 16 rows,
+// two rows at a time), and the widest rows it takes.  Measured on 32 pairs of
+// 1024 x 1024 (graph-replayed, 100 iterations): 27.3 us per iteration against
+// 28.7 us with eight waves of 8 rows, 29.4 us with 32-row blocks and 35.1 us
+// for the row pass + column reduction pair.  Rows of up to 2048 columns (8
+// float4 per lane) leave one or two waves per SIMD and blocks of very
+// different cost in a ragged batch: 56.4 against 49.8 us per iteration for
+// the pair of launches, which those batches keep.
+constexpr int kIterRows = 64;
+constexpr int kIterWaves = 4;
+constexpr int kIterMaxCols = 1024;
+
+int sink_iter_blocks(int M, int rb) { return std::max(1, (M + rb - 1) / rb); }
+
+int sink_iter_rows_per_block(const int* N, int n_pairs) {
+  for (int b = 0; b < n_pairs; ++b)
+    if (N[b] > kIterMaxCols) return 0;
+  return kIterRows;
+}
+
+hipError_t launch_sink_iter(const float* Z, const PairTable& pt, const float* Pin, const float* Pdin, float* u_out,
+                            float* Pout, float* Pdout, float* PV, int* PI, float alpha2, const float* alpha_dev,
+                            int update_u, hipStream_t st) {
+  const int blocks = pt.gpre[pt.n_pairs];
+  if (blocks <= 0) return hipSuccess;
+  if (pt.rb != kIterRows) return hipErrorInvalidValue;
+  const int nv4 = sink_nv4(max_n(pt));
+  const bool arg = PV != nullptr;
+#define SG_ITER(NV, RS)                                                                                    \
+  if (nv4 == NV) {                                                                                         \
+    if (arg)                                                                                               \
+      hipLaunchKernelGGL((k_sink_iter<kIterWaves, kIterRows / kIterWaves, NV, RS, true>), dim3(blocks),     \
+                         dim3(64 * kIterWaves), 0, st, Z, pt, Pin, Pdin, u_out, Pout, Pdout, PV, PI, alpha2, \
+                         alpha_dev, update_u);                                                             \
+    else                                                                                                   \
+      hipLaunchKernelGGL((k_sink_iter<kIterWaves, kIterRows / kIterWaves, NV, RS, false>), dim3(blocks),    \
+                         dim3(64 * kIterWaves), 0, st, Z, pt, Pin, Pdin, u_out, Pout, Pdout, PV, PI, alpha2, \
+                         alpha_dev, update_u);                                                             \
+    return hipGetLastError();                                                                              \
+  }
+  SG_ITER(1, 2) SG_ITER(2, 2) SG_ITER(4, 2)
+#undef SG_ITER
   return hipErrorInvalidValue;
 }
 
