@@ -398,6 +398,63 @@ def per_config(sg, synth, np, torch, dev, reps=10):
     return res
 
 
+def launch_floor(torch, n=200, reps=10):
+    """Per-launch time of graph-replayed chains of n dependent launches: a
+    one-element add (the dispatch floor) and a row sum over a 1025 x 1024
+    fp32 matrix (the size of a Sinkhorn sweep's read).  torch's own kernels
+    serve as the reference; only the dependency and the replay matter."""
+    out = {}
+    dev = torch.device("cuda:0")
+    x = torch.zeros(1, device=dev)
+    Z = torch.randn(1025, 1024, device=dev)
+    r = torch.empty(1025, device=dev)
+    for name, fn in (("empty_us", lambda: x.add_(1.0)), ("row_sum_4MB_us", lambda: torch.sum(Z, dim=1, out=r))):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        best = 1e9
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            b.synchronize()
+            best = min(best, a.elapsed_time(b))
+        out[name] = round(1e3 * best / n, 3)
+    return out
+
+
+def summarize_trace(path, pattern):
+    """Dispatch durations and the gaps between consecutive dispatches of the
+    kernels whose name contains `pattern`, from a rocprofv3 kernel trace
+    (run_kernel_trace.csv): gap = next dispatch's start - this one's end,
+    for consecutive dispatches that both match and lie within 20 us (the
+    back-to-back launches of one replayed pass)."""
+    import csv
+    rows = []
+    for r in csv.DictReader(open(path)):
+        rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    dur = [(e - s) / 1e3 for s, e, n in rows if pattern in n]
+    gaps = [(rows[i + 1][0] - rows[i][1]) / 1e3 for i in range(len(rows) - 1)
+            if pattern in rows[i][2] and pattern in rows[i + 1][2] and rows[i + 1][0] - rows[i][1] < 20000]
+    import statistics as st
+    return {"kernel": pattern, "dispatches": len(dur), "exec_mean_us": round(st.mean(dur), 3),
+            "exec_median_us": round(st.median(dur), 3), "gap_pairs": len(gaps),
+            "gap_mean_us": round(st.mean(gaps), 3) if gaps else None,
+            "gap_median_us": round(st.median(gaps), 3) if gaps else None,
+            "period_median_us": round(st.median(dur) + st.median(gaps), 3) if gaps else None}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -419,7 +476,14 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration context timings")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="before the steps, copy this many MiB with a plain device copy (counter scaling)")
+    ap.add_argument("--no-launch-floor", action="store_true",
+                    help="skip the dependent-launch floor of a replayed graph (launch_floor_us)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("CSV", "KERNEL"),
+                    help="print execution and gap statistics of KERNEL from a rocprofv3 kernel trace and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(*args.summarize_trace)))
+        return
     if args.gpus != 1:
         log(f"bench.py runs on one GPU only: the matching pass is measured on a single MI355X "
             f"(pairs are independent; see the sharding note of the design). --gpus {args.gpus} refused.")
@@ -635,6 +699,13 @@ def main():
         log(f"batch: {batch}")
 
     adaptive = adaptive_bench(args, cfg, dev, sg, synth, np, torch) if args.adaptive else None
+    floor = None if args.no_launch_floor else launch_floor(torch)
+    if floor:
+        log(f"launch floor: {floor}")
+        if roofline is not None and "k_lse" in roofline.get("kernel", ""):
+            # the sweep against a plain graph-replayed read of the same matrix
+            roofline["launch_floor_us"] = floor
+            roofline["avg_launch_over_row_sum_floor"] = round(roofline["avg_launch_us"] / floor["row_sum_4MB_us"], 3)
     configs = None
     if not args.no_configs and args.head == "sinkhorn" and args.cross == "standard" and not args.rope:
         configs = per_config(sg, synth, np, torch, dev)
@@ -660,7 +731,7 @@ def main():
                    "head": args.head, "cross_attention": args.cross, "rope": args.rope},
         "roofline": roofline, "mfma_util_pct": mfma_util, "cpu_baseline": cpu, "latency": latency,
         "stages_ms": stages, "kernels": kernels,
-        "batch_throughput": batch,
+        "batch_throughput": batch, "launch_floor_us": floor,
         "per_config": configs,
         "adaptive": adaptive,
         "baseline_context": {"pages_ms_per_pair": {"GTX1080_1024kp": 87.0, "unstated_hw_2048kp": 70.0},
