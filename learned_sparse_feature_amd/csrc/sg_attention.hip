@@ -349,15 +349,26 @@ __global__ __launch_bounds__(256, 4) void k_attention_wide(AttnArgs a, SegTable 
   // l of a wave writes 16 bytes at the wave's LDS base + 16 l), so no
   // registers hold the tile in flight; chunk c = tid + 256 i lands at
   // element 8 c of the buffer.
-  auto gload = [&](int k0, int buf) {
+  auto chunk_src = [&](int k0, int i) -> const bf16* {
+    const int c = tid + 256 * i;
+    const int kb = c / ((KBLK + VBLK) * 64), r = c % ((KBLK + VBLK) * 64);
+    const size_t tile = (size_t)((krow0 + 32 * min(k0 / 32 + kb, nkb - 1)) >> 5);
+    return r < KBLK * 64 ? ks + (tile * (D / 16) + h * (DH / 16)) * 512 + 8 * r
+                         : vs + (tile * (D / 32) + (h * DH) / 32) * 1024 + 8 * (r - KBLK * 64);
+  };
+  // a tile wholly inside the image starts 64 D elements (two 32-key blocks of
+  // K and of V) after the previous one: its chunk addresses are those of the
+  // first tile plus that step; only the partial tile needs the clamped form
+  const bf16* src0[KCH];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int kb = c / ((KBLK + VBLK) * 64), r = c % ((KBLK + VBLK) * 64);
-      const size_t tile = (size_t)((krow0 + 32 * min(k0 / 32 + kb, nkb - 1)) >> 5);
-      const bf16* src = r < KBLK * 64 ? ks + (tile * (D / 16) + h * (DH / 16)) * 512 + 8 * r
-                                      : vs + (tile * (D / 32) + (h * DH) / 32) * 1024 + 8 * (r - KBLK * 64);
-      lds_dma16(src, &Ts[buf][8 * (64 * w + 256 * i)]);
+  for (int i = 0; i < KCH; ++i) src0[i] = chunk_src(0, i);
+  auto gload = [&](int k0, int buf) {
+    if (k0 + BKEY <= nk) {
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) lds_dma16(src0[i] + (size_t)k0 * D, &Ts[buf][8 * (64 * w + 256 * i)]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) lds_dma16(chunk_src(k0, i), &Ts[buf][8 * (64 * w + 256 * i)]);
     }
   };
 
@@ -371,9 +382,12 @@ __global__ __launch_bounds__(256, 4) void k_attention_wide(AttnArgs a, SegTable 
   __builtin_amdgcn_s_waitcnt(0);  // the tile is in LDS
   __syncthreads();
   // Both 32-key blocks of a tile are taken together: two independent QK^T
-  // chains, one maximum, one rescale of O and 32 exponentials per lane.
+  // chains, one maximum, one rescale of O and 32 exponentials per lane.  The
+  // tiles that lie wholly inside the image run without any masking code; the
+  // last, partial tile (TAIL) masks keys past the image.
   static_assert(BKEY == 64, "two 32-key blocks per tile");
-  for (int kt = 0; kt < ntk; ++kt) {
+  auto step = [&](int kt, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
     const int cur = kt & 1;
     if (kt + 1 < ntk) gload((kt + 1) * BKEY, cur ^ 1);  // (buffer cur ^ 1 was released by the last barrier)
     const int k0 = kt * BKEY;
@@ -385,9 +399,7 @@ __global__ __launch_bounds__(256, 4) void k_attention_wide(AttnArgs a, SegTable 
       S0 = mfma(*reinterpret_cast<const bf16x8*>(tb0 + i * 512), Qr[i], S0);
       S1 = mfma(*reinterpret_cast<const bf16x8*>(tb1 + i * 512), Qr[i], S1);
     }
-    // the maximum is taken over the raw scores (the scale is positive) and the
-    // scale folded into the exponent's FMA
-    if (k0 + BKEY > nk) {  // keys past the image (a block past it re-read the last block)
+    if constexpr (TAIL) {  // keys past the image (a block past it re-read the last block)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kk = k0 + 8 * (i >> 2) + 4 * hi + (i & 3);
@@ -395,21 +407,34 @@ __global__ __launch_bounds__(256, 4) void k_attention_wide(AttnArgs a, SegTable 
         if (kk + 32 >= nk) S1[i] = -INFINITY;
       }
     }
+    // the maximum is taken over the raw scores (the scale is positive) with
+    // the three-operand maximum, which takes the accumulators as they are
+    // (the scores are never NaN), and the scale folded into the exponent's FMA
     float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, fmaxf(S0[i], S1[i]));
+    for (int i = 0; i < 16; ++i) tmax = __builtin_elementwise_maximum(tmax, __builtin_elementwise_maximum(S0[i], S1[i]));
     tmax = half_swap_max(tmax);
     const float m_new = fmaxf(m_run, tmax * a.scale2);
     const float corr = exp2_fast(m_run - m_new);
     float psum = 0.f;
+    // P in bf16, packed two keys per 32-bit word by the converter itself
     bf16x8 pb[2][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2_fast(fmaf(b ? S1[i] : S0[i], a.scale2, -m_new));
-        psum += p;
-        pb[b][i >> 3][i & 7] = (bf16)p;
+      for (int j = 0; j < 2; ++j) {
+        u32x4 u;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = 8 * j + 2 * x;
+          const float p0 = exp2_fast(fmaf(b ? S1[i] : S0[i], a.scale2, -m_new));
+          const float p1 = exp2_fast(fmaf(b ? S1[i + 1] : S0[i + 1], a.scale2, -m_new));
+          psum += p0;
+          psum += p1;
+          const bf16x2 pp = {(bf16)p0, (bf16)p1};
+          u[x] = __builtin_bit_cast(uint32_t, pp);
+        }
+        pb[b][j] = __builtin_bit_cast(bf16x8, u);
       }
     l_run = l_run * corr + psum;
     m_run = m_new;
@@ -419,30 +444,34 @@ __global__ __launch_bounds__(256, 4) void k_attention_wide(AttnArgs a, SegTable 
 #pragma unroll
         for (int i = 0; i < 16; ++i) O[c][i] *= corr;
     }
-    // values of keys past the image are zeroed (their P is 0, but padding
-    // rows may hold anything a caller staged there)
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int kb0 = k0 + 32 * b;
-      if (kb0 >= nk) break;
-      const bool vtail = kb0 + 32 > nk;
+      if (TAIL && kb0 >= nk) break;
       const bf16* tb = b ? tb1 : tb0;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int cb = 0; cb < DH / 32; ++cb) {
           bf16x8 va = *reinterpret_cast<const bf16x8*>(tb + (KBLK + 2 * cb + j) * 512);
-          if (vtail) {
+          if constexpr (TAIL) {
+            // values of keys past the image are zeroed (their P is 0, but
+            // padding rows may hold anything a caller staged there)
+            if (kb0 + 32 > nk) {
 #pragma unroll
-            for (int x = 0; x < 8; ++x)
-              if (kb0 + 16 * j + 8 * (x >> 2) + 4 * hi + (x & 3) >= nk) va[x] = (bf16)0.f;
+              for (int x = 0; x < 8; ++x)
+                if (kb0 + 16 * j + 8 * (x >> 2) + 4 * hi + (x & 3) >= nk) va[x] = (bf16)0.f;
+            }
           }
           O[cb] = mfma(va, pb[b][j], O[cb]);
         }
     }
     __builtin_amdgcn_s_waitcnt(0);  // the next tile is in LDS
     __syncthreads();
-  }
+  };
+  const int ntf = nk / BKEY;  // tiles wholly inside the image
+  for (int kt = 0; kt < ntf; ++kt) step(kt, std::false_type{});
+  if (ntf < ntk) step(ntf, std::true_type{});
 
   l_run = half_swap_sum(l_run);
   if (qvalid) {
