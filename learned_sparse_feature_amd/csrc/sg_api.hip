@@ -344,6 +344,17 @@ void make_plan(const Problem& p, Plan& pl) {
     pl.uf += ld4(M + 1);
     pl.vf += ld4(N + 1);
   }
+  // the fused iteration dispatches the blocks of the widest rows first, so
+  // that the last blocks to start are the cheapest
+  {
+    int ord[SG_MAX_BATCH];
+    for (int b = 0; b < p.B; ++b) ord[b] = b;
+    std::stable_sort(ord, ord + p.B, [&](int a, int c) { return p.N[a] > p.N[c]; });
+    for (int k = 0; k < p.B; ++k) {
+      pl.pt.ord[k] = (unsigned char)ord[k];
+      pl.pt.opre[k + 1] = pl.pt.opre[k] + pl.pt.gpre[ord[k] + 1] - pl.pt.gpre[ord[k]];
+    }
+  }
   pl.R = R;
   pl.zf = zf; pl.pf = pf; pl.pd = pl.pt.gpre[p.B];
   pl.ztf = pl.two_sweep ? ztf : 0;

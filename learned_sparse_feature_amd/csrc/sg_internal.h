@@ -39,6 +39,11 @@ struct PairTable {
   int vpre[SG_MAX_BATCH + 1];                      // prefix sums of (N+1): flattened v rows
   int gpre[SG_MAX_BATCH + 1];                      // prefix sums of G = ceil((M+1)/rb): row blocks
   int uoff[SG_MAX_BATCH], voff[SG_MAX_BATCH];      // storage offsets of u, v (multiples of 4)
+  // dispatch order of the fused Sinkhorn iteration's row blocks: the pairs
+  // ord[0], ord[1], ... (widest rows first), pair ord[k] taking blocks
+  // [opre[k], opre[k + 1])
+  int opre[SG_MAX_BATCH + 1];
+  unsigned char ord[SG_MAX_BATCH];
 };
 
 __host__ __device__ inline int ld4(int n) { return (n + 3) & ~3; }

@@ -271,25 +271,25 @@ __global__ __launch_bounds__(256) void k_sink_rows(const float* __restrict__ Zb,
 //    per-block column argmax of Z + u into PV / PI.
 // The partials are double-buffered by the caller: iteration t reads the
 // buffer iteration t - 1 wrote and writes the other one.
-template <int W, int RPW, int NV4, int RS, bool ARG>
-__global__ __launch_bounds__(64 * W) void k_sink_iter(const float* __restrict__ Zb, PairTable pt,
-                                                      const float* __restrict__ Pin, const float* __restrict__ Pdin,
-                                                      float* __restrict__ u_out, float* __restrict__ Pout,
-                                                      float* __restrict__ Pdout, float* __restrict__ PV,
-                                                      int* __restrict__ PI, float alpha2,
-                                                      const float* __restrict__ alpha_dev, int update_u) {
+// One workgroup's share of the iteration for pair b, with rows of up to
+// 256 NV4 columns held in registers (NV4 float4 per lane).  The LDS arrays
+// come from the kernel, sized for its widest rows (NGS float4 column groups):
+// sm [W][NGS], vl [NGS + 1] (vl[NGS].x: the dustbin column's dual), sm_u
+// [RB + 1] (+1: the dustbin row may follow the block's last row), smi
+// [W][NGS] (ARG only).
+template <int W, int RPW, int NV4, int RS, bool ARG, int NGS>
+__device__ __forceinline__ void sink_iter_block(const float* __restrict__ Zb, const PairTable& pt, int b, int gb,
+                                                const float* __restrict__ Pin, const float* __restrict__ Pdin,
+                                                float* __restrict__ u_out, float* __restrict__ Pout,
+                                                float* __restrict__ Pdout, float* __restrict__ PV,
+                                                int* __restrict__ PI, float alpha2, int update_u,
+                                                float4 (*sm)[NGS], float4* vl, float* sm_u, int4 (*smi)[NGS]) {
   static_assert(RPW % RS == 0, "rows per wave must be a multiple of the rows per step");
+  static_assert(64 * NV4 <= NGS, "the LDS arrays hold the widest rows");
   constexpr int NT = 64 * W;    // threads
   constexpr int RB = W * RPW;
   constexpr int NG = 64 * NV4;  // float4 column groups of a row held by one wave
   constexpr int NSTEP = RPW / RS;
-  __shared__ float4 sm[W][NG];
-  __shared__ float4 vl[NG + 1];  // v of the columns; vl[NG].x: the dustbin column's
-  __shared__ float sm_u[RB + 1];  // (+1: the dustbin row may follow the block's last row)
-  if (alpha_dev) alpha2 = alpha_dev[0] * kLog2e;
-  const int b = find_pair(pt.gpre, pt.n_pairs, blockIdx.x);
-  if (b >= pt.n_pairs) return;
-  const int gb = blockIdx.x - pt.gpre[b];
   const int G = pt.gpre[b + 1] - pt.gpre[b];
   const int M = pt.M[b], N = pt.N[b];
   const int i0 = gb * RB;
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(64 * W) void k_sink_iter(const float* __restrict__ 
       }
       float o[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = j + c < N ? -lmn - (mx[c] + log2_fast(sum[c])) : 0.f;
+      for (int c = 0; c < 4; ++c) o[c] = j + c < N ? -lmn - (mx[c] + log2_fast(sum[c])) : -INFINITY;
       vl[q] = make_float4(o[0], o[1], o[2], o[3]);
     }
     if (w == 0) {  // the dustbin column: v_N = log2 M - log2(M+N) - lse2_g Pdin[g]
@@ -361,26 +361,37 @@ __global__ __launch_bounds__(64 * W) void k_sink_iter(const float* __restrict__ 
       }
       const float wm = wave_max(m);
       sum = wave_sum(m == -INFINITY ? 0.f : sum * exp2_fast(m - wm));
-      if (lane == 0) vl[NG].x = log2f((float)M) - lmn - (wm + log2_fast(sum));
+      if (lane == 0) vl[NGS].x = log2f((float)M) - lmn - (wm + log2_fast(sum));
     }
+    for (int q = (N + 3) / 4 + threadIdx.x; q < NG; q += NT) vl[q] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
   } else {
-    for (int q = threadIdx.x; q <= NG; q += NT) vl[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = threadIdx.x; q < NG; q += NT) {
+      const int j = 4 * q;
+      vl[q] = make_float4(j < N ? 0.f : -INFINITY, j + 1 < N ? 0.f : -INFINITY, j + 2 < N ? 0.f : -INFINITY,
+                          j + 3 < N ? 0.f : -INFINITY);
+    }
+    if (threadIdx.x == 0) vl[NGS] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
 
   // ---- phase 2: row update of the wave's rows and the block's column partials
-  // The duals of masked columns are -inf, so that t = Z + v needs no select
-  // (the loads are clamped in bounds and finite); the dustbin column (the
-  // same entry alpha + v_N for every lane) joins each row's sum once, after
-  // the wave reduction; the dustbin row is done after the real rows.
-  float vc[NV4][4];
+  // The duals of masked columns are -inf in vl, so that t = Z + v needs no
+  // select (the loads are clamped in bounds and finite); the dustbin column
+  // (the same entry alpha + v_N for every lane) joins each row's sum once,
+  // after the wave reduction; the dustbin row is done after the real rows.
+  // The duals stay in registers, except for the widest rows (VCL), which
+  // read them from LDS for every row: their 32 registers buy a wave per SIMD.
+  constexpr bool VCL = NV4 >= 8;
+  float vc[VCL ? 1 : NV4][4];
+  if constexpr (!VCL) {
 #pragma unroll
-  for (int k = 0; k < NV4; ++k) {
-    const float4 q = vl[lane + 64 * k];
+    for (int k = 0; k < NV4; ++k) {
+      const float4 q = vl[lane + 64 * k];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) vc[k][c] = 4 * (lane + 64 * k) + c < N ? f4c(q, c) : -INFINITY;
+      for (int c = 0; c < 4; ++c) vc[k][c] = f4c(q, c);
+    }
   }
-  const float vN = vl[NG].x;
+  const float vN = vl[NGS].x;
   const float xd = alpha2 + vN;  // the dustbin-column entry of every row
   float acc[NV4][4];
 #pragma unroll
@@ -393,12 +404,16 @@ __global__ __launch_bounds__(64 * W) void k_sink_iter(const float* __restrict__ 
     float t[NV4][4];
     float mx = xd;
 #pragma unroll
-    for (int k = 0; k < NV4; ++k)
+    for (int k = 0; k < NV4; ++k) {
+      float4 vq;
+      if constexpr (VCL) vq = vl[lane + 64 * k];
+      else vq = make_float4(vc[k][0], vc[k][1], vc[k][2], vc[k][3]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        t[k][c] = (dust ? alpha2 : f4c(zq[k], c)) + vc[k][c];
+        t[k][c] = (dust ? alpha2 : f4c(zq[k], c)) + f4c(vq, c);
         mx = fmaxf(mx, t[k][c]);
       }
+    }
     mx = wave_max(mx);
     float sum = 0.f;
 #pragma unroll
@@ -508,7 +523,6 @@ __global__ __launch_bounds__(64 * W) void k_sink_iter(const float* __restrict__ 
     // column argmax of Z + u over the block's real rows (lowest row on ties):
     // each wave over its rows, then over the waves (rows ascending with the
     // wave index)
-    __shared__ int4 smi[W][NG];
     __syncthreads();  // the partial sums in sm have been read
 #pragma unroll
     for (int k = 0; k < NV4; ++k) {
@@ -561,6 +575,54 @@ __global__ __launch_bounds__(64 * W) void k_sink_iter(const float* __restrict__ 
       *reinterpret_cast<int4*>(PI + pbase + j) = make_int4(bi[0], bi[1], bi[2], bi[3]);
     }
   }
+}
+
+// The kernel: each workgroup runs the register layout of its own pair's row
+// width (a wave-uniform choice), so that the narrow pairs of a ragged batch
+// do not pay for the widest one; rows of more than 1024 columns take one row
+// per step (their two-step buffer would not fit the registers).  The LDS
+// arrays are shared by the layouts, sized for NVMAX.
+template <int W, int RPW, int NVMAX, int RS, bool ARG>
+__global__ __launch_bounds__(64 * W) void k_sink_iter(const float* __restrict__ Zb, PairTable pt,
+                                                      const float* __restrict__ Pin, const float* __restrict__ Pdin,
+                                                      float* __restrict__ u_out, float* __restrict__ Pout,
+                                                      float* __restrict__ Pdout, float* __restrict__ PV,
+                                                      int* __restrict__ PI, float alpha2,
+                                                      const float* __restrict__ alpha_dev, int update_u) {
+  constexpr int NGS = 64 * NVMAX;
+  __shared__ float4 sm[W][NGS];
+  __shared__ float4 vl[NGS + 1];
+  __shared__ float sm_u[W * RPW + 1];
+  __shared__ int4 smi[ARG ? W : 1][ARG ? NGS : 1];
+  if (alpha_dev) alpha2 = alpha_dev[0] * kLog2e;
+  const int k = find_pair(pt.opre, pt.n_pairs, blockIdx.x);
+  if (k >= pt.n_pairs) return;
+  const int b = pt.ord[k], gb = blockIdx.x - pt.opre[k];
+  const int N = pt.N[b];
+  int4 (*const smip)[NGS] = reinterpret_cast<int4 (*)[NGS]>(&smi[0][0]);  // (used only with ARG)
+#define SG_BLOCK(NV, R)                                                                                      \
+  sink_iter_block<W, RPW, NV, R, ARG, NGS>(Zb, pt, b, gb, Pin, Pdin, u_out, Pout, Pdout, PV, PI, alpha2, update_u, \
+                                           sm, vl, sm_u, smip)
+  if constexpr (NVMAX >= 8) {
+    if (N > 1024) {
+      SG_BLOCK(8, 1);
+      return;
+    }
+  }
+  if constexpr (NVMAX >= 4) {
+    if (N > 512) {
+      SG_BLOCK(4, RS);
+      return;
+    }
+  }
+  if constexpr (NVMAX >= 2) {
+    if (N > 256) {
+      SG_BLOCK(2, RS);
+      return;
+    }
+  }
+  SG_BLOCK(1, RS);
+#undef SG_BLOCK
 }
 
 // Column reduction of the block partials of every pair: v_j = log2 nu_j -
@@ -1118,15 +1180,17 @@ hipError_t launch_sink_rows(const float* Z, const PairTable& pt, const float* v_
 
 // Rows per workgroup of the fused one-pass iteration (four waves of 16 rows,
 // two rows at a time), and the widest rows it takes.  Measured on 32 pairs of
-// 1024 x 1024 (graph-replayed, 100 iterations): 27.3 us per iteration against
-// 28.7 us with eight waves of 8 rows, 29.4 us with 32-row blocks and 35.1 us
-// for the row pass + column reduction pair.  Rows of up to 2048 columns (8
-// float4 per lane) leave one or two waves per SIMD and blocks of very
-// different cost in a ragged batch: 56.4 against 49.8 us per iteration for
-// the pair of launches, which those batches keep.
+// 1024 x 1024 (graph-replayed, 100 iterations): 27.3-28.2 us per iteration
+// against 28.7 us with eight waves of 8 rows, 29.4 us with 32-row blocks and
+// 35.0 us for the row pass + column reduction pair.  On 32 ragged pairs (M, N
+// from 256 to 2048, 174 MB of couplings): 39.0 us against 54.8 us for the pair
+// of launches; the same kernel took 52.3 us with one register layout for
+// every pair (the widest), 47.3 us with per-pair layouts, and the duals of the
+// widest rows in registers (169 registers: two waves per SIMD), widest-first
+// order included.
 constexpr int kIterRows = 64;
 constexpr int kIterWaves = 4;
-constexpr int kIterMaxCols = 1024;
+constexpr int kIterMaxCols = 2048;
 
 int sink_iter_blocks(int M, int rb) { return std::max(1, (M + rb - 1) / rb); }
 
@@ -1156,7 +1220,7 @@ hipError_t launch_sink_iter(const float* Z, const PairTable& pt, const float* Pi
                          alpha_dev, update_u);                                                             \
     return hipGetLastError();                                                                              \
   }
-  SG_ITER(1, 2) SG_ITER(2, 2) SG_ITER(4, 2)
+  SG_ITER(1, 2) SG_ITER(2, 2) SG_ITER(4, 2) SG_ITER(8, 2)
 #undef SG_ITER
   return hipErrorInvalidValue;
 }
