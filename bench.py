@@ -339,14 +339,14 @@ def latency_percentiles(step, sg, torch, n):
     return {"passes": n, "p10_ms": q(0.1), "p50_ms": q(0.5), "p90_ms": q(0.9)}
 
 
-def per_config(sg, synth, np, torch, dev, reps=10):
+def per_config(sg, synth, np, torch, dev, reps=10, ids=(0, 1, 3, 4)):
     """Every configuration's pass (cfg 0-3 one pair per call, cfg 4 its ragged
     32-pair batch): median wall time per call over graph replays and the stage
     times of an eager pass with stage events (context beside the headline)."""
     keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
     names = ["encoder", "gnn", "projection_scores", "sinkhorn", "extraction"]
     res = {}
-    for cid in (0, 1, 3, 4):
+    for cid in ids:
         cfg = synth.CONFIGS[cid]
         w = synth.make_weights(cfg)
         W = sg.pack_weights(w, device=dev)
@@ -355,6 +355,7 @@ def per_config(sg, synth, np, torch, dev, reps=10):
             t = [torch.from_numpy(b[k]).to(dev) for k in keys]
             img = (*b["image_size0"], *b["image_size1"])
             Ms, Ns = [int(x) for x in b["M"]], [int(x) for x in b["N"]]
+            coupling_bytes = sum(4.0 * (m + 1) * (n + 1) for m, n in zip(Ms, Ns))
             ws = torch.empty(sg.workspace_size(W, cfg.pad, cfg.pad, cfg.batch), dtype=torch.uint8, device=dev)
 
             def call(**kw):
@@ -363,6 +364,7 @@ def per_config(sg, synth, np, torch, dev, reps=10):
             pairs = cfg.batch
         else:
             pair = synth.make_pair(cfg)
+            coupling_bytes = 4.0 * (cfg.M + 1) * (cfg.N + 1)
             t = [torch.from_numpy(pair[k]).to(dev) for k in keys]
             img = (*pair["image_size0"], *pair["image_size1"])
             ws = torch.empty(sg.workspace_size(W, cfg.M, cfg.N, 1), dtype=torch.uint8, device=dev)
@@ -394,6 +396,13 @@ def per_config(sg, synth, np, torch, dev, reps=10):
                             "pairs_per_call": pairs, "dtype": cfg.dtype, "T": cfg.T, "L": cfg.L,
                             "ms_per_call_p50": round(med, 4), "pairs_per_s": round(pairs / med * 1e3, 2),
                             "stages_ms": {n: round(float(v / 3), 4) for n, v in zip(names, acc)}}
+        # the Sinkhorn stage against one fused read of the couplings per
+        # iteration (the stage's T iterations and its final reduction)
+        sk_us = float(acc[names.index("sinkhorn")] / 3) * 1e3
+        if cfg.T > 0 and sk_us > 0:
+            res[f"cfg{cid}"]["sinkhorn"] = {"us_per_iteration": round(sk_us / cfg.T, 3),
+                                            "bytes_per_iteration": coupling_bytes,
+                                            "frac_hbm": round(coupling_bytes * cfg.T / (sk_us * 1e-6) / 1e9 / PEAK["hbm_GBps"], 4)}
         log(f"cfg {cid}: {res[f'cfg{cid}']}")
     return res
 
@@ -474,6 +483,8 @@ def main():
     ap.add_argument("--adaptive", action="store_true",
                     help="also time adaptive depth / width (forced exits and pruning) with the double-softmax head")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration context timings")
+    ap.add_argument("--configs", default="0,1,3,4",
+                    help="comma-separated configuration ids of the per-configuration timings (default 0,1,3,4)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="before the steps, copy this many MiB with a plain device copy (counter scaling)")
     ap.add_argument("--no-launch-floor", action="store_true",
@@ -708,7 +719,7 @@ def main():
             roofline["avg_launch_over_row_sum_floor"] = round(roofline["avg_launch_us"] / floor["row_sum_4MB_us"], 3)
     configs = None
     if not args.no_configs and args.head == "sinkhorn" and args.cross == "standard" and not args.rope:
-        configs = per_config(sg, synth, np, torch, dev)
+        configs = per_config(sg, synth, np, torch, dev, ids=[int(c) for c in args.configs.split(",") if c.strip()])
 
     cpu = None
     if not args.no_cpu:
