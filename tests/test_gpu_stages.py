@@ -148,6 +148,8 @@ SCHEDULES = ["two", "one"]
     (700, 3, 64, 50, -1.0),
     (3, 700, 64, 50, 2.0),
     (257, 1025, 64, 30, 1.0),
+    (64, 2048, 64, 30, 1.0),
+    (1, 2047, 64, 10, 0.5),
     (40, 50, 64, 0, 1.0),
     (0, 5, 64, 10, 1.0),
     (6, 0, 64, 10, 1.0),
