@@ -15,6 +15,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 instructions are kept out of every code object
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first kernel arguments arrive in SGPRs when a wave starts (kernarg
+    # preloading), so no launch waits on a scalar load of its arguments
+    "-mllvm", "-amdgpu-kernarg-preload-count=14",
     "-Wall", "-Wno-unused-result", "-Wno-unused-function",
 ]
 
