@@ -307,6 +307,25 @@ sg_status sg_stage_gnn_pos(float* xA, const float* posA, int32_t M, float* xB, c
 sg_status sg_stage_project(const float* x, int32_t n, const sg_weights* weights, float* f_out,
                            const sg_opts* opts);
 
+/*
+ * The scores of the optimal-matching layer from the last GNN states xA
+ * [M][D], xB [N][D] (fp32, device): the final projection f = W_f x + b_f of
+ * both images (realcat notes section "Attentional Aggregation", last
+ * equation), the scores S = f_A f_B^T / sqrt(D) (section "匹配得分预测"; the
+ * forward notes' scaling) and the dustbin row and column of the network's
+ * dustbin score alpha (section "遮挡以及可见性"), written as the bordered
+ * (M+1) x (N+1) matrix Z [(M+1)][ldZ] fp32, natural log, caller-owned: the
+ * input sg_stage_sinkhorn takes.  M or N may be 0 (only the border is
+ * written).  Errors: negative counts, NULL Z or states, ldZ < N+1 ->
+ * SG_ERR_INVALID_ARG; M or N above 4096 -> SG_ERR_UNSUPPORTED.  Workspace:
+ * sg_stage_scores_workspace_size.
+ */
+sg_status sg_stage_scores(const float* xA, int32_t M, const float* xB, int32_t N, const sg_weights* weights,
+                          float* Z, int64_t ldZ, const sg_opts* opts);
+
+/* Workspace bytes of sg_stage_scores for M x N points of dimension D. */
+size_t sg_stage_scores_workspace_size(int32_t M, int32_t N, int32_t D);
+
 /* The optimal-matching layer from matching descriptors fA [M][D], fB [N][D]
    (fp32): scores S = fA fB^T / sqrt(D) (realcat notes section "匹配得分预测";
    the forward notes' scaling), the dustbin row and column of score alpha

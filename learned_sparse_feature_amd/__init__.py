@@ -19,7 +19,7 @@ from ._lib import (SG_BF16, SG_CROSS_BIDIRECTIONAL, SG_CROSS_STANDARD, SG_F32, S
                    SG_K_NONE, SG_K_SINKHORN, SG_MAX_BATCH, SG_N_STAGE_EVENTS, SgError, SgOpts, SgWeights)
 
 __all__ = ["Weights", "weights_config", "pack_weights", "workspace_size", "sg_match",
-           "sg_match_batch", "sg_stage_encode", "sg_stage_gnn", "sg_stage_project",
+           "sg_match_batch", "sg_stage_encode", "sg_stage_gnn", "sg_stage_project", "sg_stage_scores",
            "sg_stage_match", "sg_stage_match_ds", "sg_stage_sinkhorn", "sg_stage_sinkhorn_noalloc", "sg_stage_extract", "lib", "SgError", "SG_K_GEMM", "SG_K_ATTENTION", "SG_K_SINKHORN",
            "SG_N_STAGE_EVENTS"]
 
@@ -370,6 +370,24 @@ def sg_stage_project(x, weights: Weights) -> torch.Tensor:
     o, keep, _ = _opts(x.device)
     _lib.check(lib().sg_stage_project(_ptr(x), n, weights.ref, _ptr(f), C.byref(o)), "sg_stage_project")
     return f
+
+
+def sg_stage_scores(xA, xB, weights: Weights, *, workspace=None) -> torch.Tensor:
+    """The final projection of both images' states xA [M][D], xB [N][D] (fp32)
+    and their bordered score matrix: Z [(M+1)][N+1] (natural log), the real
+    block f_A f_B^T / sqrt(D) and the dustbin row and column holding the
+    network's dustbin score."""
+    M, N, D = xA.shape[0], xB.shape[0], weights.D
+    _check_tensor(xA, "xA", torch.float32, (M, D))
+    _check_tensor(xB, "xB", torch.float32, (N, D))
+    dev = xA.device
+    Z = torch.empty((M + 1, N + 1), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib().sg_stage_scores_workspace_size(M, N, D)))
+    o, keep, _ = _opts(dev, workspace=workspace)
+    _lib.check(lib().sg_stage_scores(_ptr(xA), M, _ptr(xB), N, weights.ref, _ptr(Z), N + 1, C.byref(o)),
+               "sg_stage_scores")
+    return Z
 
 
 def sg_stage_match(fA, fB, alpha: float, T: int, *, threshold: float = 0.0, want_logP=True,

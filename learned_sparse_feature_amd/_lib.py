@@ -64,6 +64,8 @@ SIGNATURES = {
     "sg_stage_gnn": (_I, [_P, _I, _P, _I, _W, _I, _I, _O]),
     "sg_stage_gnn_pos": (_I, [_P, _P, _I, _P, _P, _I, _W, _I, _I, _O]),
     "sg_stage_project": (_I, [_P, _I, _W, _P, _O]),
+    "sg_stage_scores": (_I, [_P, _I, _P, _I, _W, _P, C.c_int64, _O]),
+    "sg_stage_scores_workspace_size": (C.c_size_t, [_I, _I, _I]),
     "sg_stage_match": (_I, [_P, _I, _P, _I, _I, _F, _I, _P, _P, _O]),
     "sg_stage_match_workspace_size": (C.c_size_t, [_I, _I, _I]),
     "sg_stage_match_ds": (_I, [_P, _P, _I, _P, _P, _I, _I, _P, _F, _P, _P, _O]),

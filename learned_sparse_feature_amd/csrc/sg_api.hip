@@ -1403,6 +1403,68 @@ sg_status sg_stage_project(const float* x, int32_t n, const sg_weights* weights,
   return SG_OK;
 }
 
+// Workspace of sg_stage_scores: f_A [M][D], f_B [N][D], S [M][ld4(N)].
+static size_t scores_ws(int32_t M, int32_t N, int32_t D, size_t* oB, size_t* oS) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t a = up((size_t)M * D * 4), b = up((size_t)N * D * 4), c = up((size_t)M * ld4(N) * 4);
+  if (oB) *oB = a;
+  if (oS) *oS = a + b;
+  return std::max<size_t>(a + b + c, 256);
+}
+
+size_t sg_stage_scores_workspace_size(int32_t M, int32_t N, int32_t D) {
+  if (M < 0 || N < 0 || D <= 0) return 0;
+  return scores_ws(M, N, D, nullptr, nullptr);
+}
+
+sg_status sg_stage_scores(const float* xA, int32_t M, const float* xB, int32_t N, const sg_weights* weights,
+                          float* Z, int64_t ldZ, const sg_opts* opts) {
+  g_err.clear();
+  WLayout WL;
+  sg_status s = check_weights(weights, &WL);
+  if (s != SG_OK) return s;
+  if ((s = check_opts(opts)) != SG_OK) return s;
+  if (M < 0 || N < 0) return fail(SG_ERR_INVALID_ARG, "negative point count");
+  if (M > 4096 || N > 4096) return fail(SG_ERR_UNSUPPORTED, "more than 4096 points per image");
+  if (!Z) return fail(SG_ERR_INVALID_ARG, "Z is NULL");
+  if (ldZ < (int64_t)N + 1) return fail(SG_ERR_INVALID_ARG, "ldZ < N+1");
+  if ((M > 0 && !xA) || (N > 0 && !xB)) return fail(SG_ERR_INVALID_ARG, "NULL states");
+  const int D = weights->D;
+  size_t oB, oS;
+  void* wsp;
+  if ((s = get_workspace(opts, scores_ws(M, N, D, &oB, &oS), &wsp)) != SG_OK) return s;
+  char* ws = reinterpret_cast<char*>(wsp);
+  float* FA = reinterpret_cast<float*>(ws);
+  float* FB = reinterpret_cast<float*>(ws + oB);
+  float* S = reinterpret_cast<float*>(ws + oS);
+  hipStream_t st = stream_of(opts);
+  Timer tm{opts, st};
+  const float* alpha_dev = at<float>(weights, WL, WL.alpha);
+  if (M > 0 && N > 0) {
+    Plan pa, pb;
+    pa.R = M;
+    pb.R = N;
+    if ((s = run_project(pa, weights, WL, xA, FA, tm, st)) != SG_OK) return s;
+    if ((s = run_project(pb, weights, WL, xB, FB, tm, st)) != SG_OK) return s;
+    // S = f_A f_B^T / sqrt(D), natural log (the pass keeps it times log2 e)
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.A0 = FA; g.lda0 = D; g.K0 = D; g.K = D;
+    g.W = FB; g.ldw = D;
+    g.C = S; g.C2 = nullptr;
+    g.scale = 1.f / sqrtf((float)D);
+    GemmBatch b;
+    memset(&b, 0, sizeof(b));
+    b.n = 1;
+    b.p[0] = GemmProblem{0, 0, M, N, 0, 0, ld4(N), 0};
+    HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_gemm(SG_F32, 1, SG_F32, 1, EPI_SCORE, g, b, M, N, st); }),
+           "score GEMM");
+  }
+  HIPCHK(launch_stage_border(S, ld4(N), M, N, alpha_dev, Z, ldZ, st), "bordered scores");
+  tm.finish();
+  return SG_OK;
+}
+
 sg_status sg_stage_match(const float* fA, int32_t M, const float* fB, int32_t N, int32_t D, float alpha, int32_t T,
                          int32_t* out_matches, float* out_scores, const sg_opts* opts) {
   g_err.clear();

@@ -188,6 +188,9 @@ hipError_t launch_sink_extract(const float* Z, const PairTable& pt, const float*
 // the corner last) and row (N+1 entries) times `scale`.
 hipError_t launch_stage_couplings(const float* C, int64_t ldc, int M, int N, float scale, float* Z, float* ZT,
                                   float* bcol, float* brow, hipStream_t st);
+// C [(M+1)][ldc] = S [M][lds] bordered by the dustbin score *alpha_dev.
+hipError_t launch_stage_border(const float* S, int lds, int M, int N, const float* alpha_dev, float* C, int64_t ldc,
+                               hipStream_t st);
 // u = ln2 u2, v = ln2 v2 and (logP non-null) logP = C + u + v + log(M+N).
 hipError_t launch_stage_duals(const float* C, int64_t ldc, int M, int N, const float* u2, const float* v2, float* u,
                               float* v, float* logP, int64_t ldp, hipStream_t st);

@@ -1082,6 +1082,25 @@ __global__ __launch_bounds__(256) void k_stage_duals(const float* __restrict__ C
   if (logP) logP[(int64_t)i * ldp + j] = C[(int64_t)i * ldc + j] + ((ui + vj) + lmn);
 }
 
+// The bordered couplings of the scores stage entry point: the real block S
+// [M][lds] (natural log) copied into C and the dustbin row and column set to
+// the dustbin score, read on the device.  One thread per entry of a row.
+__global__ __launch_bounds__(256) void k_stage_border(const float* __restrict__ S, int lds, int M, int N,
+                                                      const float* __restrict__ alpha_dev, float* __restrict__ C,
+                                                      int64_t ldc) {
+  const int i = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j > N) return;
+  C[(int64_t)i * ldc + j] = (i < M && j < N) ? S[(size_t)i * lds + j] : alpha_dev[0];
+}
+
+hipError_t launch_stage_border(const float* S, int lds, int M, int N, const float* alpha_dev, float* C, int64_t ldc,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(k_stage_border, dim3((N + 1 + 255) / 256, M + 1), dim3(256), 0, st, S, lds, M, N, alpha_dev, C,
+                     ldc);
+  return hipGetLastError();
+}
+
 hipError_t launch_stage_couplings(const float* C, int64_t ldc, int M, int N, float scale, float* Z, float* ZT,
                                   float* bcol, float* brow, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;

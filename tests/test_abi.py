@@ -253,3 +253,21 @@ def test_sinkhorn_and_extract_stages_validate_on_host():
     # the workspace holds Z, its transpose and the per-line vectors
     assert lib.sg_stage_sinkhorn_workspace_size(1024, 1024) >= 2 * 1024 * 1024 * 4
     assert lib.sg_stage_sinkhorn_workspace_size(-1, 3) == 0
+
+
+def test_scores_stage_validates_on_host():
+    """sg_stage_scores refuses bad arguments before any HIP call."""
+    lib = _lib.load()
+    w0 = _cfg()
+    w = _cfg(blob=C.c_void_p(0x1000), nbytes=lib.sg_weights_bytes(C.byref(w0)))
+    f = C.c_void_p(0x1000)
+    I = _lib.SG_ERR_INVALID_ARG
+    assert lib.sg_stage_scores(f, -1, f, 4, C.byref(w), f, 5, None) == I
+    assert lib.sg_stage_scores(f, 3, f, 4, C.byref(w), None, 5, None) == I          # Z NULL
+    assert lib.sg_stage_scores(f, 3, f, 4, C.byref(w), f, 4, None) == I             # ldZ < N+1
+    assert lib.sg_stage_scores(None, 3, f, 4, C.byref(w), f, 5, None) == I          # states NULL
+    assert lib.sg_stage_scores(f, 3, f, 4097, C.byref(w), f, 4098, None) == _lib.SG_ERR_UNSUPPORTED
+    assert lib.sg_stage_scores(f, 3, f, 4, C.byref(w0), f, 5, None) == I            # no blob
+    # f_A, f_B and the unbordered scores
+    assert lib.sg_stage_scores_workspace_size(1024, 1024, 256) >= (2 * 1024 * 256 + 1024 * 1024) * 4
+    assert lib.sg_stage_scores_workspace_size(-1, 3, 256) == 0

@@ -1,5 +1,12 @@
-"""The Sinkhorn and extraction stage entry points (sg_stage_sinkhorn,
-sg_stage_extract) against the oracle, through the C ABI (GPU).
+"""The scores, Sinkhorn and extraction stage entry points (sg_stage_scores,
+sg_stage_sinkhorn, sg_stage_extract) against the oracle, through the C ABI
+(GPU).
+
+sg_stage_scores projects both images' last states and writes the bordered
+score matrix: within 1e-4 of the oracle's final projection and score matrix
+(relative to max |S| where that exceeds 1), the border exactly the dustbin
+score; bf16 networks are compared on states rounded to bf16, the operands the
+GPU's projection reads.
 
 sg_stage_sinkhorn runs the pass's own sweep kernels on caller-given
 couplings: duals u, v and the log assignment within 1e-3 absolute of the
@@ -157,3 +164,56 @@ def test_extract_after_sinkhorn_stage_is_the_pass():
     torch.cuda.synchronize()
     ref = oracle.match_from_descriptors(fA, fB, 1.0, T)
     check_matches(host(e["matches0"]), host(e["matches1"]), ref["logP"], host(m["matches0"]), host(m["matches1"]))
+
+
+def _states(cfg, M, N, seed):
+    return synth.random_states(M, cfg.D, seed=seed), synth.random_states(N, cfg.D, seed=seed + 1)
+
+
+def _oracle_scores(cfg, w, xA, xB):
+    rnd = synth.round_to_bf16 if cfg.dtype == "bf16" else (lambda a: a)
+    M, N = xA.shape[0], xB.shape[0]
+    Z = np.full((M + 1, N + 1), w["alpha"])
+    fA = fB = None
+    if M and N:
+        fA = oracle.final_projection(rnd(xA), w["Wf"], w["bf"])
+        fB = oracle.final_projection(rnd(xB), w["Wf"], w["bf"])
+        Z[:M, :N] = oracle.score_matrix(fA, fB)
+    return Z, fA, fB
+
+
+@pytest.mark.parametrize("cid,M,N", [(0, 10, 12), (1, 300, 257), (2, 1024, 1024), (3, 2048, 1536), (1, 0, 7),
+                                     (1, 5, 0), (2, 1, 33)])
+def test_scores_stage_vs_oracle(cid, M, N):
+    cfg = synth.CONFIGS[cid]
+    w = synth.make_weights(cfg)
+    W = sg.pack_weights(w)
+    xA, xB = _states(cfg, M, N, seed=900 + 7 * M + N)
+    Z = host(sg.sg_stage_scores(dev(xA), dev(xB), W))
+    ref, _, _ = _oracle_scores(cfg, w, xA, xB)
+    assert Z.shape == (M + 1, N + 1)
+    assert (Z[M, :] == np.float32(w["alpha"])).all() and (Z[:, N] == np.float32(w["alpha"])).all()
+    err = np.abs(Z - ref).max()
+    big = np.abs(ref).max()
+    print(f"cfg {cid} {M}x{N}: max |dZ| {err:.2e}, max |Z| {big:.2f}")
+    assert err < 1e-4 * max(1.0, big)
+
+
+def test_stage_chain_scores_sinkhorn_extract():
+    """From the last states through the stage entry points (scores, then
+    Sinkhorn, then extraction) against the oracle's head on the oracle's
+    projection of the same states."""
+    cfg = synth.CONFIGS[1]
+    w = synth.make_weights(cfg)
+    W = sg.pack_weights(w)
+    M, N = 300, 257
+    xA, xB = _states(cfg, M, N, seed=77)
+    Z = sg.sg_stage_scores(dev(xA), dev(xB), W)
+    r = sg.sg_stage_sinkhorn(Z, cfg.T)
+    e = sg.sg_stage_extract(r["logP"])
+    _, fA, fB = _oracle_scores(cfg, w, xA, xB)
+    ref = oracle.match_from_descriptors(fA, fB, w["alpha"], cfg.T)
+    err = np.abs(host(r["logP"]) - ref["logP"]).max()
+    print(f"chain {M}x{N}: max |dlogP| {err:.2e}")
+    assert err < 1e-3
+    check_matches(host(e["matches0"]), host(e["matches1"]), ref["logP"], ref["matches0"], ref["matches1"])
