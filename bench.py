@@ -58,6 +58,39 @@ def gemm_launches(cfg, M, N, cross="standard"):
     return out
 
 
+def gemm_bytes(cfg, M, N, label, pairs=1):
+    """Algorithmic HBM bytes of one GEMM-class launch over `pairs` pairs:
+    activations read once and outputs written once per pair, the weights read
+    once per launch (bf16 networks keep q, k, v, the MLP hidden layer and a
+    copy of the residual stream in bf16; the residual stream itself and the
+    final descriptors are fp32)."""
+    R, D = M + N, cfg.D
+    os_ = 2 if cfg.dtype == "bf16" else 4
+    if label == "qkv":
+        return pairs * (R * D * os_ + 3 * R * D * os_) + 3 * D * D * os_
+    if label == "mlp1":
+        return pairs * (2 * R * D * os_ + 2 * R * D * os_) + 4 * D * D * os_
+    if label == "mlp2_residual":
+        return pairs * (2 * R * D * os_ + 2 * R * D * 4 + (R * D * 2 if os_ == 2 else 0)) + 2 * D * D * os_
+    if label == "final_projection":
+        return pairs * (R * D * 4 + R * D * 4) + D * D * os_
+    if label == "merge_fold":
+        return 2 * cfg.L * (2 * D * D + D * D + 2 * D * D) * os_
+    if label == "scores":
+        return pairs * (R * D * 4 + M * N * 4)
+    raise ValueError(label)
+
+
+def own_roofline(flops, nbytes, us):
+    """The launch against its own roofline: the larger of its flops at the
+    bf16 dense peak and its bytes at the HBM peak."""
+    t_mfma = flops / (PEAK["bf16_TFLOPs"] * 1e12) * 1e6
+    t_hbm = nbytes / (PEAK["hbm_GBps"] * 1e9) * 1e6
+    floor = max(t_mfma, t_hbm)
+    return {"bound": "mfma" if t_mfma >= t_hbm else "hbm", "roofline_us": round(floor, 2),
+            "frac_of_roofline": round(floor / us, 4)}
+
+
 def gemm_flops(cfg, M, N, cross="standard"):
     """(operand dtype, flops) of every GEMM-class launch (see gemm_launches)."""
     return [(d, f) for _, d, f in gemm_launches(cfg, M, N, cross)]
@@ -289,15 +322,26 @@ def batch_kernels(args, cfg, sg, np, torch, bstep, B, M, N, ds):
             per = {}
             for (lab, _, f), d in zip(labs, dur_us):
                 per.setdefault(lab, []).append((f * mult(lab), d))
-            r["per_launch_kind"] = {
-                k: {"launches": len(v), "avg_us": round(float(np.mean([d for _, d in v])), 2),
-                    "frac_mfma": round(float(sum(f for f, _ in v) / sum(d for _, d in v) / 1e6 / PEAK["bf16_TFLOPs"]), 4)}
-                for k, v in per.items() if k != "scores"}
+            r["per_launch_kind"] = {}
+            for k, v in per.items():
+                if k == "scores":
+                    continue
+                avg = float(np.mean([d for _, d in v]))
+                fl = float(np.mean([f for f, _ in v]))
+                nb = gemm_bytes(cfg, M, N, k, B)
+                r["per_launch_kind"][k] = {
+                    "launches": len(v), "avg_us": round(avg, 2),
+                    "frac_mfma": round(float(sum(f for f, _ in v) / sum(d for _, d in v) / 1e6 / PEAK["bf16_TFLOPs"]), 4),
+                    "algorithmic_bytes": nb, **own_roofline(fl, nb, avg)}
         elif name == "attention":
             fl = attention_flops(cfg, M, N)
             assert nl == len(fl), ("batched attention launches", nl, len(fl))
             ach = float(sum(fl) * B / dur_us.sum() / 1e6)
             r.update(achieved_TFLOPs=round(ach, 1), frac_mfma=round(ach / PEAK["bf16_TFLOPs"], 4))
+            # q, k, v read and the messages written once per stage
+            nb = 4 * (M + N) * cfg.D * (2 if cfg.dtype == "bf16" else 4) * B
+            r.update(algorithmic_bytes_per_launch=nb,
+                     **own_roofline(float(np.mean(fl)) * B, nb, float(dur_us.mean())))
         elif ds:
             r["kernel"] = "k_ds_stats"
             byt = ds_bytes(M, N, cfg.D)[0] * B

@@ -193,6 +193,23 @@ def test_match_stage_wide_score_range(scale, sched):
 
 
 @pytest.mark.parametrize("sched", SCHEDULES)
+def test_match_stage_network_score_range(sched):
+    """Scores as large as the network's own at 2048 x 1536 (|S| up to ~345):
+    descriptors at scale 4.5, the cfg-3 shape, T = 100, held to the strict
+    1e-3 bar."""
+    M, N = 2048, 1536
+    fA, fB = synth.random_matching_descriptors(M, N, 256, seed=29, scale=4.5)
+    out = sg.sg_stage_match(dev(fA), dev(fB), 1.0, 100, sinkhorn=sched)
+    r = oracle.match_from_descriptors(fA, fB, 1.0, 100)
+    big = np.abs(r["S"]).max()
+    err = np.abs(host(out["logP"]) - r["logP"]).max()
+    print(f"max |S| {big:.0f}, max |logP| {np.abs(r['logP']).max():.0f}, max |dlogP| {err:.2e}")
+    assert big > 300
+    assert err < 1e-3
+    check_matches(host(out["matches0"]), host(out["matches1"]), r["logP"], r["matches0"], r["matches1"])
+
+
+@pytest.mark.parametrize("sched", SCHEDULES)
 def test_match_stage_threshold(sched):
     fA, fB = synth.random_matching_descriptors(300, 280, 256, seed=3, scale=2.0)
     thr = 0.2
