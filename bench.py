@@ -39,16 +39,15 @@ def log(*a):
 
 def gemm_launches(cfg, M, N, cross="standard"):
     """(label, operand dtype, algorithmic flops) of every GEMM-class launch of
-    one pass, in launch order (real rows only): the merge fold of all 2L
-    stages, then per stage the QKV projection, the first MLP layer over
-    [x || a] (merge folded in) and the second with the residual, then the
-    final projection and the scores.  The fold launch is counted with its
-    own work, W1[:, D:] Wm for every stage (2 x 2D x D x D per stage, once per
-    call whatever the number of pairs); the merge projection it removes from
-    every stage (2 (M+N) D^2) is not counted anywhere.  Bidirectional cross
-    stages project qk | v (2D outputs) instead of q | k | v."""
+    one pass, in launch order (real rows only): per stage the QKV projection,
+    the first MLP layer over [x || a] (the merge projection folded in) and the
+    second with the residual, then the final projection and the scores.  The
+    merge fold itself (W1[:, D:] Wm for every stage, weights only) runs in
+    the encoder's launch and is not a GEMM-class launch; the merge projection
+    it removes from every stage (2 (M+N) D^2) is counted nowhere.
+    Bidirectional cross stages project qk | v (2D outputs) instead of q | k | v."""
     R, D, S = M + N, cfg.D, 2 * cfg.L
-    out = [("merge_fold", cfg.dtype, 2.0 * 2 * D * D * D * S)]
+    out = []
     for s in range(S):
         out.append(("qkv", cfg.dtype, 2.0 * R * D * (2 if (s % 2 == 1 and cross == "bidirectional") else 3) * D))
         out.append(("mlp1", cfg.dtype, 2.0 * R * 2 * D * 2 * D))
@@ -74,8 +73,6 @@ def gemm_bytes(cfg, M, N, label, pairs=1):
         return pairs * (2 * R * D * os_ + 2 * R * D * 4 + (R * D * 2 if os_ == 2 else 0)) + 2 * D * D * os_
     if label == "final_projection":
         return pairs * (R * D * 4 + R * D * 4) + D * D * os_
-    if label == "merge_fold":
-        return 2 * cfg.L * (2 * D * D + D * D + 2 * D * D) * os_
     if label == "scores":
         return pairs * (R * D * 4 + M * N * 4)
     raise ValueError(label)
@@ -158,7 +155,7 @@ def pass_flops(cfg, M, N, cross="standard"):
     plain oracle, which forms every merge projection instead of folding it."""
     widths = [3] + list(cfg.enc) + [cfg.D]
     enc = 2.0 * (M + N) * sum(a * b for a, b in zip(widths[:-1], widths[1:]))
-    gemm = sum(f for lab, _, f in gemm_launches(cfg, M, N, cross) if lab != "merge_fold")
+    gemm = sum(f for _, _, f in gemm_launches(cfg, M, N, cross))
     merge = 2.0 * (M + N) * cfg.D * cfg.D * 2 * cfg.L
     return enc + gemm + merge + sum(attention_flops(cfg, M, N))
 
@@ -315,7 +312,7 @@ def batch_kernels(args, cfg, sg, np, torch, bstep, B, M, N, ds):
         if name == "gemm":
             labs = gemm_launches(cfg, M, N, args.cross)
             assert nl == len(labs), ("batched GEMM launches", nl, len(labs))
-            mult = (lambda lab: 1 if lab == "merge_fold" else B)  # the fold runs once per call
+            mult = (lambda lab: B)
             bf = [(f * mult(lab), d) for (lab, dt_, f), d in zip(labs, dur_us) if dt_ == "bf16"]
             ach = float(sum(f for f, _ in bf) / sum(d for _, d in bf) / 1e6)
             r.update(achieved_TFLOPs_bf16=round(ach, 1), frac_mfma=round(ach / PEAK["bf16_TFLOPs"], 4))
@@ -659,12 +656,12 @@ def main():
             kernels["ds_stats"]["traffic"] = None if tr is None else round(tr)
         # The bracketing latency is removed from the other classes' bracketed
         # launch times.  It is measured on the GNN stage, whose 2L attention
-        # and 8L GEMM launches run back to back between two stage events: the
+        # and 6L GEMM launches run back to back between two stage events: the
         # sum of their bracketed times exceeds the stage time by the bracketing
-        # cost of 10L launches.
+        # cost of 8L launches.
         nk = "ds_stats" if ds else "sinkhorn"
-        n_gnn = 8 * cfg.L + 1  # 2L attention launches, the merge fold and 6L GEMMs
-        bracketed_gnn_ms = float(durs["attention"].sum() + durs["gemm"][:6 * cfg.L + 1].sum())
+        n_gnn = 8 * cfg.L  # 2L attention launches and 6L GEMMs
+        bracketed_gnn_ms = float(durs["attention"].sum() + durs["gemm"][:6 * cfg.L].sum())
         over = max(0.0, (bracketed_gnn_ms - stages["gnn"]) * 1e3 / n_gnn)
         # the double-softmax head has a single statistics launch, whose stage
         # time holds the events' own latency: its bracketed time less the

@@ -393,8 +393,12 @@ GemmBatch single(int rows, int n_out, int ldc, int c_off = 0) {
   } while (0)
 
 // Encoder: layer 0 (with normalisation) then GEMM layers; the last adds into X.
+FoldArgs make_fold(const sg_weights* w, const WLayout& L, int c0, int n, char* ws, const WsLayout& wl);
+
+// The encoder; with fold_n > 0 the merge fold of stages [0, fold_n) runs in
+// the same launch (at most kMaxFold stages).
 sg_status run_encoder(const Problem& p, const Plan& pl, const sg_weights* w, const WLayout& L,
-                      char* ws, const WsLayout& wl, Timer& tm, hipStream_t st) {
+                      char* ws, const WsLayout& wl, Timer& tm, hipStream_t st, int fold_n = 0) {
   (void)tm;
   EncArgs e;
   memset(&e, 0, sizeof(e));
@@ -412,7 +416,12 @@ sg_status run_encoder(const Problem& p, const Plan& pl, const sg_weights* w, con
   }
   e.X = reinterpret_cast<float*>(ws + wl.X);
   e.XB = w->dtype == SG_BF16 ? ws + wl.XB : nullptr;
-  HIPCHK(launch_encoder(w->dtype, w->dtype, e, pl.seg, st), "encoder");
+  if (fold_n > 0) {
+    const FoldArgs f = make_fold(w, L, 0, fold_n, ws, wl);
+    HIPCHK(launch_encoder(w->dtype, w->dtype, e, pl.seg, st, &f), "encoder and merge fold");
+  } else {
+    HIPCHK(launch_encoder(w->dtype, w->dtype, e, pl.seg, st), "encoder");
+  }
   return SG_OK;
 }
 
@@ -431,24 +440,30 @@ sg_status run_rope_table(const Problem& p, const Plan& pl, const sg_weights* w, 
 // Folds the merge projection of stages [s0, s1) into their update MLPs'
 // first layers (workspace WF / WFB, indexed by stage).  Every call redoes
 // it, so that weights changed in place between calls take effect.
-sg_status run_fold(const sg_weights* w, const WLayout& L, int s0, int s1, char* ws, const WsLayout& wl, Timer& tm,
-                   hipStream_t st) {
+// The fold arguments of stages [c0, c0 + n), n <= kMaxFold.
+FoldArgs make_fold(const sg_weights* w, const WLayout& L, int c0, int n, char* ws, const WsLayout& wl) {
   const int D = w->D;
   const size_t os = w->dtype == SG_BF16 ? 2 : 4;
+  FoldArgs f;
+  memset(&f, 0, sizeof(f));
+  f.D = D;
+  f.n = n;
+  for (int i = 0; i < f.n; ++i) {
+    const int base = L.stage_first + kPerStage * (c0 + i);
+    f.wm[i] = atv(w, L, base + 2);
+    f.bm[i] = atv(w, L, base + 3);
+    f.w1[i] = atv(w, L, base + 4);
+    f.b1[i] = atv(w, L, base + 5);
+  }
+  f.wf = ws + wl.WF + (size_t)c0 * 4 * D * D * os;
+  f.bf = ws + wl.WFB + (size_t)c0 * 2 * D * os;
+  return f;
+}
+
+sg_status run_fold(const sg_weights* w, const WLayout& L, int s0, int s1, char* ws, const WsLayout& wl, Timer& tm,
+                   hipStream_t st) {
   for (int c0 = s0; c0 < s1; c0 += kMaxFold) {
-    FoldArgs f;
-    memset(&f, 0, sizeof(f));
-    f.D = D;
-    f.n = std::min(kMaxFold, s1 - c0);
-    for (int i = 0; i < f.n; ++i) {
-      const int base = L.stage_first + kPerStage * (c0 + i);
-      f.wm[i] = atv(w, L, base + 2);
-      f.bm[i] = atv(w, L, base + 3);
-      f.w1[i] = atv(w, L, base + 4);
-      f.b1[i] = atv(w, L, base + 5);
-    }
-    f.wf = ws + wl.WF + (size_t)c0 * 4 * D * D * os;
-    f.bf = ws + wl.WFB + (size_t)c0 * 2 * D * os;
+    const FoldArgs f = make_fold(w, L, c0, std::min(kMaxFold, s1 - c0), ws, wl);
     HIPCHK(tm.run(SG_K_GEMM, [&] { return launch_fold_merge(w->dtype, f, st); }), "merge fold");
   }
   return SG_OK;
@@ -939,10 +954,12 @@ sg_status enqueue_full(const Problem& p, const Plan& pl, const WsLayout& wl, cha
   // alpha stays in device memory: the Sinkhorn and logP kernels read it there
   const float* alpha_dev = at<float>(w, L, L.alpha);
   tm.stage(SG_EV_START);
-  if ((s = run_encoder(p, pl, w, L, ws, wl, tm, st)) != SG_OK) return s;
+  // the merge fold of the pass's stages runs beside the encoder, in its launch
+  const int nf = std::min(2 * Lst, kMaxFold);
+  if ((s = run_encoder(p, pl, w, L, ws, wl, tm, st, nf)) != SG_OK) return s;
   if (w->rope && (s = run_rope_table(p, pl, w, L, ws, wl, st)) != SG_OK) return s;
   tm.stage(SG_EV_ENCODED);
-  if ((s = run_fold(w, L, 0, 2 * Lst, ws, wl, tm, st)) != SG_OK) return s;
+  if ((s = run_fold(w, L, nf, 2 * Lst, ws, wl, tm, st)) != SG_OK) return s;
   if ((s = run_gnn(pl, w, L, 0, 2 * Lst, ws, wl, o ? o->flags : 0, tm, st, nullptr, true)) != SG_OK) return s;
   tm.stage(SG_EV_GNN);
   float* F = reinterpret_cast<float*>(ws + wl.F);

@@ -8,19 +8,22 @@
 // into 32-column blocks, so that a 256-wide layer is one block per wave and
 // all of its weight loads are in flight together; weights stream from L2.
 #include "sg_device.h"
+#include "sg_fold.h"
 
 namespace sg {
 
 constexpr int kEncThreads = 512, kEncWaves = kEncThreads / 64;
 
-template <typename OpT, typename WT>
-__global__ __launch_bounds__(kEncThreads) void k_encoder(EncArgs e, SegTable seg) {
-  constexpr bool BF = std::is_same<OpT, bf16>::value;
-  constexpr int PADE = BF ? 8 : 4;
-  constexpr int LDH = kMaxEncWidth + PADE;
-  __shared__ __attribute__((aligned(16))) OpT hbuf[2][32 * LDH];
+template <typename OpT>
+constexpr int enc_ldh() { return kMaxEncWidth + (std::is_same<OpT, bf16>::value ? 8 : 4); }
 
-  int t = blockIdx.x;
+// Tile t (32 points) of the encoder; hbuf: the workgroup's two hidden-layer
+// buffers [2][32 * enc_ldh].
+template <typename OpT, typename WT>
+__device__ __forceinline__ void encoder_tile(const EncArgs& e, const SegTable& seg, int t,
+                                             OpT (*hbuf)[32 * enc_ldh<OpT>()]) {
+  constexpr bool BF = std::is_same<OpT, bf16>::value;
+  constexpr int LDH = enc_ldh<OpT>();
   const int s = find_segment(seg, &t);
   if (s >= seg.n_seg) return;
   const int p0 = t * 32, np = min(32, seg.n[s] - p0);
@@ -129,6 +132,27 @@ __global__ __launch_bounds__(kEncThreads) void k_encoder(EncArgs e, SegTable seg
   }
 }
 
+template <typename OpT, typename WT>
+__global__ __launch_bounds__(kEncThreads) void k_encoder(EncArgs e, SegTable seg) {
+  __shared__ __attribute__((aligned(16))) OpT hbuf[2][32 * enc_ldh<OpT>()];
+  encoder_tile<OpT, WT>(e, seg, blockIdx.x, hbuf);
+}
+
+// The pass's prologue in one launch: workgroups [0, tiles) run the encoder,
+// the others the merge fold of every stage (one fold block per wave), two
+// independent latency-bound kernels that would otherwise run one after the
+// other.
+template <typename OpT, typename WT>
+__global__ __launch_bounds__(kEncThreads) void k_encoder_fold(EncArgs e, SegTable seg, FoldArgs f, int tiles) {
+  __shared__ __attribute__((aligned(16))) OpT hbuf[2][32 * enc_ldh<OpT>()];
+  if ((int)blockIdx.x < tiles) {
+    encoder_tile<OpT, WT>(e, seg, blockIdx.x, hbuf);
+    return;
+  }
+  const int b = ((int)blockIdx.x - tiles) * kEncWaves + wave_id();
+  if (b < fold_blocks(f)) fold_block_linear<WT>(f, b);
+}
+
 // Rotary table of self-attention (section 2.2 of the LightGlue review):
 // for every compact row, (cos, sin) of theta_k = <b_k, p> for k < d_h / 2,
 // with p the point's position normalised as for the encoder; padding rows
@@ -172,20 +196,26 @@ hipError_t launch_rope_table(const EncArgs& e, const SegTable& seg, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_encoder(int op, int wd, const EncArgs& e, const SegTable& seg, hipStream_t st) {
+hipError_t launch_encoder(int op, int wd, const EncArgs& e, const SegTable& seg, hipStream_t st,
+                          const FoldArgs* fold) {
   int tiles = 0;
   for (int s = 0; s < seg.n_seg; ++s) tiles += (seg.n[s] + 31) / 32;
-  if (tiles == 0) return hipSuccess;
   for (int l = 1; l < e.n_layers; ++l)
     if (e.width[l] > kMaxEncWidth) return hipErrorInvalidValue;
   for (int l = 1; l < e.n_layers; ++l)
     if (e.width[l] % 16 || e.width[l + 1] % 32) return hipErrorInvalidValue;
-  if (op == SG_BF16 && wd == SG_BF16)
-    hipLaunchKernelGGL((k_encoder<bf16, bf16>), dim3(tiles), dim3(kEncThreads), 0, st, e, seg);
-  else if (op == SG_F32 && wd == SG_F32)
-    hipLaunchKernelGGL((k_encoder<float, float>), dim3(tiles), dim3(kEncThreads), 0, st, e, seg);
-  else
-    return hipErrorInvalidValue;
+  if (op != wd || (op != SG_BF16 && op != SG_F32)) return hipErrorInvalidValue;
+  const bool bf = op == SG_BF16;
+  if (fold && fold->n > 0) {
+    if (fold->n > kMaxFold || fold->D % 32) return hipErrorInvalidValue;
+    const dim3 grid(tiles + (fold_blocks(*fold) + kEncWaves - 1) / kEncWaves);
+    if (bf) hipLaunchKernelGGL((k_encoder_fold<bf16, bf16>), grid, dim3(kEncThreads), 0, st, e, seg, *fold, tiles);
+    else hipLaunchKernelGGL((k_encoder_fold<float, float>), grid, dim3(kEncThreads), 0, st, e, seg, *fold, tiles);
+    return hipGetLastError();
+  }
+  if (tiles == 0) return hipSuccess;
+  if (bf) hipLaunchKernelGGL((k_encoder<bf16, bf16>), dim3(tiles), dim3(kEncThreads), 0, st, e, seg);
+  else hipLaunchKernelGGL((k_encoder<float, float>), dim3(tiles), dim3(kEncThreads), 0, st, e, seg);
   return hipGetLastError();
 }
 

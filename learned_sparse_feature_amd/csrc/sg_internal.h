@@ -119,9 +119,12 @@ struct AttnArgs {
   const int* stop;   // or null: the launch does nothing when *stop != 0 (adaptive depth)
 };
 
-// Host-side launchers (sg_kernels.hip).
+struct FoldArgs;
+
+// Host-side launchers.  The encoder; with `fold` (stages of the merge fold,
+// see FoldArgs) the fold runs in the same launch, beside the encoder tiles.
 hipError_t launch_encoder(int op_dtype, int w_dtype, const EncArgs& e, const SegTable& seg,
-                          hipStream_t st);
+                          hipStream_t st, const FoldArgs* fold = nullptr);
 // (cos, sin) of the rotary angles of every compact row ([R][dh/2]) from the
 // positions in e.kpts / e.img (normalised as for the encoder); ind (or
 // null): the caller's point index of every row, -1 on padding.
