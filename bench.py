@@ -541,7 +541,7 @@ def main():
         return
     if args.gpus != 1:
         log(f"bench.py runs on one GPU only: the matching pass is measured on a single MI355X "
-            f"(pairs are independent; see the sharding note of the design). --gpus {args.gpus} refused.")
+            f"(pairs are independent: several GPUs would each match their own share of the pairs). --gpus {args.gpus} refused.")
         sys.exit(2)
 
     import numpy as np
