@@ -524,6 +524,9 @@ def main():
     ap.add_argument("--cross", choices=["standard", "bidirectional"], default="standard",
                     help="cross-attention of the odd stages")
     ap.add_argument("--rope", action="store_true", help="rotary position encoding in self-attention")
+    ap.add_argument("--shared-similarity", action="store_true",
+                    help="(--cross bidirectional) each cross stage forms its similarity once for both directions; "
+                         "the single-pair line only (no batch, no per-kernel timing)")
     ap.add_argument("--adaptive", action="store_true",
                     help="also time adaptive depth / width (forced exits and pruning) with the double-softmax head")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration context timings")
@@ -543,6 +546,11 @@ def main():
         log(f"bench.py runs on one GPU only: the matching pass is measured on a single MI355X "
             f"(pairs are independent: several GPUs would each match their own share of the pairs). --gpus {args.gpus} refused.")
         sys.exit(2)
+    if args.shared_similarity:
+        if args.cross != "bidirectional":
+            log("--shared-similarity needs --cross bidirectional")
+            sys.exit(2)
+        args.batch, args.no_kernel_timing = 0, True
 
     import numpy as np
     import torch
@@ -579,7 +587,8 @@ def main():
             "scores0": torch.empty(M, dtype=torch.float32, device=dev)}
 
     def step(**kw):
-        return sg.sg_match(*t, W, cfg.L, cfg.T, image_size=img, workspace=ws, out=bufs, sinkhorn=args.sinkhorn, **kw)
+        return sg.sg_match(*t, W, cfg.L, cfg.T, image_size=img, workspace=ws, out=bufs, sinkhorn=args.sinkhorn,
+                           shared_similarity=args.shared_similarity, **kw)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -783,7 +792,8 @@ def main():
                                 + "bf16 GNN operands / fp32 accumulation, fp32 scores + "
                                 + ("head" if ds else "Sinkhorn")),
                    "pairs_per_step": 1, "M": M, "N": N, "D": cfg.D, "L": cfg.L, "T": None if ds else cfg.T,
-                   "head": args.head, "cross_attention": args.cross, "rope": args.rope},
+                   "head": args.head, "cross_attention": args.cross, "rope": args.rope,
+                   "shared_similarity": args.shared_similarity},
         "roofline": roofline, "mfma_util_pct": mfma_util, "cpu_baseline": cpu, "latency": latency,
         "stages_ms": stages, "kernels": kernels,
         "batch_throughput": batch, "launch_floor_us": floor,

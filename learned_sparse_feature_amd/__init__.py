@@ -191,9 +191,12 @@ def _transposed_extra(sinkhorn, B, M, N):
 
 def _opts(device, *, threshold=0.0, image_size=None, workspace=None, ws_bytes=0, m1=None, s1=None,
           fA=None, fB=None, logP=None, logP_ld=0, stage_events=None, timed_kernel=SG_K_NONE,
-          kernel_events=None, stream=None, graph=True, sinkhorn="auto", adaptive=None):
+          kernel_events=None, stream=None, graph=True, sinkhorn="auto", adaptive=None,
+          shared_similarity=False):
     o = SgOpts()
     o.flags = (0 if graph else _lib.SG_FLAG_NO_GRAPH) | _SINKHORN_FLAGS[sinkhorn]
+    if shared_similarity:
+        o.flags |= _lib.SG_FLAG_SHARED_SIMILARITY
     if adaptive is not None:
         o.flags |= (_lib.SG_FLAG_EARLY_EXIT if adaptive.get("early_exit", True) else 0)
         o.flags |= (_lib.SG_FLAG_PRUNE if adaptive.get("prune", True) else 0)
@@ -235,14 +238,17 @@ def sg_match(kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int,
              threshold: float = 0.0, image_size=None, want_matches1=True, want_logP=False,
              want_desc=False, workspace=None, stage_events=None, timed_kernel=SG_K_NONE,
              kernel_events=None, stream=None, graph=True, out: Optional[dict] = None,
-             sinkhorn: str = "auto", adaptive: Optional[dict] = None) -> dict:
+             sinkhorn: str = "auto", adaptive: Optional[dict] = None,
+             shared_similarity: bool = False) -> dict:
     """One pair.  kpts [n][2] (pixels if image_size=(wA, hA, wB, hB) is given),
     desc [n][D], conf [n]: float32 CUDA tensors.  Returns device tensors;
     `out` may supply them (same keys) so that repeated calls reuse buffers.
     sinkhorn: "auto", or "two" / "one" to force a Sinkhorn schedule.
     adaptive (adaptive weights only): {"early_exit": bool, "prune": bool,
     "depth_confidence": a, "width_confidence": b, "prune_min": n} (0 = the
-    library's default); adds "exit_layer", "prune0", "prune1" to the result."""
+    library's default); adds "exit_layer", "prune0", "prune1" to the result.
+    shared_similarity (bidirectional weights): each cross stage forms every
+    head's similarity once and both directions read it."""
     dev = descA.device
     M, N, D = kptsA.shape[0], kptsB.shape[0], weights.D
     for t, nm, shp in ((kptsA, "kptsA", (M, 2)), (descA, "descA", (M, D)), (confA, "confA", (M,)),
@@ -274,7 +280,7 @@ def sg_match(kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int,
                            fB=out.get("f1"), logP=out.get("logP"), logP_ld=N + 1,
                            stage_events=stage_events, timed_kernel=timed_kernel,
                            kernel_events=kernel_events, stream=stream, graph=graph, sinkhorn=sinkhorn,
-                           adaptive=adaptive)
+                           adaptive=adaptive, shared_similarity=shared_similarity)
     exit_layer = C.c_int32(-1)
     if adaptive is not None:
         out["prune0"] = torch.empty(M, dtype=torch.int32, device=dev)

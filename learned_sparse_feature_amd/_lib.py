@@ -20,6 +20,7 @@ SG_FLAG_SINKHORN_TWO_SWEEP = 2
 SG_FLAG_SINKHORN_ONE_SWEEP = 4
 SG_FLAG_EARLY_EXIT = 8
 SG_FLAG_PRUNE = 16
+SG_FLAG_SHARED_SIMILARITY = 32
 
 STATUS_NAMES = {0: "SG_OK", -1: "SG_ERR_INVALID_ARG", -2: "SG_ERR_UNSUPPORTED", -3: "SG_ERR_WEIGHTS",
                 -4: "SG_ERR_WORKSPACE", -5: "SG_ERR_HIP"}

@@ -155,12 +155,13 @@ sg_status check_weights(const sg_weights* w, WLayout* out) {
 // ---------------------------------------------------------- workspace layout
 
 struct WsLayout {
-  size_t X, XB, QK, VT, KS, VS, MB, HB, WF, WFB, F, Z, ZT, P, PD, P2, PD2, PV, PI, U, V, UD, VD, IDX1, ROPE, ADAPT, total;
+  size_t X, XB, QK, VT, KS, VS, MB, HB, WF, WFB, F, Z, ZT, P, PD, P2, PD2, PV, PI, U, V, UD, VD, IDX1, ROPE, ADAPT, SS,
+      SS_bytes, total;
   int ldvt, ldqk;
 };
 
 WsLayout ws_layout_raw(long D, size_t os, long R, long zf, long ztf, long pf, long pd, long uf, long vf,
-                       long nb, long ropef = 0, bool adaptive = false, long nstage = 0) {
+                       long nb, long ropef = 0, bool adaptive = false, long nstage = 0, long ssf = 0) {
   WsLayout L;
   // row strides are kept off powers of two (+64 / +16 bytes) so that the
   // strided accesses of the attention kernel spread over the L2 channels
@@ -201,13 +202,26 @@ WsLayout ws_layout_raw(long D, size_t os, long R, long zf, long ztf, long pf, lo
   // adaptive calls: 10 per-row int / float arrays, the stop flag and the
   // exit head's (M+1) x (N+1) log assignment (at most zf + R + 1 floats)
   L.ADAPT = take(adaptive ? (size_t)(10 * R + 128 + zf + R + 1) * 4 : 0);
+  // the shared similarity of a bidirectional cross stage of one pair (every
+  // head's S and S^T, then their rows' log-sum-exp; SG_FLAG_SHARED_SIMILARITY)
+  L.SS_bytes = (size_t)ssf * 4;
+  L.SS = take(L.SS_bytes);
   L.total = o;
   return L;
 }
 
-WsLayout ws_layout(const sg_weights* w, long R, long zf, long ztf, long pf, long pd, long uf, long vf, long nb) {
+// Floats of the shared similarity of one M x N pair with H heads (S [H][M][ld4(N)],
+// S^T [H][N][ld4(M)], the rows' log-sum-exp [H][M] and [H][N]), zero unless
+// the network has bidirectional cross stages.
+long shared_sim_floats(const sg_weights* w, long M, long N) {
+  if (w->cross != SG_CROSS_BIDIRECTIONAL) return 0;
+  return (long)w->H * (M * ld4((int)N) + N * ld4((int)M) + M + N);
+}
+
+WsLayout ws_layout(const sg_weights* w, long R, long zf, long ztf, long pf, long pd, long uf, long vf, long nb,
+                   long ssf = 0) {
   return ws_layout_raw(w->D, w->dtype == SG_BF16 ? 2 : 4, R, zf, ztf, pf, pd, uf, vf, nb,
-                       w->rope ? R * (w->D / w->H / 2) : 0, w->adaptive != 0, 2L * w->L_max);
+                       w->rope ? R * (w->D / w->H / 2) : 0, w->adaptive != 0, 2L * w->L_max, ssf);
 }
 
 // ----------------------------------------------------------- library workspace
@@ -477,7 +491,6 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
                   const WsLayout& wl, int flags, Timer& tm, hipStream_t st, const int* stop = nullptr,
                   bool xb_valid = false) {
   const int D = w->D, op = w->dtype, R = pl.R;
-  (void)flags;
   float* X = reinterpret_cast<float*>(ws + wl.X);
   // bf16 networks read the states as bf16 (the QKV and MLP GEMMs would round
   // them on load anyway); the residual GEMM keeps the copy current
@@ -514,12 +527,51 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
     // multi-head attention: self on even stages, cross on odd stages
     {
       AttnArgs a;
+      memset(&a, 0, sizeof(a));
       a.qk = QK; a.vt = VT; a.ks = ws + wl.KS; a.vs = ws + wl.VS;
       a.out = MB; a.D = D; a.ldvt = wl.ldvt; a.ldqk = wl.ldqk; a.cross = s & 1; a.stop = stop;
       a.heads = w->H;
       const int dh = D / w->H;
       a.scale2 = log2e / sqrtf((float)dh);
-      HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_attention(op, dh, a, pl.seg, w->H, st); }), "attention");
+      const bool shared = (flags & SG_FLAG_SHARED_SIMILARITY) && (s & 1) && w->cross == SG_CROSS_BIDIRECTIONAL &&
+                          pl.seg.n_seg == 2 && wl.SS_bytes > 0;
+      if (shared) {
+        // the similarity of each head formed once, S = qk_A qk_B^T (scaled to
+        // base 2) and its transpose from the same accumulators, then the
+        // rows' log-sum-exp of both, then both images' messages from them
+        const int M = pl.seg.n[0], N = pl.seg.n[1], H = w->H;
+        float* SS = reinterpret_cast<float*>(ws + wl.SS);
+        const long sA = (long)M * ld4(N), sB = (long)N * ld4(M);
+        float* LSE = SS + H * (sA + sB);
+        if (M > 0 && N > 0) {
+          for (int h = 0; h < H; ++h) {
+            GemmArgs g;
+            memset(&g, 0, sizeof(g));
+            g.A0 = static_cast<char*>(QK) + (size_t)h * dh * os; g.lda0 = wl.ldqk; g.K0 = dh; g.K = dh;
+            g.W = g.A0; g.ldw = wl.ldqk;
+            g.C = SS; g.C2 = SS + H * sA; g.scale = a.scale2; g.stop = stop;
+            GemmBatch b;
+            memset(&b, 0, sizeof(b));
+            b.n = 1;
+            b.p[0] = GemmProblem{pl.seg.row0[0], pl.seg.row0[1], M, N, (int)(h * sA), (int)(h * sB), ld4(N), ld4(M)};
+            HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_gemm(op, 0, op, 1, EPI_SCORE, g, b, M, N, st); }),
+                   "shared similarity");
+          }
+          HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_rows_lse(SS, ld4(N), H * M, N, LSE, st); }),
+                 "similarity rows");
+          HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_rows_lse(SS + H * sA, ld4(M), H * N, M, LSE + H * M, st); }),
+                 "similarity columns");
+        }
+        a.sm = SS; a.lse = LSE; a.scale2 = 1.f;
+        a.s_off[0] = 0; a.s_hs[0] = sA; a.s_ld[0] = ld4(N);
+        a.s_off[1] = H * sA; a.s_hs[1] = sB; a.s_ld[1] = ld4(M);
+        a.l_off[0] = 0; a.l_hs[0] = M;
+        a.l_off[1] = H * M; a.l_hs[1] = N;
+        HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_attention_shared(op, dh, a, pl.seg, H, st); }),
+               "attention (shared similarity)");
+      } else {
+        HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_attention(op, dh, a, pl.seg, w->H, st); }), "attention");
+      }
     }
     // h = ReLU(W_1 [x || m] + b_1) with m = W_m a + b_m folded in (run_fold):
     // h = ReLU(W_f [x || a] + b_f), a = the attention output
@@ -938,7 +990,8 @@ sg_status run_full(const Problem& p, const sg_weights* w, const WLayout& L, int 
                    const Outputs& out, const sg_opts* o) {
   Plan pl;
   make_plan(p, pl);
-  WsLayout wl = ws_layout(w, pl.R, pl.zf, pl.ztf, pl.pf, pl.pd, pl.uf, pl.vf, pl.nb);
+  const long ssf = (o && (o->flags & SG_FLAG_SHARED_SIMILARITY) && p.B == 1) ? shared_sim_floats(w, p.M[0], p.N[0]) : 0;
+  WsLayout wl = ws_layout(w, pl.R, pl.zf, pl.ztf, pl.pf, pl.pd, pl.uf, pl.vf, pl.nb, ssf);
   void* wsp = nullptr;
   sg_status s = get_workspace(o, wl.total, &wsp);
   if (s != SG_OK) return s;
@@ -1226,8 +1279,9 @@ size_t sg_workspace_size(const sg_weights* w, int32_t Mmax, int32_t Nmax, int32_
   // column partials: at most ceil((Mmax+1)/4) row blocks per pair
   const long G = (Mmax + 4) / 4;
   const bool ds = w->head == SG_HEAD_DOUBLE_SOFTMAX;  // no column partials
+  // (one pair of a bidirectional network: room for SG_FLAG_SHARED_SIMILARITY)
   WsLayout wl = ws_layout(w, R, B * Mmax * ld4(Nmax), ztf, ds ? 0 : B * G * ld4(Nmax), ds ? 0 : B * G,
-                          B * ld4(Mmax + 1), B * ld4(Nmax + 1), B * Nmax);
+                          B * ld4(Mmax + 1), B * ld4(Nmax + 1), B * Nmax, B == 1 ? shared_sim_floats(w, Mmax, Nmax) : 0);
   return wl.total;
 }
 
@@ -1277,6 +1331,12 @@ sg_status sg_match(const float* kptsA, const float* descA, const float* confA, i
     out.descA = opts->out_desc_A; out.descB = opts->out_desc_B;
     out.logP = opts->out_logP; out.logP_ld = opts->logP_ld; out.logP_stride = 0;
   }
+  if (opts && (opts->flags & SG_FLAG_SHARED_SIMILARITY)) {
+    if (weights->cross != SG_CROSS_BIDIRECTIONAL)
+      return fail(SG_ERR_INVALID_ARG, "a shared similarity needs bidirectional cross-attention weights");
+    if (opts->flags & (SG_FLAG_EARLY_EXIT | SG_FLAG_PRUNE))
+      return fail(SG_ERR_UNSUPPORTED, "a shared similarity is not combined with adaptive depth / width");
+  }
   if (opts && (opts->flags & (SG_FLAG_EARLY_EXIT | SG_FLAG_PRUNE))) {
     if (!weights->adaptive) return fail(SG_ERR_INVALID_ARG, "adaptive flags need adaptive weights");
     return run_adaptive(p, weights, WL, L, out, opts);
@@ -1297,6 +1357,8 @@ sg_status sg_match_batch(int32_t B, int32_t Mpad, int32_t Npad, const int32_t* M
   if (B < 1 || B > SG_MAX_BATCH) return fail(SG_ERR_INVALID_ARG, "B = %d outside [1, %d]", B, SG_MAX_BATCH);
   if (opts && (opts->flags & (SG_FLAG_EARLY_EXIT | SG_FLAG_PRUNE)))
     return fail(SG_ERR_UNSUPPORTED, "adaptive depth / width runs one pair per call (sg_match)");
+  if (opts && (opts->flags & SG_FLAG_SHARED_SIMILARITY))
+    return fail(SG_ERR_UNSUPPORTED, "the shared similarity runs one pair per call (sg_match)");
   if (!M || !N) return fail(SG_ERR_INVALID_ARG, "M/N host arrays are NULL");
   if (Mpad < 0 || Npad < 0 || Mpad > 4096 || Npad > 4096) return fail(SG_ERR_UNSUPPORTED, "Mpad/Npad outside [0, 4096]");
   for (int b = 0; b < B; ++b)

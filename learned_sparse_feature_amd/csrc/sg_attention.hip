@@ -16,9 +16,15 @@
 namespace sg {
 
 // PAIR1: the two segments of a single pair (each the other's partner),
-// whose entries then sit at fixed argument offsets.
-template <typename OpT, int DH, int NW, bool PAIR1>
+// whose entries then sit at fixed argument offsets.  SH (with PAIR1, the
+// bidirectional cross stage with one similarity): the scores are not formed
+// here but read from the similarity a.sm, already scaled to base 2, and every
+// query's normaliser is its row's log-sum-exp a.lse, so the probabilities are
+// exp2(s - lse) with no running maximum; the wave merge then sums outputs
+// whose weights already total one.
+template <typename OpT, int DH, int NW, bool PAIR1, bool SH = false>
 __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg) {
+  static_assert(!SH || PAIR1, "the shared similarity is laid out for one pair");
   if constexpr (PAIR1)
     args_in_sgprs(a.qk, a.vt, a.ks, a.vs, a.D, a.ldqk, a.ldvt, a.cross, a.heads, a.scale2, a.stop, seg.n[0],
                   seg.n[1], seg.row0[0], seg.row0[1]);
@@ -35,11 +41,13 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
   const int H = a.heads;
   int t = blockIdx.x / H;
   int nq, qrow0, nk, krow0;
+  int sgi = 0;  // (SH) the query image: 0 = A, 1 = B
   if constexpr (PAIR1) {
     const int n0 = seg.n[0], n1 = seg.n[1], nt0 = (n0 + 31) >> 5;
     if (t >= nt0 + ((n1 + 31) >> 5)) return;
     const bool s1 = t >= nt0;
     if (s1) t -= nt0;
+    if constexpr (SH) sgi = s1 ? 1 : 0;
     const bool k1 = a.cross ? !s1 : s1;
     nq = s1 ? n1 : n0;
     qrow0 = s1 ? seg.row0[1] : seg.row0[0];
@@ -72,12 +80,21 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
   // Q^T operand, kept in registers for the whole key loop.  bf16: lane half
   // hi holds dims 16 i + 8 hi .. +7; fp32: dims hi*DH/2 + 4 i .. +3.
   KT Qr[QS];
-  {
+  if constexpr (!SH) {
     const OpT* qp = qk + (size_t)(qrow0 + q0 + lq) * ld2 + h * DH;
 #pragma unroll
     for (int i = 0; i < QS; ++i)
       Qr[i] = BF ? *reinterpret_cast<const KT*>(qp + i * 16 + hi * 8)
                  : *reinterpret_cast<const KT*>(qp + hi * (DH / 2) + 4 * i);
+  }
+  // (SH) this lane's similarity row (its query; rows past the image read the
+  // last one and are not stored) and its log-sum-exp
+  const float* srow = nullptr;
+  float lse_q = 0.f;
+  if constexpr (SH) {
+    const int qc = min(q0 + lq, nq - 1);
+    srow = a.sm + a.s_off[sgi] + (size_t)h * a.s_hs[sgi] + (size_t)qc * a.s_ld[sgi];
+    lse_q = a.lse[a.l_off[sgi] + h * a.l_hs[sgi] + qc];
   }
 
   // K / V registers of one 32-key block from key k0.  bf16: the swizzled
@@ -89,16 +106,20 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
   auto load_block = [&](int k0, KT* kr, VT* vr) {
     if constexpr (BF) {
       const size_t tile = (size_t)((krow0 + k0) >> 5);
-      const bf16* kp = reinterpret_cast<const bf16*>(a.ks) + (tile * (D / 16) + h * (DH / 16)) * 512 + lane * 8;
+      if constexpr (!SH) {
+        const bf16* kp = reinterpret_cast<const bf16*>(a.ks) + (tile * (D / 16) + h * (DH / 16)) * 512 + lane * 8;
 #pragma unroll
-      for (int i = 0; i < QS; ++i) kr[i] = *reinterpret_cast<const bf16x8*>(kp + i * 512);
+        for (int i = 0; i < QS; ++i) kr[i] = *reinterpret_cast<const bf16x8*>(kp + i * 512);
+      }
       const bf16* vp = reinterpret_cast<const bf16*>(a.vs) + (tile * (D / 32) + (h * DH) / 32) * 1024 + lane * 8;
 #pragma unroll
       for (int e = 0; e < NV; ++e) vr[e] = *reinterpret_cast<const bf16x8*>(vp + e * 512);
     } else {
-      const OpT* kp = qk + (size_t)(krow0 + k0 + lq) * ld2 + D + h * DH;
+      if constexpr (!SH) {
+        const OpT* kp = qk + (size_t)(krow0 + k0 + lq) * ld2 + D + h * DH;
 #pragma unroll
-      for (int i = 0; i < QS; ++i) kr[i] = *reinterpret_cast<const KT*>(kp + hi * (DH / 2) + 4 * i);
+        for (int i = 0; i < QS; ++i) kr[i] = *reinterpret_cast<const KT*>(kp + hi * (DH / 2) + 4 * i);
+      }
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const int c = cb * 32 + lq;
@@ -120,7 +141,7 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
     for (int kb = 0; kb < KB; ++kb) load_block(32 * min(kt * KB + kb, nkb - 1), kr[kb], vr[kb]);
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = SH ? lse_q : -INFINITY, l_run = 0.f;
   f32x16 O[NCB];
 #pragma unroll
   for (int c = 0; c < NCB; ++c) O[c] = zero16();
@@ -131,7 +152,22 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
     f32x16 S[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) S[kb] = zero16();
-    if constexpr (BF) {
+    if constexpr (SH) {
+      // element i of block kb: key 32 kb + 8 (i / 4) + 4 hi + i % 4 of the
+      // tile, four consecutive keys per 16-byte load (clamped into the row;
+      // keys past the image are masked below)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int key = kt * 32 * KB + 32 * kb + 8 * g4 + 4 * hi;
+          const float4 v = *reinterpret_cast<const float4*>(srow + min(key, ((nk - 1) & ~3)));
+          S[kb][4 * g4] = v.x;
+          S[kb][4 * g4 + 1] = v.y;
+          S[kb][4 * g4 + 2] = v.z;
+          S[kb][4 * g4 + 3] = v.w;
+        }
+    } else if constexpr (BF) {
 #pragma unroll
       for (int i = 0; i < QS; ++i)
 #pragma unroll
@@ -185,9 +221,9 @@ __global__ __launch_bounds__(64 * NW) void k_attention(AttnArgs a, SegTable seg)
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, S[kb][i]);
     tmax = half_swap_max(tmax);
-    const float m_new = fmaxf(m_run, tmax * a.scale2);
+    const float m_new = SH ? m_run : fmaxf(m_run, tmax * a.scale2);
     // rescale the running output only when some query's maximum moved
-    if (__ballot(m_new != m_run)) {
+    if (!SH && __ballot(m_new != m_run)) {
       const float corr = exp2_fast(m_run - m_new);
       l_run *= corr;
 #pragma unroll
@@ -487,6 +523,54 @@ __global__ __launch_bounds__(256, 4) void k_attention_wide(AttnArgs a, SegTable 
         *reinterpret_cast<bf16x4*>(out + cb * 32 + 8 * g + 4 * hi) = o;
       }
   }
+}
+
+// Base-2 log-sum-exp of every row of a row-major [rows][ld] fp32 matrix over
+// its first `cols` entries, one wave per row (the normalisers of the shared
+// similarity's two directions: rows of S for image A, rows of S^T for B).
+__global__ __launch_bounds__(256) void k_rows_lse(const float* __restrict__ S, int ld, int rows, int cols,
+                                                  float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave_id();
+  if (r >= rows) return;
+  const float* row = S + (size_t)r * ld;
+  float mx = -INFINITY;
+  for (int j = lane; j < cols; j += 64) mx = fmaxf(mx, row[j]);
+  mx = wave_max(mx);
+  float sum = 0.f;
+  for (int j = lane; j < cols; j += 64) sum += exp2_fast(row[j] - mx);
+  sum = wave_sum(sum);
+  if (lane == 0) out[r] = mx + log2_fast(sum);
+}
+
+hipError_t launch_rows_lse(const float* S, int ld, int rows, int cols, float* out, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (cols <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_rows_lse, dim3((rows + 3) / 4), dim3(256), 0, st, S, ld, rows, cols, out);
+  return hipGetLastError();
+}
+
+// The messages of a bidirectional cross stage of one pair from its shared
+// similarity (a.sm, a.lse; see AttnArgs): both images' queries in one launch.
+hipError_t launch_attention_shared(int op, int dh, const AttnArgs& a, const SegTable& seg, int heads,
+                                   hipStream_t st) {
+  if (seg.n_seg != 2 || !a.cross || !a.sm || !a.lse) return hipErrorInvalidValue;
+  const int tiles = (seg.n[0] + 31) / 32 + (seg.n[1] + 31) / 32;
+  if (tiles == 0 || seg.n[0] == 0 || seg.n[1] == 0) return hipSuccess;
+  constexpr int NW = 8;
+  dim3 grid(tiles * heads);
+#define SG_ATT(T, DHV) hipLaunchKernelGGL((k_attention<T, DHV, NW, true, true>), grid, dim3(64 * NW), 0, st, a, seg)
+  if (op == SG_BF16) {
+    if (dh == 64) SG_ATT(bf16, 64);
+    else if (dh == 16) SG_ATT(bf16, 16);
+    else return hipErrorInvalidValue;
+  } else {
+    if (dh == 64) SG_ATT(float, 64);
+    else if (dh == 16) SG_ATT(float, 16);
+    else return hipErrorInvalidValue;
+  }
+#undef SG_ATT
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(int op, int dh, const AttnArgs& a, const SegTable& seg, int heads,

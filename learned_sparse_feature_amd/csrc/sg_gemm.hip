@@ -759,6 +759,7 @@ hipError_t launch_gemm(int op, int a0f, int wd, int outf, int epi, const GemmArg
         case EPI_RESID: SG_GO(bf16, bf16, bf16, float, EPI_RESID); break;
         case EPI_QKV: SG_GO(bf16, bf16, bf16, bf16, EPI_QKV); break;
         case EPI_RELU: SG_GO(bf16, bf16, bf16, bf16, EPI_RELU); break;
+        case EPI_SCORE: SG_GO(bf16, bf16, bf16, float, EPI_SCORE); break;  // (a shared similarity)
         default: return hipErrorInvalidValue;
       }
     }

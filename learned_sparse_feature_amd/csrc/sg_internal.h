@@ -117,6 +117,14 @@ struct AttnArgs {
   int D, ldvt, ldqk, cross, heads;
   float scale2;      // log2(e) / sqrt(dh)
   const int* stop;   // or null: the launch does nothing when *stop != 0 (adaptive depth)
+  // shared similarity (bidirectional cross stage of one pair): the queries of
+  // segment g (0: image A, 1: image B) read their base-2 scaled similarity
+  // rows from sm + s_off[g] + h s_hs[g] (row pitch s_ld[g]) and the rows'
+  // base-2 log-sum-exp from lse + l_off[g] + h l_hs[g]
+  const float* sm;
+  const float* lse;
+  long s_off[2], s_hs[2];
+  int s_ld[2], l_off[2], l_hs[2];
 };
 
 struct FoldArgs;
@@ -154,6 +162,12 @@ struct FoldArgs {
 hipError_t launch_fold_merge(int w_dtype, const FoldArgs& f, hipStream_t st);
 hipError_t launch_attention(int op_dtype, int dh, const AttnArgs& a, const SegTable& seg,
                             int heads, hipStream_t st);
+// Base-2 log-sum-exp of each of `rows` rows ([rows][ld], first `cols` entries).
+hipError_t launch_rows_lse(const float* S, int ld, int rows, int cols, float* out, hipStream_t st);
+// A bidirectional cross stage of one pair from its shared similarity
+// (AttnArgs::sm / lse, scale2 = 1): the messages of both images.
+hipError_t launch_attention_shared(int op_dtype, int dh, const AttnArgs& a, const SegTable& seg, int heads,
+                                   hipStream_t st);
 // alpha_dev (device pointer to the dustbin score) overrides alpha2 when non-null.
 // Sinkhorn rows per workgroup (4 or 8) for a batch of pairs.
 int sink_rows_per_block(const int* M, const int* N, int n_pairs);

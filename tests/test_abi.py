@@ -177,6 +177,34 @@ def test_bidirectional_cross_layout_and_validation():
     assert lib.sg_weights_count(C.byref(bad)) == -1
 
 
+def test_shared_similarity_validation_and_workspace():
+    """SG_FLAG_SHARED_SIMILARITY: refused without bidirectional weights, with
+    the adaptive flags and in batches (host validation, before any HIP
+    call); a single pair's workspace holds every head's similarity, its
+    transpose and both rows' log-sum-exp."""
+    lib = _lib.load()
+    fake = C.c_void_p(0x1000)
+    plain = _cfg(blob=fake, nbytes=1 << 30)
+    wb = _cfg(blob=fake, nbytes=1 << 30)
+    wb.cross = _lib.SG_CROSS_BIDIRECTIONAL
+    o = _lib.SgOpts()
+    o.flags = _lib.SG_FLAG_SHARED_SIMILARITY
+    assert _match(lib, plain, opts=C.byref(o)) == _lib.SG_ERR_INVALID_ARG
+    assert "bidirectional" in lib.sg_last_error().decode()
+    o.flags = _lib.SG_FLAG_SHARED_SIMILARITY | _lib.SG_FLAG_EARLY_EXIT
+    assert _match(lib, wb, opts=C.byref(o)) == _lib.SG_ERR_UNSUPPORTED
+    o.flags = _lib.SG_FLAG_SHARED_SIMILARITY
+    Ms = (C.c_int32 * 1)(8)
+    st = lib.sg_match_batch(1, 8, 8, Ms, Ms, *([fake] * 6), C.byref(wb), 1, 5, fake, fake, C.byref(o))
+    assert st == _lib.SG_ERR_UNSUPPORTED
+    M, N, H = 1000, 777, 4
+    ld4 = lambda n: (n + 3) // 4 * 4
+    extra = 4 * H * (M * ld4(N) + N * ld4(M) + M + N)
+    d1 = lib.sg_workspace_size(C.byref(wb), M, N, 1) - lib.sg_workspace_size(C.byref(plain), M, N, 1)
+    assert extra <= d1 < extra + 1024
+    assert lib.sg_workspace_size(C.byref(wb), M, N, 2) == lib.sg_workspace_size(C.byref(plain), M, N, 2)
+
+
 def test_rope_layout_and_validation():
     """Rotary weights append one fp32 [d_h/2][2] basis; the GNN stage entry
     point refuses them without positions (host validation, before any HIP

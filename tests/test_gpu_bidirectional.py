@@ -7,6 +7,7 @@ Tolerances as for the standard GNN: states within 1e-5 relative per row
 (fp32) / 2e-2 (bf16), log assignments within 1e-3 (fp32, zero biases), match
 indices equal except near ties.
 """
+import dataclasses
 import functools
 
 import numpy as np
@@ -133,3 +134,80 @@ def test_batch_matches_single_pairs():
         agree.append((g["matches0"][i, :M] == s["matches0"]).mean())
     print(f"bidirectional batch vs single: f rel diff {worst:.2e}, match agreement {np.mean(agree):.3f}")
     assert worst < 2e-2 and np.mean(agree) > 0.9
+
+
+# The shared similarity (SG_FLAG_SHARED_SIMILARITY): each cross stage forms
+# every head's similarity once, its transpose and both directions' row
+# normalisers from it; the same bars against the oracle as the default path,
+# and the default path's descriptors to rounding.
+
+def _run_shared(pair, W, cfg, shared):
+    keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
+    img = (*pair["image_size0"], *pair["image_size1"])
+    out = sg.sg_match(*[dev(pair[k]) for k in keys], W, cfg.L, cfg.T, image_size=img, want_logP=True,
+                      want_desc=True, shared_similarity=shared)
+    torch.cuda.synchronize()
+    return {k: host(v) if isinstance(v, torch.Tensor) else v for k, v in out.items()}
+
+
+@pytest.mark.parametrize("cid,head,M,N", [
+    (0, "sinkhorn", None, None),    # d_h = 16
+    (0, "ds", 33, 1),               # one key for A's queries, 33 for B's
+    (1, "sinkhorn", 100, 77),       # ragged tiles in both directions
+    (1, "ds", None, None),
+])
+def test_shared_similarity_fp32(cid, head, M, N):
+    cfg = synth.CONFIGS[cid]
+    w = _weights(cid)  # zero biases: the log-assignment bar of the end-to-end tests
+    pair = synth.make_pair(cfg, M=M, N=N)
+    ref = oracle.double_softmax_match(pair, w) if head == "ds" else oracle.superglue_match(pair, w, T=cfg.T)
+    W = sg.pack_weights(w, head=head)
+    g = _run_shared(pair, W, cfg, True)
+    d = _run_shared(pair, W, cfg, False)
+    e = max(rel_rows(g["f0"], ref["f0"]).max(), rel_rows(g["f1"], ref["f1"]).max())
+    ed = max(rel_rows(g["f0"], d["f0"]).max(), rel_rows(g["f1"], d["f1"]).max())
+    dl = np.abs(g["logP"] - ref["logP"]).max()
+    ex = check_matches(g["matches0"], g["matches1"], ref["logP"], ref["matches0"], ref["matches1"])
+    print(f"cfg{cid} {head} {g['f0'].shape[0]}x{g['f1'].shape[0]} shared: f rel err {e:.2e} (vs default {ed:.2e}), "
+          f"|dlogP| {dl:.2e}, exempt {ex}")
+    assert e < 1e-4 and ed < 1e-4 and dl < 1e-3
+
+
+@pytest.mark.parametrize("cid,M,N", [(2, None, None), (2, 300, 45), (2, 68, 2000), (0, 40, 70)])
+def test_shared_similarity_bf16(cid, M, N):
+    # (configuration 0 with bf16 operands: d_h = 16)
+    cfg = synth.CONFIGS[cid] if cid == 2 else dataclasses.replace(synth.CONFIGS[cid], dtype="bf16")
+    w = synth.make_weights(cfg, cross="bidirectional")
+    pair = synth.make_pair(cfg, M=M, N=N)
+    ref = oracle.superglue_descriptors(pair, w)
+    W = sg.pack_weights(w)
+    g = _run_shared(pair, W, cfg, True)
+    d = _run_shared(pair, W, cfg, False)
+    e = max(rel_rows(g["f0"], ref["f0"]).max(), rel_rows(g["f1"], ref["f1"]).max())
+    ed = max(rel_rows(g["f0"], d["f0"]).max(), rel_rows(g["f1"], d["f1"]).max())
+    agree = (g["matches0"] == d["matches0"]).mean()
+    print(f"cfg{cid} {g['f0'].shape[0]}x{g['f1'].shape[0]} shared bf16: f rel err {e:.2e} (vs default {ed:.2e}), "
+          f"match agreement with the default {agree:.3f}")
+    assert e < 2e-2 and ed < 2e-2 and agree > 0.9
+
+
+def test_shared_similarity_repeats_and_slices():
+    """Graph replays of the shared mode give the eager result; the mode's
+    flag leaves networks without bidirectional stages refused."""
+    cfg = synth.CONFIGS[1]
+    w = _weights(1)
+    W = sg.pack_weights(w)
+    pair = synth.make_pair(cfg, M=200, N=190)
+    keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
+    t = [dev(pair[k]) for k in keys]
+    img = (*pair["image_size0"], *pair["image_size1"])
+    eager = sg.sg_match(*t, W, cfg.L, cfg.T, image_size=img, want_desc=True, graph=False, shared_similarity=True)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        r = sg.sg_match(*t, W, cfg.L, cfg.T, image_size=img, want_desc=True, shared_similarity=True)
+        torch.cuda.synchronize()
+        assert torch.equal(r["f0"], eager["f0"]) and torch.equal(r["f1"], eager["f1"])
+        assert torch.equal(r["matches0"], eager["matches0"])
+    std = sg.pack_weights(synth.make_weights(cfg))
+    with pytest.raises(RuntimeError):
+        sg.sg_match(*t, std, cfg.L, cfg.T, image_size=img, shared_similarity=True)
