@@ -533,8 +533,10 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
       a.heads = w->H;
       const int dh = D / w->H;
       a.scale2 = log2e / sqrtf((float)dh);
+      // (an image with no points: the plain kernel, which gives the other
+      // image's queries zero messages)
       const bool shared = (flags & SG_FLAG_SHARED_SIMILARITY) && (s & 1) && w->cross == SG_CROSS_BIDIRECTIONAL &&
-                          pl.seg.n_seg == 2 && wl.SS_bytes > 0;
+                          pl.seg.n_seg == 2 && wl.SS_bytes > 0 && pl.seg.n[0] > 0 && pl.seg.n[1] > 0;
       if (shared) {
         // the similarity of each head formed once, S = qk_A qk_B^T (scaled to
         // base 2) and its transpose from the same accumulators, then the
@@ -543,25 +545,23 @@ sg_status run_gnn(const Plan& pl, const sg_weights* w, const WLayout& L, int s0,
         float* SS = reinterpret_cast<float*>(ws + wl.SS);
         const long sA = (long)M * ld4(N), sB = (long)N * ld4(M);
         float* LSE = SS + H * (sA + sB);
-        if (M > 0 && N > 0) {
-          for (int h = 0; h < H; ++h) {
-            GemmArgs g;
-            memset(&g, 0, sizeof(g));
-            g.A0 = static_cast<char*>(QK) + (size_t)h * dh * os; g.lda0 = wl.ldqk; g.K0 = dh; g.K = dh;
-            g.W = g.A0; g.ldw = wl.ldqk;
-            g.C = SS; g.C2 = SS + H * sA; g.scale = a.scale2; g.stop = stop;
-            GemmBatch b;
-            memset(&b, 0, sizeof(b));
-            b.n = 1;
-            b.p[0] = GemmProblem{pl.seg.row0[0], pl.seg.row0[1], M, N, (int)(h * sA), (int)(h * sB), ld4(N), ld4(M)};
-            HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_gemm(op, 0, op, 1, EPI_SCORE, g, b, M, N, st); }),
-                   "shared similarity");
-          }
-          HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_rows_lse(SS, ld4(N), H * M, N, LSE, st); }),
-                 "similarity rows");
-          HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_rows_lse(SS + H * sA, ld4(M), H * N, M, LSE + H * M, st); }),
-                 "similarity columns");
+        for (int h = 0; h < H; ++h) {
+          GemmArgs g;
+          memset(&g, 0, sizeof(g));
+          g.A0 = static_cast<char*>(QK) + (size_t)h * dh * os; g.lda0 = wl.ldqk; g.K0 = dh; g.K = dh;
+          g.W = g.A0; g.ldw = wl.ldqk;
+          g.C = SS; g.C2 = SS + H * sA; g.scale = a.scale2; g.stop = stop;
+          GemmBatch b;
+          memset(&b, 0, sizeof(b));
+          b.n = 1;
+          b.p[0] = GemmProblem{pl.seg.row0[0], pl.seg.row0[1], M, N, (int)(h * sA), (int)(h * sB), ld4(N), ld4(M)};
+          HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_gemm(op, 0, op, 1, EPI_SCORE, g, b, M, N, st); }),
+                 "shared similarity");
         }
+        HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_rows_lse(SS, ld4(N), H * M, N, LSE, st); }),
+               "similarity rows");
+        HIPCHK(tm.run(SG_K_ATTENTION, [&] { return launch_rows_lse(SS + H * sA, ld4(M), H * N, M, LSE + H * M, st); }),
+               "similarity columns");
         a.sm = SS; a.lse = LSE; a.scale2 = 1.f;
         a.s_off[0] = 0; a.s_hs[0] = sA; a.s_ld[0] = ld4(N);
         a.s_off[1] = H * sA; a.s_hs[1] = sB; a.s_ld[1] = ld4(M);

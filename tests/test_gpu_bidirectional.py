@@ -211,3 +211,18 @@ def test_shared_similarity_repeats_and_slices():
     std = sg.pack_weights(synth.make_weights(cfg))
     with pytest.raises(RuntimeError):
         sg.sg_match(*t, std, cfg.L, cfg.T, image_size=img, shared_similarity=True)
+
+
+def test_shared_similarity_empty_image():
+    """An image without points: as in the default mode, matches -1 and
+    scores 0, and nothing else is computed (the pass returns early)."""
+    cfg = synth.CONFIGS[0]
+    W = sg.pack_weights(_weights(0, bias_on=True))
+    for M, N in ((0, 7), (6, 0), (0, 0)):
+        p = synth.make_pair(cfg, M=max(M, 1), N=max(N, 1))
+        kA, dA, cA = dev(p["kpts0"][:M]), dev(p["desc0"][:M]), dev(p["conf0"][:M])
+        kB, dB, cB = dev(p["kpts1"][:N]), dev(p["desc1"][:N]), dev(p["conf1"][:N])
+        out = sg.sg_match(kA, dA, cA, kB, dB, cB, W, cfg.L, cfg.T, shared_similarity=True)
+        torch.cuda.synchronize()
+        assert (host(out["matches0"]) == -1).all() and (host(out["scores0"]) == 0).all()
+        assert (host(out["matches1"]) == -1).all() and (host(out["scores1"]) == 0).all()
