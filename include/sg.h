@@ -224,7 +224,7 @@ typedef struct {
  * columns of pruned points are left untouched. */
 #define SG_FLAG_EARLY_EXIT 8
 #define SG_FLAG_PRUNE 16
-/* sg_opts.flags, sg_match with SG_CROSS_BIDIRECTIONAL weights: every cross
+/* sg_opts.flags, sg_match (and sg_stage_gnn) with SG_CROSS_BIDIRECTIONAL weights: every cross
  * stage forms its similarity once per head, sim = qk_A qk_B^T / sqrt(d_h),
  * and takes both directions from it, as section 2.3 of the LightGlue review
  * describes: the similarity and its transpose are written once (fp32), the

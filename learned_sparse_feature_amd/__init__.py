@@ -350,10 +350,11 @@ def sg_stage_encode(kpts, conf, desc, weights: Weights, image_size=(0.0, 0.0), w
 
 
 def sg_stage_gnn(xA, xB, weights: Weights, s0: int, s1: int, workspace=None, timed_kernel=SG_K_NONE,
-                 kernel_events=None, posA=None, posB=None, image_size=None):
+                 kernel_events=None, posA=None, posB=None, image_size=None, shared_similarity=False):
     """Runs stages [s0, s1) in place on float32 states xA [M][D], xB [N][D].
     posA [M][2], posB [N][2]: point positions (rotary self-attention), normalised,
-    or pixels with image_size=(wA, hA, wB, hB)."""
+    or pixels with image_size=(wA, hA, wB, hB).  shared_similarity: as for
+    sg_match (bidirectional weights)."""
     M, N, D = xA.shape[0], xB.shape[0], weights.D
     _check_tensor(xA, "xA", torch.float32, (M, D))
     _check_tensor(xB, "xB", torch.float32, (N, D))
@@ -363,7 +364,8 @@ def sg_stage_gnn(xA, xB, weights: Weights, s0: int, s1: int, workspace=None, tim
     if workspace is None:
         workspace = _workspace(xA.device, workspace_size(weights, M, N, 1))
     o, keep, count = _opts(xA.device, workspace=workspace, timed_kernel=timed_kernel,
-                           kernel_events=kernel_events, image_size=image_size)
+                           kernel_events=kernel_events, image_size=image_size,
+                           shared_similarity=shared_similarity)
     _lib.check(lib().sg_stage_gnn_pos(_ptr(xA), _ptr(posA), M, _ptr(xB), _ptr(posB), N, weights.ref, s0, s1,
                                       C.byref(o)), "sg_stage_gnn_pos")
     return count.value

@@ -1429,6 +1429,9 @@ sg_status sg_stage_gnn_pos(float* xA, const float* posA, int32_t M, float* xB, c
   if ((M && !xA) || (N && !xB)) return fail(SG_ERR_INVALID_ARG, "NULL state pointer");
   if (weights->rope && ((M && !posA) || (N && !posB)))
     return fail(SG_ERR_INVALID_ARG, "rotary self-attention needs the point positions");
+  const bool shared = opts && (opts->flags & SG_FLAG_SHARED_SIMILARITY);
+  if (shared && weights->cross != SG_CROSS_BIDIRECTIONAL)
+    return fail(SG_ERR_INVALID_ARG, "a shared similarity needs bidirectional cross-attention weights");
   Problem p;
   p.flags = opts ? opts->flags : 0;
   p.B = 1; p.Mpad = M; p.Npad = N; p.M = {M}; p.N = {N};
@@ -1436,7 +1439,7 @@ sg_status sg_stage_gnn_pos(float* xA, const float* posA, int32_t M, float* xB, c
   if (opts) memcpy(p.img, opts->image_size, sizeof(p.img));
   Plan pl;
   make_plan(p, pl);
-  WsLayout wl = ws_layout(weights, pl.R, 0, 0, 0, 0, 0, 0, 0);
+  WsLayout wl = ws_layout(weights, pl.R, 0, 0, 0, 0, 0, 0, 0, shared ? shared_sim_floats(weights, M, N) : 0);
   void* wsp;
   if ((s = get_workspace(opts, wl.total, &wsp)) != SG_OK) return s;
   char* ws = reinterpret_cast<char*>(wsp);

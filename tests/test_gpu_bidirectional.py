@@ -141,6 +141,29 @@ def test_batch_matches_single_pairs():
 # normalisers from it; the same bars against the oracle as the default path,
 # and the default path's descriptors to rounding.
 
+@pytest.mark.parametrize("cid,M,N,stages,tol", [
+    (1, 512, 512, (0, 2), 1e-5),
+    (1, 100, 77, (1, 3), 1e-5),
+    (3, 2048, 1536, (1, 2), 1e-5),
+    (2, 1024, 1024, (0, 4), 5e-3),
+    (2, 33, 1, (0, 3), 5e-3),
+])
+def test_shared_similarity_stage_parity(cid, M, N, stages, tol):
+    """GNN stages through the stage entry point with the similarity shared
+    by both directions, against the oracle (the default path's bars)."""
+    cfg = synth.CONFIGS[cid]
+    w = _weights(cid, bias_on=True)
+    W = sg.pack_weights(w)
+    xA = synth.random_states(M, cfg.D, seed=50 + cid)
+    xB = synth.random_states(N, cfg.D, seed=60 + cid)
+    a, b = dev(xA), dev(xB)
+    sg.sg_stage_gnn(a, b, W, *stages, shared_similarity=True)
+    A, B = oracle.attentional_gnn(xA, xB, w["stages"][stages[0]:stages[1]], cfg.H, first_stage=stages[0])
+    ea, eb = rel_rows(host(a), A), rel_rows(host(b), B)
+    print(f"cfg{cid} {M}x{N} stages {stages} shared: max rel err A {ea.max():.2e} B {eb.max():.2e}")
+    assert ea.max() < tol and eb.max() < tol
+
+
 def _run_shared(pair, W, cfg, shared):
     keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
     img = (*pair["image_size0"], *pair["image_size1"])
