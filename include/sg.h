@@ -224,16 +224,17 @@ typedef struct {
  * columns of pruned points are left untouched. */
 #define SG_FLAG_EARLY_EXIT 8
 #define SG_FLAG_PRUNE 16
-/* sg_opts.flags, sg_match (and sg_stage_gnn) with SG_CROSS_BIDIRECTIONAL weights: every cross
- * stage forms its similarity once per head, sim = qk_A qk_B^T / sqrt(d_h),
- * and takes both directions from it, as section 2.3 of the LightGlue review
- * describes: the similarity and its transpose are written once (fp32), the
- * rows' and columns' log-sum-exp taken from them, and each image's messages
- * read them.  The default forms it once per direction inside the attention
- * kernel (the same values up to rounding).  One pair per call: with
- * sg_match_batch, or combined with the adaptive flags, SG_ERR_UNSUPPORTED;
- * other weights: SG_ERR_INVALID_ARG.  Workspace: sg_workspace_size(w, M, N, 1)
- * includes it (H (M N + N M + M + N) floats, rows padded to 4). */
+/* sg_opts.flags, sg_match and sg_stage_gnn with SG_CROSS_BIDIRECTIONAL
+ * weights: every cross stage forms its similarity once per head,
+ * sim = qk_A qk_B^T / sqrt(d_h), and takes both directions from it, as
+ * section 2.3 of the LightGlue review describes: the similarity and its
+ * transpose are written once (fp32), the rows' and columns' log-sum-exp
+ * taken from them, and each image's messages read them.  The default forms
+ * it once per direction inside the attention kernel (the same values up to
+ * rounding).  One pair per call: with sg_match_batch, or combined with the
+ * adaptive flags, SG_ERR_UNSUPPORTED; other weights: SG_ERR_INVALID_ARG.
+ * Workspace: sg_workspace_size(w, M, N, 1) includes it
+ * (H (M N + N M + M + N) floats, rows padded to 4). */
 #define SG_FLAG_SHARED_SIMILARITY 32
 
 /* Number of tensors in the blob (the alpha scalar counts as one). */
