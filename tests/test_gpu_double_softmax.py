@@ -238,13 +238,15 @@ def _run_batch(cfg, W, b):
     return {k: host(v) if isinstance(v, torch.Tensor) else v for k, v in out.items()}
 
 
-def test_batch_fp32_vs_oracle():
-    """A ragged fp32 batch (empty pairs included): every pair against the
-    oracle end to end; padded entries -1 / 0."""
+@pytest.mark.parametrize("batch", [7, sg.SG_MAX_BATCH])
+def test_batch_fp32_vs_oracle(batch):
+    """A ragged fp32 batch (empty pairs included), of 7 pairs and of the
+    largest size the boundary takes: every pair against the oracle end to
+    end; padded entries -1 / 0."""
     cfg = _SMALL_BATCH
     w = synth.make_weights(synth.CONFIGS[0], bias_on=True)
-    b = synth.make_batch(cfg, seed=408)  # pair 0 has N = 0, pair 2 has M = 0
-    assert b["N"][0] == 0 and b["M"][2] == 0
+    b = synth.make_batch(cfg, seed=408, batch=batch)
+    assert len(b["pairs"]) == batch and (b["M"] == 0).any() and (b["N"] == 0).any()
     g = _run_batch(cfg, sg.pack_weights(w, head="ds"), b)
     for i, p in enumerate(b["pairs"]):
         M, N = int(b["M"][i]), int(b["N"][i])

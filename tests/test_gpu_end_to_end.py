@@ -290,6 +290,59 @@ def test_batch_fp32_sinkhorn_vs_oracle(sched):
     assert checked >= 4
 
 
+@pytest.mark.parametrize("sched", ["one", "two"])
+def test_max_batch_fp32_sinkhorn_vs_oracle(sched):
+    """The largest batch the boundary takes (SG_MAX_BATCH = 64 ragged fp32
+    pairs, empty ones among them): every pair against the oracle end to end,
+    so that every entry of the pair table is exercised."""
+    cfg = _SMALL_BATCH
+    w = synth.make_weights(synth.CONFIGS[0], bias_on=True)
+    b = synth.make_batch(cfg, seed=409, batch=sg.SG_MAX_BATCH)
+    assert len(b["pairs"]) == sg.SG_MAX_BATCH and (b["M"] * b["N"] == 0).any()
+    g = _run_batch(cfg, sg.pack_weights(w), b, sinkhorn=sched)
+    worst = 0.0
+    for i, p in enumerate(b["pairs"]):
+        M, N = int(b["M"][i]), int(b["N"][i])
+        assert (g["matches0"][i, M:] == -1).all() and (g["matches1"][i, N:] == -1).all()
+        if M == 0 or N == 0:
+            assert (g["matches0"][i] == -1).all() and (g["matches1"][i] == -1).all()
+            continue
+        ref = oracle.superglue_match(p, w, T=cfg.T)
+        lp = g["logP"][i, :M + 1, :N + 1]
+        dl = np.abs(lp - ref["logP"]).max()
+        assert dl < 1e-3, (i, M, N, dl)
+        check_matches(g["matches0"][i, :M], g["matches1"][i, :N], ref["logP"], ref["matches0"], ref["matches1"])
+        worst = max(worst, dl)
+    print(f"64 pairs ({sched}): |dlogP| up to {worst:.2e}")
+
+
+def test_max_batch_wide_rows_on_gpu_descriptors():
+    """64 bf16 pairs whose rows are just wider than 1024 columns (the fused
+    iteration's widest register layout, 1152 row blocks in one launch): for
+    sampled pairs, the oracle's scores, Sinkhorn and extraction on the batch's
+    own descriptors against its log assignment and matches; and the batch in
+    reverse order gives the same results bitwise, reversed."""
+    cfg = dataclasses.replace(synth.CONFIGS[4], cid=7, pad=1100, n_range=(1025, 1100))
+    w = synth.make_weights(synth.CONFIGS[4])
+    W = sg.pack_weights(w)
+    b = synth.make_batch(cfg, seed=410, batch=sg.SG_MAX_BATCH)
+    g = _run_batch(cfg, W, b)
+    for i in (int(np.argmax(b["M"] * b["N"])), int(np.argmin(b["M"] * b["N"]))):
+        M, N = int(b["M"][i]), int(b["N"][i])
+        ref = oracle.match_from_descriptors(g["f0"][i, :M], g["f1"][i, :N], w["alpha"], cfg.T)
+        lp = g["logP"][i, :M + 1, :N + 1]
+        dl = np.abs(lp - ref["logP"]).max()
+        ex = check_matches(g["matches0"][i, :M], g["matches1"][i, :N], ref["logP"], ref["matches0"],
+                           ref["matches1"])
+        print(f"pair {i} ({M}x{N}): |dlogP| {dl:.2e}, exempt {ex}")
+        assert dl < 1e-3, (i, dl)
+        _column_sums_ok(lp, M, N)
+    order = np.arange(len(b["pairs"]))[::-1].copy()
+    r = _run_batch(cfg, W, _reordered(b, order))
+    for key in ("logP", "matches0", "matches1", "scores0", "scores1"):
+        np.testing.assert_array_equal(r[key], g[key][order], err_msg=key)
+
+
 def _sampled_pairs(b):
     """Smallest, largest and most unequal pairs of a ragged batch, plus the first."""
     M, N = b["M"].astype(int), b["N"].astype(int)
