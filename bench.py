@@ -383,15 +383,31 @@ def latency_percentiles(step, sg, torch, n):
     return {"passes": n, "p10_ms": q(0.1), "p50_ms": q(0.5), "p90_ms": q(0.9)}
 
 
-def per_config(sg, synth, np, torch, dev, reps=10, ids=(0, 1, 3, 4)):
-    """Every configuration's pass (cfg 0-3 one pair per call, cfg 4 its ragged
-    32-pair batch): median wall time per call over graph replays and the stage
-    times of an eager pass with stage events (context beside the headline)."""
+def workload_names(synth, spec):
+    """Workload names from a comma-separated list of names or of positions in
+    synth.WORKLOADS."""
+    table = list(synth.WORKLOADS)
+    out = []
+    for c in (c.strip() for c in spec.split(",")):
+        if not c:
+            continue
+        name = table[int(c)] if c.isdigit() else c
+        if name not in synth.WORKLOADS:
+            raise SystemExit(f"unknown workload {c!r}; one of {table}")
+        out.append(name)
+    return out
+
+
+def per_config(sg, synth, np, torch, dev, names_run, reps=10):
+    """The pass of each named workload (single pairs one per call, the ragged
+    32-pair batch per call): median wall time per call over graph replays and
+    the stage times of an eager pass with stage events (context beside the
+    headline)."""
     keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
     names = ["encoder", "gnn", "projection_scores", "sinkhorn", "extraction"]
     res = {}
-    for cid in ids:
-        cfg = synth.CONFIGS[cid]
+    for wl in names_run:
+        cfg = synth.WORKLOADS[wl]
         w = synth.make_weights(cfg)
         W = sg.pack_weights(w, device=dev)
         if cfg.batch > 1:
@@ -436,18 +452,18 @@ def per_config(sg, synth, np, torch, dev, reps=10, ids=(0, 1, 3, 4)):
             torch.cuda.synchronize()
             acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(sg.SG_N_STAGE_EVENTS - 1)]
         med = float(np.median(ts))
-        res[f"cfg{cid}"] = {"M": int(cfg.M) if pairs == 1 else "U{256..2048}", "N": int(cfg.N) if pairs == 1 else "U{256..2048}",
-                            "pairs_per_call": pairs, "dtype": cfg.dtype, "T": cfg.T, "L": cfg.L,
-                            "ms_per_call_p50": round(med, 4), "pairs_per_s": round(pairs / med * 1e3, 2),
-                            "stages_ms": {n: round(float(v / 3), 4) for n, v in zip(names, acc)}}
+        res[wl] = {"M": int(cfg.M) if pairs == 1 else "U{256..2048}", "N": int(cfg.N) if pairs == 1 else "U{256..2048}",
+                   "pairs_per_call": pairs, "dtype": cfg.dtype, "T": cfg.T, "L": cfg.L,
+                   "ms_per_call_p50": round(med, 4), "pairs_per_s": round(pairs / med * 1e3, 2),
+                   "stages_ms": {n: round(float(v / 3), 4) for n, v in zip(names, acc)}}
         # the Sinkhorn stage against one fused read of the couplings per
         # iteration (the stage's T iterations and its final reduction)
         sk_us = float(acc[names.index("sinkhorn")] / 3) * 1e3
         if cfg.T > 0 and sk_us > 0:
-            res[f"cfg{cid}"]["sinkhorn"] = {"us_per_iteration": round(sk_us / cfg.T, 3),
-                                            "bytes_per_iteration": coupling_bytes,
-                                            "frac_hbm": round(coupling_bytes * cfg.T / (sk_us * 1e-6) / 1e9 / PEAK["hbm_GBps"], 4)}
-        log(f"cfg {cid}: {res[f'cfg{cid}']}")
+            res[wl]["sinkhorn"] = {"us_per_iteration": round(sk_us / cfg.T, 3),
+                                   "bytes_per_iteration": coupling_bytes,
+                                   "frac_hbm": round(coupling_bytes * cfg.T / (sk_us * 1e-6) / 1e9 / PEAK["hbm_GBps"], 4)}
+        log(f"{wl}: {res[wl]}")
     return res
 
 
@@ -530,8 +546,9 @@ def main():
     ap.add_argument("--adaptive", action="store_true",
                     help="also time adaptive depth / width (forced exits and pruning) with the double-softmax head")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration context timings")
-    ap.add_argument("--configs", default="0,1,3,4",
-                    help="comma-separated configuration ids of the per-configuration timings (default 0,1,3,4)")
+    ap.add_argument("--configs", default="pair10x12_f32,pair512_f32,pair2048x1536_f32,ragged32_bf16",
+                    help="comma-separated workloads of the per-configuration timings: names from synth.WORKLOADS, "
+                         "or their positions in it (0-4)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="before the steps, copy this many MiB with a plain device copy (counter scaling)")
     ap.add_argument("--no-launch-floor", action="store_true",
@@ -560,7 +577,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS["pair1024_bf16"]
     w = synth.make_weights(cfg, cross=args.cross, rope=args.rope)
     pair = synth.make_pair(cfg)
     W = sg.pack_weights(w, device=dev, head=args.head)
@@ -772,7 +789,7 @@ def main():
             roofline["avg_launch_over_row_sum_floor"] = round(roofline["avg_launch_us"] / floor["row_sum_4MB_us"], 3)
     configs = None
     if not args.no_configs and args.head == "sinkhorn" and args.cross == "standard" and not args.rope:
-        configs = per_config(sg, synth, np, torch, dev, ids=[int(c) for c in args.configs.split(",") if c.strip()])
+        configs = per_config(sg, synth, np, torch, dev, workload_names(synth, args.configs))
 
     cpu = None
     if not args.no_cpu:

@@ -7,9 +7,9 @@ matching method's arithmetic (no encoder, attention, scores, Sinkhorn or
 extraction); positions stay in pixels, so keypoint normalisation is left to
 each implementation.
 
-Workload shapes follow the five synthetic configurations of the matching
-benchmark (a tiny fp32 pair, the full 512/512 fp32 pair, the 1024/1024 bf16
-pair, the unequal 2048/1536 fp32 pair and the ragged 32-pair bf16 batch).
+Workload shapes (WORKLOADS) are those the matching pass is measured on: a
+tiny fp32 pair, the full 512/512 fp32 pair, the 1024/1024 bf16 pair, the
+unequal 2048/1536 fp32 pair and the ragged 32-pair bf16 batch.
 The pages measure on public benchmarks (MegaDepth-1500 with 2048 features,
 Aachen with up to 4096, HPatches with 1024); the cost of the pass depends only
 on the point counts and the network shape, so these synthetic pairs stand in
@@ -28,8 +28,8 @@ IMAGE_H = 480.0
 
 @dataclass(frozen=True)
 class Config:
-    """Network and workload shape of one synthetic configuration."""
-    cid: int
+    """Network and workload shape of one synthetic workload."""
+    seed_id: int        # offset of the default weight and input seeds
     M: int
     N: int
     D: int
@@ -46,13 +46,20 @@ class Config:
     frac_range: tuple = (0.0, 0.0)   # per-pair planted fraction range
 
 
-CONFIGS = {
-    0: Config(0, 10, 12, 64, 4, 2, (16, 32), 20, "f32"),
-    1: Config(1, 512, 512, 256, 4, 9, (32, 64, 128, 256), 100, "f32"),
-    2: Config(2, 1024, 1024, 256, 4, 9, (32, 64, 128, 256), 100, "bf16", "B", 0.4),
-    3: Config(3, 2048, 1536, 256, 4, 9, (32, 64, 128, 256), 100, "f32", "A", 0.3),
-    4: Config(4, 2048, 2048, 256, 4, 9, (32, 64, 128, 256), 100, "bf16", "pair", 0.0,
-              batch=32, pad=2048, n_range=(256, 2048), frac_range=(0.2, 0.5)),
+# The synthetic workloads, by name: point counts, network (D, H, L, encoder
+# widths), Sinkhorn iterations T and the GNN operand type.
+WORKLOADS = {
+    # 10 x 12 points, D 64, L 2, T 20, fp32: small enough for pure-Python checks
+    "pair10x12_f32": Config(0, 10, 12, 64, 4, 2, (16, 32), 20, "f32"),
+    # 512 x 512 points, D 256, H 4, L 9, T 100, fp32
+    "pair512_f32": Config(1, 512, 512, 256, 4, 9, (32, 64, 128, 256), 100, "f32"),
+    # 1024 x 1024 points, bf16 GNN operands, 40 % of B's points planted
+    "pair1024_bf16": Config(2, 1024, 1024, 256, 4, 9, (32, 64, 128, 256), 100, "bf16", "B", 0.4),
+    # 2048 x 1536 points, fp32, 30 % of A's points planted
+    "pair2048x1536_f32": Config(3, 2048, 1536, 256, 4, 9, (32, 64, 128, 256), 100, "f32", "A", 0.3),
+    # 32 independent pairs, M_b, N_b ~ U{256..2048} padded to 2048, bf16
+    "ragged32_bf16": Config(4, 2048, 2048, 256, 4, 9, (32, 64, 128, 256), 100, "bf16", "pair", 0.0,
+                            batch=32, pad=2048, n_range=(256, 2048), frac_range=(0.2, 0.5)),
 }
 
 WEIGHT_SEED_BASE = 1000
@@ -103,7 +110,7 @@ def make_weights(cfg: Config, seed: Optional[int] = None, bias_on: bool = False,
     every layer but the last (adaptive depth and width).
     """
     if seed is None:
-        seed = (BIAS_ON_SEED_BASE if bias_on else WEIGHT_SEED_BASE) + cfg.cid
+        seed = (BIAS_ON_SEED_BASE if bias_on else WEIGHT_SEED_BASE) + cfg.seed_id
     L = cfg.L if L is None else L
     if cross not in ("standard", "bidirectional"):
         raise ValueError(f"cross = {cross!r}")
@@ -227,7 +234,7 @@ def make_pair(cfg: Config, seed: Optional[int] = None, M: Optional[int] = None,
     copy their descriptors with N(0, 0.1^2) noise, renormalised; B is shuffled.
     """
     if seed is None:
-        seed = INPUT_SEED_BASE + cfg.cid
+        seed = INPUT_SEED_BASE + cfg.seed_id
     rng = np.random.Generator(np.random.PCG64(seed))
     M = cfg.M if M is None else M
     N = cfg.N if N is None else N
@@ -244,7 +251,7 @@ def make_batch(cfg: Config, seed: Optional[int] = None, batch: Optional[int] = N
     """Draw a ragged batch: per pair M_b, N_b ~ U{lo..hi}, planted fraction f ~ U[f_lo, f_hi]
     of min(M_b, N_b); arrays are zero-padded to `cfg.pad` points."""
     if seed is None:
-        seed = INPUT_SEED_BASE + cfg.cid
+        seed = INPUT_SEED_BASE + cfg.seed_id
     B = cfg.batch if batch is None else batch
     rng = np.random.Generator(np.random.PCG64(seed))
     lo, hi = cfg.n_range

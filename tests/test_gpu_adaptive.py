@@ -69,7 +69,7 @@ def _compare(g, r, M, N, logp_tol=1e-3):
 
 
 def test_without_adaptive_flags_equals_the_double_softmax_pass():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = synth.make_weights(cfg, adaptive=True, bias_on=True)
     pair = synth.make_pair(cfg)
     a = _run(pair, sg.pack_weights(w, head="ds"), cfg)
@@ -78,11 +78,11 @@ def test_without_adaptive_flags_equals_the_double_softmax_pass():
         assert np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("cid", [0, 1])
-def test_never_confident_runs_every_layer_bitwise(cid):
+@pytest.mark.parametrize("wl", ["pair10x12_f32", "pair512_f32"])
+def test_never_confident_runs_every_layer_bitwise(wl):
     """Confidence bias -40 (no point ever confident, so none is pruned): the
     adaptive call runs every layer and equals the plain pass bitwise."""
-    cfg = synth.CONFIGS[cid]
+    cfg = synth.WORKLOADS[wl]
     w = copy.deepcopy(synth.make_weights(cfg, adaptive=True, bias_on=True))
     w["conf"] = [(0 * wc, -40.0) for wc, _ in w["conf"]]
     pair = synth.make_pair(cfg)
@@ -94,12 +94,12 @@ def test_never_confident_runs_every_layer_bitwise(cid):
         assert np.array_equal(g[k], p[k]), k
 
 
-@pytest.mark.parametrize("cid,exit_at", [(0, 0), (1, 0), (1, 3)])
-def test_forced_exit(cid, exit_at):
+@pytest.mark.parametrize("wl,exit_at", [("pair10x12_f32", 0), ("pair512_f32", 0), ("pair512_f32", 3)])
+def test_forced_exit(wl, exit_at):
     """Confidence bias -40 before layer `exit_at` and +40 from it on: the
     pass stops after that layer and its own head matches."""
-    cfg = synth.CONFIGS[cid]
-    w = copy.deepcopy(synth.make_weights(cfg, adaptive=True, rope=(cid == 1)))
+    cfg = synth.WORKLOADS[wl]
+    w = copy.deepcopy(synth.make_weights(cfg, adaptive=True, rope=(wl == "pair512_f32")))
     w["conf"] = [(0 * wc, 40.0 if l >= exit_at else -40.0) for l, (wc, _) in enumerate(w["conf"])]
     pair = synth.make_pair(cfg)
     r = oracle.adaptive_match(pair, w, prune=False)
@@ -128,7 +128,7 @@ def _margin_ok(pair, chans, scale=2000.0, margin=0.5):
 
 @pytest.mark.parametrize("M,N,prune_min", [(40, 50, 0), (300, 280, 100), (1500, 1300, 1024)])
 def test_pruning_and_stop_on_crafted_states(M, N, prune_min):
-    cfg = synth.CONFIGS[0] if M < 1000 else synth.CONFIGS[1]
+    cfg = synth.WORKLOADS["pair10x12_f32"] if M < 1000 else synth.WORKLOADS["pair512_f32"]
     w = _crafted(cfg)
     pair = synth.make_pair(cfg, M=M, N=N, seed=M + N)
     r = oracle.adaptive_match(pair, w, depth_confidence=0.97, prune_min=prune_min)
@@ -141,7 +141,7 @@ def test_pruning_and_stop_on_crafted_states(M, N, prune_min):
 def test_stop_ratio_counts_pruned_points_as_confident():
     """The oracle test's construction: layer 1 stops only because the ratio
     divides by the original point count."""
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = _crafted(cfg)
     pair = synth.make_pair(cfg, M=40, N=50)
     x = [pair["desc0"].astype(np.float64), pair["desc1"].astype(np.float64)]
@@ -158,7 +158,7 @@ def test_stop_ratio_counts_pruned_points_as_confident():
 
 
 def test_image_emptied_by_pruning():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = _frozen(cfg)
     w["heads"] = [(h[0], h[1], 0.0 * h[2], -50.0) for h in w["heads"]]   # nothing matchable
     w["conf"] = [(0.0 * c[0], 40.0) for c in w["conf"]]                  # everything confident
@@ -174,7 +174,7 @@ def test_image_emptied_by_pruning():
 def test_bf16_network_crafted_decisions():
     """bf16 weights: the decisions and the bookkeeping on crafted frozen
     states; the exit head against the oracle head on the same states."""
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS["pair1024_bf16"]
     w = _crafted(cfg)
     pair = synth.make_pair(cfg, M=1300, N=1100, seed=5)
     r = oracle.adaptive_match(pair, w, depth_confidence=0.97)

@@ -30,31 +30,31 @@ def _gpu():
 
 
 @functools.lru_cache(maxsize=None)
-def _weights(cid, bias_on=False):
-    return synth.make_weights(synth.CONFIGS[cid], bias_on=bias_on, cross="bidirectional")
+def _weights(wl, bias_on=False):
+    return synth.make_weights(synth.WORKLOADS[wl], bias_on=bias_on, cross="bidirectional")
 
 
-@pytest.mark.parametrize("cid,M,N,stages,tol", [
-    (0, 10, 12, (0, 4), 1e-5),      # D = 64: the shared projection ends at column 64
-    (1, 512, 512, (0, 2), 1e-5),
-    (1, 100, 77, (1, 3), 1e-5),     # a slice that starts at a cross stage
-    (3, 2048, 1536, (0, 2), 1e-5),
-    (2, 1024, 1024, (0, 2), 5e-3),
-    (2, 300, 45, (3, 5), 5e-3),
-    (2, 33, 1, (0, 3), 5e-3),
-    (2, 68, 2000, (5, 8), 5e-3),
+@pytest.mark.parametrize("wl,M,N,stages,tol", [
+    ("pair10x12_f32", 10, 12, (0, 4), 1e-5),  # D = 64: the shared projection ends at column 64
+    ("pair512_f32", 512, 512, (0, 2), 1e-5),
+    ("pair512_f32", 100, 77, (1, 3), 1e-5),  # a slice that starts at a cross stage
+    ("pair2048x1536_f32", 2048, 1536, (0, 2), 1e-5),
+    ("pair1024_bf16", 1024, 1024, (0, 2), 5e-3),
+    ("pair1024_bf16", 300, 45, (3, 5), 5e-3),
+    ("pair1024_bf16", 33, 1, (0, 3), 5e-3),
+    ("pair1024_bf16", 68, 2000, (5, 8), 5e-3),
 ])
-def test_gnn_stage_parity(cid, M, N, stages, tol):
-    cfg = synth.CONFIGS[cid]
-    w = _weights(cid, bias_on=True)
+def test_gnn_stage_parity(wl, M, N, stages, tol):
+    cfg = synth.WORKLOADS[wl]
+    w = _weights(wl, bias_on=True)
     W = sg.pack_weights(w)
-    xA = synth.random_states(M, cfg.D, seed=30 + cid)
-    xB = synth.random_states(N, cfg.D, seed=40 + cid)
+    xA = synth.random_states(M, cfg.D, seed=30 + cfg.seed_id)
+    xB = synth.random_states(N, cfg.D, seed=40 + cfg.seed_id)
     a, b = dev(xA), dev(xB)
     sg.sg_stage_gnn(a, b, W, *stages)
     A, B = oracle.attentional_gnn(xA, xB, w["stages"][stages[0]:stages[1]], cfg.H, first_stage=stages[0])
     ea, eb = rel_rows(host(a), A), rel_rows(host(b), B)
-    print(f"cfg{cid} {M}x{N} stages {stages}: max rel err A {ea.max():.2e} B {eb.max():.2e}")
+    print(f"{wl} {M}x{N} stages {stages}: max rel err A {ea.max():.2e} B {eb.max():.2e}")
     assert ea.max() < tol and eb.max() < tol
 
 
@@ -68,36 +68,36 @@ def _run(pair, W, cfg):
 
 
 @pytest.mark.parametrize("head", ["sinkhorn", "ds"])
-@pytest.mark.parametrize("cid", [0, 1])
-def test_end_to_end_fp32(cid, head):
-    cfg = synth.CONFIGS[cid]
-    w = _weights(cid)
+@pytest.mark.parametrize("wl", ["pair10x12_f32", "pair512_f32"])
+def test_end_to_end_fp32(wl, head):
+    cfg = synth.WORKLOADS[wl]
+    w = _weights(wl)
     pair = synth.make_pair(cfg)
     ref = oracle.double_softmax_match(pair, w) if head == "ds" else oracle.superglue_match(pair, w, T=cfg.T)
     g = _run(pair, sg.pack_weights(w, head=head), cfg)
     e = max(rel_rows(g["f0"], ref["f0"]).max(), rel_rows(g["f1"], ref["f1"]).max())
     dl = np.abs(g["logP"] - ref["logP"]).max()
     ex = check_matches(g["matches0"], g["matches1"], ref["logP"], ref["matches0"], ref["matches1"])
-    print(f"cfg{cid} {head}: f rel err {e:.2e}, |dlogP| {dl:.2e}, matches {int((ref['matches0'] >= 0).sum())}, "
+    print(f"{wl} {head}: f rel err {e:.2e}, |dlogP| {dl:.2e}, matches {int((ref['matches0'] >= 0).sum())}, "
           f"exempt {ex}")
     assert e < 1e-4 and dl < 1e-3
 
 
 def test_end_to_end_bf16_descriptors():
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS["pair1024_bf16"]
     w = _weights(2)
     pair = synth.make_pair(cfg)
     ref = oracle.superglue_descriptors(pair, w)
     g = _run(pair, sg.pack_weights(w), cfg)
     e = max(rel_rows(g["f0"], ref["f0"]).max(), rel_rows(g["f1"], ref["f1"]).max())
-    print(f"cfg2 bidirectional: f rel err {e:.2e}")
+    print(f"pair1024_bf16 bidirectional: f rel err {e:.2e}")
     assert e < 2e-2
 
 
 def test_variant_changes_only_cross_stages():
     """With W_qk = W_q = W_k of a standard network, the bidirectional blob
     gives the standard network's descriptors (same kernels, tied columns)."""
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     std = synth.make_weights(cfg, bias_on=True)
     for s in range(1, len(std["stages"]), 2):
         std["stages"][s]["Wk"] = std["stages"][s]["Wq"].copy()
@@ -116,7 +116,7 @@ def test_variant_changes_only_cross_stages():
 def test_batch_matches_single_pairs():
     """The ragged bf16 batch with bidirectional cross stages: sampled pairs
     agree with sg_match on the unpadded pair to the bf16 descriptor bar."""
-    cfg = synth.CONFIGS[4]
+    cfg = synth.WORKLOADS["ragged32_bf16"]
     w = _weights(4)
     W = sg.pack_weights(w)
     b = synth.make_batch(cfg, batch=12)
@@ -141,26 +141,26 @@ def test_batch_matches_single_pairs():
 # normalisers from it; the same bars against the oracle as the default path,
 # and the default path's descriptors to rounding.
 
-@pytest.mark.parametrize("cid,M,N,stages,tol", [
-    (1, 512, 512, (0, 2), 1e-5),
-    (1, 100, 77, (1, 3), 1e-5),
-    (3, 2048, 1536, (1, 2), 1e-5),
-    (2, 1024, 1024, (0, 4), 5e-3),
-    (2, 33, 1, (0, 3), 5e-3),
+@pytest.mark.parametrize("wl,M,N,stages,tol", [
+    ("pair512_f32", 512, 512, (0, 2), 1e-5),
+    ("pair512_f32", 100, 77, (1, 3), 1e-5),
+    ("pair2048x1536_f32", 2048, 1536, (1, 2), 1e-5),
+    ("pair1024_bf16", 1024, 1024, (0, 4), 5e-3),
+    ("pair1024_bf16", 33, 1, (0, 3), 5e-3),
 ])
-def test_shared_similarity_stage_parity(cid, M, N, stages, tol):
+def test_shared_similarity_stage_parity(wl, M, N, stages, tol):
     """GNN stages through the stage entry point with the similarity shared
     by both directions, against the oracle (the default path's bars)."""
-    cfg = synth.CONFIGS[cid]
-    w = _weights(cid, bias_on=True)
+    cfg = synth.WORKLOADS[wl]
+    w = _weights(wl, bias_on=True)
     W = sg.pack_weights(w)
-    xA = synth.random_states(M, cfg.D, seed=50 + cid)
-    xB = synth.random_states(N, cfg.D, seed=60 + cid)
+    xA = synth.random_states(M, cfg.D, seed=50 + cfg.seed_id)
+    xB = synth.random_states(N, cfg.D, seed=60 + cfg.seed_id)
     a, b = dev(xA), dev(xB)
     sg.sg_stage_gnn(a, b, W, *stages, shared_similarity=True)
     A, B = oracle.attentional_gnn(xA, xB, w["stages"][stages[0]:stages[1]], cfg.H, first_stage=stages[0])
     ea, eb = rel_rows(host(a), A), rel_rows(host(b), B)
-    print(f"cfg{cid} {M}x{N} stages {stages} shared: max rel err A {ea.max():.2e} B {eb.max():.2e}")
+    print(f"{wl} {M}x{N} stages {stages} shared: max rel err A {ea.max():.2e} B {eb.max():.2e}")
     assert ea.max() < tol and eb.max() < tol
 
 
@@ -173,15 +173,15 @@ def _run_shared(pair, W, cfg, shared):
     return {k: host(v) if isinstance(v, torch.Tensor) else v for k, v in out.items()}
 
 
-@pytest.mark.parametrize("cid,head,M,N", [
-    (0, "sinkhorn", None, None),    # d_h = 16
-    (0, "ds", 33, 1),               # one key for A's queries, 33 for B's
-    (1, "sinkhorn", 100, 77),       # ragged tiles in both directions
-    (1, "ds", None, None),
+@pytest.mark.parametrize("wl,head,M,N", [
+    ("pair10x12_f32", "sinkhorn", None, None),  # d_h = 16
+    ("pair10x12_f32", "ds", 33, 1),  # one key for A's queries, 33 for B's
+    ("pair512_f32", "sinkhorn", 100, 77),  # ragged tiles in both directions
+    ("pair512_f32", "ds", None, None),
 ])
-def test_shared_similarity_fp32(cid, head, M, N):
-    cfg = synth.CONFIGS[cid]
-    w = _weights(cid)  # zero biases: the log-assignment bar of the end-to-end tests
+def test_shared_similarity_fp32(wl, head, M, N):
+    cfg = synth.WORKLOADS[wl]
+    w = _weights(wl)  # zero biases: the log-assignment bar of the end-to-end tests
     pair = synth.make_pair(cfg, M=M, N=N)
     ref = oracle.double_softmax_match(pair, w) if head == "ds" else oracle.superglue_match(pair, w, T=cfg.T)
     W = sg.pack_weights(w, head=head)
@@ -191,15 +191,20 @@ def test_shared_similarity_fp32(cid, head, M, N):
     ed = max(rel_rows(g["f0"], d["f0"]).max(), rel_rows(g["f1"], d["f1"]).max())
     dl = np.abs(g["logP"] - ref["logP"]).max()
     ex = check_matches(g["matches0"], g["matches1"], ref["logP"], ref["matches0"], ref["matches1"])
-    print(f"cfg{cid} {head} {g['f0'].shape[0]}x{g['f1'].shape[0]} shared: f rel err {e:.2e} (vs default {ed:.2e}), "
+    print(f"{wl} {head} {g['f0'].shape[0]}x{g['f1'].shape[0]} shared: f rel err {e:.2e} (vs default {ed:.2e}), "
           f"|dlogP| {dl:.2e}, exempt {ex}")
     assert e < 1e-4 and ed < 1e-4 and dl < 1e-3
 
 
-@pytest.mark.parametrize("cid,M,N", [(2, None, None), (2, 300, 45), (2, 68, 2000), (0, 40, 70)])
-def test_shared_similarity_bf16(cid, M, N):
-    # (configuration 0 with bf16 operands: d_h = 16)
-    cfg = synth.CONFIGS[cid] if cid == 2 else dataclasses.replace(synth.CONFIGS[cid], dtype="bf16")
+@pytest.mark.parametrize("wl,M,N", [
+    ("pair1024_bf16", None, None),
+    ("pair1024_bf16", 300, 45),
+    ("pair1024_bf16", 68, 2000),
+    ("pair10x12_f32", 40, 70),
+])
+def test_shared_similarity_bf16(wl, M, N):
+    # (the 10 x 12 workload with bf16 operands: d_h = 16)
+    cfg = synth.WORKLOADS[wl] if wl == "pair1024_bf16" else dataclasses.replace(synth.WORKLOADS[wl], dtype="bf16")
     w = synth.make_weights(cfg, cross="bidirectional")
     pair = synth.make_pair(cfg, M=M, N=N)
     ref = oracle.superglue_descriptors(pair, w)
@@ -209,7 +214,7 @@ def test_shared_similarity_bf16(cid, M, N):
     e = max(rel_rows(g["f0"], ref["f0"]).max(), rel_rows(g["f1"], ref["f1"]).max())
     ed = max(rel_rows(g["f0"], d["f0"]).max(), rel_rows(g["f1"], d["f1"]).max())
     agree = (g["matches0"] == d["matches0"]).mean()
-    print(f"cfg{cid} {g['f0'].shape[0]}x{g['f1'].shape[0]} shared bf16: f rel err {e:.2e} (vs default {ed:.2e}), "
+    print(f"{wl} {g['f0'].shape[0]}x{g['f1'].shape[0]} shared bf16: f rel err {e:.2e} (vs default {ed:.2e}), "
           f"match agreement with the default {agree:.3f}")
     assert e < 2e-2 and ed < 2e-2 and agree > 0.9
 
@@ -217,7 +222,7 @@ def test_shared_similarity_bf16(cid, M, N):
 def test_shared_similarity_repeats_and_slices():
     """Graph replays of the shared mode give the eager result; the mode's
     flag leaves networks without bidirectional stages refused."""
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS["pair512_f32"]
     w = _weights(1)
     W = sg.pack_weights(w)
     pair = synth.make_pair(cfg, M=200, N=190)
@@ -239,7 +244,7 @@ def test_shared_similarity_repeats_and_slices():
 def test_shared_similarity_empty_image():
     """An image without points: as in the default mode, matches -1 and
     scores 0, and nothing else is computed (the pass returns early)."""
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     W = sg.pack_weights(_weights(0, bias_on=True))
     for M, N in ((0, 7), (6, 0), (0, 0)):
         p = synth.make_pair(cfg, M=max(M, 1), N=max(N, 1))

@@ -164,21 +164,27 @@ def _run(pair, W, cfg, **kw):
 
 
 @functools.lru_cache(maxsize=None)
-def _case(cid, bias_on):
-    cfg = synth.CONFIGS[cid]
+def _case(wl, bias_on):
+    cfg = synth.WORKLOADS[wl]
     w = synth.make_weights(cfg, bias_on=bias_on)
     pair = synth.make_pair(cfg)
     return cfg, w, pair, oracle.double_softmax_match(pair, w)
 
 
-@pytest.mark.parametrize("cid,bias_on", [(0, False), (0, True), (1, False), (1, True), (3, False)])
-def test_end_to_end_fp32(cid, bias_on):
-    cfg, w, pair, ref = _case(cid, bias_on)
+@pytest.mark.parametrize("wl,bias_on", [
+    ("pair10x12_f32", False),
+    ("pair10x12_f32", True),
+    ("pair512_f32", False),
+    ("pair512_f32", True),
+    ("pair2048x1536_f32", False),
+])
+def test_end_to_end_fp32(wl, bias_on):
+    cfg, w, pair, ref = _case(wl, bias_on)
     g = _run(pair, sg.pack_weights(w, head="ds"), cfg)
     e = max(rel_rows(g["f0"], ref["f0"]).max(), rel_rows(g["f1"], ref["f1"]).max())
     dl = np.abs(g["logP"] - ref["logP"]).max()
     ex = check_matches(g["matches0"], g["matches1"], ref["logP"], ref["matches0"], ref["matches1"])
-    print(f"cfg{cid} bias={bias_on}: f rel err {e:.2e}, |dlogP| {dl:.2e} (|logP| up to "
+    print(f"{wl} bias={bias_on}: f rel err {e:.2e}, |dlogP| {dl:.2e} (|logP| up to "
           f"{np.abs(ref['logP']).max():.0f}), matches {int((ref['matches0'] >= 0).sum())}, exempt {ex}")
     assert e < 1e-4
     # with zero biases the bar is 1e-3; see _bar_S for the nonzero-bias scores
@@ -189,13 +195,13 @@ def test_end_to_end_fp32(cid, bias_on):
     np.testing.assert_allclose(g["scores0"][ok], ref["scores0"][ok], rtol=2e-3, atol=1e-6)
 
 
-@pytest.mark.parametrize("cid,bias_on", [(2, False), (2, True), (1, True)])
-def test_head_on_gpu_states(cid, bias_on):
+@pytest.mark.parametrize("wl,bias_on", [("pair1024_bf16", False), ("pair1024_bf16", True), ("pair512_f32", True)])
+def test_head_on_gpu_states(wl, bias_on):
     """The head of sg_match against the oracle's head applied to the GPU's own
     last states and descriptors, which the stage entry points reproduce
     bitwise (checked on f): the bf16 network at 1024 x 1024, and the fp32
     network whose nonzero biases grow the scores to thousands."""
-    cfg = synth.CONFIGS[cid]
+    cfg = synth.WORKLOADS[wl]
     w = synth.make_weights(cfg, bias_on=bias_on)
     pair = synth.make_pair(cfg)
     W = sg.pack_weights(w, head="ds")
@@ -210,7 +216,7 @@ def test_head_on_gpu_states(cid, bias_on):
     r = oracle.double_softmax_from_descriptors(g["f0"], g["f1"], host(xs[0]), host(xs[1]), w["wz"], w["bz"])
     dl = np.abs(g["logP"] - r["logP"]).max()
     ex = check_matches(g["matches0"], g["matches1"], r["logP"], r["matches0"], r["matches1"])
-    print(f"cfg{cid} bias={bias_on}: |dlogP| {dl:.2e} (max |S| {np.abs(r['S']).max():.0f}), "
+    print(f"{wl} bias={bias_on}: |dlogP| {dl:.2e} (max |S| {np.abs(r['S']).max():.0f}), "
           f"matches {int((r['matches0'] >= 0).sum())}, exempt {ex}")
     assert dl < _bar_S(r)
 
@@ -225,7 +231,7 @@ def test_heads_share_the_network():
 
 # ------------------------------------------------------------------ batch
 
-_SMALL_BATCH = dataclasses.replace(synth.CONFIGS[0], cid=5, batch=7, pad=40, planted="pair",
+_SMALL_BATCH = dataclasses.replace(synth.WORKLOADS["pair10x12_f32"], seed_id=5, batch=7, pad=40, planted="pair",
                                    n_range=(0, 40), frac_range=(0.2, 0.5))
 
 
@@ -244,7 +250,7 @@ def test_batch_fp32_vs_oracle(batch):
     largest size the boundary takes: every pair against the oracle end to
     end; padded entries -1 / 0."""
     cfg = _SMALL_BATCH
-    w = synth.make_weights(synth.CONFIGS[0], bias_on=True)
+    w = synth.make_weights(synth.WORKLOADS["pair10x12_f32"], bias_on=True)
     b = synth.make_batch(cfg, seed=408, batch=batch)
     assert len(b["pairs"]) == batch and (b["M"] == 0).any() and (b["N"] == 0).any()
     g = _run_batch(cfg, sg.pack_weights(w, head="ds"), b)
@@ -265,7 +271,7 @@ def test_batch_bf16_pairs_independent_and_close_to_single():
     """The 32-pair ragged bf16 batch: reversing the batch reverses the results
     bitwise, and sampled pairs agree with sg_match on the unpadded pair to the
     bf16 descriptor bar."""
-    cfg = synth.CONFIGS[4]
+    cfg = synth.WORKLOADS["ragged32_bf16"]
     w = synth.make_weights(cfg)
     b = synth.make_batch(cfg)
     W = sg.pack_weights(w, head="ds")

@@ -33,8 +33,8 @@ def _gpu():
 
 
 @functools.lru_cache(maxsize=None)
-def _case(cid, bias_on=False):
-    cfg = synth.CONFIGS[cid]
+def _case(wl, bias_on=False):
+    cfg = synth.WORKLOADS[wl]
     w = synth.make_weights(cfg, bias_on=bias_on)
     pair = synth.make_pair(cfg)
     ref = oracle.superglue_match(pair, w, T=cfg.T)
@@ -52,15 +52,21 @@ def _run(pair, W, cfg, threshold=0.0, sinkhorn="auto"):
 
 
 @pytest.mark.parametrize("sched", ["auto", "two", "one"])
-@pytest.mark.parametrize("cid,bias_on", [(0, False), (0, True), (1, False), (1, True), (3, False)])
-def test_end_to_end_fp32(cid, bias_on, sched):
-    cfg, w, pair, ref = _case(cid, bias_on)
+@pytest.mark.parametrize("wl,bias_on", [
+    ("pair10x12_f32", False),
+    ("pair10x12_f32", True),
+    ("pair512_f32", False),
+    ("pair512_f32", True),
+    ("pair2048x1536_f32", False),
+])
+def test_end_to_end_fp32(wl, bias_on, sched):
+    cfg, w, pair, ref = _case(wl, bias_on)
     W = sg.pack_weights(w)
     g = _run(pair, W, cfg, sinkhorn=sched)
     e0, e1 = rel_rows(g["f0"], ref["f0"]).max(), rel_rows(g["f1"], ref["f1"]).max()
     dl = np.abs(g["logP"] - ref["logP"]).max()
     ex = check_matches(g["matches0"], g["matches1"], ref["logP"], ref["matches0"], ref["matches1"])
-    print(f"cfg{cid} bias={bias_on}: f rel err {max(e0, e1):.2e}, |dlogP| {dl:.2e} (|logP| up to "
+    print(f"{wl} bias={bias_on}: f rel err {max(e0, e1):.2e}, |dlogP| {dl:.2e} (|logP| up to "
           f"{np.abs(ref['logP']).max():.0f}), matches {int((ref['matches0'] >= 0).sum())}, exempt {ex}")
     assert max(e0, e1) < 1e-4
     # The configurations (zero biases) keep |logP| within a few hundred and are
@@ -81,7 +87,7 @@ def test_end_to_end_bf16_descriptors(bias_on):
     g = _run(pair, W, cfg)
     e = max(rel_rows(g["f0"], ref["f0"]).max(), rel_rows(g["f1"], ref["f1"]).max())
     agree = float((g["matches0"] == ref["matches0"]).mean())
-    print(f"cfg2 bias={bias_on}: f rel err {e:.2e}; end-to-end match agreement {agree:.3f}")
+    print(f"pair1024_bf16 bias={bias_on}: f rel err {e:.2e}; end-to-end match agreement {agree:.3f}")
     assert e < 2e-2
 
 
@@ -95,7 +101,7 @@ def test_matches_point_into_the_other_image():
 
 
 def test_empty_images():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     W = sg.pack_weights(synth.make_weights(cfg))
     for M, N in ((0, 5), (4, 0), (0, 0)):
         p = synth.make_pair(cfg, M=max(M, 1), N=max(N, 1))
@@ -108,7 +114,7 @@ def test_empty_images():
 
 
 def test_single_point_images():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = synth.make_weights(cfg, bias_on=True)
     p = synth.make_pair(cfg, M=1, N=1)
     ref = oracle.superglue_match(p, w, T=cfg.T)
@@ -128,7 +134,7 @@ def test_graph_replay_equals_eager():
     """Identical repeated calls are captured into a HIP graph and replayed;
     every replay equals the eager result bitwise, with other eager work and
     synchronisations in between."""
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS["pair1024_bf16"]
     w = synth.make_weights(cfg)
     W = sg.pack_weights(w)
     pair = synth.make_pair(cfg)
@@ -155,7 +161,7 @@ def test_graph_replay_equals_eager():
 
 @functools.lru_cache(maxsize=None)
 def _batch(batch=32):
-    cfg = synth.CONFIGS[4]
+    cfg = synth.WORKLOADS["ragged32_bf16"]
     w = synth.make_weights(cfg)
     b = synth.make_batch(cfg, batch=batch)
     return cfg, w, b
@@ -247,7 +253,7 @@ def test_batch_sampled_pairs_vs_oracle(pair_index):
 
 # ------------------------------------------- batch Sinkhorn head vs the oracle
 
-_SMALL_BATCH = dataclasses.replace(synth.CONFIGS[0], cid=5, batch=7, pad=40, planted="pair",
+_SMALL_BATCH = dataclasses.replace(synth.WORKLOADS["pair10x12_f32"], seed_id=5, batch=7, pad=40, planted="pair",
                                    n_range=(0, 40), frac_range=(0.2, 0.5))
 
 
@@ -266,7 +272,7 @@ def test_batch_fp32_sinkhorn_vs_oracle(sched):
     each pair's true M_b, N_b inside the padded buffers); padded entries
     -1 / 0."""
     cfg = _SMALL_BATCH
-    w = synth.make_weights(synth.CONFIGS[0], bias_on=True)
+    w = synth.make_weights(synth.WORKLOADS["pair10x12_f32"], bias_on=True)
     b = synth.make_batch(cfg, seed=408)  # pair 0 has N = 0, pair 2 has M = 0
     assert b["N"][0] == 0 and b["M"][2] == 0
     g = _run_batch(cfg, sg.pack_weights(w), b, sinkhorn=sched)
@@ -296,7 +302,7 @@ def test_max_batch_fp32_sinkhorn_vs_oracle(sched):
     pairs, empty ones among them): every pair against the oracle end to end,
     so that every entry of the pair table is exercised."""
     cfg = _SMALL_BATCH
-    w = synth.make_weights(synth.CONFIGS[0], bias_on=True)
+    w = synth.make_weights(synth.WORKLOADS["pair10x12_f32"], bias_on=True)
     b = synth.make_batch(cfg, seed=409, batch=sg.SG_MAX_BATCH)
     assert len(b["pairs"]) == sg.SG_MAX_BATCH and (b["M"] * b["N"] == 0).any()
     g = _run_batch(cfg, sg.pack_weights(w), b, sinkhorn=sched)
@@ -322,8 +328,8 @@ def test_max_batch_wide_rows_on_gpu_descriptors():
     sampled pairs, the oracle's scores, Sinkhorn and extraction on the batch's
     own descriptors against its log assignment and matches; and the batch in
     reverse order gives the same results bitwise, reversed."""
-    cfg = dataclasses.replace(synth.CONFIGS[4], cid=7, pad=1100, n_range=(1025, 1100))
-    w = synth.make_weights(synth.CONFIGS[4])
+    cfg = dataclasses.replace(synth.WORKLOADS["ragged32_bf16"], seed_id=7, pad=1100, n_range=(1025, 1100))
+    w = synth.make_weights(synth.WORKLOADS["ragged32_bf16"])
     W = sg.pack_weights(w)
     b = synth.make_batch(cfg, seed=410, batch=sg.SG_MAX_BATCH)
     g = _run_batch(cfg, W, b)
@@ -380,14 +386,14 @@ def test_batch_bf16_sinkhorn_on_gpu_descriptors():
 def test_pair1024_bf16_sinkhorn_on_gpu_descriptors():
     """The 1024 x 1024 bf16 pair: the oracle's scores, Sinkhorn and extraction
     on sg_match's own descriptors f against its log assignment and matches."""
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS["pair1024_bf16"]
     w = synth.make_weights(cfg)
     pair = synth.make_pair(cfg)
     g = _run(pair, sg.pack_weights(w), cfg)
     ref = oracle.match_from_descriptors(g["f0"], g["f1"], w["alpha"], cfg.T)
     dl = np.abs(g["logP"] - ref["logP"]).max()
     ex = check_matches(g["matches0"], g["matches1"], ref["logP"], ref["matches0"], ref["matches1"])
-    print(f"cfg2 on GPU f: |dlogP| {dl:.2e}, matches {int((ref['matches0'] >= 0).sum())}, exempt {ex}")
+    print(f"pair1024_bf16 on GPU f: |dlogP| {dl:.2e}, matches {int((ref['matches0'] >= 0).sum())}, exempt {ex}")
     assert dl < 1e-3
     _column_sums_ok(g["logP"], cfg.M, cfg.N)
     ok = g["matches0"] == ref["matches0"]

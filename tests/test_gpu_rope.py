@@ -30,26 +30,26 @@ def _gpu():
 
 
 @functools.lru_cache(maxsize=None)
-def _weights(cid, bias_on=False, cross="standard"):
-    return synth.make_weights(synth.CONFIGS[cid], bias_on=bias_on, cross=cross, rope=True)
+def _weights(wl, bias_on=False, cross="standard"):
+    return synth.make_weights(synth.WORKLOADS[wl], bias_on=bias_on, cross=cross, rope=True)
 
 
-@pytest.mark.parametrize("cid,M,N,stages,tol", [
-    (0, 10, 12, (0, 4), 1e-5),      # d_h = 16: four rotary pairs per head
-    (1, 512, 512, (0, 2), 1e-5),
-    (1, 100, 77, (1, 4), 1e-5),     # starts at a cross stage
-    (3, 2048, 1536, (0, 1), 1e-5),
-    (2, 1024, 1024, (0, 2), 5e-3),
-    (2, 33, 1, (0, 3), 5e-3),
-    (2, 68, 2000, (6, 9), 5e-3),
+@pytest.mark.parametrize("wl,M,N,stages,tol", [
+    ("pair10x12_f32", 10, 12, (0, 4), 1e-5),  # d_h = 16: four rotary pairs per head
+    ("pair512_f32", 512, 512, (0, 2), 1e-5),
+    ("pair512_f32", 100, 77, (1, 4), 1e-5),  # starts at a cross stage
+    ("pair2048x1536_f32", 2048, 1536, (0, 1), 1e-5),
+    ("pair1024_bf16", 1024, 1024, (0, 2), 5e-3),
+    ("pair1024_bf16", 33, 1, (0, 3), 5e-3),
+    ("pair1024_bf16", 68, 2000, (6, 9), 5e-3),
 ])
-def test_gnn_stage_parity(cid, M, N, stages, tol):
-    cfg = synth.CONFIGS[cid]
-    w = _weights(cid, bias_on=True)
+def test_gnn_stage_parity(wl, M, N, stages, tol):
+    cfg = synth.WORKLOADS[wl]
+    w = _weights(wl, bias_on=True)
     W = sg.pack_weights(w)
-    pair = synth.make_pair(cfg, M=M, N=N, seed=50 + cid)
-    xA = synth.random_states(M, cfg.D, seed=60 + cid)
-    xB = synth.random_states(N, cfg.D, seed=70 + cid)
+    pair = synth.make_pair(cfg, M=M, N=N, seed=50 + cfg.seed_id)
+    xA = synth.random_states(M, cfg.D, seed=60 + cfg.seed_id)
+    xB = synth.random_states(N, cfg.D, seed=70 + cfg.seed_id)
     a, b = dev(xA), dev(xB)
     img = (*pair["image_size0"], *pair["image_size1"])
     sg.sg_stage_gnn(a, b, W, *stages, posA=dev(pair["kpts0"]), posB=dev(pair["kpts1"]), image_size=img)
@@ -57,13 +57,13 @@ def test_gnn_stage_parity(cid, M, N, stages, tol):
                                   w["rope_basis"]) for s in ("0", "1"))
     A, B = oracle.attentional_gnn(xA, xB, w["stages"][stages[0]:stages[1]], cfg.H, first_stage=stages[0], rope=th)
     ea, eb = rel_rows(host(a), A), rel_rows(host(b), B)
-    print(f"cfg{cid} {M}x{N} stages {stages}: max rel err A {ea.max():.2e} B {eb.max():.2e}")
+    print(f"{wl} {M}x{N} stages {stages}: max rel err A {ea.max():.2e} B {eb.max():.2e}")
     assert ea.max() < tol and eb.max() < tol
 
 
 def test_positions_already_normalised():
     """Without an image size the positions are taken as normalised."""
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS["pair512_f32"]
     w = _weights(1)
     W = sg.pack_weights(w)
     pair = synth.make_pair(cfg, M=200, N=150, seed=9)
@@ -86,29 +86,33 @@ def _run(pair, W, cfg):
     return {k: host(v) if isinstance(v, torch.Tensor) else v for k, v in out.items()}
 
 
-@pytest.mark.parametrize("cid,head,cross", [(0, "sinkhorn", "standard"), (1, "sinkhorn", "standard"),
-                                            (1, "ds", "standard"), (1, "ds", "bidirectional")])
-def test_end_to_end_fp32(cid, head, cross):
-    cfg = synth.CONFIGS[cid]
-    w = _weights(cid, cross=cross)
+@pytest.mark.parametrize("wl,head,cross", [
+    ("pair10x12_f32", "sinkhorn", "standard"),
+    ("pair512_f32", "sinkhorn", "standard"),
+    ("pair512_f32", "ds", "standard"),
+    ("pair512_f32", "ds", "bidirectional"),
+])
+def test_end_to_end_fp32(wl, head, cross):
+    cfg = synth.WORKLOADS[wl]
+    w = _weights(wl, cross=cross)
     pair = synth.make_pair(cfg)
     ref = oracle.double_softmax_match(pair, w) if head == "ds" else oracle.superglue_match(pair, w, T=cfg.T)
     g = _run(pair, sg.pack_weights(w, head=head), cfg)
     e = max(rel_rows(g["f0"], ref["f0"]).max(), rel_rows(g["f1"], ref["f1"]).max())
     dl = np.abs(g["logP"] - ref["logP"]).max()
     ex = check_matches(g["matches0"], g["matches1"], ref["logP"], ref["matches0"], ref["matches1"])
-    print(f"cfg{cid} {head} {cross}: f rel err {e:.2e}, |dlogP| {dl:.2e}, exempt {ex}")
+    print(f"{wl} {head} {cross}: f rel err {e:.2e}, |dlogP| {dl:.2e}, exempt {ex}")
     assert e < 1e-4 and dl < 1e-3
 
 
 def test_end_to_end_bf16_descriptors():
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS["pair1024_bf16"]
     w = _weights(2)
     pair = synth.make_pair(cfg)
     ref = oracle.superglue_descriptors(pair, w)
     g = _run(pair, sg.pack_weights(w), cfg)
     e = max(rel_rows(g["f0"], ref["f0"]).max(), rel_rows(g["f1"], ref["f1"]).max())
-    print(f"cfg2 rope: f rel err {e:.2e}")
+    print(f"pair1024_bf16 rope: f rel err {e:.2e}")
     assert e < 2e-2
 
 
@@ -116,7 +120,7 @@ def test_translation_invariance_on_the_gpu():
     """Encoder weights zero: shifting image A's keypoints by a pixel vector
     leaves the descriptors unchanged up to fp32 rounding of the angles; the
     rotary encoding does act (a zero basis changes them)."""
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS["pair512_f32"]
     w = dict(_weights(1, bias_on=True))
     w["enc"] = [(0 * W_, 0 * b) for W_, b in w["enc"]]
     pair = synth.make_pair(cfg)
@@ -131,7 +135,7 @@ def test_translation_invariance_on_the_gpu():
 
 
 def test_batch_matches_single_pairs():
-    cfg = synth.CONFIGS[4]
+    cfg = synth.WORKLOADS["ragged32_bf16"]
     w = _weights(4)
     W = sg.pack_weights(w)
     b = synth.make_batch(cfg, batch=12)

@@ -182,10 +182,17 @@ def _oracle_scores(cfg, w, xA, xB):
     return Z, fA, fB
 
 
-@pytest.mark.parametrize("cid,M,N", [(0, 10, 12), (1, 300, 257), (2, 1024, 1024), (3, 2048, 1536), (1, 0, 7),
-                                     (1, 5, 0), (2, 1, 33)])
-def test_scores_stage_vs_oracle(cid, M, N):
-    cfg = synth.CONFIGS[cid]
+@pytest.mark.parametrize("wl,M,N", [
+    ("pair10x12_f32", 10, 12),
+    ("pair512_f32", 300, 257),
+    ("pair1024_bf16", 1024, 1024),
+    ("pair2048x1536_f32", 2048, 1536),
+    ("pair512_f32", 0, 7),
+    ("pair512_f32", 5, 0),
+    ("pair1024_bf16", 1, 33),
+])
+def test_scores_stage_vs_oracle(wl, M, N):
+    cfg = synth.WORKLOADS[wl]
     w = synth.make_weights(cfg)
     W = sg.pack_weights(w)
     xA, xB = _states(cfg, M, N, seed=900 + 7 * M + N)
@@ -195,7 +202,7 @@ def test_scores_stage_vs_oracle(cid, M, N):
     assert (Z[M, :] == np.float32(w["alpha"])).all() and (Z[:, N] == np.float32(w["alpha"])).all()
     err = np.abs(Z - ref).max()
     big = np.abs(ref).max()
-    print(f"cfg {cid} {M}x{N}: max |dZ| {err:.2e}, max |Z| {big:.2f}")
+    print(f"{wl} {M}x{N}: max |dZ| {err:.2e}, max |Z| {big:.2f}")
     assert err < 1e-4 * max(1.0, big)
 
 
@@ -203,7 +210,7 @@ def test_stage_chain_scores_sinkhorn_extract():
     """From the last states through the stage entry points (scores, then
     Sinkhorn, then extraction) against the oracle's head on the oracle's
     projection of the same states."""
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS["pair512_f32"]
     w = synth.make_weights(cfg)
     W = sg.pack_weights(w)
     M, N = 300, 257

@@ -22,8 +22,8 @@ def _gpu():
     sg.lib()  # fails loudly when libsg.so is missing
 
 
-def _weights(cid, bias_on=False, L=None):
-    return synth.make_weights(synth.CONFIGS[cid], bias_on=bias_on, L=L)
+def _weights(wl, bias_on=False, L=None):
+    return synth.make_weights(synth.WORKLOADS[wl], bias_on=bias_on, L=L)
 
 
 # ------------------------------------------------------- worked example
@@ -43,7 +43,7 @@ def _example_network(dtype):
     Wv = Z.copy(); Wv[0, 0], Wv[0, 1], Wv[1, 1] = 0.5, -0.5, 1.0
     cross = dict(zero, Wq=I, Wk=Wk, Wv=Wv, Wm=I, W1=np.block([[Z, I], [Z, Z]]).astype(np.float32),
                  W2=np.block([I, Z]).astype(np.float32))
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = synth.make_weights(cfg, L=1)
     w["stages"] = [zero, cross]
     w["dtype"] = dtype
@@ -72,10 +72,15 @@ def test_attention_worked_example(dtype, tol):
 
 # ---------------------------------------------------------------- encoder
 
-@pytest.mark.parametrize("cid,n,bias_on", [(0, 10, True), (1, 512, False), (1, 77, True), (2, 1024, True)])
-def test_encoder_parity(cid, n, bias_on):
-    cfg = synth.CONFIGS[cid]
-    w = _weights(cid, bias_on, L=1)
+@pytest.mark.parametrize("wl,n,bias_on", [
+    ("pair10x12_f32", 10, True),
+    ("pair512_f32", 512, False),
+    ("pair512_f32", 77, True),
+    ("pair1024_bf16", 1024, True),
+])
+def test_encoder_parity(wl, n, bias_on):
+    cfg = synth.WORKLOADS[wl]
+    w = _weights(wl, bias_on, L=1)
     W = sg.pack_weights(w)
     pair = synth.make_pair(cfg, M=n, N=4)
     x = host(sg.sg_stage_encode(dev(pair["kpts0"]), dev(pair["conf0"]), dev(pair["desc0"]), W,
@@ -83,7 +88,7 @@ def test_encoder_parity(cid, n, bias_on):
     kn = oracle.normalize_keypoints(pair["kpts0"], *pair["image_size0"])
     want = pair["desc0"].astype(np.float64) + oracle.keypoint_encoder(kn, pair["conf0"], w["enc"])
     err = rel_rows(x, want).max()
-    print(f"cfg{cid} n={n}: encoder rel err {err:.2e}")
+    print(f"{wl} n={n}: encoder rel err {err:.2e}")
     # fp32 networks: fp32 MFMA chain; bf16 networks: bf16 activations (2^-9 rounding per layer)
     assert err < (1e-5 if cfg.dtype == "f32" else 1e-2)
 
@@ -93,34 +98,34 @@ def test_encoder_parity(cid, n, bias_on):
 # fp32: every stage is a few fp32 contractions of length <= 2D, so the
 # per-row relative error stays near 1e-6; bf16 operands carry 2^-9 relative
 # rounding, so one stage moves a state by about 1e-3 of its update.
-@pytest.mark.parametrize("cid,M,N,stages,tol", [
-    (0, 10, 12, (0, 4), 1e-5),
-    (1, 512, 512, (0, 2), 1e-5),
-    (1, 100, 77, (1, 3), 1e-5),
-    (3, 2048, 1536, (0, 2), 1e-5),
-    (2, 1024, 1024, (0, 2), 5e-3),
-    (2, 300, 45, (3, 5), 5e-3),
-    (2, 33, 1, (0, 3), 5e-3),
-    (2, 68, 2000, (6, 9), 5e-3),
+@pytest.mark.parametrize("wl,M,N,stages,tol", [
+    ("pair10x12_f32", 10, 12, (0, 4), 1e-5),
+    ("pair512_f32", 512, 512, (0, 2), 1e-5),
+    ("pair512_f32", 100, 77, (1, 3), 1e-5),
+    ("pair2048x1536_f32", 2048, 1536, (0, 2), 1e-5),
+    ("pair1024_bf16", 1024, 1024, (0, 2), 5e-3),
+    ("pair1024_bf16", 300, 45, (3, 5), 5e-3),
+    ("pair1024_bf16", 33, 1, (0, 3), 5e-3),
+    ("pair1024_bf16", 68, 2000, (6, 9), 5e-3),
 ])
-def test_gnn_stage_parity(cid, M, N, stages, tol):
-    cfg = synth.CONFIGS[cid]
-    w = _weights(cid, bias_on=True)
+def test_gnn_stage_parity(wl, M, N, stages, tol):
+    cfg = synth.WORKLOADS[wl]
+    w = _weights(wl, bias_on=True)
     W = sg.pack_weights(w)
-    xA = synth.random_states(M, cfg.D, seed=10 + cid)
-    xB = synth.random_states(N, cfg.D, seed=20 + cid)
+    xA = synth.random_states(M, cfg.D, seed=10 + cfg.seed_id)
+    xB = synth.random_states(N, cfg.D, seed=20 + cfg.seed_id)
     a, b = dev(xA), dev(xB)
     sg.sg_stage_gnn(a, b, W, *stages)
     A, B = oracle.attentional_gnn(xA, xB, w["stages"][stages[0]:stages[1]], cfg.H, first_stage=stages[0])
     ea, eb = rel_rows(host(a), A), rel_rows(host(b), B)
-    print(f"cfg{cid} {M}x{N} stages {stages}: max rel err A {ea.max():.2e} B {eb.max():.2e}")
+    print(f"{wl} {M}x{N} stages {stages}: max rel err A {ea.max():.2e} B {eb.max():.2e}")
     assert ea.max() < tol and eb.max() < tol
 
 
-@pytest.mark.parametrize("cid,n", [(1, 512), (2, 1000), (0, 12)])
-def test_final_projection_parity(cid, n):
-    cfg = synth.CONFIGS[cid]
-    w = _weights(cid, bias_on=True, L=1)
+@pytest.mark.parametrize("wl,n", [("pair512_f32", 512), ("pair1024_bf16", 1000), ("pair10x12_f32", 12)])
+def test_final_projection_parity(wl, n):
+    cfg = synth.WORKLOADS[wl]
+    w = _weights(wl, bias_on=True, L=1)
     W = sg.pack_weights(w)
     x = synth.random_states(n, cfg.D, seed=5)
     f = host(sg.sg_stage_project(dev(x), W))
@@ -195,7 +200,7 @@ def test_match_stage_wide_score_range(scale, sched):
 @pytest.mark.parametrize("sched", SCHEDULES)
 def test_match_stage_network_score_range(sched):
     """Scores as large as the network's own at 2048 x 1536 (|S| up to ~345):
-    descriptors at scale 4.5, the cfg-3 shape, T = 100, held to the strict
+    descriptors at scale 4.5, the 2048 x 1536 shape, T = 100, held to the strict
     1e-3 bar."""
     M, N = 2048, 1536
     fA, fB = synth.random_matching_descriptors(M, N, 256, seed=29, scale=4.5)

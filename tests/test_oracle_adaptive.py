@@ -48,7 +48,7 @@ def test_threshold_schedule_matches_the_page():
 
 
 def test_frozen_layers_keep_the_states():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = _frozen(cfg)
     pair = synth.make_pair(cfg)
     d = oracle.superglue_descriptors(pair, w)
@@ -56,7 +56,7 @@ def test_frozen_layers_keep_the_states():
 
 
 def test_no_adaptivity_is_the_full_double_softmax_pass():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = synth.make_weights(cfg, adaptive=True, bias_on=True)
     pair = synth.make_pair(cfg)
     a = oracle.adaptive_match(pair, w, early_exit=False, prune=False)
@@ -69,7 +69,7 @@ def test_no_adaptivity_is_the_full_double_softmax_pass():
 def test_forced_exit_uses_the_first_layers_head():
     """Confidence bias +40: every point is confident after layer 0, so the
     pass stops there and layer 0's own head gives the matches."""
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = copy.deepcopy(synth.make_weights(cfg, adaptive=True, bias_on=True))
     w["conf"] = [(0 * wc, 40.0) for wc, _ in w["conf"]]
     pair = synth.make_pair(cfg)
@@ -85,7 +85,7 @@ def test_forced_exit_uses_the_first_layers_head():
 
 
 def test_never_confident_runs_every_layer():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = copy.deepcopy(synth.make_weights(cfg, adaptive=True, bias_on=True))
     w["conf"] = [(0 * wc, -40.0) for wc, _ in w["conf"]]
     pair = synth.make_pair(cfg)
@@ -101,7 +101,7 @@ def test_stop_ratio_counts_pruned_points_as_confident():
     layer 1 divides the unconfident count by the original M + N: with the
     threshold placed just under that ratio the pass stops at layer 1 (a
     ratio over the remaining points would be smaller and run on)."""
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     L, D = 3, cfg.D
     w = _frozen(cfg, L=L)
     e = np.eye(D)
@@ -129,7 +129,7 @@ def test_pruning_bookkeeping_and_matches_mapped_back():
     keeps the points with sigmoid(z) > 1 - width_confidence, layer 1 keeps
     all; prune counts are 1 + steps survived; the exit head (the main head at
     the last layer) matches the kept subsets, mapped to original indices."""
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     L, D = 3, cfg.D
     w = _frozen(cfg, L=L)
     e = np.eye(D)
@@ -156,7 +156,7 @@ def test_pruning_bookkeeping_and_matches_mapped_back():
 
 
 def test_point_count_floor_and_empty_image():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     L, D = 3, cfg.D
     w = _frozen(cfg, L=L)
     w["heads"] = [(h[0], h[1], 0.0 * h[2], -50.0) for h in w["heads"]]   # nothing is matchable

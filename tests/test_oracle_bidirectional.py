@@ -132,7 +132,7 @@ def test_gnn_routes_bidirectional_cross_stages():
 
 
 def test_generator_draws_shared_projection_for_cross_stages_only():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = synth.make_weights(cfg, cross="bidirectional")
     assert w["cross"] == "bidirectional"
     for s, st in enumerate(w["stages"]):

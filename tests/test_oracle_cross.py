@@ -23,21 +23,21 @@ def _agree(a, b, keys, rtol=1e-10, atol=1e-10):
 @pytest.mark.parametrize("bias_on", [False, True])
 @pytest.mark.parametrize("cross,rope", [("standard", False), ("bidirectional", False), ("standard", True)])
 def test_sinkhorn_pass(bias_on, cross, rope):
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = synth.make_weights(cfg, bias_on=bias_on, cross=cross, rope=rope)
     pair = synth.make_pair(cfg)
     _agree(native.superglue_match(pair, w, T=cfg.T), reference_numpy.superglue_match(pair, w, T=cfg.T), _KEYS)
 
 
 def test_sinkhorn_pass_d256_unequal():
-    cfg = synth.CONFIGS[3]
+    cfg = synth.WORKLOADS["pair2048x1536_f32"]
     w = synth.make_weights(cfg, L=2)
     pair = synth.make_pair(cfg, M=70, N=45)
     _agree(native.superglue_match(pair, w, T=30), reference_numpy.superglue_match(pair, w, T=30), _KEYS)
 
 
 def test_double_softmax_pass():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = synth.make_weights(cfg, bias_on=True)
     pair = synth.make_pair(cfg)
     _agree(native.double_softmax_match(pair, w), reference_numpy.double_softmax_match(pair, w),
@@ -45,7 +45,7 @@ def test_double_softmax_pass():
 
 
 def test_adaptive_pass():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = synth.make_weights(cfg, adaptive=True, bias_on=True, L=3)
     pair = synth.make_pair(cfg, M=40, N=33)
     kw = dict(depth_confidence=0.5, width_confidence=0.5, prune_min=8)

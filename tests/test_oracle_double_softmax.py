@@ -182,7 +182,7 @@ def test_head_reads_states_for_matchability_and_descriptors_for_similarity():
 
 
 def test_full_pass_empty_and_weights_present():
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS["pair512_f32"]
     w = synth.make_weights(cfg, L=1)
     assert w["wz"].shape == (cfg.D,)
     pair = synth.make_pair(cfg, M=0, N=5)

@@ -155,8 +155,8 @@ def test_gnn_stage_count_is_twice_L():
     np.testing.assert_allclose(A, xA + 2 * L * 0.25, rtol=1e-13)
 
 
-def _random_weights(cid=0, bias_on=True):
-    return synth.make_weights(synth.CONFIGS[cid], bias_on=bias_on)
+def _random_weights(wl="pair10x12_f32", bias_on=True):
+    return synth.make_weights(synth.WORKLOADS[wl], bias_on=bias_on)
 
 
 def test_gnn_permutation_equivariance():
@@ -182,7 +182,7 @@ def test_gnn_swap_symmetry():
 
 def test_full_pass_permutation_equivariance():
     """Permuting A's keypoints permutes matches0 and relabels matches1."""
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = _random_weights()
     pair = synth.make_pair(cfg)
     r = oracle.superglue_match(pair, w, T=cfg.T)
@@ -363,7 +363,7 @@ def test_extraction_brute_force(seed):
 
 
 def test_empty_inputs():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = _random_weights()
     pair = synth.make_pair(cfg, M=0)
     r = oracle.superglue_match(pair, w, T=5)

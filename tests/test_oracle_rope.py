@@ -148,7 +148,7 @@ def test_full_pass_uses_normalised_positions():
     normalised keypoints: translating the keypoints of one image in pixels
     (same image size) leaves the self-stage messages unchanged, so with the
     keypoint encoder switched off (zero weights) the descriptors do not move."""
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["pair10x12_f32"]
     w = synth.make_weights(cfg, rope=True, L=1)
     assert w["rope_basis"].shape == (cfg.D // cfg.H // 2, 2)
     w["enc"] = [(0 * W, 0 * b) for W, b in w["enc"]]

@@ -5,7 +5,7 @@ import synth
 
 
 def test_generator_is_deterministic():
-    c = synth.CONFIGS[0]
+    c = synth.WORKLOADS["pair10x12_f32"]
     a, b = synth.make_pair(c), synth.make_pair(c)
     for k in ("kpts0", "desc1", "conf0"):
         np.testing.assert_array_equal(a[k], b[k])
@@ -14,7 +14,7 @@ def test_generator_is_deterministic():
 
 
 def test_bf16_weights_are_representable():
-    w = synth.make_weights(synth.CONFIGS[2], L=1)
+    w = synth.make_weights(synth.WORKLOADS["pair1024_bf16"], L=1)
     W = w["stages"][0]["Wq"]
     assert np.all(W.view(np.uint32) & 0xFFFF == 0)
 
@@ -25,9 +25,9 @@ def test_round_to_bf16_ties_to_even():
 
 
 def test_planted_counts_and_ranges():
-    p2 = synth.make_pair(synth.CONFIGS[2])
+    p2 = synth.make_pair(synth.WORKLOADS["pair1024_bf16"])
     assert p2["n_planted"] == 410
-    p3 = synth.make_pair(synth.CONFIGS[3])
+    p3 = synth.make_pair(synth.WORKLOADS["pair2048x1536_f32"])
     assert p3["n_planted"] == 614
     for p in (p2, p3):
         for s in ("0", "1"):
@@ -37,7 +37,7 @@ def test_planted_counts_and_ranges():
 
 
 def test_batch_shapes():
-    b = synth.make_batch(synth.CONFIGS[4], batch=4)
+    b = synth.make_batch(synth.WORKLOADS["ragged32_bf16"], batch=4)
     assert b["kpts0"].shape == (4, 2048, 2) and b["desc1"].shape == (4, 2048, 256)
     for i in range(4):
         assert 256 <= b["M"][i] <= 2048 and 256 <= b["N"][i] <= 2048
@@ -45,7 +45,7 @@ def test_batch_shapes():
 
 
 def test_weight_shapes_and_bias_rules():
-    c = synth.CONFIGS[0]
+    c = synth.WORKLOADS["pair10x12_f32"]
     w = synth.make_weights(c, bias_on=True)
     assert [W.shape for W, _ in w["enc"]] == [(16, 3), (32, 16), (64, 32)]
     assert np.all(w["enc"][-1][1] == 0) and np.any(w["enc"][0][1] != 0)
