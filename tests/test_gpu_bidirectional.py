@@ -85,7 +85,7 @@ def test_end_to_end_fp32(wl, head):
 
 def test_end_to_end_bf16_descriptors():
     cfg = synth.WORKLOADS["pair1024_bf16"]
-    w = _weights(2)
+    w = _weights("pair1024_bf16")
     pair = synth.make_pair(cfg)
     ref = oracle.superglue_descriptors(pair, w)
     g = _run(pair, sg.pack_weights(w), cfg)
@@ -117,7 +117,7 @@ def test_batch_matches_single_pairs():
     """The ragged bf16 batch with bidirectional cross stages: sampled pairs
     agree with sg_match on the unpadded pair to the bf16 descriptor bar."""
     cfg = synth.WORKLOADS["ragged32_bf16"]
-    w = _weights(4)
+    w = _weights("ragged32_bf16")
     W = sg.pack_weights(w)
     b = synth.make_batch(cfg, batch=12)
     keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
@@ -223,7 +223,7 @@ def test_shared_similarity_repeats_and_slices():
     """Graph replays of the shared mode give the eager result; the mode's
     flag leaves networks without bidirectional stages refused."""
     cfg = synth.WORKLOADS["pair512_f32"]
-    w = _weights(1)
+    w = _weights("pair512_f32")
     W = sg.pack_weights(w)
     pair = synth.make_pair(cfg, M=200, N=190)
     keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
@@ -245,7 +245,7 @@ def test_shared_similarity_empty_image():
     """An image without points: as in the default mode, matches -1 and
     scores 0, and nothing else is computed (the pass returns early)."""
     cfg = synth.WORKLOADS["pair10x12_f32"]
-    W = sg.pack_weights(_weights(0, bias_on=True))
+    W = sg.pack_weights(_weights("pair10x12_f32", bias_on=True))
     for M, N in ((0, 7), (6, 0), (0, 0)):
         p = synth.make_pair(cfg, M=max(M, 1), N=max(N, 1))
         kA, dA, cA = dev(p["kpts0"][:M]), dev(p["desc0"][:M]), dev(p["conf0"][:M])

@@ -223,7 +223,7 @@ def test_head_on_gpu_states(wl, bias_on):
 
 def test_heads_share_the_network():
     """Both heads run the same encoder, GNN and projection: identical f."""
-    cfg, w, pair, _ = _case(0, True)
+    cfg, w, pair, _ = _case("pair10x12_f32", True)
     a = _run(pair, sg.pack_weights(w), cfg)
     b = _run(pair, sg.pack_weights(w, head="ds"), cfg)
     assert np.array_equal(a["f0"], b["f0"]) and np.array_equal(a["f1"], b["f1"])

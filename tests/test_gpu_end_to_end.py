@@ -82,7 +82,7 @@ def test_end_to_end_fp32(wl, bias_on, sched):
 
 @pytest.mark.parametrize("bias_on", [False, True])
 def test_end_to_end_bf16_descriptors(bias_on):
-    cfg, w, pair, ref = _case(2, bias_on)
+    cfg, w, pair, ref = _case("pair1024_bf16", bias_on)
     W = sg.pack_weights(w)
     g = _run(pair, W, cfg)
     e = max(rel_rows(g["f0"], ref["f0"]).max(), rel_rows(g["f1"], ref["f1"]).max())
@@ -92,7 +92,7 @@ def test_end_to_end_bf16_descriptors(bias_on):
 
 
 def test_matches_point_into_the_other_image():
-    cfg, w, pair, ref = _case(1)
+    cfg, w, pair, ref = _case("pair512_f32")
     g = _run(pair, sg.pack_weights(w), cfg)
     m0, m1 = g["matches0"], g["matches1"]
     for i in np.nonzero(m0 >= 0)[0]:
@@ -124,7 +124,7 @@ def test_single_point_images():
 
 
 def test_end_to_end_deterministic():
-    cfg, w, pair, _ = _case(0, True)
+    cfg, w, pair, _ = _case("pair10x12_f32", True)
     W = sg.pack_weights(w)
     a, b = _run(pair, W, cfg), _run(pair, W, cfg)
     assert np.array_equal(a["logP"], b["logP"]) and np.array_equal(a["matches0"], b["matches0"])

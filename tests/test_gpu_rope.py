@@ -64,7 +64,7 @@ def test_gnn_stage_parity(wl, M, N, stages, tol):
 def test_positions_already_normalised():
     """Without an image size the positions are taken as normalised."""
     cfg = synth.WORKLOADS["pair512_f32"]
-    w = _weights(1)
+    w = _weights("pair512_f32")
     W = sg.pack_weights(w)
     pair = synth.make_pair(cfg, M=200, N=150, seed=9)
     pA = oracle.normalize_keypoints(pair["kpts0"], *pair["image_size0"]).astype(np.float32)
@@ -107,7 +107,7 @@ def test_end_to_end_fp32(wl, head, cross):
 
 def test_end_to_end_bf16_descriptors():
     cfg = synth.WORKLOADS["pair1024_bf16"]
-    w = _weights(2)
+    w = _weights("pair1024_bf16")
     pair = synth.make_pair(cfg)
     ref = oracle.superglue_descriptors(pair, w)
     g = _run(pair, sg.pack_weights(w), cfg)
@@ -121,7 +121,7 @@ def test_translation_invariance_on_the_gpu():
     leaves the descriptors unchanged up to fp32 rounding of the angles; the
     rotary encoding does act (a zero basis changes them)."""
     cfg = synth.WORKLOADS["pair512_f32"]
-    w = dict(_weights(1, bias_on=True))
+    w = dict(_weights("pair512_f32", bias_on=True))
     w["enc"] = [(0 * W_, 0 * b) for W_, b in w["enc"]]
     pair = synth.make_pair(cfg)
     shifted = dict(pair, kpts0=pair["kpts0"] + np.array([21.0, -9.0], np.float32))
@@ -136,7 +136,7 @@ def test_translation_invariance_on_the_gpu():
 
 def test_batch_matches_single_pairs():
     cfg = synth.WORKLOADS["ragged32_bf16"]
-    w = _weights(4)
+    w = _weights("ragged32_bf16")
     W = sg.pack_weights(w)
     b = synth.make_batch(cfg, batch=12)
     keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
