@@ -180,6 +180,29 @@ def test_match_stage_parity(M, N, D, T, alpha, sched):
 
 
 @pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("M,N,alpha", [(300, 257, -60.0), (300, 257, 60.0), (1024, 1024, 60.0), (200, 333, 400.0)])
+def test_match_stage_extreme_dustbin(M, N, alpha, sched):
+    """Dustbin scores far from the real ones (scores of the planted pairs
+    reach ~150, of unrelated pairs ~30): at -60 the dustbins take almost no
+    mass; at 60 every unmatched row's maximum is its dustbin entry; at 400
+    every row's and column's is, so each real entry's exponential relative to
+    its row maximum underflows and the one-pass schedule's column partials
+    take their exact path.  Held to max(1e-3, 2e-6 max|logP|)."""
+    fA, fB = synth.random_matching_descriptors(M, N, 256, seed=M + 3 * N)
+    out = sg.sg_stage_match(dev(fA), dev(fB), alpha, 100, sinkhorn=sched)
+    torch.cuda.synchronize()
+    r = oracle.match_from_descriptors(fA, fB, alpha, 100)
+    big = np.abs(r["logP"]).max()
+    err = np.abs(host(out["logP"]) - r["logP"]).max()
+    ex = check_matches(host(out["matches0"]), host(out["matches1"]), r["logP"], r["matches0"], r["matches1"])
+    print(f"{M}x{N} alpha {alpha}: max |logP| {big:.0f}, max |dlogP| {err:.2e}, "
+          f"matches {int((r['matches0'] >= 0).sum())}, exempt {ex}")
+    assert err < max(1e-3, 2e-6 * big)
+    cs = np.exp(host(out["logP"]).astype(np.float64)).sum(axis=0)
+    np.testing.assert_allclose(cs, np.append(np.ones(N), M), rtol=1e-4)
+
+
+@pytest.mark.parametrize("sched", SCHEDULES)
 @pytest.mark.parametrize("scale", [6.0, 9.0])
 def test_match_stage_wide_score_range(scale, sched):
     """Scores spanning hundreds of log2 units: exponentials relative to a row's
