@@ -106,9 +106,9 @@ typedef enum { SG_CROSS_STANDARD = 0, SG_CROSS_BIDIRECTIONAL = 1 } sg_cross;
  * pass.  The head of the last layer run (W_f,l, w_z,l; the main head for
  * layer L_max - 1) matches the remaining points; pruned points get -1 / 0.
  * Adaptive calls exist for sg_match only.  They read a few counters back
- * after every layer (one stream synchronisation per layer), always run
- * eagerly (never captured into a graph) and are refused on a stream that the
- * caller is capturing. */
+ * after every layer (the device posts them into host-visible memory and the
+ * call waits for each post on the host), always run eagerly (never captured
+ * into a graph) and are refused on a stream that the caller is capturing. */
 #define SG_MAX_ENC 8     /* hidden layers of the keypoint encoder          */
 #define SG_MAX_BATCH 64  /* pairs per sg_match_batch call                  */
 

@@ -1043,10 +1043,10 @@ sg_status enqueue_full(const Problem& p, const Plan& pl, const WsLayout& wl, cha
 
 // ------------------------------------------------- adaptive depth and width
 //
-// One pair, eager, with one stream synchronisation per layer: the stop
-// decision and the kept counts come back to the host, which re-plans the row
-// space when points are dropped (as the page's own loop does with its Python
-// control flow).
+// One pair, eager, with the host waiting for every layer's statistics: the
+// stop decision and the kept counts are posted into host-visible memory, and
+// the host re-plans the row space when points are dropped (as the page's own
+// loop does with its Python control flow).
 
 std::mutex g_pin_mu;
 int* g_pin[64] = {};      // host-visible, coherent post box per device
@@ -1097,7 +1097,7 @@ sg_status run_adaptive(const Problem& p0, const sg_weights* w, const WLayout& L,
   if (st) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
-      return fail(SG_ERR_INVALID_ARG, "adaptive calls synchronise their stream and cannot be captured");
+      return fail(SG_ERR_INVALID_ARG, "adaptive calls wait on the host for every layer and cannot be captured");
   }
   const bool depth = o->flags & SG_FLAG_EARLY_EXIT, width = o->flags & SG_FLAG_PRUNE;
   const float alpha = o->depth_confidence > 0.f ? o->depth_confidence : 0.95f;
