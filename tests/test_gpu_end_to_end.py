@@ -349,6 +349,48 @@ def test_max_batch_wide_rows_on_gpu_descriptors():
         np.testing.assert_array_equal(r[key], g[key][order], err_msg=key)
 
 
+# (M, N) on either side of the one-pass schedule's 64-row blocks: the dustbin
+# row closes a block of its own or joins the last block as an extra row; the
+# columns cover 1, 2 and both sides of 64 and 128
+_BLOCK_EDGES = [(63, 64), (64, 63), (65, 129), (128, 1), (1, 256), (127, 128), (129, 2), (2, 65), (192, 191)]
+
+
+def _batch_of(pairs, D):
+    """A padded batch (the layout make_batch draws) from given pairs."""
+    B, P = len(pairs), max(max(p["kpts0"].shape[0], p["kpts1"].shape[0]) for p in pairs)
+    out = {"M": np.array([p["kpts0"].shape[0] for p in pairs], np.int32),
+           "N": np.array([p["kpts1"].shape[0] for p in pairs], np.int32), "pairs": pairs,
+           "image_size0": pairs[0]["image_size0"], "image_size1": pairs[0]["image_size1"]}
+    for key, shape in (("kpts", (2,)), ("conf", ()), ("desc", (D,))):
+        for side in "01":
+            a = np.zeros((B, P) + shape, np.float32)
+            for i, p in enumerate(pairs):
+                a[i, :p[key + side].shape[0]] = p[key + side]
+            out[key + side] = a
+    return out
+
+
+@pytest.mark.parametrize("sched", ["one", "two"])
+def test_batch_block_edges_vs_oracle(sched):
+    """Pairs whose point counts sit on the block edges of the Sinkhorn
+    kernels, in one fp32 batch: every pair against the oracle end to end."""
+    base = synth.WORKLOADS["pair10x12_f32"]
+    cfg = dataclasses.replace(base, seed_id=8, planted="B", planted_frac=0.4)
+    w = synth.make_weights(base, bias_on=True)
+    pairs = [synth.make_pair(cfg, seed=500 + i, M=m, N=n) for i, (m, n) in enumerate(_BLOCK_EDGES)]
+    b = _batch_of(pairs, base.D)
+    g = _run_batch(cfg, sg.pack_weights(w), b, sinkhorn=sched)
+    for i, p in enumerate(pairs):
+        M, N = _BLOCK_EDGES[i]
+        ref = oracle.superglue_match(p, w, T=cfg.T)
+        lp = g["logP"][i, :M + 1, :N + 1]
+        dl = np.abs(lp - ref["logP"]).max()
+        assert dl < 1e-3, (i, M, N, dl)
+        check_matches(g["matches0"][i, :M], g["matches1"][i, :N], ref["logP"], ref["matches0"], ref["matches1"])
+        _column_sums_ok(lp, M, N)
+        assert (g["matches0"][i, M:] == -1).all() and (g["matches1"][i, N:] == -1).all()
+
+
 def _sampled_pairs(b):
     """Smallest, largest and most unequal pairs of a ragged batch, plus the first."""
     M, N = b["M"].astype(int), b["N"].astype(int)
