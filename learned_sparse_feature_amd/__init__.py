@@ -299,9 +299,11 @@ def sg_match(kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int,
 def sg_match_batch(M, N, kptsA, descA, confA, kptsB, descB, confB, weights: Weights, L: int, T: int, *,
                    threshold: float = 0.0, image_size=None, want_matches1=True, want_logP=False,
                    want_desc=False, workspace=None, stage_events=None, timed_kernel=SG_K_NONE,
-                   kernel_events=None, stream=None, graph=True, sinkhorn: str = "auto") -> dict:
+                   kernel_events=None, stream=None, graph=True, sinkhorn: str = "auto",
+                   out: Optional[dict] = None) -> dict:
     """B padded pairs: kptsA [B][Mpad][2], descA [B][Mpad][D], confA [B][Mpad] (and B
-    likewise); M, N: sequences of the true counts."""
+    likewise); M, N: sequences of the true counts.  `out` may supply the output
+    tensors (same keys and shapes) so that repeated calls reuse buffers."""
     dev = descA.device
     B, Mpad, Npad, D = kptsA.shape[0], kptsA.shape[1], kptsB.shape[1], weights.D
     for t, nm, shp in ((kptsA, "kptsA", (B, Mpad, 2)), (descA, "descA", (B, Mpad, D)), (confA, "confA", (B, Mpad)),
@@ -309,16 +311,25 @@ def sg_match_batch(M, N, kptsA, descA, confA, kptsB, descB, confB, weights: Weig
         _check_tensor(t, nm, torch.float32, shp)
     Ma = (C.c_int32 * B)(*[int(x) for x in M])
     Na = (C.c_int32 * B)(*[int(x) for x in N])
-    out = {"matches0": torch.empty((B, Mpad), dtype=torch.int32, device=dev),
-           "scores0": torch.empty((B, Mpad), dtype=torch.float32, device=dev)}
-    if want_matches1:
-        out["matches1"] = torch.empty((B, Npad), dtype=torch.int32, device=dev)
-        out["scores1"] = torch.empty((B, Npad), dtype=torch.float32, device=dev)
-    if want_logP:
-        out["logP"] = torch.full((B, Mpad + 1, Npad + 1), float("nan"), dtype=torch.float32, device=dev)
-    if want_desc:
-        out["f0"] = torch.zeros((B, Mpad, D), dtype=torch.float32, device=dev)
-        out["f1"] = torch.zeros((B, Npad, D), dtype=torch.float32, device=dev)
+    if out is None:
+        out = {"matches0": torch.empty((B, Mpad), dtype=torch.int32, device=dev),
+               "scores0": torch.empty((B, Mpad), dtype=torch.float32, device=dev)}
+        if want_matches1:
+            out["matches1"] = torch.empty((B, Npad), dtype=torch.int32, device=dev)
+            out["scores1"] = torch.empty((B, Npad), dtype=torch.float32, device=dev)
+        if want_logP:
+            out["logP"] = torch.full((B, Mpad + 1, Npad + 1), float("nan"), dtype=torch.float32, device=dev)
+        if want_desc:
+            out["f0"] = torch.zeros((B, Mpad, D), dtype=torch.float32, device=dev)
+            out["f1"] = torch.zeros((B, Npad, D), dtype=torch.float32, device=dev)
+    else:
+        out = dict(out)
+        for k, dt_, shp in (("matches0", torch.int32, (B, Mpad)), ("scores0", torch.float32, (B, Mpad)),
+                            ("matches1", torch.int32, (B, Npad)), ("scores1", torch.float32, (B, Npad)),
+                            ("logP", torch.float32, (B, Mpad + 1, Npad + 1)), ("f0", torch.float32, (B, Mpad, D)),
+                            ("f1", torch.float32, (B, Npad, D))):
+            if k in out:
+                _check_tensor(out[k], k, dt_, shp)
     if workspace is None:
         workspace = _workspace(dev, workspace_size(weights, Mpad, Npad, B) + _transposed_extra(sinkhorn, B, Mpad, Npad))
     o, keep, count = _opts(dev, threshold=threshold, image_size=image_size, workspace=workspace,

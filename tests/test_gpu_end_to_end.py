@@ -157,6 +157,33 @@ def test_graph_replay_equals_eager():
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("sched", ["one", "two"])
+def test_batch_graph_replay_equals_eager(sched):
+    """sg_match_batch calls that repeat are captured into a HIP graph and
+    replayed (under the one-pass schedule, its alternating partial buffers
+    included): every replay equals the eager result bitwise, with other
+    eager work and synchronisations in between."""
+    cfg = synth.WORKLOADS["ragged32_bf16"]
+    W = sg.pack_weights(synth.make_weights(cfg))
+    keys = ("kpts0", "desc0", "conf0", "kpts1", "desc1", "conf1")
+    b, b2 = synth.make_batch(cfg, batch=8), synth.make_batch(cfg, seed=91, batch=8)
+    t, t2 = [dev(b[k]) for k in keys], [dev(b2[k]) for k in keys]
+    kw = dict(image_size=(*b["image_size0"], *b["image_size1"]), want_logP=True, sinkhorn=sched)
+    ref = sg.sg_match_batch(b["M"], b["N"], *t, W, cfg.L, cfg.T, graph=False, **kw)
+    torch.cuda.synchronize()
+    ref = {k: torch.nan_to_num(v, nan=-9.0) for k, v in ref.items() if isinstance(v, torch.Tensor)}
+    bufs = {k: torch.empty_like(v) for k, v in ref.items()}
+    for rep in range(4):
+        for k, v in bufs.items():
+            v.fill_(float("nan") if k == "logP" else -7)
+        sg.sg_match_batch(b["M"], b["N"], *t, W, cfg.L, cfg.T, out=bufs, **kw)
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(torch.nan_to_num(bufs[k], nan=-9.0), ref[k]), (rep, k)
+        sg.sg_match_batch(b2["M"], b2["N"], *t2, W, cfg.L, cfg.T, graph=False, **kw)  # eager work in between
+        torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ batch
 
 @functools.lru_cache(maxsize=None)
