@@ -417,10 +417,12 @@ def per_config(sg, synth, np, torch, dev, names_run, reps=10):
             Ms, Ns = [int(x) for x in b["M"]], [int(x) for x in b["N"]]
             coupling_bytes = sum(4.0 * (m + 1) * (n + 1) for m, n in zip(Ms, Ns))
             ws = torch.empty(sg.workspace_size(W, cfg.pad, cfg.pad, cfg.batch), dtype=torch.uint8, device=dev)
+            bbufs = {"matches0": torch.empty((cfg.batch, cfg.pad), dtype=torch.int32, device=dev),
+                     "scores0": torch.empty((cfg.batch, cfg.pad), dtype=torch.float32, device=dev)}
 
             def call(**kw):
                 return sg.sg_match_batch(Ms, Ns, *t, W, cfg.L, cfg.T, image_size=img, workspace=ws,
-                                         want_matches1=False, **kw)
+                                         want_matches1=False, out=bbufs, **kw)
             pairs = cfg.batch
         else:
             pair = synth.make_pair(cfg)
@@ -763,7 +765,7 @@ def main():
 
         def bstep(**kw):
             return sg.sg_match_batch(Ms, Ns, *[bt[k] for k in keys], W, cfg.L, cfg.T, image_size=img,
-                                     workspace=wsb, want_matches1=False, sinkhorn=args.sinkhorn, **kw)
+                                     workspace=wsb, want_matches1=False, sinkhorn=args.sinkhorn, out=bbufs, **kw)
         for _ in range(max(2, args.warmup)):
             bstep()
         torch.cuda.synchronize()
