@@ -684,19 +684,26 @@ sg_status run_matching(const Problem& p, const Plan& pl, int D, float alpha, con
   }
   if (pl.two_sweep) {
     // T iterations: u = log mu - lse_j(Z + v) over the rows of Z, then
-    // v = log nu - lse_i(Z + u) over the rows of ZT
+    // v = log nu - lse_i(Z + u) over the rows of ZT.  For one pair the last
+    // column sweep, which reads Z + u with the final u, also takes the
+    // column argmax of the extraction.
+    const bool fused_arg = pl.pt.n_pairs == 1 && T > 0;
     for (int it = 0; it < T; ++it) {
+      const bool arg = fused_arg && it == T - 1;
       HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(Z, pl.pt, 0, it == 0 ? nullptr : V, U, alpha2, alpha_dev, pl.ru, st); }),
              "sinkhorn rows");
-      HIPCHK(tm.run(SG_K_SINKHORN, [&] { return launch_lse(ZT, pl.pt, 1, U, V, alpha2, alpha_dev, pl.rv, st); }),
-             "sinkhorn cols");
+      HIPCHK(tm.run(SG_K_SINKHORN, [&] {
+               return launch_lse(ZT, pl.pt, 1, U, V, alpha2, alpha_dev, pl.rv, st, arg ? idx1 : nullptr,
+                                 arg ? out.m1 : nullptr, arg ? out.s1 : nullptr);
+             }), "sinkhorn cols");
     }
     if (T == 0) {
       HIPCHK(launch_fill_f32(U, 0.f, (int)pl.uf, st), "zero u");
       HIPCHK(launch_fill_f32(V, 0.f, (int)pl.vf, st), "zero v");
     }
     tm.stage(SG_EV_SINKHORN);
-    HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, EXT_SINKHORN, st), "column argmax");
+    if (!fused_arg)
+      HIPCHK(launch_col_argmax(ZT, pl.pt, U, idx1, p.Npad, out.m1, out.s1, EXT_SINKHORN, st), "column argmax");
   } else if (pl.fused) {
     // T fused iterations: each reduces the previous iteration's block
     // partials into v, then updates u and writes its own partials (the two

@@ -187,8 +187,11 @@ hipError_t launch_sink_iter(const float* Z, const PairTable& pt, const float* Pi
 hipError_t launch_sink_cols(const PairTable& pt, const float* P, const float* Pd, float* v_out, const float* PV,
                             const int* PI, int* idx1, int write_v, int Npad, int32_t* m1, float* s1,
                             hipStream_t st);
+// idx1 (one pair, which = 1, w_in the final u only): the sweep also leaves
+// the column argmax and the default side-B outputs (k_col_argmax's work)
 hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const float* w_in, float* w_out,
-                      float alpha2, const float* alpha_dev, int total_rows, hipStream_t st);
+                      float alpha2, const float* alpha_dev, int total_rows, hipStream_t st, int* idx1 = nullptr,
+                      int32_t* m1 = nullptr, float* s1 = nullptr);
 // What the extraction kernels read as the real block of the log assignment
 // (their `mode`): EXT_SINKHORN: Z2 + u + v + log2(M+N) (base 2); EXT_DS: the
 // double-softmax head, 2 Z2 + u + v (base 2, see sg_double_softmax.hip);

@@ -862,18 +862,51 @@ __global__ __launch_bounds__(256) void k_lse(const float* __restrict__ Zbase, Pa
 // XB: explicit dustbins (stage entry points): bown [nr + 1] holds each row's
 // dustbin-column entry (the corner last) and bcross [ld4(nc + 1)] the
 // dustbin row's entries; alpha2 / alpha_dev are unused.
-template <int NV4, bool XB>
+// ARG (the last column sweep over ZT, whose duals wv are the final u): each
+// real row j of ZT also leaves the column argmax argmax_i Z2_ij + u_i over
+// the real rows (lowest index on ties) in idx1[j], and the default -1 / 0 in
+// m1[j] / s1[j] (when given), which k_col_argmax would otherwise compute in
+// a launch of its own: the sweep already holds every one of those sums.
+template <int NV4, bool XB, bool ARG = false>
 __global__ __launch_bounds__(256) void k_lse_one(const float* __restrict__ Z, const float* __restrict__ wv,
                                                  float* __restrict__ w_out, int nr, int nc, float alpha2,
                                                  const float* __restrict__ alpha_dev, float lm_real,
                                                  float lm_dust, const float* __restrict__ bown,
-                                                 const float* __restrict__ bcross) {
+                                                 const float* __restrict__ bcross, int* __restrict__ idx1 = nullptr,
+                                                 int32_t* __restrict__ m1 = nullptr, float* __restrict__ s1 = nullptr) {
+  static_assert(!(ARG && XB), "the fused column argmax belongs to the pass's own sweep");
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave_id();
   if (i > nr) return;
   float4 zq[NV4], wq[NV4];
   const float* row = (XB && i >= nr) ? bcross : Z + (size_t)max(min(i, nr - 1), 0) * ld4(nc);
   lse_loads<NV4>(row, wv, XB ? 1 : nr, nc, lane, zq, wq);
+  if constexpr (ARG) {
+    if (i < nr) {  // (wave-uniform)
+      float best = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int k = 0; k < NV4; ++k) {
+        const int r = 4 * (lane + 64 * k);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float y = f4c(zq[k], c) + f4c(wq[k], c);
+          if (r + c < nc && y > best) {
+            best = y;
+            bi = r + c;
+          }
+        }
+      }
+      wave_argmax(best, bi);
+      if (lane == 0) {
+        idx1[i] = bi;
+        if (m1) {
+          m1[i] = -1;
+          if (s1) s1[i] = 0.f;
+        }
+      }
+    }
+  }
   const float wd = wv ? wv[nc] : 0.f;
   const float dust = XB ? bown[i] : 0.f;
   if (!XB && alpha_dev) alpha2 = alpha_dev[0] * kLog2e;
@@ -1128,7 +1161,7 @@ hipError_t launch_lse_explicit(const float* Z, const float* w_in, float* w_out, 
 #define SG_LSEX(NV)                                                                                       \
   if (nv4 == NV) {                                                                                        \
     hipLaunchKernelGGL((k_lse_one<NV, true>), grid, dim3(256), 0, st, Z, w_in, w_out, nr, nc, 0.f, nullptr, \
-                       lm_real, lm_dust, bown, bcross);                                                   \
+                       lm_real, lm_dust, bown, bcross, nullptr, nullptr, nullptr);                        \
     return hipGetLastError();                                                                             \
   }
   SG_LSEX(1) SG_LSEX(2) SG_LSEX(4) SG_LSEX(8) SG_LSEX(16)
@@ -1257,8 +1290,10 @@ hipError_t launch_sink_cols(const PairTable& pt, const float* P, const float* Pd
 }
 
 hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const float* w_in, float* w_out,
-                      float alpha2, const float* alpha_dev, int total_rows, hipStream_t st) {
+                      float alpha2, const float* alpha_dev, int total_rows, hipStream_t st, int* idx1, int32_t* m1,
+                      float* s1) {
   if (total_rows <= 0) return hipSuccess;
+  if (idx1 && (pt.n_pairs != 1 || which != 1 || !w_in)) return hipErrorInvalidValue;
   int nc = 0;
   for (int b = 0; b < pt.n_pairs; ++b) nc = std::max(nc, which ? pt.M[b] : pt.N[b]);
   const int nv4 = sink_nv4(nc);
@@ -1273,8 +1308,12 @@ hipError_t launch_lse(const float* Z, const PairTable& pt, int which, const floa
     const float lr = 0.f - lmn, ld = std::log2((float)nc) - lmn;
 #define SG_LSE(NV)                                                                                             \
     if (nv4 == NV) {                                                                                           \
-      hipLaunchKernelGGL((k_lse_one<NV, false>), grid, dim3(256), 0, st, zp, wv, wo, nr, nc, alpha2, alpha_dev, lr, \
-                         ld, nullptr, nullptr);                                                                \
+      if (idx1)                                                                                                \
+        hipLaunchKernelGGL((k_lse_one<NV, false, true>), grid, dim3(256), 0, st, zp, wv, wo, nr, nc, alpha2,    \
+                           alpha_dev, lr, ld, nullptr, nullptr, idx1, m1, s1);                                 \
+      else                                                                                                     \
+        hipLaunchKernelGGL((k_lse_one<NV, false>), grid, dim3(256), 0, st, zp, wv, wo, nr, nc, alpha2, alpha_dev, \
+                           lr, ld, nullptr, nullptr, nullptr, nullptr, nullptr);                               \
       return hipGetLastError();                                                                                \
     }
     SG_LSE(1) SG_LSE(2) SG_LSE(4) SG_LSE(8) SG_LSE(16)
