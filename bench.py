@@ -383,6 +383,41 @@ def latency_percentiles(step, sg, torch, n):
     return {"passes": n, "p10_ms": q(0.1), "p50_ms": q(0.5), "p90_ms": q(0.9)}
 
 
+def concurrent_calls(args, sg, torch, W, t, img, cfg, M, N, dev, calls=400):
+    """Single-pair calls (the headline's pair, one per call) spread round-robin
+    over S streams of default priority, each stream with its own workspace
+    and outputs (so each replays its own captured graph) and the inputs
+    shared: pairs/s over `calls` calls, and the mean time from a call's
+    enqueue to its end on its stream.  Context for serving independent
+    requests; the headline value stays one call in flight."""
+    res = {}
+    for S in sorted({2, args.streams} if args.streams > 2 else {2}):
+        streams = [torch.cuda.Stream(device=dev) for _ in range(S)]
+        wss = [torch.empty(sg.workspace_size(W, M, N, 1), dtype=torch.uint8, device=dev) for _ in range(S)]
+        outs = [{"matches0": torch.empty(M, dtype=torch.int32, device=dev),
+                 "scores0": torch.empty(M, dtype=torch.float32, device=dev)} for _ in range(S)]
+
+        def call(i):
+            sg.sg_match(*t, W, cfg.L, cfg.T, image_size=img, workspace=wss[i], out=outs[i], stream=streams[i],
+                        sinkhorn=args.sinkhorn)
+        for _ in range(3):  # eager, capture, replay
+            for i in range(S):
+                call(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(calls):
+            call(k % S)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        # per-call time with S calls in flight: each stream's calls run back to
+        # back, so a call takes the stream's wall time over its calls
+        res[f"streams_{S}"] = {"calls": calls, "pairs_per_s": round(calls / dt, 1),
+                               "ms_per_call_per_stream": round(1e3 * dt / (calls / S), 3)}
+        same = all(bool(torch.equal(outs[0]["matches0"], o["matches0"])) for o in outs[1:])
+        res[f"streams_{S}"]["outputs_equal_across_streams"] = same
+    return res
+
+
 def workload_names(synth, spec):
     """Workload names from a comma-separated list of names or of positions in
     synth.WORKLOADS."""
@@ -553,6 +588,8 @@ def main():
                          "or their positions in it (0-4)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="before the steps, copy this many MiB with a plain device copy (counter scaling)")
+    ap.add_argument("--streams", type=int, default=4,
+                    help="also time single-pair calls spread over 2..this many streams (context; 1: skip)")
     ap.add_argument("--no-launch-floor", action="store_true",
                     help="skip the dependent-launch floor of a replayed graph (launch_floor_us)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("CSV", "KERNEL"),
@@ -624,6 +661,10 @@ def main():
     log(f"{ms:.3f} ms/step, {value:.1f} pairs/s; matches {(out['matches0'] >= 0).sum().item()}")
     latency = latency_percentiles(step, sg, torch, max(10, min(100, args.steps)))
     log(f"latency: {latency}")
+    concurrent = None
+    if args.streams > 1:
+        concurrent = concurrent_calls(args, sg, torch, W, t, img, cfg, M, N, dev)
+        log(f"concurrent single-pair calls: {concurrent}")
 
     # per-stage times (a separate pass: stage events perturb the stream slightly)
     stages = {}
@@ -779,6 +820,24 @@ def main():
                  "pairs_per_s": round(nb * Bn / dtb, 2)}
         if not args.no_kernel_timing:
             batch["kernels"] = batch_kernels(args, cfg, sg, np, torch, bstep, Bn, M, N, ds)
+        if not ds and cfg.T > 0:
+            # the Sinkhorn stage as the single pair's is measured: one event
+            # pair around the stage's launches (T fused iterations and the
+            # final column reduction) in an eager pass (stage events run the
+            # call without its graph), against one read of every pair's
+            # couplings per iteration; no per-launch events in between
+            ev = sg.make_events(sg.SG_N_STAGE_EVENTS)
+            sk = []
+            for _ in range(3):
+                bstep(stage_events=ev)
+                torch.cuda.synchronize()
+                sk.append(ev[3].elapsed_time(ev[4]) * 1e3)
+            per_it = 4.0 * (M + 1) * (N + 1) * Bn
+            us_it = float(np.median(sk)) / cfg.T
+            batch["sinkhorn_stage"] = {"stage_us": round(float(np.median(sk)), 1), "us_per_iteration": round(us_it, 2),
+                                       "bytes_per_iteration": per_it,
+                                       "achieved_GBps": round(per_it / us_it / 1e3, 1),
+                                       "frac_hbm": round(per_it / us_it / 1e3 / PEAK["hbm_GBps"], 4)}
         log(f"batch: {batch}")
 
     adaptive = adaptive_bench(args, cfg, dev, sg, synth, np, torch) if args.adaptive else None
@@ -815,7 +874,7 @@ def main():
                    "shared_similarity": args.shared_similarity},
         "roofline": roofline, "mfma_util_pct": mfma_util, "cpu_baseline": cpu, "latency": latency,
         "stages_ms": stages, "kernels": kernels,
-        "batch_throughput": batch, "launch_floor_us": floor,
+        "batch_throughput": batch, "concurrent_streams": concurrent, "launch_floor_us": floor,
         "per_config": configs,
         "adaptive": adaptive,
         "baseline_context": {"pages_ms_per_pair": {"GTX1080_1024kp": 87.0, "unstated_hw_2048kp": 70.0},
