@@ -277,8 +277,19 @@ __global__ __launch_bounds__(256) void k_sink_rows(const float* __restrict__ Zb,
 // sm [W][NGS], vl [NGS + 1] (vl[NGS].x: the dustbin column's dual), sm_u
 // [RB + 1] (+1: the dustbin row may follow the block's last row), smi
 // [W][NGS] (ARG only).
+// The fields of the pair that a workgroup of the fused iteration works on.
+struct IterPair {
+  int gb;     // the workgroup's row block within the pair
+  int M, N;   // the pair's point counts
+  int G;      // its row blocks
+  int gpre;   // its first row block over the batch (dustbin-column partials)
+  int z_off;  // float offsets of its couplings, its column partials and its u
+  int p_off;
+  int uoff;
+};
+
 template <int W, int RPW, int NV4, int RS, bool ARG, int NGS>
-__device__ __forceinline__ void sink_iter_block(const float* __restrict__ Zb, const PairTable& pt, int b, int gb,
+__device__ __forceinline__ void sink_iter_block(const float* __restrict__ Zb, const IterPair& ip,
                                                 const float* __restrict__ Pin, const float* __restrict__ Pdin,
                                                 float* __restrict__ u_out, float* __restrict__ Pout,
                                                 float* __restrict__ Pdout, float* __restrict__ PV,
@@ -290,12 +301,12 @@ __device__ __forceinline__ void sink_iter_block(const float* __restrict__ Zb, co
   constexpr int RB = W * RPW;
   constexpr int NG = 64 * NV4;  // float4 column groups of a row held by one wave
   constexpr int NSTEP = RPW / RS;
-  const int G = pt.gpre[b + 1] - pt.gpre[b];
-  const int M = pt.M[b], N = pt.N[b];
+  const int G = ip.G, gb = ip.gb;
+  const int M = ip.M, N = ip.N;
   const int i0 = gb * RB;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int ldz = ld4(N);
-  const float* zp = Zb + pt.z_off[b];
+  const float* zp = Zb + ip.z_off;
   const float lmn = log2f((float)(M + N));
 
   // loads of step p of the wave's rows (at a real row and column, clamped in
@@ -317,7 +328,7 @@ __device__ __forceinline__ void sink_iter_block(const float* __restrict__ Zb, co
 
   // ---- phase 1: the column duals of the previous iteration
   if (Pin) {
-    const float* pp = Pin + pt.p_off[b];
+    const float* pp = Pin + ip.p_off;
     constexpr int U = 8;
     for (int q = threadIdx.x; 4 * q < N; q += NT) {
       const int j = 4 * q;
@@ -351,7 +362,7 @@ __device__ __forceinline__ void sink_iter_block(const float* __restrict__ Zb, co
       vl[q] = make_float4(o[0], o[1], o[2], o[3]);
     }
     if (w == 0) {  // the dustbin column: v_N = log2 M - log2(M+N) - lse2_g Pdin[g]
-      const float* pd = Pdin + pt.gpre[b];
+      const float* pd = Pdin + ip.gpre;
       float m = -INFINITY, sum = 0.f;
       for (int g = lane; g < G; g += 64) {
         const float x = pd[g];
@@ -434,7 +445,7 @@ __device__ __forceinline__ void sink_iter_block(const float* __restrict__ Zb, co
       for (int c = 0; c < 4; ++c) acc[k][c] = fmaf(t[k][c], wgt, acc[k][c]);
     if (lane == 0) {
       sm_u[w * RPW + ri] = update_u ? ur : 0.f;
-      if (update_u) u_out[pt.uoff[b] + i0 + w * RPW + ri] = ur;
+      if (update_u) u_out[ip.uoff + i0 + w * RPW + ri] = ur;
     }
   };
   const int nreal = min(max(M - (i0 + w * RPW), 0), RPW);  // the wave's real rows (a prefix of its rows)
@@ -455,7 +466,7 @@ __device__ __forceinline__ void sink_iter_block(const float* __restrict__ Zb, co
     if (w == W - 1 && lane == 0 && rd != RPW) sm_u[RB] = -INFINITY;
   }
 
-  const size_t pbase = (size_t)pt.p_off[b] + (size_t)gb * ldz;
+  const size_t pbase = (size_t)ip.p_off + (size_t)gb * ldz;
   if (update_u) {
 #pragma unroll
     for (int k = 0; k < NV4; ++k) sm[w][lane + 64 * k] = make_float4(acc[k][0], acc[k][1], acc[k][2], acc[k][3]);
@@ -515,7 +526,7 @@ __device__ __forceinline__ void sink_iter_block(const float* __restrict__ Zb, co
       for (int r = lane; r <= RB; r += 64)
         if (i0 + r <= M) sum += exp2_fast(sm_u[r] - mx);
       sum = wave_sum(sum);
-      if (lane == 0) Pdout[pt.gpre[b] + gb] = alpha2 + mx + log2_fast(sum);
+      if (lane == 0) Pdout[ip.gpre + gb] = alpha2 + mx + log2_fast(sum);
     }
   }
 
@@ -594,15 +605,37 @@ __global__ __launch_bounds__(64 * W) void k_sink_iter(const float* __restrict__ 
   __shared__ float4 vl[NGS + 1];
   __shared__ float sm_u[W * RPW + 1];
   __shared__ int4 smi[ARG ? W : 1][ARG ? NGS : 1];
+  // The workgroup's pair and row block from one round of table reads: lane
+  // l reads entry l of every per-pair array (vector loads, all in flight
+  // together), the pair in dispatch order is the count of pairs whose blocks
+  // end at or before this one (a ballot over the prefix sums), and its fields
+  // are read out of the lanes.  (A search over the prefix sums and lookups
+  // through the dispatch order would be a chain of dependent scalar loads,
+  // all on the path to the first row load.)
+  static_assert(SG_MAX_BATCH <= 64, "one lane per pair");
+  const int lane = threadIdx.x & 63, g = blockIdx.x;
+  const int np = pt.n_pairs;
+  const int e_end = pt.opre[lane + 1], e_beg = pt.opre[lane], e_ord = pt.ord[lane];
+  const int e_M = pt.M[lane], e_N = pt.N[lane], e_z = pt.z_off[lane], e_p = pt.p_off[lane], e_u = pt.uoff[lane];
+  const int e_g0 = pt.gpre[lane], e_g1 = pt.gpre[lane + 1];
   if (alpha_dev) alpha2 = alpha_dev[0] * kLog2e;
-  const int k = find_pair(pt.opre, pt.n_pairs, blockIdx.x);
-  if (k >= pt.n_pairs) return;
-  const int b = pt.ord[k], gb = blockIdx.x - pt.opre[k];
-  const int N = pt.N[b];
+  const int k = __popcll(__ballot(lane < np && g >= e_end));
+  if (k >= np) return;
+  const int b = __builtin_amdgcn_readlane(e_ord, k);
+  IterPair ip;
+  ip.gb = g - __builtin_amdgcn_readlane(e_beg, k);
+  ip.M = __builtin_amdgcn_readlane(e_M, b);
+  ip.N = __builtin_amdgcn_readlane(e_N, b);
+  ip.gpre = __builtin_amdgcn_readlane(e_g0, b);
+  ip.G = __builtin_amdgcn_readlane(e_g1, b) - ip.gpre;
+  ip.z_off = __builtin_amdgcn_readlane(e_z, b);
+  ip.p_off = __builtin_amdgcn_readlane(e_p, b);
+  ip.uoff = __builtin_amdgcn_readlane(e_u, b);
+  const int N = ip.N;
   int4 (*const smip)[NGS] = reinterpret_cast<int4 (*)[NGS]>(&smi[0][0]);  // (used only with ARG)
 #define SG_BLOCK(NV, R)                                                                                      \
-  sink_iter_block<W, RPW, NV, R, ARG, NGS>(Zb, pt, b, gb, Pin, Pdin, u_out, Pout, Pdout, PV, PI, alpha2, update_u, \
-                                           sm, vl, sm_u, smip)
+  sink_iter_block<W, RPW, NV, R, ARG, NGS>(Zb, ip, Pin, Pdin, u_out, Pout, Pdout, PV, PI, alpha2, update_u, sm, vl, \
+                                           sm_u, smip)
   if constexpr (NVMAX >= 8) {
     if (N > 1024) {
       SG_BLOCK(8, 1);
