@@ -179,11 +179,17 @@ __device__ __forceinline__ void args_in_sgprs(const T&... v) {
   (arg_in_sgprs(v), ...);
 }
 
-// Pair of a flattened row index given prefix sums `pre` of per-pair rows.
+// Pair of a flattened row index g (the same in every lane of the wave) given
+// prefix sums `pre` of per-pair rows (n_pairs + 1 entries, n_pairs <= 64):
+// the count of pairs whose rows end at or before g, from one load per lane
+// and a ballot.  (A search over the sums would chain up to n_pairs dependent
+// scalar loads before the kernel's first data load.)  Call with the whole
+// wave active; returns n_pairs when g is past the last pair.
+static_assert(SG_MAX_BATCH <= 64, "find_pair takes one lane per pair");
 __device__ __forceinline__ int find_pair(const int* pre, int n_pairs, int g) {
-  int b = 0;
-  while (b < n_pairs && g >= pre[b + 1]) ++b;
-  return b;
+  const int lane = threadIdx.x & 63;
+  const int e = lane < n_pairs ? pre[lane + 1] : 0;
+  return __popcll(__ballot(lane < n_pairs && g >= e));
 }
 
 }  // namespace sg
