@@ -383,6 +383,31 @@ def latency_percentiles(step, sg, torch, n):
     return {"passes": n, "p10_ms": q(0.1), "p50_ms": q(0.5), "p90_ms": q(0.9)}
 
 
+def graph_iteration_us(sg, torch, step, steps, T, reps=3):
+    """Microseconds per Sinkhorn iteration inside the replayed graph of the
+    pass: (time of a pass with T iterations - time of the same pass with
+    none) / T, each the median over `reps` runs of `steps` back-to-back
+    replays bracketed by HIP events on the current stream (the library's)."""
+    if T <= 0:
+        return None
+
+    def per_pass(t_iter):
+        for _ in range(3):  # eager, capture, replay
+            step(T=t_iter)
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                step(T=t_iter)
+            e.record()
+            e.synchronize()
+            out.append(a.elapsed_time(e) * 1e3 / steps)
+        return sorted(out)[reps // 2]
+    return (per_pass(T) - per_pass(0)) / T
+
+
 def concurrent_calls(args, sg, torch, W, t, img, cfg, M, N, dev, calls=400):
     """Single-pair calls (the headline's pair, one per call) spread round-robin
     over S streams of default priority, each stream with its own workspace
@@ -642,8 +667,9 @@ def main():
     bufs = {"matches0": torch.empty(M, dtype=torch.int32, device=dev),
             "scores0": torch.empty(M, dtype=torch.float32, device=dev)}
 
-    def step(**kw):
-        return sg.sg_match(*t, W, cfg.L, cfg.T, image_size=img, workspace=ws, out=bufs, sinkhorn=args.sinkhorn,
+    def step(T=None, **kw):
+        return sg.sg_match(*t, W, cfg.L, cfg.T if T is None else T, image_size=img, workspace=ws, out=bufs,
+                           sinkhorn=args.sinkhorn,
                            shared_similarity=args.shared_similarity, **kw)
 
     log(f"warmup {args.warmup} steps")
@@ -782,6 +808,15 @@ def main():
                         "algorithmic_bytes_per_iteration": 2 * per_launch,
                         "iteration_us": round(2 * kernels[dom]["avg_us"], 3),
                         "avg_launch_us": kernels[dom]["avg_us"]}
+            # the same iterations inside the replayed graph the headline runs:
+            # the pass with T iterations against the same pass with none (its
+            # extraction then takes the column argmax of Z itself), both timed
+            # with HIP events around back-to-back replays on the library's stream
+            it_graph = graph_iteration_us(sg, torch, step, args.steps, cfg.T)
+            if it_graph is not None:
+                ach_g = 2 * per_launch / (it_graph * 1e-6) / 1e9
+                roofline["graph_replayed"] = {"iteration_us": round(it_graph, 3), "achieved": round(ach_g, 1),
+                                              "frac": round(ach_g / PEAK["hbm_GBps"], 4)}
         elif dom == "attention":
             fl = attention_flops(cfg, M, N)
             ach = (sum(fl) / len(fl)) / (kernels[dom]["avg_us"] * 1e-6) / 1e12
@@ -804,9 +839,10 @@ def main():
         bbufs = {"matches0": torch.empty((Bn, M), dtype=torch.int32, device=dev),
                  "scores0": torch.empty((Bn, M), dtype=torch.float32, device=dev)}
 
-        def bstep(**kw):
-            return sg.sg_match_batch(Ms, Ns, *[bt[k] for k in keys], W, cfg.L, cfg.T, image_size=img,
-                                     workspace=wsb, want_matches1=False, sinkhorn=args.sinkhorn, out=bbufs, **kw)
+        def bstep(T=None, **kw):
+            return sg.sg_match_batch(Ms, Ns, *[bt[k] for k in keys], W, cfg.L, cfg.T if T is None else T,
+                                     image_size=img, workspace=wsb, want_matches1=False, sinkhorn=args.sinkhorn,
+                                     out=bbufs, **kw)
         for _ in range(max(2, args.warmup)):
             bstep()
         torch.cuda.synchronize()
