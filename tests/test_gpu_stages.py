@@ -187,7 +187,7 @@ def test_match_stage_extreme_dustbin(M, N, alpha, sched):
     mass; at 60 every unmatched row's maximum is its dustbin entry; at 400
     every row's and column's is, so each real entry's exponential relative to
     its row maximum underflows and the one-pass schedule's column partials
-    take their exact path.  Held to max(1e-3, 2e-6 max|logP|)."""
+    take their exact path.  Held to the 1e-3 bar (|logP| reaches ~440)."""
     fA, fB = synth.random_matching_descriptors(M, N, 256, seed=M + 3 * N)
     out = sg.sg_stage_match(dev(fA), dev(fB), alpha, 100, sinkhorn=sched)
     torch.cuda.synchronize()
@@ -197,7 +197,7 @@ def test_match_stage_extreme_dustbin(M, N, alpha, sched):
     ex = check_matches(host(out["matches0"]), host(out["matches1"]), r["logP"], r["matches0"], r["matches1"])
     print(f"{M}x{N} alpha {alpha}: max |logP| {big:.0f}, max |dlogP| {err:.2e}, "
           f"matches {int((r['matches0'] >= 0).sum())}, exempt {ex}")
-    assert err < max(1e-3, 2e-6 * big)
+    assert err < 1e-3
     cs = np.exp(host(out["logP"]).astype(np.float64)).sum(axis=0)
     np.testing.assert_allclose(cs, np.append(np.ones(N), M), rtol=1e-4)
 
@@ -207,8 +207,10 @@ def test_match_stage_extreme_dustbin(M, N, alpha, sched):
 def test_match_stage_wide_score_range(scale, sched):
     """Scores spanning hundreds of log2 units: exponentials relative to a row's
     maximum underflow, which the one-pass schedule's column partials must
-    detect and recompute exactly.  logP reaches several hundred, where fp32
-    spacing is ~3e-5; held to max(1e-3, 2e-6 max|logP|)."""
+    detect and recompute exactly.  At scale 6 (|logP| up to ~550) held to the
+    1e-3 bar; at scale 9 |logP| reaches ~1250, where one fp32 step of logP is
+    1.2e-4 and the bar is 8 such steps, so it is held to 2e-6 max|logP|
+    instead (the two-sweep schedule measured 2.1e-3 there)."""
     fA, fB = synth.random_matching_descriptors(300, 280, 64, seed=5, scale=scale)
     out = sg.sg_stage_match(dev(fA), dev(fB), 1.0, 100, sinkhorn=sched)
     r = oracle.match_from_descriptors(fA, fB, 1.0, 100)
@@ -216,7 +218,7 @@ def test_match_stage_wide_score_range(scale, sched):
     err = np.abs(host(out["logP"]) - r["logP"]).max()
     print(f"scale {scale}: max |logP| {big:.0f}, max |dlogP| {err:.2e}")
     assert big > 100
-    assert err < max(1e-3, 2e-6 * big)
+    assert err < (1e-3 if scale <= 6.0 else max(1e-3, 2e-6 * big))
     check_matches(host(out["matches0"]), host(out["matches1"]), r["logP"], r["matches0"], r["matches1"])
 
 
